@@ -1,0 +1,337 @@
+"""Pins for the CPU oracle: each test checks the oracle against something other
+than itself (a format table, a hand-worked example, brute force, a closed
+form, a mathematical identity or a special case that reduces to a library
+routine), chosen so that a dropped term, a wrong sign or index, or a
+transposed operand fails at least one of them."""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_token_lightning_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---- element decoders --------------------------------------------------------
+
+def test_e4m3fn_decoder_matches_format_table():
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.decode_element(codes, "fp8_e4m3")
+    # hand-known points of OCP E4M3FN: max normal, min subnormal, min normal, +-1, zero
+    assert got[0x7E] == 448.0 and got[0xFE] == -448.0
+    assert got[0x01] == 2.0 ** -9 and got[0x07] == 7 * 2.0 ** -9
+    assert got[0x08] == 2.0 ** -6
+    assert got[0x38] == 1.0 and got[0xB8] == -1.0
+    assert got[0x00] == 0.0 and np.signbit(got[0x80])
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+    # every code against torch's float8_e4m3fn cast (an independent library)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok]) and np.isnan(got[~ok]).all()
+
+
+def test_bf16_and_fp16_decoders_match_library_casts():
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 2 ** 16, size=4096, dtype=np.uint16)
+    finite = ((bits >> 7) & 0xFF) != 0xFF
+    got = oracle.decode_element(bits[finite], "bf16")
+    ref = torch.from_numpy(bits[finite].view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(got, ref.astype(np.float64))
+    finite16 = ((bits >> 10) & 0x1F) != 0x1F
+    got16 = oracle.decode_element(bits[finite16], "fp16")
+    assert np.array_equal(got16, bits[finite16].view(np.float16).astype(np.float64))
+
+
+# ---- top-k ------------------------------------------------------------------
+
+def _brute_topk(s, k):
+    """The unique k-subset whose every member beats every non-member under
+    (score desc, position asc), found by enumerating all subsets."""
+    n = len(s)
+    if k >= n:
+        return list(range(n)) + [-1] * (k - n)
+
+    def beats(i, j):
+        return s[i] > s[j] or (s[i] == s[j] and i < j)
+
+    winners = [c for c in itertools.combinations(range(n), k)
+               if all(beats(i, j) for i in c for j in range(n) if j not in c)]
+    assert len(winners) == 1
+    return list(winners[0])
+
+
+def test_topk_matches_brute_force_on_tiny_rows():
+    rng = np.random.default_rng(11)
+    for trial in range(300):
+        n = int(rng.integers(1, 11))
+        s = rng.integers(-3, 4, size=n).astype(np.float64)  # many ties
+        if trial % 3 == 0:
+            s = rng.standard_normal(n)
+        for k in range(1, n + 3):
+            got = oracle.topk(s[None, :], [n], k)[0].tolist()
+            assert got == _brute_topk(s.tolist(), k), (s, k)
+
+
+def test_topk_special_cases():
+    # all-equal: the first k positions
+    assert oracle.topk(np.zeros((1, 9)), [9], 4)[0].tolist() == [0, 1, 2, 3]
+    # -0 and +0 are one value: the lower position wins
+    s = np.array([[-0.0, 0.0, -1.0]])
+    assert oracle.topk(s, [3], 1)[0].tolist() == [0]
+    s = np.array([[0.0, -0.0, -1.0]])
+    assert oracle.topk(s, [3], 1)[0].tolist() == [0]
+    # visible length shorter than the stored row
+    s = np.array([[1.0, 2.0, 3.0, 100.0]])
+    assert oracle.topk(s, [3], 2)[0].tolist() == [1, 2]
+    # textbook case: distinct scores -> the positions of the k largest (numpy argsort)
+    rng = np.random.default_rng(5)
+    s = rng.permutation(5000).astype(np.float64)[None, :]
+    ref = np.sort(np.argsort(-s[0])[:100])
+    assert np.array_equal(oracle.topk(s, [5000], 100)[0], ref)
+
+
+# ---- decode scoring -----------------------------------------------------------
+
+def _decode_from_lists(q, w, keys, k):
+    H, D = len(q), len(q[0])
+    return inputs.Decode(q=inputs.encode_bf16(np.array([q], np.float32)), w=np.array([w], np.float32),
+                         kc=inputs.encode_bf16(np.array(keys, np.float32)), k_scale=None,
+                         kv_off=np.array([0, len(keys)], np.int64), H=H, D=D, k=k, k_dt="bf16")
+
+
+def _run_decode(x, k=None):
+    return oracle.index_decode(x.q, x.q_dt, x.w, x.kc, x.k_dt, x.k_scale, x.kv_off, x.H, x.D,
+                               x.k if k is None else k)
+
+
+def test_decode_hand_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "decode_hand_example.json")))
+    for req in g["requests"]:
+        for k, want in req["topk"].items():
+            x = _decode_from_lists(req["q"], req["w"], req["keys"], int(k))
+            idx, sc, ab = _run_decode(x)
+            assert sc.tolist() == req["scores"]
+            assert ab.tolist() == req["abs"]
+            assert idx[0].tolist() == want
+
+
+def test_decode_single_head_one_hot_reads_the_key():
+    """H = 1, w = 1, q = e_d: the score is ReLU(sigma_s * k_s[d]), the d-th
+    decoded key element (catches a transposed key index or a wrong scale)."""
+    x = inputs.make_decode(21, [300], H=1, D=128, k=7)
+    dec = oracle.decode_element(x.kc, "fp8_e4m3").reshape(300, 128)
+    for d in (0, 5, 127):
+        q = np.zeros((1, 1, 128), np.float32)
+        q[0, 0, d] = 1.0
+        x.q = inputs.encode_bf16(q)
+        x.w = np.ones((1, 1), np.float32)
+        _, sc, _ = _run_decode(x)
+        ref = np.maximum(x.k_scale.astype(np.float64) * dec[:, d], 0.0)
+        assert np.array_equal(sc, ref)
+
+
+def test_decode_single_head_is_relu_of_a_dot_product():
+    x = inputs.make_decode(22, [500], H=1, D=128, k=10, k_dt="bf16", dist="int")
+    x.w = np.ones((1, 1), np.float32)
+    qd = oracle.decode_element(x.q, "bf16").reshape(128)
+    kd = oracle.decode_element(x.kc, "bf16").reshape(500, 128)
+    _, sc, ab = _run_decode(x)
+    assert np.array_equal(sc, np.maximum(kd @ qd, 0))
+    assert np.array_equal(ab, np.abs(kd @ qd))
+
+
+def test_decode_integer_metamorphic_identities():
+    """Exact on integer data: linear in w, invariant to a joint head permutation,
+    equivariant under a token permutation, |S| <= A, sign follows w."""
+    x = inputs.make_decode(23, [700], H=8, D=128, k=50, k_dt="bf16", dist="int")
+    _, s0, a0 = _run_decode(x)
+    assert np.all(np.abs(s0) <= a0)
+    w0, q0 = x.w.copy(), x.q.copy()
+    rng = np.random.default_rng(3)
+    w1 = rng.integers(-2, 3, size=w0.shape).astype(np.float32)
+    x.w = w1
+    _, s1, _ = _run_decode(x)
+    x.w = w0 + w1
+    _, s01, _ = _run_decode(x)
+    assert np.array_equal(s01, s0 + s1)
+    # joint head permutation
+    perm = rng.permutation(8)
+    x.w = w0[:, perm]
+    x.q = x.q.reshape(1, 8, 128)[:, perm].copy()
+    _, sp, _ = _run_decode(x)
+    assert np.array_equal(sp, s0)
+    # non-negative weights give non-negative scores, non-positive give non-positive
+    x.w = np.abs(w0)
+    _, spos, _ = _run_decode(x)
+    x.w = -np.abs(w0)
+    _, sneg, _ = _run_decode(x)
+    assert (spos >= 0).all() and (sneg <= 0).all() and np.array_equal(spos, -sneg)
+    # token permutation
+    x.w, x.q = w0, q0
+    tperm = rng.permutation(700)
+    x.kc = x.kc.reshape(700, 128)[tperm].copy()
+    _, st, _ = _run_decode(x)
+    assert np.array_equal(st, s0[tperm])
+
+
+def test_decode_scale_by_two_is_exact_and_keeps_indices():
+    x = inputs.make_decode(24, [900, 40, 1300], H=64, D=128, k=64)
+    i0, s0, _ = _run_decode(x)
+    x.k_scale = x.k_scale * np.float32(2)
+    i1, s1, _ = _run_decode(x)
+    assert np.array_equal(s1, 2 * s0) and np.array_equal(i0, i1)
+    x.w = x.w * np.float32(2)
+    i2, s2, _ = _run_decode(x)
+    assert np.array_equal(s2, 4 * s0) and np.array_equal(i0, i2)
+
+
+def test_decode_ragged_rows_zero_query_and_short_rows():
+    x = inputs.make_decode(25, [5, 0, 12], H=4, D=128, k=8)
+    x.q = np.zeros_like(x.q)
+    idx, sc, _ = _run_decode(x)
+    assert (sc == 0).all()
+    assert idx[0].tolist() == [0, 1, 2, 3, 4, -1, -1, -1]
+    assert idx[1].tolist() == [-1] * 8
+    assert idx[2].tolist() == list(range(8))
+
+
+def test_decode_selection_separates_scores():
+    x = inputs.make_decode(26, [3000, 2500], H=64, D=128, k=300)
+    idx, sc, _ = _run_decode(x)
+    for b in range(2):
+        s = sc[x.kv_off[b]:x.kv_off[b + 1]]
+        sel = idx[b][idx[b] >= 0]
+        assert len(sel) == 300 and np.all(np.diff(sel) > 0)
+        rest = np.setdiff1d(np.arange(len(s)), sel)
+        assert s[sel].min() >= s[rest].max()
+
+
+# ---- prefill ------------------------------------------------------------------
+
+def test_prefill_rows_are_decodes_of_the_visible_prefix():
+    x = inputs.make_prefill(31, T=6, L=200, H=8, D=128, k=150)
+    idx, sc, ab = oracle.index_prefill(x.q, x.q_dt, None, x.w, x.kc, x.k_dt, x.k_scale, x.T, x.L, x.qpos0,
+                                       x.H, x.D, x.k)
+    for t in range(x.T):
+        vis = x.qpos0 + t + 1
+        # the same row through the decode oracle, with fp8 keys read as a cache
+        # of length vis and the fp8 query re-encoded exactly into bf16
+        qf = oracle.decode_element(x.q[t], "fp8_e4m3").astype(np.float32)
+        d = inputs.Decode(q=inputs.encode_bf16(qf.reshape(1, 8, 128)), w=x.w[t:t + 1], kc=x.kc[:vis],
+                          k_scale=x.k_scale[:vis], kv_off=np.array([0, vis], np.int64), H=8, D=128, k=150)
+        di, ds, da = _run_decode(d)
+        assert np.array_equal(ds, sc[t, :vis]) and np.array_equal(da, ab[t, :vis])
+        assert np.array_equal(di[0], idx[t])
+        assert np.isneginf(sc[t, vis:]).all()
+        assert idx[t].max() <= x.qpos0 + t
+
+
+def test_prefill_short_rows_return_everything_visible():
+    x = inputs.make_prefill(32, T=5, L=7, H=4, D=128, k=6)
+    idx, _, _ = oracle.index_prefill(x.q, x.q_dt, x.q_scale, x.w, x.kc, x.k_dt, x.k_scale, x.T, x.L, x.qpos0,
+                                     x.H, x.D, x.k)
+    assert x.qpos0 == 2
+    assert idx[0].tolist() == [0, 1, 2, -1, -1, -1]
+    assert idx[1].tolist() == [0, 1, 2, 3, -1, -1]
+    assert idx[3].tolist() == [0, 1, 2, 3, 4, 5]
+    assert sorted(set(idx[4].tolist())) == idx[4].tolist() and len(set(idx[4].tolist())) == 6
+
+
+def test_prefill_query_scale_power_of_two_is_exact():
+    x = inputs.make_prefill(33, T=3, L=64, H=4, D=128, k=9)
+    a = oracle.index_prefill(x.q, x.q_dt, x.q_scale, x.w, x.kc, x.k_dt, x.k_scale, x.T, x.L, x.qpos0, x.H,
+                             x.D, x.k)
+    b = oracle.index_prefill(x.q, x.q_dt, x.q_scale * np.float32(4), x.w, x.kc, x.k_dt, x.k_scale, x.T, x.L,
+                             x.qpos0, x.H, x.D, x.k)
+    vis = np.isfinite(a[1])
+    assert np.array_equal(b[1][vis], 4 * a[1][vis]) and np.array_equal(a[0], b[0])
+
+
+# ---- LatentIndex ----------------------------------------------------------------
+
+def _latent_call(x, k=None):
+    return oracle.latent_score_group(x.q, x.q_dt, x.w, x.w_dec, x.w_dt, x.latent, x.c_dt, x.c_scale, x.kv_off,
+                                     x.G, x.H, x.Dh, x.Dc, x.k if k is None else k)
+
+
+def test_latent_absorption_equals_key_reconstruction():
+    """Absorbing W_l into the query equals scoring the reconstructed
+    layer-specific keys (LatentIndex, Abstract / Figure 1)."""
+    x = inputs.make_latent(41, [37, 0, 21], G=3, H=4, Dh=16, Dc=24, k=5)
+    _, sc, ab = _latent_call(x)
+    rec = oracle.latent_reconstruct_scores(x.q, x.q_dt, x.w, x.w_dec, x.w_dt, x.latent, x.c_dt, x.c_scale,
+                                           x.kv_off, x.G, x.H, x.Dh, x.Dc)
+    assert np.all(np.abs(sc - rec) <= 1e-12 * ab + 1e-300)
+
+
+def test_latent_identity_decoder_reduces_to_native_decode():
+    """G = 1, Dc = Dh and W_{l,h} = I for every head: the latent is the key."""
+    d = inputs.make_decode(42, [130, 77], H=6, D=32, k=20, k_dt="bf16", scales=False)
+    W = np.zeros((1, 32, 6 * 32), np.float32)
+    for h in range(6):
+        W[0, :, h * 32:(h + 1) * 32] = np.eye(32)
+    x = inputs.Latent(q=d.q.reshape(2, 1, 6, 32), w=d.w.reshape(2, 1, 6), w_dec=inputs.encode_bf16(W),
+                      latent=d.kc, c_scale=None, kv_off=d.kv_off, G=1, H=6, Dh=32, Dc=32, k=20)
+    li, ls, la = _latent_call(x)
+    di, ds, da = _run_decode(d)
+    assert np.array_equal(ls[0], ds) and np.array_equal(la[0], da) and np.array_equal(li[:, 0], di)
+
+
+def test_latent_layers_are_independent_selections():
+    """Each layer's row equals the same request scored as a G = 1 group."""
+    x = inputs.make_latent(43, [90, 60], G=3, H=4, Dh=16, Dc=24, k=11)
+    li, ls, _ = _latent_call(x)
+    for l in range(3):
+        y = inputs.Latent(q=x.q[:, l:l + 1].copy(), w=x.w[:, l:l + 1].copy(), w_dec=x.w_dec[l:l + 1].copy(),
+                          latent=x.latent, c_scale=None, kv_off=x.kv_off, G=1, H=4, Dh=16, Dc=24, k=11)
+        yi, ys, _ = _latent_call(y)
+        assert np.array_equal(ys[0], ls[l]) and np.array_equal(yi[:, 0], li[:, l])
+
+
+# ---- HS -------------------------------------------------------------------------
+
+def _hs_call(cand, x, k):
+    return oracle.hs_refine(cand, x.q, x.q_dt, x.w, x.w_dec, x.w_dt, x.latent, x.c_dt, x.c_scale, x.kv_off, x.G,
+                            x.H, x.Dh, x.Dc, k)
+
+
+def test_hs_with_every_position_as_candidate_equals_the_group():
+    x = inputs.make_latent(51, [70, 45], G=3, H=4, Dh=16, Dc=24, k=9)
+    li, ls, _ = _latent_call(x)
+    C = 80
+    cand = np.full((2, C), -1, np.int32)
+    cand[0, :70] = np.arange(70)
+    cand[1, :45] = np.arange(45)
+    hi, hs, _ = _hs_call(cand, x, 9)
+    assert np.array_equal(hi, li)
+    for b in range(2):
+        n = int(x.kv_off[b + 1] - x.kv_off[b])
+        for f in range(3):
+            assert np.array_equal(hs[b, f, :n], ls[f, x.kv_off[b]:x.kv_off[b + 1]])
+
+
+def test_hs_with_k_equal_to_the_candidate_count_returns_the_candidates():
+    x = inputs.make_latent(52, [200], G=2, H=4, Dh=16, Dc=24, k=5)
+    cand = np.array([[3, 17, 18, 90, 150, 199, -1, -1]], np.int32)
+    hi, _, _ = _hs_call(cand, x, 6)
+    assert hi[0, 0].tolist() == [3, 17, 18, 90, 150, 199] and hi[0, 1].tolist() == hi[0, 0].tolist()
+    hi, _, _ = _hs_call(cand, x, 8)
+    assert hi[0, 0].tolist() == [3, 17, 18, 90, 150, 199, -1, -1]
+
+
+def test_hs_followers_pick_from_the_candidate_set_by_their_own_scores():
+    x = inputs.make_latent(53, [300], G=2, H=4, Dh=16, Dc=24, k=10)
+    _, ls, _ = _latent_call(x, k=10)
+    rng = np.random.default_rng(9)
+    cand = np.sort(rng.choice(300, size=40, replace=False)).astype(np.int32)[None, :]
+    hi, hs, _ = _hs_call(cand, x, 10)
+    for f in range(2):
+        s = ls[f, cand[0]]
+        assert np.array_equal(hs[0, f], s)
+        want = cand[0][np.sort(np.argsort(-s, kind="stable")[:10])]
+        assert np.array_equal(hi[0, f], want)
