@@ -1,0 +1,211 @@
+/*
+ * li.h — C ABI of the MI355X (gfx950) lightning-indexer library.
+ *
+ * The operation (sources are page titles and sections):
+ *   For each query token the lightning indexer scores every visible cached
+ *   token, one score per visible position, and keeps the k highest-scoring
+ *   positions (k = 2,048 in the pages) as the index tensor that sparse
+ *   attention consumes.  ("IndexCache: Cross-Layer Index Reuse for Sparse
+ *   Attention", Symbol Map and Deep Dive; "Multi-layer Indexer: Overlapping
+ *   Selection and Attention in DeepSeek Sparse Attention", The abstract.)
+ *   The score this library computes is
+ *       S[s] = sum_h w[h] * ReLU(q[h] . k[s])
+ *   with per-token scales applied to the dequantised operands, and ties in the
+ *   selection go to the lower position.
+ *   LatentIndex variant: a group of layers shares one latent cache; each layer's
+ *   key decoder is absorbed into its query so the shared cache is scored
+ *   directly, with layer-specific selection.  HS variant: follower layers
+ *   refine a candidate set proposed by the anchor layer.  ("LatentIndex:
+ *   Cross-Layer Sharing with Layer-Specific Selection for Sparse Attention",
+ *   Abstract and Figure 1.)  Shapes: 64 indexer heads x 128 dims per key
+ *   (same page, Table 5).
+ *
+ * Conventions for every entry point:
+ *   - Every array pointer is caller-owned DEVICE memory (e.g. a torch tensor's
+ *     data_ptr()); nothing is copied to or from the host.  The library keeps no
+ *     state between calls and never allocates device memory: scratch space is
+ *     the caller's workspace `ws` of `ws_bytes` bytes, sized by the matching
+ *     li_*_ws() query (it may be NULL when that query returns 0).  The query's
+ *     has_out_scores flag says whether the call will be given an out_scores
+ *     buffer; without one the scores live in the workspace.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue kernels on it and return without synchronising; results are
+ *     ready when the stream has drained.  Ragged lengths are read on the
+ *     device from `kv_off`, so the host never reads device memory.
+ *   - Errors found on the host (a NULL required pointer, a bad size, an
+ *     unsupported dtype or shape, a workspace that is too small) return a
+ *     status before anything is enqueued.  A failed kernel launch returns
+ *     LI_E_HIP; li_last_error() then holds the HIP error text (thread-local).
+ *   - Device contents are not validated: kv_off must be non-decreasing with
+ *     kv_off[0] >= 0, lengths must not exceed max_len, scales must be finite
+ *     and positive, inputs must not hold NaN/Inf codes.  Otherwise the
+ *     results are undefined (but every access stays inside the sizes the
+ *     host was given).
+ *   - Output index rows hold the kept positions in ascending order; a row
+ *     with fewer than k visible positions returns all of them and pads the
+ *     rest of its k slots with -1.  Scores compare as IEEE values with
+ *     -0 == +0; the lower position wins a tie.
+ *   - Element types: LI_BF16 (bfloat16), LI_FP8_E4M3 (OCP FP8 E4M3FN: bias 7,
+ *     max 448, no infinities), LI_FP16 (IEEE binary16), LI_FP32.
+ */
+#ifndef LI_H
+#define LI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t li_status;
+#define LI_OK 0
+#define LI_E_NULL 1        /* a required pointer is NULL */
+#define LI_E_SHAPE 2       /* a size is negative, zero where it must not be, or inconsistent */
+#define LI_E_DTYPE 3       /* an element type this entry point does not take */
+#define LI_E_WORKSPACE 4   /* ws_bytes is smaller than the li_*_ws() query */
+#define LI_E_UNSUPPORTED 5 /* a shape outside the supported set (see each entry point) */
+#define LI_E_HIP 6         /* a HIP runtime call or kernel launch failed */
+
+typedef int32_t li_dtype;
+#define LI_BF16 0
+#define LI_FP8_E4M3 1
+#define LI_FP16 2
+#define LI_FP32 3
+
+/* Largest k any entry point takes. */
+#define LI_MAX_K 16384
+
+/* ---------------------------------------------------------------------------
+ * li_index_decode — one decode step of the DSA lightning indexer.
+ *
+ * B requests with one query token each score their own ragged slice of a
+ * shared key cache and keep their top-k.  Request b owns cache rows
+ * [kv_off[b], kv_off[b+1]); its L_b = kv_off[b+1] - kv_off[b] positions are
+ * all visible.  Score of position s of request b (row r = kv_off[b] + s):
+ *     S = sum_h w[b][h] * ReLU( (q[b][h] . dec(k_cache[r])) * k_scale[r] )
+ *
+ *   q        [B][H][D]   LI_BF16
+ *   w        [B][H]      fp32 head weights
+ *   k_cache  [n_tok][D]  LI_BF16 or LI_FP8_E4M3 (one key per token, shared by all heads)
+ *   k_scale  [n_tok]     fp32 per-token dequantisation scale, or NULL (= 1)
+ *   kv_off   [B+1]       int64, device
+ *   n_tok    rows in k_cache (>= kv_off[B]); max_len >= every L_b (grid sizing)
+ *   H        1..64 heads; D must be 128; 1 <= k <= LI_MAX_K
+ *   out_idx  [B][k]      int32 positions in [0, L_b), ascending, -1 padded
+ *   out_scores [n_tok]   fp32 score of every cache row, or NULL
+ * ------------------------------------------------------------------------- */
+li_status li_index_decode(const void* q, li_dtype q_dt, const float* w, const void* k_cache,
+                          li_dtype k_dt, const float* k_scale, const int64_t* kv_off, int32_t B,
+                          int64_t n_tok, int32_t max_len, int32_t H, int32_t D, int32_t k,
+                          int32_t* out_idx, float* out_scores, void* ws, size_t ws_bytes,
+                          void* stream);
+size_t li_index_decode_ws(int32_t B, int64_t n_tok, int32_t max_len, int32_t k,
+                          int32_t has_out_scores);
+
+/* ---------------------------------------------------------------------------
+ * li_index_prefill — the indexer over a prefill chunk of one sequence.
+ *
+ * T new query tokens at positions qpos0 .. qpos0+T-1 of an L-token cache that
+ * already holds their keys.  Row t sees positions s <= qpos0 + t (causal,
+ * diagonal included).  Score:
+ *     S[t][s] = sum_h w[t][h] * ReLU( q_scale[t] * k_scale[s] * (dec(q[t][h]) . dec(k_cache[s])) )
+ *
+ *   q        [T][H][D]  LI_FP8_E4M3 ; q_scale [T] fp32 or NULL (= 1)
+ *   w        [T][H]     fp32
+ *   k_cache  [L][D]     LI_FP8_E4M3 ; k_scale [L] fp32 or NULL (= 1)
+ *   0 <= qpos0, qpos0 + T <= L;  H 1..64;  D must be 128;  1 <= k <= LI_MAX_K
+ *   out_idx    [T][k]   int32 positions, ascending, -1 padded
+ *   out_scores [T][L]   fp32 or NULL; masked positions hold -inf
+ * ------------------------------------------------------------------------- */
+li_status li_index_prefill(const void* q, li_dtype q_dt, const float* q_scale, const float* w,
+                           const void* k_cache, li_dtype k_dt, const float* k_scale, int32_t T,
+                           int32_t L, int32_t qpos0, int32_t H, int32_t D, int32_t k,
+                           int32_t* out_idx, float* out_scores, void* ws, size_t ws_bytes,
+                           void* stream);
+size_t li_index_prefill_ws(int32_t T, int32_t L, int32_t k, int32_t has_out_scores);
+
+/* Selects the MFMA operand form of the absorbed latent queries. */
+#define LI_LATENT_FP16 0u /* fp16 absorbed query (per-row power-of-two range scaling), latent
+                             converted bf16 -> fp16 on the fly; requires latent magnitudes
+                             within fp16 range (|c| <= 65504). */
+
+/* ---------------------------------------------------------------------------
+ * li_latent_score_group — LatentIndex: G layers score one shared latent cache.
+ *
+ * Layer l's key decoder w_dec[l] (stored [Dc][H*Dh]; head h's key is
+ * k[j] = sum_c w_dec[l][c][h*Dh + j] * c[c]) is absorbed into the query,
+ *     qt[b][l][h][c] = sum_j w_dec[l][c][h*Dh + j] * q[b][l][h][j],
+ * and every position s of request b is scored for every layer in one pass
+ * over the latent cache:
+ *     S_l[s] = sum_h w[b][l][h] * ReLU( c_scale[r] * (qt[b][l][h] . dec(latent[r])) )
+ * Each layer then keeps its own top-k (layer-specific selection).
+ *
+ *   q       [B][G][H][Dh] LI_BF16;  w [B][G][H] fp32
+ *   w_dec   [G][Dc][H*Dh] LI_BF16
+ *   latent  [n_tok][Dc]   LI_BF16;  c_scale [n_tok] fp32 or NULL (= 1)
+ *   kv_off  [B+1] int64, device;  max_len >= every L_b
+ *   G >= 1;  H 1..64;  Dh must be 128;  Dc 128 or 256;  1 <= k <= LI_MAX_K
+ *   out_idx    [B][G][k]  int32 positions, ascending, -1 padded
+ *   out_scores [G][n_tok] fp32 or NULL
+ *   flags      LI_LATENT_FP16
+ * ------------------------------------------------------------------------- */
+li_status li_latent_score_group(const void* q, li_dtype q_dt, const float* w, const void* w_dec,
+                                li_dtype w_dt, const void* latent, li_dtype c_dt,
+                                const float* c_scale, const int64_t* kv_off, int32_t B,
+                                int64_t n_tok, int32_t max_len, int32_t G, int32_t H, int32_t Dh,
+                                int32_t Dc, int32_t k, int32_t* out_idx, float* out_scores,
+                                uint32_t flags, void* ws, size_t ws_bytes, void* stream);
+size_t li_latent_score_group_ws(int32_t B, int64_t n_tok, int32_t G, int32_t H, int32_t Dc,
+                                int32_t k, int32_t has_out_scores);
+
+/* ---------------------------------------------------------------------------
+ * li_hs_refine — HS followers rescore only the anchor's candidate set.
+ *
+ * cand_idx [B][C] holds the anchor's kept positions for each request in
+ * ascending order, -1 padded (e.g. out_idx of li_index_decode called with
+ * k = C).  Each follower layer f < Gf absorbs its decoder into its query (as in
+ * li_latent_score_group), scores the latent rows kv_off[b] + cand_idx[b][j] of
+ * the valid candidates, and keeps its own top-k among them.
+ *
+ *   q [B][Gf][H][Dh] LI_BF16; w [B][Gf][H] fp32; w_dec [Gf][Dc][H*Dh] LI_BF16
+ *   latent [n_tok][Dc] LI_BF16; c_scale [n_tok] or NULL; kv_off [B+1] int64
+ *   1 <= C <= 65536; Gf >= 1; H 1..64; Dh 128; Dc 128 or 256; 1 <= k <= LI_MAX_K
+ *   out_idx    [B][Gf][k] int32 TOKEN positions (taken from cand_idx), ascending, -1 padded
+ *   out_scores [B][Gf][C] fp32 score of candidate slot j, or NULL (slots past
+ *              the valid candidates are not written)
+ *   flags      LI_LATENT_FP16
+ * ------------------------------------------------------------------------- */
+li_status li_hs_refine(const int32_t* cand_idx, int32_t C, const void* q, li_dtype q_dt,
+                       const float* w, const void* w_dec, li_dtype w_dt, const void* latent,
+                       li_dtype c_dt, const float* c_scale, const int64_t* kv_off, int32_t B,
+                       int32_t Gf, int32_t H, int32_t Dh, int32_t Dc, int32_t k, int32_t* out_idx,
+                       float* out_scores, uint32_t flags, void* ws, size_t ws_bytes, void* stream);
+size_t li_hs_refine_ws(int32_t B, int32_t C, int32_t Gf, int32_t H, int32_t Dc, int32_t k,
+                       int32_t has_out_scores);
+
+/* ---------------------------------------------------------------------------
+ * li_topk — the selection step on its own: per-row top-k of fp32 scores.
+ *
+ * Row r holds row_len[r] (or n, when row_len is NULL) scores at
+ * scores + r * row_stride.  Keeps the k highest (ties: lower position; -0 == +0),
+ * writes their positions ascending, -1 padded.  (IndexCache page, Deep Dive:
+ * the indexer takes top-k of its scores to obtain the index tensor.)
+ *
+ *   scores [rows][row_stride] fp32; row_len [rows] int32 device or NULL,
+ *   each 0 <= row_len[r] <= row_stride (not checked: device memory)
+ *   0 <= n <= row_stride; 1 <= k <= LI_MAX_K; out_idx [rows][k] int32
+ * ------------------------------------------------------------------------- */
+li_status li_topk(const float* scores, int64_t row_stride, const int32_t* row_len, int32_t rows,
+                  int32_t n, int32_t k, int32_t* out_idx, void* ws, size_t ws_bytes, void* stream);
+size_t li_topk_ws(int32_t rows, int32_t n, int32_t k);
+
+/* Human-readable name of a status code (static storage). */
+const char* li_status_str(li_status s);
+/* Detail of the last error on this thread (e.g. the HIP error text); "" if none. */
+const char* li_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LI_H */

@@ -1,1 +1,193 @@
+"""Python binding of the MI355X lightning-indexer library (libli.so).
 
+Argument marshalling only: every step of the scan, the selection, the latent
+absorption and the HS rescoring runs in the HIP kernels behind the C ABI
+declared in ``include/li.h``.  The functions carry the ABI's names and take
+torch tensors that already live on the GPU; torch supplies device memory (the
+workspace and default outputs) and the current stream.
+
+There is no fallback: if ``libli.so`` has not been built, or the GPU is
+missing, every call raises.
+"""
+import ctypes as C
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libli.so")
+
+LI_OK, LI_E_NULL, LI_E_SHAPE, LI_E_DTYPE, LI_E_WORKSPACE, LI_E_UNSUPPORTED, LI_E_HIP = range(7)
+LI_BF16, LI_FP8_E4M3, LI_FP16, LI_FP32 = range(4)
+LI_LATENT_FP16 = 0
+LI_MAX_K = 16384
+
+# Every symbol include/li.h declares.
+SYMBOLS = ("li_index_decode", "li_index_decode_ws", "li_index_prefill", "li_index_prefill_ws",
+           "li_latent_score_group", "li_latent_score_group_ws", "li_hs_refine", "li_hs_refine_ws",
+           "li_topk", "li_topk_ws", "li_status_str", "li_last_error")
+
+_lib = None
+
+
+class LiError(RuntimeError):
+    def __init__(self, status, detail):
+        self.status = status
+        super().__init__(f"{detail}")
+
+
+def lib():
+    """Load libli.so (built by ``build.py``); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run sparse_attention_token_lightning_amd/build.py")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, i64, sz, u32 = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t, C.c_uint32
+        L.li_index_decode.argtypes = [vp, i32, vp, vp, i32, vp, vp, i32, i64, i32, i32, i32, i32, vp, vp, vp, sz, vp]
+        L.li_index_decode_ws.argtypes = [i32, i64, i32, i32, i32]
+        L.li_index_prefill.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp]
+        L.li_index_prefill_ws.argtypes = [i32, i32, i32, i32]
+        L.li_latent_score_group.argtypes = [vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, i64, i32, i32, i32, i32, i32,
+                                            i32, vp, vp, u32, vp, sz, vp]
+        L.li_latent_score_group_ws.argtypes = [i32, i64, i32, i32, i32, i32, i32]
+        L.li_hs_refine.argtypes = [vp, i32, vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, vp,
+                                   vp, u32, vp, sz, vp]
+        L.li_hs_refine_ws.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        L.li_topk.argtypes = [vp, i64, vp, i32, i32, i32, vp, vp, sz, vp]
+        L.li_topk_ws.argtypes = [i32, i32, i32]
+        for f in ("li_index_decode", "li_index_prefill", "li_latent_score_group", "li_hs_refine", "li_topk"):
+            getattr(L, f).restype = C.c_int32
+        for f in ("li_index_decode_ws", "li_index_prefill_ws", "li_latent_score_group_ws", "li_hs_refine_ws",
+                  "li_topk_ws"):
+            getattr(L, f).restype = C.c_size_t
+        L.li_status_str.argtypes = [i32]
+        L.li_status_str.restype = C.c_char_p
+        L.li_last_error.argtypes = []
+        L.li_last_error.restype = C.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(st):
+    if st != LI_OK:
+        L = lib()
+        raise LiError(st, f"{L.li_status_str(st).decode()}: {L.li_last_error().decode()}")
+
+
+_DT = {torch.bfloat16: LI_BF16, torch.float8_e4m3fn: LI_FP8_E4M3, torch.float16: LI_FP16, torch.float32: LI_FP32}
+
+
+def _dt(t):
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported element type {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _workspace(nbytes, device, ws):
+    if nbytes == 0:
+        return None, 0
+    if ws is not None:
+        return ws, ws.numel() * ws.element_size()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def li_index_decode(q, w, k_cache, k_scale, kv_off, max_len, k, out_idx=None, out_scores=None, ws=None,
+                    stream=None):
+    """Decode scan + top-k.  q [B,H,D] bf16, w [B,H] fp32, k_cache [n_tok,D] bf16 or
+    float8_e4m3fn, k_scale [n_tok] fp32 or None, kv_off [B+1] int64.  Returns
+    out_idx [B,k] int32."""
+    B, H, D = q.shape
+    n_tok = k_cache.shape[0]
+    if out_idx is None:
+        out_idx = torch.empty((B, k), dtype=torch.int32, device=q.device)
+    L = lib()
+    need = L.li_index_decode_ws(B, n_tok, max_len, k, int(out_scores is not None))
+    wst, wsb = _workspace(need, q.device, ws)
+    _check(L.li_index_decode(_ptr(q), _dt(q), _ptr(w), _ptr(k_cache), _dt(k_cache), _ptr(k_scale), _ptr(kv_off), B,
+                             n_tok, max_len, H, D, k, _ptr(out_idx), _ptr(out_scores), _ptr(wst), wsb,
+                             _stream(stream)))
+    return out_idx
+
+
+def li_index_prefill(q, q_scale, w, k_cache, k_scale, qpos0, k, out_idx=None, out_scores=None, ws=None,
+                     stream=None):
+    """Causal prefill scan + top-k.  q [T,H,D] float8_e4m3fn, q_scale [T] or None,
+    w [T,H] fp32, k_cache [L,D] float8_e4m3fn, k_scale [L] or None.  Returns
+    out_idx [T,k] int32."""
+    T, H, D = q.shape
+    Lc = k_cache.shape[0]
+    if out_idx is None:
+        out_idx = torch.empty((T, k), dtype=torch.int32, device=q.device)
+    L = lib()
+    need = L.li_index_prefill_ws(T, Lc, k, int(out_scores is not None))
+    wst, wsb = _workspace(need, q.device, ws)
+    _check(L.li_index_prefill(_ptr(q), _dt(q), _ptr(q_scale), _ptr(w), _ptr(k_cache), _dt(k_cache), _ptr(k_scale),
+                              T, Lc, qpos0, H, D, k, _ptr(out_idx), _ptr(out_scores), _ptr(wst), wsb,
+                              _stream(stream)))
+    return out_idx
+
+
+def li_latent_score_group(q, w, w_dec, latent, c_scale, kv_off, max_len, k, out_idx=None, out_scores=None,
+                          flags=LI_LATENT_FP16, ws=None, stream=None):
+    """LatentIndex group scan + per-layer top-k.  q [B,G,H,Dh] bf16, w [B,G,H] fp32,
+    w_dec [G,Dc,H*Dh] bf16, latent [n_tok,Dc] bf16.  Returns out_idx [B,G,k]."""
+    B, G, H, Dh = q.shape
+    n_tok, Dc = latent.shape
+    if out_idx is None:
+        out_idx = torch.empty((B, G, k), dtype=torch.int32, device=q.device)
+    L = lib()
+    need = L.li_latent_score_group_ws(B, n_tok, G, H, Dc, k, int(out_scores is not None))
+    wst, wsb = _workspace(need, q.device, ws)
+    _check(L.li_latent_score_group(_ptr(q), _dt(q), _ptr(w), _ptr(w_dec), _dt(w_dec), _ptr(latent), _dt(latent),
+                                   _ptr(c_scale), _ptr(kv_off), B, n_tok, max_len, G, H, Dh, Dc, k, _ptr(out_idx),
+                                   _ptr(out_scores), flags, _ptr(wst), wsb, _stream(stream)))
+    return out_idx
+
+
+def li_hs_refine(cand_idx, q, w, w_dec, latent, c_scale, kv_off, k, out_idx=None, out_scores=None,
+                 flags=LI_LATENT_FP16, ws=None, stream=None):
+    """HS follower rescoring.  cand_idx [B,C] int32 (ascending, -1 padded),
+    q [B,Gf,H,Dh] bf16, w [B,Gf,H], w_dec [Gf,Dc,H*Dh] bf16, latent [n_tok,Dc]
+    bf16.  Returns out_idx [B,Gf,k] token positions."""
+    B, Cn = cand_idx.shape
+    _, Gf, H, Dh = q.shape
+    Dc = latent.shape[1]
+    if out_idx is None:
+        out_idx = torch.empty((B, Gf, k), dtype=torch.int32, device=q.device)
+    L = lib()
+    need = L.li_hs_refine_ws(B, Cn, Gf, H, Dc, k, int(out_scores is not None))
+    wst, wsb = _workspace(need, q.device, ws)
+    _check(L.li_hs_refine(_ptr(cand_idx), Cn, _ptr(q), _dt(q), _ptr(w), _ptr(w_dec), _dt(w_dec), _ptr(latent),
+                          _dt(latent), _ptr(c_scale), _ptr(kv_off), B, Gf, H, Dh, Dc, k, _ptr(out_idx),
+                          _ptr(out_scores), flags, _ptr(wst), wsb, _stream(stream)))
+    return out_idx
+
+
+def li_topk(scores, k, row_len=None, n=None, out_idx=None, ws=None, stream=None):
+    """Row-wise top-k of scores [rows, stride] fp32; row_len [rows] int32 or None."""
+    rows, stride = scores.shape
+    n = stride if n is None else n
+    if out_idx is None:
+        out_idx = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
+    L = lib()
+    need = L.li_topk_ws(rows, n, k)
+    wst, wsb = _workspace(need, scores.device, ws)
+    _check(L.li_topk(_ptr(scores), stride, _ptr(row_len), rows, n, k, _ptr(out_idx), _ptr(wst), wsb,
+                     _stream(stream)))
+    return out_idx

@@ -1,0 +1,274 @@
+// LatentIndex and HS kernels on gfx950 ("LatentIndex: Cross-Layer Sharing with
+// Layer-Specific Selection for Sparse Attention", Abstract and Figure 1).
+//
+// A group of G layers shares one latent cache c (one Dc-dim row per token).
+// Layer l's key decoder W_l ([Dc][H*Dh]; head h's key is
+// k[j] = sum_c W_l[c][h*Dh + j] c[c]) is absorbed into the query,
+//   qt[l][h][c] = sum_j W_l[c][h*Dh + j] q[l][h][j],
+// so every historical token is scored straight from the shared cache,
+//   S_l[s] = c_scale[s] * sum_h w[l][h] * ReLU(qt[l][h] . c_s),
+// without reconstructing per-layer keys.  HS followers do the same over the
+// anchor's candidate rows only.
+//
+// latent_absorb: one workgroup per (layer, head); fp32 accumulation; the
+//   result is stored as an fp16 MFMA operand after scaling the row by a power
+//   of two that puts its largest magnitude in [2^14, 2^15) (exact), with the
+//   inverse folded into the head weight.  fp16 keeps 11 significant bits,
+//   which is what the score tolerance needs; bf16 (8 bits) would not.
+// latent_score: one pass over the latent rows for all layers of the group.  A
+//   workgroup stages 32 latent rows at a time through LDS, converting bf16 ->
+//   fp16 once (exact in fp16 range) and writing them in MFMA-fragment order;
+//   each of its four waves holds one layer's 64 x Dc absorbed query in
+//   registers and runs v_mfma_f32_32x32x16_f16 against the shared tile, then
+//   the same ReLU-weighted head reduction as the native scan.  The gather
+//   variant (HS) reads rows kv_off[b] + cand[b][j] instead of contiguous ones.
+#include <math.h>
+
+#include "li_device.h"
+#include "li_internal.h"
+
+namespace li {
+namespace {
+
+constexpr int kAbsB = 32;  // requests per absorb pass
+
+__global__ __launch_bounds__(256) void latent_absorb_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ w_dec,
+    int B, int G, int H, int Dc, uint16_t* __restrict__ qt16, float* __restrict__ wsc) {
+  constexpr int Dh = 128;
+  __shared__ float qs[kAbsB][Dh];
+  __shared__ float red[kAbsB][4];
+  const int l = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+  const int c = threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint16_t* wrow = w_dec + ((int64_t)l * Dc + (c < Dc ? c : 0)) * (int64_t)H * Dh + (int64_t)h * Dh;
+
+  for (int b0 = 0; b0 < B; b0 += kAbsB) {
+    const int nb = (B - b0) < kAbsB ? (B - b0) : kAbsB;
+    for (int i = threadIdx.x; i < kAbsB * Dh; i += 256) {
+      const int bi = i / Dh, j = i - (i / Dh) * Dh;
+      float v = 0.0f;
+      if (bi < nb) {
+        const uint16_t raw = q[(((int64_t)(b0 + bi) * G + l) * H + h) * Dh + j];
+        v = __builtin_bit_cast(float, (uint32_t)raw << 16);
+      }
+      qs[bi][j] = v;
+    }
+    __syncthreads();
+    float acc[kAbsB];
+#pragma unroll
+    for (int bi = 0; bi < kAbsB; ++bi) acc[bi] = 0.0f;
+    if (c < Dc) {
+#pragma unroll 1
+      for (int j0 = 0; j0 < Dh; j0 += 8) {
+        const i32x4 v = ld16(wrow + j0);
+        const int parts[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int word = parts[e >> 1];
+          const float wv = __builtin_bit_cast(float, (e & 1) ? (word & (int)0xFFFF0000u) : (word << 16));
+#pragma unroll
+          for (int bi = 0; bi < kAbsB; ++bi) acc[bi] = fmaf(wv, qs[bi][j0 + e], acc[bi]);
+        }
+      }
+    }
+#pragma unroll
+    for (int bi = 0; bi < kAbsB; ++bi) {
+      const float m = wave_max(c < Dc ? fabsf(acc[bi]) : 0.0f);
+      if (lane == 0) red[bi][wave] = m;
+    }
+    __syncthreads();
+    for (int bi = 0; bi < nb; ++bi) {
+      const float mx = fmaxf(fmaxf(red[bi][0], red[bi][1]), fmaxf(red[bi][2], red[bi][3]));
+      int E = 0;
+      if (mx > 0.0f) frexpf(mx, &E);
+      const int e = mx > 0.0f ? 15 - E : 0;  // mx * 2^e in [2^14, 2^15)
+      const int64_t rowi = ((int64_t)(b0 + bi) * G + l) * H + h;
+      if (c < Dc) {
+        const _Float16 hv = (_Float16)ldexpf(acc[bi], e);
+        qt16[rowi * Dc + c] = __builtin_bit_cast(uint16_t, hv);
+      }
+      if (c == 0) wsc[rowi] = ldexpf(w[rowi], -e);
+    }
+    __syncthreads();
+  }
+}
+
+constexpr int kLsWaves = 4;  // layers per workgroup, one per wave
+
+// DC: latent width (128 or 256).  GATHER: rows come from the candidate list.
+template <int DC, bool GATHER>
+__global__ __launch_bounds__(256) void latent_score_kernel(
+    const uint16_t* __restrict__ qt16, const float* __restrict__ wsc,
+    const uint16_t* __restrict__ latent, const float* __restrict__ c_scale,
+    const int64_t* __restrict__ kv_off, const int32_t* __restrict__ cand, int C, int64_t n_tok,
+    int G, int H, int tiles_per_block, float* __restrict__ scores) {
+  constexpr int KSTEPS = DC / 16;  // K = 16 per MFMA
+  constexpr int HALF = DC / 2;     // dims per lane half
+  constexpr int CPT = DC / 64;     // 8-element chunks per thread per tile
+  __shared__ i32x4 lds[2][KSTEPS * 64];
+  __shared__ int32_t sh_n;
+
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 31, g = lane >> 5;
+  const int l = blockIdx.z * kLsWaves + wave;
+  const bool active = l < G;
+
+  const int64_t off = kv_off[b];
+  int64_t n;
+  const int32_t* cb = nullptr;
+  if constexpr (GATHER) {
+    cb = cand + (int64_t)b * C;
+    if (threadIdx.x == 0) {
+      int lo = 0, hi = C;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (cb[mid] < 0) hi = mid; else lo = mid + 1;
+      }
+      sh_n = lo;
+    }
+    __syncthreads();
+    n = sh_n;
+  } else {
+    n = kv_off[b + 1] - off;
+  }
+  const int64_t tok0 = (int64_t)blockIdx.x * tiles_per_block * 32;
+  if (tok0 >= n) return;
+  int64_t ntl = (n - tok0 + 31) / 32;
+  const int ntiles = (int)(ntl < tiles_per_block ? ntl : tiles_per_block);
+
+  f16x8 qa[2][KSTEPS];
+  float wl[2][16];
+  if (active) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int row = hb * 32 + col;
+      const uint16_t* qp = qt16 + (((int64_t)b * G + l) * H + row) * DC + HALF * g;
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j) {
+        i32x4 v = {0, 0, 0, 0};
+        if (row < H) v = ld16(qp + 8 * j);
+        qa[hb][j] = __builtin_bit_cast(f16x8, v);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int head = hb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        wl[hb][r] = head < H ? wsc[((int64_t)b * G + l) * H + head] : 0.0f;
+      }
+    }
+  }
+
+  // Producer: thread -> (row pt, dims [p*CPT*8, +CPT*8)).
+  const int pt = threadIdx.x & 31, p = threadIdx.x >> 5;
+  auto row_of = [&](int64_t s) -> int64_t {
+    s = s < n ? s : n - 1;
+    if constexpr (GATHER) return off + cb[s];
+    else return off + s;
+  };
+  i32x4 pre[CPT];
+  auto gload = [&](int tile) {
+    const int64_t r = row_of(tok0 + (int64_t)tile * 32 + pt);
+    const uint16_t* src = latent + r * DC + p * CPT * 8;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) pre[i] = ld16(src + 8 * i);
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int d0 = (p * CPT + i) * 8;
+      const int gg = d0 / HALF, jj = (d0 - gg * HALF) / 8;
+      lds[buf][jj * 64 + pt + 32 * gg] = bf16x8_to_f16x8(pre[i]);
+    }
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < ntiles) gload(it + 1);
+    if (active) {
+      f32x16 a0 = {}, a1 = {};
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j) {
+        const f16x8 kb = __builtin_bit_cast(f16x8, lds[buf][j * 64 + lane]);
+        a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[0][j], kb, a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[1][j], kb, a1, 0, 0, 0);
+      }
+      float part = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        part = fmaf(wl[0][r], fmaxf(a0[r], 0.0f), part);
+        part = fmaf(wl[1][r], fmaxf(a1[r], 0.0f), part);
+      }
+      part += __shfl_xor(part, 32, 64);
+      const int64_t s = tok0 + (int64_t)it * 32 + col;
+      if (g == 0 && s < n) {
+        const float sc = c_scale ? c_scale[row_of(s)] : 1.0f;
+        if constexpr (GATHER)
+          scores[((int64_t)b * G + l) * C + s] = part * sc;
+        else
+          scores[(int64_t)l * n_tok + off + s] = part * sc;
+      }
+    }
+    if (it + 1 < ntiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+}
+
+template <bool GATHER>
+hipError_t launch_ls(int Dc, dim3 grid, hipStream_t stream, const uint16_t* qt16, const float* wsc,
+                     const uint16_t* latent, const float* c_scale, const int64_t* kv_off,
+                     const int32_t* cand, int C, int64_t n_tok, int G, int H, int tpb,
+                     float* scores) {
+  if (Dc == 256)
+    latent_score_kernel<256, GATHER><<<grid, dim3(256), 0, stream>>>(
+        qt16, wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, scores);
+  else
+    latent_score_kernel<128, GATHER><<<grid, dim3(256), 0, stream>>>(
+        qt16, wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, scores);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_latent_absorb(const uint16_t* q, const float* w, const uint16_t* w_dec,
+                                int32_t B, int32_t G, int32_t H, int32_t Dh, int32_t Dc,
+                                uint16_t* qt16, float* wsc, hipStream_t stream) {
+  (void)Dh;
+  if (B <= 0) return hipSuccess;
+  latent_absorb_kernel<<<dim3((unsigned)(G * H)), dim3(256), 0, stream>>>(q, w, w_dec, B, G, H, Dc,
+                                                                          qt16, wsc);
+  return hipGetLastError();
+}
+
+hipError_t launch_latent_score(const uint16_t* qt16, const float* wsc, const uint16_t* latent,
+                               const float* c_scale, const int64_t* kv_off, int32_t B,
+                               int64_t n_tok, int32_t max_len, int32_t G, int32_t H, int32_t Dc,
+                               float* scores, hipStream_t stream) {
+  if (B <= 0 || max_len <= 0) return hipSuccess;
+  int64_t tpb = n_tok / ((int64_t)1024 * 32);
+  tpb = tpb < 4 ? 4 : (tpb > 64 ? 64 : tpb);
+  const int64_t chunk = tpb * 32;
+  dim3 grid((unsigned)((max_len + chunk - 1) / chunk), (unsigned)B,
+            (unsigned)((G + kLsWaves - 1) / kLsWaves));
+  return launch_ls<false>(Dc, grid, stream, qt16, wsc, latent, c_scale, kv_off, nullptr, 0, n_tok,
+                          G, H, (int)tpb, scores);
+}
+
+hipError_t launch_hs_score(const uint16_t* qt16, const float* wsc, const uint16_t* latent,
+                           const float* c_scale, const int64_t* kv_off, const int32_t* cand,
+                           int32_t C, int32_t B, int32_t Gf, int32_t H, int32_t Dc, float* scores,
+                           hipStream_t stream) {
+  if (B <= 0 || C <= 0) return hipSuccess;
+  int64_t tpb = ((int64_t)B * C) / ((int64_t)512 * 32);
+  tpb = tpb < 2 ? 2 : (tpb > 32 ? 32 : tpb);
+  const int64_t chunk = tpb * 32;
+  dim3 grid((unsigned)((C + chunk - 1) / chunk), (unsigned)B,
+            (unsigned)((Gf + kLsWaves - 1) / kLsWaves));
+  return launch_ls<true>(Dc, grid, stream, qt16, wsc, latent, c_scale, kv_off, cand, C, 0, Gf, H,
+                         (int)tpb, scores);
+}
+
+}  // namespace li

@@ -1,0 +1,338 @@
+// C-ABI entry points of the lightning-indexer library (declared in li.h):
+// argument validation, workspace carving and kernel dispatch.  Every check
+// that can fail happens before the first launch; calls only enqueue work on
+// the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/li.h"
+#include "li_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+li_status fail(li_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+li_status hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return LI_OK;
+  return fail(LI_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kHistBins = 2048;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Carves consecutive aligned regions out of the caller's workspace.
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* ws) : base((char*)ws) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + used : nullptr;
+    used += align_up(bytes);
+    return p;
+  }
+};
+
+size_t decode_ws(int32_t B, int64_t n_tok, bool scores_given) {
+  size_t s = 0;
+  if (!scores_given) s += align_up((size_t)n_tok * 4);
+  s += align_up((size_t)(B > 0 ? B : 0) * kHistBins * 4);  // per-row histograms
+  return s;
+}
+
+size_t prefill_ws(int32_t T, int32_t L, bool scores_given) {
+  size_t s = 0;
+  if (!scores_given) s += align_up((size_t)T * (size_t)L * 4);
+  s += align_up((size_t)(T > 0 ? T : 0) * kHistBins * 4);
+  return s;
+}
+
+size_t latent_ws(int32_t B, int64_t n_tok, int32_t G, int32_t H, int32_t Dc, bool scores_given) {
+  const size_t rows = (size_t)B * G;
+  size_t s = align_up(rows * H * Dc * 2) + align_up(rows * H * 4);
+  if (!scores_given) s += align_up((size_t)G * (size_t)n_tok * 4);
+  s += align_up(rows * kHistBins * 4);
+  return s;
+}
+
+size_t hs_ws(int32_t B, int32_t C, int32_t Gf, int32_t H, int32_t Dc, bool scores_given) {
+  const size_t rows = (size_t)B * Gf;
+  size_t s = align_up(rows * H * Dc * 2) + align_up(rows * H * 4);
+  if (!scores_given) s += align_up(rows * (size_t)C * 4);
+  s += align_up(rows * kHistBins * 4);
+  return s;
+}
+
+li_status check_k(int32_t k) {
+  if (k <= 0) return fail(LI_E_SHAPE, "k must be >= 1 (got %d)", k);
+  if (k > LI_MAX_K) return fail(LI_E_UNSUPPORTED, "k must be <= %d (got %d)", LI_MAX_K, k);
+  return LI_OK;
+}
+
+li_status check_heads(int32_t H, int32_t D, const char* dname) {
+  if (H <= 0 || D <= 0) return fail(LI_E_SHAPE, "H and %s must be positive (H=%d %s=%d)", dname, H, dname, D);
+  if (H > 64) return fail(LI_E_UNSUPPORTED, "H must be <= 64 (got %d)", H);
+  if (D != 128) return fail(LI_E_UNSUPPORTED, "%s must be 128 (got %d)", dname, D);
+  return LI_OK;
+}
+
+li_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (ws_bytes < need)
+    return fail(LI_E_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", ws_bytes, need);
+  if (need > 0 && ws == nullptr) return fail(LI_E_NULL, "workspace pointer is NULL");
+  return LI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* li_status_str(li_status s) {
+  switch (s) {
+    case LI_OK: return "LI_OK";
+    case LI_E_NULL: return "LI_E_NULL";
+    case LI_E_SHAPE: return "LI_E_SHAPE";
+    case LI_E_DTYPE: return "LI_E_DTYPE";
+    case LI_E_WORKSPACE: return "LI_E_WORKSPACE";
+    case LI_E_UNSUPPORTED: return "LI_E_UNSUPPORTED";
+    case LI_E_HIP: return "LI_E_HIP";
+    default: return "LI_E_UNKNOWN";
+  }
+}
+
+const char* li_last_error(void) { return g_err.c_str(); }
+
+size_t li_index_decode_ws(int32_t B, int64_t n_tok, int32_t max_len, int32_t k,
+                          int32_t has_out_scores) {
+  (void)max_len;
+  (void)k;
+  return decode_ws(B, n_tok, has_out_scores != 0);
+}
+
+li_status li_index_decode(const void* q, li_dtype q_dt, const float* w, const void* k_cache,
+                          li_dtype k_dt, const float* k_scale, const int64_t* kv_off, int32_t B,
+                          int64_t n_tok, int32_t max_len, int32_t H, int32_t D, int32_t k,
+                          int32_t* out_idx, float* out_scores, void* ws, size_t ws_bytes,
+                          void* stream) {
+  g_err.clear();
+  if (!q || !w || !k_cache || !kv_off || !out_idx)
+    return fail(LI_E_NULL, "q, w, k_cache, kv_off and out_idx are required");
+  if (q_dt != LI_BF16) return fail(LI_E_DTYPE, "decode q must be LI_BF16");
+  if (k_dt != LI_BF16 && k_dt != LI_FP8_E4M3)
+    return fail(LI_E_DTYPE, "decode k_cache must be LI_BF16 or LI_FP8_E4M3");
+  if (B < 0 || n_tok < 0 || max_len < 0)
+    return fail(LI_E_SHAPE, "B, n_tok and max_len must be >= 0");
+  if (n_tok >= (int64_t)1 << 40) return fail(LI_E_UNSUPPORTED, "n_tok too large");
+  li_status st;
+  if ((st = check_k(k)) || (st = check_heads(H, D, "D"))) return st;
+  if ((st = check_ws(ws, ws_bytes, decode_ws(B, n_tok, out_scores != nullptr)))) return st;
+  if (B == 0) return LI_OK;
+  hipStream_t s = (hipStream_t)stream;
+  Carver cv(ws);
+  float* scores = out_scores ? out_scores : (float*)cv.take((size_t)n_tok * 4);
+  if ((st = hip_check(li::launch_decode_score((const uint16_t*)q, w, k_cache, k_dt == LI_FP8_E4M3,
+                                              k_scale, kv_off, B, n_tok, max_len, H, scores, s),
+                      "decode_score launch")))
+    return st;
+  li::TopkRows tr = {};
+  tr.scores = scores;
+  tr.mode = li::kRowsOffsets;
+  tr.rows = B;
+  tr.row_stride = 0;
+  tr.kv_off = kv_off;
+  tr.G = 1;
+  tr.k = k;
+  tr.out = out_idx;
+  return hip_check(li::launch_topk(tr, s), "topk launch");
+}
+
+size_t li_index_prefill_ws(int32_t T, int32_t L, int32_t k, int32_t has_out_scores) {
+  (void)k;
+  return prefill_ws(T, L, has_out_scores != 0);
+}
+
+li_status li_index_prefill(const void* q, li_dtype q_dt, const float* q_scale, const float* w,
+                           const void* k_cache, li_dtype k_dt, const float* k_scale, int32_t T,
+                           int32_t L, int32_t qpos0, int32_t H, int32_t D, int32_t k,
+                           int32_t* out_idx, float* out_scores, void* ws, size_t ws_bytes,
+                           void* stream) {
+  g_err.clear();
+  if (!q || !w || !k_cache || !out_idx)
+    return fail(LI_E_NULL, "q, w, k_cache and out_idx are required");
+  if (q_dt != LI_FP8_E4M3 || k_dt != LI_FP8_E4M3)
+    return fail(LI_E_DTYPE, "prefill q and k_cache must be LI_FP8_E4M3");
+  if (T < 0 || L < 0 || qpos0 < 0 || (int64_t)qpos0 + T > L)
+    return fail(LI_E_SHAPE, "need T >= 0, qpos0 >= 0 and qpos0 + T <= L (T=%d L=%d qpos0=%d)", T, L,
+                qpos0);
+  li_status st;
+  if ((st = check_k(k)) || (st = check_heads(H, D, "D"))) return st;
+  if ((st = check_ws(ws, ws_bytes, prefill_ws(T, L, out_scores != nullptr)))) return st;
+  if (T == 0) return LI_OK;
+  hipStream_t s = (hipStream_t)stream;
+  Carver cv(ws);
+  float* scores = out_scores ? out_scores : (float*)cv.take((size_t)T * (size_t)L * 4);
+  if ((st = hip_check(li::launch_prefill_score((const uint8_t*)q, q_scale, w, (const uint8_t*)k_cache,
+                                               k_scale, T, L, qpos0, H, out_scores != nullptr,
+                                               scores, s),
+                      "prefill_score launch")))
+    return st;
+  li::TopkRows tr = {};
+  tr.scores = scores;
+  tr.mode = li::kRowsCausal;
+  tr.rows = T;
+  tr.row_stride = L;
+  tr.n = L;
+  tr.qpos0 = qpos0;
+  tr.k = k;
+  tr.out = out_idx;
+  return hip_check(li::launch_topk(tr, s), "topk launch");
+}
+
+static li_status check_latent_common(li_dtype q_dt, li_dtype w_dt, li_dtype c_dt, int32_t H,
+                                     int32_t Dh, int32_t Dc, uint32_t flags) {
+  if (q_dt != LI_BF16 || w_dt != LI_BF16 || c_dt != LI_BF16)
+    return fail(LI_E_DTYPE, "latent q, w_dec and latent must be LI_BF16");
+  li_status st;
+  if ((st = check_heads(H, Dh, "Dh"))) return st;
+  if (Dc != 128 && Dc != 256) return fail(LI_E_UNSUPPORTED, "Dc must be 128 or 256 (got %d)", Dc);
+  if (flags != LI_LATENT_FP16) return fail(LI_E_UNSUPPORTED, "unknown flags 0x%x", flags);
+  return LI_OK;
+}
+
+size_t li_latent_score_group_ws(int32_t B, int64_t n_tok, int32_t G, int32_t H, int32_t Dc,
+                                int32_t k, int32_t has_out_scores) {
+  (void)k;
+  return latent_ws(B, n_tok, G, H, Dc, has_out_scores != 0);
+}
+
+li_status li_latent_score_group(const void* q, li_dtype q_dt, const float* w, const void* w_dec,
+                                li_dtype w_dt, const void* latent, li_dtype c_dt,
+                                const float* c_scale, const int64_t* kv_off, int32_t B,
+                                int64_t n_tok, int32_t max_len, int32_t G, int32_t H, int32_t Dh,
+                                int32_t Dc, int32_t k, int32_t* out_idx, float* out_scores,
+                                uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (!q || !w || !w_dec || !latent || !kv_off || !out_idx)
+    return fail(LI_E_NULL, "q, w, w_dec, latent, kv_off and out_idx are required");
+  li_status st;
+  if ((st = check_latent_common(q_dt, w_dt, c_dt, H, Dh, Dc, flags))) return st;
+  if (B < 0 || n_tok < 0 || max_len < 0 || G <= 0)
+    return fail(LI_E_SHAPE, "need B, n_tok, max_len >= 0 and G >= 1");
+  if ((int64_t)G * n_tok >= (int64_t)1 << 40) return fail(LI_E_UNSUPPORTED, "G * n_tok too large");
+  if ((st = check_k(k))) return st;
+  if ((st = check_ws(ws, ws_bytes, latent_ws(B, n_tok, G, H, Dc, out_scores != nullptr)))) return st;
+  if (B == 0) return LI_OK;
+  hipStream_t s = (hipStream_t)stream;
+  Carver cv(ws);
+  uint16_t* qt16 = (uint16_t*)cv.take((size_t)B * G * H * Dc * 2);
+  float* wsc = (float*)cv.take((size_t)B * G * H * 4);
+  float* scores = out_scores ? out_scores : (float*)cv.take((size_t)G * (size_t)n_tok * 4);
+  if ((st = hip_check(li::launch_latent_absorb((const uint16_t*)q, w, (const uint16_t*)w_dec, B, G,
+                                               H, Dh, Dc, qt16, wsc, s),
+                      "latent_absorb launch")))
+    return st;
+  if ((st = hip_check(li::launch_latent_score(qt16, wsc, (const uint16_t*)latent, c_scale, kv_off, B,
+                                              n_tok, max_len, G, H, Dc, scores, s),
+                      "latent_score launch")))
+    return st;
+  li::TopkRows tr = {};
+  tr.scores = scores;
+  tr.mode = li::kRowsOffsets;
+  tr.rows = B * G;
+  tr.row_stride = n_tok;
+  tr.kv_off = kv_off;
+  tr.G = G;
+  tr.k = k;
+  tr.out = out_idx;
+  return hip_check(li::launch_topk(tr, s), "topk launch");
+}
+
+size_t li_hs_refine_ws(int32_t B, int32_t C, int32_t Gf, int32_t H, int32_t Dc, int32_t k,
+                       int32_t has_out_scores) {
+  (void)k;
+  return hs_ws(B, C, Gf, H, Dc, has_out_scores != 0);
+}
+
+li_status li_hs_refine(const int32_t* cand_idx, int32_t C, const void* q, li_dtype q_dt,
+                       const float* w, const void* w_dec, li_dtype w_dt, const void* latent,
+                       li_dtype c_dt, const float* c_scale, const int64_t* kv_off, int32_t B,
+                       int32_t Gf, int32_t H, int32_t Dh, int32_t Dc, int32_t k, int32_t* out_idx,
+                       float* out_scores, uint32_t flags, void* ws, size_t ws_bytes,
+                       void* stream) {
+  g_err.clear();
+  if (!cand_idx || !q || !w || !w_dec || !latent || !kv_off || !out_idx)
+    return fail(LI_E_NULL, "cand_idx, q, w, w_dec, latent, kv_off and out_idx are required");
+  li_status st;
+  if ((st = check_latent_common(q_dt, w_dt, c_dt, H, Dh, Dc, flags))) return st;
+  if (B < 0 || Gf <= 0 || C <= 0) return fail(LI_E_SHAPE, "need B >= 0, Gf >= 1 and C >= 1");
+  if (C > 65536) return fail(LI_E_UNSUPPORTED, "C must be <= 65536 (got %d)", C);
+  if ((st = check_k(k))) return st;
+  if ((st = check_ws(ws, ws_bytes, hs_ws(B, C, Gf, H, Dc, out_scores != nullptr)))) return st;
+  if (B == 0) return LI_OK;
+  hipStream_t s = (hipStream_t)stream;
+  Carver cv(ws);
+  uint16_t* qt16 = (uint16_t*)cv.take((size_t)B * Gf * H * Dc * 2);
+  float* wsc = (float*)cv.take((size_t)B * Gf * H * 4);
+  float* scores = out_scores ? out_scores : (float*)cv.take((size_t)B * Gf * (size_t)C * 4);
+  if ((st = hip_check(li::launch_latent_absorb((const uint16_t*)q, w, (const uint16_t*)w_dec, B, Gf,
+                                               H, Dh, Dc, qt16, wsc, s),
+                      "latent_absorb launch")))
+    return st;
+  if ((st = hip_check(li::launch_hs_score(qt16, wsc, (const uint16_t*)latent, c_scale, kv_off,
+                                          cand_idx, C, B, Gf, H, Dc, scores, s),
+                      "hs_score launch")))
+    return st;
+  li::TopkRows tr = {};
+  tr.scores = scores;
+  tr.mode = li::kRowsCands;
+  tr.rows = B * Gf;
+  tr.cand = cand_idx;
+  tr.C = C;
+  tr.G = Gf;
+  tr.k = k;
+  tr.out = out_idx;
+  return hip_check(li::launch_topk(tr, s), "topk launch");
+}
+
+size_t li_topk_ws(int32_t rows, int32_t n, int32_t k) {
+  (void)n;
+  (void)k;
+  return align_up((size_t)(rows > 0 ? rows : 0) * kHistBins * 4);
+}
+
+li_status li_topk(const float* scores, int64_t row_stride, const int32_t* row_len, int32_t rows,
+                  int32_t n, int32_t k, int32_t* out_idx, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (!scores || !out_idx) return fail(LI_E_NULL, "scores and out_idx are required");
+  if (rows < 0 || n < 0 || row_stride < n)
+    return fail(LI_E_SHAPE, "need rows >= 0 and 0 <= n <= row_stride");
+  li_status st;
+  if ((st = check_k(k))) return st;
+  if ((st = check_ws(ws, ws_bytes, li_topk_ws(rows, n, k)))) return st;
+  if (rows == 0) return LI_OK;
+  li::TopkRows tr = {};
+  tr.scores = scores;
+  tr.mode = li::kRowsDense;
+  tr.rows = rows;
+  tr.row_stride = row_stride;
+  tr.row_len = row_len;
+  tr.n = n;
+  tr.k = k;
+  tr.out = out_idx;
+  return hip_check(li::launch_topk(tr, (hipStream_t)stream), "topk launch");
+}
+
+}  // extern "C"

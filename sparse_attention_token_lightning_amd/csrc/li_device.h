@@ -1,0 +1,86 @@
+// Device-side helpers shared by the gfx950 kernels of the lightning-indexer
+// library: MFMA operand vector types, exact fp8/bf16 -> MFMA-operand
+// conversions, the order-preserving key used by the top-k selection, and
+// wavefront (64-lane) scans.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace li {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+
+constexpr int kWave = 64;
+
+// 16-byte global load / store through a plain vector type.
+__device__ __forceinline__ i32x4 ld16(const void* p) { return *reinterpret_cast<const i32x4*>(p); }
+
+// Four OCP E4M3FN bytes (one dword, byte 0 first) -> four bf16, exact: every
+// E4M3FN value, subnormals included, is a bf16 normal number.  Uses gfx950's
+// packed fp8 -> bf16 conversion with a unit scale.
+__device__ __forceinline__ i32x2 fp8x4_to_bf16x4(int v) {
+  bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, false);
+  bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, true);
+  i32x2 r;
+  r.x = __builtin_bit_cast(int, lo);
+  r.y = __builtin_bit_cast(int, hi);
+  return r;
+}
+
+// Eight fp8 bytes (two dwords) -> one bf16x8 MFMA operand.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(int a, int b) {
+  i32x2 x = fp8x4_to_bf16x4(a), y = fp8x4_to_bf16x4(b);
+  i32x4 r = {x.x, x.y, y.x, y.y};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Two bf16 (one dword) -> two fp16.  Exact for |x| in [2^-17, 65504]: bf16
+// carries 8 significant bits, fp16 11 (subnormals down to 2^-24).
+__device__ __forceinline__ int bf16x2_to_f16x2(int v) {
+  float lo = __builtin_bit_cast(float, v << 16);
+  float hi = __builtin_bit_cast(float, v & (int)0xFFFF0000u);
+  f16x2 h = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  return __builtin_bit_cast(int, h);
+}
+
+__device__ __forceinline__ i32x4 bf16x8_to_f16x8(i32x4 v) {
+  i32x4 r = {bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z),
+             bf16x2_to_f16x2(v.w)};
+  return r;
+}
+
+// Order-preserving map from an fp32 score to a uint32 key: a larger score
+// gives a larger key, and -0 maps to the key of +0 so that the two compare
+// equal (the tie then goes to the lower position).  NaN is not expected.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inclusive scan of a uint32 over the 64 lanes of a wavefront.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    uint32_t o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
+  return v;
+}
+
+}  // namespace li

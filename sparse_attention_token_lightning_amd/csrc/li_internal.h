@@ -1,0 +1,68 @@
+// Host-side launchers shared between the kernel files and the C-ABI layer.
+// Every launcher only enqueues work on `stream` and returns the launch status.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace li {
+
+// How the top-k kernel finds row r of the score matrix.
+enum TopkMode : int32_t {
+  kRowsDense = 0,    // row r at scores + r*row_stride, length row_len[r] or n
+  kRowsOffsets = 1,  // row r = b*G + l at scores + l*plane + kv_off[b], length kv_off[b+1]-kv_off[b]
+  kRowsCausal = 2,   // row t at scores + t*row_stride, length min(n, qpos0 + t + 1)
+  kRowsCands = 3,    // row r = b*G + f at scores + r*C, length = valid candidates of b,
+                     // positions mapped through cand[b][.]
+};
+
+struct TopkRows {
+  const float* scores;
+  int32_t mode;
+  int32_t rows;
+  int64_t row_stride;      // dense / causal: row stride; offsets: plane stride (n_tok)
+  const int32_t* row_len;  // dense, may be null
+  int32_t n;               // dense: default length; causal: L
+  const int64_t* kv_off;   // offsets
+  int32_t G;               // offsets / candidates: rows per request
+  int32_t qpos0;           // causal
+  const int32_t* cand;     // candidates [B][C]
+  int32_t C;
+  int32_t k;
+  int32_t* out;            // [rows][k]
+};
+
+hipError_t launch_topk(const TopkRows& a, hipStream_t stream);
+
+// Decode scan: scores[kv_off[b] + s] for every request b and s < L_b.
+hipError_t launch_decode_score(const uint16_t* q, const float* w, const void* kc, bool kc_fp8,
+                               const float* k_scale, const int64_t* kv_off, int32_t B,
+                               int64_t n_tok, int32_t max_len, int32_t H, float* scores,
+                               hipStream_t stream);
+
+// Prefill scan: scores[t][s] for s <= qpos0 + t; with fill_masked also -inf
+// for the masked rest of every row.
+hipError_t launch_prefill_score(const uint8_t* q, const float* q_scale, const float* w,
+                                const uint8_t* kc, const float* k_scale, int32_t T, int32_t L,
+                                int32_t qpos0, int32_t H, bool fill_masked, float* scores,
+                                hipStream_t stream);
+
+// Latent absorption: qt16[b][l][h][Dc] (fp16, range-scaled by 2^e per row) and
+// wsc[b][l][h] = w * 2^-e.
+hipError_t launch_latent_absorb(const uint16_t* q, const float* w, const uint16_t* w_dec,
+                                int32_t B, int32_t G, int32_t H, int32_t Dh, int32_t Dc,
+                                uint16_t* qt16, float* wsc, hipStream_t stream);
+
+// Latent scan over contiguous ragged rows: scores[l*n_tok + kv_off[b] + s].
+hipError_t launch_latent_score(const uint16_t* qt16, const float* wsc, const uint16_t* latent,
+                               const float* c_scale, const int64_t* kv_off, int32_t B,
+                               int64_t n_tok, int32_t max_len, int32_t G, int32_t H, int32_t Dc,
+                               float* scores, hipStream_t stream);
+
+// HS gather scan: scores[(b*Gf + f)*C + j] for the valid candidates j of b.
+hipError_t launch_hs_score(const uint16_t* qt16, const float* wsc, const uint16_t* latent,
+                           const float* c_scale, const int64_t* kv_off, const int32_t* cand,
+                           int32_t C, int32_t B, int32_t Gf, int32_t H, int32_t Dc, float* scores,
+                           hipStream_t stream);
+
+}  // namespace li

@@ -1,0 +1,153 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/li.h declares, sizes workspaces, and rejects bad
+arguments with the documented status before touching the device."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_attention_token_lightning_amd as li
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "li.h")
+FAKE = 0x1000  # never dereferenced: every call below fails host validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(li_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert sorted(li.SYMBOLS) == declared_functions()
+
+
+def test_library_exports_every_declared_symbol():
+    L = li.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", li.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (li_[a-z_]+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_header_compiles_as_plain_c(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "li.h"\nint main(void){return LI_OK;}\n')
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), "-o",
+                    str(tmp_path / "t"), str(src)], check=True)
+
+
+def test_status_strings():
+    L = li.lib()
+    assert L.li_status_str(li.LI_OK) == b"LI_OK"
+    assert L.li_status_str(li.LI_E_WORKSPACE) == b"LI_E_WORKSPACE"
+    assert L.li_status_str(99) == b"LI_E_UNKNOWN"
+
+
+def test_workspace_queries():
+    L = li.lib()
+    n = 655360
+    with_s = L.li_index_decode_ws(32, n, 32768, 2048, 1)
+    without = L.li_index_decode_ws(32, n, 32768, 2048, 0)
+    assert without - with_s >= n * 4 and with_s >= 32 * 2048 * 4
+    assert L.li_index_prefill_ws(4096, 65536, 2048, 0) >= 4096 * 65536 * 4
+    # absorbed fp16 queries + scaled weights + scores
+    assert L.li_latent_score_group_ws(16, 1 << 21, 4, 64, 256, 2048, 0) >= 16 * 4 * 64 * 256 * 2 + 4 * (1 << 21) * 4
+    assert L.li_hs_refine_ws(16, 8192, 3, 64, 256, 2048, 0) >= 16 * 3 * 8192 * 4
+    assert L.li_topk_ws(10, 100, 5) % 256 == 0
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, q_dt=li.LI_BF16, w=FAKE, k=FAKE, k_dt=li.LI_FP8_E4M3, ks=None, off=FAKE, B=2, n_tok=100,
+             max_len=60, H=64, D=128, kk=16, out=FAKE, sc=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    L = li.lib()
+    return L.li_index_decode(a["q"], a["q_dt"], a["w"], a["k"], a["k_dt"], a["ks"], a["off"], a["B"], a["n_tok"],
+                             a["max_len"], a["H"], a["D"], a["kk"], a["out"], a["sc"], a["ws"], a["wsb"], None)
+
+
+def test_decode_validation():
+    assert _decode(q=None) == li.LI_E_NULL
+    assert _decode(off=None) == li.LI_E_NULL
+    assert _decode(q_dt=li.LI_FP16) == li.LI_E_DTYPE
+    assert _decode(k_dt=li.LI_FP32) == li.LI_E_DTYPE
+    assert _decode(kk=0) == li.LI_E_SHAPE
+    assert _decode(kk=li.LI_MAX_K + 1) == li.LI_E_UNSUPPORTED
+    assert _decode(H=65) == li.LI_E_UNSUPPORTED
+    assert _decode(H=0) == li.LI_E_SHAPE
+    assert _decode(D=64) == li.LI_E_UNSUPPORTED
+    assert _decode(B=-1) == li.LI_E_SHAPE
+    assert _decode(wsb=10) == li.LI_E_WORKSPACE
+    assert _decode(ws=None) == li.LI_E_NULL
+    assert b"workspace" in li.lib().li_last_error()
+    assert _decode(B=0) == li.LI_OK  # nothing to do: returns before any launch
+
+
+def test_prefill_validation():
+    L = li.lib()
+
+    def call(**kw):
+        a = dict(q=FAKE, q_dt=li.LI_FP8_E4M3, k_dt=li.LI_FP8_E4M3, T=10, Lc=100, qpos0=90, H=64, D=128, kk=5,
+                 wsb=1 << 34)
+        a.update(kw)
+        return L.li_index_prefill(a["q"], a["q_dt"], None, FAKE, FAKE, a["k_dt"], None, a["T"], a["Lc"], a["qpos0"],
+                                  a["H"], a["D"], a["kk"], FAKE, None, FAKE, a["wsb"], None)
+
+    assert call(q=None) == li.LI_E_NULL
+    assert call(q_dt=li.LI_BF16) == li.LI_E_DTYPE
+    assert call(qpos0=91) == li.LI_E_SHAPE
+    assert call(qpos0=-1) == li.LI_E_SHAPE
+    assert call(D=256) == li.LI_E_UNSUPPORTED
+    assert call(wsb=100) == li.LI_E_WORKSPACE
+    assert call(T=0, qpos0=0) == li.LI_OK
+
+
+def test_latent_and_hs_validation():
+    L = li.lib()
+
+    def lat(**kw):
+        a = dict(q_dt=li.LI_BF16, G=4, Dc=256, Dh=128, flags=0, kk=8, wsb=1 << 34, B=2)
+        a.update(kw)
+        return L.li_latent_score_group(FAKE, a["q_dt"], FAKE, FAKE, li.LI_BF16, FAKE, li.LI_BF16, None, FAKE, a["B"],
+                                       1000, 600, a["G"], 64, a["Dh"], a["Dc"], a["kk"], FAKE, None, a["flags"], FAKE,
+                                       a["wsb"], None)
+
+    assert lat(q_dt=li.LI_FP8_E4M3) == li.LI_E_DTYPE
+    assert lat(G=0) == li.LI_E_SHAPE
+    assert lat(Dc=192) == li.LI_E_UNSUPPORTED
+    assert lat(Dh=64) == li.LI_E_UNSUPPORTED
+    assert lat(flags=7) == li.LI_E_UNSUPPORTED
+    assert lat(wsb=1) == li.LI_E_WORKSPACE
+    assert lat(B=0) == li.LI_OK
+
+    def hs(**kw):
+        a = dict(C=8192, Gf=3, kk=2048, wsb=1 << 34)
+        a.update(kw)
+        return L.li_hs_refine(FAKE, a["C"], FAKE, li.LI_BF16, FAKE, FAKE, li.LI_BF16, FAKE, li.LI_BF16, None, FAKE,
+                              0, a["Gf"], 64, 128, 256, a["kk"], FAKE, None, 0, FAKE, a["wsb"], None)
+
+    assert hs(C=0) == li.LI_E_SHAPE
+    assert hs(C=70000) == li.LI_E_UNSUPPORTED
+    assert hs(Gf=0) == li.LI_E_SHAPE
+    assert hs() == li.LI_OK
+    assert L.li_hs_refine(None, 8, FAKE, 0, FAKE, FAKE, 0, FAKE, 0, None, FAKE, 1, 1, 64, 128, 256, 4, FAKE, None,
+                          0, FAKE, 1 << 30, None) == li.LI_E_NULL
+
+
+def test_topk_validation():
+    L = li.lib()
+    assert L.li_topk(None, 10, None, 1, 10, 1, FAKE, FAKE, 1 << 20, None) == li.LI_E_NULL
+    assert L.li_topk(FAKE, 5, None, 1, 10, 1, FAKE, FAKE, 1 << 20, None) == li.LI_E_SHAPE
+    assert L.li_topk(FAKE, 10, None, 1, 10, 0, FAKE, FAKE, 1 << 20, None) == li.LI_E_SHAPE
+    assert L.li_topk(FAKE, 10, None, 0, 10, 1, FAKE, None, 0, None) == li.LI_OK
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(li, "_lib", None)
+    monkeypatch.setattr(li, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        li.lib()

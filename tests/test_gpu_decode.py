@@ -1,0 +1,117 @@
+"""GPU parity of li_index_decode (decode scan + top-k) against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_token_lightning_amd as li
+from sparse_attention_token_lightning_amd import inputs
+from _parity import check_scores, check_sets, check_topk_of_own_scores, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(x, k=None, with_scores=True):
+    k = x.k if k is None else k
+    sc = torch.full((max(x.n_tok, 1),), float("nan"), dtype=torch.float32, device="cuda") if with_scores else None
+    idx = li.li_index_decode(dev(x.q, "bf16"), dev(x.w), dev(x.kc, x.k_dt), dev(x.k_scale), dev(x.kv_off),
+                             int(x.lens.max(initial=0)), k, out_scores=sc)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), (sc.cpu().numpy()[:x.n_tok] if with_scores else None)
+
+
+def parity(x, exact=False, what=""):
+    print(f"[decode parity] {what} B={x.B} n_tok={x.n_tok} k_dt={x.k_dt} k={x.k}", flush=True)
+    gi, gs = run_gpu(x)
+    ri, rs, ra = oracle.index_decode(x.q, x.q_dt, x.w, x.kc, x.k_dt, x.k_scale, x.kv_off, x.H, x.D, x.k)
+    check_scores(gs, rs, ra, exact=exact, what=what)
+    if exact:
+        assert np.array_equal(gi, ri), f"{what}: indices not bit-exact"
+        return
+    lens = x.lens
+    rows = [gs[x.kv_off[b]:x.kv_off[b + 1]] for b in range(x.B)]
+    check_topk_of_own_scores(gi, rows, lens, x.k, what)
+    for b in range(x.B):
+        sl = slice(x.kv_off[b], x.kv_off[b + 1])
+        check_sets(gi[b], ri[b], rs[sl], ra[sl], int(lens[b]), what=f"{what} b={b}")
+
+
+def test_cfg1_integer_decode_is_bit_exact():
+    """Single decode query, L = 4096, integer-valued bf16: scores and indices bit-exact."""
+    parity(inputs.cfg1(), exact=True, what="cfg1")
+
+
+def test_integer_decode_ragged_bit_exact():
+    x = inputs.make_decode(101, [1, 33, 0, 4095, 2049, 97], H=64, D=128, k=2048, k_dt="bf16", dist="int")
+    parity(x, exact=True, what="int ragged")
+    x = inputs.make_decode(102, [300, 31], H=64, D=128, k=1, k_dt="bf16", dist="int")
+    parity(x, exact=True, what="int k=1")
+
+
+def test_fp8_decode_ragged_small():
+    x = inputs.make_decode(103, [5000, 0, 1, 31, 2047, 2048, 2049, 7777], k=2048)
+    parity(x, what="fp8 ragged")
+
+
+def test_bf16_float_decode_and_fewer_heads():
+    x = inputs.make_decode(104, [3000, 1234], k=256, k_dt="bf16")
+    parity(x, what="bf16 float")
+    x = inputs.make_decode(105, [2500, 900], H=40, k=300)
+    parity(x, what="fp8 H=40")
+    x = inputs.make_decode(106, [700], H=1, k=64)
+    parity(x, what="fp8 H=1")
+
+
+def test_cfg2_batched_ragged_decode():
+    """B = 32 requests, L_b ~ U{8192..32768}, fp8 keys with per-token scales."""
+    parity(inputs.cfg2(), what="cfg2")
+
+
+def test_fp8_conversion_covers_every_code():
+    """Keys holding each of the 254 finite E4M3FN codes, read through q = +e_0
+    (w = +1) and q = -e_0 (w = -1): the two scores are max(k, 0) and min(k, 0),
+    so the GPU must reproduce the exact decoded value of every code."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    n = codes.size
+    kc = np.repeat(codes[:, None], 128, axis=1)
+    kc = np.concatenate([kc, kc])
+    q = np.zeros((2, 1, 128), np.float32)
+    q[0, 0, 0], q[1, 0, 0] = 1.0, -1.0
+    x = inputs.Decode(q=inputs.encode_bf16(q), w=np.array([[1.0], [-1.0]], np.float32), kc=kc, k_scale=None,
+                      kv_off=np.array([0, n, 2 * n], np.int64), H=1, D=128, k=4)
+    _, gs = run_gpu(x)
+    dec = oracle.decode_element(codes, "fp8_e4m3")
+    assert np.array_equal(gs[:n] + gs[n:], dec)
+
+
+def test_decode_scale_doubling_and_determinism():
+    x = inputs.make_decode(107, [6000, 4100], k=512)
+    i0, s0 = run_gpu(x)
+    i1, s1 = run_gpu(x)
+    assert np.array_equal(i0, i1) and np.array_equal(s0.view(np.uint32), s1.view(np.uint32))
+    x.k_scale = x.k_scale * np.float32(2)
+    i2, s2 = run_gpu(x)
+    assert np.array_equal(s2, 2 * s0) and np.array_equal(i2, i0)
+
+
+def test_decode_without_score_output_matches():
+    x = inputs.make_decode(108, [9000, 3000], k=2048)
+    i0, _ = run_gpu(x)
+    i1, _ = run_gpu(x, with_scores=False)
+    assert np.array_equal(i0, i1)
+
+
+def test_decode_128k_sampled_requests():
+    """The decode sweep's headline point (B = 32, L = 131072, fp8) on the GPU;
+    the oracle checks two of the requests in full."""
+    x = inputs.decode_sweep(131072)
+    print(f"[decode parity] sweep L=131072 B={x.B}", flush=True)
+    gi, gs = run_gpu(x)
+    for b in (0, 31):
+        sl = slice(x.kv_off[b], x.kv_off[b + 1])
+        y = inputs.Decode(q=x.q[b:b + 1], w=x.w[b:b + 1], kc=x.kc[sl], k_scale=x.k_scale[sl],
+                          kv_off=np.array([0, 131072], np.int64), H=64, D=128, k=x.k)
+        ri, rs, ra = oracle.index_decode(y.q, y.q_dt, y.w, y.kc, y.k_dt, y.k_scale, y.kv_off, 64, 128, x.k)
+        check_scores(gs[sl], rs, ra, what=f"128K b={b}")
+        check_topk_of_own_scores(gi[b:b + 1], [gs[sl]], [131072], x.k, f"128K b={b}")
+        check_sets(gi[b], ri[0], rs, ra, 131072, what=f"128K b={b}")

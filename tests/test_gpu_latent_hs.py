@@ -1,0 +1,149 @@
+"""GPU parity of li_latent_score_group (LatentIndex) and li_hs_refine (HS)
+against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_token_lightning_amd as li
+from sparse_attention_token_lightning_amd import inputs
+from _parity import check_scores, check_sets, check_topk_of_own_scores, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_latent(x, with_scores=True):
+    sc = torch.full((x.G, max(x.n_tok, 1)), float("nan"), dtype=torch.float32, device="cuda") if with_scores else None
+    idx = li.li_latent_score_group(dev(x.q, "bf16"), dev(x.w), dev(x.w_dec, "bf16"), dev(x.latent, "bf16"),
+                                   dev(x.c_scale), dev(x.kv_off), int(np.diff(x.kv_off).max(initial=0)), x.k,
+                                   out_scores=sc)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), (sc.cpu().numpy()[:, :x.n_tok] if with_scores else None)
+
+
+def latent_parity(x, what):
+    print(f"[latent parity] {what} B={x.B} G={x.G} Dc={x.Dc} n_tok={x.n_tok}", flush=True)
+    gi, gs = run_latent(x)
+    ri, rs, ra = oracle.latent_score_group(x.q, x.q_dt, x.w, x.w_dec, x.w_dt, x.latent, x.c_dt, x.c_scale, x.kv_off,
+                                           x.G, x.H, x.Dh, x.Dc, x.k)
+    check_scores(gs, rs, ra, what=what)
+    for b in range(x.B):
+        sl = slice(x.kv_off[b], x.kv_off[b + 1])
+        n = int(x.kv_off[b + 1] - x.kv_off[b])
+        check_topk_of_own_scores(gi[b], [gs[l, sl] for l in range(x.G)], [n] * x.G, x.k, f"{what} b={b}")
+        for l in range(x.G):
+            check_sets(gi[b, l], ri[b, l], rs[l, sl], ra[l, sl], n, what=f"{what} b={b} l={l}")
+
+
+def test_latent_group_small_ragged():
+    latent_parity(inputs.make_latent(301, [3000, 0, 77, 1025], G=4, k=512), "G4 Dc256")
+
+
+def test_latent_group_dc128_g3_and_g5():
+    latent_parity(inputs.make_latent(302, [2000, 500], G=3, Dc=128, k=256), "G3 Dc128")
+    latent_parity(inputs.make_latent(303, [1500, 2100], G=5, k=300), "G5 Dc256")
+
+
+def test_latent_group_fewer_heads_and_scales():
+    x = inputs.make_latent(304, [1800, 650], G=2, H=48, k=200)
+    x.c_scale = np.random.default_rng(5).uniform(0.5, 2.0, size=x.n_tok).astype(np.float32)
+    latent_parity(x, "G2 H48 scaled")
+
+
+def test_cfg4_latent_group_sampled_requests():
+    """G = 4 layers over one shared latent [16 x 131072, 256] in one pass on the
+    GPU; the oracle checks two of the 16 requests (all four layers) in full."""
+    x = inputs.cfg4()
+    print(f"[latent parity] cfg4 n_tok={x.n_tok}", flush=True)
+    gi, gs = run_latent(x)
+    for b in (0, 15):
+        sl = slice(x.kv_off[b], x.kv_off[b + 1])
+        y = inputs.Latent(q=x.q[b:b + 1], w=x.w[b:b + 1], w_dec=x.w_dec, latent=x.latent[sl], c_scale=None,
+                          kv_off=np.array([0, 131072], np.int64), G=4, H=64, Dh=128, Dc=256, k=x.k)
+        ri, rs, ra = oracle.latent_score_group(y.q, y.q_dt, y.w, y.w_dec, y.w_dt, y.latent, y.c_dt, None, y.kv_off,
+                                               4, 64, 128, 256, x.k)
+        check_scores(gs[:, sl], rs, ra, what=f"cfg4 b={b}")
+        check_topk_of_own_scores(gi[b], [gs[l, sl] for l in range(4)], [131072] * 4, x.k, f"cfg4 b={b}")
+        for l in range(4):
+            check_sets(gi[b, l], ri[0, l], rs[l], ra[l], 131072, what=f"cfg4 b={b} l={l}")
+
+
+# ---- HS ------------------------------------------------------------------------
+
+def run_anchor(a):
+    idx = li.li_index_decode(dev(a.q, "bf16"), dev(a.w), dev(a.kc, a.k_dt), dev(a.k_scale), dev(a.kv_off),
+                             int(np.diff(a.kv_off).max(initial=0)), a.k)
+    torch.cuda.synchronize()
+    return idx
+
+
+def run_followers(cand, f, with_scores=True):
+    B, C = cand.shape
+    sc = torch.full((B, f.G, C), float("nan"), dtype=torch.float32, device="cuda") if with_scores else None
+    idx = li.li_hs_refine(cand, dev(f.q, "bf16"), dev(f.w), dev(f.w_dec, "bf16"), dev(f.latent, "bf16"),
+                          dev(f.c_scale), dev(f.kv_off), f.k, out_scores=sc)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), (sc.cpu().numpy() if with_scores else None)
+
+
+def hs_parity(h, what, requests=None):
+    a, f = h.anchor, h.followers
+    print(f"[hs parity] {what} B={a.B} C={h.C} Gf={f.G}", flush=True)
+    cand_t = run_anchor(a)
+    cand = cand_t.cpu().numpy()
+    gi, gs = run_followers(cand_t, f)
+    requests = range(a.B) if requests is None else requests
+    for b in requests:
+        sl = slice(a.kv_off[b], a.kv_off[b + 1])
+        n = int(a.kv_off[b + 1] - a.kv_off[b])
+        one = np.array([0, n], np.int64)
+        # (i) the anchor: its own top-C against the oracle's
+        ai, as_, aa = oracle.index_decode(a.q[b:b + 1], a.q_dt, a.w[b:b + 1], a.kc[sl], a.k_dt, a.k_scale[sl], one,
+                                          a.H, a.D, h.C)
+        check_sets(cand[b], ai[0], as_, aa, n, what=f"{what} anchor b={b}")
+        # (ii) followers fed the GPU's candidates: scores, own-score top-k, sets
+        ri, rs, ra = oracle.hs_refine(cand[b:b + 1], f.q[b:b + 1], f.q_dt, f.w[b:b + 1], f.w_dec, f.w_dt,
+                                      f.latent[sl], f.c_dt, None if f.c_scale is None else f.c_scale[sl], one,
+                                      f.G, f.H, f.Dh, f.Dc, f.k)
+        nv = int((cand[b] >= 0).sum())
+        check_scores(gs[b, :, :nv], rs[0, :, :nv], ra[0, :, :nv], what=f"{what} b={b}")
+        for fl in range(f.G):
+            slot = oracle.topk(gs[b, fl, :nv].astype(np.float64)[None, :], [nv], f.k)[0]
+            want = np.where(slot >= 0, cand[b][np.maximum(slot, 0)], -1)
+            assert np.array_equal(gi[b, fl], want), f"{what} b={b} f={fl}: selection != top-k of own scores"
+            # positions -> compare with the oracle's selection in slot space
+            pos_s = np.full(n, np.nan)
+            pos_a = np.full(n, np.nan)
+            pos_s[cand[b][:nv]] = rs[0, fl, :nv]
+            pos_a[cand[b][:nv]] = ra[0, fl, :nv]
+            g = gi[b, fl]
+            r = ri[0, fl]
+            gv, rv = g[g >= 0], r[r >= 0]
+            assert len(gv) == len(rv) == min(nv, f.k)
+            assert np.isin(gv, cand[b][:nv]).all(), "followers must choose from the candidate set"
+            diff = np.setxor1d(gv, rv)
+            if diff.size:
+                th = rv[np.argmin(pos_s[rv])]
+                ok = np.abs(pos_s[diff] - pos_s[th]) <= 2e-3 * (pos_a[diff] + pos_a[th])
+                assert ok.all(), f"{what} b={b} f={fl}: set differences beyond tolerance"
+
+
+def test_hs_small():
+    hs_parity(inputs.make_hs(401, [9000, 3000, 500, 0], C=4096, Gf=3, k=1024), "small")
+
+
+def test_hs_candidates_equal_k_and_two_followers():
+    h = inputs.make_hs(402, [5000, 2000], C=1024, Gf=2, k=1024)
+    hs_parity(h, "C=k")
+    cand = run_anchor(h.anchor)
+    gi, _ = run_followers(cand, h.followers, with_scores=False)
+    c = cand.cpu().numpy()
+    for b in range(2):
+        for fl in range(2):
+            assert np.array_equal(gi[b, fl], c[b])
+
+
+def test_cfg5_hs_sampled_requests():
+    """Anchor top-8192 over 16 x 131072 fp8 keys, three latent followers
+    rescoring 8192 candidates each; the oracle checks two requests in full."""
+    hs_parity(inputs.cfg5(), "cfg5", requests=(0, 15))

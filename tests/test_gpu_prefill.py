@@ -1,0 +1,85 @@
+"""GPU parity of li_index_prefill (causal fp8 scan + top-k) against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_token_lightning_amd as li
+from sparse_attention_token_lightning_amd import inputs
+from _parity import check_scores, check_sets, check_topk_of_own_scores, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(x, with_scores=True):
+    sc = torch.full((x.T, x.L), float("nan"), dtype=torch.float32, device="cuda") if with_scores else None
+    idx = li.li_index_prefill(dev(x.q, "fp8_e4m3"), dev(x.q_scale), dev(x.w), dev(x.kc, "fp8_e4m3"),
+                              dev(x.k_scale), x.qpos0, x.k, out_scores=sc)
+    torch.cuda.synchronize()
+    return idx, sc
+
+
+def parity_rows(x, gi, gs, rows, what):
+    for t in rows:
+        vis = x.qpos0 + t + 1
+        ri, rs, ra = oracle.index_prefill(x.q[t:t + 1], x.q_dt, x.q_scale[t:t + 1], x.w[t:t + 1], x.kc, x.k_dt,
+                                          x.k_scale, 1, x.L, x.qpos0 + t, x.H, x.D, x.k)
+        g = gs[t]
+        assert np.isneginf(g[vis:]).all(), f"{what} t={t}: masked positions must be -inf"
+        check_scores(g[:vis], rs[0, :vis], ra[0, :vis], what=f"{what} t={t}")
+        check_topk_of_own_scores(gi[t:t + 1], [g], [vis], x.k, f"{what} t={t}")
+        check_sets(gi[t], ri[0], rs[0], ra[0], vis, what=f"{what} t={t}")
+        assert gi[t].max() <= x.qpos0 + t
+
+
+def test_prefill_small_all_rows():
+    x = inputs.make_prefill(201, T=37, L=1000, k=300)
+    print(f"[prefill parity] T={x.T} L={x.L} qpos0={x.qpos0}", flush=True)
+    gi, gs = run_gpu(x)
+    parity_rows(x, gi.cpu().numpy(), gs.cpu().numpy(), range(x.T), "small")
+
+
+def test_prefill_rows_shorter_than_k():
+    x = inputs.make_prefill(202, T=9, L=70, k=64)
+    gi, gs = run_gpu(x)
+    gi, gs = gi.cpu().numpy(), gs.cpu().numpy()
+    parity_rows(x, gi, gs, range(x.T), "short")
+    assert gi[0].tolist() == list(range(62)) + [-1, -1]
+
+
+def test_prefill_chunk_not_at_the_end_and_few_heads():
+    x = inputs.make_prefill(203, T=20, L=600, H=24, k=128, qpos0=300)
+    gi, gs = run_gpu(x)
+    parity_rows(x, gi.cpu().numpy(), gs.cpu().numpy(), range(x.T), "mid-chunk H=24")
+
+
+def test_prefill_without_score_output_matches():
+    x = inputs.make_prefill(204, T=16, L=3000, k=2048)
+    i0, _ = run_gpu(x)
+    i1, _ = run_gpu(x, with_scores=False)
+    assert torch.equal(i0, i1)
+
+
+def test_cfg3_prefill_sampled_rows():
+    """T = 4096 new tokens against a causal L = 65536 cache on the GPU; the
+    oracle checks sampled rows in full (first, last, around powers of two)."""
+    x = inputs.cfg3()
+    print(f"[prefill parity] cfg3 T={x.T} L={x.L}", flush=True)
+    gi, gs = run_gpu(x)
+    rows = [0, 1, 2047, 4094, 4095, 1234]
+    sel = torch.tensor(rows, device="cuda")
+    gi_np = gi.cpu().numpy()
+    gsub = gs.index_select(0, sel).cpu().numpy()
+    for j, t in enumerate(rows):
+        vis = x.qpos0 + t + 1
+        ri, rs, ra = oracle.index_prefill(x.q[t:t + 1], x.q_dt, x.q_scale[t:t + 1], x.w[t:t + 1], x.kc, x.k_dt,
+                                          x.k_scale, 1, x.L, x.qpos0 + t, x.H, x.D, x.k)
+        g = gsub[j]
+        assert np.isneginf(g[vis:]).all()
+        check_scores(g[:vis], rs[0, :vis], ra[0, :vis], what=f"cfg3 t={t}")
+        check_topk_of_own_scores(gi_np[t:t + 1], [g], [vis], x.k, f"cfg3 t={t}")
+        check_sets(gi_np[t], ri[0], rs[0], ra[0], vis, what=f"cfg3 t={t}")
+    # every row: sizes, order, causal bound
+    assert (gi_np >= 0).all()
+    assert np.all(np.diff(gi_np, axis=1) > 0)
+    assert np.all(gi_np.max(axis=1) <= x.qpos0 + np.arange(x.T))
