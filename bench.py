@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Benchmark of the lightning-indexer hot path on one MI355X.
+
+One step = one decode step of the indexer for the headline workload: B = 32
+requests, each with a 131072-token fp8 (E4M3FN) key cache plus fp32 per-token
+scales, 64 heads x 128 dims, bf16 queries: the scan over every cached key and
+the top-2048 selection per request (li_index_decode).  `value` is keys scored
+per second over the K timed steps (inputs resident in HBM before timing).
+
+The same run also reports, under "components": per-kernel times of that step
+from HIP events recorded on the library's stream, the prefill chunk
+(T = 4096 against a causal 65536-token cache: TFLOP/s), the LatentIndex group
+(G = 4 over a [16 x 131072, 256] bf16 latent: GB/s and MFMA share), the HS
+decode (anchor top-8192 + three followers) against four native decodes, and
+the ragged batched decode (B = 32, L ~ U{8K..32K}); and under "cpu_baseline"
+the CPU oracle timed on a sample of the headline workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0    # dense fp8 MFMA
+BF16_PEAK_TFLOPS = 2500.0   # dense bf16 / fp16 MFMA
+FP8_KEY_BYTES = 128 + 4     # one fp8 key row + its fp32 scale
+METRIC = "decode indexer keys scored/s + HBM GB/s at 128K; prefill TFLOP/s; top-2048 µs"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Trace:
+    """Per-call HIP events recorded by the library around its kernels."""
+
+    def __init__(self, torch, li, per_call, calls):
+        self.torch, self.li, self.per = torch, li, per_call
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(per_call * calls)]
+        for e in self.ev:
+            e.record()
+        torch.cuda.synchronize()
+        self.handles = (ctypes.c_void_p * len(self.ev))(*[e.cuda_event for e in self.ev])
+
+    def arm(self, i):
+        addr = ctypes.addressof(self.handles) + i * self.per * ctypes.sizeof(ctypes.c_void_p)
+        self.li.li_trace_events(ctypes.c_void_p(addr), self.per)
+
+    def off(self):
+        self.li.li_trace_events(None, 0)
+
+    def spans(self, i):
+        """Milliseconds between consecutive events of call i."""
+        e = self.ev[i * self.per:(i + 1) * self.per]
+        return [e[j].elapsed_time(e[j + 1]) for j in range(self.per - 1)]
+
+
+def timed(torch, li, fn, per_call, iters, warmup, check_count=True):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    tr = Trace(torch, li, per_call, iters)
+    t0 = time.perf_counter()
+    for i in range(iters):
+        tr.arm(i)
+        fn()
+        if check_count and li.li_trace_count() != per_call:
+            raise RuntimeError(f"expected {per_call} trace events, got {li.li_trace_count()}")
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / iters * 1e3
+    tr.off()
+    spans = [tr.spans(i) for i in range(iters)]
+    mean = [sum(s[j] for s in spans) / iters for j in range(per_call - 1)]
+    return wall, mean
+
+
+def dev(torch, a, dt=None):
+    import numpy as np
+    if a is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dt == "bf16":
+        t = t.view(torch.int16).view(torch.bfloat16)
+    elif dt == "fp8_e4m3":
+        t = t.view(torch.float8_e4m3fn)
+    return t.cuda()
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "sparse_attention_token_lightning_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, src_hash, launches_keys):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they
+    were taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p)).get(kernel)
+    except (ValueError, OSError):
+        return None
+    if not d or d.get("source_hash") != src_hash:
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(x, sample):
+    """The CPU oracle on the first `sample` requests of the headline workload."""
+    import numpy as np
+    import oracle
+
+    b = min(sample, x.B)
+    off = x.kv_off[:b + 1].copy()
+    n = int(off[-1])
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    oracle.index_decode(x.q[:b], x.q_dt, x.w[:b], x.kc[:n], x.k_dt, x.k_scale[:n], off, x.H, x.D, x.k,
+                        want_scores=False)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "keys/s", "cores": min(threads, b), "kind": "oracle",
+            "sample": f"{b} of {x.B} requests x {int(x.kv_off[1] - x.kv_off[0])} keys "
+                      f"(scan + top-{x.k}, fp64, OpenMP over requests), {dt:.1f} s"}
+
+
+def components(torch, li, inputs, args):
+    import numpy as np
+    out = {}
+    # ---- prefill chunk: T = 4096 against a causal L = 65536 cache (fp8) --------
+    x = inputs.cfg3()
+    q, qs, w, kc, ks = dev(torch, x.q, "fp8_e4m3"), dev(torch, x.q_scale), dev(torch, x.w), \
+        dev(torch, x.kc, "fp8_e4m3"), dev(torch, x.k_scale)
+    idx = torch.empty((x.T, x.k), dtype=torch.int32, device="cuda")
+    ws = torch.empty(li.lib().li_index_prefill_ws(x.T, x.L, x.k, 0), dtype=torch.uint8, device="cuda")
+    fn = lambda: li.li_index_prefill(q, qs, w, kc, ks, x.qpos0, x.k, out_idx=idx, ws=ws)
+    wall, (scan, topk) = timed(torch, li, fn, 3, args.comp_iters, 2)
+    pairs = sum(x.qpos0 + t + 1 for t in range(x.T))
+    flop = 2.0 * x.H * x.D * pairs
+    out["prefill_fp8_T4096_L65536"] = {
+        "scan_ms": scan, "topk_ms": topk, "total_ms": wall, "visible_pairs": pairs,
+        "tflops": flop / (scan * 1e-3) / 1e12, "mfma_frac_fp8": flop / (scan * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
+        "topk_us_per_row": topk * 1e3 / x.T}
+    del q, qs, w, kc, ks, idx, ws, x
+    # ---- LatentIndex group: G = 4, B = 16, L = 131072, Dc = 256 (bf16) ----------
+    x = inputs.cfg4()
+    q, w, wd, lat, off = dev(torch, x.q, "bf16"), dev(torch, x.w), dev(torch, x.w_dec, "bf16"), \
+        dev(torch, x.latent, "bf16"), dev(torch, x.kv_off)
+    idx = torch.empty((x.B, x.G, x.k), dtype=torch.int32, device="cuda")
+    ws = torch.empty(li.lib().li_latent_score_group_ws(x.B, x.n_tok, x.G, x.H, x.Dc, x.k, 0), dtype=torch.uint8,
+                     device="cuda")
+    fn = lambda: li.li_latent_score_group(q, w, wd, lat, None, off, 131072, x.k, out_idx=idx, ws=ws)
+    wall, (absorb, scan, topk) = timed(torch, li, fn, 4, args.comp_iters, 2)
+    lat_bytes = x.n_tok * x.Dc * 2
+    flop = 2.0 * x.G * x.H * x.Dc * x.n_tok
+    out["latent_G4_B16_L131072"] = {
+        "absorb_ms": absorb, "scan_ms": scan, "topk_ms": topk, "total_ms": wall,
+        "scan_gbs": lat_bytes / (scan * 1e-3) / 1e9, "scan_hbm_frac": lat_bytes / (scan * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "scan_mfma_frac_fp16": flop / (scan * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+    del q, w, wd, lat, off, idx, ws, x
+    # ---- HS decode: fp8 anchor top-8192 + 3 latent followers, B = 16, L = 131072 --
+    h = inputs.cfg5()
+    a, f = h.anchor, h.followers
+    aq, aw, akc, aks, off = dev(torch, a.q, "bf16"), dev(torch, a.w), dev(torch, a.kc, "fp8_e4m3"), \
+        dev(torch, a.k_scale), dev(torch, a.kv_off)
+    fq, fw, fwd, lat = dev(torch, f.q, "bf16"), dev(torch, f.w), dev(torch, f.w_dec, "bf16"), \
+        dev(torch, f.latent, "bf16")
+    cand = torch.empty((a.B, h.C), dtype=torch.int32, device="cuda")
+    fidx = torch.empty((a.B, f.G, f.k), dtype=torch.int32, device="cuda")
+    nidx = torch.empty((a.B, 2048), dtype=torch.int32, device="cuda")
+    L = li.lib()
+    ws_a = torch.empty(L.li_index_decode_ws(a.B, a.n_tok, 131072, h.C, 0), dtype=torch.uint8, device="cuda")
+    ws_f = torch.empty(L.li_hs_refine_ws(a.B, h.C, f.G, f.H, f.Dc, f.k, 0), dtype=torch.uint8, device="cuda")
+    fa = lambda: li.li_index_decode(aq, aw, akc, aks, off, 131072, h.C, out_idx=cand, ws=ws_a)
+    ff = lambda: li.li_hs_refine(cand, fq, fw, fwd, lat, None, off, f.k, out_idx=fidx, ws=ws_f)
+    fn_native = lambda: li.li_index_decode(aq, aw, akc, aks, off, 131072, 2048, out_idx=nidx, ws=ws_a)
+    _, (a_scan, a_topk) = timed(torch, li, fa, 3, args.comp_iters, 2)
+    _, (f_abs, f_scan, f_topk) = timed(torch, li, ff, 4, args.comp_iters, 2)
+    _, (n_scan, n_topk) = timed(torch, li, fn_native, 3, args.comp_iters, 2)
+    hs_ms = a_scan + a_topk + f_abs + f_scan + f_topk
+    native = n_scan + n_topk
+    out["hs_B16_L131072_C8192_F3"] = {
+        "anchor_scan_ms": a_scan, "anchor_top8192_ms": a_topk, "follower_absorb_ms": f_abs,
+        "follower_gather_scan_ms": f_scan, "follower_top2048_ms": f_topk, "hs_total_ms": hs_ms,
+        "native_decode_ms": native, "four_native_layers_over_hs": 4 * native / hs_ms}
+    del aq, aw, akc, aks, off, fq, fw, fwd, lat, cand, fidx, nidx, ws_a, ws_f, h, a, f
+    # ---- ragged batched decode: B = 32, L_b ~ U{8192..32768} (fp8) --------------
+    x = inputs.cfg2()
+    q, w, kc, ks, off = dev(torch, x.q, "bf16"), dev(torch, x.w), dev(torch, x.kc, "fp8_e4m3"), \
+        dev(torch, x.k_scale), dev(torch, x.kv_off)
+    idx = torch.empty((x.B, x.k), dtype=torch.int32, device="cuda")
+    ws = torch.empty(L.li_index_decode_ws(x.B, x.n_tok, int(x.lens.max()), x.k, 0), dtype=torch.uint8, device="cuda")
+    fn = lambda: li.li_index_decode(q, w, kc, ks, off, int(x.lens.max()), x.k, out_idx=idx, ws=ws)
+    wall, (scan, topk) = timed(torch, li, fn, 3, args.comp_iters, 2)
+    out["decode_fp8_B32_ragged8K-32K"] = {
+        "scan_ms": scan, "topk_ms": topk, "total_ms": wall, "keys": x.n_tok,
+        "scan_gbs_algorithmic": x.n_tok * FP8_KEY_BYTES / (scan * 1e-3) / 1e9,
+        "note": "86.5 MB of keys fit in the 256 MB MALL; not an HBM figure"}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--comp-iters", type=int, default=5, help="timed iterations per component")
+    ap.add_argument("--no-components", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=32, help="requests in the oracle's timed sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM counter scaling)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}, WORLD_SIZE {world}): the indexer "
+              f"path here is single-GPU; sharding across GPUs is a design note, not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_attention_token_lightning_amd as li
+    from sparse_attention_token_lightning_amd import inputs
+
+    torch.cuda.set_device(0)
+    log("[bench] generating decode B=32 L=131072 fp8 inputs")
+    x = inputs.decode_sweep(131072)
+    B, Lk = x.B, 131072
+    q, w, kc, ks, off = dev(torch, x.q, "bf16"), dev(torch, x.w), dev(torch, x.kc, "fp8_e4m3"), \
+        dev(torch, x.k_scale), dev(torch, x.kv_off)
+    idx = torch.empty((B, x.k), dtype=torch.int32, device="cuda")
+    ws = torch.empty(li.lib().li_index_decode_ws(B, x.n_tok, Lk, x.k, 0), dtype=torch.uint8, device="cuda")
+    step = lambda: li.li_index_decode(q, w, kc, ks, off, Lk, x.k, out_idx=idx, ws=ws)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    log(f"[bench] warmup {args.warmup}, timing {args.steps} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    tr = Trace(torch, li, 3, args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        tr.arm(i)
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    tr.off()
+    ms_per_step = elapsed / args.steps * 1e3
+    spans = [tr.spans(i) for i in range(args.steps)]
+    scan_ms = sum(s[0] for s in spans) / args.steps
+    topk_ms = sum(s[1] for s in spans) / args.steps
+    keys = B * Lk
+    achieved = keys * FP8_KEY_BYTES / (scan_ms * 1e-3) / 1e9
+    traffic = load_traffic("decode_score", source_hash("decode.hip", "li_device.h"), keys)
+    log(f"[bench] step {ms_per_step:.3f} ms, scan {scan_ms * 1e3:.1f} us ({achieved:.0f} GB/s), "
+        f"top-2048 {topk_ms * 1e3:.1f} us")
+
+    result = {
+        "metric": METRIC,
+        "value": keys / (ms_per_step * 1e-3),
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_fp8_B32_L131072", "B": B, "L": Lk, "H": x.H, "D": x.D, "k": x.k,
+                   "k_cache": "fp8_e4m3 + fp32 per-token scale", "q": "bf16", "mfma": "bf16 x bf16 -> fp32",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "decode_score", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": keys * FP8_KEY_BYTES, "avg_launch_ms": scan_ms},
+        "components": {"decode_fp8_B32_L131072": {"scan_ms": scan_ms, "top2048_ms": topk_ms,
+                                                  "top2048_us": topk_ms * 1e3,
+                                                  "scan_gbs": achieved}},
+    }
+    if not args.no_components:
+        log("[bench] components: prefill, latent, HS, ragged decode")
+        del ws
+        result["components"].update(components(torch, li, inputs, args))
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle on {args.cpu_sample} requests")
+        result["cpu_baseline"] = cpu_baseline(x, args.cpu_sample)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

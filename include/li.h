@@ -200,6 +200,17 @@ li_status li_topk(const float* scores, int64_t row_stride, const int32_t* row_le
                   int32_t n, int32_t k, int32_t* out_idx, void* ws, size_t ws_bytes, void* stream);
 size_t li_topk_ws(int32_t rows, int32_t n, int32_t k);
 
+/* ---------------------------------------------------------------------------
+ * Measurement hook (not part of the computation): after li_trace_events(ev, n)
+ * with n > 0, every entry point called on this thread records ev[0] on its
+ * stream before its first kernel and ev[i] after its i-th kernel launch, as
+ * long as slots remain; li_trace_count() returns how many events the last
+ * call recorded.  `events` are caller-created hipEvent_t handles that must
+ * outlive their use.  li_trace_events(NULL, 0) switches the hook off.
+ * ------------------------------------------------------------------------- */
+void li_trace_events(void** events, int32_t capacity);
+int32_t li_trace_count(void);
+
 /* Human-readable name of a status code (static storage). */
 const char* li_status_str(li_status s);
 /* Detail of the last error on this thread (e.g. the HIP error text); "" if none. */

@@ -25,7 +25,7 @@ LI_MAX_K = 16384
 # Every symbol include/li.h declares.
 SYMBOLS = ("li_index_decode", "li_index_decode_ws", "li_index_prefill", "li_index_prefill_ws",
            "li_latent_score_group", "li_latent_score_group_ws", "li_hs_refine", "li_hs_refine_ws",
-           "li_topk", "li_topk_ws", "li_status_str", "li_last_error")
+           "li_topk", "li_topk_ws", "li_status_str", "li_last_error", "li_trace_events", "li_trace_count")
 
 _lib = None
 
@@ -65,6 +65,10 @@ def lib():
         L.li_status_str.restype = C.c_char_p
         L.li_last_error.argtypes = []
         L.li_last_error.restype = C.c_char_p
+        L.li_trace_events.argtypes = [vp, i32]
+        L.li_trace_events.restype = None
+        L.li_trace_count.argtypes = []
+        L.li_trace_count.restype = i32
         _lib = L
     return _lib
 
@@ -191,3 +195,12 @@ def li_topk(scores, k, row_len=None, n=None, out_idx=None, ws=None, stream=None)
     _check(L.li_topk(_ptr(scores), stride, _ptr(row_len), rows, n, k, _ptr(out_idx), _ptr(wst), wsb,
                      _stream(stream)))
     return out_idx
+
+
+def li_trace_events(events, capacity):
+    """Switch the measurement hook on (a ctypes array of hipEvent_t) or off (None, 0)."""
+    lib().li_trace_events(events, capacity)
+
+
+def li_trace_count():
+    return lib().li_trace_count()

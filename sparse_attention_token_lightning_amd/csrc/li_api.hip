@@ -14,6 +14,23 @@ namespace {
 
 thread_local std::string g_err;
 
+// Opt-in measurement trace (li_trace_events): caller-created hipEvents that the
+// entry points record around their kernels.
+thread_local hipEvent_t* g_trace = nullptr;
+thread_local int32_t g_trace_cap = 0;
+thread_local int32_t g_trace_n = 0;
+
+void trace_begin(hipStream_t s) {
+  g_trace_n = 0;
+  if (g_trace && g_trace_cap > 0 && hipEventRecord(g_trace[0], s) == hipSuccess) g_trace_n = 1;
+}
+
+void trace_mark(hipStream_t s) {
+  if (g_trace && g_trace_n > 0 && g_trace_n < g_trace_cap &&
+      hipEventRecord(g_trace[g_trace_n], s) == hipSuccess)
+    ++g_trace_n;
+}
+
 li_status fail(li_status s, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -24,8 +41,11 @@ li_status fail(li_status s, const char* fmt, ...) {
   return s;
 }
 
-li_status hip_check(hipError_t e, const char* what) {
-  if (e == hipSuccess) return LI_OK;
+li_status hip_check(hipError_t e, const char* what, hipStream_t s) {
+  if (e == hipSuccess) {
+    trace_mark(s);
+    return LI_OK;
+  }
   return fail(LI_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
@@ -115,6 +135,14 @@ const char* li_status_str(li_status s) {
 
 const char* li_last_error(void) { return g_err.c_str(); }
 
+void li_trace_events(void** events, int32_t capacity) {
+  g_trace = capacity > 0 ? (hipEvent_t*)events : nullptr;
+  g_trace_cap = (events && capacity > 0) ? capacity : 0;
+  g_trace_n = 0;
+}
+
+int32_t li_trace_count(void) { return g_trace_n; }
+
 size_t li_index_decode_ws(int32_t B, int64_t n_tok, int32_t max_len, int32_t k,
                           int32_t has_out_scores) {
   (void)max_len;
@@ -141,11 +169,12 @@ li_status li_index_decode(const void* q, li_dtype q_dt, const float* w, const vo
   if ((st = check_ws(ws, ws_bytes, decode_ws(B, n_tok, out_scores != nullptr)))) return st;
   if (B == 0) return LI_OK;
   hipStream_t s = (hipStream_t)stream;
+  trace_begin(s);
   Carver cv(ws);
   float* scores = out_scores ? out_scores : (float*)cv.take((size_t)n_tok * 4);
   if ((st = hip_check(li::launch_decode_score((const uint16_t*)q, w, k_cache, k_dt == LI_FP8_E4M3,
                                               k_scale, kv_off, B, n_tok, max_len, H, scores, s),
-                      "decode_score launch")))
+                      "decode_score launch", s)))
     return st;
   li::TopkRows tr = {};
   tr.scores = scores;
@@ -156,7 +185,7 @@ li_status li_index_decode(const void* q, li_dtype q_dt, const float* w, const vo
   tr.G = 1;
   tr.k = k;
   tr.out = out_idx;
-  return hip_check(li::launch_topk(tr, s), "topk launch");
+  return hip_check(li::launch_topk(tr, s), "topk launch", s);
 }
 
 size_t li_index_prefill_ws(int32_t T, int32_t L, int32_t k, int32_t has_out_scores) {
@@ -182,12 +211,13 @@ li_status li_index_prefill(const void* q, li_dtype q_dt, const float* q_scale, c
   if ((st = check_ws(ws, ws_bytes, prefill_ws(T, L, out_scores != nullptr)))) return st;
   if (T == 0) return LI_OK;
   hipStream_t s = (hipStream_t)stream;
+  trace_begin(s);
   Carver cv(ws);
   float* scores = out_scores ? out_scores : (float*)cv.take((size_t)T * (size_t)L * 4);
   if ((st = hip_check(li::launch_prefill_score((const uint8_t*)q, q_scale, w, (const uint8_t*)k_cache,
                                                k_scale, T, L, qpos0, H, out_scores != nullptr,
                                                scores, s),
-                      "prefill_score launch")))
+                      "prefill_score launch", s)))
     return st;
   li::TopkRows tr = {};
   tr.scores = scores;
@@ -198,7 +228,7 @@ li_status li_index_prefill(const void* q, li_dtype q_dt, const float* q_scale, c
   tr.qpos0 = qpos0;
   tr.k = k;
   tr.out = out_idx;
-  return hip_check(li::launch_topk(tr, s), "topk launch");
+  return hip_check(li::launch_topk(tr, s), "topk launch", s);
 }
 
 static li_status check_latent_common(li_dtype q_dt, li_dtype w_dt, li_dtype c_dt, int32_t H,
@@ -236,17 +266,18 @@ li_status li_latent_score_group(const void* q, li_dtype q_dt, const float* w, co
   if ((st = check_ws(ws, ws_bytes, latent_ws(B, n_tok, G, H, Dc, out_scores != nullptr)))) return st;
   if (B == 0) return LI_OK;
   hipStream_t s = (hipStream_t)stream;
+  trace_begin(s);
   Carver cv(ws);
   uint16_t* qt16 = (uint16_t*)cv.take((size_t)B * G * H * Dc * 2);
   float* wsc = (float*)cv.take((size_t)B * G * H * 4);
   float* scores = out_scores ? out_scores : (float*)cv.take((size_t)G * (size_t)n_tok * 4);
   if ((st = hip_check(li::launch_latent_absorb((const uint16_t*)q, w, (const uint16_t*)w_dec, B, G,
                                                H, Dh, Dc, qt16, wsc, s),
-                      "latent_absorb launch")))
+                      "latent_absorb launch", s)))
     return st;
   if ((st = hip_check(li::launch_latent_score(qt16, wsc, (const uint16_t*)latent, c_scale, kv_off, B,
                                               n_tok, max_len, G, H, Dc, scores, s),
-                      "latent_score launch")))
+                      "latent_score launch", s)))
     return st;
   li::TopkRows tr = {};
   tr.scores = scores;
@@ -257,7 +288,7 @@ li_status li_latent_score_group(const void* q, li_dtype q_dt, const float* w, co
   tr.G = G;
   tr.k = k;
   tr.out = out_idx;
-  return hip_check(li::launch_topk(tr, s), "topk launch");
+  return hip_check(li::launch_topk(tr, s), "topk launch", s);
 }
 
 size_t li_hs_refine_ws(int32_t B, int32_t C, int32_t Gf, int32_t H, int32_t Dc, int32_t k,
@@ -283,17 +314,18 @@ li_status li_hs_refine(const int32_t* cand_idx, int32_t C, const void* q, li_dty
   if ((st = check_ws(ws, ws_bytes, hs_ws(B, C, Gf, H, Dc, out_scores != nullptr)))) return st;
   if (B == 0) return LI_OK;
   hipStream_t s = (hipStream_t)stream;
+  trace_begin(s);
   Carver cv(ws);
   uint16_t* qt16 = (uint16_t*)cv.take((size_t)B * Gf * H * Dc * 2);
   float* wsc = (float*)cv.take((size_t)B * Gf * H * 4);
   float* scores = out_scores ? out_scores : (float*)cv.take((size_t)B * Gf * (size_t)C * 4);
   if ((st = hip_check(li::launch_latent_absorb((const uint16_t*)q, w, (const uint16_t*)w_dec, B, Gf,
                                                H, Dh, Dc, qt16, wsc, s),
-                      "latent_absorb launch")))
+                      "latent_absorb launch", s)))
     return st;
   if ((st = hip_check(li::launch_hs_score(qt16, wsc, (const uint16_t*)latent, c_scale, kv_off,
                                           cand_idx, C, B, Gf, H, Dc, scores, s),
-                      "hs_score launch")))
+                      "hs_score launch", s)))
     return st;
   li::TopkRows tr = {};
   tr.scores = scores;
@@ -304,7 +336,7 @@ li_status li_hs_refine(const int32_t* cand_idx, int32_t C, const void* q, li_dty
   tr.G = Gf;
   tr.k = k;
   tr.out = out_idx;
-  return hip_check(li::launch_topk(tr, s), "topk launch");
+  return hip_check(li::launch_topk(tr, s), "topk launch", s);
 }
 
 size_t li_topk_ws(int32_t rows, int32_t n, int32_t k) {
@@ -332,7 +364,9 @@ li_status li_topk(const float* scores, int64_t row_stride, const int32_t* row_le
   tr.n = n;
   tr.k = k;
   tr.out = out_idx;
-  return hip_check(li::launch_topk(tr, (hipStream_t)stream), "topk launch");
+  hipStream_t s = (hipStream_t)stream;
+  trace_begin(s);
+  return hip_check(li::launch_topk(tr, s), "topk launch", s);
 }
 
 }  // extern "C"
