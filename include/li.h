@@ -156,8 +156,8 @@ li_status li_latent_score_group(const void* q, li_dtype q_dt, const float* w, co
                                 int64_t n_tok, int32_t max_len, int32_t G, int32_t H, int32_t Dh,
                                 int32_t Dc, int32_t k, int32_t* out_idx, float* out_scores,
                                 uint32_t flags, void* ws, size_t ws_bytes, void* stream);
-size_t li_latent_score_group_ws(int32_t B, int64_t n_tok, int32_t G, int32_t H, int32_t Dc,
-                                int32_t k, int32_t has_out_scores);
+size_t li_latent_score_group_ws(int32_t B, int64_t n_tok, int32_t max_len, int32_t G, int32_t H,
+                                int32_t Dc, int32_t k, int32_t has_out_scores);
 
 /* ---------------------------------------------------------------------------
  * li_hs_refine — HS followers rescore only the anchor's candidate set.

@@ -50,7 +50,7 @@ def lib():
         L.li_index_prefill_ws.argtypes = [i32, i32, i32, i32]
         L.li_latent_score_group.argtypes = [vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, i64, i32, i32, i32, i32, i32,
                                             i32, vp, vp, u32, vp, sz, vp]
-        L.li_latent_score_group_ws.argtypes = [i32, i64, i32, i32, i32, i32, i32]
+        L.li_latent_score_group_ws.argtypes = [i32, i64, i32, i32, i32, i32, i32, i32]
         L.li_hs_refine.argtypes = [vp, i32, vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, vp,
                                    vp, u32, vp, sz, vp]
         L.li_hs_refine_ws.argtypes = [i32, i32, i32, i32, i32, i32, i32]
@@ -156,7 +156,7 @@ def li_latent_score_group(q, w, w_dec, latent, c_scale, kv_off, max_len, k, out_
     if out_idx is None:
         out_idx = torch.empty((B, G, k), dtype=torch.int32, device=q.device)
     L = lib()
-    need = L.li_latent_score_group_ws(B, n_tok, G, H, Dc, k, int(out_scores is not None))
+    need = L.li_latent_score_group_ws(B, n_tok, max_len, G, H, Dc, k, int(out_scores is not None))
     wst, wsb = _workspace(need, q.device, ws)
     _check(L.li_latent_score_group(_ptr(q), _dt(q), _ptr(w), _ptr(w_dec), _dt(w_dec), _ptr(latent), _dt(latent),
                                    _ptr(c_scale), _ptr(kv_off), B, n_tok, max_len, G, H, Dh, Dc, k, _ptr(out_idx),

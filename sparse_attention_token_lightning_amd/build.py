@@ -22,6 +22,9 @@ def sources():
 def build(verbose: bool = False, extra=None) -> str:
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # MFMA accumulators in ordinary VGPRs: the epilogues read them with
+           # VALU ops, which would otherwise need a copy out of AGPRs each time.
+           "-mllvm", "-amdgpu-mfma-vgpr-form",
            "-Wno-unused-command-line-argument", "-I", os.path.join(HERE, "..", "include"),
            "-o", LIB + ".tmp"] + sources() + list(extra or [])
     if verbose:

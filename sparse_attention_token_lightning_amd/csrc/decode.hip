@@ -20,30 +20,48 @@
 // lane 16 heads of its key per block: ReLU, the head weight and the sum over
 // the lane's 32 heads happen in registers, and one cross-half shuffle finishes
 // the 64-head sum.
+//
+// Latency hiding: each wave keeps 3 (fp8) or 2 (bf16) key tiles in flight in
+// registers while it computes a fourth (a ring indexed at compile time, so no
+// register copies force early waits), together with their per-token scales.
+//
+// The selection's first radix level is fused in: every score also lands in a
+// per-workgroup LDS histogram of its top 11 key bits, stored as that
+// workgroup's partial of the request's histogram (plain stores: dozens of
+// workgroups adding into the same hot bins with atomics serialise badly).
 #include "li_device.h"
 #include "li_internal.h"
+#include "li_select.h"
 
 namespace li {
 namespace {
 
-constexpr int kDecWaves = 4;       // waves per workgroup
-constexpr int kTile = 32;          // keys per MFMA tile
+constexpr int kDecWaves = 4;  // waves per workgroup
+constexpr int kTile = 32;     // keys per MFMA tile
+constexpr int kStagesFp8 = 4;   // key-tile buffers per wave (fp8 keys)
+constexpr int kStagesBf16 = 3;  // (bf16 keys: twice the registers per tile)
 
 template <bool FP8>
 __global__ __launch_bounds__(256) void decode_score_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ kc,
     const float* __restrict__ k_scale, const int64_t* __restrict__ kv_off, int H,
-    int tiles_per_wave, float* __restrict__ scores) {
-  constexpr int NV = FP8 ? 4 : 8;              // 16-byte vectors per lane per tile
-  constexpr int kRowBytes = FP8 ? 128 : 256;   // one key row
+    int tiles_per_wave, int k, float* __restrict__ scores, SelWs sel) {
+  constexpr int NV = FP8 ? 4 : 8;             // 16-byte vectors per lane per tile
+  constexpr int kRowBytes = FP8 ? 128 : 256;  // one key row
+  constexpr int kStages = FP8 ? kStagesFp8 : kStagesBf16;
+  __shared__ uint32_t lhist[kSelBins];
+
   const int b = blockIdx.y;
   const int64_t off = kv_off[b];
   const int64_t L = kv_off[b + 1] - off;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, g = lane >> 5;
   const int64_t chunk = (int64_t)kDecWaves * tiles_per_wave * kTile;
-  int64_t t0 = (int64_t)blockIdx.x * chunk + (int64_t)wave * kTile;
-  if (t0 >= L) return;
+  const int64_t wg0 = (int64_t)blockIdx.x * chunk;
+  if (wg0 >= L) return;  // whole workgroup: no key of this request here
+  const bool select = L > k;
+  for (int i = tid; i < kSelBins; i += 256) lhist[i] = 0;
 
   // Query heads as MFMA A operand: row = head (hb*32 + col), dims 64g + 8j .. +7.
   bf16x8 qa[2][8];
@@ -64,32 +82,37 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
       wl[hb][r] = head < H ? w[(int64_t)b * H + head] : 0.0f;
     }
   }
+  __syncthreads();
 
-  const uint8_t* kbase = kc + (off * kRowBytes) + (FP8 ? 64 : 128) * g;
-  auto load_tile = [&](i32x4 (&raw)[NV], int64_t tt0) {
-    int64_t s = tt0 + col;
+  // This wave's tiles: it = 0 .. nt-1 at tokens wg0 + 32*(wave + 4*it).
+  const int64_t w0 = wg0 + (int64_t)wave * kTile;
+  int nt = 0;
+  if (w0 < L) {
+    const int64_t t = (L - w0 + (int64_t)kDecWaves * kTile - 1) / ((int64_t)kDecWaves * kTile);
+    nt = (int)(t < tiles_per_wave ? t : tiles_per_wave);
+  }
+  const uint8_t* kbase = kc + off * kRowBytes + (FP8 ? 64 : 128) * g;
+  auto tok = [&](int it) { return w0 + (int64_t)it * kDecWaves * kTile + col; };
+  auto load_tile = [&](i32x4 (&raw)[NV], float& sc, int it) {
+    int64_t s = tok(it);
     s = s < L ? s : L - 1;
     const uint8_t* p = kbase + s * kRowBytes;
 #pragma unroll
     for (int v = 0; v < NV; ++v) raw[v] = ld16(p + 16 * v);
+    sc = k_scale ? k_scale[off + s] : 1.0f;
   };
-
-  i32x4 cur[NV], nxt[NV];
-  load_tile(cur, t0);
-  for (int it = 0;;) {
-    const int64_t t1 = t0 + (int64_t)kDecWaves * kTile;
-    const bool has_next = (++it < tiles_per_wave) && (t1 < L);
-    if (has_next) load_tile(nxt, t1);
-
+  // `it` is already clamped to a valid tile; `live` is false for the repeated
+  // last tile that pads the pipeline, whose (identical) scores are not counted.
+  auto compute = [&](const i32x4 (&raw)[NV], float sc, int it, bool live) {
     f32x16 a0 = {}, a1 = {};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       bf16x8 kb;
       if constexpr (FP8) {
-        const i32x4 v = cur[j >> 1];
+        const i32x4 v = raw[j >> 1];
         kb = (j & 1) ? fp8x8_to_bf16x8(v.z, v.w) : fp8x8_to_bf16x8(v.x, v.y);
       } else {
-        kb = __builtin_bit_cast(bf16x8, cur[j]);
+        kb = __builtin_bit_cast(bf16x8, raw[j]);
       }
       a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][j], kb, a0, 0, 0, 0);
       a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][j], kb, a1, 0, 0, 0);
@@ -97,42 +120,76 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
     float part = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      part = fmaf(wl[0][r], fmaxf(a0[r], 0.0f), part);
-      part = fmaf(wl[1][r], fmaxf(a1[r], 0.0f), part);
+      part = fmaf(wl[0][r], relu(a0[r]), part);
+      part = fmaf(wl[1][r], relu(a1[r]), part);
     }
-    part += __shfl_xor(part, 32, 64);
-    const int64_t s = t0 + col;
-    if (g == 0 && s < L) {
-      const float sc = k_scale ? k_scale[off + s] : 1.0f;
-      scores[off + s] = part * sc;
-    }
-    if (!has_next) break;
+    part = sum_halves(part);
+    // Straight-line on purpose (no branch around the global store) so the
+    // compiler can keep the other stages' loads in flight: both lane halves
+    // hold the same total and store it, and a position past L was loaded as
+    // row L-1, so its store rewrites row L-1 with that row's own score.
+    const int64_t s = tok(it);
+    const int64_t sc_row = s < L ? s : L - 1;
+    const float val = part * sc;
+    scores[off + sc_row] = val;
+    // (an LDS-only branch: it holds no global-memory op, so the loads' wait
+    // counting across it stays exact)
+    if (select && live && g == 0 && s < L) atomicAdd(&lhist[score_key(val) >> kSelShift], 1u);
+  };
+
+  if (nt > 0) {
+    // A ring of kStages tile buffers: while tile it is computed, the loads of
+    // tiles it+1 .. it+kStages-1 are in flight, the last of them issued just
+    // before the compute.  Tile indices past nt-1 repeat the last tile.
+    i32x4 buf[kStages][NV];
+    float scb[kStages];
 #pragma unroll
-    for (int v = 0; v < NV; ++v) cur[v] = nxt[v];
-    t0 = t1;
+    for (int st = 0; st < kStages - 1; ++st) load_tile(buf[st], scb[st], st < nt ? st : nt - 1);
+    const int nit = (nt + kStages - 1) / kStages * kStages;
+    for (int base = 0; base < nit; base += kStages) {
+#pragma unroll
+      for (int st = 0; st < kStages; ++st) {
+        const int it = base + st;
+        const int nx = it + kStages - 1;
+        load_tile(buf[(st + kStages - 1) % kStages], scb[(st + kStages - 1) % kStages], nx < nt ? nx : nt - 1);
+        compute(buf[st], scb[st], it < nt ? it : nt - 1, it < nt);
+      }
+    }
   }
+  if (!select) return;
+
+  // This workgroup's share of the request's level-0 histogram, as 16-bit
+  // partials (a workgroup covers at most 2048 positions).
+  __syncthreads();
+  store_partial<256>(lhist, sel.part + ((int64_t)b * sel.nwg + blockIdx.x) * kSelBins);
 }
 
 }  // namespace
 
+int64_t decode_chunk(int64_t n_tok) {
+  // Tiles per wave: about two workgroups per CU when there is enough work (the
+  // kernel holds two 4-wave workgroups per CU), long runs so each workgroup's
+  // one-off query load and histogram store are amortised.
+  int64_t tpw = n_tok / ((int64_t)512 * kDecWaves * kTile);
+  tpw = tpw < 4 ? 4 : (tpw > 64 ? 64 : tpw);
+  return (int64_t)kDecWaves * tpw * kTile;
+}
+
 hipError_t launch_decode_score(const uint16_t* q, const float* w, const void* kc, bool kc_fp8,
                                const float* k_scale, const int64_t* kv_off, int32_t B,
-                               int64_t n_tok, int32_t max_len, int32_t H, float* scores,
-                               hipStream_t stream) {
+                               int64_t n_tok, int32_t max_len, int32_t H, int32_t k,
+                               float* scores, const SelWs& sel, hipStream_t stream) {
   if (B <= 0 || max_len <= 0) return hipSuccess;
-  // Tiles per wave: enough workgroups to fill 256 CUs several times over, but
-  // long enough runs that each workgroup's one-off query load is amortised.
-  int64_t tpw = n_tok / ((int64_t)2048 * kDecWaves * kTile);
-  tpw = tpw < 1 ? 1 : (tpw > 16 ? 16 : tpw);
-  const int64_t chunk = (int64_t)kDecWaves * tpw * kTile;
+  const int64_t chunk = decode_chunk(n_tok);
+  const int tpw = (int)(chunk / ((int64_t)kDecWaves * kTile));
   dim3 grid((unsigned)((max_len + chunk - 1) / chunk), (unsigned)B);
   dim3 block(64 * kDecWaves);
   if (kc_fp8)
     decode_score_kernel<true><<<grid, block, 0, stream>>>(
-        q, w, (const uint8_t*)kc, k_scale, kv_off, H, (int)tpw, scores);
+        q, w, (const uint8_t*)kc, k_scale, kv_off, H, tpw, k, scores, sel);
   else
     decode_score_kernel<false><<<grid, block, 0, stream>>>(
-        q, w, (const uint8_t*)kc, k_scale, kv_off, H, (int)tpw, scores);
+        q, w, (const uint8_t*)kc, k_scale, kv_off, H, tpw, k, scores, sel);
   return hipGetLastError();
 }
 

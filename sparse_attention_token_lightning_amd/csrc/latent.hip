@@ -22,10 +22,13 @@
 //   registers and runs v_mfma_f32_32x32x16_f16 against the shared tile, then
 //   the same ReLU-weighted head reduction as the native scan.  The gather
 //   variant (HS) reads rows kv_off[b] + cand[b][j] instead of contiguous ones.
+//   The contiguous variant also builds each (request, layer) row's level-0
+//   selection histogram in LDS and stores it as the workgroup's partial.
 #include <math.h>
 
 #include "li_device.h"
 #include "li_internal.h"
+#include "li_select.h"
 
 namespace li {
 namespace {
@@ -102,11 +105,13 @@ __global__ __launch_bounds__(256) void latent_score_kernel(
     const uint16_t* __restrict__ qt16, const float* __restrict__ wsc,
     const uint16_t* __restrict__ latent, const float* __restrict__ c_scale,
     const int64_t* __restrict__ kv_off, const int32_t* __restrict__ cand, int C, int64_t n_tok,
-    int G, int H, int tiles_per_block, float* __restrict__ scores) {
+    int G, int H, int tiles_per_block, int k, float* __restrict__ scores, SelWs sel) {
   constexpr int KSTEPS = DC / 16;  // K = 16 per MFMA
   constexpr int HALF = DC / 2;     // dims per lane half
   constexpr int CPT = DC / 64;     // 8-element chunks per thread per tile
+  constexpr int HB = GATHER ? 1 : kLsWaves;  // histogram planes (unused when gathering)
   __shared__ i32x4 lds[2][KSTEPS * 64];
+  __shared__ uint32_t lhist[HB][GATHER ? 1 : kSelBins];
   __shared__ int32_t sh_n;
 
   const int b = blockIdx.y;
@@ -137,6 +142,10 @@ __global__ __launch_bounds__(256) void latent_score_kernel(
   if (tok0 >= n) return;
   int64_t ntl = (n - tok0 + 31) / 32;
   const int ntiles = (int)(ntl < tiles_per_block ? ntl : tiles_per_block);
+  const bool select = !GATHER && n > k;
+  if constexpr (!GATHER) {
+    for (int i = threadIdx.x; i < kLsWaves * kSelBins; i += 256) (&lhist[0][0])[i] = 0;
+  }
 
   f16x8 qa[2][KSTEPS];
   float wl[2][16];
@@ -199,35 +208,57 @@ __global__ __launch_bounds__(256) void latent_score_kernel(
       float part = 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        part = fmaf(wl[0][r], fmaxf(a0[r], 0.0f), part);
-        part = fmaf(wl[1][r], fmaxf(a1[r], 0.0f), part);
+        part = fmaf(wl[0][r], relu(a0[r]), part);
+        part = fmaf(wl[1][r], relu(a1[r]), part);
       }
-      part += __shfl_xor(part, 32, 64);
+      part = sum_halves(part);
       const int64_t s = tok0 + (int64_t)it * 32 + col;
       if (g == 0 && s < n) {
         const float sc = c_scale ? c_scale[row_of(s)] : 1.0f;
-        if constexpr (GATHER)
-          scores[((int64_t)b * G + l) * C + s] = part * sc;
-        else
-          scores[(int64_t)l * n_tok + off + s] = part * sc;
+        const float val = part * sc;
+        if constexpr (GATHER) {
+          scores[((int64_t)b * G + l) * C + s] = val;
+        } else {
+          scores[(int64_t)l * n_tok + off + s] = val;
+          if (select) atomicAdd(&lhist[wave][score_key(val) >> kSelShift], 1u);
+        }
       }
     }
     if (it + 1 < ntiles) lstore(buf ^ 1);
     __syncthreads();
   }
+  if constexpr (!GATHER) {
+    if (!select) return;
+    // Each layer's share of its (b, l) row histogram, as 16-bit partials.
+    const int nl = (G - (int)blockIdx.z * kLsWaves) < kLsWaves ? (G - (int)blockIdx.z * kLsWaves) : kLsWaves;
+    for (int lw = 0; lw < nl; ++lw) {
+      const int64_t r = (int64_t)b * G + blockIdx.z * kLsWaves + lw;
+      store_partial<256>(lhist[lw], sel.part + (r * sel.nwg + blockIdx.x) * kSelBins);
+    }
+  }
 }
+
+}  // namespace
+
+int64_t latent_chunk(int64_t n_tok) {
+  int64_t tpb = n_tok / ((int64_t)1024 * 32);
+  tpb = tpb < 4 ? 4 : (tpb > 64 ? 64 : tpb);
+  return tpb * 32;
+}
+
+namespace {
 
 template <bool GATHER>
 hipError_t launch_ls(int Dc, dim3 grid, hipStream_t stream, const uint16_t* qt16, const float* wsc,
                      const uint16_t* latent, const float* c_scale, const int64_t* kv_off,
-                     const int32_t* cand, int C, int64_t n_tok, int G, int H, int tpb,
-                     float* scores) {
+                     const int32_t* cand, int C, int64_t n_tok, int G, int H, int tpb, int k,
+                     float* scores, const SelWs& sel) {
   if (Dc == 256)
     latent_score_kernel<256, GATHER><<<grid, dim3(256), 0, stream>>>(
-        qt16, wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, scores);
+        qt16, wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
   else
     latent_score_kernel<128, GATHER><<<grid, dim3(256), 0, stream>>>(
-        qt16, wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, scores);
+        qt16, wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
   return hipGetLastError();
 }
 
@@ -246,15 +277,14 @@ hipError_t launch_latent_absorb(const uint16_t* q, const float* w, const uint16_
 hipError_t launch_latent_score(const uint16_t* qt16, const float* wsc, const uint16_t* latent,
                                const float* c_scale, const int64_t* kv_off, int32_t B,
                                int64_t n_tok, int32_t max_len, int32_t G, int32_t H, int32_t Dc,
-                               float* scores, hipStream_t stream) {
+                               int32_t k, float* scores, const SelWs& sel, hipStream_t stream) {
   if (B <= 0 || max_len <= 0) return hipSuccess;
-  int64_t tpb = n_tok / ((int64_t)1024 * 32);
-  tpb = tpb < 4 ? 4 : (tpb > 64 ? 64 : tpb);
-  const int64_t chunk = tpb * 32;
+  const int64_t chunk = latent_chunk(n_tok);
+  const int64_t tpb = chunk / 32;
   dim3 grid((unsigned)((max_len + chunk - 1) / chunk), (unsigned)B,
             (unsigned)((G + kLsWaves - 1) / kLsWaves));
   return launch_ls<false>(Dc, grid, stream, qt16, wsc, latent, c_scale, kv_off, nullptr, 0, n_tok,
-                          G, H, (int)tpb, scores);
+                          G, H, (int)tpb, k, scores, sel);
 }
 
 hipError_t launch_hs_score(const uint16_t* qt16, const float* wsc, const uint16_t* latent,
@@ -267,8 +297,9 @@ hipError_t launch_hs_score(const uint16_t* qt16, const float* wsc, const uint16_
   const int64_t chunk = tpb * 32;
   dim3 grid((unsigned)((C + chunk - 1) / chunk), (unsigned)B,
             (unsigned)((Gf + kLsWaves - 1) / kLsWaves));
+  SelWs none = {};
   return launch_ls<true>(Dc, grid, stream, qt16, wsc, latent, c_scale, kv_off, cand, C, 0, Gf, H,
-                         (int)tpb, scores);
+                         (int)tpb, 0, scores, none);
 }
 
 }  // namespace li

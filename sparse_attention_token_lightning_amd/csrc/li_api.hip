@@ -50,7 +50,7 @@ li_status hip_check(hipError_t e, const char* what, hipStream_t s) {
 }
 
 constexpr size_t kAlign = 256;
-constexpr int64_t kHistBins = 2048;
+constexpr int64_t kHistBins = li::kSelBins;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -66,25 +66,58 @@ struct Carver {
   }
 };
 
-size_t decode_ws(int32_t B, int64_t n_tok, bool scores_given) {
+int64_t nseg_for(int64_t max_len) { return (max_len + li::kSeg - 1) / li::kSeg; }
+
+// Selection state for `rows` rows: per-row thresholds; with `chunk` > 0 also
+// the scan workgroups' partial histograms (ceil(max_len / chunk) per row), the
+// summed histograms and the collect segments' candidates.
+size_t sel_ws(int64_t rows, int64_t max_len, int64_t chunk) {
+  size_t s = align_up((size_t)rows * 16);  // thr
+  if (chunk > 0) {
+    const int64_t nwg = (max_len + chunk - 1) / chunk, nseg = nseg_for(max_len);
+    s += align_up((size_t)rows * nwg * kHistBins * 2) + align_up((size_t)rows * kHistBins * 4);
+    s += align_up((size_t)rows * nseg * 4) + align_up((size_t)rows * nseg * li::kSeg * 8);
+  }
+  return s;
+}
+
+li::SelWs carve_sel(Carver& cv, int64_t rows, int64_t max_len, int64_t chunk) {
+  li::SelWs w = {};
+  w.thr = (uint32_t*)cv.take((size_t)rows * 16);
+  if (chunk > 0) {
+    const int64_t nwg = (max_len + chunk - 1) / chunk, nseg = nseg_for(max_len);
+    w.part = (uint16_t*)cv.take((size_t)rows * nwg * kHistBins * 2);
+    w.ghist = (uint32_t*)cv.take((size_t)rows * kHistBins * 4);
+    w.cnt = (uint32_t*)cv.take((size_t)rows * nseg * 4);
+    w.cand = (uint2*)cv.take((size_t)rows * nseg * li::kSeg * 8);
+    w.nwg = (int32_t)nwg;
+    w.chunk = (int32_t)chunk;
+    w.nseg = (int32_t)nseg;
+  }
+  return w;
+}
+
+size_t decode_ws(int32_t B, int64_t n_tok, int32_t max_len, bool scores_given) {
   size_t s = 0;
   if (!scores_given) s += align_up((size_t)n_tok * 4);
-  s += align_up((size_t)(B > 0 ? B : 0) * kHistBins * 4);  // per-row histograms
+  const int64_t rows = B > 0 ? B : 0;
+  s += sel_ws(rows, max_len > 0 ? max_len : 0, li::decode_chunk(n_tok));
   return s;
 }
 
 size_t prefill_ws(int32_t T, int32_t L, bool scores_given) {
   size_t s = 0;
   if (!scores_given) s += align_up((size_t)T * (size_t)L * 4);
-  s += align_up((size_t)(T > 0 ? T : 0) * kHistBins * 4);
+  s += sel_ws(T > 0 ? T : 0, 0, 0);
   return s;
 }
 
-size_t latent_ws(int32_t B, int64_t n_tok, int32_t G, int32_t H, int32_t Dc, bool scores_given) {
-  const size_t rows = (size_t)B * G;
+size_t latent_ws(int32_t B, int64_t n_tok, int32_t max_len, int32_t G, int32_t H, int32_t Dc,
+                 bool scores_given) {
+  const size_t rows = (size_t)(B > 0 ? B : 0) * (G > 0 ? G : 0);
   size_t s = align_up(rows * H * Dc * 2) + align_up(rows * H * 4);
   if (!scores_given) s += align_up((size_t)G * (size_t)n_tok * 4);
-  s += align_up(rows * kHistBins * 4);
+  s += sel_ws((int64_t)rows, max_len > 0 ? max_len : 0, li::latent_chunk(n_tok));
   return s;
 }
 
@@ -92,7 +125,6 @@ size_t hs_ws(int32_t B, int32_t C, int32_t Gf, int32_t H, int32_t Dc, bool score
   const size_t rows = (size_t)B * Gf;
   size_t s = align_up(rows * H * Dc * 2) + align_up(rows * H * 4);
   if (!scores_given) s += align_up(rows * (size_t)C * 4);
-  s += align_up(rows * kHistBins * 4);
   return s;
 }
 
@@ -145,9 +177,8 @@ int32_t li_trace_count(void) { return g_trace_n; }
 
 size_t li_index_decode_ws(int32_t B, int64_t n_tok, int32_t max_len, int32_t k,
                           int32_t has_out_scores) {
-  (void)max_len;
   (void)k;
-  return decode_ws(B, n_tok, has_out_scores != 0);
+  return decode_ws(B, n_tok, max_len, has_out_scores != 0);
 }
 
 li_status li_index_decode(const void* q, li_dtype q_dt, const float* w, const void* k_cache,
@@ -166,14 +197,16 @@ li_status li_index_decode(const void* q, li_dtype q_dt, const float* w, const vo
   if (n_tok >= (int64_t)1 << 40) return fail(LI_E_UNSUPPORTED, "n_tok too large");
   li_status st;
   if ((st = check_k(k)) || (st = check_heads(H, D, "D"))) return st;
-  if ((st = check_ws(ws, ws_bytes, decode_ws(B, n_tok, out_scores != nullptr)))) return st;
+  if ((st = check_ws(ws, ws_bytes, decode_ws(B, n_tok, max_len, out_scores != nullptr)))) return st;
   if (B == 0) return LI_OK;
   hipStream_t s = (hipStream_t)stream;
   trace_begin(s);
   Carver cv(ws);
   float* scores = out_scores ? out_scores : (float*)cv.take((size_t)n_tok * 4);
+  const li::SelWs sel = carve_sel(cv, B, max_len, li::decode_chunk(n_tok));
   if ((st = hip_check(li::launch_decode_score((const uint16_t*)q, w, k_cache, k_dt == LI_FP8_E4M3,
-                                              k_scale, kv_off, B, n_tok, max_len, H, scores, s),
+                                              k_scale, kv_off, B, n_tok, max_len, H, k, scores, sel,
+                                              s),
                       "decode_score launch", s)))
     return st;
   li::TopkRows tr = {};
@@ -185,7 +218,9 @@ li_status li_index_decode(const void* q, li_dtype q_dt, const float* w, const vo
   tr.G = 1;
   tr.k = k;
   tr.out = out_idx;
-  return hip_check(li::launch_topk(tr, s), "topk launch", s);
+  if ((st = hip_check(li::launch_hist_reduce(tr, sel, s), "histogram reduce launch", s))) return st;
+  if ((st = hip_check(li::launch_topk_collect(tr, sel, s), "topk collect launch", s))) return st;
+  return hip_check(li::launch_topk_pre(tr, sel, s), "topk launch", s);
 }
 
 size_t li_index_prefill_ws(int32_t T, int32_t L, int32_t k, int32_t has_out_scores) {
@@ -214,9 +249,10 @@ li_status li_index_prefill(const void* q, li_dtype q_dt, const float* q_scale, c
   trace_begin(s);
   Carver cv(ws);
   float* scores = out_scores ? out_scores : (float*)cv.take((size_t)T * (size_t)L * 4);
+  const li::SelWs sel = carve_sel(cv, T, 0, 0);
   if ((st = hip_check(li::launch_prefill_score((const uint8_t*)q, q_scale, w, (const uint8_t*)k_cache,
-                                               k_scale, T, L, qpos0, H, out_scores != nullptr,
-                                               scores, s),
+                                               k_scale, T, L, qpos0, H, k, out_scores != nullptr,
+                                               scores, sel, s),
                       "prefill_score launch", s)))
     return st;
   li::TopkRows tr = {};
@@ -228,7 +264,7 @@ li_status li_index_prefill(const void* q, li_dtype q_dt, const float* q_scale, c
   tr.qpos0 = qpos0;
   tr.k = k;
   tr.out = out_idx;
-  return hip_check(li::launch_topk(tr, s), "topk launch", s);
+  return hip_check(li::launch_topk_self(tr, sel, s), "topk launch", s);
 }
 
 static li_status check_latent_common(li_dtype q_dt, li_dtype w_dt, li_dtype c_dt, int32_t H,
@@ -242,10 +278,10 @@ static li_status check_latent_common(li_dtype q_dt, li_dtype w_dt, li_dtype c_dt
   return LI_OK;
 }
 
-size_t li_latent_score_group_ws(int32_t B, int64_t n_tok, int32_t G, int32_t H, int32_t Dc,
-                                int32_t k, int32_t has_out_scores) {
+size_t li_latent_score_group_ws(int32_t B, int64_t n_tok, int32_t max_len, int32_t G, int32_t H,
+                                int32_t Dc, int32_t k, int32_t has_out_scores) {
   (void)k;
-  return latent_ws(B, n_tok, G, H, Dc, has_out_scores != 0);
+  return latent_ws(B, n_tok, max_len, G, H, Dc, has_out_scores != 0);
 }
 
 li_status li_latent_score_group(const void* q, li_dtype q_dt, const float* w, const void* w_dec,
@@ -263,7 +299,8 @@ li_status li_latent_score_group(const void* q, li_dtype q_dt, const float* w, co
     return fail(LI_E_SHAPE, "need B, n_tok, max_len >= 0 and G >= 1");
   if ((int64_t)G * n_tok >= (int64_t)1 << 40) return fail(LI_E_UNSUPPORTED, "G * n_tok too large");
   if ((st = check_k(k))) return st;
-  if ((st = check_ws(ws, ws_bytes, latent_ws(B, n_tok, G, H, Dc, out_scores != nullptr)))) return st;
+  if ((st = check_ws(ws, ws_bytes, latent_ws(B, n_tok, max_len, G, H, Dc, out_scores != nullptr))))
+    return st;
   if (B == 0) return LI_OK;
   hipStream_t s = (hipStream_t)stream;
   trace_begin(s);
@@ -271,12 +308,13 @@ li_status li_latent_score_group(const void* q, li_dtype q_dt, const float* w, co
   uint16_t* qt16 = (uint16_t*)cv.take((size_t)B * G * H * Dc * 2);
   float* wsc = (float*)cv.take((size_t)B * G * H * 4);
   float* scores = out_scores ? out_scores : (float*)cv.take((size_t)G * (size_t)n_tok * 4);
+  const li::SelWs sel = carve_sel(cv, (int64_t)B * G, max_len, li::latent_chunk(n_tok));
   if ((st = hip_check(li::launch_latent_absorb((const uint16_t*)q, w, (const uint16_t*)w_dec, B, G,
                                                H, Dh, Dc, qt16, wsc, s),
                       "latent_absorb launch", s)))
     return st;
   if ((st = hip_check(li::launch_latent_score(qt16, wsc, (const uint16_t*)latent, c_scale, kv_off, B,
-                                              n_tok, max_len, G, H, Dc, scores, s),
+                                              n_tok, max_len, G, H, Dc, k, scores, sel, s),
                       "latent_score launch", s)))
     return st;
   li::TopkRows tr = {};
@@ -288,7 +326,9 @@ li_status li_latent_score_group(const void* q, li_dtype q_dt, const float* w, co
   tr.G = G;
   tr.k = k;
   tr.out = out_idx;
-  return hip_check(li::launch_topk(tr, s), "topk launch", s);
+  if ((st = hip_check(li::launch_hist_reduce(tr, sel, s), "histogram reduce launch", s))) return st;
+  if ((st = hip_check(li::launch_topk_collect(tr, sel, s), "topk collect launch", s))) return st;
+  return hip_check(li::launch_topk_pre(tr, sel, s), "topk launch", s);
 }
 
 size_t li_hs_refine_ws(int32_t B, int32_t C, int32_t Gf, int32_t H, int32_t Dc, int32_t k,
@@ -340,9 +380,10 @@ li_status li_hs_refine(const int32_t* cand_idx, int32_t C, const void* q, li_dty
 }
 
 size_t li_topk_ws(int32_t rows, int32_t n, int32_t k) {
+  (void)rows;
   (void)n;
   (void)k;
-  return align_up((size_t)(rows > 0 ? rows : 0) * kHistBins * 4);
+  return 0;
 }
 
 li_status li_topk(const float* scores, int64_t row_stride, const int32_t* row_len, int32_t rows,

@@ -57,6 +57,14 @@ __device__ __forceinline__ i32x4 bf16x8_to_f16x8(i32x4 v) {
   return r;
 }
 
+// ReLU on the bit pattern: a float with the sign bit set (negative, or -0) is
+// a negative int32, so max(int, 0) yields +0 for it and leaves positive
+// floats unchanged.  One integer op, with none of the NaN canonicalisation an
+// IEEE float max needs.
+__device__ __forceinline__ float relu(float x) {
+  return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+}
+
 // Order-preserving map from an fp32 score to a uint32 key: a larger score
 // gives a larger key, and -0 maps to the key of +0 so that the two compare
 // equal (the tie then goes to the lower position).  NaN is not expected.
@@ -65,6 +73,11 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+
+// Sum of v over lanes l and l^32, in every lane.  (A cross-lane shuffle;
+// gfx950's v_permlane32_swap would avoid the LDS crossbar, but this compiler
+// folds the two results of that builtin into one register.)
+__device__ __forceinline__ float sum_halves(float v) { return v + __shfl_xor(v, 32, 64); }
 
 // Inclusive scan of a uint32 over the 64 lanes of a wavefront.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {

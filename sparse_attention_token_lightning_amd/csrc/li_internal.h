@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "li_select.h"
+
 namespace li {
 
 // How the top-k kernel finds row r of the score matrix.
@@ -32,20 +34,35 @@ struct TopkRows {
   int32_t* out;            // [rows][k]
 };
 
+// Top-k with the level-0 histogram built on the fly (one workgroup per row).
 hipError_t launch_topk(const TopkRows& a, hipStream_t stream);
+// Top-k from scan-built thresholds: collect candidates per segment (many
+// workgroups per row), then finish each row from its candidates.
+hipError_t launch_topk_collect(const TopkRows& a, const SelWs& ws, hipStream_t stream);
+hipError_t launch_topk_pre(const TopkRows& a, const SelWs& ws, hipStream_t stream);
+// Top-k from scan-built thresholds, one workgroup per row collecting its own candidates.
+hipError_t launch_topk_self(const TopkRows& a, const SelWs& ws, hipStream_t stream);
+// Sum the scan workgroups' partial histograms into ws.ghist (rows longer than k).
+hipError_t launch_hist_reduce(const TopkRows& a, const SelWs& ws, hipStream_t stream);
 
-// Decode scan: scores[kv_off[b] + s] for every request b and s < L_b.
+// Positions of one row covered by one scan workgroup (decode / latent).
+int64_t decode_chunk(int64_t n_tok);
+int64_t latent_chunk(int64_t n_tok);
+
+// Decode scan: scores[kv_off[b] + s] for every request b and s < L_b; rows
+// longer than k also get their partial level-0 histograms in `sel`.
 hipError_t launch_decode_score(const uint16_t* q, const float* w, const void* kc, bool kc_fp8,
                                const float* k_scale, const int64_t* kv_off, int32_t B,
-                               int64_t n_tok, int32_t max_len, int32_t H, float* scores,
-                               hipStream_t stream);
+                               int64_t n_tok, int32_t max_len, int32_t H, int32_t k,
+                               float* scores, const SelWs& sel, hipStream_t stream);
 
 // Prefill scan: scores[t][s] for s <= qpos0 + t; with fill_masked also -inf
-// for the masked rest of every row.
+// for the masked rest of every row.  Rows with more than k visible keys get
+// their threshold bin in sel.thr.
 hipError_t launch_prefill_score(const uint8_t* q, const float* q_scale, const float* w,
                                 const uint8_t* kc, const float* k_scale, int32_t T, int32_t L,
-                                int32_t qpos0, int32_t H, bool fill_masked, float* scores,
-                                hipStream_t stream);
+                                int32_t qpos0, int32_t H, int32_t k, bool fill_masked,
+                                float* scores, const SelWs& sel, hipStream_t stream);
 
 // Latent absorption: qt16[b][l][h][Dc] (fp16, range-scaled by 2^e per row) and
 // wsc[b][l][h] = w * 2^-e.
@@ -53,11 +70,12 @@ hipError_t launch_latent_absorb(const uint16_t* q, const float* w, const uint16_
                                 int32_t B, int32_t G, int32_t H, int32_t Dh, int32_t Dc,
                                 uint16_t* qt16, float* wsc, hipStream_t stream);
 
-// Latent scan over contiguous ragged rows: scores[l*n_tok + kv_off[b] + s].
+// Latent scan over contiguous ragged rows: scores[l*n_tok + kv_off[b] + s];
+// rows (b, l) longer than k also get their partial histograms in `sel`.
 hipError_t launch_latent_score(const uint16_t* qt16, const float* wsc, const uint16_t* latent,
                                const float* c_scale, const int64_t* kv_off, int32_t B,
                                int64_t n_tok, int32_t max_len, int32_t G, int32_t H, int32_t Dc,
-                               float* scores, hipStream_t stream);
+                               int32_t k, float* scores, const SelWs& sel, hipStream_t stream);
 
 // HS gather scan: scores[(b*Gf + f)*C + j] for the valid candidates j of b.
 hipError_t launch_hs_score(const uint16_t* qt16, const float* wsc, const uint16_t* latent,

@@ -56,9 +56,11 @@ def test_workspace_queries():
     assert without - with_s >= n * 4 and with_s >= 32 * 2048 * 4
     assert L.li_index_prefill_ws(4096, 65536, 2048, 0) >= 4096 * 65536 * 4
     # absorbed fp16 queries + scaled weights + scores
-    assert L.li_latent_score_group_ws(16, 1 << 21, 4, 64, 256, 2048, 0) >= 16 * 4 * 64 * 256 * 2 + 4 * (1 << 21) * 4
+    assert L.li_latent_score_group_ws(16, 1 << 21, 131072, 4, 64, 256, 2048, 0) >= 16 * 4 * 64 * 256 * 2 + 4 * (1 << 21) * 4
     assert L.li_hs_refine_ws(16, 8192, 3, 64, 256, 2048, 0) >= 16 * 3 * 8192 * 4
     assert L.li_topk_ws(10, 100, 5) % 256 == 0
+    # selection state: candidates of up to max_len / 8192 segments per row
+    assert L.li_index_decode_ws(32, 32 * 131072, 131072, 2048, 1) >= 32 * 16 * 8192 * 8
 
 
 def _decode(**kw):
