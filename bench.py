@@ -161,8 +161,7 @@ def components(torch, li, inputs, args):
     ws = torch.empty(li.lib().li_latent_score_group_ws(x.B, x.n_tok, 131072, x.G, x.H, x.Dc, x.k, 0),
                      dtype=torch.uint8, device="cuda")
     fn = lambda: li.li_latent_score_group(q, w, wd, lat, None, off, 131072, x.k, out_idx=idx, ws=ws)
-    wall, (absorb, scan, reduce, collect, final) = timed(torch, li, fn, 6, args.comp_iters, 2)
-    topk = reduce + collect + final
+    wall, (absorb, scan, topk) = timed(torch, li, fn, 4, args.comp_iters, 2)
     lat_bytes = x.n_tok * x.Dc * 2
     flop = 2.0 * x.G * x.H * x.Dc * x.n_tok
     out["latent_G4_B16_L131072"] = {
@@ -186,11 +185,9 @@ def components(torch, li, inputs, args):
     fa = lambda: li.li_index_decode(aq, aw, akc, aks, off, 131072, h.C, out_idx=cand, ws=ws_a)
     ff = lambda: li.li_hs_refine(cand, fq, fw, fwd, lat, None, off, f.k, out_idx=fidx, ws=ws_f)
     fn_native = lambda: li.li_index_decode(aq, aw, akc, aks, off, 131072, 2048, out_idx=nidx, ws=ws_a)
-    _, (a_scan, a_red, a_col, a_fin) = timed(torch, li, fa, 5, args.comp_iters, 2)
-    a_topk = a_red + a_col + a_fin
+    _, (a_scan, a_topk) = timed(torch, li, fa, 3, args.comp_iters, 2)
     _, (f_abs, f_scan, f_topk) = timed(torch, li, ff, 4, args.comp_iters, 2)
-    _, (n_scan, n_red, n_col, n_fin) = timed(torch, li, fn_native, 5, args.comp_iters, 2)
-    n_topk = n_red + n_col + n_fin
+    _, (n_scan, n_topk) = timed(torch, li, fn_native, 3, args.comp_iters, 2)
     hs_ms = a_scan + a_topk + f_abs + f_scan + f_topk
     native = n_scan + n_topk
     out["hs_B16_L131072_C8192_F3"] = {
@@ -205,8 +202,7 @@ def components(torch, li, inputs, args):
     idx = torch.empty((x.B, x.k), dtype=torch.int32, device="cuda")
     ws = torch.empty(L.li_index_decode_ws(x.B, x.n_tok, int(x.lens.max()), x.k, 0), dtype=torch.uint8, device="cuda")
     fn = lambda: li.li_index_decode(q, w, kc, ks, off, int(x.lens.max()), x.k, out_idx=idx, ws=ws)
-    wall, (scan, reduce, collect, final) = timed(torch, li, fn, 5, args.comp_iters, 2)
-    topk = reduce + collect + final
+    wall, (scan, topk) = timed(torch, li, fn, 3, args.comp_iters, 2)
     out["decode_fp8_B32_ragged8K-32K"] = {
         "scan_ms": scan, "topk_ms": topk, "total_ms": wall, "keys": x.n_tok,
         "scan_gbs_algorithmic": x.n_tok * FP8_KEY_BYTES / (scan * 1e-3) / 1e9,
@@ -258,7 +254,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    tr = Trace(torch, li, 5, args.steps)  # start | scan | reduce | collect | final
+    tr = Trace(torch, li, 3, args.steps)  # start | scan | top-k
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -269,8 +265,7 @@ def main():
     tr.off()
     ms_per_step = elapsed / args.steps * 1e3
     spans = [tr.spans(i) for i in range(args.steps)]
-    scan_ms, reduce_ms, collect_ms, final_ms = [sum(s[j] for s in spans) / args.steps for j in range(4)]
-    topk_ms = reduce_ms + collect_ms + final_ms
+    scan_ms, topk_ms = [sum(s[j] for s in spans) / args.steps for j in range(2)]
     keys = B * Lk
     achieved = keys * FP8_KEY_BYTES / (scan_ms * 1e-3) / 1e9
     traffic = load_traffic("decode_score", source_hash("decode.hip", "li_device.h"), keys)
@@ -298,9 +293,6 @@ def main():
                      "algorithmic_bytes_per_launch": keys * FP8_KEY_BYTES, "avg_launch_ms": scan_ms},
         "components": {"decode_fp8_B32_L131072": {"scan_ms": scan_ms, "top2048_ms": topk_ms,
                                                   "top2048_us": topk_ms * 1e3,
-                                                  "top2048_parts_us": {"hist_reduce": reduce_ms * 1e3,
-                                                                       "collect": collect_ms * 1e3,
-                                                                       "final": final_ms * 1e3},
                                                   "scan_gbs": achieved}},
     }
     if not args.no_components:

@@ -62,6 +62,8 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
   if (wg0 >= L) return;  // whole workgroup: no key of this request here
   const bool select = L > k;
   for (int i = tid; i < kSelBins; i += 256) lhist[i] = 0;
+  // The top-k kernel that follows counts finished segments per request.
+  if (select && blockIdx.x == 0 && tid == 0) sel.done[b] = 0u;
 
   // Query heads as MFMA A operand: row = head (hb*32 + col), dims 64g + 8j .. +7.
   bf16x8 qa[2][8];

@@ -145,6 +145,9 @@ __global__ __launch_bounds__(256) void latent_score_kernel(
   const bool select = !GATHER && n > k;
   if constexpr (!GATHER) {
     for (int i = threadIdx.x; i < kLsWaves * kSelBins; i += 256) (&lhist[0][0])[i] = 0;
+    // The top-k kernel that follows counts finished segments per (b, l) row.
+    if (select && blockIdx.x == 0 && threadIdx.x < kLsWaves && blockIdx.z * kLsWaves + threadIdx.x < G)
+      sel.done[(int64_t)b * G + blockIdx.z * kLsWaves + threadIdx.x] = 0u;
   }
 
   f16x8 qa[2][KSTEPS];

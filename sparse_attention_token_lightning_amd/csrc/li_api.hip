@@ -75,24 +75,25 @@ size_t sel_ws(int64_t rows, int64_t max_len, int64_t chunk) {
   size_t s = align_up((size_t)rows * 16);  // thr
   if (chunk > 0) {
     const int64_t nwg = (max_len + chunk - 1) / chunk, nseg = nseg_for(max_len);
-    s += align_up((size_t)rows * nwg * kHistBins * 2) + align_up((size_t)rows * kHistBins * 4);
+    s += align_up((size_t)rows * nwg * kHistBins * 2) + align_up((size_t)rows * 4);
     s += align_up((size_t)rows * nseg * 4) + align_up((size_t)rows * nseg * li::kSeg * 8);
   }
   return s;
 }
 
-li::SelWs carve_sel(Carver& cv, int64_t rows, int64_t max_len, int64_t chunk) {
+li::SelWs carve_sel(Carver& cv, int64_t rows, int64_t max_len, int64_t chunk, int32_t k) {
   li::SelWs w = {};
   w.thr = (uint32_t*)cv.take((size_t)rows * 16);
   if (chunk > 0) {
     const int64_t nwg = (max_len + chunk - 1) / chunk, nseg = nseg_for(max_len);
     w.part = (uint16_t*)cv.take((size_t)rows * nwg * kHistBins * 2);
-    w.ghist = (uint32_t*)cv.take((size_t)rows * kHistBins * 4);
+    w.done = (uint32_t*)cv.take((size_t)rows * 4);
     w.cnt = (uint32_t*)cv.take((size_t)rows * nseg * 4);
     w.cand = (uint2*)cv.take((size_t)rows * nseg * li::kSeg * 8);
     w.nwg = (int32_t)nwg;
     w.chunk = (int32_t)chunk;
     w.nseg = (int32_t)nseg;
+    w.cap = li::seg_cap_for(k);
   }
   return w;
 }
@@ -203,7 +204,7 @@ li_status li_index_decode(const void* q, li_dtype q_dt, const float* w, const vo
   trace_begin(s);
   Carver cv(ws);
   float* scores = out_scores ? out_scores : (float*)cv.take((size_t)n_tok * 4);
-  const li::SelWs sel = carve_sel(cv, B, max_len, li::decode_chunk(n_tok));
+  const li::SelWs sel = carve_sel(cv, B, max_len, li::decode_chunk(n_tok), k);
   if ((st = hip_check(li::launch_decode_score((const uint16_t*)q, w, k_cache, k_dt == LI_FP8_E4M3,
                                               k_scale, kv_off, B, n_tok, max_len, H, k, scores, sel,
                                               s),
@@ -218,9 +219,7 @@ li_status li_index_decode(const void* q, li_dtype q_dt, const float* w, const vo
   tr.G = 1;
   tr.k = k;
   tr.out = out_idx;
-  if ((st = hip_check(li::launch_hist_reduce(tr, sel, s), "histogram reduce launch", s))) return st;
-  if ((st = hip_check(li::launch_topk_collect(tr, sel, s), "topk collect launch", s))) return st;
-  return hip_check(li::launch_topk_pre(tr, sel, s), "topk launch", s);
+  return hip_check(li::launch_topk_segmented(tr, sel, s), "topk launch", s);
 }
 
 size_t li_index_prefill_ws(int32_t T, int32_t L, int32_t k, int32_t has_out_scores) {
@@ -249,7 +248,7 @@ li_status li_index_prefill(const void* q, li_dtype q_dt, const float* q_scale, c
   trace_begin(s);
   Carver cv(ws);
   float* scores = out_scores ? out_scores : (float*)cv.take((size_t)T * (size_t)L * 4);
-  const li::SelWs sel = carve_sel(cv, T, 0, 0);
+  const li::SelWs sel = carve_sel(cv, T, 0, 0, k);
   if ((st = hip_check(li::launch_prefill_score((const uint8_t*)q, q_scale, w, (const uint8_t*)k_cache,
                                                k_scale, T, L, qpos0, H, k, out_scores != nullptr,
                                                scores, sel, s),
@@ -308,7 +307,7 @@ li_status li_latent_score_group(const void* q, li_dtype q_dt, const float* w, co
   uint16_t* qt16 = (uint16_t*)cv.take((size_t)B * G * H * Dc * 2);
   float* wsc = (float*)cv.take((size_t)B * G * H * 4);
   float* scores = out_scores ? out_scores : (float*)cv.take((size_t)G * (size_t)n_tok * 4);
-  const li::SelWs sel = carve_sel(cv, (int64_t)B * G, max_len, li::latent_chunk(n_tok));
+  const li::SelWs sel = carve_sel(cv, (int64_t)B * G, max_len, li::latent_chunk(n_tok), k);
   if ((st = hip_check(li::launch_latent_absorb((const uint16_t*)q, w, (const uint16_t*)w_dec, B, G,
                                                H, Dh, Dc, qt16, wsc, s),
                       "latent_absorb launch", s)))
@@ -326,9 +325,7 @@ li_status li_latent_score_group(const void* q, li_dtype q_dt, const float* w, co
   tr.G = G;
   tr.k = k;
   tr.out = out_idx;
-  if ((st = hip_check(li::launch_hist_reduce(tr, sel, s), "histogram reduce launch", s))) return st;
-  if ((st = hip_check(li::launch_topk_collect(tr, sel, s), "topk collect launch", s))) return st;
-  return hip_check(li::launch_topk_pre(tr, sel, s), "topk launch", s);
+  return hip_check(li::launch_topk_segmented(tr, sel, s), "topk launch", s);
 }
 
 size_t li_hs_refine_ws(int32_t B, int32_t C, int32_t Gf, int32_t H, int32_t Dc, int32_t k,

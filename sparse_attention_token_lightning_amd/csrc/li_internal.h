@@ -36,15 +36,13 @@ struct TopkRows {
 
 // Top-k with the level-0 histogram built on the fly (one workgroup per row).
 hipError_t launch_topk(const TopkRows& a, hipStream_t stream);
-// Top-k from scan-built thresholds: collect candidates per segment (many
-// workgroups per row), then finish each row from its candidates.
-hipError_t launch_topk_collect(const TopkRows& a, const SelWs& ws, hipStream_t stream);
-hipError_t launch_topk_pre(const TopkRows& a, const SelWs& ws, hipStream_t stream);
+// Top-k from the scan's partial histograms: many workgroups per row collect
+// candidates; the last one of each row finishes it (one launch).
+hipError_t launch_topk_segmented(const TopkRows& a, const SelWs& ws, hipStream_t stream);
+// LDS candidate capacity of the segmented top-k's final step for a given k.
+int32_t seg_cap_for(int32_t k);
 // Top-k from scan-built thresholds, one workgroup per row collecting its own candidates.
 hipError_t launch_topk_self(const TopkRows& a, const SelWs& ws, hipStream_t stream);
-// Sum the scan workgroups' partial histograms into ws.ghist (rows longer than k).
-hipError_t launch_hist_reduce(const TopkRows& a, const SelWs& ws, hipStream_t stream);
-
 // Positions of one row covered by one scan workgroup (decode / latent).
 int64_t decode_chunk(int64_t n_tok);
 int64_t latent_chunk(int64_t n_tok);

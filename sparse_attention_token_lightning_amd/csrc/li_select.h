@@ -17,11 +17,12 @@ struct SelWs {
   uint16_t* part;   // [rows][nwg][kSelBins] per-workgroup level-0 histograms (scan kernels)
   int32_t nwg;      // partial histograms per row (the scan grid's x extent)
   int32_t chunk;    // positions of a row covered by one scan workgroup
-  uint32_t* ghist;  // [rows][kSelBins] summed level-0 histogram
   uint32_t* thr;    // [rows][4] {threshold bin, #keys above it, #keys in it, valid} (prefill)
   uint32_t* cnt;    // [rows][nseg] candidates per segment
   uint2* cand;      // [rows][nseg][kSeg] (key, position) candidates in position order
   int32_t nseg;
+  uint32_t* done;   // [rows] finished-segment counters (zeroed by the scan kernel)
+  int32_t cap;      // LDS candidates of the final selection in the segmented top-k
 };
 
 // Writes a workgroup's LDS histogram (counts < 65536) as 16-bit partials:

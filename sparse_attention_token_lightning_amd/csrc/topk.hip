@@ -3,35 +3,38 @@
 // Attention", Deep Dive, the F layer takes top-k of its scores).
 //
 // Scores map to order-preserving uint32 keys (-0 folded onto +0).  The
-// selection is a radix select whose first level (the top 11 key bits) is a
-// histogram that the scan kernels build while they write the scores, so the
-// threshold bin b* -- the level-0 bin holding the k-th largest key -- is known
-// before the selection starts ("pre" mode: the scan workgroups store partial
-// histograms that hist_reduce sums per row).  Then:
-//   collect (many workgroups per row, "pre" mode): each 8192-score segment of a
-//     row keeps, in position order, the (key, position) pairs whose bin is
-//     >= b*; at most (k-1) + |b*| of them exist in the whole row.
-//   final (one workgroup per row): loads those candidates into LDS in position
-//     order (or collects them itself in "self" mode, or first builds the
-//     level-0 histogram itself in "full" mode), resolves the remaining 21 key
-//     bits among the keys of bin b* with two more LDS histogram levels, and
-//     writes the kept positions with an ordered compaction:
-//       slot = #greater-before + min(#equal-before, m),
-//     where m is how many keys equal to the k-th key still fit -- so the output
-//     is in ascending position order and the lower position wins a tie.
-// Rows whose candidates do not fit in LDS (heavy ties) take a fallback that
-// runs the same radix select straight over the row in global memory.
-// Integer histograms make every path deterministic.
+// selection is a radix select whose first level is the top 11 key bits: the
+// threshold bin b* is the level-0 bin that holds the k-th largest key.  Then
+// the keys whose bin is >= b* -- at most (k-1) + |b*| of them -- are gathered
+// in position order, two more LDS histogram levels over the keys of bin b*
+// give the exact k-th key T and the number m of keys equal to T that still
+// fit, and an ordered compaction writes the kept positions:
+//   slot = #greater-before + min(#equal-before, m),
+// so the output is in ascending position order and the lower position wins a
+// tie.  Rows with at most k visible keys return all of them; unused slots are
+// -1.  Candidate sets too large for LDS (heavy ties) are resolved the same way
+// from global memory.  Integer histograms make every path deterministic.
+//
+// Two kernels:
+//   segmented (decode, LatentIndex: few long rows): one workgroup per
+//     (8192-score segment, row).  Each sums the row's per-scan-workgroup
+//     partial histograms to find b*, keeps its segment's candidates, and the
+//     last workgroup of the row to finish (device-scope counter; the scan
+//     kernel zeroes it) performs the final selection over all of them.  One
+//     launch after the scan.
+//   per-row (prefill, HS followers, standalone): one workgroup per row, which
+//     builds or is handed the level-0 histogram, collects its own candidates
+//     into LDS and finishes.
 #include "li_internal.h"
 #include "li_select.h"
 
 namespace li {
 namespace {
 
-constexpr int kFin = 1024;  // threads of the final kernel
-constexpr int kFinWaves = kFin / 64;
-constexpr int kCap = 12288;  // candidates held in LDS
-constexpr int kCol = 256;    // threads of the collect kernel
+constexpr int kRowThreads = 1024;  // per-row kernel
+constexpr int kRowCap = 12288;     // LDS candidates of the per-row kernel
+constexpr int kSegThreads = 256;   // segmented kernel
+constexpr int kSegMaxCap = 12288;  // largest LDS candidate buffer of the segmented kernel
 
 struct Row {
   const float* p;
@@ -91,60 +94,75 @@ __device__ __forceinline__ int32_t map_pos(const Row& row, int64_t i) {
   return row.map ? row.map[i] : (int32_t)i;
 }
 
-// One radix level over `count` keys: histogram of the `nb` digits at `shift`
-// among the keys matching (prefix, pmask), then the digit that holds the
-// `remaining`-th largest.  Leaves {digit, #keys above it} in sh[1], sh[2].
-template <typename KeyAt>
-__device__ void radix_level(KeyAt key_at, int64_t count, uint32_t prefix, uint32_t pmask, int shift,
-                            uint32_t nb, uint32_t remaining, uint32_t* hist, uint32_t* wsum,
-                            int32_t* sh) {
-  const int tid = threadIdx.x;
-  for (int i = tid; i < kSelBins; i += kFin) hist[i] = 0;
-  if (tid == 0) {
-    sh[1] = 0;
-    sh[2] = 0;
-  }
-  __syncthreads();
-  for (int64_t i = tid; i < count; i += kFin) {
-    const uint32_t key = key_at(i);
-    if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & (nb - 1)], 1u);
-  }
-  __syncthreads();
-  // Digits in descending order: thread t owns nb-1-2t and nb-2-2t (nb = 2048)
-  // or nb-1-t (nb = 1024).
-  const int per = (int)nb / kFin;
-  uint32_t hhi, hlo = 0;
-  int dhi, dlo = -1;
-  if (per == 2) {
-    dhi = (int)nb - 1 - 2 * tid;
-    dlo = dhi - 1;
-    hhi = hist[dhi];
-    hlo = hist[dlo];
-  } else {
-    dhi = (int)nb - 1 - tid;
-    hhi = hist[dhi];
-  }
+// Writes all n visible positions and pads the row with -1 (rows with n <= k).
+template <int NT>
+__device__ void keep_all(const Row& row, int64_t n, int k) {
+  for (int64_t i = threadIdx.x; i < k; i += NT) row.out[i] = (i < n) ? map_pos(row, i) : -1;
+}
+
+// Given per-thread counts of PER consecutive digits taken in descending order
+// (thread t owns digits top - t*PER - i), find the digit holding the
+// `remaining`-th largest key: {digit, #keys in higher digits, #keys in it}
+// land in out[0..2].  Ends with a barrier.
+template <int NT, int PER>
+__device__ void find_digit(const uint32_t (&h)[PER], int top, uint32_t remaining, uint32_t* wsum,
+                           uint32_t* out) {
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) sum += h[i];
   uint32_t total;
-  const uint32_t above = block_excl_scan<kFin>(hhi + hlo, wsum, total);
-  if (above < remaining && above + hhi >= remaining) {
-    sh[1] = dhi;
-    sh[2] = (int32_t)above;
-  } else if (dlo >= 0 && above + hhi < remaining && above + hhi + hlo >= remaining) {
-    sh[1] = dlo;
-    sh[2] = (int32_t)(above + hhi);
+  uint32_t run = block_excl_scan<NT>(sum, wsum, total);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (run < remaining && run + h[i] >= remaining) {
+      out[0] = (uint32_t)(top - ((int)threadIdx.x * PER + i));
+      out[1] = run;
+      out[2] = h[i];
+    }
+    run += h[i];
   }
   __syncthreads();
 }
 
+// One radix level over `count` keys: histogram of the nb digits at `shift`
+// among the keys matching (prefix, pmask), then the digit holding the
+// `remaining`-th largest.  Leaves {digit, #keys above it, #in it} in out.
+template <int NT, typename KeyAt>
+__device__ void radix_level(KeyAt key_at, int64_t count, uint32_t prefix, uint32_t pmask, int shift,
+                            int nb, uint32_t remaining, uint32_t* hist, uint32_t* wsum,
+                            uint32_t* out) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kSelBins; i += NT) hist[i] = 0;
+  __syncthreads();
+  for (int64_t i = tid; i < count; i += NT) {
+    const uint32_t key = key_at(i);
+    if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+  }
+  __syncthreads();
+  constexpr int PER = kSelBins / NT;  // digits per thread when nb = 2048
+  if (nb == kSelBins) {
+    uint32_t h[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) h[i] = hist[nb - 1 - (tid * PER + i)];
+    find_digit<NT, PER>(h, nb - 1, remaining, wsum, out);
+  } else {  // nb = 1024
+    constexpr int PH = PER / 2;
+    uint32_t h[PH];
+#pragma unroll
+    for (int i = 0; i < PH; ++i) h[i] = hist[nb - 1 - (tid * PH + i)];
+    find_digit<NT, PH>(h, nb - 1, remaining, wsum, out);
+  }
+}
+
 // Ordered compaction over `count` candidates in position order: keep keys > T
 // and the first m keys equal to T, writing slot = #gt-before + min(#eq-before, m).
-template <typename KeyAt, typename PosAt>
+template <int NT, typename KeyAt, typename PosAt>
 __device__ void compact(const Row& row, KeyAt key_at, PosAt pos_at, int64_t count, uint32_t T,
                         uint32_t m, int64_t kk, uint32_t* wsum) {
   const int tid = threadIdx.x;
   uint32_t gt_run = 0, eq_run = 0;
 #pragma unroll 1
-  for (int64_t base = 0; base < count; base += 4 * kFin) {
+  for (int64_t base = 0; base < count; base += 4 * NT) {
     const int64_t i0 = base + 4 * tid;
     uint32_t fl[4];
     uint32_t cg = 0, ce = 0;
@@ -159,7 +177,7 @@ __device__ void compact(const Row& row, KeyAt key_at, PosAt pos_at, int64_t coun
       ce += fl[e] & 1u;
     }
     uint32_t total;
-    const uint32_t ex = block_excl_scan<kFin>((cg << 16) | ce, wsum, total);
+    const uint32_t ex = block_excl_scan<NT>((cg << 16) | ce, wsum, total);
     uint32_t gb = gt_run + (ex >> 16), eb = eq_run + (ex & 0xFFFFu);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -178,34 +196,35 @@ __device__ void compact(const Row& row, KeyAt key_at, PosAt pos_at, int64_t coun
   }
 }
 
-// Full radix select over keys read through key_at (3 levels of 11/11/10 bits
-// starting from a known level-0 digit when `levels_from` = 1), then the
-// ordered compaction.  Used both on LDS candidates and, as the fallback, on a
-// row in global memory.
-template <typename KeyAt, typename PosAt>
+// Radix levels first_level..2 (11/11/10 bits) over keys read through key_at,
+// then the ordered compaction.  Used on LDS candidates (first_level = 1, the
+// level-0 digit already known) and on whole rows in global memory (0).
+template <int NT, typename KeyAt, typename PosAt>
 __device__ void select_keys(const Row& row, KeyAt key_at, PosAt pos_at, int64_t count,
                             uint32_t prefix, uint32_t pmask, uint32_t remaining, int first_level,
-                            int64_t kk, uint32_t* hist, uint32_t* wsum, int32_t* sh) {
+                            int64_t kk, uint32_t* hist, uint32_t* wsum, uint32_t* out) {
 #pragma unroll 1
   for (int level = first_level; level < 3; ++level) {
     const int shift = level == 0 ? 21 : (level == 1 ? 10 : 0);
-    const uint32_t nb = level == 2 ? 1024u : 2048u;
-    radix_level(key_at, count, prefix, pmask, shift, nb, remaining, hist, wsum, sh);
-    prefix |= (uint32_t)sh[1] << shift;
-    pmask |= (nb - 1) << shift;
-    remaining -= (uint32_t)sh[2];
+    const int nb = level == 2 ? 1024 : 2048;
+    radix_level<NT>(key_at, count, prefix, pmask, shift, nb, remaining, hist, wsum, out);
+    prefix |= out[0] << shift;
+    pmask |= (uint32_t)(nb - 1) << shift;
+    remaining -= out[1];
     __syncthreads();
   }
-  compact(row, key_at, pos_at, count, prefix, remaining, kk, wsum);
+  compact<NT>(row, key_at, pos_at, count, prefix, remaining, kk, wsum);
 }
 
-enum SelHow : int32_t { kSelPre = 0, kSelSelf = 1, kSelFull = 2 };
+enum SelHow : int32_t { kSelSelf = 1, kSelFull = 2 };
 
-__global__ __launch_bounds__(kFin) void topk_final_kernel(TopkRows a, SelWs ws, int how) {
-  __shared__ uint2 cand[kCap];
+// One workgroup per row.  kSelSelf: the row's level-0 threshold is in ws.thr
+// (prefill scan).  kSelFull: the workgroup builds the histogram itself.
+__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkRows a, SelWs ws, int how) {
+  __shared__ uint2 cand[kRowCap];
   __shared__ uint32_t hist[kSelBins];
-  __shared__ uint32_t segoff[kFin];
-  __shared__ uint32_t wsum[kFinWaves];
+  __shared__ uint32_t rcnt[8 * (kRowThreads / 64)];
+  __shared__ uint32_t wsum[kRowThreads / 64];
   __shared__ int32_t sh[4];
   __shared__ uint32_t shb[4];
   const int tid = threadIdx.x;
@@ -214,29 +233,36 @@ __global__ __launch_bounds__(kFin) void topk_final_kernel(TopkRows a, SelWs ws, 
   const int64_t n = row.n;
   const int k = a.k;
   const int64_t kk = n < k ? n : (int64_t)k;
-
-  if (kk == n) {  // everything visible is kept
-    for (int64_t i = tid; i < k; i += kFin) row.out[i] = (i < n) ? map_pos(row, i) : -1;
+  if (kk == n) {
+    keep_all<kRowThreads>(row, n, k);
     return;
   }
-  for (int64_t i = kk + tid; i < k; i += kFin) row.out[i] = -1;
-
+  for (int64_t i = kk + tid; i < k; i += kRowThreads) row.out[i] = -1;
   auto gkey = [&](int64_t i) { return score_key(row.p[i]); };
   auto gpos = [&](int64_t i) { return i; };
 
   uint32_t bstar, above, eq;
   if (how == kSelFull) {
-    for (int i = tid; i < kSelBins; i += kFin) hist[i] = 0;
+    for (int i = tid; i < kSelBins; i += kRowThreads) hist[i] = 0;
     __syncthreads();
-    for (int64_t i = tid; i < n; i += kFin) atomicAdd(&hist[gkey(i) >> kSelShift], 1u);
+#pragma unroll 1
+    for (int64_t b0 = 0; b0 < n; b0 += 8LL * kRowThreads) {
+      uint32_t kb[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t i = b0 + (int64_t)j * kRowThreads + tid;
+        kb[j] = i < n ? gkey(i) : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (b0 + (int64_t)j * kRowThreads + tid < n) atomicAdd(&hist[kb[j] >> kSelShift], 1u);
+    }
     __syncthreads();
-    block_find_bin<kFin>([&](int b) { return hist[b]; }, (uint32_t)kk, wsum, shb);
-    bstar = shb[0];
-    above = shb[1];
-    eq = shb[2];
-  } else if (how == kSelPre) {
-    const uint32_t* gh = ws.ghist + (int64_t)r * kSelBins;
-    block_find_bin<kFin>([&](int b) { return gh[b]; }, (uint32_t)kk, wsum, shb);
+    constexpr int PER = kSelBins / kRowThreads;
+    uint32_t h[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) h[i] = hist[kSelBins - 1 - (tid * PER + i)];
+    find_digit<kRowThreads, PER>(h, kSelBins - 1, (uint32_t)kk, wsum, shb);
     bstar = shb[0];
     above = shb[1];
     eq = shb[2];
@@ -247,161 +273,258 @@ __global__ __launch_bounds__(kFin) void topk_final_kernel(TopkRows a, SelWs ws, 
     eq = t[2];
   }
   const int64_t nc = (int64_t)above + eq;
-  if (nc > kCap || above >= (uint32_t)kk) {
-    // Fallback: radix select straight over the row in global memory.
-    select_keys(row, gkey, gpos, n, 0u, 0u, (uint32_t)kk, 0, kk, hist, wsum, sh);
+  if (nc > kRowCap || above >= (uint32_t)kk) {
+    select_keys<kRowThreads>(row, gkey, gpos, n, 0u, 0u, (uint32_t)kk, 0, kk, hist, wsum, shb);
     return;
   }
-
-  if (how == kSelPre) {
-    // Segment offsets (one thread per segment), then every candidate is copied
-    // independently: candidate i belongs to the last segment starting at or before i.
-    int64_t nseg_row = (n + kSeg - 1) / kSeg;
-    nseg_row = nseg_row < ws.nseg ? nseg_row : ws.nseg;
-    nseg_row = nseg_row < kFin ? nseg_row : kFin;
-    const uint32_t c = tid < nseg_row ? ws.cnt[(int64_t)r * ws.nseg + tid] : 0u;
-    uint32_t total;
-    const uint32_t o = block_excl_scan<kFin>(c, wsum, total);
-    if (tid < nseg_row) segoff[tid] = o;
-    __syncthreads();
-    const int64_t ncp = (int64_t)total < nc ? (int64_t)total : nc;
-    for (int64_t i = tid; i < ncp; i += kFin) {
-      int lo = 0, hi = (int)nseg_row - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (segoff[mid] <= (uint32_t)i) lo = mid; else hi = mid - 1;
-      }
-      cand[i] = ws.cand[((int64_t)r * ws.nseg + lo) * kSeg + (i - segoff[lo])];
-    }
-  } else {
-    // Ordered collection of the keys whose level-0 bin is >= b*.
-    uint32_t run = 0;
+  // Ordered collection of the keys whose level-0 bin is >= b*: chunks of
+  // kRounds * kRowThreads positions; round e of a chunk covers positions
+  // base + e*kRowThreads + tid (coalesced), a ballot ranks the kept ones inside
+  // each wave, and one scan over the (round, wave) counts places every wave.
+  constexpr int kRounds = 8;
+  constexpr int kW = kRowThreads / 64;
+  const int lane = tid & 63, wave = tid >> 6;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint32_t run = 0;
 #pragma unroll 1
-    for (int64_t base = 0; base < n; base += 4 * kFin) {
-      const int64_t i0 = base + 4 * tid;
-      uint32_t key[4];
-      uint32_t c = 0;
+  for (int64_t base = 0; base < n; base += (int64_t)kRounds * kRowThreads) {
+    uint32_t key[kRounds];
+    uint64_t ball[kRounds];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        key[e] = (i0 + e < n) ? gkey(i0 + e) : 0u;
-        c += (i0 + e < n && (key[e] >> kSelShift) >= bstar) ? 1u : 0u;
-      }
-      uint32_t total;
-      uint32_t pos = run + block_excl_scan<kFin>(c, wsum, total);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (i0 + e < n && (key[e] >> kSelShift) >= bstar) {
-          if (pos < (uint32_t)kCap) cand[pos] = make_uint2(key[e], (uint32_t)(i0 + e));
-          ++pos;
-        }
-      }
-      run += total;
+    for (int e = 0; e < kRounds; ++e) {
+      const int64_t i = base + (int64_t)e * kRowThreads + tid;
+      key[e] = i < n ? gkey(i) : 0u;
     }
+#pragma unroll
+    for (int e = 0; e < kRounds; ++e) {
+      const int64_t i = base + (int64_t)e * kRowThreads + tid;
+      ball[e] = __ballot(i < n && (key[e] >> kSelShift) >= bstar);
+      if (lane == 0) rcnt[e * kW + wave] = (uint32_t)__popcll(ball[e]);
+    }
+    __syncthreads();
+    uint32_t total;
+    const uint32_t cv = tid < kRounds * kW ? rcnt[tid] : 0u;
+    const uint32_t ex = block_excl_scan<kRowThreads>(cv, wsum, total);
+    if (tid < kRounds * kW) rcnt[tid] = ex;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kRounds; ++e) {
+      if ((ball[e] >> lane) & 1ull) {
+        const uint32_t pos = run + rcnt[e * kW + wave] + (uint32_t)__popcll(ball[e] & below);
+        const int64_t i = base + (int64_t)e * kRowThreads + tid;
+        if (pos < (uint32_t)kRowCap) cand[pos] = make_uint2(key[e], (uint32_t)i);
+      }
+    }
+    run += total;
+    __syncthreads();  // rcnt is reused
   }
   __syncthreads();
   auto lkey = [&](int64_t i) { return cand[i].x; };
   auto lpos = [&](int64_t i) { return (int64_t)cand[i].y; };
-  select_keys(row, lkey, lpos, nc, bstar << kSelShift, 0xFFE00000u, (uint32_t)kk - above, 1, kk, hist,
-              wsum, sh);
+  select_keys<kRowThreads>(row, lkey, lpos, nc, bstar << kSelShift, 0xFFE00000u, (uint32_t)kk - above,
+                           1, kk, hist, wsum, shb);
 }
 
-// One workgroup per (segment, row): the segment's candidates, in position
-// order.  Each thread owns 32 consecutive positions, so all loads are issued
-// before the single block scan.
-constexpr int kColPer = kSeg / kCol;
+// One workgroup per (segment, row); see the file comment.  Dynamic LDS holds
+// the last workgroup's candidates (ws.cap pairs).
+constexpr int kSegPer = kSeg / kSegThreads;  // positions per thread in a segment
 
-__global__ __launch_bounds__(kCol) void topk_collect_kernel(TopkRows a, SelWs ws) {
-  __shared__ uint32_t wsum[kCol / 64];
+__global__ __launch_bounds__(kSegThreads) void topk_segmented_kernel(TopkRows a, SelWs ws) {
+  extern __shared__ uint2 lcand[];
+  __shared__ uint32_t hist[kSelBins];
+  __shared__ uint32_t wsum[kSegThreads / 64];
+  __shared__ uint32_t segoff[kSegThreads];
   __shared__ int32_t sh[4];
   __shared__ uint32_t shb[4];
+  __shared__ int32_t sh_last;
   const int tid = threadIdx.x;
   const int r = blockIdx.y, s = blockIdx.x;
   const Row row = get_row(a, r, sh);
   const int64_t n = row.n;
-  if (n <= a.k) return;
-  const int64_t s0 = (int64_t)s * kSeg;
-  if (s0 >= n) return;
-  const int64_t s1 = (s0 + kSeg) < n ? (s0 + kSeg) : n;
-  const uint32_t* gh = ws.ghist + (int64_t)r * kSelBins;
-  block_find_bin<kCol>([&](int b) { return gh[b]; }, (uint32_t)a.k, wsum, shb);
-  const uint32_t bstar = shb[0];
-  const int64_t i0 = s0 + (int64_t)kColPer * tid;
-  uint32_t key[kColPer];
-  uint32_t flags = 0, c = 0;
-#pragma unroll
-  for (int e = 0; e < kColPer; ++e) {
-    const bool in = i0 + e < s1;
-    key[e] = in ? score_key(row.p[i0 + e]) : 0u;
-    const uint32_t f = (in && (key[e] >> kSelShift) >= bstar) ? 1u : 0u;
-    flags |= f << e;
-    c += f;
+  const int k = a.k;
+  if (n <= k) {
+    if (s == 0) keep_all<kSegThreads>(row, n, k);
+    return;
   }
-  uint32_t total;
-  uint32_t pos = block_excl_scan<kCol>(c, wsum, total);
-  uint2* dst = ws.cand + ((int64_t)r * ws.nseg + s) * kSeg;
+  int64_t nseg_row = (n + kSeg - 1) / kSeg;
+  nseg_row = nseg_row < ws.nseg ? nseg_row : ws.nseg;
+  if (s >= nseg_row) return;
+
+  // 1. Threshold bin from the row's partial histograms (16-bit, one per scan
+  //    workgroup); thread t owns the 8 bins 2047 - 8t ... 2040 - 8t, which are
+  //    16 contiguous bytes of each partial (ascending bin order).
+  constexpr int PER = kSelBins / kSegThreads;
+  int64_t nw = (n + ws.chunk - 1) / ws.chunk;
+  nw = nw < ws.nwg ? nw : ws.nwg;
+  uint32_t h[PER];
 #pragma unroll
-  for (int e = 0; e < kColPer; ++e) {
-    if ((flags >> e) & 1u) {
-      dst[pos] = make_uint2(key[e], (uint32_t)(i0 + e));
-      ++pos;
+  for (int i = 0; i < PER; ++i) h[i] = 0;
+  const uint16_t* part = ws.part + (int64_t)r * ws.nwg * kSelBins + (kSelBins - PER - tid * PER);
+  for (int64_t wgi = 0; wgi < nw; ++wgi) {
+    const i32x4 v = ld16(part + wgi * kSelBins);
+    const uint32_t w4[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int asc = PER - 1 - i;  // h[i] is bin 2047 - 8t - i, ascending slot 7 - i
+      h[i] += (w4[asc >> 1] >> (16 * (asc & 1))) & 0xFFFFu;
     }
   }
-  if (tid == 0) ws.cnt[(int64_t)r * ws.nseg + s] = total;
-}
+  find_digit<kSegThreads, PER>(h, kSelBins - 1, (uint32_t)k, wsum, shb);
+  const uint32_t bstar = shb[0], above = shb[1], eq = shb[2];
 
-// Sums the scan workgroups' 16-bit partial histograms of each row:
-// one workgroup per (256-bin slice, row).
-__global__ __launch_bounds__(256) void hist_reduce_kernel(TopkRows a, SelWs ws) {
-  __shared__ int32_t sh[4];
-  const int r = blockIdx.y;
-  const Row row = get_row(a, r, sh);
-  if (row.n <= a.k) return;
-  int64_t nw = (row.n + ws.chunk - 1) / ws.chunk;
-  nw = nw < ws.nwg ? nw : ws.nwg;
-  const int bin = blockIdx.x * 256 + threadIdx.x;
-  const uint16_t* p = ws.part + (int64_t)r * ws.nwg * kSelBins + bin;
-  uint32_t s0 = 0, s1 = 0, s2 = 0, s3 = 0;
-  int64_t w = 0;
-  for (; w + 4 <= nw; w += 4) {
-    s0 += p[(w + 0) * kSelBins];
-    s1 += p[(w + 1) * kSelBins];
-    s2 += p[(w + 2) * kSelBins];
-    s3 += p[(w + 3) * kSelBins];
+  // 2. This segment's candidates, in position order.  Round e covers
+  //    positions s0 + 256e + tid (coalesced loads); within a wave the kept
+  //    positions are ranked with a ballot, and one scan over the
+  //    (round, wave) counts gives every wave its output offset per round.
+  const int64_t s0 = (int64_t)s * kSeg;
+  const int64_t s1 = (s0 + kSeg) < n ? (s0 + kSeg) : n;
+  const int lane = tid & 63, wave = tid >> 6;
+  uint32_t key[kSegPer];
+  uint64_t ball[kSegPer];
+#pragma unroll
+  for (int e = 0; e < kSegPer; ++e) {
+    const int64_t i = s0 + (int64_t)e * kSegThreads + tid;
+    key[e] = i < s1 ? score_key(row.p[i]) : 0u;
   }
-  for (; w < nw; ++w) s0 += p[w * kSelBins];
-  ws.ghist[(int64_t)r * kSelBins + bin] = s0 + s1 + s2 + s3;
+#pragma unroll
+  for (int e = 0; e < kSegPer; ++e) {
+    const int64_t i = s0 + (int64_t)e * kSegThreads + tid;
+    ball[e] = __ballot(i < s1 && (key[e] >> kSelShift) >= bstar);
+    if (lane == 0) segoff[e * (kSegThreads / 64) + wave] = (uint32_t)__popcll(ball[e]);
+  }
+  __syncthreads();
+  uint32_t total;
+  {
+    const uint32_t v = segoff[tid];  // kSegPer * 4 = 128 (round, wave) counts
+    const uint32_t ex = block_excl_scan<kSegThreads>(tid < kSegPer * (kSegThreads / 64) ? v : 0u, wsum, total);
+    if (tid < kSegPer * (kSegThreads / 64)) segoff[tid] = ex;
+    __syncthreads();
+  }
+  // Candidates and counts are published with agent-scope atomic stores,
+  // which write through the (per-XCD, non-coherent) L2, and read back the same
+  // way by the finishing workgroup; a full __threadfence() would instead write
+  // back every dirty L2 line at each of these workgroups.
+  uint64_t* dst = reinterpret_cast<uint64_t*>(ws.cand + ((int64_t)r * ws.nseg + s) * kSeg);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int e = 0; e < kSegPer; ++e) {
+    if ((ball[e] >> lane) & 1ull) {
+      const uint32_t pos = segoff[e * (kSegThreads / 64) + wave] + (uint32_t)__popcll(ball[e] & below);
+      const int64_t i = s0 + (int64_t)e * kSegThreads + tid;
+      const uint64_t pr = (uint64_t)key[e] | ((uint64_t)(uint32_t)i << 32);
+      __hip_atomic_store(dst + pos, pr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (tid == 0)
+    __hip_atomic_store(ws.cnt + (int64_t)r * ws.nseg + s, total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();  // segoff is reused below
+
+  // 3. The last segment of the row to finish does the final selection.  The
+  //    workgroup-scope release waits for this workgroup's stores to complete
+  //    before the counter moves.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  if (tid == 0)
+    sh_last = (__hip_atomic_fetch_add(ws.done + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 ==
+               (uint32_t)nseg_row);
+  __syncthreads();
+  if (!sh_last) return;
+  if (tid == 0) __hip_atomic_store(ws.done + r, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  const int64_t kk = k;
+  const int64_t nc = (int64_t)above + eq;
+  auto gkey = [&](int64_t i) { return score_key(row.p[i]); };
+  auto gpos = [&](int64_t i) { return i; };
+  if (above >= (uint32_t)kk || nseg_row > kSegThreads) {
+    select_keys<kSegThreads>(row, gkey, gpos, n, 0u, 0u, (uint32_t)kk, 0, kk, hist, wsum, shb);
+    return;
+  }
+  // Segment offsets of the candidate lists.
+  const uint32_t cs = tid < nseg_row ? __hip_atomic_load(ws.cnt + (int64_t)r * ws.nseg + tid, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT)
+                                     : 0u;
+  uint32_t ctot;
+  const uint32_t co = block_excl_scan<kSegThreads>(cs, wsum, ctot);
+  if (tid < nseg_row) segoff[tid] = co;
+  __syncthreads();
+  const int64_t ncl = (int64_t)ctot < nc ? (int64_t)ctot : nc;
+  auto seg_of = [&](int64_t i) {
+    int lo = 0, hi = (int)nseg_row - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (segoff[mid] <= (uint32_t)i) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+  auto gcand = [&](int64_t i) {
+    const int sg = seg_of(i);
+    uint64_t* p = reinterpret_cast<uint64_t*>(ws.cand + ((int64_t)r * ws.nseg + sg) * kSeg + (i - segoff[sg]));
+    const uint64_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_uint2((uint32_t)v, (uint32_t)(v >> 32));
+  };
+  const uint32_t pfx = bstar << kSelShift, pmask = 0xFFE00000u, rem = (uint32_t)kk - above;
+  if (ncl <= ws.cap) {
+    // Batches of 8 independent loads per thread, so their latencies overlap.
+    constexpr int kBatch = 8;
+#pragma unroll 1
+    for (int64_t b0 = 0; b0 < ncl; b0 += (int64_t)kBatch * kSegThreads) {
+      uint2 v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int64_t i = b0 + (int64_t)j * kSegThreads + tid;
+        v[j] = i < ncl ? gcand(i) : make_uint2(0u, 0u);
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int64_t i = b0 + (int64_t)j * kSegThreads + tid;
+        if (i < ncl) lcand[i] = v[j];
+      }
+    }
+    __syncthreads();
+    auto lkey = [&](int64_t i) { return lcand[i].x; };
+    auto lpos = [&](int64_t i) { return (int64_t)lcand[i].y; };
+    select_keys<kSegThreads>(row, lkey, lpos, ncl, pfx, pmask, rem, 1, kk, hist, wsum, shb);
+  } else {
+    auto ckey = [&](int64_t i) { return gcand(i).x; };
+    auto cpos = [&](int64_t i) { return (int64_t)gcand(i).y; };
+    select_keys<kSegThreads>(row, ckey, cpos, ncl, pfx, pmask, rem, 1, kk, hist, wsum, shb);
+  }
 }
 
 }  // namespace
 
-hipError_t launch_hist_reduce(const TopkRows& a, const SelWs& ws, hipStream_t stream) {
-  if (a.rows <= 0) return hipSuccess;
-  hist_reduce_kernel<<<dim3(kSelBins / 256, (unsigned)a.rows), dim3(256), 0, stream>>>(a, ws);
-  return hipGetLastError();
+int32_t seg_cap_for(int32_t k) {
+  const int64_t cap = 2 * (int64_t)k + 2048;
+  return (int32_t)(cap < kSegMaxCap ? cap : kSegMaxCap);
 }
 
-hipError_t launch_topk_collect(const TopkRows& a, const SelWs& ws, hipStream_t stream) {
-  if (a.rows <= 0 || ws.nseg <= 0) return hipSuccess;
-  topk_collect_kernel<<<dim3((unsigned)ws.nseg, (unsigned)a.rows), dim3(kCol), 0, stream>>>(a, ws);
-  return hipGetLastError();
-}
-
-hipError_t launch_topk_pre(const TopkRows& a, const SelWs& ws, hipStream_t stream) {
+hipError_t launch_topk_segmented(const TopkRows& a, const SelWs& ws, hipStream_t stream) {
   if (a.rows <= 0) return hipSuccess;
-  topk_final_kernel<<<dim3((unsigned)a.rows), dim3(kFin), 0, stream>>>(a, ws, kSelPre);
+  const int nseg = ws.nseg > 0 ? ws.nseg : 1;
+  // Allow dynamic LDS beyond the default 64 KB limit (up to kSegMaxCap pairs).
+  static bool lds_set = false;
+  if (!lds_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)topk_segmented_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       kSegMaxCap * (int)sizeof(uint2));
+    if (e != hipSuccess) return e;
+    lds_set = true;
+  }
+  topk_segmented_kernel<<<dim3((unsigned)nseg, (unsigned)a.rows), dim3(kSegThreads),
+                          (size_t)ws.cap * sizeof(uint2), stream>>>(a, ws);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_self(const TopkRows& a, const SelWs& ws, hipStream_t stream) {
   if (a.rows <= 0) return hipSuccess;
-  topk_final_kernel<<<dim3((unsigned)a.rows), dim3(kFin), 0, stream>>>(a, ws, kSelSelf);
+  topk_row_kernel<<<dim3((unsigned)a.rows), dim3(kRowThreads), 0, stream>>>(a, ws, kSelSelf);
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const TopkRows& a, hipStream_t stream) {
   if (a.rows <= 0) return hipSuccess;
   SelWs none = {};
-  topk_final_kernel<<<dim3((unsigned)a.rows), dim3(kFin), 0, stream>>>(a, none, kSelFull);
+  topk_row_kernel<<<dim3((unsigned)a.rows), dim3(kRowThreads), 0, stream>>>(a, none, kSelFull);
   return hipGetLastError();
 }
 
