@@ -31,10 +31,9 @@
 namespace li {
 namespace {
 
-constexpr int kRowThreads = 1024;  // per-row kernel
-constexpr int kRowCap = 12288;     // LDS candidates of the per-row kernel
-constexpr int kSegThreads = 256;   // segmented kernel
-constexpr int kSegMaxCap = 12288;  // largest LDS candidate buffer of the segmented kernel
+constexpr int kRowThreads = 512;   // per-row kernel
+constexpr int kSegThreads = 512;   // segmented kernel
+constexpr int kMaxCap = 12288;     // largest LDS candidate buffer (pairs) of either kernel
 
 struct Row {
   const float* p;
@@ -92,6 +91,14 @@ __device__ Row get_row(const TopkRows& a, int r, int32_t* sh) {
 
 __device__ __forceinline__ int32_t map_pos(const Row& row, int64_t i) {
   return row.map ? row.map[i] : (int32_t)i;
+}
+
+// Key of element i of p[0 .. n-1] (n >= 1), loaded without a branch: an index
+// past the end reads element n-1 instead, and the caller ignores that key.
+// (A load under a branch makes the compiler wait for it before the branch
+// joins, which serialises a batch of loads.)
+__device__ __forceinline__ uint32_t key_clamped(const float* p, int64_t i, int64_t n) {
+  return score_key(p[i < n ? i : n - 1]);
 }
 
 // Writes all n visible positions and pads the row with -1 (rows with n <= k).
@@ -220,11 +227,14 @@ enum SelHow : int32_t { kSelSelf = 1, kSelFull = 2 };
 
 // One workgroup per row.  kSelSelf: the row's level-0 threshold is in ws.thr
 // (prefill scan).  kSelFull: the workgroup builds the histogram itself.
-__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkRows a, SelWs ws, int how) {
-  __shared__ uint2 cand[kRowCap];
+// Dynamic LDS holds `cap` candidate pairs.
+__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkRows a, SelWs ws, int how, int cap) {
+  extern __shared__ uint2 cand[];
   __shared__ uint32_t hist[kSelBins];
-  __shared__ uint32_t rcnt[8 * (kRowThreads / 64)];
-  __shared__ uint32_t wsum[kRowThreads / 64];
+  constexpr int kRounds = 16;  // collection rounds per chunk
+  constexpr int kW = kRowThreads / 64;
+  __shared__ uint32_t rcnt[kRounds * kW];
+  __shared__ uint32_t wsum[kW];
   __shared__ int32_t sh[4];
   __shared__ uint32_t shb[4];
   const int tid = threadIdx.x;
@@ -251,7 +261,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkRows a, SelWs
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int64_t i = b0 + (int64_t)j * kRowThreads + tid;
-        kb[j] = i < n ? gkey(i) : 0u;
+        kb[j] = key_clamped(row.p, i, n);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j)
@@ -273,7 +283,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkRows a, SelWs
     eq = t[2];
   }
   const int64_t nc = (int64_t)above + eq;
-  if (nc > kRowCap || above >= (uint32_t)kk) {
+  if (nc > cap || above >= (uint32_t)kk) {
     select_keys<kRowThreads>(row, gkey, gpos, n, 0u, 0u, (uint32_t)kk, 0, kk, hist, wsum, shb);
     return;
   }
@@ -281,20 +291,25 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkRows a, SelWs
   // kRounds * kRowThreads positions; round e of a chunk covers positions
   // base + e*kRowThreads + tid (coalesced), a ballot ranks the kept ones inside
   // each wave, and one scan over the (round, wave) counts places every wave.
-  constexpr int kRounds = 8;
-  constexpr int kW = kRowThreads / 64;
   const int lane = tid & 63, wave = tid >> 6;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   uint32_t run = 0;
-#pragma unroll 1
-  for (int64_t base = 0; base < n; base += (int64_t)kRounds * kRowThreads) {
-    uint32_t key[kRounds];
-    uint64_t ball[kRounds];
+  // The next chunk's keys are loaded while this one is ranked and stored.
+  uint32_t key[kRounds], nkey[kRounds];
+  auto load_chunk = [&](uint32_t (&dst)[kRounds], int64_t base) {
 #pragma unroll
     for (int e = 0; e < kRounds; ++e) {
       const int64_t i = base + (int64_t)e * kRowThreads + tid;
-      key[e] = i < n ? gkey(i) : 0u;
+      dst[e] = key_clamped(row.p, i, n);
     }
+  };
+  load_chunk(nkey, 0);
+#pragma unroll 1
+  for (int64_t base = 0; base < n; base += (int64_t)kRounds * kRowThreads) {
+    uint64_t ball[kRounds];
+#pragma unroll
+    for (int e = 0; e < kRounds; ++e) key[e] = nkey[e];
+    load_chunk(nkey, base + (int64_t)kRounds * kRowThreads);
 #pragma unroll
     for (int e = 0; e < kRounds; ++e) {
       const int64_t i = base + (int64_t)e * kRowThreads + tid;
@@ -303,6 +318,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkRows a, SelWs
     }
     __syncthreads();
     uint32_t total;
+    static_assert(kRounds * kW <= kRowThreads, "one (round, wave) count per thread");
     const uint32_t cv = tid < kRounds * kW ? rcnt[tid] : 0u;
     const uint32_t ex = block_excl_scan<kRowThreads>(cv, wsum, total);
     if (tid < kRounds * kW) rcnt[tid] = ex;
@@ -312,7 +328,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkRows a, SelWs
       if ((ball[e] >> lane) & 1ull) {
         const uint32_t pos = run + rcnt[e * kW + wave] + (uint32_t)__popcll(ball[e] & below);
         const int64_t i = base + (int64_t)e * kRowThreads + tid;
-        if (pos < (uint32_t)kRowCap) cand[pos] = make_uint2(key[e], (uint32_t)i);
+        if (pos < (uint32_t)cap) cand[pos] = make_uint2(key[e], (uint32_t)i);
       }
     }
     run += total;
@@ -350,54 +366,72 @@ __global__ __launch_bounds__(kSegThreads) void topk_segmented_kernel(TopkRows a,
   nseg_row = nseg_row < ws.nseg ? nseg_row : ws.nseg;
   if (s >= nseg_row) return;
 
+  // The segment's scores are loaded first: their latency overlaps the
+  // reduction of the partial histograms below.  Round e covers positions
+  // s0 + NT*e + tid (coalesced).
+  const int64_t s0 = (int64_t)s * kSeg;
+  const int64_t s1 = (s0 + kSeg) < n ? (s0 + kSeg) : n;
+  const int lane = tid & 63, wave = tid >> 6;
+  constexpr int kW = kSegThreads / 64;
+  uint32_t key[kSegPer];
+#pragma unroll
+  for (int e = 0; e < kSegPer; ++e) {
+    const int64_t i = s0 + (int64_t)e * kSegThreads + tid;
+    key[e] = key_clamped(row.p, i, s1);
+  }
+
   // 1. Threshold bin from the row's partial histograms (16-bit, one per scan
-  //    workgroup); thread t owns the 8 bins 2047 - 8t ... 2040 - 8t, which are
-  //    16 contiguous bytes of each partial (ascending bin order).
+  //    workgroup); thread t owns the 4 bins 2047 - 4t ... 2044 - 4t, which are
+  //    8 contiguous bytes of each partial (ascending bin order).  Loads go out
+  //    in batches of 8 partials.
   constexpr int PER = kSelBins / kSegThreads;
+  static_assert(PER == 4, "one 8-byte slice of each partial per thread");
   int64_t nw = (n + ws.chunk - 1) / ws.chunk;
   nw = nw < ws.nwg ? nw : ws.nwg;
   uint32_t h[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) h[i] = 0;
   const uint16_t* part = ws.part + (int64_t)r * ws.nwg * kSelBins + (kSelBins - PER - tid * PER);
-  for (int64_t wgi = 0; wgi < nw; ++wgi) {
-    const i32x4 v = ld16(part + wgi * kSelBins);
-    const uint32_t w4[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
+  constexpr int kPB = 8;
+#pragma unroll 1
+  for (int64_t w0 = 0; w0 < nw; w0 += kPB) {
+    i32x2 v[kPB];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int asc = PER - 1 - i;  // h[i] is bin 2047 - 8t - i, ascending slot 7 - i
-      h[i] += (w4[asc >> 1] >> (16 * (asc & 1))) & 0xFFFFu;
+    for (int j = 0; j < kPB; ++j) {
+      const int64_t wj = (w0 + j < nw) ? w0 + j : nw - 1;  // branch-free; repeats are dropped below
+      v[j] = *reinterpret_cast<const i32x2*>(part + wj * kSelBins);
+    }
+#pragma unroll
+    for (int j = 0; j < kPB; ++j) {
+      const bool in = w0 + j < nw;
+      const uint32_t lo = in ? (uint32_t)v[j].x : 0u, hi = in ? (uint32_t)v[j].y : 0u;
+      // ascending slots 0..3 = bins 2044-4t .. 2047-4t; h[i] is bin 2047-4t-i
+      h[0] += hi >> 16;
+      h[1] += hi & 0xFFFFu;
+      h[2] += lo >> 16;
+      h[3] += lo & 0xFFFFu;
     }
   }
   find_digit<kSegThreads, PER>(h, kSelBins - 1, (uint32_t)k, wsum, shb);
   const uint32_t bstar = shb[0], above = shb[1], eq = shb[2];
 
-  // 2. This segment's candidates, in position order.  Round e covers
-  //    positions s0 + 256e + tid (coalesced loads); within a wave the kept
-  //    positions are ranked with a ballot, and one scan over the
-  //    (round, wave) counts gives every wave its output offset per round.
-  const int64_t s0 = (int64_t)s * kSeg;
-  const int64_t s1 = (s0 + kSeg) < n ? (s0 + kSeg) : n;
-  const int lane = tid & 63, wave = tid >> 6;
-  uint32_t key[kSegPer];
+  // 2. This segment's candidates, in position order: within a wave the kept
+  //    positions are ranked with a ballot, and one scan over the (round, wave)
+  //    counts gives every wave its output offset per round.
   uint64_t ball[kSegPer];
 #pragma unroll
   for (int e = 0; e < kSegPer; ++e) {
     const int64_t i = s0 + (int64_t)e * kSegThreads + tid;
-    key[e] = i < s1 ? score_key(row.p[i]) : 0u;
-  }
-#pragma unroll
-  for (int e = 0; e < kSegPer; ++e) {
-    const int64_t i = s0 + (int64_t)e * kSegThreads + tid;
     ball[e] = __ballot(i < s1 && (key[e] >> kSelShift) >= bstar);
-    if (lane == 0) segoff[e * (kSegThreads / 64) + wave] = (uint32_t)__popcll(ball[e]);
+    if (lane == 0) segoff[e * kW + wave] = (uint32_t)__popcll(ball[e]);
   }
   __syncthreads();
   uint32_t total;
   {
-    const uint32_t v = segoff[tid];  // kSegPer * 4 = 128 (round, wave) counts
-    const uint32_t ex = block_excl_scan<kSegThreads>(tid < kSegPer * (kSegThreads / 64) ? v : 0u, wsum, total);
-    if (tid < kSegPer * (kSegThreads / 64)) segoff[tid] = ex;
+    static_assert(kSegPer * kW <= kSegThreads, "one (round, wave) count per thread");
+    const uint32_t v = tid < kSegPer * kW ? segoff[tid] : 0u;
+    const uint32_t ex = block_excl_scan<kSegThreads>(v, wsum, total);
+    if (tid < kSegPer * kW) segoff[tid] = ex;
     __syncthreads();
   }
   // Candidates and counts are published with agent-scope atomic stores,
@@ -409,7 +443,7 @@ __global__ __launch_bounds__(kSegThreads) void topk_segmented_kernel(TopkRows a,
 #pragma unroll
   for (int e = 0; e < kSegPer; ++e) {
     if ((ball[e] >> lane) & 1ull) {
-      const uint32_t pos = segoff[e * (kSegThreads / 64) + wave] + (uint32_t)__popcll(ball[e] & below);
+      const uint32_t pos = segoff[e * kW + wave] + (uint32_t)__popcll(ball[e] & below);
       const int64_t i = s0 + (int64_t)e * kSegThreads + tid;
       const uint64_t pr = (uint64_t)key[e] | ((uint64_t)(uint32_t)i << 32);
       __hip_atomic_store(dst + pos, pr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -464,15 +498,29 @@ __global__ __launch_bounds__(kSegThreads) void topk_segmented_kernel(TopkRows a,
   };
   const uint32_t pfx = bstar << kSelShift, pmask = 0xFFE00000u, rem = (uint32_t)kk - above;
   if (ncl <= ws.cap) {
-    // Batches of 8 independent loads per thread, so their latencies overlap.
-    constexpr int kBatch = 8;
+    // Batches of kBatch independent loads per thread, so their latencies
+    // overlap.  A thread's positions only grow, so its segment is tracked with
+    // a cursor that moves forward (next segment start cached in a register).
+    constexpr int kBatch = 16;
+    int sg = seg_of(tid < ncl ? tid : ncl - 1);
+    uint32_t cur = segoff[sg];
+    uint32_t nxt = sg + 1 < nseg_row ? segoff[sg + 1] : 0xFFFFFFFFu;
 #pragma unroll 1
     for (int64_t b0 = 0; b0 < ncl; b0 += (int64_t)kBatch * kSegThreads) {
       uint2 v[kBatch];
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
+        // Clamped to the last candidate (branch-free load; repeats are not stored).
         const int64_t i = b0 + (int64_t)j * kSegThreads + tid;
-        v[j] = i < ncl ? gcand(i) : make_uint2(0u, 0u);
+        const uint32_t ic = (uint32_t)(i < ncl ? i : ncl - 1);
+        while (ic >= nxt) {
+          ++sg;
+          cur = nxt;
+          nxt = sg + 1 < nseg_row ? segoff[sg + 1] : 0xFFFFFFFFu;
+        }
+        uint64_t* p = reinterpret_cast<uint64_t*>(ws.cand + ((int64_t)r * ws.nseg + sg) * kSeg + (ic - cur));
+        const uint64_t x = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v[j] = make_uint2((uint32_t)x, (uint32_t)(x >> 32));
       }
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
@@ -495,37 +543,46 @@ __global__ __launch_bounds__(kSegThreads) void topk_segmented_kernel(TopkRows a,
 
 int32_t seg_cap_for(int32_t k) {
   const int64_t cap = 2 * (int64_t)k + 2048;
-  return (int32_t)(cap < kSegMaxCap ? cap : kSegMaxCap);
+  return (int32_t)(cap < kMaxCap ? cap : kMaxCap);
+}
+
+// Dynamic LDS beyond the default 64 KB needs a one-time opt-in per kernel.
+template <typename K>
+hipError_t allow_lds(K kernel, bool& done) {
+  if (done) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     kMaxCap * (int)sizeof(uint2));
+  if (e == hipSuccess) done = true;
+  return e;
 }
 
 hipError_t launch_topk_segmented(const TopkRows& a, const SelWs& ws, hipStream_t stream) {
   if (a.rows <= 0) return hipSuccess;
   const int nseg = ws.nseg > 0 ? ws.nseg : 1;
-  // Allow dynamic LDS beyond the default 64 KB limit (up to kSegMaxCap pairs).
   static bool lds_set = false;
-  if (!lds_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)topk_segmented_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       kSegMaxCap * (int)sizeof(uint2));
-    if (e != hipSuccess) return e;
-    lds_set = true;
-  }
+  if (hipError_t e = allow_lds(topk_segmented_kernel, lds_set)) return e;
   topk_segmented_kernel<<<dim3((unsigned)nseg, (unsigned)a.rows), dim3(kSegThreads),
                           (size_t)ws.cap * sizeof(uint2), stream>>>(a, ws);
   return hipGetLastError();
 }
 
-hipError_t launch_topk_self(const TopkRows& a, const SelWs& ws, hipStream_t stream) {
+static hipError_t launch_row(const TopkRows& a, const SelWs& ws, int how, hipStream_t stream) {
   if (a.rows <= 0) return hipSuccess;
-  topk_row_kernel<<<dim3((unsigned)a.rows), dim3(kRowThreads), 0, stream>>>(a, ws, kSelSelf);
+  static bool lds_set = false;
+  if (hipError_t e = allow_lds(topk_row_kernel, lds_set)) return e;
+  const int cap = seg_cap_for(a.k);
+  topk_row_kernel<<<dim3((unsigned)a.rows), dim3(kRowThreads), (size_t)cap * sizeof(uint2), stream>>>(
+      a, ws, how, cap);
   return hipGetLastError();
 }
 
+hipError_t launch_topk_self(const TopkRows& a, const SelWs& ws, hipStream_t stream) {
+  return launch_row(a, ws, kSelSelf, stream);
+}
+
 hipError_t launch_topk(const TopkRows& a, hipStream_t stream) {
-  if (a.rows <= 0) return hipSuccess;
   SelWs none = {};
-  topk_row_kernel<<<dim3((unsigned)a.rows), dim3(kRowThreads), 0, stream>>>(a, none, kSelFull);
-  return hipGetLastError();
+  return launch_row(a, none, kSelFull, stream);
 }
 
 }  // namespace li
