@@ -58,76 +58,120 @@ __device__ void wave_find_bin(const uint32_t* hist, uint32_t kk, uint32_t* thr) 
   }
 }
 
+constexpr int kPfStages = 3;  // key tiles per wave in the register ring
+
 __global__ __launch_bounds__(256) void prefill_score_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ kc, const float* __restrict__ k_scale, int T, int L, int qpos0,
     int H, int k, int fill_masked, float* __restrict__ scores, uint32_t* __restrict__ thr) {
   __shared__ uint32_t phist[kPfWaves][kPfTokPerWave][kSelBins];
+  // Head weights of the block's tokens.  In the MFMA result a lane holds heads
+  // 8*(r/4) + 4*g + r%4 (+32 per row block): every lane of a half reads the
+  // same four consecutive weights, so these reads are LDS broadcasts.
+  __shared__ float wsh[kPfTokPerBlock][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 31, g = lane >> 5;
   const int t_base = (blockIdx.x * kPfWaves + wave) * kPfTokPerWave;
-  for (int i = lane; i < kPfTokPerWave * kSelBins; i += 64) (&phist[wave][0][0])[i] = 0;
-  __syncthreads();
   const int nt = t_base >= T ? 0 : ((T - t_base) < kPfTokPerWave ? (T - t_base) : kPfTokPerWave);
+  // Token slot tk computes row trow[tk]; slots past the end of the chunk
+  // repeat the wave's first token (so their stores rewrite identical values)
+  // and are never counted in a histogram.
+  int trow[kPfTokPerWave];
+#pragma unroll
+  for (int tk = 0; tk < kPfTokPerWave; ++tk) trow[tk] = nt > 0 ? t_base + (tk < nt ? tk : 0) : 0;
+
+  for (int i = lane; i < kPfTokPerWave * kSelBins; i += 64) (&phist[wave][0][0])[i] = 0;
+#pragma unroll
+  for (int tk = 0; tk < kPfTokPerWave; ++tk)
+    wsh[wave * kPfTokPerWave + tk][lane] = lane < H ? w[(int64_t)trow[tk] * H + lane] : 0.0f;
 
   i32x8 qa[kPfTokPerWave][2][2];
-  float wl[kPfTokPerWave][2][16];
   float sq[kPfTokPerWave];
 #pragma unroll
   for (int tk = 0; tk < kPfTokPerWave; ++tk) {
-    const int t = nt > 0 ? t_base + (tk < nt ? tk : 0) : 0;  // always a valid row
-    sq[tk] = q_scale ? q_scale[t] : 1.0f;
+    sq[tk] = q_scale ? q_scale[trow[tk]] : 1.0f;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const int row = hb * 32 + col;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         i32x8 v = {};
-        if (row < H) v = ld32(q + ((int64_t)t * H + row) * 128 + 64 * g + 32 * j);
+        if (row < H) v = ld32(q + ((int64_t)trow[tk] * H + row) * 128 + 64 * g + 32 * j);
         qa[tk][hb][j] = v;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int head = hb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        wl[tk][hb][r] = head < H ? w[(int64_t)t * H + head] : 0.0f;
       }
     }
   }
+  __syncthreads();
 
   const int vis_end = qpos0 + t_base + nt;  // exclusive end of the last token's visible range
   const int n_tiles = nt > 0 ? (vis_end + 31) / 32 : 0;
   const uint8_t* kbase = kc + 64 * g;
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int s = kt * 32 + col;
-    const int srow = s < L ? s : L - 1;
-    const i32x8 kb0 = ld32(kbase + (int64_t)srow * 128);
-    const i32x8 kb1 = ld32(kbase + (int64_t)srow * 128 + 32);
-    const float sk = k_scale ? k_scale[srow] : 1.0f;
+  // Key row of tile `it` for this lane, clamped into the cache: a lane past
+  // the end recomputes row L-1 and rewrites that row's own score.
+  auto key_row = [&](int it) {
+    const int s = it * 32 + col;
+    return s < L ? s : L - 1;
+  };
+  auto load_tile = [&](i32x8 (&kb)[2], float& sk, int it) {
+    const int srow = key_row(it);
+    const uint8_t* p = kbase + (int64_t)srow * 128;
+    kb[0] = ld32(p);
+    kb[1] = ld32(p + 32);
+    sk = k_scale ? k_scale[srow] : 1.0f;
+  };
+  auto compute = [&](const i32x8 (&kb)[2], float sk, int it, bool live) {
+    const int s = it * 32 + col;
+    const int srow = key_row(it);
+    f32x16 acc[kPfTokPerWave][2];
 #pragma unroll
     for (int tk = 0; tk < kPfTokPerWave; ++tk) {
-      if (tk < nt) {
-        f32x16 a0 = {}, a1 = {};
-        a0 = mfma_fp8(qa[tk][0][0], kb0, a0);
-        a1 = mfma_fp8(qa[tk][1][0], kb0, a1);
-        a0 = mfma_fp8(qa[tk][0][1], kb1, a0);
-        a1 = mfma_fp8(qa[tk][1][1], kb1, a1);
-        float part = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          part = fmaf(wl[tk][0][r], relu(a0[r]), part);
-          part = fmaf(wl[tk][1][r], relu(a1[r]), part);
+      for (int hb = 0; hb < 2; ++hb) {
+        f32x16 a = {};
+        a = mfma_fp8(qa[tk][hb][0], kb[0], a);
+        acc[tk][hb] = mfma_fp8(qa[tk][hb][1], kb[1], a);
+      }
+    }
+#pragma unroll
+    for (int tk = 0; tk < kPfTokPerWave; ++tk) {
+      const float* wt = &wsh[wave * kPfTokPerWave + tk][4 * g];
+      float part = 0.0f;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 wv = *reinterpret_cast<const f32x4*>(wt + hb * 32 + 8 * r4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) part = fmaf(wv[i], relu(acc[tk][hb][4 * r4 + i]), part);
         }
-        part = sum_halves(part);
-        const int t = t_base + tk;
-        if (g == 0 && s < L) {
-          if (s <= qpos0 + t) {
-            const float val = part * sq[tk] * sk;
-            scores[(int64_t)t * L + s] = val;
-            atomicAdd(&phist[wave][tk][score_key(val) >> kSelShift], 1u);
-          } else {
-            scores[(int64_t)t * L + s] = -INFINITY;
-          }
-        }
+      }
+      part = sum_halves(part);
+      const int t = trow[tk];
+      const bool vis = srow <= qpos0 + t;
+      const float val = vis ? part * sq[tk] * sk : -INFINITY;
+      // Straight-line store (both halves write the same value) so the loads
+      // of the next tiles stay in flight.
+      scores[(int64_t)t * L + srow] = val;
+      // (an LDS-only branch)
+      if (live && tk < nt && g == 0 && s < L && vis)
+        atomicAdd(&phist[wave][tk][score_key(val) >> kSelShift], 1u);
+    }
+  };
+
+  if (n_tiles > 0) {
+    i32x8 buf[kPfStages][2];
+    float skb[kPfStages];
+#pragma unroll
+    for (int st = 0; st < kPfStages - 1; ++st) load_tile(buf[st], skb[st], st < n_tiles ? st : n_tiles - 1);
+    const int nit = (n_tiles + kPfStages - 1) / kPfStages * kPfStages;
+    for (int base = 0; base < nit; base += kPfStages) {
+#pragma unroll
+      for (int st = 0; st < kPfStages; ++st) {
+        const int it = base + st;
+        const int nx = it + kPfStages - 1;
+        load_tile(buf[(st + kPfStages - 1) % kPfStages], skb[(st + kPfStages - 1) % kPfStages],
+                  nx < n_tiles ? nx : n_tiles - 1);
+        compute(buf[st], skb[st], it < n_tiles ? it : n_tiles - 1, it < n_tiles);
       }
     }
   }
