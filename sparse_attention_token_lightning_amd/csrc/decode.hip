@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
   const int64_t off = kv_off[b];
   const int64_t L = kv_off[b + 1] - off;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = wave_id();
   const int col = lane & 31, g = lane >> 5;
   const int64_t chunk = (int64_t)kDecWaves * tiles_per_wave * kTile;
   const int64_t wg0 = (int64_t)blockIdx.x * chunk;
@@ -73,15 +73,18 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
     const int row = hb * 32 + col;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      i32x4 v = {0, 0, 0, 0};
-      if (row < H) v = ld16(q + ((int64_t)b * H + row) * 128 + 64 * g + 8 * j);
+      // Clamped, unconditional load (rows past H are zeroed afterwards): a
+      // load under a branch would be waited for before the next one issues.
+      i32x4 v = ld16(q + ((int64_t)b * H + (row < H ? row : H - 1)) * 128 + 64 * g + 8 * j);
+      if (row >= H) v = i32x4{0, 0, 0, 0};
       qa[hb][j] = __builtin_bit_cast(bf16x8, v);
     }
     // The heads whose results this lane holds: rows 8*(r/4) + 4*g + r%4 of the block.
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int head = hb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-      wl[hb][r] = head < H ? w[(int64_t)b * H + head] : 0.0f;
+      const float wv = w[(int64_t)b * H + (head < H ? head : H - 1)];
+      wl[hb][r] = head < H ? wv : 0.0f;
     }
   }
   __syncthreads();

@@ -156,17 +156,19 @@ __global__ __launch_bounds__(256) void latent_score_kernel(
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const int row = hb * 32 + col;
-      const uint16_t* qp = qt16 + (((int64_t)b * G + l) * H + row) * DC + HALF * g;
+      // Clamped, unconditional loads (rows past H are zeroed afterwards).
+      const uint16_t* qp = qt16 + (((int64_t)b * G + l) * H + (row < H ? row : H - 1)) * DC + HALF * g;
 #pragma unroll
       for (int j = 0; j < KSTEPS; ++j) {
-        i32x4 v = {0, 0, 0, 0};
-        if (row < H) v = ld16(qp + 8 * j);
+        i32x4 v = ld16(qp + 8 * j);
+        if (row >= H) v = i32x4{0, 0, 0, 0};
         qa[hb][j] = __builtin_bit_cast(f16x8, v);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int head = hb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        wl[hb][r] = head < H ? wsc[((int64_t)b * G + l) * H + head] : 0.0f;
+        const float wv = wsc[((int64_t)b * G + l) * H + (head < H ? head : H - 1)];
+        wl[hb][r] = head < H ? wv : 0.0f;
       }
     }
   }

@@ -109,6 +109,8 @@ size_t decode_ws(int32_t B, int64_t n_tok, int32_t max_len, bool scores_given) {
 size_t prefill_ws(int32_t T, int32_t L, bool scores_given) {
   size_t s = 0;
   if (!scores_given) s += align_up((size_t)T * (size_t)L * 4);
+  const size_t rows = T > 0 ? (size_t)T : 0;
+  s += align_up(rows * li::kLinRows * 128) + align_up(rows * li::kLinRows * 4);
   s += sel_ws(T > 0 ? T : 0, 0, 0);
   return s;
 }
@@ -248,10 +250,15 @@ li_status li_index_prefill(const void* q, li_dtype q_dt, const float* q_scale, c
   trace_begin(s);
   Carver cv(ws);
   float* scores = out_scores ? out_scores : (float*)cv.take((size_t)T * (size_t)L * 4);
+  uint8_t* uq = (uint8_t*)cv.take((size_t)T * li::kLinRows * 128);
+  float* usc = (float*)cv.take((size_t)T * li::kLinRows * 4);
   const li::SelWs sel = carve_sel(cv, T, 0, 0, k);
-  if ((st = hip_check(li::launch_prefill_score((const uint8_t*)q, q_scale, w, (const uint8_t*)k_cache,
-                                               k_scale, T, L, qpos0, H, k, out_scores != nullptr,
-                                               scores, sel, s),
+  if ((st = hip_check(li::launch_prefill_linear((const uint8_t*)q, w, T, H, uq, usc, s),
+                      "prefill_linear launch", s)))
+    return st;
+  if ((st = hip_check(li::launch_prefill_score((const uint8_t*)q, q_scale, w, uq, usc,
+                                               (const uint8_t*)k_cache, k_scale, T, L, qpos0, H, k,
+                                               out_scores != nullptr, scores, sel, s),
                       "prefill_score launch", s)))
     return st;
   li::TopkRows tr = {};

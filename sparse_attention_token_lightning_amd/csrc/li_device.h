@@ -20,6 +20,12 @@ typedef __attribute__((ext_vector_type(2))) int i32x2;
 
 constexpr int kWave = 64;
 
+// Index of the calling wavefront in its workgroup, as a wave-uniform (scalar)
+// value: the compiler cannot prove threadIdx.x >> 6 is uniform, and loops
+// bounded by values derived from it would otherwise run under an exec mask,
+// with conservative waits for every outstanding load.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 // 16-byte global load / store through a plain vector type.
 __device__ __forceinline__ i32x4 ld16(const void* p) { return *reinterpret_cast<const i32x4*>(p); }
 

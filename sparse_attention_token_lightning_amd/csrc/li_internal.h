@@ -57,10 +57,16 @@ hipError_t launch_decode_score(const uint16_t* q, const float* w, const void* kc
 // Prefill scan: scores[t][s] for s <= qpos0 + t; with fill_masked also -inf
 // for the masked rest of every row.  Rows with more than k visible keys get
 // their threshold bin in sel.thr.
+// Prefill: u = sum_h w_h q_hat_h per token as kLinRows fp8 rows + scales
+// (uq [T][4][128] bytes, usc [T][4]), then the causal scan.
+constexpr int kLinRows = 4;
+hipError_t launch_prefill_linear(const uint8_t* q, const float* w, int32_t T, int32_t H, uint8_t* uq,
+                                 float* usc, hipStream_t stream);
 hipError_t launch_prefill_score(const uint8_t* q, const float* q_scale, const float* w,
-                                const uint8_t* kc, const float* k_scale, int32_t T, int32_t L,
-                                int32_t qpos0, int32_t H, int32_t k, bool fill_masked,
-                                float* scores, const SelWs& sel, hipStream_t stream);
+                                const uint8_t* uq, const float* usc, const uint8_t* kc,
+                                const float* k_scale, int32_t T, int32_t L, int32_t qpos0, int32_t H,
+                                int32_t k, bool fill_masked, float* scores, const SelWs& sel,
+                                hipStream_t stream);
 
 // Latent absorption: qt16[b][l][h][Dc] (fp16, range-scaled by 2^e per row) and
 // wsc[b][l][h] = w * 2^-e.

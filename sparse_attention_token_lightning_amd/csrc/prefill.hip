@@ -4,16 +4,29 @@
 //   S[t][s] = q_scale[t] * k_scale[s] * sum_h w[t][h] * ReLU(q_hat[t][h] . k_hat[s]),
 //   visible iff s <= qpos0 + t
 //
-// This is a real dense contraction (M = T*64 query-head rows, N = L keys,
-// K = 128) with fp8 operands, so it runs on the fp8 matrix cores
-// (v_mfma_f32_32x32x64_f8f6f4, OCP E4M3 for both operands), with the
-// ReLU-weighted head reduction, the two scales and the causal mask fused into
-// the epilogue; fully masked key tiles are never computed.
+// This is a dense contraction (M = T*64 query-head rows, N = L keys, K = 128)
+// with fp8 operands, so it runs on the fp8 matrix cores
+// (v_mfma_f32_32x32x64_f8f6f4, OCP E4M3 for both operands); fully masked key
+// tiles are never computed.
 //
-// Mapping: a wave owns two query tokens (2 x 64 heads = four 32-row M blocks,
-// held in registers) and walks the visible keys 32 at a time.  Lane l works on
-// key (l & 31) and dims 64*(l >> 5) .. +63 of it; the head sum is finished in
-// registers plus one cross-half shuffle, as in the decode scan.
+// The epilogue is the expensive part: every (head, key) product needs a ReLU
+// and a weighted add, which on the vector ALU costs as much time as the MFMA
+// that produced it.  It is halved with the identity
+//   sum_h w_h ReLU(x_h) = 1/2 * ( sum_h w_h |x_h|  +  sum_h w_h x_h ):
+// the first sum is one FMA per element (|x| is a free source modifier), and
+// the second is linear in the key,
+//   sum_h w_h x_h = u . k_hat,   u = sum_h w_h q_hat_h,
+// so it runs on the matrix cores as a few extra MFMA rows.  u is stored as
+// four fp8 rows f_i with power-of-two scales, u ~= sum_i 2^e_i f_i, each row
+// encoding what the previous rows left over (relative residual ~2^-16; the
+// tolerance on a score is 2e-3 of sum_h |w_h x_h|).
+//
+// Mapping: a wave owns two query tokens: four 32-row M blocks of heads plus
+// one block holding both tokens' u rows (rows 4*slot + i), all in registers,
+// and walks the visible keys 32 at a time.  Lane l works on key (l & 31) and
+// dims 64*(l >> 5) .. +63 of it.  After the MFMAs, lane half g finishes token
+// slot g: it adds its half of the |x| sum to the other half's (one shuffle),
+// takes u . k from the u rows it holds (rows 4g .. 4g+3), and stores.
 //
 // A wave owns whole rows, so it also builds each row's level-0 selection
 // histogram in LDS and finds the row's threshold bin for the top-k itself.
@@ -38,16 +51,29 @@ __device__ __forceinline__ i32x8 ld32(const uint8_t* p) {
   return r;
 }
 
+// Row histograms are packed two 16-bit bins per 32-bit word (bin b in the
+// half b & 1 of word b >> 1) to halve their LDS footprint.  A bin that passes
+// 65535 carries into its neighbour or wraps, so the bins then no longer sum to
+// the row's visible count; that is detected here and the row is marked for
+// the top-k kernel to rebuild its histogram itself (thr[3] = 0).
+__device__ __forceinline__ uint32_t hist16(const uint32_t* h, int b) { return (h[b >> 1] >> (16 * (b & 1))) & 0xFFFFu; }
+
 // The wave's lanes each own 32 consecutive bins of a row's histogram (from the
 // top); the lane whose bins cross the kk-th largest key writes the threshold.
-__device__ void wave_find_bin(const uint32_t* hist, uint32_t kk, uint32_t* thr) {
+__device__ void wave_find_bin(const uint32_t* hist, uint32_t kk, uint32_t n, uint32_t* thr) {
   const int lane = threadIdx.x & 63;
   constexpr int PER = kSelBins / 64;
   uint32_t sum = 0;
-  for (int i = 0; i < PER; ++i) sum += hist[kSelBins - 1 - (lane * PER + i)];
-  uint32_t run = wave_incl_scan(sum) - sum;
+  for (int i = 0; i < PER; ++i) sum += hist16(hist, kSelBins - 1 - (lane * PER + i));
+  const uint32_t incl = wave_incl_scan(sum);
+  const uint32_t total = __shfl(incl, 63, 64);
+  if (total != n) {  // a bin overflowed
+    if (lane == 0) thr[3] = 0u;
+    return;
+  }
+  uint32_t run = incl - sum;
   for (int i = 0; i < PER; ++i) {
-    const uint32_t h = hist[kSelBins - 1 - (lane * PER + i)];
+    const uint32_t h = hist16(hist, kSelBins - 1 - (lane * PER + i));
     if (run < kk && run + h >= kk) {
       thr[0] = (uint32_t)(kSelBins - 1 - (lane * PER + i));
       thr[1] = run;
@@ -58,146 +84,271 @@ __device__ void wave_find_bin(const uint32_t* hist, uint32_t kk, uint32_t* thr) 
   }
 }
 
-constexpr int kPfStages = 3;  // key tiles per wave in the register ring
+constexpr int kLinTerms = kLinRows;  // fp8 rows per token for u
+constexpr int kPfRing = 4;   // LDS key-tile slots per workgroup
+constexpr int kPfLead = 5;   // a tile's global loads are issued this many tiles before it is computed
+constexpr int kPfWrite = 2;  // ... and written to LDS this many tiles before
+constexpr int kPfRegs = kPfLead - kPfWrite + 1;  // register slots for loads in flight
+static_assert(kPfRegs == 4 && kPfRing == 4, "the main loop is unrolled by 4");
+constexpr int kTileBytes = 32 * 128;
 
+// One fp8 byte (OCP E4M3FN) -> float, exact.
+__device__ __forceinline__ float fp8_to_f32(uint32_t byte) {
+  const int v = (int)(byte & 0xFFu);
+  return __builtin_bit_cast(float, fp8x4_to_bf16x4(v).x << 16);
+}
+
+// u[t][d] = sum_h w[t][h] * q_hat[t][h][d] in fp32, then split into
+// kLinTerms fp8 rows: row i holds round(r_i * 2^-e_i) with 2^e_i chosen so the
+// largest |r_i| lands in [128, 256), and r_{i+1} = r_i - 2^e_i * row_i (the
+// residual uses the row's exact fp8 value, so any rounding of the encoder is
+// compensated by the next row).  Two tokens per 256-thread block, one dim per
+// thread.
+__global__ __launch_bounds__(256) void prefill_linear_kernel(const uint8_t* __restrict__ q,
+                                                             const float* __restrict__ w, int T, int H,
+                                                             uint8_t* __restrict__ uq,
+                                                             float* __restrict__ usc) {
+  __shared__ float red[4];
+  const int slot = threadIdx.x >> 7, d = threadIdx.x & 127;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 2 + slot;
+  const int tt = t < T ? t : T - 1;
+  float u = 0.0f;
+  for (int h = 0; h < H; ++h) u = fmaf(w[(int64_t)tt * H + h], fp8_to_f32(q[((int64_t)tt * H + h) * 128 + d]), u);
+  float r = u;
+#pragma unroll
+  for (int i = 0; i < kLinTerms; ++i) {
+    const float m = wave_max(fabsf(r));
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    const float mt = fmaxf(red[2 * slot], red[2 * slot + 1]);
+    __syncthreads();
+    // exponent of the row scale; a (near-)zero residual gets an all-zero row
+    const int e = mt > 0x1p-100f ? ilogbf(mt) - 7 : 0;
+    const float sc = ldexpf(1.0f, e);
+    uint32_t f = 0u;
+    if (mt > 0x1p-100f) {
+      const float v = r * ldexpf(1.0f, -e);  // |v| < 256: no saturation
+      f = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xFFu;
+    }
+    r -= fp8_to_f32(f) * sc;
+    if (t < T) {
+      uq[((int64_t)t * kLinTerms + i) * 128 + d] = (uint8_t)f;
+      if (d == 0) usc[(int64_t)t * kLinTerms + i] = sc;
+    }
+  }
+}
+
+template <bool KSCALE>
 __global__ __launch_bounds__(256) void prefill_score_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
-    const uint8_t* __restrict__ kc, const float* __restrict__ k_scale, int T, int L, int qpos0,
-    int H, int k, int fill_masked, float* __restrict__ scores, uint32_t* __restrict__ thr) {
-  __shared__ uint32_t phist[kPfWaves][kPfTokPerWave][kSelBins];
-  // Head weights of the block's tokens.  In the MFMA result a lane holds heads
-  // 8*(r/4) + 4*g + r%4 (+32 per row block): every lane of a half reads the
-  // same four consecutive weights, so these reads are LDS broadcasts.
-  __shared__ float wsh[kPfTokPerBlock][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint8_t* __restrict__ uq, const float* __restrict__ usc, const uint8_t* __restrict__ kc,
+    const float* __restrict__ k_scale, int T, int L, int qpos0, int H, int k, int fill_masked,
+    float* __restrict__ scores, uint32_t* __restrict__ thr) {
+  static_assert(kPfTokPerWave == 2 && kPfWaves == 4, "lane half g finishes token slot g; 4 loader waves");
+  __shared__ uint32_t phist[kPfWaves][kPfTokPerWave][kSelBins / 2];
+  // Key tiles shared by the workgroup's waves (which walk the same keys): 32
+  // keys x 128 bytes per slot, 16-byte chunk c of key r stored at chunk
+  // c ^ (r & 7) so that the MFMA operand reads are free of bank conflicts.
+  __shared__ __attribute__((aligned(16))) uint8_t ktile[kPfRing][kTileBytes];
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int col = lane & 31, g = lane >> 5;
   const int t_base = (blockIdx.x * kPfWaves + wave) * kPfTokPerWave;
   const int nt = t_base >= T ? 0 : ((T - t_base) < kPfTokPerWave ? (T - t_base) : kPfTokPerWave);
   // Token slot tk computes row trow[tk]; slots past the end of the chunk
-  // repeat the wave's first token (so their stores rewrite identical values)
-  // and are never counted in a histogram.
+  // repeat a valid token (so their stores rewrite identical values) and are
+  // never counted in a histogram.
   int trow[kPfTokPerWave];
 #pragma unroll
-  for (int tk = 0; tk < kPfTokPerWave; ++tk) trow[tk] = nt > 0 ? t_base + (tk < nt ? tk : 0) : 0;
+  for (int tk = 0; tk < kPfTokPerWave; ++tk) trow[tk] = nt > 0 ? t_base + (tk < nt ? tk : 0) : T - 1;
 
-  for (int i = lane; i < kPfTokPerWave * kSelBins; i += 64) (&phist[wave][0][0])[i] = 0;
-#pragma unroll
-  for (int tk = 0; tk < kPfTokPerWave; ++tk)
-    wsh[wave * kPfTokPerWave + tk][lane] = lane < H ? w[(int64_t)trow[tk] * H + lane] : 0.0f;
+  for (int i = lane; i < kPfTokPerWave * kSelBins / 2; i += 64) (&phist[wave][0][0])[i] = 0;
 
+  // Query heads (A operand, row = head hb*32 + col), the weights of the heads
+  // whose results this lane holds (rows 8*(r/4) + 4*g + r%4 of each block),
+  // and the u rows: A row col < 8 is u row (col & 3) of token slot col >> 2.
   i32x8 qa[kPfTokPerWave][2][2];
-  float sq[kPfTokPerWave];
+  float wl[kPfTokPerWave][2][16];
+  i32x8 ua[2];
 #pragma unroll
   for (int tk = 0; tk < kPfTokPerWave; ++tk) {
-    sq[tk] = q_scale ? q_scale[trow[tk]] : 1.0f;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const int row = hb * 32 + col;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        i32x8 v = {};
-        if (row < H) v = ld32(q + ((int64_t)trow[tk] * H + row) * 128 + 64 * g + 32 * j);
+        // Clamped, unconditional load (rows past H are zeroed afterwards).
+        i32x8 v = ld32(q + ((int64_t)trow[tk] * H + (row < H ? row : H - 1)) * 128 + 64 * g + 32 * j);
+        if (row >= H) v = i32x8{};
         qa[tk][hb][j] = v;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int head = hb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const float wv = w[(int64_t)trow[tk] * H + (head < H ? head : H - 1)];
+        wl[tk][hb][r] = head < H ? wv : 0.0f;
       }
     }
   }
-  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const bool urow = col < kLinTerms * kPfTokPerWave;
+    const int uc = urow ? col : 0;
+    i32x8 v = ld32(uq + ((int64_t)trow[uc >> 2] * kLinTerms + (uc & 3)) * 128 + 64 * g + 32 * j);
+    if (!urow) v = i32x8{};
+    ua[j] = v;
+  }
+  // This half's token: its scales and the scales of its u rows.
+  const int tg = trow[g];
+  const float sq = (q_scale ? q_scale[tg] : 1.0f) * 0.5f;
+  float us[kLinTerms];
+#pragma unroll
+  for (int i = 0; i < kLinTerms; ++i) us[i] = usc[(int64_t)tg * kLinTerms + i];
 
-  const int vis_end = qpos0 + t_base + nt;  // exclusive end of the last token's visible range
-  const int n_tiles = nt > 0 ? (vis_end + 31) / 32 : 0;
-  const uint8_t* kbase = kc + 64 * g;
+  // Tiles this wave needs, and tiles the workgroup walks (every wave takes
+  // part in every tile's barrier; the extra tiles are fully masked for it).
+  const int wg_t_end = (blockIdx.x + 1) * kPfTokPerBlock < T ? (blockIdx.x + 1) * kPfTokPerBlock : T;
+  const int n_tiles = nt > 0 ? (qpos0 + t_base + nt + 31) / 32 : 0;
+  const int n_wg = (qpos0 + wg_t_end + 31) / 32;
+  auto clamp_tile = [&](int it) { return it < n_wg ? it : n_wg - 1; };
   // Key row of tile `it` for this lane, clamped into the cache: a lane past
   // the end recomputes row L-1 and rewrites that row's own score.
   auto key_row = [&](int it) {
     const int s = it * 32 + col;
     return s < L ? s : L - 1;
   };
-  auto load_tile = [&](i32x8 (&kb)[2], float& sk, int it) {
-    const int srow = key_row(it);
-    const uint8_t* p = kbase + (int64_t)srow * 128;
-    kb[0] = ld32(p);
-    kb[1] = ld32(p + 32);
-    sk = k_scale ? k_scale[srow] : 1.0f;
+  // This wave's share of a tile: keys 8*wave + lane/8, chunk lane % 8.
+  const int ld_key = 8 * wave + (lane >> 3), ld_chunk = lane & 7;
+  const int ld_off = ld_key * 128 + 16 * (ld_chunk ^ (ld_key & 7));
+  auto gload = [&](int it) {
+    int row = it * 32 + ld_key;
+    row = row < L ? row : L - 1;
+    return ld16(kc + (int64_t)row * 128 + 16 * ld_chunk);
   };
+  auto lds_put = [&](int slot, i32x4 v) { *reinterpret_cast<i32x4*>(&ktile[slot][ld_off]) = v; };
+  auto lds_get = [&](int slot, i32x8 (&kb)[2]) {
+    const uint8_t* base = &ktile[slot][col * 128];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c0 = (4 * g + 2 * j) ^ (col & 7), c1 = (4 * g + 2 * j + 1) ^ (col & 7);
+      const i32x4 x = *reinterpret_cast<const i32x4*>(base + 16 * c0);
+      const i32x4 y = *reinterpret_cast<const i32x4*>(base + 16 * c1);
+      kb[j] = i32x8{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+    }
+  };
+  auto load_scale = [&](int it) {
+    if constexpr (KSCALE) return k_scale[key_row(it)];
+    else return 1.0f;
+  };
+
   auto compute = [&](const i32x8 (&kb)[2], float sk, int it, bool live) {
     const int s = it * 32 + col;
     const int srow = key_row(it);
-    f32x16 acc[kPfTokPerWave][2];
+    __builtin_amdgcn_s_setprio(1);
+    float p[kPfTokPerWave];
 #pragma unroll
     for (int tk = 0; tk < kPfTokPerWave; ++tk) {
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        f32x16 a = {};
-        a = mfma_fp8(qa[tk][hb][0], kb[0], a);
-        acc[tk][hb] = mfma_fp8(qa[tk][hb][1], kb[1], a);
-      }
-    }
-#pragma unroll
-    for (int tk = 0; tk < kPfTokPerWave; ++tk) {
-      const float* wt = &wsh[wave * kPfTokPerWave + tk][4 * g];
+      f32x16 a0 = {}, a1 = {};
+      a0 = mfma_fp8(qa[tk][0][0], kb[0], a0);
+      a1 = mfma_fp8(qa[tk][1][0], kb[0], a1);
+      a0 = mfma_fp8(qa[tk][0][1], kb[1], a0);
+      a1 = mfma_fp8(qa[tk][1][1], kb[1], a1);
       float part = 0.0f;
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 wv = *reinterpret_cast<const f32x4*>(wt + hb * 32 + 8 * r4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) part = fmaf(wv[i], relu(acc[tk][hb][4 * r4 + i]), part);
-        }
+      for (int r = 0; r < 16; ++r) {
+        part = fmaf(wl[tk][0][r], fabsf(a0[r]), part);
+        part = fmaf(wl[tk][1][r], fabsf(a1[r]), part);
       }
-      part = sum_halves(part);
-      const int t = trow[tk];
-      const bool vis = srow <= qpos0 + t;
-      const float val = vis ? part * sq[tk] * sk : -INFINITY;
-      // Straight-line store (both halves write the same value) so the loads
-      // of the next tiles stay in flight.
-      scores[(int64_t)t * L + srow] = val;
-      // (an LDS-only branch)
-      if (live && tk < nt && g == 0 && s < L && vis)
-        atomicAdd(&phist[wave][tk][score_key(val) >> kSelShift], 1u);
+      p[tk] = part;
+    }
+    f32x16 lin = {};
+    lin = mfma_fp8(ua[0], kb[0], lin);
+    lin = mfma_fp8(ua[1], kb[1], lin);
+    __builtin_amdgcn_s_setprio(0);
+    // Half g keeps token g: send the other token's half-sum to the partner.
+    const float mine = g ? p[1] : p[0], other = g ? p[0] : p[1];
+    const float pa = mine + __shfl_xor(other, 32, 64);
+    float lsum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kLinTerms; ++i) lsum = fmaf(us[i], lin[i], lsum);
+    const bool vis = srow <= qpos0 + tg;
+    const float val = vis ? (pa + lsum) * sq * sk : -INFINITY;
+    // Straight-line store (a lane past the end rewrites row L-1 with its own
+    // value) so the loads of the next tiles stay in flight.
+    scores[(int64_t)tg * L + srow] = val;
+    // (an LDS-only branch)
+    if (live && g < nt && it < n_tiles && s < L && vis) {
+      const uint32_t b = score_key(val) >> kSelShift;
+      atomicAdd(&phist[wave][g][b >> 1], 1u << (16 * (b & 1)));
     }
   };
 
-  if (n_tiles > 0) {
-    i32x8 buf[kPfStages][2];
-    float skb[kPfStages];
+  // Software pipeline over the workgroup's tiles (step i computes tile i):
+  //   tile i+kPfLead: global -> registers (slot (i+kPfLead) % 4)
+  //   tile i+kPfWrite: registers -> LDS slot (i+kPfWrite) % 4
+  //   barrier; tile i: LDS -> MFMA operand, compute.
+  // LDS slot (i+2)%4 last held tile i-2, which every wave finished before the
+  // barrier of step i-1; tile i was written at step i-2, before two barriers.
+  // The key scales ride in a register ring loaded kPfRegs steps ahead.
+  i32x4 kreg[kPfRegs];
+  float skr[kPfRegs];
+  lds_put(0, gload(clamp_tile(0)));
+  lds_put(1, gload(clamp_tile(1)));
 #pragma unroll
-    for (int st = 0; st < kPfStages - 1; ++st) load_tile(buf[st], skb[st], st < n_tiles ? st : n_tiles - 1);
-    const int nit = (n_tiles + kPfStages - 1) / kPfStages * kPfStages;
-    for (int base = 0; base < nit; base += kPfStages) {
+  for (int j = kPfWrite; j <= kPfLead; ++j) kreg[j % kPfRegs] = gload(clamp_tile(j));
 #pragma unroll
-      for (int st = 0; st < kPfStages; ++st) {
-        const int it = base + st;
-        const int nx = it + kPfStages - 1;
-        load_tile(buf[(st + kPfStages - 1) % kPfStages], skb[(st + kPfStages - 1) % kPfStages],
-                  nx < n_tiles ? nx : n_tiles - 1);
-        compute(buf[st], skb[st], it < n_tiles ? it : n_tiles - 1, it < n_tiles);
-      }
+  for (int j = 0; j < kPfRegs; ++j) skr[j] = load_scale(clamp_tile(j));
+  const int nsteps = (n_wg + kPfRegs - 1) / kPfRegs * kPfRegs;
+  for (int base = 0; base < nsteps; base += kPfRegs) {
+#pragma unroll
+    for (int st = 0; st < kPfRegs; ++st) {
+      const int i = base + st;
+      lds_put((st + kPfWrite) % kPfRing, kreg[(st + kPfWrite) % kPfRegs]);
+      kreg[(st + kPfLead) % kPfRegs] = gload(clamp_tile(i + kPfLead));
+      __syncthreads();
+      i32x8 kb[2];
+      lds_get(st % kPfRing, kb);
+      const int it = clamp_tile(i);
+      compute(kb, skr[st], it, i < n_wg);
+      skr[st] = load_scale(clamp_tile(i + kPfRegs));
     }
   }
   __syncthreads();
   for (int tk = 0; tk < nt; ++tk) {
     const int t = t_base + tk;
-    if (qpos0 + t + 1 > k) wave_find_bin(phist[wave][tk], (uint32_t)k, thr + (int64_t)t * 4);
+    const int vis = qpos0 + t + 1;
+    if (vis > k) wave_find_bin(phist[wave][tk], (uint32_t)k, (uint32_t)(vis < L ? vis : L), thr + (int64_t)t * 4);
   }
   if (fill_masked) {
     for (int tk = 0; tk < nt; ++tk) {
       const int t = t_base + tk;
-      for (int s = n_tiles * 32 + lane; s < L; s += 64) scores[(int64_t)t * L + s] = -INFINITY;
+      for (int s = n_wg * 32 + lane; s < L; s += 64) scores[(int64_t)t * L + s] = -INFINITY;
     }
   }
 }
 
 }  // namespace
 
+hipError_t launch_prefill_linear(const uint8_t* q, const float* w, int32_t T, int32_t H, uint8_t* uq,
+                                 float* usc, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  prefill_linear_kernel<<<dim3((unsigned)((T + 1) / 2)), dim3(256), 0, stream>>>(q, w, T, H, uq, usc);
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill_score(const uint8_t* q, const float* q_scale, const float* w,
-                                const uint8_t* kc, const float* k_scale, int32_t T, int32_t L,
-                                int32_t qpos0, int32_t H, int32_t k, bool fill_masked,
-                                float* scores, const SelWs& sel, hipStream_t stream) {
+                                const uint8_t* uq, const float* usc, const uint8_t* kc,
+                                const float* k_scale, int32_t T, int32_t L, int32_t qpos0, int32_t H,
+                                int32_t k, bool fill_masked, float* scores, const SelWs& sel,
+                                hipStream_t stream) {
   if (T <= 0 || L <= 0) return hipSuccess;
   dim3 grid((unsigned)((T + kPfTokPerBlock - 1) / kPfTokPerBlock));
-  prefill_score_kernel<<<grid, dim3(64 * kPfWaves), 0, stream>>>(
-      q, q_scale, w, kc, k_scale, T, L, qpos0, H, k, fill_masked ? 1 : 0, scores, sel.thr);
+  if (k_scale)
+    prefill_score_kernel<true><<<grid, dim3(64 * kPfWaves), 0, stream>>>(
+        q, q_scale, w, uq, usc, kc, k_scale, T, L, qpos0, H, k, fill_masked ? 1 : 0, scores, sel.thr);
+  else
+    prefill_score_kernel<false><<<grid, dim3(64 * kPfWaves), 0, stream>>>(
+        q, q_scale, w, uq, usc, kc, k_scale, T, L, qpos0, H, k, fill_masked ? 1 : 0, scores, sel.thr);
   return hipGetLastError();
 }
 

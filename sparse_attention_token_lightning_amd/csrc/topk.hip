@@ -226,7 +226,8 @@ __device__ void select_keys(const Row& row, KeyAt key_at, PosAt pos_at, int64_t 
 enum SelHow : int32_t { kSelSelf = 1, kSelFull = 2 };
 
 // One workgroup per row.  kSelSelf: the row's level-0 threshold is in ws.thr
-// (prefill scan).  kSelFull: the workgroup builds the histogram itself.
+// (prefill scan), unless the scan flagged it invalid (thr[3] == 0).
+// kSelFull: the workgroup builds the histogram itself.
 // Dynamic LDS holds `cap` candidate pairs.
 __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkRows a, SelWs ws, int how, int cap) {
   extern __shared__ uint2 cand[];
@@ -252,7 +253,9 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkRows a, SelWs
   auto gpos = [&](int64_t i) { return i; };
 
   uint32_t bstar, above, eq;
-  if (how == kSelFull) {
+  // kSelSelf rows whose scan histogram overflowed (thr[3] == 0) build it here.
+  const bool build = how == kSelFull || ws.thr[(int64_t)r * 4 + 3] == 0u;
+  if (build) {
     for (int i = tid; i < kSelBins; i += kRowThreads) hist[i] = 0;
     __syncthreads();
 #pragma unroll 1
