@@ -25,6 +25,10 @@
 // registers while it computes a fourth (a ring indexed at compile time, so no
 // register copies force early waits), together with their per-token scales.
 //
+// Scores collect in LDS and leave in one coalesced burst per workgroup: a
+// 4-byte store per key interleaved with the key stream costs several times its
+// own share of HBM time.
+//
 // The selection's first radix level is fused in: every score also lands in a
 // per-workgroup LDS histogram of its top 11 key bits, stored as that
 // workgroup's partial of the request's histogram (plain stores: dozens of
@@ -40,6 +44,8 @@ constexpr int kDecWaves = 4;  // waves per workgroup
 constexpr int kTile = 32;     // keys per MFMA tile
 constexpr int kStagesFp8 = 4;   // key-tile buffers per wave (fp8 keys)
 constexpr int kStagesBf16 = 3;  // (bf16 keys: twice the registers per tile)
+constexpr int kDecMaxTpw = 64;  // tiles per wave at most
+constexpr int kDecMaxChunk = kDecWaves * kDecMaxTpw * kTile;  // positions per workgroup at most
 
 template <bool FP8>
 __global__ __launch_bounds__(256) void decode_score_kernel(
@@ -50,6 +56,10 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
   constexpr int kRowBytes = FP8 ? 128 : 256;  // one key row
   constexpr int kStages = FP8 ? kStagesFp8 : kStagesBf16;
   __shared__ uint32_t lhist[kSelBins];
+  // The workgroup's scores, written to HBM in one burst at the end: small
+  // writes interleaved with the key stream cost far more read bandwidth than
+  // their own size.
+  __shared__ __attribute__((aligned(16))) float ssc[kDecMaxChunk];
 
   const int b = blockIdx.y;
   const int64_t off = kv_off[b];
@@ -129,16 +139,12 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
       part = fmaf(wl[1][r], relu(a1[r]), part);
     }
     part = sum_halves(part);
-    // Straight-line on purpose (no branch around the global store) so the
-    // compiler can keep the other stages' loads in flight: both lane halves
-    // hold the same total and store it, and a position past L was loaded as
-    // row L-1, so its store rewrites row L-1 with that row's own score.
+    // LDS only from here on (no global-memory op under a branch, so the
+    // loads' wait counting stays exact).  Positions past L are dropped at the
+    // final write; a repeated padding tile rewrites identical values.
     const int64_t s = tok(it);
-    const int64_t sc_row = s < L ? s : L - 1;
     const float val = part * sc;
-    scores[off + sc_row] = val;
-    // (an LDS-only branch: it holds no global-memory op, so the loads' wait
-    // counting across it stays exact)
+    if (g == 0) ssc[s - wg0] = val;
     if (select && live && g == 0 && s < L) atomicAdd(&lhist[score_key(val) >> kSelShift], 1u);
   };
 
@@ -161,11 +167,23 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
       }
     }
   }
+  __syncthreads();
+  // Scores of positions wg0 .. min(wg0 + chunk, L) - 1, 16 bytes per store
+  // where the request's offset keeps them aligned.
+  const int64_t n = (L - wg0) < chunk ? (L - wg0) : chunk;
+  float* dst = scores + off + wg0;
+  if (((off + wg0) & 3) == 0) {
+    const int64_t n4 = n >> 2;
+    for (int64_t i = tid; i < n4; i += 256)
+      *reinterpret_cast<f32x4*>(dst + 4 * i) = *reinterpret_cast<const f32x4*>(&ssc[4 * i]);
+    for (int64_t i = 4 * n4 + tid; i < n; i += 256) dst[i] = ssc[i];
+  } else {
+    for (int64_t i = tid; i < n; i += 256) dst[i] = ssc[i];
+  }
   if (!select) return;
 
   // This workgroup's share of the request's level-0 histogram, as 16-bit
-  // partials (a workgroup covers at most 2048 positions).
-  __syncthreads();
+  // partials (a workgroup covers at most 8192 positions).
   store_partial<256>(lhist, sel.part + ((int64_t)b * sel.nwg + blockIdx.x) * kSelBins);
 }
 
@@ -176,7 +194,7 @@ int64_t decode_chunk(int64_t n_tok) {
   // kernel holds two 4-wave workgroups per CU), long runs so each workgroup's
   // one-off query load and histogram store are amortised.
   int64_t tpw = n_tok / ((int64_t)512 * kDecWaves * kTile);
-  tpw = tpw < 4 ? 4 : (tpw > 64 ? 64 : tpw);
+  tpw = tpw < 4 ? 4 : (tpw > kDecMaxTpw ? kDecMaxTpw : tpw);
   return (int64_t)kDecWaves * tpw * kTile;
 }
 
