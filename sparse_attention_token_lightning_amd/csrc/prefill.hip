@@ -113,8 +113,21 @@ __global__ __launch_bounds__(256) void prefill_linear_kernel(const uint8_t* __re
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 2 + slot;
   const int tt = t < T ? t : T - 1;
+  // All of a thread's loads are issued before the arithmetic (clamped head
+  // index, zero weight past H), 16 heads per batch.
   float u = 0.0f;
-  for (int h = 0; h < H; ++h) u = fmaf(w[(int64_t)tt * H + h], fp8_to_f32(q[((int64_t)tt * H + h) * 128 + d]), u);
+  for (int h0 = 0; h0 < H; h0 += 16) {
+    uint32_t qb[16];
+    float wv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int h = h0 + i < H ? h0 + i : H - 1;
+      qb[i] = q[((int64_t)tt * H + h) * 128 + d];
+      wv[i] = w[(int64_t)tt * H + h];
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) u = fmaf(h0 + i < H ? wv[i] : 0.0f, fp8_to_f32(qb[i]), u);
+  }
   float r = u;
 #pragma unroll
   for (int i = 0; i < kLinTerms; ++i) {
@@ -276,11 +289,11 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
     // Straight-line store (a lane past the end rewrites row L-1 with its own
     // value) so the loads of the next tiles stay in flight.
     scores[(int64_t)tg * L + srow] = val;
-    // (an LDS-only branch)
-    if (live && g < nt && it < n_tiles && s < L && vis) {
-      const uint32_t b = score_key(val) >> kSelShift;
-      atomicAdd(&phist[wave][g][b >> 1], 1u << (16 * (b & 1)));
-    }
+    // Unconditional LDS update (adds 0 where the score is not counted), so
+    // the tile stays one basic block.
+    const uint32_t b = score_key(val) >> kSelShift;
+    const uint32_t inc = (live && g < nt && it < n_tiles && s < L && vis) ? 1u : 0u;
+    atomicAdd(&phist[wave][g][b >> 1], inc << (16 * (b & 1)));
   };
 
   // Software pipeline over the workgroup's tiles (step i computes tile i):
@@ -298,7 +311,12 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
   for (int j = kPfWrite; j <= kPfLead; ++j) kreg[j % kPfRegs] = gload(clamp_tile(j));
 #pragma unroll
   for (int j = 0; j < kPfRegs; ++j) skr[j] = load_scale(clamp_tile(j));
+  // The MFMA operand of tile i+1 is read from LDS while tile i is computed
+  // (tile i+1 was written at step i-1, before the barrier of step i).
+  i32x8 kbuf[2][2];
   const int nsteps = (n_wg + kPfRegs - 1) / kPfRegs * kPfRegs;
+  __syncthreads();
+  lds_get(0, kbuf[0]);
   for (int base = 0; base < nsteps; base += kPfRegs) {
 #pragma unroll
     for (int st = 0; st < kPfRegs; ++st) {
@@ -306,10 +324,9 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
       lds_put((st + kPfWrite) % kPfRing, kreg[(st + kPfWrite) % kPfRegs]);
       kreg[(st + kPfLead) % kPfRegs] = gload(clamp_tile(i + kPfLead));
       __syncthreads();
-      i32x8 kb[2];
-      lds_get(st % kPfRing, kb);
+      lds_get((st + 1) % kPfRing, kbuf[(st + 1) & 1]);
       const int it = clamp_tile(i);
-      compute(kb, skr[st], it, i < n_wg);
+      compute(kbuf[st & 1], skr[st], it, i < n_wg);
       skr[st] = load_scale(clamp_tile(i + kPfRegs));
     }
   }
