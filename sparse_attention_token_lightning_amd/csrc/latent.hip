@@ -98,9 +98,18 @@ __global__ __launch_bounds__(256) void latent_absorb_kernel(
 }
 
 constexpr int kLsWaves = 4;  // layers per workgroup, one per wave
+constexpr int kLsMaxTiles = 64;  // tiles (32 rows) per workgroup at most
+constexpr int kLsMaxRows = kLsMaxTiles * 32;
 
 // DC: latent width (128 or 256).  GATHER: rows come from the candidate list.
-template <int DC, bool GATHER>
+// CSCALE: a per-row latent scale is given.
+//
+// The workgroup streams its rows 32 at a time: the global loads of tile it+2
+// are issued while tile it is computed, tile it+1 (loaded one step earlier)
+// goes to LDS at the end of the step.  Scores collect in LDS (one row per
+// layer) and are written in one burst at the end; the level-0 histograms are
+// 16-bit, packed two bins per word (a workgroup covers at most 2048 rows).
+template <int DC, bool GATHER, bool CSCALE>
 __global__ __launch_bounds__(256) void latent_score_kernel(
     const uint16_t* __restrict__ qt16, const float* __restrict__ wsc,
     const uint16_t* __restrict__ latent, const float* __restrict__ c_scale,
@@ -109,13 +118,13 @@ __global__ __launch_bounds__(256) void latent_score_kernel(
   constexpr int KSTEPS = DC / 16;  // K = 16 per MFMA
   constexpr int HALF = DC / 2;     // dims per lane half
   constexpr int CPT = DC / 64;     // 8-element chunks per thread per tile
-  constexpr int HB = GATHER ? 1 : kLsWaves;  // histogram planes (unused when gathering)
   __shared__ i32x4 lds[2][KSTEPS * 64];
-  __shared__ uint32_t lhist[HB][GATHER ? 1 : kSelBins];
+  __shared__ uint32_t lhist[kLsWaves][kSelBins / 2];
+  __shared__ __attribute__((aligned(16))) float ssc[kLsWaves][kLsMaxRows];
   __shared__ int32_t sh_n;
 
   const int b = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int col = lane & 31, g = lane >> 5;
   const int l = blockIdx.z * kLsWaves + wave;
   const bool active = l < G;
@@ -144,32 +153,34 @@ __global__ __launch_bounds__(256) void latent_score_kernel(
   const int ntiles = (int)(ntl < tiles_per_block ? ntl : tiles_per_block);
   const bool select = !GATHER && n > k;
   if constexpr (!GATHER) {
-    for (int i = threadIdx.x; i < kLsWaves * kSelBins; i += 256) (&lhist[0][0])[i] = 0;
+    for (int i = threadIdx.x; i < kLsWaves * kSelBins / 2; i += 256) (&lhist[0][0])[i] = 0;
     // The top-k kernel that follows counts finished segments per (b, l) row.
     if (select && blockIdx.x == 0 && threadIdx.x < kLsWaves && blockIdx.z * kLsWaves + threadIdx.x < G)
       sel.done[(int64_t)b * G + blockIdx.z * kLsWaves + threadIdx.x] = 0u;
   }
 
+  // Absorbed queries (A operand: row = head, K = latent dims; lane half g
+  // holds dims HALF*g ..) and the weights of the heads whose results this
+  // lane holds (rows 8*(r/4) + 4*g + r%4 of each 32-row block).
+  const int la = active ? l : 0;  // inactive waves compute a copy of layer 0 and discard it
   f16x8 qa[2][KSTEPS];
   float wl[2][16];
-  if (active) {
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int row = hb * 32 + col;
-      // Clamped, unconditional loads (rows past H are zeroed afterwards).
-      const uint16_t* qp = qt16 + (((int64_t)b * G + l) * H + (row < H ? row : H - 1)) * DC + HALF * g;
+  for (int hb = 0; hb < 2; ++hb) {
+    const int row = hb * 32 + col;
+    // Clamped, unconditional loads (rows past H are zeroed afterwards).
+    const uint16_t* qp = qt16 + (((int64_t)b * G + la) * H + (row < H ? row : H - 1)) * DC + HALF * g;
 #pragma unroll
-      for (int j = 0; j < KSTEPS; ++j) {
-        i32x4 v = ld16(qp + 8 * j);
-        if (row >= H) v = i32x4{0, 0, 0, 0};
-        qa[hb][j] = __builtin_bit_cast(f16x8, v);
-      }
+    for (int j = 0; j < KSTEPS; ++j) {
+      i32x4 v = ld16(qp + 8 * j);
+      if (row >= H) v = i32x4{0, 0, 0, 0};
+      qa[hb][j] = __builtin_bit_cast(f16x8, v);
+    }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int head = hb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        const float wv = wsc[((int64_t)b * G + l) * H + (head < H ? head : H - 1)];
-        wl[hb][r] = head < H ? wv : 0.0f;
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int head = hb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+      const float wv = wsc[((int64_t)b * G + la) * H + (head < H ? head : H - 1)];
+      wl[hb][r] = head < H ? wv : 0.0f;
     }
   }
 
@@ -180,65 +191,101 @@ __global__ __launch_bounds__(256) void latent_score_kernel(
     if constexpr (GATHER) return off + cb[s];
     else return off + s;
   };
-  i32x4 pre[CPT];
-  auto gload = [&](int tile) {
-    const int64_t r = row_of(tok0 + (int64_t)tile * 32 + pt);
+  auto gload = [&](i32x4 (&dst)[CPT], int tile) {
+    const int t = tile < ntiles ? tile : ntiles - 1;
+    const int64_t r = row_of(tok0 + (int64_t)t * 32 + pt);
     const uint16_t* src = latent + r * DC + p * CPT * 8;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) pre[i] = ld16(src + 8 * i);
+    for (int i = 0; i < CPT; ++i) dst[i] = ld16(src + 8 * i);
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf, const i32x4 (&src)[CPT]) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int d0 = (p * CPT + i) * 8;
       const int gg = d0 / HALF, jj = (d0 - gg * HALF) / 8;
-      lds[buf][jj * 64 + pt + 32 * gg] = bf16x8_to_f16x8(pre[i]);
+      lds[buf][jj * 64 + pt + 32 * gg] = bf16x8_to_f16x8(src[i]);
+    }
+  };
+  auto row_scale = [&](int tile) {
+    if constexpr (CSCALE) return c_scale[row_of(tok0 + (int64_t)(tile < ntiles ? tile : ntiles - 1) * 32 + col)];
+    else return 1.0f;
+  };
+
+  auto compute = [&](int buf, int it, float sc) {
+    f32x16 a0 = {}, a1 = {};
+#pragma unroll
+    for (int j = 0; j < KSTEPS; ++j) {
+      const f16x8 kb = __builtin_bit_cast(f16x8, lds[buf][j * 64 + lane]);
+      a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[0][j], kb, a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[1][j], kb, a1, 0, 0, 0);
+    }
+    float part = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      part = fmaf(wl[0][r], relu(a0[r]), part);
+      part = fmaf(wl[1][r], relu(a1[r]), part);
+    }
+    part = sum_halves(part);
+    // LDS only from here on; every tile index here is < ntiles.
+    const int64_t s = tok0 + (int64_t)it * 32 + col;
+    const float val = part * sc;
+    if (g == 0) ssc[wave][it * 32 + col] = val;
+    if constexpr (!GATHER) {
+      const uint32_t bin = score_key(val) >> kSelShift;
+      const uint32_t inc = (select && active && g == 0 && s < n) ? 1u : 0u;
+      atomicAdd(&lhist[wave][bin >> 1], inc << (16 * (bin & 1)));
     }
   };
 
-  gload(0);
-  lstore(0);
+  // Ring of two register sets for tiles in flight; the step is unrolled by
+  // two so that the set indices are compile-time constants.
+  i32x4 pre[2][CPT];
+  float skr[2];
+  gload(pre[0], 0);
+  gload(pre[1], 1);
+  skr[0] = row_scale(0);
+  skr[1] = row_scale(1);
+  lstore(0, pre[0]);
+  gload(pre[0], 2);
   __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < ntiles) gload(it + 1);
-    if (active) {
-      f32x16 a0 = {}, a1 = {};
+  const int nsteps = (ntiles + 1) / 2 * 2;
+  for (int base = 0; base < nsteps; base += 2) {
 #pragma unroll
-      for (int j = 0; j < KSTEPS; ++j) {
-        const f16x8 kb = __builtin_bit_cast(f16x8, lds[buf][j * 64 + lane]);
-        a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[0][j], kb, a0, 0, 0, 0);
-        a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[1][j], kb, a1, 0, 0, 0);
+    for (int st = 0; st < 2; ++st) {
+      const int it = base + st;
+      if (it < ntiles) {
+        compute(st, it, skr[st]);
       }
-      float part = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        part = fmaf(wl[0][r], relu(a0[r]), part);
-        part = fmaf(wl[1][r], relu(a1[r]), part);
-      }
-      part = sum_halves(part);
-      const int64_t s = tok0 + (int64_t)it * 32 + col;
-      if (g == 0 && s < n) {
-        const float sc = c_scale ? c_scale[row_of(s)] : 1.0f;
-        const float val = part * sc;
-        if constexpr (GATHER) {
-          scores[((int64_t)b * G + l) * C + s] = val;
-        } else {
-          scores[(int64_t)l * n_tok + off + s] = val;
-          if (select) atomicAdd(&lhist[wave][score_key(val) >> kSelShift], 1u);
-        }
-      }
+      skr[st] = row_scale(it + 2);
+      lstore(st ^ 1, pre[st ^ 1]);  // tile it+1
+      gload(pre[st ^ 1], it + 3);
+      __syncthreads();
     }
-    if (it + 1 < ntiles) lstore(buf ^ 1);
-    __syncthreads();
+  }
+
+  // Scores of this workgroup's rows, one burst per layer (16-byte stores
+  // where the destination is aligned).
+  const int nrow = (int)((n - tok0) < (int64_t)ntiles * 32 ? (n - tok0) : (int64_t)ntiles * 32);
+  const int nl = (G - (int)blockIdx.z * kLsWaves) < kLsWaves ? (G - (int)blockIdx.z * kLsWaves) : kLsWaves;
+  for (int lw = 0; lw < nl; ++lw) {
+    const int lg = blockIdx.z * kLsWaves + lw;
+    float* dst = GATHER ? scores + ((int64_t)b * G + lg) * C + tok0 : scores + (int64_t)lg * n_tok + off + tok0;
+    if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+      const int n4 = nrow >> 2;
+      for (int i = threadIdx.x; i < n4; i += 256)
+        *reinterpret_cast<f32x4*>(dst + 4 * i) = *reinterpret_cast<const f32x4*>(&ssc[lw][4 * i]);
+      for (int i = 4 * n4 + threadIdx.x; i < nrow; i += 256) dst[i] = ssc[lw][i];
+    } else {
+      for (int i = threadIdx.x; i < nrow; i += 256) dst[i] = ssc[lw][i];
+    }
   }
   if constexpr (!GATHER) {
     if (!select) return;
-    // Each layer's share of its (b, l) row histogram, as 16-bit partials.
-    const int nl = (G - (int)blockIdx.z * kLsWaves) < kLsWaves ? (G - (int)blockIdx.z * kLsWaves) : kLsWaves;
+    // Each layer's share of its (b, l) row histogram (already 16-bit bins).
     for (int lw = 0; lw < nl; ++lw) {
       const int64_t r = (int64_t)b * G + blockIdx.z * kLsWaves + lw;
-      store_partial<256>(lhist[lw], sel.part + (r * sel.nwg + blockIdx.x) * kSelBins);
+      uint32_t* d = reinterpret_cast<uint32_t*>(sel.part + (r * sel.nwg + blockIdx.x) * kSelBins);
+      for (int i = threadIdx.x; i < kSelBins / 2; i += 256) d[i] = lhist[lw][i];
     }
   }
 }
@@ -247,24 +294,36 @@ __global__ __launch_bounds__(256) void latent_score_kernel(
 
 int64_t latent_chunk(int64_t n_tok) {
   int64_t tpb = n_tok / ((int64_t)1024 * 32);
-  tpb = tpb < 4 ? 4 : (tpb > 64 ? 64 : tpb);
+  tpb = tpb < 4 ? 4 : (tpb > kLsMaxTiles ? kLsMaxTiles : tpb);
   return tpb * 32;
 }
 
 namespace {
+
+template <bool GATHER, bool CSCALE>
+hipError_t launch_ls2(int Dc, dim3 grid, hipStream_t stream, const uint16_t* qt16, const float* wsc,
+                      const uint16_t* latent, const float* c_scale, const int64_t* kv_off,
+                      const int32_t* cand, int C, int64_t n_tok, int G, int H, int tpb, int k,
+                      float* scores, const SelWs& sel) {
+  if (Dc == 256)
+    latent_score_kernel<256, GATHER, CSCALE><<<grid, dim3(256), 0, stream>>>(
+        qt16, wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
+  else
+    latent_score_kernel<128, GATHER, CSCALE><<<grid, dim3(256), 0, stream>>>(
+        qt16, wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
+  return hipGetLastError();
+}
 
 template <bool GATHER>
 hipError_t launch_ls(int Dc, dim3 grid, hipStream_t stream, const uint16_t* qt16, const float* wsc,
                      const uint16_t* latent, const float* c_scale, const int64_t* kv_off,
                      const int32_t* cand, int C, int64_t n_tok, int G, int H, int tpb, int k,
                      float* scores, const SelWs& sel) {
-  if (Dc == 256)
-    latent_score_kernel<256, GATHER><<<grid, dim3(256), 0, stream>>>(
-        qt16, wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
-  else
-    latent_score_kernel<128, GATHER><<<grid, dim3(256), 0, stream>>>(
-        qt16, wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
-  return hipGetLastError();
+  if (c_scale)
+    return launch_ls2<GATHER, true>(Dc, grid, stream, qt16, wsc, latent, c_scale, kv_off, cand, C, n_tok,
+                                    G, H, tpb, k, scores, sel);
+  return launch_ls2<GATHER, false>(Dc, grid, stream, qt16, wsc, latent, c_scale, kv_off, cand, C, n_tok, G,
+                                   H, tpb, k, scores, sel);
 }
 
 }  // namespace
