@@ -184,7 +184,8 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
 
   // This workgroup's share of the request's level-0 histogram, as 16-bit
   // partials (a workgroup covers at most 8192 positions).
-  store_partial<256>(lhist, sel.part + ((int64_t)b * sel.nwg + blockIdx.x) * kSelBins);
+  const int64_t pi = (int64_t)b * sel.nwg + blockIdx.x;
+  store_partial<256>(lhist, sel.part + pi * kSelBins, sel.cpart + pi * kSelCoarse);
 }
 
 }  // namespace

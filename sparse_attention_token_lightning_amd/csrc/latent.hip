@@ -283,9 +283,8 @@ __global__ __launch_bounds__(256) void latent_score_kernel(
     if (!select) return;
     // Each layer's share of its (b, l) row histogram (already 16-bit bins).
     for (int lw = 0; lw < nl; ++lw) {
-      const int64_t r = (int64_t)b * G + blockIdx.z * kLsWaves + lw;
-      uint32_t* d = reinterpret_cast<uint32_t*>(sel.part + (r * sel.nwg + blockIdx.x) * kSelBins);
-      for (int i = threadIdx.x; i < kSelBins / 2; i += 256) d[i] = lhist[lw][i];
+      const int64_t pi = ((int64_t)b * G + blockIdx.z * kLsWaves + lw) * sel.nwg + blockIdx.x;
+      store_partial_packed<256>(lhist[lw], sel.part + pi * kSelBins, sel.cpart + pi * kSelCoarse);
     }
   }
 }

@@ -75,7 +75,8 @@ size_t sel_ws(int64_t rows, int64_t max_len, int64_t chunk) {
   size_t s = align_up((size_t)rows * 16);  // thr
   if (chunk > 0) {
     const int64_t nwg = (max_len + chunk - 1) / chunk, nseg = nseg_for(max_len);
-    s += align_up((size_t)rows * nwg * kHistBins * 2) + align_up((size_t)rows * 4);
+    s += align_up((size_t)rows * nwg * kHistBins * 2) + align_up((size_t)rows * nwg * li::kSelCoarse * 2) +
+         align_up((size_t)rows * 4);
     s += align_up((size_t)rows * nseg * 4) + align_up((size_t)rows * nseg * li::kSeg * 8);
   }
   return s;
@@ -87,6 +88,7 @@ li::SelWs carve_sel(Carver& cv, int64_t rows, int64_t max_len, int64_t chunk, in
   if (chunk > 0) {
     const int64_t nwg = (max_len + chunk - 1) / chunk, nseg = nseg_for(max_len);
     w.part = (uint16_t*)cv.take((size_t)rows * nwg * kHistBins * 2);
+    w.cpart = (uint16_t*)cv.take((size_t)rows * nwg * li::kSelCoarse * 2);
     w.done = (uint32_t*)cv.take((size_t)rows * 4);
     w.cnt = (uint32_t*)cv.take((size_t)rows * nseg * 4);
     w.cand = (uint2*)cv.take((size_t)rows * nseg * li::kSeg * 8);

@@ -9,12 +9,15 @@ namespace li {
 
 constexpr int kSelBins = 2048;   // level-0 bins
 constexpr int kSelShift = 21;    // key >> kSelShift = level-0 bin
+constexpr int kSelCoarse = 64;   // coarse bins: 32 consecutive level-0 bins each
+constexpr int kSelFine = kSelBins / kSelCoarse;
 constexpr int kSeg = 8192;       // scores per collect segment
 
 // Per-row state that the scan kernels hand to the top-k kernels through the
 // caller's workspace.
 struct SelWs {
   uint16_t* part;   // [rows][nwg][kSelBins] per-workgroup level-0 histograms (scan kernels)
+  uint16_t* cpart;  // [rows][nwg][kSelCoarse] the same, summed over 32 consecutive bins
   int32_t nwg;      // partial histograms per row (the scan grid's x extent)
   int32_t chunk;    // positions of a row covered by one scan workgroup
   uint32_t* thr;    // [rows][4] {threshold bin, #keys above it, #keys in it, valid} (prefill)
@@ -25,12 +28,34 @@ struct SelWs {
   int32_t cap;      // LDS candidates of the final selection in the segmented top-k
 };
 
-// Writes a workgroup's LDS histogram (counts < 65536) as 16-bit partials:
-// NT threads, two bins per 32-bit store.
+// Writes a workgroup's LDS histogram (one 32-bit counter per bin, counts <
+// 65536) as 16-bit partials, two bins per 32-bit store, and its coarse
+// partial.  NT threads.
 template <int NT>
-__device__ __forceinline__ void store_partial(const uint32_t* lhist, uint16_t* dst) {
+__device__ __forceinline__ void store_partial(const uint32_t* lhist, uint16_t* dst, uint16_t* cdst) {
   uint32_t* d = reinterpret_cast<uint32_t*>(dst);
   for (int i = threadIdx.x; i < kSelBins / 2; i += NT) d[i] = lhist[2 * i] | (lhist[2 * i + 1] << 16);
+  for (int c = threadIdx.x; c < kSelCoarse; c += NT) {
+    uint32_t sum = 0;
+    for (int i = 0; i < kSelFine; ++i) sum += lhist[c * kSelFine + i];
+    cdst[c] = (uint16_t)sum;
+  }
+}
+
+// The same for a histogram already packed two 16-bit bins per word (bin b in
+// half b & 1 of word b >> 1).
+template <int NT>
+__device__ __forceinline__ void store_partial_packed(const uint32_t* lhist, uint16_t* dst, uint16_t* cdst) {
+  uint32_t* d = reinterpret_cast<uint32_t*>(dst);
+  for (int i = threadIdx.x; i < kSelBins / 2; i += NT) d[i] = lhist[i];
+  for (int c = threadIdx.x; c < kSelCoarse; c += NT) {
+    uint32_t sum = 0;
+    for (int i = 0; i < kSelFine / 2; ++i) {
+      const uint32_t v = lhist[c * (kSelFine / 2) + i];
+      sum += (v & 0xFFFFu) + (v >> 16);
+    }
+    cdst[c] = (uint16_t)sum;
+  }
 }
 
 // Exclusive scan of one uint32 per thread over a block of NT threads (NT/64

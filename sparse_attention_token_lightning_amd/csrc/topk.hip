@@ -383,39 +383,81 @@ __global__ __launch_bounds__(kSegThreads) void topk_segmented_kernel(TopkRows a,
     key[e] = key_clamped(row.p, i, s1);
   }
 
-  // 1. Threshold bin from the row's partial histograms (16-bit, one per scan
-  //    workgroup); thread t owns the 4 bins 2047 - 4t ... 2044 - 4t, which are
-  //    8 contiguous bytes of each partial (ascending bin order).  Loads go out
-  //    in batches of 8 partials.
-  constexpr int PER = kSelBins / kSegThreads;
-  static_assert(PER == 4, "one 8-byte slice of each partial per thread");
+  // 1. Threshold bin b* from the row's partial histograms (16-bit, one per
+  //    scan workgroup), in two small reads: the coarse partials (64 bins of
+  //    32) give the coarse bin holding the k-th key, then only its 32 fine
+  //    bins are read from each partial.  hist[] is the reduction scratch.
   int64_t nw = (n + ws.chunk - 1) / ws.chunk;
   nw = nw < ws.nwg ? nw : ws.nwg;
-  uint32_t h[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) h[i] = 0;
-  const uint16_t* part = ws.part + (int64_t)r * ws.nwg * kSelBins + (kSelBins - PER - tid * PER);
-  constexpr int kPB = 8;
+  const int64_t prow = (int64_t)r * ws.nwg;
+  {
+    constexpr int kCG = kSegThreads / kSelCoarse;  // partial groups in the coarse pass
+    const int c = tid % kSelCoarse, grp = tid / kSelCoarse;
+    uint32_t cs = 0;
 #pragma unroll 1
-  for (int64_t w0 = 0; w0 < nw; w0 += kPB) {
-    i32x2 v[kPB];
+    for (int64_t w0 = grp; w0 < nw; w0 += 4 * kCG) {
+      uint32_t v[4];
 #pragma unroll
-    for (int j = 0; j < kPB; ++j) {
-      const int64_t wj = (w0 + j < nw) ? w0 + j : nw - 1;  // branch-free; repeats are dropped below
-      v[j] = *reinterpret_cast<const i32x2*>(part + wj * kSelBins);
-    }
+      for (int j = 0; j < 4; ++j) {
+        const int64_t wj = w0 + (int64_t)j * kCG;
+        v[j] = ws.cpart[(prow + (wj < nw ? wj : nw - 1)) * kSelCoarse + c];
+      }
 #pragma unroll
-    for (int j = 0; j < kPB; ++j) {
-      const bool in = w0 + j < nw;
-      const uint32_t lo = in ? (uint32_t)v[j].x : 0u, hi = in ? (uint32_t)v[j].y : 0u;
-      // ascending slots 0..3 = bins 2044-4t .. 2047-4t; h[i] is bin 2047-4t-i
-      h[0] += hi >> 16;
-      h[1] += hi & 0xFFFFu;
-      h[2] += lo >> 16;
-      h[3] += lo & 0xFFFFu;
+      for (int j = 0; j < 4; ++j) cs += (w0 + (int64_t)j * kCG < nw) ? v[j] : 0u;
     }
+    hist[grp * kSelCoarse + c] = cs;
+    __syncthreads();
+    if (wave == 0) {
+      // lane i: coarse bin 63 - i (descending order)
+      const int cb = kSelCoarse - 1 - lane;
+      uint32_t h = 0;
+#pragma unroll
+      for (int gI = 0; gI < kCG; ++gI) h += hist[gI * kSelCoarse + cb];
+      const uint32_t incl = wave_incl_scan(h);
+      if (incl - h < (uint32_t)k && incl >= (uint32_t)k) {
+        shb[0] = (uint32_t)cb;
+        shb[1] = incl - h;
+      }
+    }
+    __syncthreads();
   }
-  find_digit<kSegThreads, PER>(h, kSelBins - 1, (uint32_t)k, wsum, shb);
+  const uint32_t cstar = shb[0], cabove = shb[1];
+  __syncthreads();
+  {
+    constexpr int kFG = kSegThreads / kSelFine;  // partial groups in the fine pass
+    const int i = tid % kSelFine, grp = tid / kSelFine;
+    const int bin = (int)cstar * kSelFine + i;
+    uint32_t fs = 0;
+#pragma unroll 1
+    for (int64_t w0 = grp; w0 < nw; w0 += 4 * kFG) {
+      uint32_t v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t wj = w0 + (int64_t)j * kFG;
+        v[j] = ws.part[(prow + (wj < nw ? wj : nw - 1)) * kSelBins + bin];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fs += (w0 + (int64_t)j * kFG < nw) ? v[j] : 0u;
+    }
+    hist[grp * kSelFine + i] = fs;
+    __syncthreads();
+    if (wave == 0) {
+      // lane i < 32: fine bin 32 c* + 31 - i (descending), after cabove keys
+      const int fb = kSelFine - 1 - lane;
+      uint32_t h = 0;
+      if (lane < kSelFine) {
+#pragma unroll
+        for (int gI = 0; gI < kFG; ++gI) h += hist[gI * kSelFine + fb];
+      }
+      const uint32_t incl = cabove + wave_incl_scan(h);
+      if (lane < kSelFine && incl - h < (uint32_t)k && incl >= (uint32_t)k) {
+        shb[0] = cstar * kSelFine + (uint32_t)fb;
+        shb[1] = incl - h;
+        shb[2] = h;
+      }
+    }
+    __syncthreads();
+  }
   const uint32_t bstar = shb[0], above = shb[1], eq = shb[2];
 
   // 2. This segment's candidates, in position order: within a wave the kept
