@@ -66,7 +66,10 @@ struct Carver {
   }
 };
 
-int64_t nseg_for(int64_t max_len) { return (max_len + li::kSeg - 1) / li::kSeg; }
+int64_t nseg_for(int64_t rows, int64_t max_len) {
+  const int64_t seg = li::seg_len_for(rows, max_len);
+  return (max_len + seg - 1) / seg;
+}
 
 // Selection state for `rows` rows: per-row thresholds; with `chunk` > 0 also
 // the scan workgroups' partial histograms (ceil(max_len / chunk) per row), the
@@ -74,10 +77,11 @@ int64_t nseg_for(int64_t max_len) { return (max_len + li::kSeg - 1) / li::kSeg; 
 size_t sel_ws(int64_t rows, int64_t max_len, int64_t chunk) {
   size_t s = align_up((size_t)rows * 16);  // thr
   if (chunk > 0) {
-    const int64_t nwg = (max_len + chunk - 1) / chunk, nseg = nseg_for(max_len);
+    const int64_t nwg = (max_len + chunk - 1) / chunk, nseg = nseg_for(rows, max_len);
+    const int64_t seg = li::seg_len_for(rows, max_len);
     s += align_up((size_t)rows * nwg * kHistBins * 2) + align_up((size_t)rows * nwg * li::kSelCoarse * 2) +
          align_up((size_t)rows * 4);
-    s += align_up((size_t)rows * nseg * 4) + align_up((size_t)rows * nseg * li::kSeg * 8);
+    s += align_up((size_t)rows * nseg * 4) + align_up((size_t)rows * nseg * seg * 8);
   }
   return s;
 }
@@ -86,15 +90,17 @@ li::SelWs carve_sel(Carver& cv, int64_t rows, int64_t max_len, int64_t chunk, in
   li::SelWs w = {};
   w.thr = (uint32_t*)cv.take((size_t)rows * 16);
   if (chunk > 0) {
-    const int64_t nwg = (max_len + chunk - 1) / chunk, nseg = nseg_for(max_len);
+    const int64_t nwg = (max_len + chunk - 1) / chunk, nseg = nseg_for(rows, max_len);
+    const int64_t seg = li::seg_len_for(rows, max_len);
     w.part = (uint16_t*)cv.take((size_t)rows * nwg * kHistBins * 2);
     w.cpart = (uint16_t*)cv.take((size_t)rows * nwg * li::kSelCoarse * 2);
     w.done = (uint32_t*)cv.take((size_t)rows * 4);
     w.cnt = (uint32_t*)cv.take((size_t)rows * nseg * 4);
-    w.cand = (uint2*)cv.take((size_t)rows * nseg * li::kSeg * 8);
+    w.cand = (uint2*)cv.take((size_t)rows * nseg * seg * 8);
     w.nwg = (int32_t)nwg;
     w.chunk = (int32_t)chunk;
     w.nseg = (int32_t)nseg;
+    w.seg = (int32_t)seg;
     w.cap = li::seg_cap_for(k);
   }
   return w;

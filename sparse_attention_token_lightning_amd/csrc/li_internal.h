@@ -41,6 +41,9 @@ hipError_t launch_topk(const TopkRows& a, hipStream_t stream);
 hipError_t launch_topk_segmented(const TopkRows& a, const SelWs& ws, hipStream_t stream);
 // LDS candidate capacity of the segmented top-k's final step for a given k.
 int32_t seg_cap_for(int32_t k);
+// Scores per collect segment of the segmented top-k for `rows` rows of up to
+// max_len scores (larger segments when the grid would not fit the GPU at once).
+int64_t seg_len_for(int64_t rows, int64_t max_len);
 // Top-k from scan-built thresholds, one workgroup per row collecting its own candidates.
 hipError_t launch_topk_self(const TopkRows& a, const SelWs& ws, hipStream_t stream);
 // Positions of one row covered by one scan workgroup (decode / latent).

@@ -11,7 +11,7 @@ constexpr int kSelBins = 2048;   // level-0 bins
 constexpr int kSelShift = 21;    // key >> kSelShift = level-0 bin
 constexpr int kSelCoarse = 64;   // coarse bins: 32 consecutive level-0 bins each
 constexpr int kSelFine = kSelBins / kSelCoarse;
-constexpr int kSeg = 8192;       // scores per collect segment
+constexpr int kSeg = 8192;       // scores per collect segment (doubled for large grids)
 
 // Per-row state that the scan kernels hand to the top-k kernels through the
 // caller's workspace.
@@ -22,8 +22,9 @@ struct SelWs {
   int32_t chunk;    // positions of a row covered by one scan workgroup
   uint32_t* thr;    // [rows][4] {threshold bin, #keys above it, #keys in it, valid} (prefill)
   uint32_t* cnt;    // [rows][nseg] candidates per segment
-  uint2* cand;      // [rows][nseg][kSeg] (key, position) candidates in position order
+  uint2* cand;      // [rows][nseg][seg] (key, position) candidates in position order
   int32_t nseg;
+  int32_t seg;      // scores per collect segment (kSeg or 2 * kSeg)
   uint32_t* done;   // [rows] finished-segment counters (zeroed by the scan kernel)
   int32_t cap;      // LDS candidates of the final selection in the segmented top-k
 };

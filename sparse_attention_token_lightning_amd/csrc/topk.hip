@@ -346,9 +346,11 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkRows a, SelWs
 
 // One workgroup per (segment, row); see the file comment.  Dynamic LDS holds
 // the last workgroup's candidates (ws.cap pairs).
-constexpr int kSegPer = kSeg / kSegThreads;  // positions per thread in a segment
-
+// SEGPER: positions per thread in a segment (segment = SEGPER * kSegThreads).
+template <int SEGPER>
 __global__ __launch_bounds__(kSegThreads) void topk_segmented_kernel(TopkRows a, SelWs ws) {
+  constexpr int kSegPer = SEGPER;
+  constexpr int kSegLen = SEGPER * kSegThreads;
   extern __shared__ uint2 lcand[];
   __shared__ uint32_t hist[kSelBins];
   __shared__ uint32_t wsum[kSegThreads / 64];
@@ -365,15 +367,15 @@ __global__ __launch_bounds__(kSegThreads) void topk_segmented_kernel(TopkRows a,
     if (s == 0) keep_all<kSegThreads>(row, n, k);
     return;
   }
-  int64_t nseg_row = (n + kSeg - 1) / kSeg;
+  int64_t nseg_row = (n + kSegLen - 1) / kSegLen;
   nseg_row = nseg_row < ws.nseg ? nseg_row : ws.nseg;
   if (s >= nseg_row) return;
 
   // The segment's scores are loaded first: their latency overlaps the
   // reduction of the partial histograms below.  Round e covers positions
   // s0 + NT*e + tid (coalesced).
-  const int64_t s0 = (int64_t)s * kSeg;
-  const int64_t s1 = (s0 + kSeg) < n ? (s0 + kSeg) : n;
+  const int64_t s0 = (int64_t)s * kSegLen;
+  const int64_t s1 = (s0 + kSegLen) < n ? (s0 + kSegLen) : n;
   const int lane = tid & 63, wave = tid >> 6;
   constexpr int kW = kSegThreads / 64;
   uint32_t key[kSegPer];
@@ -483,7 +485,7 @@ __global__ __launch_bounds__(kSegThreads) void topk_segmented_kernel(TopkRows a,
   // which write through the (per-XCD, non-coherent) L2, and read back the same
   // way by the finishing workgroup; a full __threadfence() would instead write
   // back every dirty L2 line at each of these workgroups.
-  uint64_t* dst = reinterpret_cast<uint64_t*>(ws.cand + ((int64_t)r * ws.nseg + s) * kSeg);
+  uint64_t* dst = reinterpret_cast<uint64_t*>(ws.cand + ((int64_t)r * ws.nseg + s) * kSegLen);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int e = 0; e < kSegPer; ++e) {
@@ -537,7 +539,7 @@ __global__ __launch_bounds__(kSegThreads) void topk_segmented_kernel(TopkRows a,
   };
   auto gcand = [&](int64_t i) {
     const int sg = seg_of(i);
-    uint64_t* p = reinterpret_cast<uint64_t*>(ws.cand + ((int64_t)r * ws.nseg + sg) * kSeg + (i - segoff[sg]));
+    uint64_t* p = reinterpret_cast<uint64_t*>(ws.cand + ((int64_t)r * ws.nseg + sg) * kSegLen + (i - segoff[sg]));
     const uint64_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return make_uint2((uint32_t)v, (uint32_t)(v >> 32));
   };
@@ -563,7 +565,7 @@ __global__ __launch_bounds__(kSegThreads) void topk_segmented_kernel(TopkRows a,
           cur = nxt;
           nxt = sg + 1 < nseg_row ? segoff[sg + 1] : 0xFFFFFFFFu;
         }
-        uint64_t* p = reinterpret_cast<uint64_t*>(ws.cand + ((int64_t)r * ws.nseg + sg) * kSeg + (ic - cur));
+        uint64_t* p = reinterpret_cast<uint64_t*>(ws.cand + ((int64_t)r * ws.nseg + sg) * kSegLen + (ic - cur));
         const uint64_t x = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         v[j] = make_uint2((uint32_t)x, (uint32_t)(x >> 32));
       }
@@ -586,6 +588,13 @@ __global__ __launch_bounds__(kSegThreads) void topk_segmented_kernel(TopkRows a,
 
 }  // namespace
 
+int64_t seg_len_for(int64_t rows, int64_t max_len) {
+  // One round of segment workgroups on the GPU (2 per CU at the default LDS
+  // size); beyond that, twice as many scores per workgroup.
+  const int64_t nseg = (max_len + kSeg - 1) / kSeg;
+  return rows * nseg > 512 ? 2 * kSeg : kSeg;
+}
+
 int32_t seg_cap_for(int32_t k) {
   const int64_t cap = 2 * (int64_t)k + 2048;
   return (int32_t)(cap < kMaxCap ? cap : kMaxCap);
@@ -604,10 +613,17 @@ hipError_t allow_lds(K kernel, bool& done) {
 hipError_t launch_topk_segmented(const TopkRows& a, const SelWs& ws, hipStream_t stream) {
   if (a.rows <= 0) return hipSuccess;
   const int nseg = ws.nseg > 0 ? ws.nseg : 1;
-  static bool lds_set = false;
-  if (hipError_t e = allow_lds(topk_segmented_kernel, lds_set)) return e;
-  topk_segmented_kernel<<<dim3((unsigned)nseg, (unsigned)a.rows), dim3(kSegThreads),
-                          (size_t)ws.cap * sizeof(uint2), stream>>>(a, ws);
+  const dim3 grid((unsigned)nseg, (unsigned)a.rows);
+  const size_t lds = (size_t)ws.cap * sizeof(uint2);
+  if (ws.seg == 2 * kSeg) {
+    static bool lds_set = false;
+    if (hipError_t e = allow_lds(topk_segmented_kernel<2 * kSeg / kSegThreads>, lds_set)) return e;
+    topk_segmented_kernel<2 * kSeg / kSegThreads><<<grid, dim3(kSegThreads), lds, stream>>>(a, ws);
+  } else {
+    static bool lds_set = false;
+    if (hipError_t e = allow_lds(topk_segmented_kernel<kSeg / kSegThreads>, lds_set)) return e;
+    topk_segmented_kernel<kSeg / kSegThreads><<<grid, dim3(kSegThreads), lds, stream>>>(a, ws);
+  }
   return hipGetLastError();
 }
 
