@@ -83,3 +83,22 @@ def test_cfg3_prefill_sampled_rows():
     assert (gi_np >= 0).all()
     assert np.all(np.diff(gi_np, axis=1) > 0)
     assert np.all(gi_np.max(axis=1) <= x.qpos0 + np.arange(x.T))
+
+
+def test_prefill_all_equal_scores_overflow_a_histogram_bin():
+    # Zero head weights make every visible score 0, so one level-0 bin holds
+    # every visible key; rows with more than 65535 of them exceed the scan's
+    # 16-bit bin counters and must take the selection's own-histogram path.
+    # With all scores tied the lowest positions win.
+    x = inputs.make_prefill(205, T=3, L=65600, k=2048)
+    x.w[:] = 0.0
+    print(f"[prefill parity] tied scores T={x.T} L={x.L} qpos0={x.qpos0}", flush=True)
+    gi, gs = run_gpu(x)
+    gi, gs = gi.cpu().numpy(), gs.cpu().numpy()
+    for t in range(x.T):
+        vis = x.qpos0 + t + 1
+        assert vis > 65535
+        assert (gs[t, :vis] == 0.0).all() and np.isneginf(gs[t, vis:]).all()
+        ri, _, _ = oracle.index_prefill(x.q[t:t + 1], x.q_dt, x.q_scale[t:t + 1], x.w[t:t + 1], x.kc, x.k_dt,
+                                        x.k_scale, 1, x.L, x.qpos0 + t, x.H, x.D, x.k, want_scores=False)
+        assert np.array_equal(gi[t], ri[0]) and np.array_equal(ri[0], np.arange(x.k, dtype=np.int32))

@@ -25,7 +25,7 @@ def ref(scores, k, lens=None):
 
 
 @pytest.mark.parametrize("n,k", [(1, 1), (5, 3), (4096, 2048), (4097, 2048), (65536, 2048), (131072, 2048),
-                                 (131072, 8192), (20000, 16384), (3000, 1)])
+                                 (131072, 8192), (20000, 16384), (3000, 1), (70001, 2048)])
 def test_topk_random_rows(n, k):
     rng = np.random.default_rng(n * 7 + k)
     s = rng.standard_normal((3, n)).astype(np.float32)
