@@ -33,7 +33,7 @@ namespace {
 
 constexpr int kRowThreads = 512;   // per-row kernel
 constexpr int kSegThreads = 512;   // segmented kernel
-constexpr int kMaxCap = 12288;     // largest LDS candidate buffer (pairs) of either kernel
+constexpr int kMaxCap = 18432;     // largest LDS candidate buffer (pairs) of either kernel (144 KB)
 
 struct Row {
   const float* p;
