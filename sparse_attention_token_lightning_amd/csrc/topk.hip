@@ -34,6 +34,7 @@ namespace {
 constexpr int kRowThreads = 512;   // per-row kernel
 constexpr int kSegThreads = 512;   // segmented kernel
 constexpr int kMaxCap = 18432;     // largest LDS candidate buffer (pairs) of either kernel (144 KB)
+constexpr int kRegCand = 16;       // segmented kernel: candidates per thread held in registers
 
 struct Row {
   const float* p;
@@ -131,6 +132,27 @@ __device__ void find_digit(const uint32_t (&h)[PER], int top, uint32_t remaining
   __syncthreads();
 }
 
+// The digit of an nb-bin histogram (nb = 2048 or 1024) that holds the
+// `remaining`-th largest key; {digit, #keys above it, #in it} land in out[0..2].
+template <int NT>
+__device__ void hist_digit(const uint32_t* hist, int nb, uint32_t remaining, uint32_t* wsum,
+                           uint32_t* out) {
+  const int tid = threadIdx.x;
+  constexpr int PER = kSelBins / NT;  // digits per thread when nb = 2048
+  if (nb == kSelBins) {
+    uint32_t h[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) h[i] = hist[nb - 1 - (tid * PER + i)];
+    find_digit<NT, PER>(h, nb - 1, remaining, wsum, out);
+  } else {  // nb = 1024
+    constexpr int PH = PER / 2;
+    uint32_t h[PH];
+#pragma unroll
+    for (int i = 0; i < PH; ++i) h[i] = hist[nb - 1 - (tid * PH + i)];
+    find_digit<NT, PH>(h, nb - 1, remaining, wsum, out);
+  }
+}
+
 // One radix level over `count` keys: histogram of the nb digits at `shift`
 // among the keys matching (prefix, pmask), then the digit holding the
 // `remaining`-th largest.  Leaves {digit, #keys above it, #in it} in out.
@@ -146,19 +168,7 @@ __device__ void radix_level(KeyAt key_at, int64_t count, uint32_t prefix, uint32
     if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
   }
   __syncthreads();
-  constexpr int PER = kSelBins / NT;  // digits per thread when nb = 2048
-  if (nb == kSelBins) {
-    uint32_t h[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) h[i] = hist[nb - 1 - (tid * PER + i)];
-    find_digit<NT, PER>(h, nb - 1, remaining, wsum, out);
-  } else {  // nb = 1024
-    constexpr int PH = PER / 2;
-    uint32_t h[PH];
-#pragma unroll
-    for (int i = 0; i < PH; ++i) h[i] = hist[nb - 1 - (tid * PH + i)];
-    find_digit<NT, PH>(h, nb - 1, remaining, wsum, out);
-  }
+  hist_digit<NT>(hist, nb, remaining, wsum, out);
 }
 
 // Ordered compaction over `count` candidates in position order: keep keys > T
@@ -221,6 +231,73 @@ __device__ void select_keys(const Row& row, KeyAt key_at, PosAt pos_at, int64_t 
     __syncthreads();
   }
   compact<NT>(row, key_at, pos_at, count, prefix, remaining, kk, wsum);
+}
+
+// select_keys over candidates held in registers: thread t holds candidates
+// t + NT*j (j < R), so (round j, wave, lane) is position order; entries at or
+// past `count` are ignored.  The histograms are built from the registers, a
+// level whose threshold digit is kept whole ends the descent (keys are then
+// compared on the digits resolved so far), and the ordered compaction ranks
+// each round with two ballots (greater / equal) plus one block-wide scan of
+// the packed per-(round, wave) counts.  rcnt holds R * NT / 64 entries.
+template <int NT, int R>
+__device__ void select_regs(const Row& row, const uint2 (&v)[R], int64_t count, uint32_t prefix,
+                            uint32_t pmask, uint32_t remaining, int64_t kk, uint32_t* hist,
+                            uint32_t* wsum, uint32_t* rcnt, uint32_t* out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  constexpr int kW = NT / 64;
+  static_assert(R * kW <= NT, "one (round, wave) count per thread");
+#pragma unroll 1
+  for (int level = 1; level < 3; ++level) {
+    const int shift = level == 1 ? 10 : 0;
+    const int nb = level == 1 ? kSelBins : kSelBins / 2;
+    for (int i = tid; i < kSelBins; i += NT) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      if (j * NT + tid < (int)count && (v[j].x & pmask) == prefix)
+        atomicAdd(&hist[(v[j].x >> shift) & (uint32_t)(nb - 1)], 1u);
+    }
+    __syncthreads();
+    hist_digit<NT>(hist, nb, remaining, wsum, out);
+    prefix |= out[0] << shift;
+    pmask |= (uint32_t)(nb - 1) << shift;
+    remaining -= out[1];
+    const bool whole = out[2] == remaining;
+    __syncthreads();
+    if (whole) break;
+  }
+  // Counts are < 2^16 (count <= R * NT), so (greater, equal) share one word.
+  // The ballots are taken again in the write pass rather than kept.
+  const int cnt32 = (int)count;
+  auto gt = [&](int j) { return __ballot(j * NT + tid < cnt32 && (v[j].x & pmask) > prefix); };
+  auto eq = [&](int j) { return __ballot(j * NT + tid < cnt32 && (v[j].x & pmask) == prefix); };
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const uint64_t bg = gt(j), be = eq(j);
+    if (lane == 0) rcnt[j * kW + wave] = ((uint32_t)__popcll(bg) << 16) | (uint32_t)__popcll(be);
+  }
+  __syncthreads();
+  {
+    uint32_t total;
+    const uint32_t c = tid < R * kW ? rcnt[tid] : 0u;
+    const uint32_t ex = block_excl_scan<NT>(c, wsum, total);
+    if (tid < R * kW) rcnt[tid] = ex;
+    __syncthreads();
+  }
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  const uint32_t m = remaining;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const uint64_t bg = gt(j), be = eq(j);
+    const uint32_t base = rcnt[j * kW + wave];
+    const uint32_t gb = (base >> 16) + (uint32_t)__popcll(bg & below);
+    const uint32_t eb = (base & 0xFFFFu) + (uint32_t)__popcll(be & below);
+    int64_t slot = -1;
+    if ((bg >> lane) & 1ull) slot = (int64_t)gb + (eb < m ? eb : m);
+    else if (((be >> lane) & 1ull) && eb < m) slot = (int64_t)gb + eb;
+    if (slot >= 0 && slot < kk) row.out[slot] = map_pos(row, (int64_t)v[j].y);
+  }
 }
 
 enum SelHow : int32_t { kSelSelf = 1, kSelFull = 2 };
@@ -376,13 +453,15 @@ __global__ __launch_bounds__(kSegThreads) void topk_segmented_kernel(TopkRows a,
   // s0 + NT*e + tid (coalesced).
   const int64_t s0 = (int64_t)s * kSegLen;
   const int64_t s1 = (s0 + kSegLen) < n ? (s0 + kSegLen) : n;
+  const int slen = (int)(s1 - s0);  // segment-local indices are 32-bit
+  const float* sp = row.p + s0;
   const int lane = tid & 63, wave = tid >> 6;
   constexpr int kW = kSegThreads / 64;
   uint32_t key[kSegPer];
 #pragma unroll
   for (int e = 0; e < kSegPer; ++e) {
-    const int64_t i = s0 + (int64_t)e * kSegThreads + tid;
-    key[e] = key_clamped(row.p, i, s1);
+    const int ii = e * kSegThreads + tid;  // clamped, branch-free (ignored past the end)
+    key[e] = score_key(sp[ii < slen ? ii : slen - 1]);
   }
 
   // 1. Threshold bin b* from the row's partial histograms (16-bit, one per
@@ -465,12 +544,13 @@ __global__ __launch_bounds__(kSegThreads) void topk_segmented_kernel(TopkRows a,
   // 2. This segment's candidates, in position order: within a wave the kept
   //    positions are ranked with a ballot, and one scan over the (round, wave)
   //    counts gives every wave its output offset per round.
-  uint64_t ball[kSegPer];
+  // The ballots are taken again in the write pass rather than kept (64 bits
+  // per round would hold 2 kSegPer more registers across the scan).
+  auto keep = [&](int e) { return __ballot(e * kSegThreads + tid < slen && (key[e] >> kSelShift) >= bstar); };
 #pragma unroll
   for (int e = 0; e < kSegPer; ++e) {
-    const int64_t i = s0 + (int64_t)e * kSegThreads + tid;
-    ball[e] = __ballot(i < s1 && (key[e] >> kSelShift) >= bstar);
-    if (lane == 0) segoff[e * kW + wave] = (uint32_t)__popcll(ball[e]);
+    const uint64_t b = keep(e);
+    if (lane == 0) segoff[e * kW + wave] = (uint32_t)__popcll(b);
   }
   __syncthreads();
   uint32_t total;
@@ -489,10 +569,11 @@ __global__ __launch_bounds__(kSegThreads) void topk_segmented_kernel(TopkRows a,
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int e = 0; e < kSegPer; ++e) {
-    if ((ball[e] >> lane) & 1ull) {
-      const uint32_t pos = segoff[e * kW + wave] + (uint32_t)__popcll(ball[e] & below);
-      const int64_t i = s0 + (int64_t)e * kSegThreads + tid;
-      const uint64_t pr = (uint64_t)key[e] | ((uint64_t)(uint32_t)i << 32);
+    const uint64_t b = keep(e);
+    if ((b >> lane) & 1ull) {
+      const uint32_t pos = segoff[e * kW + wave] + (uint32_t)__popcll(b & below);
+      const uint32_t i = (uint32_t)s0 + (uint32_t)(e * kSegThreads + tid);
+      const uint64_t pr = (uint64_t)key[e] | ((uint64_t)i << 32);
       __hip_atomic_store(dst + pos, pr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -544,7 +625,30 @@ __global__ __launch_bounds__(kSegThreads) void topk_segmented_kernel(TopkRows a,
     return make_uint2((uint32_t)v, (uint32_t)(v >> 32));
   };
   const uint32_t pfx = bstar << kSelShift, pmask = 0xFFE00000u, rem = (uint32_t)kk - above;
-  if (ncl <= ws.cap) {
+  if (ncl <= (int64_t)kRegCand * kSegThreads) {
+    // Thread t loads candidates t + 512 j; its positions only grow, so its
+    // segment is tracked with a cursor that moves forward.  Indices past the
+    // end load the last candidate (branch-free loads), which is ignored.
+    int sg = seg_of(tid < ncl ? tid : ncl - 1);
+    uint32_t cur = segoff[sg];
+    uint32_t nxt = sg + 1 < nseg_row ? segoff[sg + 1] : 0xFFFFFFFFu;
+    uint2 v[kRegCand];
+#pragma unroll
+    for (int j = 0; j < kRegCand; ++j) {
+      const int64_t i = (int64_t)j * kSegThreads + tid;
+      const uint32_t ic = (uint32_t)(i < ncl ? i : ncl - 1);
+      while (ic >= nxt) {
+        ++sg;
+        cur = nxt;
+        nxt = sg + 1 < nseg_row ? segoff[sg + 1] : 0xFFFFFFFFu;
+      }
+      uint64_t* p = reinterpret_cast<uint64_t*>(ws.cand + ((int64_t)r * ws.nseg + sg) * kSegLen + (ic - cur));
+      const uint64_t x = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      v[j] = make_uint2((uint32_t)x, (uint32_t)(x >> 32));
+    }
+    __syncthreads();  // segoff is reused as the compaction's count table
+    select_regs<kSegThreads, kRegCand>(row, v, ncl, pfx, pmask, rem, kk, hist, wsum, segoff, shb);
+  } else if (ncl <= ws.cap) {
     // Batches of kBatch independent loads per thread, so their latencies
     // overlap.  A thread's positions only grow, so its segment is tracked with
     // a cursor that moves forward (next segment start cached in a register).
@@ -596,7 +700,13 @@ int64_t seg_len_for(int64_t rows, int64_t max_len) {
 }
 
 int32_t seg_cap_for(int32_t k) {
-  const int64_t cap = 2 * (int64_t)k + 2048;
+  // The candidates are the keys above the threshold bin (fewer than k) plus the
+  // whole threshold bin, a quarter of an octave of score values that can hold
+  // thousands of keys near the cut (rows of 128K LatentIndex scores put up to
+  // ~4.3K there at k = 2048).  8192 pairs still leave room for two workgroups
+  // per CU; rows beyond the cap take the slower global-memory path.
+  const int64_t a = 2 * (int64_t)k + 2048, b = 4 * (int64_t)k;
+  const int64_t cap = a > b ? a : b;
   return (int32_t)(cap < kMaxCap ? cap : kMaxCap);
 }
 
@@ -614,15 +724,19 @@ hipError_t launch_topk_segmented(const TopkRows& a, const SelWs& ws, hipStream_t
   if (a.rows <= 0) return hipSuccess;
   const int nseg = ws.nseg > 0 ? ws.nseg : 1;
   const dim3 grid((unsigned)nseg, (unsigned)a.rows);
-  const size_t lds = (size_t)ws.cap * sizeof(uint2);
-  if (ws.seg == 2 * kSeg) {
+  // Candidate sets up to kRegCand * kSegThreads stay in registers; the LDS
+  // buffer is only allocated for larger caps (k above 2048).
+  SelWs w = ws;
+  if (w.cap <= kRegCand * kSegThreads) w.cap = 0;
+  const size_t lds = (size_t)w.cap * sizeof(uint2);
+  if (w.seg == 2 * kSeg) {
     static bool lds_set = false;
     if (hipError_t e = allow_lds(topk_segmented_kernel<2 * kSeg / kSegThreads>, lds_set)) return e;
-    topk_segmented_kernel<2 * kSeg / kSegThreads><<<grid, dim3(kSegThreads), lds, stream>>>(a, ws);
+    topk_segmented_kernel<2 * kSeg / kSegThreads><<<grid, dim3(kSegThreads), lds, stream>>>(a, w);
   } else {
     static bool lds_set = false;
     if (hipError_t e = allow_lds(topk_segmented_kernel<kSeg / kSegThreads>, lds_set)) return e;
-    topk_segmented_kernel<kSeg / kSegThreads><<<grid, dim3(kSegThreads), lds, stream>>>(a, ws);
+    topk_segmented_kernel<kSeg / kSegThreads><<<grid, dim3(kSegThreads), lds, stream>>>(a, w);
   }
   return hipGetLastError();
 }

@@ -101,6 +101,19 @@ def test_decode_without_score_output_matches():
     assert np.array_equal(i0, i1)
 
 
+def test_decode_all_equal_scores_take_the_lowest_positions():
+    """w = 0 makes every score +0: the selection is positions 0 .. k-1.  Rows
+    whose candidate sets exceed the final step's register capacity (8192 keys)
+    and, for k = 4096, its LDS capacity (16384) take the slower paths."""
+    for seed, lens, k in ((109, [20000, 12000, 8192, 70000], 2048), (110, [12000, 30000, 4096], 4096)):
+        x = inputs.make_decode(seed, lens, k=k)
+        x.w = np.zeros_like(x.w)
+        parity(x, exact=True, what=f"all-equal k={k}")
+        gi, _ = run_gpu(x)
+        for b, n in enumerate(lens):
+            assert np.array_equal(gi[b], np.arange(min(n, k), dtype=np.int32)), f"all-equal k={k} b={b}"
+
+
 def test_decode_128k_sampled_requests():
     """The decode sweep's headline point (B = 32, L = 131072, fp8) on the GPU;
     the oracle checks two of the requests in full."""

@@ -66,6 +66,11 @@ def test_cfg4_latent_group_sampled_requests():
         check_topk_of_own_scores(gi[b], [gs[l, sl] for l in range(4)], [131072] * 4, x.k, f"cfg4 b={b}")
         for l in range(4):
             check_sets(gi[b, l], ri[0, l], rs[l], ra[l], 131072, what=f"cfg4 b={b} l={l}")
+    # Every request's selection against its own GPU scores: some of these rows
+    # put over 6000 candidate keys at or above the threshold bin.
+    for b in range(1, 15):
+        sl = slice(x.kv_off[b], x.kv_off[b + 1])
+        check_topk_of_own_scores(gi[b], [gs[l, sl] for l in range(4)], [131072] * 4, x.k, f"cfg4 b={b}")
 
 
 # ---- HS ------------------------------------------------------------------------
