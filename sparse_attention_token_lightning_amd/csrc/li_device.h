@@ -48,6 +48,17 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(int a, int b) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// One fp8 byte (OCP E4M3FN) -> float, exact.
+__device__ __forceinline__ float fp8_to_f32(uint32_t byte) {
+  const int v = (int)(byte & 0xFFu);
+  return __builtin_bit_cast(float, fp8x4_to_bf16x4(v).x << 16);
+}
+
+// 32x32x64 fp8 x fp8 -> fp32 matrix product (E4M3 operands, unit scales).
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 // Two bf16 (one dword) -> two fp16.  Exact for |x| in [2^-17, 65504]: bf16
 // carries 8 significant bits, fp16 11 (subnormals down to 2^-24).
 __device__ __forceinline__ int bf16x2_to_f16x2(int v) {

@@ -41,10 +41,6 @@ constexpr int kPfWaves = 4;
 constexpr int kPfTokPerWave = 2;
 constexpr int kPfTokPerBlock = kPfWaves * kPfTokPerWave;
 
-__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-
 __device__ __forceinline__ i32x8 ld32(const uint8_t* p) {
   const i32x4 x = ld16(p), y = ld16(p + 16);
   i32x8 r = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
@@ -91,12 +87,6 @@ constexpr int kPfWrite = 2;  // ... and written to LDS this many tiles before
 constexpr int kPfRegs = kPfLead - kPfWrite + 1;  // register slots for loads in flight
 static_assert(kPfRegs == 4 && kPfRing == 4, "the main loop is unrolled by 4");
 constexpr int kTileBytes = 32 * 128;
-
-// One fp8 byte (OCP E4M3FN) -> float, exact.
-__device__ __forceinline__ float fp8_to_f32(uint32_t byte) {
-  const int v = (int)(byte & 0xFFu);
-  return __builtin_bit_cast(float, fp8x4_to_bf16x4(v).x << 16);
-}
 
 // u[t][d] = sum_h w[t][h] * q_hat[t][h][d] in fp32, then split into
 // kLinTerms fp8 rows: row i holds round(r_i * 2^-e_i) with 2^e_i chosen so the

@@ -94,6 +94,27 @@ __device__ __forceinline__ int32_t map_pos(const Row& row, int64_t i) {
   return row.map ? row.map[i] : (int32_t)i;
 }
 
+// out[slot[e]] = position src[e] (through the row's map when it has one) for
+// the entries with 0 <= slot < kk.  The map loads are all issued before the
+// first store: gfx9's vmcnt counts stores too, so a load issued between stores
+// (or under a branch) would make every store wait for all earlier ones.
+template <int E>
+__device__ __forceinline__ void emit_slots(const Row& row, const int32_t (&slot)[E],
+                                           const int32_t (&src)[E], int64_t kk) {
+  if (row.map) {
+    int32_t pv[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) pv[e] = row.map[slot[e] >= 0 ? src[e] : 0];  // row.n >= 1 here
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (slot[e] >= 0 && slot[e] < kk) row.out[slot[e]] = pv[e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (slot[e] >= 0 && slot[e] < kk) row.out[slot[e]] = src[e];
+  }
+}
+
 // Key of element i of p[0 .. n-1] (n >= 1), loaded without a branch: an index
 // past the end reads element n-1 instead, and the caller ignores that key.
 // (A load under a branch makes the compiler wait for it before the branch
@@ -185,29 +206,30 @@ __device__ void compact(const Row& row, KeyAt key_at, PosAt pos_at, int64_t coun
     uint32_t cg = 0, ce = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      fl[e] = 0;
-      if (i0 + e < count) {
-        const uint32_t key = key_at(i0 + e);
-        fl[e] = key > T ? 2u : (key == T ? 1u : 0u);
-      }
+      const int64_t i = i0 + e < count ? i0 + e : count - 1;  // clamped, branch-free read
+      const uint32_t key = key_at(i);
+      fl[e] = i0 + e < count ? (key > T ? 2u : (key == T ? 1u : 0u)) : 0u;
       cg += fl[e] >> 1;
       ce += fl[e] & 1u;
     }
     uint32_t total;
     const uint32_t ex = block_excl_scan<NT>((cg << 16) | ce, wsum, total);
     uint32_t gb = gt_run + (ex >> 16), eb = eq_run + (ex & 0xFFFFu);
+    int32_t slot[4], src[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
+      slot[e] = -1;
+      src[e] = 0;
       if (fl[e] == 2u) {
-        const int64_t slot = (int64_t)gb + (eb < m ? eb : m);
-        if (slot < kk) row.out[slot] = map_pos(row, pos_at(i0 + e));
+        slot[e] = (int32_t)(gb + (eb < m ? eb : m));
         ++gb;
       } else if (fl[e] == 1u) {
-        const int64_t slot = (int64_t)gb + eb;
-        if (eb < m && slot < kk) row.out[slot] = map_pos(row, pos_at(i0 + e));
+        if (eb < m) slot[e] = (int32_t)(gb + eb);
         ++eb;
       }
+      if (slot[e] >= 0) src[e] = (int32_t)pos_at(i0 + e);
     }
+    emit_slots<4>(row, slot, src, kk);
     gt_run += total >> 16;
     eq_run += total & 0xFFFFu;
   }
@@ -287,17 +309,19 @@ __device__ void select_regs(const Row& row, const uint2 (&v)[R], int64_t count, 
   }
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   const uint32_t m = remaining;
+  int32_t slot[R], src[R];
 #pragma unroll
   for (int j = 0; j < R; ++j) {
     const uint64_t bg = gt(j), be = eq(j);
     const uint32_t base = rcnt[j * kW + wave];
     const uint32_t gb = (base >> 16) + (uint32_t)__popcll(bg & below);
     const uint32_t eb = (base & 0xFFFFu) + (uint32_t)__popcll(be & below);
-    int64_t slot = -1;
-    if ((bg >> lane) & 1ull) slot = (int64_t)gb + (eb < m ? eb : m);
-    else if (((be >> lane) & 1ull) && eb < m) slot = (int64_t)gb + eb;
-    if (slot >= 0 && slot < kk) row.out[slot] = map_pos(row, (int64_t)v[j].y);
+    slot[j] = -1;
+    if ((bg >> lane) & 1ull) slot[j] = (int32_t)(gb + (eb < m ? eb : m));
+    else if (((be >> lane) & 1ull) && eb < m) slot[j] = (int32_t)(gb + eb);
+    src[j] = (int32_t)v[j].y;
   }
+  emit_slots<R>(row, slot, src, kk);
 }
 
 enum SelHow : int32_t { kSelSelf = 1, kSelFull = 2 };

@@ -84,6 +84,23 @@ def test_fp8_conversion_covers_every_code():
     assert np.array_equal(gs[:n] + gs[n:], dec)
 
 
+def test_fp8_decode_query_spanning_many_octaves():
+    """fp8 keys against query rows whose elements span 2^0 .. 2^-30 inside each
+    head and whose heads differ by up to 2^40 in size: the fp8 path writes every
+    bf16 query row as two E4M3 rows under a per-head power-of-two scale, and
+    the scores must still meet the tolerance."""
+    x = inputs.make_decode(111, [3000, 1500, 40], k=256)
+    rng = np.random.default_rng(1111)
+    octave = 2.0 ** -(np.arange(128) % 31)
+    head = 2.0 ** (20.0 * (np.arange(64) % 3) - 20.0)
+    q = rng.standard_normal((x.B, 64, 128)) * octave[None, None, :] * head[None, :, None]
+    x.q = inputs.encode_bf16(q.astype(np.float32))
+    parity(x, what="fp8 q octaves")
+    x1 = inputs.make_decode(112, [2000], H=1, k=64)
+    x1.q = inputs.encode_bf16((rng.standard_normal((1, 1, 128)) * octave[None, None, :]).astype(np.float32))
+    parity(x1, what="fp8 q octaves H=1")
+
+
 def test_decode_scale_doubling_and_determinism():
     x = inputs.make_decode(107, [6000, 4100], k=512)
     i0, s0 = run_gpu(x)
