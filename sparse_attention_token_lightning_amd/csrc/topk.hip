@@ -6,14 +6,15 @@
 // selection is a radix select whose first level is the top 11 key bits: the
 // threshold bin b* is the level-0 bin that holds the k-th largest key.  Then
 // the keys whose bin is >= b* -- at most (k-1) + |b*| of them -- are gathered
-// in position order, two more LDS histogram levels over the keys of bin b*
-// give the exact k-th key T and the number m of keys equal to T that still
-// fit, and an ordered compaction writes the kept positions:
+// in position order (into registers or LDS), two more histogram levels over
+// the keys of bin b* give the exact k-th key T and the number m of keys equal
+// to T that still fit, and an ordered compaction writes the kept positions:
 //   slot = #greater-before + min(#equal-before, m),
 // so the output is in ascending position order and the lower position wins a
 // tie.  Rows with at most k visible keys return all of them; unused slots are
-// -1.  Candidate sets too large for LDS (heavy ties) are resolved the same way
-// from global memory.  Integer histograms make every path deterministic.
+// -1.  Candidate sets too large for registers and LDS (heavy ties) are
+// resolved the same way from global memory.  Integer histograms make every
+// path deterministic.
 //
 // Two kernels:
 //   segmented (decode, LatentIndex: few long rows): one workgroup per
