@@ -34,6 +34,7 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0    # dense fp8 MFMA
 BF16_PEAK_TFLOPS = 2500.0   # dense bf16 / fp16 MFMA
 FP8_KEY_BYTES = 128 + 4     # one fp8 key row + its fp32 scale
+RAGGED_COPIES = 6           # key-cache copies the ragged decode rotates over (MALL is 256 MB)
 METRIC = "decode indexer keys scored/s + HBM GB/s at 128K; prefill TFLOP/s; top-2048 µs"
 
 
@@ -150,7 +151,20 @@ def cpu_baseline(x, sample, min_s=10.0):
             break
     return {"value": n * runs / dt, "unit": "keys/s", "cores": min(threads, b), "kind": "oracle",
             "sample": f"{b} of {x.B} requests x {int(x.kv_off[1] - x.kv_off[0])} keys "
-                      f"(scan + top-{x.k}, fp64, OpenMP over requests), {runs} runs in {dt:.1f} s"}
+                      f"(scan + top-{x.k}, fp64, OpenMP over requests), {runs} runs in {dt:.1f} s",
+            "host_cpu": host_cpu(), "host_logical_cpus": os.cpu_count()}
+
+
+def host_cpu():
+    """The host's CPU model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def components(torch, li, inputs, args):
@@ -216,17 +230,27 @@ def components(torch, li, inputs, args):
         "native_decode_ms": native, "four_native_layers_over_hs": 4 * native / hs_ms}
     del aq, aw, akc, aks, off, fq, fw, fwd, lat, cand, fidx, nidx, ws_a, ws_f, h, a, f
     # ---- ragged batched decode: B = 32, L_b ~ U{8192..32768} (fp8) --------------
+    # Its 86.5 MB of keys would fit in the 256 MB MALL, so the calls rotate over
+    # six copies of the cache (519 MB): each call reads keys last touched five
+    # calls earlier, after more than the MALL's size of other traffic.
     x = inputs.cfg2()
-    q, w, kc, ks, off = dev(torch, x.q, "bf16"), dev(torch, x.w), dev(torch, x.kc, "fp8_e4m3"), \
-        dev(torch, x.k_scale), dev(torch, x.kv_off)
+    q, w, off = dev(torch, x.q, "bf16"), dev(torch, x.w), dev(torch, x.kv_off)
+    copies = [(dev(torch, x.kc, "fp8_e4m3"), dev(torch, x.k_scale)) for _ in range(RAGGED_COPIES)]
     idx = torch.empty((x.B, x.k), dtype=torch.int32, device="cuda")
     ws = torch.empty(L.li_index_decode_ws(x.B, x.n_tok, int(x.lens.max()), x.k, 0), dtype=torch.uint8, device="cuda")
-    fn = lambda: li.li_index_decode(q, w, kc, ks, off, int(x.lens.max()), x.k, out_idx=idx, ws=ws)
-    wall, (scan, topk) = timed(torch, li, fn, 3, args.comp_iters, 2)
+    turn = [0]
+
+    def fn():
+        kc, ks = copies[turn[0] % RAGGED_COPIES]
+        turn[0] += 1
+        li.li_index_decode(q, w, kc, ks, off, int(x.lens.max()), x.k, out_idx=idx, ws=ws)
+    wall, (scan, topk) = timed(torch, li, fn, 3, max(args.comp_iters, 2 * RAGGED_COPIES), 2)
     out["decode_fp8_B32_ragged8K-32K"] = {
         "scan_ms": scan, "topk_ms": topk, "total_ms": wall, "keys": x.n_tok,
-        "scan_gbs_algorithmic": x.n_tok * FP8_KEY_BYTES / (scan * 1e-3) / 1e9,
-        "note": "86.5 MB of keys fit in the 256 MB MALL; not an HBM figure"}
+        "scan_gbs": x.n_tok * FP8_KEY_BYTES / (scan * 1e-3) / 1e9,
+        "scan_hbm_frac": x.n_tok * FP8_KEY_BYTES / (scan * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "note": f"calls rotate over {RAGGED_COPIES} copies of the 86.5 MB cache so the keys come from HBM, "
+                "not the 256 MB MALL"}
     return out
 
 

@@ -38,9 +38,16 @@
  *     LI_E_HIP; li_last_error() then holds the HIP error text (thread-local).
  *   - Device contents are not validated: kv_off must be non-decreasing with
  *     kv_off[0] >= 0, lengths must not exceed max_len, scales must be finite
- *     and positive, inputs must not hold NaN/Inf codes.  Otherwise the
- *     results are undefined (but every access stays inside the sizes the
- *     host was given).
+ *     and positive, inputs must not hold NaN/Inf codes, candidate rows must be
+ *     ascending inside [0, L_b) with -1 only at their end.  Otherwise the
+ *     results are undefined, and an offset or candidate pointing past its
+ *     buffer makes the kernels read past it too.
+ *   - Debug validation: with the environment variable LI_DEBUG_VALIDATE set
+ *     (to anything but "" or "0") at the time of a call, the entry point
+ *     first runs device-side checks of those preconditions on its
+ *     inputs, waits for them on `stream` (so such calls synchronise and must
+ *     not be captured into a graph) and returns LI_E_VALUE if one fails;
+ *     li_last_error() names the failed check and the element index.
  *   - Output index rows hold the kept positions in ascending order; a row
  *     with fewer than k visible positions returns all of them and pads the
  *     rest of its k slots with -1.  Scores compare as IEEE values with
@@ -66,6 +73,7 @@ typedef int32_t li_status;
 #define LI_E_WORKSPACE 4   /* ws_bytes is smaller than the li_*_ws() query */
 #define LI_E_UNSUPPORTED 5 /* a shape outside the supported set (see each entry point) */
 #define LI_E_HIP 6         /* a HIP runtime call or kernel launch failed */
+#define LI_E_VALUE 7       /* LI_DEBUG_VALIDATE only: a device input broke a precondition */
 
 typedef int32_t li_dtype;
 #define LI_BF16 0

@@ -4,6 +4,8 @@
 // the caller's stream.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include <string>
 
@@ -47,6 +49,29 @@ li_status hip_check(hipError_t e, const char* what, hipStream_t s) {
     return LI_OK;
   }
   return fail(LI_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// LI_DEBUG_VALIDATE, read at every call.
+bool validate_on() {
+  const char* e = getenv("LI_DEBUG_VALIDATE");
+  return e != nullptr && *e != '\0' && strcmp(e, "0") != 0;
+}
+
+// Enqueues the checks `enqueue` adds, waits for them and reports the first
+// failed one as LI_E_VALUE.
+template <typename F>
+li_status run_validation(hipStream_t s, F enqueue) {
+  hipError_t e = li::validate_begin(s);
+  if (e != hipSuccess) return fail(LI_E_HIP, "validation: %s", hipGetErrorString(e));
+  enqueue();
+  uint32_t check = 0;
+  int64_t index = 0;
+  e = li::validate_end(s, &check, &index);
+  if (e != hipSuccess) return fail(LI_E_HIP, "validation: %s", hipGetErrorString(e));
+  if (check != 0)
+    return fail(LI_E_VALUE, "LI_DEBUG_VALIDATE: %s (element %lld)", li::validate_name(check),
+                (long long)index);
+  return LI_OK;
 }
 
 constexpr size_t kAlign = 256;
@@ -172,6 +197,7 @@ const char* li_status_str(li_status s) {
     case LI_E_WORKSPACE: return "LI_E_WORKSPACE";
     case LI_E_UNSUPPORTED: return "LI_E_UNSUPPORTED";
     case LI_E_HIP: return "LI_E_HIP";
+    case LI_E_VALUE: return "LI_E_VALUE";
     default: return "LI_E_UNKNOWN";
   }
 }
@@ -211,6 +237,15 @@ li_status li_index_decode(const void* q, li_dtype q_dt, const float* w, const vo
   if ((st = check_ws(ws, ws_bytes, decode_ws(B, n_tok, max_len, out_scores != nullptr)))) return st;
   if (B == 0) return LI_OK;
   hipStream_t s = (hipStream_t)stream;
+  if (validate_on() && (st = run_validation(s, [&] {
+        li::validate_offsets(kv_off, B, n_tok, max_len, s);
+        li::validate_bf16(q, (int64_t)B * H * D, li::kBadQ, s);
+        li::validate_f32(w, (int64_t)B * H, li::kBadW, s);
+        if (k_dt == LI_FP8_E4M3) li::validate_fp8(k_cache, n_tok * D, li::kBadKeys, s);
+        else li::validate_bf16(k_cache, n_tok * D, li::kBadKeys, s);
+        li::validate_scales(k_scale, n_tok, li::kBadKScale, s);
+      })))
+    return st;
   trace_begin(s);
   Carver cv(ws);
   float* scores = out_scores ? out_scores : (float*)cv.take((size_t)n_tok * 4);
@@ -255,6 +290,14 @@ li_status li_index_prefill(const void* q, li_dtype q_dt, const float* q_scale, c
   if ((st = check_ws(ws, ws_bytes, prefill_ws(T, L, out_scores != nullptr)))) return st;
   if (T == 0) return LI_OK;
   hipStream_t s = (hipStream_t)stream;
+  if (validate_on() && (st = run_validation(s, [&] {
+        li::validate_fp8(q, (int64_t)T * H * D, li::kBadQ, s);
+        li::validate_scales(q_scale, T, li::kBadQScale, s);
+        li::validate_f32(w, (int64_t)T * H, li::kBadW, s);
+        li::validate_fp8(k_cache, (int64_t)L * D, li::kBadKeys, s);
+        li::validate_scales(k_scale, L, li::kBadKScale, s);
+      })))
+    return st;
   trace_begin(s);
   Carver cv(ws);
   float* scores = out_scores ? out_scores : (float*)cv.take((size_t)T * (size_t)L * 4);
@@ -317,6 +360,15 @@ li_status li_latent_score_group(const void* q, li_dtype q_dt, const float* w, co
     return st;
   if (B == 0) return LI_OK;
   hipStream_t s = (hipStream_t)stream;
+  if (validate_on() && (st = run_validation(s, [&] {
+        li::validate_offsets(kv_off, B, n_tok, max_len, s);
+        li::validate_bf16(q, (int64_t)B * G * H * Dh, li::kBadQ, s);
+        li::validate_f32(w, (int64_t)B * G * H, li::kBadW, s);
+        li::validate_bf16(w_dec, (int64_t)G * Dc * H * Dh, li::kBadWDec, s);
+        li::validate_bf16(latent, n_tok * Dc, li::kBadLatent, s);
+        li::validate_scales(c_scale, n_tok, li::kBadCScale, s);
+      })))
+    return st;
   trace_begin(s);
   Carver cv(ws);
   uint16_t* qt16 = (uint16_t*)cv.take((size_t)B * G * H * Dc * 2);
@@ -366,6 +418,16 @@ li_status li_hs_refine(const int32_t* cand_idx, int32_t C, const void* q, li_dty
   if ((st = check_ws(ws, ws_bytes, hs_ws(B, C, Gf, H, Dc, out_scores != nullptr)))) return st;
   if (B == 0) return LI_OK;
   hipStream_t s = (hipStream_t)stream;
+  // The latent cache's length is not an argument here: its rows are checked
+  // through the candidates (each inside its request) and kv_off's order.
+  if (validate_on() && (st = run_validation(s, [&] {
+        li::validate_offsets(kv_off, B, INT64_MAX, INT32_MAX, s);
+        li::validate_cands(cand_idx, B, C, kv_off, s);
+        li::validate_bf16(q, (int64_t)B * Gf * H * Dh, li::kBadQ, s);
+        li::validate_f32(w, (int64_t)B * Gf * H, li::kBadW, s);
+        li::validate_bf16(w_dec, (int64_t)Gf * Dc * H * Dh, li::kBadWDec, s);
+      })))
+    return st;
   trace_begin(s);
   Carver cv(ws);
   uint16_t* qt16 = (uint16_t*)cv.take((size_t)B * Gf * H * Dc * 2);
@@ -418,6 +480,11 @@ li_status li_topk(const float* scores, int64_t row_stride, const int32_t* row_le
   tr.k = k;
   tr.out = out_idx;
   hipStream_t s = (hipStream_t)stream;
+  if (validate_on() && (st = run_validation(s, [&] {
+        li::validate_row_len(row_len, rows, row_stride, s);
+        li::validate_score_rows(scores, row_stride, rows, n, row_len, s);
+      })))
+    return st;
   trace_begin(s);
   return hip_check(li::launch_topk(tr, s), "topk launch", s);
 }

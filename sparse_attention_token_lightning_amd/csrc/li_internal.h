@@ -90,4 +90,37 @@ hipError_t launch_hs_score(const uint16_t* qt16, const float* wsc, const uint16_
                            int32_t C, int32_t B, int32_t Gf, int32_t H, int32_t Dc, float* scores,
                            hipStream_t stream);
 
+// Opt-in input checks (LI_DEBUG_VALIDATE): validate_begin clears the device
+// record, the validate_* calls enqueue one check each, validate_end waits for
+// them and returns the first failed check (0 = none) and its element index.
+enum ValidateCheck : uint32_t {
+  kBadOffsetRange = 1,
+  kBadOffsetOrder,
+  kBadLength,
+  kBadKScale,
+  kBadQScale,
+  kBadCScale,
+  kBadW,
+  kBadQ,
+  kBadKeys,
+  kBadLatent,
+  kBadWDec,
+  kBadCandidate,
+  kBadCandidateOrder,
+  kBadScores,
+  kBadRowLen,
+};
+hipError_t validate_begin(hipStream_t s);
+void validate_offsets(const int64_t* off, int32_t B, int64_t n_tok, int32_t max_len, hipStream_t s);
+void validate_scales(const float* p, int64_t n, uint32_t check, hipStream_t s);
+void validate_f32(const float* p, int64_t n, uint32_t check, hipStream_t s);
+void validate_bf16(const void* p, int64_t n, uint32_t check, hipStream_t s);
+void validate_fp8(const void* p, int64_t n, uint32_t check, hipStream_t s);
+void validate_cands(const int32_t* cand, int32_t B, int32_t C, const int64_t* off, hipStream_t s);
+void validate_score_rows(const float* p, int64_t stride, int32_t rows, int32_t n, const int32_t* len,
+                         hipStream_t s);
+void validate_row_len(const int32_t* len, int32_t rows, int64_t stride, hipStream_t s);
+hipError_t validate_end(hipStream_t s, uint32_t* check, int64_t* index);
+const char* validate_name(uint32_t check);
+
 }  // namespace li

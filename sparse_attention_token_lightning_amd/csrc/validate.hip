@@ -1,0 +1,175 @@
+// Opt-in checks of device inputs (the LI_DEBUG_VALIDATE environment variable).
+//
+// The entry points never read device memory on the host, so on the normal
+// path the preconditions on device contents (monotone kv_off, positive finite
+// scales, no NaN/Inf codes, ascending candidate rows) are the caller's to
+// keep.  With LI_DEBUG_VALIDATE set, an entry point first runs these kernels
+// over its inputs, waits for them and returns LI_E_VALUE naming a violation
+// it found.  Each kernel is a grid-stride loop with no other synchronisation;
+// a violation is recorded by a compare-and-swap on a small device-resident
+// record (the first report to land wins, its element index alongside).
+#include "li_device.h"
+#include "li_internal.h"
+
+namespace li {
+namespace {
+
+__device__ uint32_t g_bad[4];  // [0] check id (0 = none), [1..2] element index (lo, hi)
+
+__device__ void report(uint32_t check, int64_t i) {
+  if (atomicCAS(&g_bad[0], 0u, check) == 0u) {
+    g_bad[1] = (uint32_t)(uint64_t)i;
+    g_bad[2] = (uint32_t)((uint64_t)i >> 32);
+  }
+}
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ int64_t gtid() { return (int64_t)blockIdx.x * kThreads + threadIdx.x; }
+__device__ __forceinline__ int64_t gstride() { return (int64_t)gridDim.x * kThreads; }
+
+__global__ __launch_bounds__(kThreads) void offsets_kernel(const int64_t* off, int32_t B, int64_t n_tok,
+                                                           int32_t max_len) {
+  for (int64_t b = gtid(); b <= B; b += gstride()) {
+    const int64_t v = off[b];
+    if (v < 0 || v > n_tok) report(kBadOffsetRange, b);
+    if (b < B) {
+      const int64_t len = off[b + 1] - v;
+      if (len < 0) report(kBadOffsetOrder, b);
+      else if (len > max_len) report(kBadLength, b);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void scales_kernel(const float* p, int64_t n, uint32_t check) {
+  for (int64_t i = gtid(); i < n; i += gstride()) {
+    const float v = p[i];
+    if (!(v > 0.0f) || !isfinite(v)) report(check, i);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void f32_kernel(const float* p, int64_t n, uint32_t check) {
+  for (int64_t i = gtid(); i < n; i += gstride())
+    if (!isfinite(p[i])) report(check, i);
+}
+
+// bf16: exponent field all ones is Inf or NaN.
+__global__ __launch_bounds__(kThreads) void bf16_kernel(const uint16_t* p, int64_t n, uint32_t check) {
+  for (int64_t i = gtid(); i < n; i += gstride())
+    if ((p[i] & 0x7F80u) == 0x7F80u) report(check, i);
+}
+
+// OCP E4M3FN: 0x7F and 0xFF are its only NaN codes (it has no infinities).
+__global__ __launch_bounds__(kThreads) void fp8_kernel(const uint8_t* p, int64_t n, uint32_t check) {
+  for (int64_t i = gtid(); i < n; i += gstride())
+    if ((p[i] & 0x7Fu) == 0x7Fu) report(check, i);
+}
+
+// Scores handed to li_topk: +-Inf are valid (masked entries), NaN is not.
+// Row r holds len[r] scores (clamped to [0, cols]) or, without len, cols.
+__global__ __launch_bounds__(kThreads) void nan_rows_kernel(const float* p, int64_t stride, int32_t rows,
+                                                            int64_t cols, const int32_t* len) {
+  for (int64_t i = gtid(); i < (int64_t)rows * cols; i += gstride()) {
+    const int64_t r = i / cols, c = i % cols;
+    int64_t n = len ? (int64_t)len[r] : cols;
+    n = n < 0 ? 0 : (n > cols ? cols : n);
+    if (c < n) {
+      const float v = p[r * stride + c];
+      if (v != v) report(kBadScores, r * stride + c);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void row_len_kernel(const int32_t* len, int32_t rows, int64_t stride) {
+  for (int64_t r = gtid(); r < rows; r += gstride())
+    if (len[r] < 0 || len[r] > stride) report(kBadRowLen, r);
+}
+
+// Candidate rows: valid entries strictly ascending inside [0, L_b), then -1 only.
+__global__ __launch_bounds__(kThreads) void cands_kernel(const int32_t* cand, int32_t B, int32_t C,
+                                                         const int64_t* off) {
+  for (int64_t i = gtid(); i < (int64_t)B * C; i += gstride()) {
+    const int64_t b = i / C, j = i % C;
+    const int64_t len = off[b + 1] - off[b];
+    const int32_t v = cand[i];
+    if (v < -1 || v >= len) report(kBadCandidate, i);
+    else if (j > 0) {
+      const int32_t u = cand[i - 1];
+      if (u == -1 ? v != -1 : (v != -1 && v <= u)) report(kBadCandidateOrder, i);
+    }
+  }
+}
+
+unsigned blocks_for(int64_t n) {
+  const int64_t b = (n + kThreads - 1) / kThreads;
+  return (unsigned)(b < 1 ? 1 : (b > 2048 ? 2048 : b));
+}
+
+}  // namespace
+
+hipError_t validate_begin(hipStream_t s) {
+  static const uint32_t zero[4] = {0u, 0u, 0u, 0u};
+  return hipMemcpyToSymbolAsync(HIP_SYMBOL(g_bad), zero, sizeof zero, 0, hipMemcpyHostToDevice, s);
+}
+
+void validate_offsets(const int64_t* off, int32_t B, int64_t n_tok, int32_t max_len, hipStream_t s) {
+  offsets_kernel<<<blocks_for((int64_t)B + 1), kThreads, 0, s>>>(off, B, n_tok, max_len);
+}
+void validate_scales(const float* p, int64_t n, uint32_t check, hipStream_t s) {
+  if (p && n > 0) scales_kernel<<<blocks_for(n), kThreads, 0, s>>>(p, n, check);
+}
+void validate_f32(const float* p, int64_t n, uint32_t check, hipStream_t s) {
+  if (p && n > 0) f32_kernel<<<blocks_for(n), kThreads, 0, s>>>(p, n, check);
+}
+void validate_bf16(const void* p, int64_t n, uint32_t check, hipStream_t s) {
+  if (p && n > 0) bf16_kernel<<<blocks_for(n), kThreads, 0, s>>>((const uint16_t*)p, n, check);
+}
+void validate_fp8(const void* p, int64_t n, uint32_t check, hipStream_t s) {
+  if (p && n > 0) fp8_kernel<<<blocks_for(n), kThreads, 0, s>>>((const uint8_t*)p, n, check);
+}
+void validate_cands(const int32_t* cand, int32_t B, int32_t C, const int64_t* off, hipStream_t s) {
+  if (B > 0 && C > 0) cands_kernel<<<blocks_for((int64_t)B * C), kThreads, 0, s>>>(cand, B, C, off);
+}
+
+void validate_score_rows(const float* p, int64_t stride, int32_t rows, int32_t n, const int32_t* len,
+                         hipStream_t s) {
+  const int64_t cols = len ? stride : n;
+  if (rows > 0 && cols > 0)
+    nan_rows_kernel<<<blocks_for((int64_t)rows * cols), kThreads, 0, s>>>(p, stride, rows, cols, len);
+}
+void validate_row_len(const int32_t* len, int32_t rows, int64_t stride, hipStream_t s) {
+  if (len && rows > 0) row_len_kernel<<<blocks_for(rows), kThreads, 0, s>>>(len, rows, stride);
+}
+
+hipError_t validate_end(hipStream_t s, uint32_t* check, int64_t* index) {
+  uint32_t r[4] = {0u, 0u, 0u, 0u};
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = hipMemcpyFromSymbolAsync(r, HIP_SYMBOL(g_bad), sizeof r, 0, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  *check = r[0];
+  *index = (int64_t)(((uint64_t)r[2] << 32) | r[1]);
+  return e;
+}
+
+const char* validate_name(uint32_t check) {
+  switch (check) {
+    case kBadOffsetRange: return "kv_off entry outside [0, n_tok]";
+    case kBadOffsetOrder: return "kv_off decreases";
+    case kBadLength: return "a request longer than max_len";
+    case kBadKScale: return "k_scale not finite and positive";
+    case kBadQScale: return "q_scale not finite and positive";
+    case kBadCScale: return "c_scale not finite and positive";
+    case kBadW: return "w not finite";
+    case kBadQ: return "q holds a NaN/Inf code";
+    case kBadKeys: return "k_cache holds a NaN/Inf code";
+    case kBadLatent: return "latent holds a NaN/Inf code";
+    case kBadWDec: return "w_dec holds a NaN/Inf code";
+    case kBadCandidate: return "cand_idx entry outside [-1, L_b)";
+    case kBadCandidateOrder: return "cand_idx row not ascending with -1 only at its end";
+    case kBadScores: return "scores hold a NaN";
+    case kBadRowLen: return "row_len entry outside [0, row_stride]";
+    default: return "unknown check";
+  }
+}
+
+}  // namespace li

@@ -45,6 +45,7 @@ def test_status_strings():
     L = li.lib()
     assert L.li_status_str(li.LI_OK) == b"LI_OK"
     assert L.li_status_str(li.LI_E_WORKSPACE) == b"LI_E_WORKSPACE"
+    assert L.li_status_str(li.LI_E_VALUE) == b"LI_E_VALUE"
     assert L.li_status_str(99) == b"LI_E_UNKNOWN"
 
 
