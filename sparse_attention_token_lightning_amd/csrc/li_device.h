@@ -59,6 +59,35 @@ __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// 16x16x128 fp8 x fp8 -> fp32 matrix product (E4M3 operands, unit scales).
+// Operand lane l holds row / column (l & 15) and 32 consecutive K bytes of
+// lane group l >> 4 (A and B pair K the same way); result lane l holds rows
+// 4 * (l >> 4) + i, column l & 15.
+__device__ __forceinline__ f32x4 mfma_fp8_16(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Cross-lane folds with gfx950's lane-swap instructions.  swap_sum32(a, b):
+// lanes 0-31 get a[l] + a[l + 32], lanes 32-63 get b[l - 32] + b[l].
+// swap_sum16(a, b): in each 32-lane half, lanes 0-15 get a[l] + a[l + 16] and
+// lanes 16-31 get b[l - 16] + b[l].  The swap returns both registers; the
+// empty asm keeps the second one a distinct value (without it this compiler
+// folds first + second into first + first).
+__device__ __forceinline__ float swap_sum32(float a, float b) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a),
+                                                   __builtin_bit_cast(unsigned, b), false, false);
+  unsigned x = sw[0], y = sw[1];
+  asm volatile("" : "+v"(y));
+  return __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
+}
+__device__ __forceinline__ float swap_sum16(float a, float b) {
+  const auto sw = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a),
+                                                   __builtin_bit_cast(unsigned, b), false, false);
+  unsigned x = sw[0], y = sw[1];
+  asm volatile("" : "+v"(y));
+  return __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
+}
+
 // Two bf16 (one dword) -> two fp16.  Exact for |x| in [2^-17, 65504]: bf16
 // carries 8 significant bits, fp16 11 (subnormals down to 2^-24).
 __device__ __forceinline__ int bf16x2_to_f16x2(int v) {

@@ -6,7 +6,7 @@
 //
 // This is a dense contraction (M = T*64 query-head rows, N = L keys, K = 128)
 // with fp8 operands, so it runs on the fp8 matrix cores
-// (v_mfma_f32_32x32x64_f8f6f4, OCP E4M3 for both operands); fully masked key
+// (v_mfma_f32_16x16x128_f8f6f4, OCP E4M3 for both operands); fully masked key
 // tiles are never computed.
 //
 // The epilogue is the expensive part: every (head, key) product needs a ReLU
@@ -21,12 +21,15 @@
 // encoding what the previous rows left over (relative residual ~2^-16; the
 // tolerance on a score is 2e-3 of sum_h |w_h x_h|).
 //
-// Mapping: a wave owns two query tokens: four 32-row M blocks of heads plus
-// one block holding both tokens' u rows (rows 4*slot + i), all in registers,
-// and walks the visible keys 32 at a time.  Lane l works on key (l & 31) and
-// dims 64*(l >> 5) .. +63 of it.  After the MFMAs, lane half g finishes token
-// slot g: it adds its half of the |x| sum to the other half's (one shuffle),
-// takes u . k from the u rows it holds (rows 4g .. 4g+3), and stores.
+// Mapping: a wave owns two query tokens: four 16-row blocks of heads per
+// token plus one block holding both tokens' u rows (rows 4*slot + i), all in
+// registers, and walks the visible keys 32 at a time as two 16-key blocks, one
+// 16x16x128 product per (head block, key block) covering all 128 dims.  Small
+// products keep the epilogue's registers small, so each block's epilogue runs
+// on the VALU while the matrix core works on the products issued after it
+// (two blocks ahead).  A lane's block results are 4 heads of one key; after
+// the tile, two permlane32 swaps and one permlane16 swap fold the four lane
+// groups' head sums so that lane l holds token slot l >> 5 at key l & 31.
 //
 // A wave owns whole rows, so it also builds each row's level-0 selection
 // histogram in LDS and finds the row's threshold bin for the top-k itself.
@@ -167,46 +170,51 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
 
   for (int i = lane; i < kPfTokPerWave * kSelBins / 2; i += 64) (&phist[wave][0][0])[i] = 0;
 
-  // Query heads (A operand, row = head hb*32 + col), the weights of the heads
-  // whose results this lane holds (rows 8*(r/4) + 4*g + r%4 of each block),
-  // and the u rows: A row col < 8 is u row (col & 3) of token slot col >> 2.
-  i32x8 qa[kPfTokPerWave][2][2];
-  float wl[kPfTokPerWave][2][16];
-  i32x8 ua[2];
+  // Query heads (A operand: row = head 16*hb + c16, dims 32*g4 .. +31), the
+  // weights of the heads whose results this lane holds (rows 4*g4 + i of each
+  // head block), and the u rows: A row c16 < 8 is u row (c16 & 3) of token
+  // slot c16 >> 2.  Lane group g4 < 2 holds token slot g4's u results and its
+  // u-row scales; the other groups' rows are zero.
+  const int c16 = lane & 15, g4 = lane >> 4;
+  i32x8 qa[kPfTokPerWave][4];
+  float wl[kPfTokPerWave][4][4];
 #pragma unroll
   for (int tk = 0; tk < kPfTokPerWave; ++tk) {
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int row = hb * 32 + col;
+    for (int hb = 0; hb < 4; ++hb) {
+      const int head = 16 * hb + c16;
+      // Clamped, unconditional load (rows past H are zeroed afterwards).
+      i32x8 v = ld32(q + ((int64_t)trow[tk] * H + (head < H ? head : H - 1)) * 128 + 32 * g4);
+      if (head >= H) v = i32x8{};
+      qa[tk][hb] = v;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        // Clamped, unconditional load (rows past H are zeroed afterwards).
-        i32x8 v = ld32(q + ((int64_t)trow[tk] * H + (row < H ? row : H - 1)) * 128 + 64 * g + 32 * j);
-        if (row >= H) v = i32x8{};
-        qa[tk][hb][j] = v;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int head = hb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        const float wv = w[(int64_t)trow[tk] * H + (head < H ? head : H - 1)];
-        wl[tk][hb][r] = head < H ? wv : 0.0f;
+      for (int i = 0; i < 4; ++i) {
+        const int hr = 16 * hb + 4 * g4 + i;
+        const float wv = w[(int64_t)trow[tk] * H + (hr < H ? hr : H - 1)];
+        wl[tk][hb][i] = hr < H ? wv : 0.0f;
       }
     }
   }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const bool urow = col < kLinTerms * kPfTokPerWave;
-    const int uc = urow ? col : 0;
-    i32x8 v = ld32(uq + ((int64_t)trow[uc >> 2] * kLinTerms + (uc & 3)) * 128 + 64 * g + 32 * j);
+  i32x8 ua;
+  {
+    const bool urow = c16 < kLinTerms * kPfTokPerWave;
+    const int uc = urow ? c16 : 0;
+    i32x8 v = ld32(uq + ((int64_t)trow[uc >> 2] * kLinTerms + (uc & 3)) * 128 + 32 * g4);
     if (!urow) v = i32x8{};
-    ua[j] = v;
+    ua = v;
   }
-  // This half's token: its scales and the scales of its u rows.
+  float us[kLinTerms];
+  {
+    const int ut = trow[g4 < kPfTokPerWave ? g4 : 0];
+#pragma unroll
+    for (int i = 0; i < kLinTerms; ++i) {
+      const float v = usc[(int64_t)ut * kLinTerms + i];
+      us[i] = g4 < kPfTokPerWave ? v : 0.0f;
+    }
+  }
+  // This half's token (the one lane l finishes: slot l >> 5) and its scale.
   const int tg = trow[g];
   const float sq = (q_scale ? q_scale[tg] : 1.0f) * 0.5f;
-  float us[kLinTerms];
-#pragma unroll
-  for (int i = 0; i < kLinTerms; ++i) us[i] = usc[(int64_t)tg * kLinTerms + i];
 
   // Tiles this wave needs, and tiles the workgroup walks (every wave takes
   // part in every tile's barrier; the extra tiles are fully masked for it).
@@ -222,20 +230,24 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
   };
   // This wave's share of a tile: keys 8*wave + lane/8, chunk lane % 8.
   const int ld_key = 8 * wave + (lane >> 3), ld_chunk = lane & 7;
-  const int ld_off = ld_key * 128 + 16 * (ld_chunk ^ (ld_key & 7));
+  const int ld_off = ld_key * 128 + 16 * (ld_chunk ^ ((ld_key >> 1) & 7));
   auto gload = [&](int it) {
     int row = it * 32 + ld_key;
     row = row < L ? row : L - 1;
     return ld16(kc + (int64_t)row * 128 + 16 * ld_chunk);
   };
   auto lds_put = [&](int slot, i32x4 v) { *reinterpret_cast<i32x4*>(&ktile[slot][ld_off]) = v; };
+  // B operand of key block j: key 16*j + c16, dims 32*g4 .. +31 (chunks 2*g4
+  // and 2*g4 + 1).  Each 16-lane group of a 16-byte read then touches 16
+  // different 4-bank groups (key parity x swizzled chunk), so the reads are
+  // free of bank conflicts, and so are the writes (two keys x eight chunks).
   auto lds_get = [&](int slot, i32x8 (&kb)[2]) {
-    const uint8_t* base = &ktile[slot][col * 128];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int c0 = (4 * g + 2 * j) ^ (col & 7), c1 = (4 * g + 2 * j + 1) ^ (col & 7);
-      const i32x4 x = *reinterpret_cast<const i32x4*>(base + 16 * c0);
-      const i32x4 y = *reinterpret_cast<const i32x4*>(base + 16 * c1);
+      const int key = 16 * j + c16, f = (key >> 1) & 7;
+      const uint8_t* base = &ktile[slot][key * 128];
+      const i32x4 x = *reinterpret_cast<const i32x4*>(base + 16 * ((2 * g4) ^ f));
+      const i32x4 y = *reinterpret_cast<const i32x4*>(base + 16 * ((2 * g4 + 1) ^ f));
       kb[j] = i32x8{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
     }
   };
@@ -248,34 +260,50 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
     const int s = it * 32 + col;
     const int srow = key_row(it);
     __builtin_amdgcn_s_setprio(1);
-    float p[kPfTokPerWave];
+    // 18 products per tile: for key block j, the four head blocks of token
+    // slot 0, those of slot 1, then the u block.  Product n + 2 is issued
+    // before the epilogue of product n; the scheduling barriers keep that
+    // order (the compiler would otherwise group the products together).
+    constexpr int kBlk = 2 * (4 * kPfTokPerWave + 1);
+    float P[kPfTokPerWave][2] = {};
+    float lsum[2] = {};
+    f32x4 acc[kBlk];
+    auto issue = [&](int n) {
+      const int j = n / 9, m = n % 9;
+      const f32x4 z = {};
+      acc[n] = m < 8 ? mfma_fp8_16(qa[m >> 2][m & 3], kb[j], z) : mfma_fp8_16(ua, kb[j], z);
+    };
+    auto epilogue = [&](int n) {
+      const int j = n / 9, m = n % 9;
+      if (m < 8) {
 #pragma unroll
-    for (int tk = 0; tk < kPfTokPerWave; ++tk) {
-      f32x16 a0 = {}, a1 = {};
-      a0 = mfma_fp8(qa[tk][0][0], kb[0], a0);
-      a1 = mfma_fp8(qa[tk][1][0], kb[0], a1);
-      a0 = mfma_fp8(qa[tk][0][1], kb[1], a0);
-      a1 = mfma_fp8(qa[tk][1][1], kb[1], a1);
-      float part = 0.0f;
+        for (int i = 0; i < 4; ++i) P[m >> 2][j] = fmaf(wl[m >> 2][m & 3][i], fabsf(acc[n][i]), P[m >> 2][j]);
+      } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        part = fmaf(wl[tk][0][r], fabsf(a0[r]), part);
-        part = fmaf(wl[tk][1][r], fabsf(a1[r]), part);
+        for (int i = 0; i < 4; ++i) lsum[j] = fmaf(us[i], acc[n][i], lsum[j]);
       }
-      p[tk] = part;
-    }
-    f32x16 lin = {};
-    lin = mfma_fp8(ua[0], kb[0], lin);
-    lin = mfma_fp8(ua[1], kb[1], lin);
-    __builtin_amdgcn_s_setprio(0);
-    // Half g keeps token g: send the other token's half-sum to the partner.
-    const float mine = g ? p[1] : p[0], other = g ? p[0] : p[1];
-    const float pa = mine + __shfl_xor(other, 32, 64);
-    float lsum = 0.0f;
+    };
+    issue(0);
+    issue(1);
 #pragma unroll
-    for (int i = 0; i < kLinTerms; ++i) lsum = fmaf(us[i], lin[i], lsum);
+    for (int n = 0; n < kBlk; ++n) {
+      if (n + 2 < kBlk) issue(n + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      epilogue(n);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    // u . k joins the token its rows belong to (lane group g4 holds slot g4's),
+    // then the four lane groups' head sums fold onto lane l = (slot, key):
+    // the 32-lane swap pairs groups {0,2} and {1,3} per slot, the 16-lane swap
+    // pairs the key blocks.
+    float R[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      R[j] = swap_sum32(P[0][j] + (g4 == 0 ? lsum[j] : 0.0f), P[1][j] + (g4 == 1 ? lsum[j] : 0.0f));
+    const float pa = swap_sum16(R[0], R[1]);
     const bool vis = srow <= qpos0 + tg;
-    const float val = vis ? (pa + lsum) * sq * sk : -INFINITY;
+    const float val = vis ? pa * sq * sk : -INFINITY;
     // Straight-line store (a lane past the end rewrites row L-1 with its own
     // value) so the loads of the next tiles stay in flight.
     scores[(int64_t)tg * L + srow] = val;
