@@ -19,8 +19,9 @@
 //   workgroup stages 32 latent rows at a time through LDS, converting bf16 ->
 //   fp16 once (exact in fp16 range) and writing them in MFMA-fragment order;
 //   each of its four waves holds one layer's 64 x Dc absorbed query in
-//   registers and runs v_mfma_f32_32x32x16_f16 against the shared tile, then
-//   the same ReLU-weighted head reduction as the native scan.  The gather
+//   registers and runs v_mfma_f32_16x16x32_f16 against the shared tile, one
+//   16-head x 16-row unit at a time, with each unit's ReLU-weighted head
+//   reduction on the VALU under the next unit's products.  The gather
 //   variant (HS) reads rows kv_off[b] + cand[b][j] instead of contiguous ones.
 //   The contiguous variant also builds each (request, layer) row's level-0
 //   selection histogram in LDS and stores it as the workgroup's partial.
@@ -98,34 +99,49 @@ __global__ __launch_bounds__(256) void latent_absorb_kernel(
 }
 
 constexpr int kLsWaves = 4;  // layers per workgroup, one per wave
+constexpr int kLsThreads = 64 * kLsWaves;
 constexpr int kLsMaxTiles = 64;  // tiles (32 rows) per workgroup at most
 constexpr int kLsMaxRows = kLsMaxTiles * 32;
 
 // DC: latent width (128 or 256).  GATHER: rows come from the candidate list.
 // CSCALE: a per-row latent scale is given.
 //
-// The workgroup streams its rows 32 at a time: the global loads of tile it+2
-// are issued while tile it is computed, tile it+1 (loaded one step earlier)
-// goes to LDS at the end of the step.  Scores collect in LDS (one row per
-// layer) and are written in one burst at the end; the level-0 histograms are
-// 16-bit, packed two bins per word (a workgroup covers at most 2048 rows).
+// Wave l holds its layer's 64 x DC absorbed query in registers (four 16-head
+// blocks).  A 32-row tile is eight units (16-row block rb x head block hb),
+// each a chain of DC/32 v_mfma_f32_16x16x32_f16 products over all the dims;
+// the epilogue of unit n (ReLU and head weights, on the VALU) runs while the
+// products of unit n + 1 execute, and the tile producer's conversion runs
+// between the two row blocks.  A lane's unit results are 4 heads of one row;
+// after the tile a permlane32 and a permlane16 swap fold the four lane
+// groups' sums, leaving row block 0 in lanes 0-15 and row block 1 in lanes
+// 32-47.  The workgroup stages 32 latent rows at a time through LDS,
+// converted bf16 -> fp16 once and shared by its four waves; two workgroups
+// fit on a CU, so each SIMD runs waves of two workgroups that pass their
+// barriers at different times.  Scores collect in LDS and are written in one
+// burst at the end; the level-0 histograms are 16-bit, packed two bins per
+// word (a workgroup covers at most 2048 rows).
 template <int DC, bool GATHER, bool CSCALE>
-__global__ __launch_bounds__(256) void latent_score_kernel(
+__global__ __launch_bounds__(kLsThreads, 2) void latent_score_kernel(
     const uint16_t* __restrict__ qt16, const float* __restrict__ wsc,
     const uint16_t* __restrict__ latent, const float* __restrict__ c_scale,
     const int64_t* __restrict__ kv_off, const int32_t* __restrict__ cand, int C, int64_t n_tok,
     int G, int H, int tiles_per_block, int k, float* __restrict__ scores, SelWs sel) {
-  constexpr int KSTEPS = DC / 16;  // K = 16 per MFMA
-  constexpr int HALF = DC / 2;     // dims per lane half
-  constexpr int CPT = DC / 64;     // 8-element chunks per thread per tile
-  __shared__ i32x4 lds[2][KSTEPS * 64];
+  constexpr int KS = DC / 32;   // products per unit (K = 32 each)
+  constexpr int NCR = DC / 8;   // 16-byte chunks per latent row
+  constexpr int CPT = NCR / 8;  // chunks per producer thread (8 threads per row)
+  static_assert(CPT >= 1 && 32 * 8 == kLsThreads, "tile producer layout");
+  // Tile slot in MFMA fragment order: the 16 bytes lane l needs for product s
+  // of row block rb sit at (rb * KS + s) * 64 + l, so fragment reads are
+  // lane-linear; producer lanes (one row each) also write consecutive slots.
+  __shared__ i32x4 ktile[2][32 * NCR];
   __shared__ uint32_t lhist[kLsWaves][kSelBins / 2];
   __shared__ __attribute__((aligned(16))) float ssc[kLsWaves][kLsMaxRows];
   __shared__ int32_t sh_n;
 
   const int b = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = wave_id();
-  const int col = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = wave_id();
+  const int c16 = lane & 15, g4 = lane >> 4;
   const int l = blockIdx.z * kLsWaves + wave;
   const bool active = l < G;
 
@@ -134,7 +150,7 @@ __global__ __launch_bounds__(256) void latent_score_kernel(
   const int32_t* cb = nullptr;
   if constexpr (GATHER) {
     cb = cand + (int64_t)b * C;
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
       int lo = 0, hi = C;
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
@@ -149,43 +165,43 @@ __global__ __launch_bounds__(256) void latent_score_kernel(
   }
   const int64_t tok0 = (int64_t)blockIdx.x * tiles_per_block * 32;
   if (tok0 >= n) return;
-  int64_t ntl = (n - tok0 + 31) / 32;
+  const int64_t ntl = (n - tok0 + 31) / 32;
   const int ntiles = (int)(ntl < tiles_per_block ? ntl : tiles_per_block);
   const bool select = !GATHER && n > k;
   if constexpr (!GATHER) {
-    for (int i = threadIdx.x; i < kLsWaves * kSelBins / 2; i += 256) (&lhist[0][0])[i] = 0;
+    for (int i = tid; i < kLsWaves * kSelBins / 2; i += kLsThreads) (&lhist[0][0])[i] = 0;
     // The top-k kernel that follows counts finished segments per (b, l) row.
-    if (select && blockIdx.x == 0 && threadIdx.x < kLsWaves && blockIdx.z * kLsWaves + threadIdx.x < G)
-      sel.done[(int64_t)b * G + blockIdx.z * kLsWaves + threadIdx.x] = 0u;
+    if (select && blockIdx.x == 0 && tid < kLsWaves && blockIdx.z * kLsWaves + tid < G)
+      sel.done[(int64_t)b * G + blockIdx.z * kLsWaves + tid] = 0u;
   }
 
-  // Absorbed queries (A operand: row = head, K = latent dims; lane half g
-  // holds dims HALF*g ..) and the weights of the heads whose results this
-  // lane holds (rows 8*(r/4) + 4*g + r%4 of each 32-row block).
-  const int la = active ? l : 0;  // inactive waves compute a copy of layer 0 and discard it
-  f16x8 qa[2][KSTEPS];
-  float wl[2][16];
+  // Absorbed query as the A operand (row = head 16*hb + c16, dims 32*s +
+  // 8*g4 .. +7 of product s) and the weights of the heads whose results this
+  // lane holds (rows 4*g4 + r of each block).
+  const int la = active ? l : 0;
+  f16x8 qa[4][KS];
+  float wl[4][4];
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const int row = hb * 32 + col;
+  for (int hb = 0; hb < 4; ++hb) {
+    const int head = 16 * hb + c16;
     // Clamped, unconditional loads (rows past H are zeroed afterwards).
-    const uint16_t* qp = qt16 + (((int64_t)b * G + la) * H + (row < H ? row : H - 1)) * DC + HALF * g;
+    const uint16_t* qp = qt16 + (((int64_t)b * G + la) * H + (head < H ? head : H - 1)) * DC + 8 * g4;
 #pragma unroll
-    for (int j = 0; j < KSTEPS; ++j) {
-      i32x4 v = ld16(qp + 8 * j);
-      if (row >= H) v = i32x4{0, 0, 0, 0};
-      qa[hb][j] = __builtin_bit_cast(f16x8, v);
+    for (int s = 0; s < KS; ++s) {
+      i32x4 v = ld16(qp + 32 * s);
+      if (head >= H) v = i32x4{0, 0, 0, 0};
+      qa[hb][s] = __builtin_bit_cast(f16x8, v);
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int head = hb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-      const float wv = wsc[((int64_t)b * G + la) * H + (head < H ? head : H - 1)];
-      wl[hb][r] = head < H ? wv : 0.0f;
+    for (int r = 0; r < 4; ++r) {
+      const int hr = 16 * hb + 4 * g4 + r;
+      const float wv = wsc[((int64_t)b * G + la) * H + (hr < H ? hr : H - 1)];
+      wl[hb][r] = hr < H ? wv : 0.0f;
     }
   }
 
-  // Producer: thread -> (row pt, dims [p*CPT*8, +CPT*8)).
-  const int pt = threadIdx.x & 31, p = threadIdx.x >> 5;
+  // Producer: thread -> row pt of the tile, chunks CPT*p .. +CPT-1.
+  const int pt = tid & 31, p = tid >> 5;
   auto row_of = [&](int64_t s) -> int64_t {
     s = s < n ? s : n - 1;
     if constexpr (GATHER) return off + cb[s];
@@ -193,72 +209,110 @@ __global__ __launch_bounds__(256) void latent_score_kernel(
   };
   auto gload = [&](i32x4 (&dst)[CPT], int tile) {
     const int t = tile < ntiles ? tile : ntiles - 1;
-    const int64_t r = row_of(tok0 + (int64_t)t * 32 + pt);
-    const uint16_t* src = latent + r * DC + p * CPT * 8;
+    const uint16_t* src = latent + row_of(tok0 + (int64_t)t * 32 + pt) * DC + 8 * CPT * p;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) dst[i] = ld16(src + 8 * i);
   };
-  auto lstore = [&](int buf, const i32x4 (&src)[CPT]) {
+  auto lstore = [&](int slot, const i32x4 (&src)[CPT]) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int d0 = (p * CPT + i) * 8;
-      const int gg = d0 / HALF, jj = (d0 - gg * HALF) / 8;
-      lds[buf][jj * 64 + pt + 32 * gg] = bf16x8_to_f16x8(src[i]);
+      const int c = CPT * p + i;
+      ktile[slot][((pt >> 4) * KS + (c >> 2)) * 64 + (c & 3) * 16 + (pt & 15)] = bf16x8_to_f16x8(src[i]);
     }
   };
+  // B operand of row block rb, product s: row 16*rb + c16, dims 32*s + 8*g4 .. +7.
+  auto bfrag = [&](int slot, int rb, i32x4 (&dst)[KS]) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) dst[s] = ktile[slot][(rb * KS + s) * 64 + lane];
+  };
+  // This lane's row after the fold: row block lane >> 5, row c16 of it.
+  const int frow = 16 * (lane >> 5) + c16;
   auto row_scale = [&](int tile) {
-    if constexpr (CSCALE) return c_scale[row_of(tok0 + (int64_t)(tile < ntiles ? tile : ntiles - 1) * 32 + col)];
+    if constexpr (CSCALE) return c_scale[row_of(tok0 + (int64_t)(tile < ntiles ? tile : ntiles - 1) * 32 + frow)];
     else return 1.0f;
   };
 
-  auto compute = [&](int buf, int it, float sc) {
-    f32x16 a0 = {}, a1 = {};
-#pragma unroll
-    for (int j = 0; j < KSTEPS; ++j) {
-      const f16x8 kb = __builtin_bit_cast(f16x8, lds[buf][j * 64 + lane]);
-      a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[0][j], kb, a0, 0, 0, 0);
-      a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[1][j], kb, a1, 0, 0, 0);
-    }
-    float part = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      part = fmaf(wl[0][r], relu(a0[r]), part);
-      part = fmaf(wl[1][r], relu(a1[r]), part);
-    }
-    part = sum_halves(part);
-    // LDS only from here on; every tile index here is < ntiles.
-    const int64_t s = tok0 + (int64_t)it * 32 + col;
-    const float val = part * sc;
-    if (g == 0) ssc[wave][it * 32 + col] = val;
-    if constexpr (!GATHER) {
-      const uint32_t bin = score_key(val) >> kSelShift;
-      const uint32_t inc = (select && active && g == 0 && s < n) ? 1u : 0u;
-      atomicAdd(&lhist[wave][bin >> 1], inc << (16 * (bin & 1)));
-    }
-  };
-
-  // Ring of two register sets for tiles in flight; the step is unrolled by
-  // two so that the set indices are compile-time constants.
-  i32x4 pre[2][CPT];
+  // Step i computes tile i from LDS slot i & 1, writes tile i+1 into the
+  // other slot (whose readers finished tile i-1 before the previous barrier)
+  // and loads tile i+3 into the register set tile i+1 had.
+  i32x4 gk[2][CPT];
   float skr[2];
-  gload(pre[0], 0);
-  gload(pre[1], 1);
+  gload(gk[0], 0);
+  gload(gk[1], 1);
   skr[0] = row_scale(0);
-  skr[1] = row_scale(1);
-  lstore(0, pre[0]);
-  gload(pre[0], 2);
+  lstore(0, gk[0]);
+  gload(gk[0], 2);
   __syncthreads();
   const int nsteps = (ntiles + 1) / 2 * 2;
   for (int base = 0; base < nsteps; base += 2) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int it = base + st;
-      if (it < ntiles) {
-        compute(st, it, skr[st]);
+      const bool work = active && it < ntiles;  // uniform across the wave
+      skr[st ^ 1] = row_scale(it + 1);
+      i32x4 bk[KS];
+      f32x4 acc[8];
+      float P0 = 0.0f, P1 = 0.0f;
+      auto issue = [&](int u) {  // unit u: row block u >> 2 (in bk), head block u & 3
+        f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          a = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[u & 3][s], __builtin_bit_cast(f16x8, bk[s]), a, 0, 0, 0);
+        acc[u] = a;
+      };
+      auto epi = [&](int u) {
+        float& P = (u >> 2) ? P1 : P0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) P = fmaf(wl[u & 3][r], relu(acc[u][r]), P);
+      };
+      if (work) {
+        bfrag(st, 0, bk);
+        issue(0);
+        issue(1);
+        __builtin_amdgcn_sched_barrier(0);
+        epi(0);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(2);
+        __builtin_amdgcn_sched_barrier(0);
+        epi(1);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(3);
+        __builtin_amdgcn_sched_barrier(0);
+        epi(2);
+        __builtin_amdgcn_sched_barrier(0);
+        bfrag(st, 1, bk);
       }
-      skr[st] = row_scale(it + 2);
-      lstore(st ^ 1, pre[st ^ 1]);  // tile it+1
-      gload(pre[st ^ 1], it + 3);
+      lstore(st ^ 1, gk[st ^ 1]);
+      gload(gk[st ^ 1], it + 3);
+      if (work) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(4);
+        __builtin_amdgcn_sched_barrier(0);
+        epi(3);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(5);
+        __builtin_amdgcn_sched_barrier(0);
+        epi(4);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(6);
+        __builtin_amdgcn_sched_barrier(0);
+        epi(5);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(7);
+        __builtin_amdgcn_sched_barrier(0);
+        epi(6);
+        epi(7);
+        const float R = swap_sum32(P0, P1);
+        const float val = swap_sum16(R, R) * skr[st];
+        if ((g4 & 1) == 0) {
+          ssc[wave][it * 32 + frow] = val;
+          if constexpr (!GATHER) {
+            const uint32_t bin = score_key(val) >> kSelShift;
+            const uint32_t inc = (select && tok0 + it * 32 + frow < n) ? 1u : 0u;
+            atomicAdd(&lhist[wave][bin >> 1], inc << (16 * (bin & 1)));
+          }
+        }
+      }
       __syncthreads();
     }
   }
@@ -272,11 +326,11 @@ __global__ __launch_bounds__(256) void latent_score_kernel(
     float* dst = GATHER ? scores + ((int64_t)b * G + lg) * C + tok0 : scores + (int64_t)lg * n_tok + off + tok0;
     if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
       const int n4 = nrow >> 2;
-      for (int i = threadIdx.x; i < n4; i += 256)
+      for (int i = tid; i < n4; i += kLsThreads)
         *reinterpret_cast<f32x4*>(dst + 4 * i) = *reinterpret_cast<const f32x4*>(&ssc[lw][4 * i]);
-      for (int i = 4 * n4 + threadIdx.x; i < nrow; i += 256) dst[i] = ssc[lw][i];
+      for (int i = 4 * n4 + tid; i < nrow; i += kLsThreads) dst[i] = ssc[lw][i];
     } else {
-      for (int i = threadIdx.x; i < nrow; i += 256) dst[i] = ssc[lw][i];
+      for (int i = tid; i < nrow; i += kLsThreads) dst[i] = ssc[lw][i];
     }
   }
   if constexpr (!GATHER) {
@@ -284,7 +338,7 @@ __global__ __launch_bounds__(256) void latent_score_kernel(
     // Each layer's share of its (b, l) row histogram (already 16-bit bins).
     for (int lw = 0; lw < nl; ++lw) {
       const int64_t pi = ((int64_t)b * G + blockIdx.z * kLsWaves + lw) * sel.nwg + blockIdx.x;
-      store_partial_packed<256>(lhist[lw], sel.part + pi * kSelBins, sel.cpart + pi * kSelCoarse);
+      store_partial_packed<kLsThreads>(lhist[lw], sel.part + pi * kSelBins, sel.cpart + pi * kSelCoarse);
     }
   }
 }
@@ -305,10 +359,10 @@ hipError_t launch_ls2(int Dc, dim3 grid, hipStream_t stream, const uint16_t* qt1
                       const int32_t* cand, int C, int64_t n_tok, int G, int H, int tpb, int k,
                       float* scores, const SelWs& sel) {
   if (Dc == 256)
-    latent_score_kernel<256, GATHER, CSCALE><<<grid, dim3(256), 0, stream>>>(
+    latent_score_kernel<256, GATHER, CSCALE><<<grid, dim3(kLsThreads), 0, stream>>>(
         qt16, wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
   else
-    latent_score_kernel<128, GATHER, CSCALE><<<grid, dim3(256), 0, stream>>>(
+    latent_score_kernel<128, GATHER, CSCALE><<<grid, dim3(kLsThreads), 0, stream>>>(
         qt16, wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
   return hipGetLastError();
 }
