@@ -232,6 +232,14 @@ def components(torch, li, inputs, args):
         "absorb_ms": absorb, "scan_ms": scan, "topk_ms": topk, "total_ms": wall,
         "scan_gbs": lat_bytes / (scan * 1e-3) / 1e9, "scan_hbm_frac": lat_bytes / (scan * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "scan_mfma_frac_fp16": flop / (scan * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+    # the same step with LI_LATENT_SPLIT_BF16 (two bf16 products per element)
+    fn = lambda: li.li_latent_score_group(q, w, wd, lat, None, off, 131072, x.k, out_idx=idx, ws=ws,
+                                          flags=li.LI_LATENT_SPLIT_BF16)
+    wall, (absorb, scan, topk) = timed(torch, li, fn, 4, args.comp_iters, 2)
+    out["latent_split_bf16_G4_B16_L131072"] = {
+        "absorb_ms": absorb, "scan_ms": scan, "topk_ms": topk, "total_ms": wall,
+        "scan_gbs": lat_bytes / (scan * 1e-3) / 1e9, "scan_hbm_frac": lat_bytes / (scan * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "scan_mfma_frac_bf16": 2 * flop / (scan * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
     del q, w, wd, lat, off, idx, ws, x
     # ---- HS decode: fp8 anchor top-8192 + 3 latent followers, B = 16, L = 131072 --
     h = inputs.cfg5()

@@ -136,7 +136,14 @@ size_t li_index_prefill_ws(int32_t T, int32_t L, int32_t k, int32_t has_out_scor
 /* Selects the MFMA operand form of the absorbed latent queries. */
 #define LI_LATENT_FP16 0u /* fp16 absorbed query (per-row power-of-two range scaling), latent
                              converted bf16 -> fp16 on the fly; requires latent magnitudes
-                             within fp16 range (|c| <= 65504). */
+                             within fp16 range (|c| <= 65504).  One product per element;
+                             score error up to about 2e-4 of sum_h |w_h x_h| (measured on
+                             N(0,1) latents). */
+#define LI_LATENT_SPLIT_BF16 1u /* absorbed query as two bf16 parts, hi + lo (lo = the bf16
+                                   rounding of the exact residual), against the bf16 latent as
+                                   stored (any magnitude bf16 holds).  Two products per element
+                                   (about 1.8x the fp16 form's scan time); score error up to
+                                   about 2e-6 of sum_h |w_h x_h| (same measurement). */
 
 /* ---------------------------------------------------------------------------
  * li_latent_score_group — LatentIndex: G layers score one shared latent cache.
@@ -156,7 +163,7 @@ size_t li_index_prefill_ws(int32_t T, int32_t L, int32_t k, int32_t has_out_scor
  *   G >= 1;  H 1..64;  Dh must be 128;  Dc 128 or 256;  1 <= k <= LI_MAX_K
  *   out_idx    [B][G][k]  int32 positions, ascending, -1 padded
  *   out_scores [G][n_tok] fp32 or NULL
- *   flags      LI_LATENT_FP16
+ *   flags      LI_LATENT_FP16 or LI_LATENT_SPLIT_BF16
  * ------------------------------------------------------------------------- */
 li_status li_latent_score_group(const void* q, li_dtype q_dt, const float* w, const void* w_dec,
                                 li_dtype w_dt, const void* latent, li_dtype c_dt,
@@ -182,7 +189,7 @@ size_t li_latent_score_group_ws(int32_t B, int64_t n_tok, int32_t max_len, int32
  *   out_idx    [B][Gf][k] int32 TOKEN positions (taken from cand_idx), ascending, -1 padded
  *   out_scores [B][Gf][C] fp32 score of candidate slot j, or NULL (slots past
  *              the valid candidates are not written)
- *   flags      LI_LATENT_FP16
+ *   flags      LI_LATENT_FP16 or LI_LATENT_SPLIT_BF16
  * ------------------------------------------------------------------------- */
 li_status li_hs_refine(const int32_t* cand_idx, int32_t C, const void* q, li_dtype q_dt,
                        const float* w, const void* w_dec, li_dtype w_dt, const void* latent,

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(HERE, "libli.so")
 LI_OK, LI_E_NULL, LI_E_SHAPE, LI_E_DTYPE, LI_E_WORKSPACE, LI_E_UNSUPPORTED, LI_E_HIP, LI_E_VALUE = range(8)
 LI_BF16, LI_FP8_E4M3, LI_FP16, LI_FP32 = range(4)
 LI_LATENT_FP16 = 0
+LI_LATENT_SPLIT_BF16 = 1
 LI_MAX_K = 16384
 
 # Every symbol include/li.h declares.

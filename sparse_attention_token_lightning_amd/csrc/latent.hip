@@ -36,9 +36,19 @@ namespace {
 
 constexpr int kAbsB = 32;  // requests per absorb pass
 
+// bf16 of an fp32 value, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// split = false: qt16[row] = fp16 of the scaled row.  split = true: qt16[row]
+// = hi, qt16[nrows + row] = lo, two bf16 parts with hi + lo = the scaled row
+// to within 2^-17 of its magnitude (hi is the bf16 rounding, lo that of the
+// exact fp32 residual).
 __global__ __launch_bounds__(256) void latent_absorb_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ w_dec,
-    int B, int G, int H, int Dc, uint16_t* __restrict__ qt16, float* __restrict__ wsc) {
+    int B, int G, int H, int Dc, bool split, uint16_t* __restrict__ qt16, float* __restrict__ wsc) {
   constexpr int Dh = 128;
   __shared__ float qs[kAbsB][Dh];
   __shared__ float red[kAbsB][4];
@@ -89,8 +99,15 @@ __global__ __launch_bounds__(256) void latent_absorb_kernel(
       const int e = mx > 0.0f ? 15 - E : 0;  // mx * 2^e in [2^14, 2^15)
       const int64_t rowi = ((int64_t)(b0 + bi) * G + l) * H + h;
       if (c < Dc) {
-        const _Float16 hv = (_Float16)ldexpf(acc[bi], e);
-        qt16[rowi * Dc + c] = __builtin_bit_cast(uint16_t, hv);
+        const float v = ldexpf(acc[bi], e);
+        if (split) {
+          const uint16_t hi = f32_to_bf16_rne(v);
+          const float res = v - __builtin_bit_cast(float, (uint32_t)hi << 16);  // exact in fp32
+          qt16[rowi * Dc + c] = hi;
+          qt16[((int64_t)B * G * H + rowi) * Dc + c] = f32_to_bf16_rne(res);
+        } else {
+          qt16[rowi * Dc + c] = __builtin_bit_cast(uint16_t, (_Float16)v);
+        }
       }
       if (c == 0) wsc[rowi] = ldexpf(w[rowi], -e);
     }
@@ -343,6 +360,244 @@ __global__ __launch_bounds__(kLsThreads, 2) void latent_score_kernel(
   }
 }
 
+constexpr int kSpWaves = 8;               // LI_LATENT_SPLIT_BF16 scan: one wave per (layer, head half)
+constexpr int kSpLayers = kSpWaves / 2;   // layers per workgroup
+constexpr int kSpThreads = 64 * kSpWaves;
+
+// The LI_LATENT_SPLIT_BF16 form of the scan: the absorbed query is hi + lo
+// (two bf16 rows) and the latent is used as stored (bf16), so each product
+// is two v_mfma_f32_16x16x32_bf16 into one accumulator.  The query of 64
+// heads would take all 256 registers of a wave in this form, so a wave holds
+// half the heads of one layer (two 16-head blocks, hi and lo: 128 VGPRs at
+// Dc = 256) and the two halves of a layer meet in an LDS float add of their
+// scaled partial sums (two partials added to zero give the same bits in
+// either order).  A 32-row tile is four units (16-row block x head block),
+// each unit's epilogue running under the next unit's products; the latent
+// tile goes through LDS once, unconverted, in MFMA-fragment order.  After the
+// last tile one pass writes the scores out and builds the level-0
+// histograms of the contiguous variant.
+template <int DC, bool GATHER, bool CSCALE>
+__global__ __launch_bounds__(kSpThreads) void latent_split_kernel(
+    const uint16_t* __restrict__ qhi, const uint16_t* __restrict__ qlo, const float* __restrict__ wsc,
+    const uint16_t* __restrict__ latent, const float* __restrict__ c_scale,
+    const int64_t* __restrict__ kv_off, const int32_t* __restrict__ cand, int C, int64_t n_tok,
+    int G, int H, int tiles_per_block, int k, float* __restrict__ scores, SelWs sel) {
+  constexpr int KS = DC / 32;    // products per unit and query part (K = 32 each)
+  constexpr int NCR = DC / 8;    // 16-byte chunks per latent row
+  constexpr int CPT = NCR / 16;  // chunks per producer thread (16 threads per row)
+  static_assert(CPT >= 1 && 32 * 16 == kSpThreads, "tile producer layout");
+  // Tile slot in MFMA fragment order: the 16 bytes lane l needs for product s
+  // of row block rb sit at (rb * KS + s) * 64 + l.
+  __shared__ i32x4 ktile[2][32 * NCR];
+  __shared__ uint32_t lhist[kSpLayers][kSelBins / 2];
+  __shared__ __attribute__((aligned(16))) float ssc[kSpLayers][kLsMaxRows];
+  __shared__ int32_t sh_n;
+
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = wave_id();
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int lw = wave >> 1, hh = wave & 1;
+  const int l = blockIdx.z * kSpLayers + lw;
+  const bool active = l < G;
+
+  const int64_t off = kv_off[b];
+  int64_t n;
+  const int32_t* cb = nullptr;
+  if constexpr (GATHER) {
+    cb = cand + (int64_t)b * C;
+    if (tid == 0) {
+      int lo = 0, hi = C;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (cb[mid] < 0) hi = mid; else lo = mid + 1;
+      }
+      sh_n = lo;
+    }
+    __syncthreads();
+    n = sh_n;
+  } else {
+    n = kv_off[b + 1] - off;
+  }
+  const int64_t tok0 = (int64_t)blockIdx.x * tiles_per_block * 32;
+  if (tok0 >= n) return;
+  const int64_t ntl = (n - tok0 + 31) / 32;
+  const int ntiles = (int)(ntl < tiles_per_block ? ntl : tiles_per_block);
+  const bool select = !GATHER && n > k;
+  for (int i = tid; i < kSpLayers * kSelBins / 2; i += kSpThreads) (&lhist[0][0])[i] = 0;
+  for (int i = tid; i < kSpLayers * kLsMaxRows / 4; i += kSpThreads)
+    reinterpret_cast<f32x4*>(&ssc[0][0])[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (!GATHER) {
+    // The top-k kernel that follows counts finished segments per (b, l) row.
+    if (select && blockIdx.x == 0 && tid < kSpLayers && blockIdx.z * kSpLayers + tid < G)
+      sel.done[(int64_t)b * G + blockIdx.z * kSpLayers + tid] = 0u;
+  }
+
+  // Query parts as A operands (row = head 32*hh + 16*hb + c16, dims 32*s +
+  // 8*g4 .. +7 of product s) and the weights of the heads whose results this
+  // lane holds (rows 4*g4 + r of each block).
+  const int la = active ? l : 0;
+  bf16x8 qh[2][KS], ql[2][KS];
+  float wl[2][4];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const int head = 32 * hh + 16 * hb + c16;
+    // Clamped, unconditional loads (rows past H are zeroed afterwards).
+    const int64_t qo = (((int64_t)b * G + la) * H + (head < H ? head : H - 1)) * DC + 8 * g4;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      i32x4 vh = ld16(qhi + qo + 32 * s), vl = ld16(qlo + qo + 32 * s);
+      if (head >= H) vh = vl = i32x4{0, 0, 0, 0};
+      qh[hb][s] = __builtin_bit_cast(bf16x8, vh);
+      ql[hb][s] = __builtin_bit_cast(bf16x8, vl);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int hr = 32 * hh + 16 * hb + 4 * g4 + r;
+      const float wv = wsc[((int64_t)b * G + la) * H + (hr < H ? hr : H - 1)];
+      wl[hb][r] = hr < H ? wv : 0.0f;
+    }
+  }
+
+  // Producer: thread -> row pt of the tile, chunks CPT*p .. +CPT-1.
+  const int pt = tid & 31, p = tid >> 5;
+  auto row_of = [&](int64_t s) -> int64_t {
+    s = s < n ? s : n - 1;
+    if constexpr (GATHER) return off + cb[s];
+    else return off + s;
+  };
+  auto gload = [&](i32x4 (&dst)[CPT], int tile) {
+    const int t = tile < ntiles ? tile : ntiles - 1;
+    const uint16_t* src = latent + row_of(tok0 + (int64_t)t * 32 + pt) * DC + 8 * CPT * p;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) dst[i] = ld16(src + 8 * i);
+  };
+  auto lstore = [&](int slot, const i32x4 (&src)[CPT]) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = CPT * p + i;
+      ktile[slot][((pt >> 4) * KS + (c >> 2)) * 64 + (c & 3) * 16 + (pt & 15)] = src[i];
+    }
+  };
+  auto bfrag = [&](int slot, int rb, i32x4 (&dst)[KS]) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) dst[s] = ktile[slot][(rb * KS + s) * 64 + lane];
+  };
+  // This lane's row after the fold: row block lane >> 5, row c16 of it.
+  const int frow = 16 * (lane >> 5) + c16;
+  auto row_scale = [&](int tile) {
+    if constexpr (CSCALE) return c_scale[row_of(tok0 + (int64_t)(tile < ntiles ? tile : ntiles - 1) * 32 + frow)];
+    else return 1.0f;
+  };
+
+  // Step i computes tile i from LDS slot i & 1, writes tile i+1 into the
+  // other slot (whose readers finished tile i-1 before the previous barrier)
+  // and loads tile i+3 into the register set tile i+1 had.
+  i32x4 gk[2][CPT];
+  float skr[2];
+  gload(gk[0], 0);
+  gload(gk[1], 1);
+  skr[0] = row_scale(0);
+  lstore(0, gk[0]);
+  gload(gk[0], 2);
+  __syncthreads();
+  const int nsteps = (ntiles + 1) / 2 * 2;
+  for (int base = 0; base < nsteps; base += 2) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int it = base + st;
+      const bool work = active && it < ntiles;  // uniform across the wave
+      skr[st ^ 1] = row_scale(it + 1);
+      i32x4 bk[KS];
+      f32x4 acc[4];
+      float P0 = 0.0f, P1 = 0.0f;
+      auto issue = [&](int u) {  // unit u: row block u >> 1 (in bk), head block u & 1
+        f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const bf16x8 kb = __builtin_bit_cast(bf16x8, bk[s]);
+          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[u & 1][s], kb, a, 0, 0, 0);
+          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[u & 1][s], kb, a, 0, 0, 0);
+        }
+        acc[u] = a;
+      };
+      auto epi = [&](int u) {
+        float& P = (u >> 1) ? P1 : P0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) P = fmaf(wl[u & 1][r], relu(acc[u][r]), P);
+      };
+      if (work) {
+        bfrag(st, 0, bk);
+        issue(0);
+        issue(1);
+        __builtin_amdgcn_sched_barrier(0);
+        epi(0);
+        __builtin_amdgcn_sched_barrier(0);
+        bfrag(st, 1, bk);
+      }
+      lstore(st ^ 1, gk[st ^ 1]);
+      gload(gk[st ^ 1], it + 3);
+      if (work) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(2);
+        __builtin_amdgcn_sched_barrier(0);
+        epi(1);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(3);
+        __builtin_amdgcn_sched_barrier(0);
+        epi(2);
+        epi(3);
+        const float R = swap_sum32(P0, P1);
+        const float part = swap_sum16(R, R) * skr[st];
+        if ((g4 & 1) == 0) atomicAdd(&ssc[lw][it * 32 + frow], part);
+      }
+      __syncthreads();
+    }
+  }
+
+  // Scores of this workgroup's rows, one pass per layer (16-byte stores where
+  // the destination is aligned), and their histogram counts.
+  const int nrow = (int)((n - tok0) < (int64_t)ntiles * 32 ? (n - tok0) : (int64_t)ntiles * 32);
+  const int nl = (G - (int)blockIdx.z * kSpLayers) < kSpLayers ? (G - (int)blockIdx.z * kSpLayers) : kSpLayers;
+  auto count = [&](int ly, float v) {
+    const uint32_t bin = score_key(v) >> kSelShift;
+    atomicAdd(&lhist[ly][bin >> 1], 1u << (16 * (bin & 1)));
+  };
+  for (int ly = 0; ly < nl; ++ly) {
+    const int lg = blockIdx.z * kSpLayers + ly;
+    float* dst = GATHER ? scores + ((int64_t)b * G + lg) * C + tok0 : scores + (int64_t)lg * n_tok + off + tok0;
+    int done = 0;
+    if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+      const int n4 = nrow >> 2;
+      for (int i = tid; i < n4; i += kSpThreads) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&ssc[ly][4 * i]);
+        *reinterpret_cast<f32x4*>(dst + 4 * i) = v;
+        if (select) {
+          count(ly, v[0]);
+          count(ly, v[1]);
+          count(ly, v[2]);
+          count(ly, v[3]);
+        }
+      }
+      done = 4 * n4;
+    }
+    for (int i = done + tid; i < nrow; i += kSpThreads) {
+      const float v = ssc[ly][i];
+      dst[i] = v;
+      if (select) count(ly, v);
+    }
+  }
+  if constexpr (!GATHER) {
+    if (!select) return;
+    __syncthreads();
+    // Each layer's share of its (b, l) row histogram (already 16-bit bins).
+    for (int ly = 0; ly < nl; ++ly) {
+      const int64_t pi = ((int64_t)b * G + blockIdx.z * kSpLayers + ly) * sel.nwg + blockIdx.x;
+      store_partial_packed<kSpThreads>(lhist[ly], sel.part + pi * kSelBins, sel.cpart + pi * kSelCoarse);
+    }
+  }
+}
+
 }  // namespace
 
 int64_t latent_chunk(int64_t n_tok) {
@@ -353,40 +608,50 @@ int64_t latent_chunk(int64_t n_tok) {
 
 namespace {
 
+// qlo: the lo parts of the split form (ignored otherwise).
 template <bool GATHER, bool CSCALE>
-hipError_t launch_ls2(int Dc, dim3 grid, hipStream_t stream, const uint16_t* qt16, const float* wsc,
-                      const uint16_t* latent, const float* c_scale, const int64_t* kv_off,
-                      const int32_t* cand, int C, int64_t n_tok, int G, int H, int tpb, int k,
-                      float* scores, const SelWs& sel) {
-  if (Dc == 256)
+hipError_t launch_ls2(bool split, int Dc, dim3 grid, hipStream_t stream, const uint16_t* qt16,
+                      const uint16_t* qlo, const float* wsc, const uint16_t* latent, const float* c_scale,
+                      const int64_t* kv_off, const int32_t* cand, int C, int64_t n_tok, int G, int H, int tpb,
+                      int k, float* scores, const SelWs& sel) {
+  static_assert(kSpLayers == kLsWaves, "both forms cover the same layers per workgroup (grid z)");
+  if (split) {
+    if (Dc == 256)
+      latent_split_kernel<256, GATHER, CSCALE><<<grid, dim3(kSpThreads), 0, stream>>>(
+          qt16, qlo, wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
+    else
+      latent_split_kernel<128, GATHER, CSCALE><<<grid, dim3(kSpThreads), 0, stream>>>(
+          qt16, qlo, wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
+  } else if (Dc == 256) {
     latent_score_kernel<256, GATHER, CSCALE><<<grid, dim3(kLsThreads), 0, stream>>>(
         qt16, wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
-  else
+  } else {
     latent_score_kernel<128, GATHER, CSCALE><<<grid, dim3(kLsThreads), 0, stream>>>(
         qt16, wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
+  }
   return hipGetLastError();
 }
 
 template <bool GATHER>
-hipError_t launch_ls(int Dc, dim3 grid, hipStream_t stream, const uint16_t* qt16, const float* wsc,
-                     const uint16_t* latent, const float* c_scale, const int64_t* kv_off,
-                     const int32_t* cand, int C, int64_t n_tok, int G, int H, int tpb, int k,
-                     float* scores, const SelWs& sel) {
+hipError_t launch_ls(bool split, int Dc, dim3 grid, hipStream_t stream, const uint16_t* qt16,
+                     const uint16_t* qlo, const float* wsc, const uint16_t* latent, const float* c_scale,
+                     const int64_t* kv_off, const int32_t* cand, int C, int64_t n_tok, int G, int H, int tpb,
+                     int k, float* scores, const SelWs& sel) {
   if (c_scale)
-    return launch_ls2<GATHER, true>(Dc, grid, stream, qt16, wsc, latent, c_scale, kv_off, cand, C, n_tok,
-                                    G, H, tpb, k, scores, sel);
-  return launch_ls2<GATHER, false>(Dc, grid, stream, qt16, wsc, latent, c_scale, kv_off, cand, C, n_tok, G,
-                                   H, tpb, k, scores, sel);
+    return launch_ls2<GATHER, true>(split, Dc, grid, stream, qt16, qlo, wsc, latent, c_scale, kv_off, cand, C,
+                                    n_tok, G, H, tpb, k, scores, sel);
+  return launch_ls2<GATHER, false>(split, Dc, grid, stream, qt16, qlo, wsc, latent, c_scale, kv_off, cand, C,
+                                   n_tok, G, H, tpb, k, scores, sel);
 }
 
 }  // namespace
 
 hipError_t launch_latent_absorb(const uint16_t* q, const float* w, const uint16_t* w_dec,
-                                int32_t B, int32_t G, int32_t H, int32_t Dh, int32_t Dc,
+                                int32_t B, int32_t G, int32_t H, int32_t Dh, int32_t Dc, bool split,
                                 uint16_t* qt16, float* wsc, hipStream_t stream) {
   (void)Dh;
   if (B <= 0) return hipSuccess;
-  latent_absorb_kernel<<<dim3((unsigned)(G * H)), dim3(256), 0, stream>>>(q, w, w_dec, B, G, H, Dc,
+  latent_absorb_kernel<<<dim3((unsigned)(G * H)), dim3(256), 0, stream>>>(q, w, w_dec, B, G, H, Dc, split,
                                                                           qt16, wsc);
   return hipGetLastError();
 }
@@ -394,20 +659,21 @@ hipError_t launch_latent_absorb(const uint16_t* q, const float* w, const uint16_
 hipError_t launch_latent_score(const uint16_t* qt16, const float* wsc, const uint16_t* latent,
                                const float* c_scale, const int64_t* kv_off, int32_t B,
                                int64_t n_tok, int32_t max_len, int32_t G, int32_t H, int32_t Dc,
-                               int32_t k, float* scores, const SelWs& sel, hipStream_t stream) {
+                               int32_t k, bool split, float* scores, const SelWs& sel, hipStream_t stream) {
   if (B <= 0 || max_len <= 0) return hipSuccess;
   const int64_t chunk = latent_chunk(n_tok);
   const int64_t tpb = chunk / 32;
   dim3 grid((unsigned)((max_len + chunk - 1) / chunk), (unsigned)B,
             (unsigned)((G + kLsWaves - 1) / kLsWaves));
-  return launch_ls<false>(Dc, grid, stream, qt16, wsc, latent, c_scale, kv_off, nullptr, 0, n_tok,
-                          G, H, (int)tpb, k, scores, sel);
+  const uint16_t* qlo = qt16 + (int64_t)B * G * H * Dc;
+  return launch_ls<false>(split, Dc, grid, stream, qt16, qlo, wsc, latent, c_scale, kv_off, nullptr, 0,
+                          n_tok, G, H, (int)tpb, k, scores, sel);
 }
 
 hipError_t launch_hs_score(const uint16_t* qt16, const float* wsc, const uint16_t* latent,
                            const float* c_scale, const int64_t* kv_off, const int32_t* cand,
-                           int32_t C, int32_t B, int32_t Gf, int32_t H, int32_t Dc, float* scores,
-                           hipStream_t stream) {
+                           int32_t C, int32_t B, int32_t Gf, int32_t H, int32_t Dc, bool split,
+                           float* scores, hipStream_t stream) {
   if (B <= 0 || C <= 0) return hipSuccess;
   int64_t tpb = ((int64_t)B * C) / ((int64_t)512 * 32);
   tpb = tpb < 2 ? 2 : (tpb > 32 ? 32 : tpb);
@@ -415,8 +681,9 @@ hipError_t launch_hs_score(const uint16_t* qt16, const float* wsc, const uint16_
   dim3 grid((unsigned)((C + chunk - 1) / chunk), (unsigned)B,
             (unsigned)((Gf + kLsWaves - 1) / kLsWaves));
   SelWs none = {};
-  return launch_ls<true>(Dc, grid, stream, qt16, wsc, latent, c_scale, kv_off, cand, C, 0, Gf, H,
-                         (int)tpb, 0, scores, none);
+  const uint16_t* qlo = qt16 + (int64_t)B * Gf * H * Dc;
+  return launch_ls<true>(split, Dc, grid, stream, qt16, qlo, wsc, latent, c_scale, kv_off, cand, C, 0, Gf,
+                         H, (int)tpb, 0, scores, none);
 }
 
 }  // namespace li

@@ -151,7 +151,8 @@ size_t prefill_ws(int32_t T, int32_t L, bool scores_given) {
 size_t latent_ws(int32_t B, int64_t n_tok, int32_t max_len, int32_t G, int32_t H, int32_t Dc,
                  bool scores_given) {
   const size_t rows = (size_t)(B > 0 ? B : 0) * (G > 0 ? G : 0);
-  size_t s = align_up(rows * H * Dc * 2) + align_up(rows * H * 4);
+  // absorbed queries: room for the two bf16 parts of LI_LATENT_SPLIT_BF16
+  size_t s = align_up(rows * H * Dc * 4) + align_up(rows * H * 4);
   if (!scores_given) s += align_up((size_t)G * (size_t)n_tok * 4);
   s += sel_ws((int64_t)rows, max_len > 0 ? max_len : 0, li::latent_chunk(n_tok));
   return s;
@@ -159,7 +160,7 @@ size_t latent_ws(int32_t B, int64_t n_tok, int32_t max_len, int32_t G, int32_t H
 
 size_t hs_ws(int32_t B, int32_t C, int32_t Gf, int32_t H, int32_t Dc, bool scores_given) {
   const size_t rows = (size_t)B * Gf;
-  size_t s = align_up(rows * H * Dc * 2) + align_up(rows * H * 4);
+  size_t s = align_up(rows * H * Dc * 4) + align_up(rows * H * 4);
   if (!scores_given) s += align_up(rows * (size_t)C * 4);
   return s;
 }
@@ -331,7 +332,8 @@ static li_status check_latent_common(li_dtype q_dt, li_dtype w_dt, li_dtype c_dt
   li_status st;
   if ((st = check_heads(H, Dh, "Dh"))) return st;
   if (Dc != 128 && Dc != 256) return fail(LI_E_UNSUPPORTED, "Dc must be 128 or 256 (got %d)", Dc);
-  if (flags != LI_LATENT_FP16) return fail(LI_E_UNSUPPORTED, "unknown flags 0x%x", flags);
+  if (flags != LI_LATENT_FP16 && flags != LI_LATENT_SPLIT_BF16)
+    return fail(LI_E_UNSUPPORTED, "unknown flags 0x%x", flags);
   return LI_OK;
 }
 
@@ -371,16 +373,17 @@ li_status li_latent_score_group(const void* q, li_dtype q_dt, const float* w, co
     return st;
   trace_begin(s);
   Carver cv(ws);
-  uint16_t* qt16 = (uint16_t*)cv.take((size_t)B * G * H * Dc * 2);
+  uint16_t* qt16 = (uint16_t*)cv.take((size_t)B * G * H * Dc * 4);
+  const bool split = flags == LI_LATENT_SPLIT_BF16;
   float* wsc = (float*)cv.take((size_t)B * G * H * 4);
   float* scores = out_scores ? out_scores : (float*)cv.take((size_t)G * (size_t)n_tok * 4);
   const li::SelWs sel = carve_sel(cv, (int64_t)B * G, max_len, li::latent_chunk(n_tok), k);
   if ((st = hip_check(li::launch_latent_absorb((const uint16_t*)q, w, (const uint16_t*)w_dec, B, G,
-                                               H, Dh, Dc, qt16, wsc, s),
+                                               H, Dh, Dc, split, qt16, wsc, s),
                       "latent_absorb launch", s)))
     return st;
   if ((st = hip_check(li::launch_latent_score(qt16, wsc, (const uint16_t*)latent, c_scale, kv_off, B,
-                                              n_tok, max_len, G, H, Dc, k, scores, sel, s),
+                                              n_tok, max_len, G, H, Dc, k, split, scores, sel, s),
                       "latent_score launch", s)))
     return st;
   li::TopkRows tr = {};
@@ -430,15 +433,16 @@ li_status li_hs_refine(const int32_t* cand_idx, int32_t C, const void* q, li_dty
     return st;
   trace_begin(s);
   Carver cv(ws);
-  uint16_t* qt16 = (uint16_t*)cv.take((size_t)B * Gf * H * Dc * 2);
+  uint16_t* qt16 = (uint16_t*)cv.take((size_t)B * Gf * H * Dc * 4);
+  const bool split = flags == LI_LATENT_SPLIT_BF16;
   float* wsc = (float*)cv.take((size_t)B * Gf * H * 4);
   float* scores = out_scores ? out_scores : (float*)cv.take((size_t)B * Gf * (size_t)C * 4);
   if ((st = hip_check(li::launch_latent_absorb((const uint16_t*)q, w, (const uint16_t*)w_dec, B, Gf,
-                                               H, Dh, Dc, qt16, wsc, s),
+                                               H, Dh, Dc, split, qt16, wsc, s),
                       "latent_absorb launch", s)))
     return st;
   if ((st = hip_check(li::launch_hs_score(qt16, wsc, (const uint16_t*)latent, c_scale, kv_off,
-                                          cand_idx, C, B, Gf, H, Dc, scores, s),
+                                          cand_idx, C, B, Gf, H, Dc, split, scores, s),
                       "hs_score launch", s)))
     return st;
   li::TopkRows tr = {};

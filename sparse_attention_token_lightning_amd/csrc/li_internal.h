@@ -71,10 +71,11 @@ hipError_t launch_prefill_score(const uint8_t* q, const float* q_scale, const fl
                                 int32_t k, bool fill_masked, float* scores, const SelWs& sel,
                                 hipStream_t stream);
 
-// Latent absorption: qt16[b][l][h][Dc] (fp16, range-scaled by 2^e per row) and
-// wsc[b][l][h] = w * 2^-e.
+// Latent absorption: qt16[b][l][h][Dc] (range-scaled by 2^e per row) and
+// wsc[b][l][h] = w * 2^-e.  The row is fp16, or with split two bf16 parts,
+// hi at qt16[row] and lo at qt16[B*G*H + row] (qt16 then holds 2*B*G*H*Dc).
 hipError_t launch_latent_absorb(const uint16_t* q, const float* w, const uint16_t* w_dec,
-                                int32_t B, int32_t G, int32_t H, int32_t Dh, int32_t Dc,
+                                int32_t B, int32_t G, int32_t H, int32_t Dh, int32_t Dc, bool split,
                                 uint16_t* qt16, float* wsc, hipStream_t stream);
 
 // Latent scan over contiguous ragged rows: scores[l*n_tok + kv_off[b] + s];
@@ -82,13 +83,13 @@ hipError_t launch_latent_absorb(const uint16_t* q, const float* w, const uint16_
 hipError_t launch_latent_score(const uint16_t* qt16, const float* wsc, const uint16_t* latent,
                                const float* c_scale, const int64_t* kv_off, int32_t B,
                                int64_t n_tok, int32_t max_len, int32_t G, int32_t H, int32_t Dc,
-                               int32_t k, float* scores, const SelWs& sel, hipStream_t stream);
+                               int32_t k, bool split, float* scores, const SelWs& sel, hipStream_t stream);
 
 // HS gather scan: scores[(b*Gf + f)*C + j] for the valid candidates j of b.
 hipError_t launch_hs_score(const uint16_t* qt16, const float* wsc, const uint16_t* latent,
                            const float* c_scale, const int64_t* kv_off, const int32_t* cand,
-                           int32_t C, int32_t B, int32_t Gf, int32_t H, int32_t Dc, float* scores,
-                           hipStream_t stream);
+                           int32_t C, int32_t B, int32_t Gf, int32_t H, int32_t Dc, bool split,
+                           float* scores, hipStream_t stream);
 
 // Opt-in input checks (LI_DEBUG_VALIDATE): validate_begin clears the device
 // record, the validate_* calls enqueue one check each, validate_end waits for

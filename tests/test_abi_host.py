@@ -23,6 +23,15 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     assert sorted(li.SYMBOLS) == declared_functions()
+    # every #define LI_* value the binding mirrors
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"#define (LI_[A-Z0-9_]+)\s+(-?\d+)u?\b", text))
+    assert defs, "no LI_ constants parsed"
+    for name, value in defs.items():
+        if hasattr(li, name):
+            assert getattr(li, name) == int(value), name
+    for name in ("LI_LATENT_FP16", "LI_LATENT_SPLIT_BF16", "LI_E_VALUE", "LI_MAX_K"):
+        assert name in defs and hasattr(li, name), name
 
 
 def test_library_exports_every_declared_symbol():
@@ -124,6 +133,9 @@ def test_latent_and_hs_validation():
     assert lat(Dc=192) == li.LI_E_UNSUPPORTED
     assert lat(Dh=64) == li.LI_E_UNSUPPORTED
     assert lat(flags=7) == li.LI_E_UNSUPPORTED
+    assert lat(flags=2) == li.LI_E_UNSUPPORTED
+    # the split form is accepted: the call gets as far as the workspace check
+    assert lat(flags=li.LI_LATENT_SPLIT_BF16, wsb=1) == li.LI_E_WORKSPACE
     assert lat(wsb=1) == li.LI_E_WORKSPACE
     assert lat(B=0) == li.LI_OK
 

@@ -7,32 +7,40 @@ import torch
 import oracle
 import sparse_attention_token_lightning_amd as li
 from sparse_attention_token_lightning_amd import inputs
-from _parity import check_scores, check_sets, check_topk_of_own_scores, dev
+from _parity import TOL, check_scores, check_sets, check_topk_of_own_scores, dev
 
 pytestmark = pytest.mark.gpu
 
 
-def run_latent(x, with_scores=True):
+def run_latent(x, with_scores=True, flags=li.LI_LATENT_FP16):
     sc = torch.full((x.G, max(x.n_tok, 1)), float("nan"), dtype=torch.float32, device="cuda") if with_scores else None
     idx = li.li_latent_score_group(dev(x.q, "bf16"), dev(x.w), dev(x.w_dec, "bf16"), dev(x.latent, "bf16"),
                                    dev(x.c_scale), dev(x.kv_off), int(np.diff(x.kv_off).max(initial=0)), x.k,
-                                   out_scores=sc)
+                                   out_scores=sc, flags=flags)
     torch.cuda.synchronize()
     return idx.cpu().numpy(), (sc.cpu().numpy()[:, :x.n_tok] if with_scores else None)
 
 
-def latent_parity(x, what):
-    print(f"[latent parity] {what} B={x.B} G={x.G} Dc={x.Dc} n_tok={x.n_tok}", flush=True)
-    gi, gs = run_latent(x)
+def rel_err(gpu, ref, mag):
+    """Largest |gpu - ref| / A over the scores (A = sum_h |w_h x_h|, nonzero)."""
+    mag = np.asarray(mag, np.float64)
+    ok = mag > 0
+    return float((np.abs(np.asarray(gpu, np.float64) - ref)[ok] / mag[ok]).max(initial=0.0))
+
+
+def latent_parity(x, what, flags=li.LI_LATENT_FP16, tol=TOL):
+    print(f"[latent parity] {what} B={x.B} G={x.G} Dc={x.Dc} n_tok={x.n_tok} flags={flags}", flush=True)
+    gi, gs = run_latent(x, flags=flags)
     ri, rs, ra = oracle.latent_score_group(x.q, x.q_dt, x.w, x.w_dec, x.w_dt, x.latent, x.c_dt, x.c_scale, x.kv_off,
                                            x.G, x.H, x.Dh, x.Dc, x.k)
-    check_scores(gs, rs, ra, what=what)
+    print(f"[latent parity] {what}: max |err| / A = {rel_err(gs, rs, ra):.3g}", flush=True)
+    check_scores(gs, rs, ra, tol=tol, what=what)
     for b in range(x.B):
         sl = slice(x.kv_off[b], x.kv_off[b + 1])
         n = int(x.kv_off[b + 1] - x.kv_off[b])
         check_topk_of_own_scores(gi[b], [gs[l, sl] for l in range(x.G)], [n] * x.G, x.k, f"{what} b={b}")
         for l in range(x.G):
-            check_sets(gi[b, l], ri[b, l], rs[l, sl], ra[l, sl], n, what=f"{what} b={b} l={l}")
+            check_sets(gi[b, l], ri[b, l], rs[l, sl], ra[l, sl], n, tol=tol, what=f"{what} b={b} l={l}")
 
 
 def test_latent_group_small_ragged():
@@ -82,21 +90,21 @@ def run_anchor(a):
     return idx
 
 
-def run_followers(cand, f, with_scores=True):
+def run_followers(cand, f, with_scores=True, flags=li.LI_LATENT_FP16):
     B, C = cand.shape
     sc = torch.full((B, f.G, C), float("nan"), dtype=torch.float32, device="cuda") if with_scores else None
     idx = li.li_hs_refine(cand, dev(f.q, "bf16"), dev(f.w), dev(f.w_dec, "bf16"), dev(f.latent, "bf16"),
-                          dev(f.c_scale), dev(f.kv_off), f.k, out_scores=sc)
+                          dev(f.c_scale), dev(f.kv_off), f.k, out_scores=sc, flags=flags)
     torch.cuda.synchronize()
     return idx.cpu().numpy(), (sc.cpu().numpy() if with_scores else None)
 
 
-def hs_parity(h, what, requests=None):
+def hs_parity(h, what, requests=None, flags=li.LI_LATENT_FP16, tol=TOL):
     a, f = h.anchor, h.followers
-    print(f"[hs parity] {what} B={a.B} C={h.C} Gf={f.G}", flush=True)
+    print(f"[hs parity] {what} B={a.B} C={h.C} Gf={f.G} flags={flags}", flush=True)
     cand_t = run_anchor(a)
     cand = cand_t.cpu().numpy()
-    gi, gs = run_followers(cand_t, f)
+    gi, gs = run_followers(cand_t, f, flags=flags)
     requests = range(a.B) if requests is None else requests
     for b in requests:
         sl = slice(a.kv_off[b], a.kv_off[b + 1])
@@ -111,7 +119,9 @@ def hs_parity(h, what, requests=None):
                                       f.latent[sl], f.c_dt, None if f.c_scale is None else f.c_scale[sl], one,
                                       f.G, f.H, f.Dh, f.Dc, f.k)
         nv = int((cand[b] >= 0).sum())
-        check_scores(gs[b, :, :nv], rs[0, :, :nv], ra[0, :, :nv], what=f"{what} b={b}")
+        print(f"[hs parity] {what} b={b}: max |err| / A = {rel_err(gs[b, :, :nv], rs[0, :, :nv], ra[0, :, :nv]):.3g}",
+              flush=True)
+        check_scores(gs[b, :, :nv], rs[0, :, :nv], ra[0, :, :nv], tol=tol, what=f"{what} b={b}")
         for fl in range(f.G):
             slot = oracle.topk(gs[b, fl, :nv].astype(np.float64)[None, :], [nv], f.k)[0]
             want = np.where(slot >= 0, cand[b][np.maximum(slot, 0)], -1)
@@ -129,7 +139,7 @@ def hs_parity(h, what, requests=None):
             diff = np.setxor1d(gv, rv)
             if diff.size:
                 th = rv[np.argmin(pos_s[rv])]
-                ok = np.abs(pos_s[diff] - pos_s[th]) <= 2e-3 * (pos_a[diff] + pos_a[th])
+                ok = np.abs(pos_s[diff] - pos_s[th]) <= tol * (pos_a[diff] + pos_a[th])
                 assert ok.all(), f"{what} b={b} f={fl}: set differences beyond tolerance"
 
 
@@ -152,3 +162,26 @@ def test_cfg5_hs_sampled_requests():
     """Anchor top-8192 over 16 x 131072 fp8 keys, three latent followers
     rescoring 8192 candidates each; the oracle checks two requests in full."""
     hs_parity(inputs.cfg5(), "cfg5", requests=(0, 15))
+
+
+# ---- LI_LATENT_SPLIT_BF16 ------------------------------------------------------
+# The same parity checks with the absorbed query as two bf16 parts against the
+# latent as stored; its scores are also held to a tighter bound than 2e-3 * A
+# (the form's error measures about 2e-6 * A; the fp16 form's about 2e-4 * A).
+
+SPLIT_TOL = 2e-5
+
+
+def test_latent_group_split_bf16():
+    latent_parity(inputs.make_latent(311, [3000, 0, 77, 1025], G=4, k=512), "split G4 Dc256",
+                  flags=li.LI_LATENT_SPLIT_BF16, tol=SPLIT_TOL)
+    x = inputs.make_latent(312, [2000, 700], G=3, Dc=128, H=48, k=256)
+    x.c_scale = np.random.default_rng(6).uniform(0.5, 2.0, size=x.n_tok).astype(np.float32)
+    latent_parity(x, "split G3 Dc128 H48 scaled", flags=li.LI_LATENT_SPLIT_BF16, tol=SPLIT_TOL)
+    latent_parity(inputs.make_latent(313, [1500, 2100], G=5, k=300), "split G5 Dc256",
+                  flags=li.LI_LATENT_SPLIT_BF16, tol=SPLIT_TOL)
+
+
+def test_hs_split_bf16():
+    hs_parity(inputs.make_hs(411, [9000, 3000, 500, 0], C=4096, Gf=3, k=1024), "split",
+              flags=li.LI_LATENT_SPLIT_BF16, tol=SPLIT_TOL)
