@@ -145,3 +145,20 @@ def test_decode_128k_sampled_requests():
         check_scores(gs[sl], rs, ra, what=f"128K b={b}")
         check_topk_of_own_scores(gi[b:b + 1], [gs[sl]], [131072], x.k, f"128K b={b}")
         check_sets(gi[b], ri[0], rs, ra, 131072, what=f"128K b={b}")
+
+
+def test_decode_largest_k():
+    """k = LI_MAX_K (16384): the top-k's final step holds the candidates in
+    dynamic LDS; with w = 0 (every score +0) the candidates exceed that and
+    the step runs from global memory."""
+    x = inputs.make_decode(111, [40000, 16384, 16385, 70000, 5], k=li.LI_MAX_K)
+    parity(x, what="k=16384")
+    x.w = np.zeros_like(x.w)
+    parity(x, exact=True, what="k=16384 all-equal")
+
+
+def test_decode_many_short_requests():
+    """A batch of 300 short requests (0 .. 400 keys) with k = 64: many rows
+    keep all their keys, the rest select from a few hundred."""
+    lens = np.random.default_rng(112).integers(0, 401, size=300)
+    parity(inputs.make_decode(112, lens.tolist(), k=64), what="B=300 short")
