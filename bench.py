@@ -43,15 +43,13 @@ def log(*a):
 
 
 class Trace:
-    """Per-call HIP events recorded by the library around its kernels.
-
-    The events are created through the HIP runtime this process already runs
-    (torch's), with hipEventDisableSystemFence: an event used only for timing
-    then skips the system-scope cache writeback and invalidation a default
-    event performs, which would otherwise delay and slow the kernel after it.
-    An event still sits between two kernels, so a span includes the few
-    microseconds from the event to the next kernel's start; back-to-back
-    kernels without events between them start with no gap."""
+    """Per-kernel HIP events: the library launches kernel i of a call with
+    events 2i and 2i+1 as the launch's start and stop events, which the
+    runtime sets to that kernel's own start and end (no event marker sits
+    between two kernels, so the kernels run back to back as they do
+    untraced).  The events are created through the HIP runtime this process
+    already runs (torch's), with hipEventDisableSystemFence, since they serve
+    only for timing."""
 
     DISABLE_SYSTEM_FENCE = 0x20000000
 
@@ -79,10 +77,10 @@ class Trace:
         self.li.li_trace_events(None, 0)
 
     def spans(self, i):
-        """Milliseconds between consecutive events of call i."""
+        """Milliseconds of each kernel of call i (its start/stop event pair)."""
         e = self.ev[i * self.per:(i + 1) * self.per]
         out = []
-        for j in range(self.per - 1):
+        for j in range(0, self.per, 2):
             ms = ctypes.c_float()
             if self.hip.hipEventElapsedTime(ctypes.byref(ms), e[j], e[j + 1]) != 0:
                 raise RuntimeError("hipEventElapsedTime failed")
@@ -95,10 +93,11 @@ class Trace:
         self.ev = []
 
 
-def traced(torch, li, fn, per_call, iters, check_count=True):
-    """Per-kernel milliseconds of `iters` calls, from the HIP events the library
-    records on its own stream around each kernel (each event adds a few
-    microseconds to the step, so the wall-clock timing runs without them)."""
+def traced(torch, li, fn, kernels, iters, check_count=True):
+    """Per-kernel milliseconds (averages over `iters` calls of fn, which
+    launches `kernels` kernels), from the start/stop events the library
+    attaches to its kernel launches."""
+    per_call = 2 * kernels
     tr = Trace(torch, li, per_call, iters)
     for i in range(iters):
         tr.arm(i)
@@ -109,10 +108,10 @@ def traced(torch, li, fn, per_call, iters, check_count=True):
     tr.off()
     spans = [tr.spans(i) for i in range(iters)]
     tr.close()
-    return [sum(s[j] for s in spans) / iters for j in range(per_call - 1)]
+    return [sum(s[j] for s in spans) / iters for j in range(kernels)]
 
 
-def timed(torch, li, fn, per_call, iters, warmup, check_count=True):
+def timed(torch, li, fn, kernels, iters, warmup, check_count=True):
     """Wall-clock milliseconds per call over `iters` calls (no events), then the
     per-kernel split from a traced repetition of the same calls."""
     for _ in range(warmup):
@@ -123,7 +122,7 @@ def timed(torch, li, fn, per_call, iters, warmup, check_count=True):
         fn()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / iters * 1e3
-    return wall, traced(torch, li, fn, per_call, iters, check_count)
+    return wall, traced(torch, li, fn, kernels, iters, check_count)
 
 
 def dev(torch, a, dt=None):
@@ -208,7 +207,7 @@ def components(torch, li, inputs, args):
     ws = torch.empty(li.lib().li_index_prefill_ws(x.T, x.L, x.k, 0), dtype=torch.uint8, device="cuda")
     fn = lambda: li.li_index_prefill(q, qs, w, kc, ks, x.qpos0, x.k, out_idx=idx, ws=ws)
     # u-row preparation, scan (+ thresholds), select
-    wall, (prep, scan, topk) = timed(torch, li, fn, 4, args.comp_iters, 2)
+    wall, (prep, scan, topk) = timed(torch, li, fn, 3, args.comp_iters, 2)
     pairs = sum(x.qpos0 + t + 1 for t in range(x.T))
     flop = 2.0 * x.H * x.D * pairs
     out["prefill_fp8_T4096_L65536"] = {
@@ -225,7 +224,7 @@ def components(torch, li, inputs, args):
     ws = torch.empty(li.lib().li_latent_score_group_ws(x.B, x.n_tok, 131072, x.G, x.H, x.Dc, x.k, 0),
                      dtype=torch.uint8, device="cuda")
     fn = lambda: li.li_latent_score_group(q, w, wd, lat, None, off, 131072, x.k, out_idx=idx, ws=ws)
-    wall, (absorb, scan, topk) = timed(torch, li, fn, 4, args.comp_iters, 2)
+    wall, (absorb, scan, topk) = timed(torch, li, fn, 3, args.comp_iters, 2)
     lat_bytes = x.n_tok * x.Dc * 2
     flop = 2.0 * x.G * x.H * x.Dc * x.n_tok
     out["latent_G4_B16_L131072"] = {
@@ -235,7 +234,7 @@ def components(torch, li, inputs, args):
     # the same step with LI_LATENT_SPLIT_BF16 (two bf16 products per element)
     fn = lambda: li.li_latent_score_group(q, w, wd, lat, None, off, 131072, x.k, out_idx=idx, ws=ws,
                                           flags=li.LI_LATENT_SPLIT_BF16)
-    wall, (absorb, scan, topk) = timed(torch, li, fn, 4, args.comp_iters, 2)
+    wall, (absorb, scan, topk) = timed(torch, li, fn, 3, args.comp_iters, 2)
     out["latent_split_bf16_G4_B16_L131072"] = {
         "absorb_ms": absorb, "scan_ms": scan, "topk_ms": topk, "total_ms": wall,
         "scan_gbs": lat_bytes / (scan * 1e-3) / 1e9, "scan_hbm_frac": lat_bytes / (scan * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -257,9 +256,9 @@ def components(torch, li, inputs, args):
     fa = lambda: li.li_index_decode(aq, aw, akc, aks, off, 131072, h.C, out_idx=cand, ws=ws_a)
     ff = lambda: li.li_hs_refine(cand, fq, fw, fwd, lat, None, off, f.k, out_idx=fidx, ws=ws_f)
     fn_native = lambda: li.li_index_decode(aq, aw, akc, aks, off, 131072, 2048, out_idx=nidx, ws=ws_a)
-    _, (a_scan, a_topk) = timed(torch, li, fa, 3, args.comp_iters, 2)
-    _, (f_abs, f_scan, f_topk) = timed(torch, li, ff, 4, args.comp_iters, 2)
-    _, (n_scan, n_topk) = timed(torch, li, fn_native, 3, args.comp_iters, 2)
+    _, (a_scan, a_topk) = timed(torch, li, fa, 2, args.comp_iters, 2)
+    _, (f_abs, f_scan, f_topk) = timed(torch, li, ff, 3, args.comp_iters, 2)
+    _, (n_scan, n_topk) = timed(torch, li, fn_native, 2, args.comp_iters, 2)
     hs_ms = a_scan + a_topk + f_abs + f_scan + f_topk
     native = n_scan + n_topk
     out["hs_B16_L131072_C8192_F3"] = {
@@ -282,7 +281,7 @@ def components(torch, li, inputs, args):
         kc, ks = copies[turn[0] % RAGGED_COPIES]
         turn[0] += 1
         li.li_index_decode(q, w, kc, ks, off, int(x.lens.max()), x.k, out_idx=idx, ws=ws)
-    wall, (scan, topk) = timed(torch, li, fn, 3, max(args.comp_iters, 2 * RAGGED_COPIES), 2)
+    wall, (scan, topk) = timed(torch, li, fn, 2, max(args.comp_iters, 2 * RAGGED_COPIES), 2)
     out["decode_fp8_B32_ragged8K-32K"] = {
         "scan_ms": scan, "topk_ms": topk, "total_ms": wall, "keys": x.n_tok,
         "scan_gbs": x.n_tok * FP8_KEY_BYTES / (scan * 1e-3) / 1e9,
@@ -344,7 +343,7 @@ def main():
     ms_per_step = elapsed / args.steps * 1e3
     # The same steps again with the library's HIP events on its stream:
     # start | after scan | after top-k.
-    scan_ms, topk_ms = traced(torch, li, step, 3, args.steps)
+    scan_ms, topk_ms = traced(torch, li, step, 2, args.steps)
     keys = B * Lk
     achieved = keys * FP8_KEY_BYTES / (scan_ms * 1e-3) / 1e9
     traffic = load_traffic("decode_score", source_hash("decode.hip", "li_device.h"), keys)
@@ -370,9 +369,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "decode_score", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": keys * FP8_KEY_BYTES, "avg_launch_ms": scan_ms,
-                     "timing": "HIP events (hipEventDisableSystemFence) that the library records on its "
-                               "stream around each kernel, over a repetition of the timed steps; a span "
-                               "includes the gap from the event to the kernel's start (about 5 us)"},
+                     "timing": "HIP start/stop events of the kernel's own launch (hipExtLaunchKernel), on "
+                               "the library's stream, averaged over a repetition of the timed steps"},
         "components": {"decode_fp8_B32_L131072": {"scan_ms": scan_ms, "top2048_ms": topk_ms,
                                                   "top2048_us": topk_ms * 1e3,
                                                   "scan_gbs": achieved}},

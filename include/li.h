@@ -217,11 +217,14 @@ size_t li_topk_ws(int32_t rows, int32_t n, int32_t k);
 
 /* ---------------------------------------------------------------------------
  * Measurement hook (not part of the computation): after li_trace_events(ev, n)
- * with n > 0, every entry point called on this thread records ev[0] on its
- * stream before its first kernel and ev[i] after its i-th kernel launch, as
- * long as slots remain; li_trace_count() returns how many events the last
- * call recorded.  `events` are caller-created hipEvent_t handles that must
- * outlive their use.  li_trace_events(NULL, 0) switches the hook off.
+ * with n > 0, every entry point called on this thread launches its i-th
+ * kernel (i = 0, 1, ...) with ev[2i] and ev[2i+1] as the launch's start and
+ * stop events (hipExtLaunchKernel), which the runtime sets to that kernel's
+ * own start and end, as long as pairs remain; hipEventElapsedTime(ev[2i],
+ * ev[2i+1]) is then kernel i's duration.  li_trace_count() returns how many
+ * events the last call used.  `events` are caller-created hipEvent_t handles
+ * that must outlive their use.  li_trace_events(NULL, 0) switches the hook
+ * off.
  * ------------------------------------------------------------------------- */
 void li_trace_events(void** events, int32_t capacity);
 int32_t li_trace_count(void);

@@ -209,12 +209,10 @@ hipError_t launch_decode_score(const uint16_t* q, const float* w, const void* kc
   dim3 grid((unsigned)((max_len + chunk - 1) / chunk), (unsigned)B);
   dim3 block(64 * kDecWaves);
   if (kc_fp8)
-    decode_score_kernel<true><<<grid, block, 0, stream>>>(
-        q, w, (const uint8_t*)kc, k_scale, kv_off, H, tpw, k, scores, sel);
-  else
-    decode_score_kernel<false><<<grid, block, 0, stream>>>(
-        q, w, (const uint8_t*)kc, k_scale, kv_off, H, tpw, k, scores, sel);
-  return hipGetLastError();
+    return launch_kernel(decode_score_kernel<true>, grid, block, 0, stream, q, w, (const uint8_t*)kc, k_scale,
+                         kv_off, H, tpw, k, scores, sel);
+  return launch_kernel(decode_score_kernel<false>, grid, block, 0, stream, q, w, (const uint8_t*)kc, k_scale,
+                       kv_off, H, tpw, k, scores, sel);
 }
 
 }  // namespace li

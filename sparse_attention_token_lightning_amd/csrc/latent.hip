@@ -617,19 +617,16 @@ hipError_t launch_ls2(bool split, int Dc, dim3 grid, hipStream_t stream, const u
   static_assert(kSpLayers == kLsWaves, "both forms cover the same layers per workgroup (grid z)");
   if (split) {
     if (Dc == 256)
-      latent_split_kernel<256, GATHER, CSCALE><<<grid, dim3(kSpThreads), 0, stream>>>(
-          qt16, qlo, wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
-    else
-      latent_split_kernel<128, GATHER, CSCALE><<<grid, dim3(kSpThreads), 0, stream>>>(
-          qt16, qlo, wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
-  } else if (Dc == 256) {
-    latent_score_kernel<256, GATHER, CSCALE><<<grid, dim3(kLsThreads), 0, stream>>>(
-        qt16, wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
-  } else {
-    latent_score_kernel<128, GATHER, CSCALE><<<grid, dim3(kLsThreads), 0, stream>>>(
-        qt16, wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
+      return launch_kernel(latent_split_kernel<256, GATHER, CSCALE>, grid, dim3(kSpThreads), 0, stream, qt16, qlo,
+                           wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
+    return launch_kernel(latent_split_kernel<128, GATHER, CSCALE>, grid, dim3(kSpThreads), 0, stream, qt16, qlo,
+                         wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
   }
-  return hipGetLastError();
+  if (Dc == 256)
+    return launch_kernel(latent_score_kernel<256, GATHER, CSCALE>, grid, dim3(kLsThreads), 0, stream, qt16, wsc,
+                         latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
+  return launch_kernel(latent_score_kernel<128, GATHER, CSCALE>, grid, dim3(kLsThreads), 0, stream, qt16, wsc,
+                       latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
 }
 
 template <bool GATHER>
@@ -651,9 +648,8 @@ hipError_t launch_latent_absorb(const uint16_t* q, const float* w, const uint16_
                                 uint16_t* qt16, float* wsc, hipStream_t stream) {
   (void)Dh;
   if (B <= 0) return hipSuccess;
-  latent_absorb_kernel<<<dim3((unsigned)(G * H)), dim3(256), 0, stream>>>(q, w, w_dec, B, G, H, Dc, split,
-                                                                          qt16, wsc);
-  return hipGetLastError();
+  return launch_kernel(latent_absorb_kernel, dim3((unsigned)(G * H)), dim3(256), 0, stream, q, w, w_dec, B, G, H, Dc,
+                       split, qt16, wsc);
 }
 
 hipError_t launch_latent_score(const uint16_t* qt16, const float* wsc, const uint16_t* latent,

@@ -17,21 +17,12 @@ namespace {
 thread_local std::string g_err;
 
 // Opt-in measurement trace (li_trace_events): caller-created hipEvents that the
-// entry points record around their kernels.
+// entry points attach, two per kernel (start, stop), to their kernel launches.
 thread_local hipEvent_t* g_trace = nullptr;
 thread_local int32_t g_trace_cap = 0;
 thread_local int32_t g_trace_n = 0;
 
-void trace_begin(hipStream_t s) {
-  g_trace_n = 0;
-  if (g_trace && g_trace_cap > 0 && hipEventRecord(g_trace[0], s) == hipSuccess) g_trace_n = 1;
-}
-
-void trace_mark(hipStream_t s) {
-  if (g_trace && g_trace_n > 0 && g_trace_n < g_trace_cap &&
-      hipEventRecord(g_trace[g_trace_n], s) == hipSuccess)
-    ++g_trace_n;
-}
+void trace_begin() { g_trace_n = 0; }
 
 li_status fail(li_status s, const char* fmt, ...) {
   char buf[512];
@@ -44,10 +35,8 @@ li_status fail(li_status s, const char* fmt, ...) {
 }
 
 li_status hip_check(hipError_t e, const char* what, hipStream_t s) {
-  if (e == hipSuccess) {
-    trace_mark(s);
-    return LI_OK;
-  }
+  (void)s;
+  if (e == hipSuccess) return LI_OK;
   return fail(LI_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
@@ -187,6 +176,17 @@ li_status check_ws(void* ws, size_t ws_bytes, size_t need) {
 
 }  // namespace
 
+namespace li {
+void trace_next(hipEvent_t* start, hipEvent_t* stop) {
+  *start = *stop = nullptr;
+  if (g_trace && g_trace_n + 2 <= g_trace_cap) {
+    *start = g_trace[g_trace_n];
+    *stop = g_trace[g_trace_n + 1];
+    g_trace_n += 2;
+  }
+}
+}  // namespace li
+
 extern "C" {
 
 const char* li_status_str(li_status s) {
@@ -212,6 +212,7 @@ void li_trace_events(void** events, int32_t capacity) {
 }
 
 int32_t li_trace_count(void) { return g_trace_n; }
+
 
 size_t li_index_decode_ws(int32_t B, int64_t n_tok, int32_t max_len, int32_t k,
                           int32_t has_out_scores) {
@@ -247,7 +248,7 @@ li_status li_index_decode(const void* q, li_dtype q_dt, const float* w, const vo
         li::validate_scales(k_scale, n_tok, li::kBadKScale, s);
       })))
     return st;
-  trace_begin(s);
+  trace_begin();
   Carver cv(ws);
   float* scores = out_scores ? out_scores : (float*)cv.take((size_t)n_tok * 4);
   const li::SelWs sel = carve_sel(cv, B, max_len, li::decode_chunk(n_tok), k);
@@ -299,7 +300,7 @@ li_status li_index_prefill(const void* q, li_dtype q_dt, const float* q_scale, c
         li::validate_scales(k_scale, L, li::kBadKScale, s);
       })))
     return st;
-  trace_begin(s);
+  trace_begin();
   Carver cv(ws);
   float* scores = out_scores ? out_scores : (float*)cv.take((size_t)T * (size_t)L * 4);
   uint8_t* uq = (uint8_t*)cv.take((size_t)T * li::kLinRows * 128);
@@ -371,7 +372,7 @@ li_status li_latent_score_group(const void* q, li_dtype q_dt, const float* w, co
         li::validate_scales(c_scale, n_tok, li::kBadCScale, s);
       })))
     return st;
-  trace_begin(s);
+  trace_begin();
   Carver cv(ws);
   uint16_t* qt16 = (uint16_t*)cv.take((size_t)B * G * H * Dc * 4);
   const bool split = flags == LI_LATENT_SPLIT_BF16;
@@ -431,7 +432,7 @@ li_status li_hs_refine(const int32_t* cand_idx, int32_t C, const void* q, li_dty
         li::validate_bf16(w_dec, (int64_t)Gf * Dc * H * Dh, li::kBadWDec, s);
       })))
     return st;
-  trace_begin(s);
+  trace_begin();
   Carver cv(ws);
   uint16_t* qt16 = (uint16_t*)cv.take((size_t)B * Gf * H * Dc * 4);
   const bool split = flags == LI_LATENT_SPLIT_BF16;
@@ -489,7 +490,7 @@ li_status li_topk(const float* scores, int64_t row_stride, const int32_t* row_le
         li::validate_score_rows(scores, row_stride, rows, n, row_len, s);
       })))
     return st;
-  trace_begin(s);
+  trace_begin();
   return hip_check(li::launch_topk(tr, s), "topk launch", s);
 }
 

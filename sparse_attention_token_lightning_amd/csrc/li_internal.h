@@ -1,6 +1,7 @@
 // Host-side launchers shared between the kernel files and the C-ABI layer.
 // Every launcher only enqueues work on `stream` and returns the launch status.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -8,6 +9,22 @@
 #include "li_select.h"
 
 namespace li {
+
+// Measurement hook (li_trace_events): the (start, stop) events to attach to
+// the next kernel launch of the current entry point, or two nulls.
+void trace_next(hipEvent_t* start, hipEvent_t* stop);
+
+// Every kernel of the entry points is launched through here.  With the
+// measurement hook on, the launch carries a (start, stop) event pair that
+// the runtime sets to the kernel's own start and end, so no event marker
+// sits between two kernels of a call.
+template <typename F, typename... Args>
+hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t stream, Args... args) {
+  hipEvent_t start = nullptr, stop = nullptr;
+  trace_next(&start, &stop);
+  hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, start, stop, 0u, args...);
+  return hipGetLastError();
+}
 
 // How the top-k kernel finds row r of the score matrix.
 enum TopkMode : int32_t {

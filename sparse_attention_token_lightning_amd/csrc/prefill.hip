@@ -367,8 +367,8 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
 hipError_t launch_prefill_linear(const uint8_t* q, const float* w, int32_t T, int32_t H, uint8_t* uq,
                                  float* usc, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
-  prefill_linear_kernel<<<dim3((unsigned)((T + 1) / 2)), dim3(256), 0, stream>>>(q, w, T, H, uq, usc);
-  return hipGetLastError();
+  return launch_kernel(prefill_linear_kernel, dim3((unsigned)((T + 1) / 2)), dim3(256), 0, stream, q, w, T, H, uq,
+                       usc);
 }
 
 hipError_t launch_prefill_score(const uint8_t* q, const float* q_scale, const float* w,
@@ -378,13 +378,12 @@ hipError_t launch_prefill_score(const uint8_t* q, const float* q_scale, const fl
                                 hipStream_t stream) {
   if (T <= 0 || L <= 0) return hipSuccess;
   dim3 grid((unsigned)((T + kPfTokPerBlock - 1) / kPfTokPerBlock));
+  const int fill = fill_masked ? 1 : 0;
   if (k_scale)
-    prefill_score_kernel<true><<<grid, dim3(64 * kPfWaves), 0, stream>>>(
-        q, q_scale, w, uq, usc, kc, k_scale, T, L, qpos0, H, k, fill_masked ? 1 : 0, scores, sel.thr);
-  else
-    prefill_score_kernel<false><<<grid, dim3(64 * kPfWaves), 0, stream>>>(
-        q, q_scale, w, uq, usc, kc, k_scale, T, L, qpos0, H, k, fill_masked ? 1 : 0, scores, sel.thr);
-  return hipGetLastError();
+    return launch_kernel(prefill_score_kernel<true>, grid, dim3(64 * kPfWaves), 0, stream, q, q_scale, w, uq, usc,
+                         kc, k_scale, T, L, qpos0, H, k, fill, scores, sel.thr);
+  return launch_kernel(prefill_score_kernel<false>, grid, dim3(64 * kPfWaves), 0, stream, q, q_scale, w, uq, usc,
+                       kc, k_scale, T, L, qpos0, H, k, fill, scores, sel.thr);
 }
 
 }  // namespace li

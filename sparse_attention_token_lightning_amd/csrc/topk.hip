@@ -757,13 +757,13 @@ hipError_t launch_topk_segmented(const TopkRows& a, const SelWs& ws, hipStream_t
   if (w.seg == 2 * kSeg) {
     static bool lds_set = false;
     if (hipError_t e = allow_lds(topk_segmented_kernel<2 * kSeg / kSegThreads>, lds_set)) return e;
-    topk_segmented_kernel<2 * kSeg / kSegThreads><<<grid, dim3(kSegThreads), lds, stream>>>(a, w);
-  } else {
-    static bool lds_set = false;
-    if (hipError_t e = allow_lds(topk_segmented_kernel<kSeg / kSegThreads>, lds_set)) return e;
-    topk_segmented_kernel<kSeg / kSegThreads><<<grid, dim3(kSegThreads), lds, stream>>>(a, w);
+    return launch_kernel(topk_segmented_kernel<2 * kSeg / kSegThreads>, grid, dim3(kSegThreads), (uint32_t)lds,
+                         stream, a, w);
   }
-  return hipGetLastError();
+  static bool lds_set = false;
+  if (hipError_t e = allow_lds(topk_segmented_kernel<kSeg / kSegThreads>, lds_set)) return e;
+  return launch_kernel(topk_segmented_kernel<kSeg / kSegThreads>, grid, dim3(kSegThreads), (uint32_t)lds, stream,
+                       a, w);
 }
 
 static hipError_t launch_row(const TopkRows& a, const SelWs& ws, int how, hipStream_t stream) {
@@ -771,9 +771,8 @@ static hipError_t launch_row(const TopkRows& a, const SelWs& ws, int how, hipStr
   static bool lds_set = false;
   if (hipError_t e = allow_lds(topk_row_kernel, lds_set)) return e;
   const int cap = seg_cap_for(a.k);
-  topk_row_kernel<<<dim3((unsigned)a.rows), dim3(kRowThreads), (size_t)cap * sizeof(uint2), stream>>>(
-      a, ws, how, cap);
-  return hipGetLastError();
+  return launch_kernel(topk_row_kernel, dim3((unsigned)a.rows), dim3(kRowThreads), (uint32_t)(cap * sizeof(uint2)),
+                       stream, a, ws, how, cap);
 }
 
 hipError_t launch_topk_self(const TopkRows& a, const SelWs& ws, hipStream_t stream) {
