@@ -31,7 +31,9 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *     enqueue kernels on it and return without synchronising; results are
  *     ready when the stream has drained.  Ragged lengths are read on the
- *     device from `kv_off`, so the host never reads device memory.
+ *     device from `kv_off`, so the host never reads device memory.  A call
+ *     may be captured into a HIP graph (stream capture) and replayed; the
+ *     workspace and outputs it was given are then reused by every replay.
  *   - Errors found on the host (a NULL required pointer, a bad size, an
  *     unsupported dtype or shape, a workspace that is too small) return a
  *     status before anything is enqueued.  A failed kernel launch returns
