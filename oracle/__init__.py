@@ -39,8 +39,12 @@ def lib():
         _lib.oracle_latent_score_group.argtypes = [vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, vp, dp, dp]
         _lib.oracle_latent_reconstruct_scores.argtypes = [vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, dp]
         _lib.oracle_hs_refine.argtypes = [vp, i32, vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, vp, dp, dp]
+        _lib.oracle_latent_append.argtypes = [vp, i32, vp, i32, vp, i32, i32, i32, vp, i64, dp]
+        _lib.oracle_encode_bf16.restype = C.c_uint16
+        _lib.oracle_encode_bf16.argtypes = [C.c_double]
         for f in ("oracle_topk", "oracle_index_decode", "oracle_index_prefill", "oracle_latent_absorb",
-                  "oracle_latent_score_group", "oracle_latent_reconstruct_scores", "oracle_hs_refine"):
+                  "oracle_latent_score_group", "oracle_latent_reconstruct_scores", "oracle_hs_refine",
+                  "oracle_latent_append"):
             getattr(_lib, f).restype = C.c_int
     return _lib
 
@@ -164,3 +168,26 @@ def hs_refine(cand_idx, q, q_dt, w, w_dec, w_dt, latent, c_dt, c_scale, kv_off, 
                                 _p(idx), _p(sc), _p(ab))
     _check(rc, "oracle_hs_refine")
     return idx, sc, ab
+
+
+def encode_bf16(v):
+    """The bfloat16 code (uint16) nearest to float v, ties to even."""
+    return int(lib().oracle_encode_bf16(float(v)))
+
+
+def latent_append(h, h_dt, w_enc, w_dt, dst_row, latent):
+    """Latent-cache append: c[b][d] = sum_i h[b][i] * w_enc[d][i] (fp64), stored
+    as bf16 (nearest, ties to even) at row dst_row[b] of a copy of `latent`
+    ([n_tok][Dc] raw bf16).  Returns (new latent, exact sums [B][Dc])."""
+    h = _arr(h, h_dt)
+    w_enc = _arr(w_enc, w_dt)
+    B, d_model = h.shape
+    Dc = w_enc.shape[0]
+    assert w_enc.shape == (Dc, d_model)
+    out = np.array(_arr(latent, "bf16"), copy=True)
+    n_tok = out.shape[0]
+    dst = np.ascontiguousarray(dst_row, dtype=np.int64)
+    exact = np.zeros((B, Dc), np.float64)
+    _check(lib().oracle_latent_append(_p(h), _CODES[h_dt], _p(w_enc), _CODES[w_dt], _p(dst), B, d_model, Dc,
+                                      _p(out), n_tok, _p(exact)), "oracle_latent_append")
+    return out, exact

@@ -38,7 +38,11 @@
  *   - fp8 is OCP E4M3FN (bias 7, no infinities, S.1111.111 is NaN);
  *   - the latent decoder W_l is stored [Dc][H*Dh]; head h's key is
  *     k[j] = sum_c W_l[c][h*Dh + j] * c_s[c], so the absorbed query is
- *     qt[c] = sum_j W_l[c][h*Dh + j] * q[j].
+ *     qt[c] = sum_j W_l[c][h*Dh + j] * q[j];
+ *   - latent-cache append: the page builds the group's shared latent from
+ *     the first layer's hidden state without giving the encoder; read as a
+ *     linear down-projection c = W_enc h (W_enc stored [Dc][d_model]), the
+ *     sum taken exactly and stored once as bfloat16, nearest, ties to even.
  *
  * Every function returns 0 on success and a negative value on a bad argument.
  */
@@ -464,3 +468,58 @@ int oracle_hs_refine(const int32_t* cand_idx, int C, const void* q, int q_dt, co
   free(qt);
   return rc;
 }
+
+/* ---- latent-cache append ---------------------------------------------------- */
+/*
+ * "LatentIndex: Cross-Layer Sharing with Layer-Specific Selection for Sparse
+ * Attention", Abstract and Figure 1: a layer group builds its shared latent
+ * cache from the group's first layer's hidden states.  The pages do not give
+ * the encoder; the reading here is a linear down-projection (the latent of
+ * Multi-head Latent Attention, whose principle the page extends):
+ *     c[b][d] = sum_i h[b][i] * w_enc[d][i]
+ * stored as bfloat16 (nearest, ties to even) at latent row dst_row[b].
+ */
+
+/* bfloat16 code nearest to a finite real value, ties to the even code.
+ * bfloat16 keeps 8 significant bits (exponent range of binary32): a normal
+ * value is s * 2^(e-7) with s an integer in [128, 256); below 2^-126 the
+ * spacing is fixed at 2^-133. */
+static uint16_t enc_bf16_rne(double v) {
+  uint16_t sgn = signbit(v) ? 0x8000u : 0u;
+  double a = fabs(v);
+  if (a == 0.0) return sgn;
+  if (a < ldexp(1.0, -126)) {                  /* subnormal range */
+    double q = rint(ldexp(a, 133));            /* rint: nearest, ties to even */
+    return (uint16_t)(sgn | (uint16_t)q);      /* q == 128 is the smallest normal */
+  }
+  int e;
+  double m = frexp(a, &e);                     /* a = m * 2^e, m in [0.5, 1) */
+  double s = rint(ldexp(m, 8));                /* significand, 8 bits: [128, 256] */
+  if (s == 256.0) {                            /* rounded up to the next binade */
+    s = 128.0;
+    e += 1;
+  }
+  int biased = (e - 1) + 127;                  /* a ~ (s/128) * 2^(e-1) */
+  if (biased >= 255) return (uint16_t)(sgn | 0x7F80u); /* beyond range: infinity */
+  return (uint16_t)(sgn | (uint16_t)(biased << 7) | (uint16_t)((int)s - 128));
+}
+
+int oracle_latent_append(const void* h, int h_dt, const void* w_enc, int w_dt, const int64_t* dst_row, int B,
+                         int d_model, int Dc, uint16_t* latent, int64_t n_tok, double* exact) {
+  if (!dt_ok(h_dt) || !dt_ok(w_dt) || B < 0 || d_model <= 0 || Dc <= 0) return -1;
+  for (int b = 0; b < B; ++b)
+    if (dst_row[b] < 0 || dst_row[b] >= n_tok) return -1;
+  for (int b = 0; b < B; ++b) {
+    for (int d = 0; d < Dc; ++d) {
+      double acc = 0.0;
+      for (int i = 0; i < d_model; ++i)
+        acc += dec_at(h, h_dt, (int64_t)b * d_model + i) * dec_at(w_enc, w_dt, (int64_t)d * d_model + i);
+      if (exact) exact[(int64_t)b * Dc + d] = acc;
+      latent[dst_row[b] * Dc + d] = enc_bf16_rne(acc);
+    }
+  }
+  return 0;
+}
+
+/* Exported so that tests can pin the bfloat16 encoder on its own. */
+uint16_t oracle_encode_bf16(double v) { return enc_bf16_rne(v); }

@@ -335,3 +335,100 @@ def test_hs_followers_pick_from_the_candidate_set_by_their_own_scores():
         assert np.array_equal(hs[0, f], s)
         want = cand[0][np.sort(np.argsort(-s, kind="stable")[:10])]
         assert np.array_equal(hi[0, f], want)
+
+
+# ---- latent-cache append -------------------------------------------------------
+
+def test_bf16_encoder_matches_format_points_and_library_cast():
+    enc = oracle.encode_bf16
+    # hand-known codes: 1.0, exact integers, ties to even, signed zero, subnormals, max, overflow
+    assert enc(1.0) == 0x3F80 and enc(-2.0) == 0xC000
+    assert enc(258.0) == 0x4381                      # 258 = 129 * 2: exact
+    assert enc(257.0) == 0x4380                      # tie between 256 and 258 -> even significand (256)
+    assert enc(259.0) == 0x4382                      # tie between 258 and 260 -> even significand (260)
+    assert enc(0.0) == 0x0000 and enc(-0.0) == 0x8000
+    assert enc(2.0 ** -133) == 0x0001                # smallest subnormal
+    assert enc(0.5 * 2.0 ** -133) == 0x0000          # tie with zero -> even (zero)
+    assert enc(1.5 * 2.0 ** -133) == 0x0002          # tie between 1 and 2 -> even (2)
+    assert enc(2.0 ** -126) == 0x0080                # smallest normal
+    assert enc(255 / 128 * 2.0 ** 127) == 0x7F7F     # largest finite
+    assert enc((2 - 2.0 ** -9) * 2.0 ** 127) == 0x7F80  # tie above the largest finite -> infinity
+    # fp32 inputs against torch's float32 -> bfloat16 cast (round to nearest even)
+    rng = np.random.default_rng(11)
+    vals = np.concatenate([rng.standard_normal(3000) * 10.0 ** rng.integers(-30, 30, 3000),
+                           rng.standard_normal(500) * 1e-39]).astype(np.float32)
+    ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    got = np.array([enc(float(v)) for v in vals], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def _bf16_codes(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_latent_append_small_integers_equal_integer_matmul():
+    rng = np.random.default_rng(21)
+    B, d_model, Dc, n_tok = 5, 96, 24, 40
+    h = rng.integers(-3, 4, size=(B, d_model))
+    w = rng.integers(-3, 4, size=(Dc, d_model))
+    dst = np.array([7, 0, 39, 12, 13], np.int64)
+    before = rng.integers(0, 2 ** 16, size=(n_tok, Dc), dtype=np.uint16)
+    out, exact = oracle.latent_append(_bf16_codes(h), "bf16", _bf16_codes(w), "bf16", dst, before)
+    want = h @ w.T                                    # integers, |value| <= 864: exact in bf16 only if small
+    assert np.array_equal(exact, want.astype(np.float64))
+    small = np.abs(want) <= 256
+    assert small.mean() > 0.9
+    got_vals = torch.from_numpy(out[dst].view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(got_vals[small], want[small].astype(np.float32))
+    untouched = np.setdiff1d(np.arange(n_tok), dst)
+    assert np.array_equal(out[untouched], before[untouched])
+
+
+def test_latent_append_identity_encoder_copies_the_hidden_state():
+    rng = np.random.default_rng(22)
+    B, d = 4, 64
+    h = _bf16_codes(rng.standard_normal((B, d)))
+    eye = _bf16_codes(np.eye(d))
+    dst = np.array([3, 1, 2, 0], np.int64)
+    out, _ = oracle.latent_append(h, "bf16", eye, "bf16", dst, np.zeros((4, d), np.uint16))
+    assert np.array_equal(out[dst], h)
+
+
+def test_latent_append_rounds_the_exact_sum_to_nearest_even():
+    # one hidden row [256, 1, 0, ...] against encoder rows picking (a) 256 + 1 = 257 (tie -> 256),
+    # (b) 256 + 3 = 259 (tie -> 260), (c) 256 + 2 = 258 (exact), (d) a sum below bf16 resolution
+    d_model = 32
+    h = np.zeros((1, d_model)); h[0, 0] = 256.0; h[0, 1] = 1.0; h[0, 2] = 2.0 ** -20
+    w = np.zeros((4, d_model))
+    w[0, 0] = 1; w[0, 1] = 1
+    w[1, 0] = 1; w[1, 1] = 3
+    w[2, 0] = 1; w[2, 1] = 2
+    w[3, 1] = 1; w[3, 2] = 1                          # 1 + 2^-20 -> 1.0
+    out, exact = oracle.latent_append(_bf16_codes(h), "bf16", _bf16_codes(w), "bf16",
+                                      np.array([0], np.int64), np.zeros((1, 4), np.uint16))
+    assert list(exact[0]) == [257.0, 259.0, 258.0, 1.0 + 2.0 ** -20]
+    assert list(out[0]) == [0x4380, 0x4382, 0x4381, 0x3F80]
+
+
+def test_latent_append_random_matches_float64_matmul_then_rounding():
+    rng = np.random.default_rng(23)
+    B, d_model, Dc = 6, 256, 48
+    h = _bf16_codes(rng.standard_normal((B, d_model)))
+    w = _bf16_codes(rng.standard_normal((Dc, d_model)) * 0.05)
+    hv = torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).double()
+    wv = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).double()
+    ref = (hv @ wv.T).numpy()                         # library matmul, non-square operands
+    dst = np.arange(B, dtype=np.int64)[::-1].copy()
+    out, exact = oracle.latent_append(h, "bf16", w, "bf16", dst, np.zeros((B, Dc), np.uint16))
+    assert np.allclose(exact, ref, rtol=0, atol=1e-12)
+    # rounding: each stored code brackets the exact value within half a bf16 step
+    got = torch.from_numpy(out[dst].view(np.int16)).view(torch.bfloat16).double().numpy()
+    step = np.exp2(np.floor(np.log2(np.abs(ref))) - 7)
+    assert np.all(np.abs(got - ref) <= step / 2)
+
+
+def test_latent_append_rejects_rows_outside_the_cache():
+    h = np.zeros((1, 32), np.uint16)
+    w = np.zeros((2, 32), np.uint16)
+    with pytest.raises(Exception):
+        oracle.latent_append(h, "bf16", w, "bf16", np.array([5], np.int64), np.zeros((5, 2), np.uint16))
