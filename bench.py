@@ -34,6 +34,7 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0    # dense fp8 MFMA
 BF16_PEAK_TFLOPS = 2500.0   # dense bf16 / fp16 MFMA
 FP8_KEY_BYTES = 128 + 4     # one fp8 key row + its fp32 scale
+APPEND_COPIES = 6           # hidden-state / encoder copies the append rotates over
 RAGGED_COPIES = 6           # key-cache copies the ragged decode rotates over (MALL is 256 MB)
 METRIC = "decode indexer keys scored/s + HBM GB/s at 128K; prefill TFLOP/s; top-2048 µs"
 
@@ -288,6 +289,31 @@ def components(torch, li, inputs, args):
         "scan_hbm_frac": x.n_tok * FP8_KEY_BYTES / (scan * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "note": f"calls rotate over {RAGGED_COPIES} copies of the 86.5 MB cache so the keys come from HBM, "
                 "not the 256 MB MALL"}
+    del q, w, off, copies, idx, ws, x
+    # ---- latent-cache append: prefill chunk (T = 4096) and decode step (B = 16) ---
+    # h and W_enc rotate over copies (the chunk's 59 MB would otherwise be served
+    # from the 256 MB MALL), as a model step streams other weights in between.
+    for x in (inputs.append_prefill(), inputs.append_decode()):
+        srcs = [(dev(torch, x.h, "bf16"), dev(torch, x.w_enc, "bf16")) for _ in range(APPEND_COPIES)]
+        dst = dev(torch, x.dst_row)
+        lat = torch.zeros((x.n_tok, x.Dc), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(L.li_latent_append_ws(x.M, x.d_model, x.Dc), dtype=torch.uint8, device="cuda")
+        turn = [0]
+
+        def fn():
+            h, wenc = srcs[turn[0] % APPEND_COPIES]
+            turn[0] += 1
+            li.li_latent_append(h, wenc, dst, lat, ws=ws)
+        wall, (gemm, red) = timed(torch, li, fn, 2, max(args.comp_iters, 2 * APPEND_COPIES), 2)
+        nbytes = 2 * (x.M * x.d_model + x.Dc * x.d_model + x.M * x.Dc) + 8 * x.M
+        flop = 2.0 * x.M * x.Dc * x.d_model
+        t = (gemm + red) * 1e-3
+        out[x.name] = {
+            "gemm_ms": gemm, "reduce_ms": red, "total_ms": wall, "splits": L.li_latent_append_ws(x.M, x.d_model, x.Dc)
+            // max(1, x.M * x.Dc * 4), "algorithmic_bytes": nbytes,
+            "gbs": nbytes / t / 1e9, "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBS,
+            "tflops": flop / t / 1e12, "mfma_frac_bf16": flop / t / 1e12 / BF16_PEAK_TFLOPS}
+        del srcs, dst, lat, ws
     return out
 
 
@@ -376,7 +402,7 @@ def main():
                                                   "scan_gbs": achieved}},
     }
     if not args.no_components:
-        log("[bench] components: prefill, latent, HS, ragged decode")
+        log("[bench] components: prefill, latent, HS, ragged decode, latent append")
         del ws
         result["components"].update(components(torch, li, inputs, args))
     if not args.no_cpu_baseline:

@@ -202,6 +202,32 @@ size_t li_hs_refine_ws(int32_t B, int32_t C, int32_t Gf, int32_t H, int32_t Dc, 
                        int32_t has_out_scores);
 
 /* ---------------------------------------------------------------------------
+ * li_latent_append — LatentIndex: write new tokens' rows of a group's shared
+ * latent cache, built from the group's first-layer hidden states (LatentIndex
+ * page, Abstract and Figure 1).  The page does not give the encoder; this is
+ * the linear down-projection of Multi-head Latent Attention:
+ *     latent[dst_row[m]][c] = bf16( sum_i h[m][i] * w_enc[c][i] )
+ * accumulated in fp32 and rounded once to bfloat16 (nearest, ties to even).
+ * A ragged batch appends each request's new tokens at rows of its own, e.g.
+ * dst_row = kv_off[b] + old_len_b + j for its j-th new token.
+ *
+ *   h       [M][d_model]  LI_BF16, hidden states of the M new tokens
+ *   w_enc   [Dc][d_model] LI_BF16
+ *   dst_row [M] int64, device; each in [0, n_tok) and all distinct (a repeated
+ *           row's contents are unspecified; the range is checked only under
+ *           LI_DEBUG_VALIDATE)
+ *   latent  [n_tok][Dc]   LI_BF16, written in place; other rows are untouched
+ *   M >= 0 (M = 0 does nothing; h and dst_row may then be NULL);
+ *   d_model a positive multiple of 64;  Dc 128 or 256
+ *   ws      li_latent_append_ws(M, d_model, Dc) bytes (fp32 partial sums of
+ *           the K split; 0 when one split covers K)
+ * ------------------------------------------------------------------------- */
+li_status li_latent_append(const void* h, li_dtype h_dt, const void* w_enc, li_dtype w_dt,
+                           const int64_t* dst_row, int32_t M, int32_t d_model, int32_t Dc, void* latent,
+                           int64_t n_tok, void* ws, size_t ws_bytes, void* stream);
+size_t li_latent_append_ws(int32_t M, int32_t d_model, int32_t Dc);
+
+/* ---------------------------------------------------------------------------
  * li_topk — the selection step on its own: per-row top-k of fp32 scores.
  *
  * Row r holds row_len[r] (or n, when row_len is NULL) scores at

@@ -26,7 +26,7 @@ LI_MAX_K = 16384
 # Every symbol include/li.h declares.
 SYMBOLS = ("li_index_decode", "li_index_decode_ws", "li_index_prefill", "li_index_prefill_ws",
            "li_latent_score_group", "li_latent_score_group_ws", "li_hs_refine", "li_hs_refine_ws",
-           "li_topk", "li_topk_ws", "li_status_str", "li_last_error", "li_trace_events", "li_trace_count")
+           "li_latent_append", "li_latent_append_ws", "li_topk", "li_topk_ws", "li_status_str", "li_last_error", "li_trace_events", "li_trace_count")
 
 _lib = None
 
@@ -55,12 +55,15 @@ def lib():
         L.li_hs_refine.argtypes = [vp, i32, vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, vp,
                                    vp, u32, vp, sz, vp]
         L.li_hs_refine_ws.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        L.li_latent_append.argtypes = [vp, i32, vp, i32, vp, i32, i32, i32, vp, i64, vp, sz, vp]
+        L.li_latent_append_ws.argtypes = [i32, i32, i32]
         L.li_topk.argtypes = [vp, i64, vp, i32, i32, i32, vp, vp, sz, vp]
         L.li_topk_ws.argtypes = [i32, i32, i32]
-        for f in ("li_index_decode", "li_index_prefill", "li_latent_score_group", "li_hs_refine", "li_topk"):
+        for f in ("li_index_decode", "li_index_prefill", "li_latent_score_group", "li_hs_refine", "li_latent_append",
+                  "li_topk"):
             getattr(L, f).restype = C.c_int32
         for f in ("li_index_decode_ws", "li_index_prefill_ws", "li_latent_score_group_ws", "li_hs_refine_ws",
-                  "li_topk_ws"):
+                  "li_latent_append_ws", "li_topk_ws"):
             getattr(L, f).restype = C.c_size_t
         L.li_status_str.argtypes = [i32]
         L.li_status_str.restype = C.c_char_p
@@ -182,6 +185,21 @@ def li_hs_refine(cand_idx, q, w, w_dec, latent, c_scale, kv_off, k, out_idx=None
                           _dt(latent), _ptr(c_scale), _ptr(kv_off), B, Gf, H, Dh, Dc, k, _ptr(out_idx),
                           _ptr(out_scores), flags, _ptr(wst), wsb, _stream(stream)))
     return out_idx
+
+
+def li_latent_append(h, w_enc, dst_row, latent, ws=None, stream=None):
+    """Latent-cache append: latent[dst_row[m]] = bf16(w_enc @ h[m]) in place.
+    h [M,d_model] bf16, w_enc [Dc,d_model] bf16, dst_row [M] int64,
+    latent [n_tok,Dc] bf16.  Returns latent."""
+    M, d_model = h.shape
+    Dc = w_enc.shape[0]
+    n_tok = latent.shape[0]
+    L = lib()
+    need = L.li_latent_append_ws(M, d_model, Dc)
+    wst, wsb = _workspace(need, latent.device, ws)
+    _check(L.li_latent_append(_ptr(h), _dt(h), _ptr(w_enc), _dt(w_enc), _ptr(dst_row), M, d_model, Dc, _ptr(latent),
+                              n_tok, _ptr(wst), wsb, _stream(stream)))
+    return latent
 
 
 def li_topk(scores, k, row_len=None, n=None, out_idx=None, ws=None, stream=None):

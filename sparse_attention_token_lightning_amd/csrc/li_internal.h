@@ -108,6 +108,13 @@ hipError_t launch_hs_score(const uint16_t* qt16, const float* wsc, const uint16_
                            int32_t C, int32_t B, int32_t Gf, int32_t H, int32_t Dc, bool split,
                            float* scores, hipStream_t stream);
 
+// Latent-cache append: latent[dst[m]] = bf16(sum_i h[m][i] * w_enc[c][i]).
+// K is split over append_splits(M, d_model) workgroups; with more than one
+// split, `part` ([S][M][Dc] fp32) holds the partial sums.
+int32_t append_splits(int32_t M, int32_t d_model);
+hipError_t launch_latent_append(const uint16_t* h, const uint16_t* w_enc, const int64_t* dst, int32_t M,
+                                int32_t d_model, int32_t Dc, float* part, uint16_t* latent, hipStream_t stream);
+
 // Opt-in input checks (LI_DEBUG_VALIDATE): validate_begin clears the device
 // record, the validate_* calls enqueue one check each, validate_end waits for
 // them and returns the first failed check (0 = none) and its element index.
@@ -127,6 +134,9 @@ enum ValidateCheck : uint32_t {
   kBadCandidateOrder,
   kBadScores,
   kBadRowLen,
+  kBadDstRow,
+  kBadHidden,
+  kBadWEnc,
 };
 hipError_t validate_begin(hipStream_t s);
 void validate_offsets(const int64_t* off, int32_t B, int64_t n_tok, int32_t max_len, hipStream_t s);
@@ -138,6 +148,7 @@ void validate_cands(const int32_t* cand, int32_t B, int32_t C, const int64_t* of
 void validate_score_rows(const float* p, int64_t stride, int32_t rows, int32_t n, const int32_t* len,
                          hipStream_t s);
 void validate_row_len(const int32_t* len, int32_t rows, int64_t stride, hipStream_t s);
+void validate_dst_rows(const int64_t* dst, int32_t M, int64_t n_tok, hipStream_t s);
 hipError_t validate_end(hipStream_t s, uint32_t* check, int64_t* index);
 const char* validate_name(uint32_t check);
 

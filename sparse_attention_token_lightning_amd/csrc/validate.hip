@@ -85,6 +85,11 @@ __global__ __launch_bounds__(kThreads) void row_len_kernel(const int32_t* len, i
     if (len[r] < 0 || len[r] > stride) report(kBadRowLen, r);
 }
 
+__global__ __launch_bounds__(kThreads) void dst_rows_kernel(const int64_t* dst, int32_t M, int64_t n_tok) {
+  for (int64_t m = gtid(); m < M; m += gstride())
+    if (dst[m] < 0 || dst[m] >= n_tok) report(kBadDstRow, m);
+}
+
 // Candidate rows: valid entries strictly ascending inside [0, L_b), then -1 only.
 __global__ __launch_bounds__(kThreads) void cands_kernel(const int32_t* cand, int32_t B, int32_t C,
                                                          const int64_t* off) {
@@ -141,6 +146,10 @@ void validate_row_len(const int32_t* len, int32_t rows, int64_t stride, hipStrea
   if (len && rows > 0) row_len_kernel<<<blocks_for(rows), kThreads, 0, s>>>(len, rows, stride);
 }
 
+void validate_dst_rows(const int64_t* dst, int32_t M, int64_t n_tok, hipStream_t s) {
+  if (M > 0) dst_rows_kernel<<<blocks_for(M), kThreads, 0, s>>>(dst, M, n_tok);
+}
+
 hipError_t validate_end(hipStream_t s, uint32_t* check, int64_t* index) {
   uint32_t r[4] = {0u, 0u, 0u, 0u};
   hipError_t e = hipGetLastError();
@@ -168,6 +177,9 @@ const char* validate_name(uint32_t check) {
     case kBadCandidateOrder: return "cand_idx row not ascending with -1 only at its end";
     case kBadScores: return "scores hold a NaN";
     case kBadRowLen: return "row_len entry outside [0, row_stride]";
+    case kBadDstRow: return "dst_row entry outside [0, n_tok)";
+    case kBadHidden: return "h holds a NaN/Inf code";
+    case kBadWEnc: return "w_enc holds a NaN/Inf code";
     default: return "unknown check";
   }
 }

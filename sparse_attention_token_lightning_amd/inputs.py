@@ -225,6 +225,59 @@ def make_hs(seed, lens, C=8192, Gf=3, H=64, D=128, Dc=256, k=2048, name="") -> H
 
 # ---- the five workloads (seed = 1000 + workload number) ------------------------
 
+@dataclass
+class Append:
+    """Latent-cache append: M new tokens' hidden states written into a ragged
+    latent cache, request b's j-th new token at row kv_off[b] + old_b + j."""
+    h: np.ndarray            # [M][d_model] bf16 bits
+    w_enc: np.ndarray        # [Dc][d_model] bf16 bits
+    dst_row: np.ndarray      # [M] int64
+    kv_off: np.ndarray       # [B+1] int64 over each request's old + new length
+    n_tok: int
+    d_model: int
+    Dc: int
+    name: str = ""
+
+    @property
+    def M(self):
+        return int(self.dst_row.size)
+
+
+def make_append(seed, old_lens, new_lens, d_model=7168, Dc=256, dist="normal", name="") -> Append:
+    """Append inputs.  dist "normal": h ~ N(0,1) -> bf16 and W_enc ~
+    N(0, 1/d_model) -> bf16 (latent entries of unit scale); "int": both
+    integers uniform on -3..3 (every sum exact in fp32).  The cache row of
+    each new token follows its request's old tokens.  The pages give no
+    hidden size or encoder distribution: d_model = 7168 is a stand-in."""
+    rng = np.random.default_rng(seed)
+    old = np.asarray(old_lens, dtype=np.int64)
+    new = np.asarray(new_lens, dtype=np.int64)
+    off = _offsets(old + new)
+    dst = np.concatenate([off[b] + old[b] + np.arange(new[b], dtype=np.int64) for b in range(old.size)] +
+                         [np.zeros(0, np.int64)])
+    M = int(dst.size)
+    if dist == "int":
+        h = rng.integers(-3, 4, size=(M, d_model)).astype(np.float32)
+        W = rng.integers(-3, 4, size=(Dc, d_model)).astype(np.float32)
+    else:
+        h = rng.standard_normal((M, d_model), dtype=np.float32)
+        W = (rng.standard_normal((Dc, d_model), dtype=np.float32) * np.float32(1.0 / np.sqrt(d_model))).astype(
+            np.float32)
+    return Append(h=encode_bf16(h), w_enc=encode_bf16(W), dst_row=dst, kv_off=off, n_tok=int(off[-1]),
+                  d_model=d_model, Dc=Dc, name=name)
+
+
+def append_decode() -> Append:
+    """One decode step's append for the LatentIndex group: B = 16 requests at
+    L = 131072, one new token each, Dc = 256."""
+    return make_append(1006, [131072] * 16, [1] * 16, name="append_decode_B16_L131072_d7168_Dc256")
+
+
+def append_prefill() -> Append:
+    """A prefill chunk's append: 4096 new tokens ending a 65536-token cache, Dc = 256."""
+    return make_append(1007, [65536 - 4096], [4096], name="append_prefill_T4096_L65536_d7168_Dc256")
+
+
 def cfg1() -> Decode:
     """Single decode query, L = 4096, integer-valued bf16 q and K, integer w."""
     return make_decode(1001, [4096], k_dt="bf16", dist="int", name="decode_int_L4096")

@@ -1,0 +1,139 @@
+"""GPU parity of li_latent_append (the LatentIndex shared-latent append)
+against the CPU oracle.
+
+Integer-valued inputs make every fp32 partial sum exact, so there the stored
+bf16 codes must equal the oracle's bit for bit.  With normal inputs the
+kernel's fp32 sum y may differ from the exact sum e by up to the summation
+bound b = (d_model + 64) * 2^-24 * sum_i |h_i w_i|; rounding is monotone, so a
+stored code that differs from the oracle's must lie between the roundings of
+e - b and e + b (near cancellation that can be several bf16 steps of a tiny
+result), and such codes must stay rare."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_token_lightning_amd as li
+from sparse_attention_token_lightning_amd import inputs
+from _parity import dev
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = -7.0  # initial value of every latent row; rows not appended to must keep it
+
+def bf16_values(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes).view(np.int16)).view(torch.bfloat16).double().numpy()
+
+def run_append(x, ws=None):
+    lat = torch.full((x.n_tok, x.Dc), SENTINEL, dtype=torch.bfloat16, device="cuda")
+    li.li_latent_append(dev(x.h, "bf16"), dev(x.w_enc, "bf16"), dev(x.dst_row), lat, ws=ws)
+    torch.cuda.synchronize()
+    return lat
+
+def rows_of(lat, rows):
+    r = torch.from_numpy(np.asarray(rows, np.int64)).cuda()
+    return lat.index_select(0, r).view(torch.int16).cpu().numpy().view(np.uint16)
+
+def untouched_keep_sentinel(lat, dst, what):
+    changed = (lat != SENTINEL).any(dim=1).nonzero().flatten().cpu().numpy()
+    assert np.isin(changed, dst).all(), f"{what}: rows outside dst_row were written: {changed[~np.isin(changed, dst)][:8]}"
+
+def check_codes(got, ref, exact, h_rows, w_enc, d_model, what, exact_only=False):
+    """got/ref [m][Dc] bf16 codes, exact [m][Dc] fp64 sums of the same rows."""
+    diff = got != ref
+    nd = int(diff.sum())
+    print(f"[append parity] {what}: {nd} of {got.size} codes differ from the oracle", flush=True)
+    if exact_only:
+        assert nd == 0, f"{what}: integer-valued sums must round identically"
+        return
+    if nd == 0:
+        return
+    hv = np.abs(bf16_values(h_rows))
+    wv = np.abs(bf16_values(w_enc))
+    bound = ((d_model + 64) * 2.0 ** -24 * (hv @ wv.T))[diff]
+    e = exact[diff]
+    lo = bf16_values(np.array([oracle.encode_bf16(v) for v in e - bound], np.uint16))
+    hi = bf16_values(np.array([oracle.encode_bf16(v) for v in e + bound], np.uint16))
+    gv = bf16_values(got[diff])
+    assert np.all((lo <= gv) & (gv <= hi)), f"{what}: a differing code is not explained by fp32 summation"
+    assert nd <= max(4, got.size // 200), f"{what}: too many boundary cases ({nd})"
+
+def append_parity(x, what, rows=None, exact_only=False):
+    """Compare the rows `rows` (indices into the M new tokens; all by default)."""
+    print(f"[append parity] {what} M={x.M} d_model={x.d_model} Dc={x.Dc} n_tok={x.n_tok}", flush=True)
+    lat = run_append(x)
+    untouched_keep_sentinel(lat, x.dst_row, what)
+    m = np.arange(x.M) if rows is None else np.asarray(rows)
+    got = rows_of(lat, x.dst_row[m])
+    sub_dst = np.arange(m.size, dtype=np.int64)
+    ref, exact = oracle.latent_append(x.h[m], "bf16", x.w_enc, "bf16", sub_dst, np.zeros((m.size, x.Dc), np.uint16))
+    check_codes(got, ref, exact, x.h[m], x.w_enc, x.d_model, what, exact_only)
+    return lat
+
+def test_append_integer_exact_ragged_requests():
+    x = inputs.make_append(401, [5, 0, 300, 17], [130, 1, 200, 3], d_model=1024, dist="int")
+    append_parity(x, "int ragged d1024", exact_only=True)
+
+def test_append_integer_exact_full_hidden_size():
+    x = inputs.make_append(402, [1000], [200], d_model=7168, dist="int")
+    append_parity(x, "int d7168", exact_only=True)
+
+def test_append_normal_ragged_dc256_and_dc128():
+    append_parity(inputs.make_append(403, [10, 4000, 0], [150, 7, 143], d_model=2048), "normal Dc256 d2048")
+    append_parity(inputs.make_append(404, [64, 3], [129, 255], d_model=1536, Dc=128), "normal Dc128 d1536")
+
+def test_append_one_split_writes_the_cache_directly():
+    # d_model = 64 and 128 give one K split: no partial sums, no workspace
+    for d, seed in ((64, 405), (128, 406)):
+        assert li.lib().li_latent_append_ws(300, d, 256) == 0
+        append_parity(inputs.make_append(seed, [2, 9], [131, 126], d_model=d, dist="int"), f"int d{d}",
+                      exact_only=True)
+        append_parity(inputs.make_append(seed + 10, [2, 9], [131, 126], d_model=d, Dc=128), f"normal d{d} Dc128")
+
+def test_append_single_token_and_empty_batch():
+    append_parity(inputs.make_append(407, [77], [1], d_model=7168), "M=1 d7168")
+    x = inputs.make_append(408, [5, 6], [0, 0], d_model=256)
+    assert x.M == 0
+    lat = run_append(x)
+    assert bool((lat == SENTINEL).all())
+
+def test_append_prefill_chunk_full_size_sampled_rows():
+    x = inputs.append_prefill()
+    rng = np.random.default_rng(409)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(x.M - 8, x.M), np.arange(120, 136),
+                                     rng.choice(x.M, 40, replace=False)]))
+    lat = append_parity(x, x.name, rows=rows)
+    # every appended row is finite
+    new = lat[torch.from_numpy(x.dst_row).cuda()].float()
+    assert bool(torch.isfinite(new).all())
+
+def test_append_decode_step_full_size():
+    x = inputs.append_decode()
+    append_parity(x, x.name)
+
+def test_append_ignores_workspace_contents_and_repeats():
+    x = inputs.make_append(410, [40, 7], [300, 90], d_model=3072)
+    need = li.lib().li_latent_append_ws(x.M, x.d_model, x.Dc)
+    assert need > 0
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda").view(torch.uint8)
+    first = run_append(x, ws=ws)
+    again = run_append(x, ws=ws)
+    assert torch.equal(first.view(torch.int16), again.view(torch.int16))
+    small = inputs.make_append(411, [3], [50], d_model=3072)
+    append_parity(small, "after a larger call")
+    ws.fill_(255)
+    third = run_append(x, ws=ws)
+    assert torch.equal(first.view(torch.int16), third.view(torch.int16))
+
+def test_append_debug_validation_rejects_rows_outside_the_cache(monkeypatch):
+    x = inputs.make_append(412, [10], [20], d_model=256)
+    x.dst_row = x.dst_row.copy()
+    x.dst_row[7] = x.n_tok  # one past the cache
+    monkeypatch.setenv("LI_DEBUG_VALIDATE", "1")
+    lat = torch.full((x.n_tok, x.Dc), SENTINEL, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(li.LiError) as e:
+        li.li_latent_append(dev(x.h, "bf16"), dev(x.w_enc, "bf16"), dev(x.dst_row), lat)
+    assert e.value.status == li.LI_E_VALUE and "dst_row" in str(e.value)
+    torch.cuda.synchronize()
+    assert bool((lat == SENTINEL).all())

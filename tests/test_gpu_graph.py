@@ -85,3 +85,14 @@ def test_hs_graph():
         li.li_hs_refine(cand, fq, fw, fwd, lat, None, off, f.k, out_idx=fout, ws=ws_f)
 
     check_replays(run, [cand, fout], "hs")
+
+
+def test_append_graph():
+    # no old tokens: every cache row is appended to, so each replay rewrites the whole output
+    x = inputs.make_append(905, [0, 0, 0], [300, 5, 77], d_model=2048)
+    assert x.n_tok == x.M
+    h, wenc, dst = dev(x.h, "bf16"), dev(x.w_enc, "bf16"), dev(x.dst_row)
+    lat = torch.zeros((x.n_tok, x.Dc), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(li.lib().li_latent_append_ws(x.M, x.d_model, x.Dc), dtype=torch.uint8, device="cuda")
+    assert ws.numel() > 0  # the split path (partial sums + reduction) is the one captured
+    check_replays(lambda: li.li_latent_append(h, wenc, dst, lat, ws=ws), [lat], "append")
