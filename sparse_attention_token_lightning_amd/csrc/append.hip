@@ -27,6 +27,10 @@ constexpr int kApK = 64;      // K elements per pipeline step (two MFMA K blocks
 constexpr int kApWaves = 8;
 constexpr int kApThreads = 64 * kApWaves;
 constexpr int kApSlotsA = kApRows / 16 * 2 * 64;  // 16-byte fragment slots of the h tile
+#ifndef LI_APPEND_DEPTH
+#define LI_APPEND_DEPTH 2
+#endif
+constexpr int kApDepth = LI_APPEND_DEPTH;  // K steps loaded ahead of their use
 
 __device__ __forceinline__ uint16_t bf16_rne(float v) {
   const uint32_t u = __builtin_bit_cast(uint32_t, v);
@@ -35,21 +39,23 @@ __device__ __forceinline__ uint16_t bf16_rne(float v) {
 
 // LDS holds each K step's tiles in MFMA fragment order: slot
 // ((t * 2 + ks) * 64 + lane) is the 16 bytes that `lane` feeds to the MFMA of
-// 16-row tile t and 32-wide K block ks (row t*16 + (lane & 15), K elements
-// ks*32 + 8*(lane >> 4) .. +7), so fragment reads are consecutive per wave.
-// The producer of a slot is the thread with that slot's index, so the LDS
-// writes are consecutive too; its global read covers 64 contiguous bytes of a
-// row per four lanes.
-template <int DC>
+// 16-row tile t and K block ks: row t*16 + (lane & 15), K elements
+// 16*(lane >> 4) + 8*ks .. +7 of the step's 64.  The MFMA sums over its 32 K
+// positions, so any assignment of the step's K elements to (ks, lane group)
+// is the same product as long as both operands use it; this one gives each
+// producer thread 32 contiguous bytes (its two ks slots), so four lanes read
+// a whole 128-byte line of a row.  Fragment reads and LDS writes are
+// consecutive per wave.
+template <int DC, int D>
 __global__ __launch_bounds__(kApThreads, 1) void append_gemm_kernel(
-    const uint16_t* __restrict__ h, const uint16_t* __restrict__ w_enc, const int64_t* __restrict__ dst,
+    const uint16_t* h, const uint16_t* w_enc, const int64_t* __restrict__ dst,
     int32_t M, int32_t d_model, int32_t steps_per_split, float* __restrict__ part,
     uint16_t* __restrict__ latent) {
   constexpr int kSlotsB = DC / 16 * 2 * 64;
-  constexpr int kPerA = kApSlotsA / kApThreads;
-  constexpr int kPerB = kSlotsB / kApThreads;
+  constexpr int kPerA = kApSlotsA / 2 / kApThreads;  // 32-byte slot pairs per thread
+  constexpr int kPerB = kSlotsB / 2 / kApThreads;
   constexpr int kWct = DC / 16 / 4;  // 16-column tiles per wave
-  static_assert(kPerA * kApThreads == kApSlotsA && kPerB * kApThreads == kSlotsB, "tile split");
+  static_assert(2 * kPerA * kApThreads == kApSlotsA && 2 * kPerB * kApThreads == kSlotsB, "tile split");
   __shared__ i32x4 tile[2][kApSlotsA + kSlotsB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -59,39 +65,52 @@ __global__ __launch_bounds__(kApThreads, 1) void append_gemm_kernel(
   const int st0 = blockIdx.y * steps_per_split;
   const int st1 = min(st0 + steps_per_split, nsteps);
 
-  // Element offsets of this thread's slots (at K step 0).
+  // Pair p = tid + j*kApThreads covers tile p >> 6, lane p & 63: slots
+  // ((p >> 6) * 2 + ks) * 64 + (p & 63) for ks = 0, 1.  Element offsets at K
+  // step 0; a pair of a row past M reads row M-1 instead: that row's products
+  // only reach output rows that are never stored, and the loads stay
+  // unconditional.
   int64_t aoff[kPerA];
-  bool aok[kPerA];
   int64_t boff[kPerB];
 #pragma unroll
   for (int j = 0; j < kPerA; ++j) {
-    const int q = tid + j * kApThreads;
-    const int64_t row = row0 + (q >> 7) * 16 + (q & 15);
-    const int c = ((q >> 6) & 1) * 4 + ((q >> 4) & 3);
-    aok[j] = row < M;
-    aoff[j] = (aok[j] ? row : 0) * d_model + c * 8;
+    const int p = tid + j * kApThreads;
+    const int64_t row = min(row0 + (p >> 6) * 16 + (p & 15), (int64_t)M - 1);
+    aoff[j] = row * d_model + 16 * ((p >> 4) & 3);
   }
 #pragma unroll
   for (int j = 0; j < kPerB; ++j) {
-    const int q = tid + j * kApThreads;
-    const int col = (q >> 7) * 16 + (q & 15);
-    const int c = ((q >> 6) & 1) * 4 + ((q >> 4) & 3);
-    boff[j] = (int64_t)col * d_model + c * 8;
+    const int p = tid + j * kApThreads;
+    const int col = (p >> 6) * 16 + (p & 15);
+    boff[j] = (int64_t)col * d_model + 16 * ((p >> 4) & 3);
   }
+  auto slot = [&](int j, int ks) { return (((tid + j * kApThreads) >> 6) * 2 + ks) * 64 + (tid & 63); };
 
-  i32x4 ra[kPerA], rb[kPerB];
-  auto gload = [&](int st) {
+  // D register stages: stage u holds the step st0 + u (mod D) loaded D steps
+  // ahead of its use, so D steps of MFMA work cover each load's latency.
+  i32x4 ra[D][kPerA][2], rb[D][kPerB][2];
+  auto gload = [&](int u, int st) {
     const int64_t k0 = (int64_t)st * kApK;
 #pragma unroll
-    for (int j = 0; j < kPerA; ++j) ra[j] = aok[j] ? ld16(h + aoff[j] + k0) : i32x4{0, 0, 0, 0};
+    for (int j = 0; j < kPerA; ++j) {
+      ra[u][j][0] = ld16(h + aoff[j] + k0);
+      ra[u][j][1] = ld16(h + aoff[j] + k0 + 8);
+    }
 #pragma unroll
-    for (int j = 0; j < kPerB; ++j) rb[j] = ld16(w_enc + boff[j] + k0);
+    for (int j = 0; j < kPerB; ++j) {
+      rb[u][j][0] = ld16(w_enc + boff[j] + k0);
+      rb[u][j][1] = ld16(w_enc + boff[j] + k0 + 8);
+    }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf, int u) {
 #pragma unroll
-    for (int j = 0; j < kPerA; ++j) tile[buf][tid + j * kApThreads] = ra[j];
+    for (int j = 0; j < kPerA; ++j)
 #pragma unroll
-    for (int j = 0; j < kPerB; ++j) tile[buf][kApSlotsA + tid + j * kApThreads] = rb[j];
+      for (int ks = 0; ks < 2; ++ks) tile[buf][slot(j, ks)] = ra[u][j][ks];
+#pragma unroll
+    for (int j = 0; j < kPerB; ++j)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) tile[buf][kApSlotsA + slot(j, ks)] = rb[u][j][ks];
   };
 
   f32x4 acc[4][kWct];
@@ -100,13 +119,7 @@ __global__ __launch_bounds__(kApThreads, 1) void append_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < kWct; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  gload(st0);
-  lstore(0);
-  __syncthreads();
-  for (int st = st0; st < st1; ++st) {
-    const int buf = (st - st0) & 1;
-    const bool more = st + 1 < st1;
-    if (more) gload(st + 1);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8 a[4], b[kWct];
@@ -119,13 +132,42 @@ __global__ __launch_bounds__(kApThreads, 1) void append_gemm_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < kWct; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < kWct; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
+  };
+
+  // Loads and LDS stores are unconditional, so the compiler's wait counts
+  // track exactly the D steps in flight: a load past the split's last step
+  // re-reads that step (in bounds), and the last step's store fills the buffer
+  // no wave reads again.
+#pragma unroll
+  for (int u = 0; u < D; ++u) gload(u, min(st0 + u, st1 - 1));
+  lstore(0, 0);
+  __syncthreads();
+  auto step = [&](int u, int st) {
+    const int buf = (st - st0) & 1;
+    // stage u's step is in LDS already (stored before the last barrier)
+    gload(u, min(st + D, st1 - 1));
+    // keep the loads first: the scheduler would otherwise sink them below the
+    // step's MFMAs, shortening the distance they run ahead by a step
+    __builtin_amdgcn_sched_barrier(0);
+    compute(buf);
     // The other buffer was last read in the previous step, which every wave
     // finished before the barrier that ended it.
-    if (more) lstore(buf ^ 1);
+    lstore(buf ^ 1, (u + 1) % D);
     __syncthreads();
+  };
+  // Whole groups of D steps in the loop, the rest after it: no path through
+  // the loop skips a store, so no wait drains the loads in flight.
+  int base = st0;
+  for (; base + D <= st1; base += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) step(u, base + u);
   }
+#pragma unroll
+  for (int u = 0; u + 1 < D; ++u)
+    if (base + u < st1) step(u, base + u);
 
   // acc[i][j][e]: row 64*wr + 16*i + 4*(lane >> 4) + e, column 16*(kWct*wc + j) + (lane & 15).
 #pragma unroll
@@ -147,29 +189,55 @@ __global__ __launch_bounds__(kApThreads, 1) void append_gemm_kernel(
   }
 }
 
-// Sum of the S partial tiles in split order, rounded to bf16, at dst_row.
-// One thread per four consecutive columns of a row.
+// Sum of the S partial tiles, rounded to bf16 and stored at dst_row.  A
+// workgroup covers R rows; thread (r, g, quad) adds splits g, g + G, g + 2G,
+// ... in increasing order for four consecutive columns of its row, and thread
+// (r, 0, quad) then adds the G group sums in order g = 0 .. G-1.  The order
+// depends only on S and G, never on scheduling.
 template <int DC>
-__global__ __launch_bounds__(256) void append_reduce_kernel(const float* __restrict__ part, int32_t S, int32_t M,
-                                                            const int64_t* __restrict__ dst,
-                                                            uint16_t* __restrict__ latent) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = t / (DC / 4);
-  const int c = (int)(t % (DC / 4)) * 4;
-  if (row >= M) return;
+__global__ __launch_bounds__(1024) void append_reduce_kernel(const float* __restrict__ part, int32_t S, int32_t G,
+                                                             int32_t M, const int64_t* __restrict__ dst,
+                                                             uint16_t* __restrict__ latent) {
+  constexpr int QD = DC / 4;
+  __shared__ f32x4 red[1024];
+  const int tid = threadIdx.x;
+  const int q = tid % QD, g = (tid / QD) % G;
+  const int64_t row = (int64_t)blockIdx.x * (blockDim.x / (QD * G)) + tid / (QD * G);
+  const bool live = row < M;
   const int64_t plane = (int64_t)M * DC;
-  const float* p = part + row * DC + c;
-  f32x4 v = *reinterpret_cast<const f32x4*>(p);
-  for (int s = 1; s < S; ++s) {
-    const f32x4 u = *reinterpret_cast<const f32x4*>(p + s * plane);
-    v[0] += u[0];
-    v[1] += u[1];
-    v[2] += u[2];
-    v[3] += u[3];
+  const float* p = part + (live ? row : 0) * DC + 4 * q;
+  f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+  int s = g;
+  if (live) {
+    for (; s + 7 * G < S; s += 8 * G) {  // eight independent loads in flight
+      f32x4 u[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) u[j] = *reinterpret_cast<const f32x4*>(p + (s + j * G) * plane);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += u[j][e];
+    }
+    for (; s < S; s += G) {
+      const f32x4 u = *reinterpret_cast<const f32x4*>(p + s * plane);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += u[e];
+    }
   }
+  if (G > 1) {
+    red[tid] = v;
+    __syncthreads();
+    if (g != 0) return;
+    for (int j = 1; j < G; ++j) {
+      const f32x4 u = red[tid + j * QD];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += u[e];
+    }
+  }
+  if (!live) return;
   const uint32_t lo = (uint32_t)bf16_rne(v[0]) | ((uint32_t)bf16_rne(v[1]) << 16);
   const uint32_t hi = (uint32_t)bf16_rne(v[2]) | ((uint32_t)bf16_rne(v[3]) << 16);
-  *reinterpret_cast<i32x2*>(latent + dst[row] * DC + c) = i32x2{(int)lo, (int)hi};
+  *reinterpret_cast<i32x2*>(latent + dst[row] * DC + 4 * q) = i32x2{(int)lo, (int)hi};
 }
 
 }  // namespace
@@ -177,17 +245,17 @@ __global__ __launch_bounds__(256) void append_reduce_kernel(const float* __restr
 int32_t append_splits(int32_t M, int32_t d_model) {
   const int32_t nsteps = d_model / kApK;
   const int32_t row_blocks = (M + kApRows - 1) / kApRows;
-  // Enough workgroups to cover the 256 compute units, each split keeping at
-  // least two K steps; one split writes the cache directly.
+  // Enough workgroups to cover the 256 compute units (one K step per split at
+  // the least); one split writes the cache directly.
   int32_t s = (256 + row_blocks - 1) / row_blocks;
-  const int32_t cap = nsteps / 2 > 1 ? nsteps / 2 : 1;
-  if (s > cap) s = cap;
+  if (s > nsteps) s = nsteps;
   const int32_t per = (nsteps + s - 1) / s;
   return (nsteps + per - 1) / per;  // no empty split
 }
 
 hipError_t launch_latent_append(const uint16_t* h, const uint16_t* w_enc, const int64_t* dst, int32_t M,
                                 int32_t d_model, int32_t Dc, float* part, uint16_t* latent, hipStream_t stream) {
+  constexpr int D = kApDepth;
   const int32_t S = append_splits(M, d_model);
   const int32_t nsteps = d_model / kApK;
   const int32_t per = (nsteps + S - 1) / S;
@@ -195,18 +263,23 @@ hipError_t launch_latent_append(const uint16_t* h, const uint16_t* w_enc, const 
   float* p = S > 1 ? part : nullptr;
   hipError_t e;
   if (Dc == 256)
-    e = launch_kernel(append_gemm_kernel<256>, grid, dim3(kApThreads), 0, stream, h, w_enc, dst, M, d_model, per, p,
-                      latent);
+    e = launch_kernel(append_gemm_kernel<256, D>, grid, dim3(kApThreads), 0, stream, h, w_enc, dst, M, d_model, per,
+                      p, latent);
   else
-    e = launch_kernel(append_gemm_kernel<128>, grid, dim3(kApThreads), 0, stream, h, w_enc, dst, M, d_model, per, p,
-                      latent);
+    e = launch_kernel(append_gemm_kernel<128, D>, grid, dim3(kApThreads), 0, stream, h, w_enc, dst, M, d_model, per,
+                      p, latent);
   if (e != hipSuccess || S == 1) return e;
-  const unsigned blocks = (unsigned)(((int64_t)M * (Dc / 4) + 255) / 256);
+  // G split groups per row, each summing at most eight splits (G <= 16); a
+  // workgroup holds 256 threads or one row's Dc/4 * G, whichever is larger.
+  int32_t G = 1;
+  while (G < 16 && G * 8 < S) G *= 2;
+  const int32_t per_row = Dc / 4 * G;
+  const int32_t rows = per_row >= 256 ? 1 : 256 / per_row;
+  const dim3 grid_r((unsigned)((M + rows - 1) / rows)), block_r((unsigned)(rows * per_row));
   if (Dc == 256)
-    return launch_kernel(append_reduce_kernel<256>, dim3(blocks), dim3(256), 0, stream, (const float*)part, S, M, dst,
+    return launch_kernel(append_reduce_kernel<256>, grid_r, block_r, 0, stream, (const float*)part, S, G, M, dst,
                          latent);
-  return launch_kernel(append_reduce_kernel<128>, dim3(blocks), dim3(256), 0, stream, (const float*)part, S, M, dst,
-                       latent);
+  return launch_kernel(append_reduce_kernel<128>, grid_r, block_r, 0, stream, (const float*)part, S, G, M, dst, latent);
 }
 
 }  // namespace li

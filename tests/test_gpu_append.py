@@ -84,9 +84,10 @@ def test_append_normal_ragged_dc256_and_dc128():
     append_parity(inputs.make_append(404, [64, 3], [129, 255], d_model=1536, Dc=128), "normal Dc128 d1536")
 
 def test_append_one_split_writes_the_cache_directly():
-    # d_model = 64 and 128 give one K split: no partial sums, no workspace
+    # d_model = 64 is one K step, hence one split: no partial sums, no workspace;
+    # d_model = 128 splits its two K steps
     for d, seed in ((64, 405), (128, 406)):
-        assert li.lib().li_latent_append_ws(300, d, 256) == 0
+        assert (li.lib().li_latent_append_ws(300, d, 256) == 0) == (d == 64)
         append_parity(inputs.make_append(seed, [2, 9], [131, 126], d_model=d, dist="int"), f"int d{d}",
                       exact_only=True)
         append_parity(inputs.make_append(seed + 10, [2, 9], [131, 126], d_model=d, Dc=128), f"normal d{d} Dc128")
