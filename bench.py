@@ -314,7 +314,89 @@ def components(torch, li, inputs, args):
             "gbs": nbytes / t / 1e9, "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBS,
             "tflops": flop / t / 1e12, "mfma_frac_bf16": flop / t / 1e12 / BF16_PEAK_TFLOPS}
         del srcs, dst, lat, ws
+    out.update(stack_component(torch, li, args))
     return out
+
+
+def stack_component(torch, li, args, n_layers=61, B=16, L=131072, G=4, C=8192):
+    """Decode-indexer time per step over a 61-layer stack (DeepSeek-V3.2's indexer
+    count), every layer with its own cache: native DSA (every layer scans),
+    IndexCache at 1/2 and 1/4 retention (li_indexcache_plan: F layers scan into
+    the index buffer, S layers reuse it), and LatentIndex + HS (groups of G: an
+    fp8 anchor proposing C candidates, G - 1 latent followers refining them).
+    Inputs are drawn on the GPU from a seeded generator in the distributions of
+    the decode and latent workloads (about 33 GB: too large for host drawing)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4242)
+    H, D, Dc, k = 64, 128, 256, 2048
+    n_tok = B * L
+    off = torch.arange(0, (B + 1) * L, L, dtype=torch.int64, device="cuda")
+    layers = []
+    for _ in range(n_layers):
+        q = torch.randn((B, H, D), generator=g, device="cuda").to(torch.bfloat16)
+        w = torch.randn((B, H), generator=g, device="cuda") / 8
+        kc = torch.randn((n_tok, D), generator=g, device="cuda").clamp_(-448, 448).to(torch.float8_e4m3fn)
+        ks = torch.rand((n_tok,), generator=g, device="cuda") * 1.5 + 0.5
+        layers.append((q, w, kc, ks))
+    n_groups = n_layers // G
+    groups = []
+    for _ in range(n_groups):
+        fq = torch.randn((B, G - 1, H, D), generator=g, device="cuda").to(torch.bfloat16)
+        fw = torch.randn((B, G - 1, H), generator=g, device="cuda") / 8
+        wd = (torch.randn((G - 1, Dc, H * D), generator=g, device="cuda") / Dc ** 0.5).to(torch.bfloat16)
+        lat = torch.randn((n_tok, Dc), generator=g, device="cuda").to(torch.bfloat16)
+        groups.append((fq, fw, wd, lat))
+    L_ = li.lib()
+    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    cand = torch.empty((B, C), dtype=torch.int32, device="cuda")
+    fidx = torch.empty((B, G - 1, k), dtype=torch.int32, device="cuda")
+    ws_d = torch.empty(L_.li_index_decode_ws(B, n_tok, L, C, 0), dtype=torch.uint8, device="cuda")
+    ws_f = torch.empty(L_.li_hs_refine_ws(B, C, G - 1, H, Dc, k, 0), dtype=torch.uint8, device="cuda")
+
+    def indexcache(retain_every):
+        n_f, src = li.li_indexcache_plan(n_layers, retain_every)
+        full = [l for l in range(n_layers) if src[l] == l]
+        assert len(full) == n_f
+
+        def step():
+            for l in full:  # S layers attend idx as the last F layer left it
+                q, w, kc, ks = layers[l]
+                li.li_index_decode(q, w, kc, ks, off, L, k, out_idx=idx, ws=ws_d)
+        return step, n_f
+
+    def hs_step():
+        for gi in range(n_groups):
+            q, w, kc, ks = layers[gi * G]
+            fq, fw, wd, lat = groups[gi]
+            li.li_index_decode(q, w, kc, ks, off, L, C, out_idx=cand, ws=ws_d)
+            li.li_hs_refine(cand, fq, fw, wd, lat, None, off, k, out_idx=fidx, ws=ws_f)
+        for l in range(n_groups * G, n_layers):  # layers past the last whole group scan natively
+            q, w, kc, ks = layers[l]
+            li.li_index_decode(q, w, kc, ks, off, L, k, out_idx=idx, ws=ws_d)
+
+    def wall(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / reps * 1e3
+
+    res = {}
+    for name, r in (("dsa", 1), ("indexcache_half", 2), ("indexcache_quarter", 4)):
+        fn, n_f = indexcache(r)
+        res[name + "_ms"] = wall(fn)
+        res[name + "_scans"] = n_f
+    res["latentindex_hs_ms"] = wall(hs_step)
+    res["latentindex_hs_anchor_scans"] = n_groups + (n_layers - n_groups * G)
+    for name in ("indexcache_half", "indexcache_quarter", "latentindex_hs"):
+        res[name + "_speedup"] = res["dsa_ms"] / res[name + "_ms"]
+    res["note"] = (f"decode-indexer ms per step (B = {B} tokens) summed over {n_layers} indexer layers, each with its "
+                   f"own fp8 key cache at L = {L}; HS groups of {G} share a bf16 latent (Dc = {Dc}), C = {C}")
+    del layers, groups, idx, cand, fidx, ws_d, ws_f
+    torch.cuda.empty_cache()
+    return {f"stack{n_layers}_B{B}_L{L}": res}
 
 
 def main():

@@ -228,6 +228,25 @@ li_status li_latent_append(const void* h, li_dtype h_dt, const void* w_enc, li_d
 size_t li_latent_append_ws(int32_t M, int32_t d_model, int32_t Dc);
 
 /* ---------------------------------------------------------------------------
+ * li_indexcache_plan — IndexCache layer roles (host only; no device work).
+ *
+ * ("IndexCache: Cross-Layer Index Reuse for Sparse Attention", Deep Dive and
+ * its role table.)  A Full (F) layer runs its indexer and overwrites the index
+ * buffer; a Shared (S) layer skips its indexer and attends the buffer left by
+ * the nearest preceding F layer.  The first layer is always F.
+ *
+ *   roles    [n_layers] uint8, host: 1 = F, 0 = S; or NULL for the uniform
+ *            pattern in which layer l is F when l % retain_every == 0 (retention
+ *            1/retain_every, e.g. 4 gives F S S S F S S S ...)
+ *   src      [n_layers] int32, host, written: the layer whose indexer produced
+ *            the selection layer l attends (l itself for an F layer)
+ *   returns  the number of F layers (indexer scans per token), or a negative
+ *            li_status: -LI_E_NULL (src NULL), -LI_E_SHAPE (n_layers < 1,
+ *            retain_every < 1 with roles NULL, or roles[0] not F)
+ * ------------------------------------------------------------------------- */
+int32_t li_indexcache_plan(const uint8_t* roles, int32_t n_layers, int32_t retain_every, int32_t* src);
+
+/* ---------------------------------------------------------------------------
  * li_topk — the selection step on its own: per-row top-k of fp32 scores.
  *
  * Row r holds row_len[r] (or n, when row_len is NULL) scores at

@@ -26,7 +26,7 @@ LI_MAX_K = 16384
 # Every symbol include/li.h declares.
 SYMBOLS = ("li_index_decode", "li_index_decode_ws", "li_index_prefill", "li_index_prefill_ws",
            "li_latent_score_group", "li_latent_score_group_ws", "li_hs_refine", "li_hs_refine_ws",
-           "li_latent_append", "li_latent_append_ws", "li_topk", "li_topk_ws", "li_status_str", "li_last_error", "li_trace_events", "li_trace_count")
+           "li_latent_append", "li_latent_append_ws", "li_indexcache_plan", "li_topk", "li_topk_ws", "li_status_str", "li_last_error", "li_trace_events", "li_trace_count")
 
 _lib = None
 
@@ -57,6 +57,8 @@ def lib():
         L.li_hs_refine_ws.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.li_latent_append.argtypes = [vp, i32, vp, i32, vp, i32, i32, i32, vp, i64, vp, sz, vp]
         L.li_latent_append_ws.argtypes = [i32, i32, i32]
+        L.li_indexcache_plan.restype = i32
+        L.li_indexcache_plan.argtypes = [vp, i32, i32, vp]
         L.li_topk.argtypes = [vp, i64, vp, i32, i32, i32, vp, vp, sz, vp]
         L.li_topk_ws.argtypes = [i32, i32, i32]
         for f in ("li_index_decode", "li_index_prefill", "li_latent_score_group", "li_hs_refine", "li_latent_append",
@@ -200,6 +202,19 @@ def li_latent_append(h, w_enc, dst_row, latent, ws=None, stream=None):
     _check(L.li_latent_append(_ptr(h), _dt(h), _ptr(w_enc), _dt(w_enc), _ptr(dst_row), M, d_model, Dc, _ptr(latent),
                               n_tok, _ptr(wst), wsb, _stream(stream)))
     return latent
+
+
+def li_indexcache_plan(n_layers, retain_every=1, roles=None):
+    """IndexCache schedule (host only): returns (number of F layers, src) where
+    src[l] is the layer whose selection layer l attends.  roles: optional
+    sequence of 1 (F) / 0 (S); otherwise every retain_every-th layer is F."""
+    import ctypes
+    src = (ctypes.c_int32 * n_layers)()
+    r = None if roles is None else (ctypes.c_uint8 * n_layers)(*[1 if x else 0 for x in roles])
+    n = lib().li_indexcache_plan(r, n_layers, retain_every, src)
+    if n < 0:
+        _check(-n)
+    return n, list(src)
 
 
 def li_topk(scores, k, row_len=None, n=None, out_idx=None, ws=None, stream=None):

@@ -490,6 +490,24 @@ li_status li_latent_append(const void* h, li_dtype h_dt, const void* w_enc, li_d
                    "latent_append launch", s);
 }
 
+int32_t li_indexcache_plan(const uint8_t* roles, int32_t n_layers, int32_t retain_every, int32_t* src) {
+  g_err.clear();
+  if (!src) return -fail(LI_E_NULL, "src is required");
+  if (n_layers < 1) return -fail(LI_E_SHAPE, "n_layers must be >= 1 (got %d)", n_layers);
+  if (!roles && retain_every < 1) return -fail(LI_E_SHAPE, "retain_every must be >= 1 (got %d)", retain_every);
+  if (roles && roles[0] != 1) return -fail(LI_E_SHAPE, "the first layer must be F (roles[0] = 1)");
+  int32_t full = 0, last = 0;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const bool f = roles ? roles[l] != 0 : l % retain_every == 0;
+    if (f) {
+      last = l;
+      ++full;
+    }
+    src[l] = last;
+  }
+  return full;
+}
+
 size_t li_topk_ws(int32_t rows, int32_t n, int32_t k) {
   (void)rows;
   (void)n;

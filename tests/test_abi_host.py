@@ -193,3 +193,26 @@ def test_latent_append_validation_and_workspace():
     assert L.li_latent_append_ws(0, 7168, 256) == 0
     # one K step covers d_model = 64: a single split writes the cache directly
     assert L.li_latent_append_ws(16, 64, 128) == 0
+
+
+def test_indexcache_plan():
+    # uniform retention over DeepSeek-V3.2's 61 indexer layers: 61, 31 and 16 scans per token
+    for r, full in ((1, 61), (2, 31), (4, 16)):
+        n, src = li.li_indexcache_plan(61, r)
+        assert n == full
+        assert all(src[l] == l - l % r for l in range(61))
+    # the page's worked group F S S S F: layers 13-15 attend layer 12's selection
+    roles = [0] * 20
+    roles[0] = roles[12] = roles[16] = 1
+    n, src = li.li_indexcache_plan(20, roles=roles)
+    assert n == 3 and src[12:17] == [12, 12, 12, 12, 16] and src[:12] == [0] * 12 and src[19] == 16
+    # every layer F is native DSA
+    assert li.li_indexcache_plan(5, roles=[1] * 5) == (5, [0, 1, 2, 3, 4])
+    L = li.lib()
+    assert L.li_indexcache_plan(None, 4, 1, None) == -li.LI_E_NULL
+    with pytest.raises(li.LiError):
+        li.li_indexcache_plan(0, 1)
+    with pytest.raises(li.LiError):
+        li.li_indexcache_plan(8, 0)
+    with pytest.raises(li.LiError):
+        li.li_indexcache_plan(3, roles=[0, 1, 1])
