@@ -40,11 +40,12 @@ def lib():
         _lib.oracle_latent_reconstruct_scores.argtypes = [vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, dp]
         _lib.oracle_hs_refine.argtypes = [vp, i32, vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, vp, dp, dp]
         _lib.oracle_latent_append.argtypes = [vp, i32, vp, i32, vp, i32, i32, i32, vp, i64, dp]
+        _lib.oracle_sparse_attention.argtypes = [vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, C.c_double, dp, dp]
         _lib.oracle_encode_bf16.restype = C.c_uint16
         _lib.oracle_encode_bf16.argtypes = [C.c_double]
         for f in ("oracle_topk", "oracle_index_decode", "oracle_index_prefill", "oracle_latent_absorb",
                   "oracle_latent_score_group", "oracle_latent_reconstruct_scores", "oracle_hs_refine",
-                  "oracle_latent_append"):
+                  "oracle_latent_append", "oracle_sparse_attention"):
             getattr(_lib, f).restype = C.c_int
     return _lib
 
@@ -191,3 +192,20 @@ def latent_append(h, h_dt, w_enc, w_dt, dst_row, latent):
     _check(lib().oracle_latent_append(_p(h), _CODES[h_dt], _p(w_enc), _CODES[w_dt], _p(dst), B, d_model, Dc,
                                       _p(out), n_tok, _p(exact)), "oracle_latent_append")
     return out, exact
+
+
+def sparse_attention(q, q_dt, kv, kv_dt, idx, kv_off, scale, Dv):
+    """Attention of each request's heads over its selected cache rows.
+    q [B][H][Dk], kv [n_tok][Dk], idx [B][K] int32 (-1 = none), kv_off [B+1].
+    Returns (out [B][H][Dv] fp64, mag [B][H][Dv] = sum p|v| / sum p)."""
+    q = _arr(q, q_dt)
+    kv = _arr(kv, kv_dt)
+    B, H, Dk = q.shape
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    K = idx.shape[1] if idx.ndim == 2 else 0
+    off = np.ascontiguousarray(kv_off, dtype=np.int64)
+    out = np.zeros((B, H, Dv), np.float64)
+    mag = np.zeros((B, H, Dv), np.float64)
+    _check(lib().oracle_sparse_attention(_p(q), _CODES[q_dt], _p(kv), _CODES[kv_dt], _p(idx), _p(off), B, H, K, Dk,
+                                          Dv, float(scale), _p(out), _p(mag)), "oracle_sparse_attention")
+    return out, mag

@@ -42,7 +42,10 @@
  *   - latent-cache append: the page builds the group's shared latent from
  *     the first layer's hidden state without giving the encoder; read as a
  *     linear down-projection c = W_enc h (W_enc stored [Dc][d_model]), the
- *     sum taken exactly and stored once as bfloat16, nearest, ties to even.
+ *     sum taken exactly and stored once as bfloat16, nearest, ties to even;
+ *   - sparse-attention consumer: the selected rows of a latent KV cache
+ *     shared by all heads (keys = the whole row, values = its first Dv
+ *     values), softmax with a caller-given scale, -1 entries skipped.
  *
  * Every function returns 0 on success and a negative value on a bad argument.
  */
@@ -523,3 +526,70 @@ int oracle_latent_append(const void* h, int h_dt, const void* w_enc, int w_dt, c
 
 /* Exported so that tests can pin the bfloat16 encoder on its own. */
 uint16_t oracle_encode_bf16(double v) { return enc_bf16_rne(v); }
+
+/* ---- sparse-attention consumer -------------------------------------------------- */
+/*
+ * The attention that consumes the indexer's selection ("IndexCache: Cross-Layer
+ * Index Reuse for Sparse Attention", Symbol Map: the selected set holds the k
+ * positions sent to core sparse attention; "Multi-layer Indexer ...", The
+ * abstract: each layer attends the tokens its indexer kept).  The pages do not
+ * give the attention's form; the reading here is the decode attention of the
+ * pages' model in its latent form: every selected token contributes one cached
+ * row kv[r] of Dk values shared by all heads, its first Dv values are the value
+ *     o[b][h] = sum_j p_j kv[r_j][0:Dv] / sum_j p_j,
+ *     p_j = exp(s_j - max s),  s_j = scale * (q[b][h] . kv[r_j]),
+ * over the valid entries j of idx[b] (r_j = kv_off[b] + idx[b][j]; -1 entries
+ * are skipped).  A request with no valid entry gets o = 0.  `mag` receives
+ * sum_j p_j |kv[r_j][d]| / sum_j p_j, the scale of each output's error.
+ */
+int oracle_sparse_attention(const void* q, int q_dt, const void* kv, int kv_dt, const int32_t* idx,
+                            const int64_t* kv_off, int B, int H, int K, int Dk, int Dv, double scale, double* out,
+                            double* mag) {
+  if (!dt_ok(q_dt) || !dt_ok(kv_dt) || B < 0 || H <= 0 || K <= 0 || Dk <= 0 || Dv <= 0 || Dv > Dk) return -1;
+  double* s = (double*)malloc(sizeof(double) * (size_t)K);
+  if (!s) return -2;
+  for (int b = 0; b < B; ++b) {
+    const int64_t len = kv_off[b + 1] - kv_off[b];
+    for (int j = 0; j < K; ++j)
+      if (idx[(int64_t)b * K + j] < -1 || idx[(int64_t)b * K + j] >= len) {
+        free(s);
+        return -1;
+      }
+    for (int h = 0; h < H; ++h) {
+      const int64_t qo = ((int64_t)b * H + h) * Dk;
+      double m = -INFINITY;
+      for (int j = 0; j < K; ++j) {
+        const int32_t t = idx[(int64_t)b * K + j];
+        if (t < 0) continue;
+        const int64_t r = (kv_off[b] + t) * Dk;
+        double acc = 0.0;
+        for (int d = 0; d < Dk; ++d) acc += dec_at(q, q_dt, qo + d) * dec_at(kv, kv_dt, r + d);
+        s[j] = scale * acc;
+        if (s[j] > m) m = s[j];
+      }
+      double l = 0.0;
+      double* o = out + ((int64_t)b * H + h) * Dv;
+      double* g = mag + ((int64_t)b * H + h) * Dv;
+      for (int d = 0; d < Dv; ++d) o[d] = g[d] = 0.0;
+      for (int j = 0; j < K; ++j) {
+        const int32_t t = idx[(int64_t)b * K + j];
+        if (t < 0) continue;
+        const int64_t r = (kv_off[b] + t) * Dk;
+        const double p = exp(s[j] - m);
+        l += p;
+        for (int d = 0; d < Dv; ++d) {
+          const double v = dec_at(kv, kv_dt, r + d);
+          o[d] += p * v;
+          g[d] += p * fabs(v);
+        }
+      }
+      if (l > 0.0)
+        for (int d = 0; d < Dv; ++d) {
+          o[d] /= l;
+          g[d] /= l;
+        }
+    }
+  }
+  free(s);
+  return 0;
+}

@@ -432,3 +432,61 @@ def test_latent_append_rejects_rows_outside_the_cache():
     w = np.zeros((2, 32), np.uint16)
     with pytest.raises(Exception):
         oracle.latent_append(h, "bf16", w, "bf16", np.array([5], np.int64), np.zeros((5, 2), np.uint16))
+
+
+# ---- sparse-attention consumer ------------------------------------------------------
+
+def _attn_inputs(seed, lens, H=4, Dk=40, K=12):
+    rng = np.random.default_rng(seed)
+    off = np.zeros(len(lens) + 1, np.int64)
+    off[1:] = np.cumsum(lens)
+    q = _bf16_codes(rng.standard_normal((len(lens), H, Dk)))
+    kv = _bf16_codes(rng.standard_normal((int(off[-1]), Dk)))
+    idx = np.full((len(lens), K), -1, np.int32)
+    for b, n in enumerate(lens):
+        m = min(n, K)
+        idx[b, :m] = rng.choice(n, m, replace=False)
+    return q, kv, idx, off
+
+
+def test_attention_matches_library_sdpa_on_gathered_rows():
+    q, kv, idx, off = _attn_inputs(31, [30, 17, 12])
+    Dv, scale = 32, 0.17
+    out, mag = oracle.sparse_attention(q, "bf16", kv, "bf16", idx, off, scale, Dv)
+    qv = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).double()
+    kvv = torch.from_numpy(kv.view(np.int16)).view(torch.bfloat16).double()
+    for b in range(3):
+        rows = torch.from_numpy(off[b] + idx[b][idx[b] >= 0].astype(np.int64))
+        k_ = kvv[rows]                                  # [n][Dk]
+        ref = torch.nn.functional.scaled_dot_product_attention(qv[b][None], k_[None], k_[None, :, :Dv], scale=scale)[0]
+        assert np.allclose(out[b], ref.numpy(), rtol=0, atol=1e-12)
+    assert np.all(mag >= np.abs(out) - 1e-15)
+
+
+def test_attention_single_token_returns_its_value_row():
+    q, kv, idx, off = _attn_inputs(32, [25])
+    idx[0, 1:] = -1
+    out, mag = oracle.sparse_attention(q, "bf16", kv, "bf16", idx, off, 0.5, 24)
+    v = torch.from_numpy(kv.view(np.int16)).view(torch.bfloat16).double().numpy()[off[0] + idx[0, 0], :24]
+    assert np.array_equal(out[0], np.broadcast_to(v, out[0].shape))
+    assert np.array_equal(mag[0], np.broadcast_to(np.abs(v), out[0].shape))
+
+
+def test_attention_zero_query_is_the_mean_of_the_selected_values():
+    q, kv, idx, off = _attn_inputs(33, [40, 9])
+    q[:] = 0
+    idx[0, 5] = idx[0, 4]                               # a repeated entry counts twice
+    out, _ = oracle.sparse_attention(q, "bf16", kv, "bf16", idx, off, 1.0, 16)
+    v = torch.from_numpy(kv.view(np.int16)).view(torch.bfloat16).double().numpy()
+    for b in range(2):
+        sel = idx[b][idx[b] >= 0]
+        assert np.allclose(out[b], v[off[b] + sel, :16].mean(axis=0)[None, :], rtol=0, atol=1e-14)
+
+
+def test_attention_ignores_entry_order_and_padding_and_empty_requests():
+    q, kv, idx, off = _attn_inputs(34, [50, 0, 20])
+    a, _ = oracle.sparse_attention(q, "bf16", kv, "bf16", idx, off, 0.3, 8)
+    perm = idx[:, ::-1].copy()                          # reversed order, padding first
+    b_, _ = oracle.sparse_attention(q, "bf16", kv, "bf16", perm, off, 0.3, 8)
+    assert np.allclose(a, b_, rtol=0, atol=1e-13)
+    assert np.all(a[1] == 0.0)                          # no selected token
