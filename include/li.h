@@ -228,6 +228,34 @@ li_status li_latent_append(const void* h, li_dtype h_dt, const void* w_enc, li_d
 size_t li_latent_append_ws(int32_t M, int32_t d_model, int32_t Dc);
 
 /* ---------------------------------------------------------------------------
+ * li_sparse_attention — the consumer of a selection: each request's heads
+ * attend the cache rows its indexer kept.
+ *
+ * (IndexCache page, Symbol Map: the selected set holds the k positions sent to
+ * core sparse attention.  "Multi-layer Indexer ...", The Brief: attention
+ * consumes a selection, so an indexer on a second stream can run beside it.)
+ * The pages do not give the attention; this is the latent decode attention of
+ * their model: a cached row of Dk = 576 values per token, shared by all heads,
+ * is the key and its first Dv = 512 values the value:
+ *     out[b][h] = sum_j p_j kv[r_j][0:512] / sum_j p_j,  p_j = exp(s_j - max_j s_j),
+ *     s_j = scale * (q[b][h] . kv[r_j]),  r_j = kv_off[b] + idx[b][j]
+ * over the entries j with idx[b][j] >= 0.  A request with none gets out = 0.
+ * Scores accumulate in fp32; p is rounded to bf16 for the value product and
+ * for its sum.
+ *
+ *   q       [B][H][576] LI_BF16;  H a multiple of 64, at most 256
+ *   kv      [n_tok][576] LI_BF16;  kv_off [B+1] int64, device
+ *   idx     [B][k] int32, device: positions in [0, L_b), ascending, -1 padded
+ *           (out_idx of li_index_decode); 1 <= k <= 65536
+ *   out     [B][H][512] fp32
+ *   ws      li_sparse_attention_ws(B, H, k) bytes (per-split partial outputs)
+ * ------------------------------------------------------------------------- */
+li_status li_sparse_attention(const void* q, li_dtype q_dt, const void* kv, li_dtype kv_dt, const int32_t* idx,
+                              const int64_t* kv_off, int32_t B, int64_t n_tok, int32_t H, int32_t Dk, int32_t Dv,
+                              int32_t k, float scale, float* out, void* ws, size_t ws_bytes, void* stream);
+size_t li_sparse_attention_ws(int32_t B, int32_t H, int32_t k);
+
+/* ---------------------------------------------------------------------------
  * li_indexcache_plan — IndexCache layer roles (host only; no device work).
  *
  * ("IndexCache: Cross-Layer Index Reuse for Sparse Attention", Deep Dive and

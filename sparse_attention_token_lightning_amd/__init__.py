@@ -26,7 +26,7 @@ LI_MAX_K = 16384
 # Every symbol include/li.h declares.
 SYMBOLS = ("li_index_decode", "li_index_decode_ws", "li_index_prefill", "li_index_prefill_ws",
            "li_latent_score_group", "li_latent_score_group_ws", "li_hs_refine", "li_hs_refine_ws",
-           "li_latent_append", "li_latent_append_ws", "li_indexcache_plan", "li_topk", "li_topk_ws", "li_status_str", "li_last_error", "li_trace_events", "li_trace_count")
+           "li_latent_append", "li_latent_append_ws", "li_sparse_attention", "li_sparse_attention_ws", "li_indexcache_plan", "li_topk", "li_topk_ws", "li_status_str", "li_last_error", "li_trace_events", "li_trace_count")
 
 _lib = None
 
@@ -57,15 +57,18 @@ def lib():
         L.li_hs_refine_ws.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.li_latent_append.argtypes = [vp, i32, vp, i32, vp, i32, i32, i32, vp, i64, vp, sz, vp]
         L.li_latent_append_ws.argtypes = [i32, i32, i32]
+        L.li_sparse_attention.argtypes = [vp, i32, vp, i32, vp, vp, i32, i64, i32, i32, i32, i32, C.c_float, vp, vp, sz,
+                                          vp]
+        L.li_sparse_attention_ws.argtypes = [i32, i32, i32]
         L.li_indexcache_plan.restype = i32
         L.li_indexcache_plan.argtypes = [vp, i32, i32, vp]
         L.li_topk.argtypes = [vp, i64, vp, i32, i32, i32, vp, vp, sz, vp]
         L.li_topk_ws.argtypes = [i32, i32, i32]
         for f in ("li_index_decode", "li_index_prefill", "li_latent_score_group", "li_hs_refine", "li_latent_append",
-                  "li_topk"):
+                  "li_sparse_attention", "li_topk"):
             getattr(L, f).restype = C.c_int32
         for f in ("li_index_decode_ws", "li_index_prefill_ws", "li_latent_score_group_ws", "li_hs_refine_ws",
-                  "li_latent_append_ws", "li_topk_ws"):
+                  "li_latent_append_ws", "li_sparse_attention_ws", "li_topk_ws"):
             getattr(L, f).restype = C.c_size_t
         L.li_status_str.argtypes = [i32]
         L.li_status_str.restype = C.c_char_p
@@ -202,6 +205,21 @@ def li_latent_append(h, w_enc, dst_row, latent, ws=None, stream=None):
     _check(L.li_latent_append(_ptr(h), _dt(h), _ptr(w_enc), _dt(w_enc), _ptr(dst_row), M, d_model, Dc, _ptr(latent),
                               n_tok, _ptr(wst), wsb, _stream(stream)))
     return latent
+
+
+def li_sparse_attention(q, kv, idx, kv_off, scale, out=None, ws=None, stream=None):
+    """Attention over selected rows.  q [B,H,576] bf16, kv [n_tok,576] bf16,
+    idx [B,k] int32 (-1 padded), kv_off [B+1] int64.  Returns out [B,H,512] fp32."""
+    B, H, Dk = q.shape
+    k = idx.shape[1]
+    if out is None:
+        out = torch.empty((B, H, 512), dtype=torch.float32, device=q.device)
+    L = lib()
+    need = L.li_sparse_attention_ws(B, H, k)
+    wst, wsb = _workspace(need, q.device, ws)
+    _check(L.li_sparse_attention(_ptr(q), _dt(q), _ptr(kv), _dt(kv), _ptr(idx), _ptr(kv_off), B, kv.shape[0], H, Dk,
+                                 512, k, float(scale), _ptr(out), _ptr(wst), wsb, _stream(stream)))
+    return out
 
 
 def li_indexcache_plan(n_layers, retain_every=1, roles=None):

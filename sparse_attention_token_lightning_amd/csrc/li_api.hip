@@ -490,6 +490,44 @@ li_status li_latent_append(const void* h, li_dtype h_dt, const void* w_enc, li_d
                    "latent_append launch", s);
 }
 
+size_t li_sparse_attention_ws(int32_t B, int32_t H, int32_t k) {
+  if (B <= 0 || H <= 0 || H % 64 != 0 || k <= 0) return 0;
+  const size_t rows = (size_t)li::attention_splits(B, H, k) * B * H;
+  return align_up(rows * 512 * 4) + align_up(rows * 2 * 4);
+}
+
+li_status li_sparse_attention(const void* q, li_dtype q_dt, const void* kv, li_dtype kv_dt, const int32_t* idx,
+                              const int64_t* kv_off, int32_t B, int64_t n_tok, int32_t H, int32_t Dk, int32_t Dv,
+                              int32_t k, float scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (!q || !kv || !idx || !kv_off || !out) return fail(LI_E_NULL, "q, kv, idx, kv_off and out are required");
+  if (q_dt != LI_BF16 || kv_dt != LI_BF16) return fail(LI_E_DTYPE, "q and kv must be LI_BF16");
+  if (B < 0 || n_tok <= 0 || H <= 0 || k <= 0) return fail(LI_E_SHAPE, "need B >= 0, n_tok >= 1, H >= 1 and k >= 1");
+  if (Dk != 576 || Dv != 512) return fail(LI_E_UNSUPPORTED, "Dk must be 576 and Dv 512 (got %d, %d)", Dk, Dv);
+  if (H % 64 != 0 || H > 256) return fail(LI_E_UNSUPPORTED, "H must be 64, 128, 192 or 256 (got %d)", H);
+  if (k > 65536) return fail(LI_E_UNSUPPORTED, "k must be <= 65536 (got %d)", k);
+  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY) return fail(LI_E_SHAPE, "scale must be finite");
+  li_status st;
+  if ((st = check_ws(ws, ws_bytes, li_sparse_attention_ws(B, H, k)))) return st;
+  if (B == 0) return LI_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (validate_on() && (st = run_validation(s, [&] {
+        li::validate_offsets(kv_off, B, n_tok, INT32_MAX, s);
+        li::validate_cands(idx, B, k, kv_off, s);
+        li::validate_bf16(q, (int64_t)B * H * Dk, li::kBadQ, s);
+        li::validate_bf16(kv, n_tok * Dk, li::kBadKeys, s);
+      })))
+    return st;
+  trace_begin();
+  Carver cv(ws);
+  const size_t rows = (size_t)li::attention_splits(B, H, k) * B * H;
+  float* o_part = (float*)cv.take(rows * 512 * 4);
+  float* ml_part = (float*)cv.take(rows * 2 * 4);
+  return hip_check(li::launch_sparse_attention((const uint16_t*)q, (const uint16_t*)kv, idx, kv_off, B, H, k, scale,
+                                               o_part, ml_part, out, s),
+                   "sparse_attention launch", s);
+}
+
 int32_t li_indexcache_plan(const uint8_t* roles, int32_t n_layers, int32_t retain_every, int32_t* src) {
   g_err.clear();
   if (!src) return -fail(LI_E_NULL, "src is required");

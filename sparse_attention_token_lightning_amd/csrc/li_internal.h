@@ -112,6 +112,14 @@ hipError_t launch_hs_score(const uint16_t* qt16, const float* wsc, const uint16_
 // K is split over append_splits(M, d_model) workgroups; with more than one
 // split, `part` ([S][M][Dc] fp32) holds the partial sums.
 int32_t append_splits(int32_t M, int32_t d_model);
+
+// Sparse attention over selected rows (Dk = 576, Dv = 512, H a multiple of
+// 64): token splits write partial outputs o_part [S][B][H][512] and (max, sum)
+// pairs ml_part [S][B][H][2]; a second kernel combines them into out.
+int32_t attention_splits(int32_t B, int32_t H, int32_t K);
+hipError_t launch_sparse_attention(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const int64_t* kv_off,
+                                   int32_t B, int32_t H, int32_t K, float scale, float* o_part, float* ml_part,
+                                   float* out, hipStream_t stream);
 hipError_t launch_latent_append(const uint16_t* h, const uint16_t* w_enc, const int64_t* dst, int32_t M,
                                 int32_t d_model, int32_t Dc, float* part, uint16_t* latent, hipStream_t stream);
 

@@ -278,6 +278,67 @@ def append_prefill() -> Append:
     return make_append(1007, [65536 - 4096], [4096], name="append_prefill_T4096_L65536_d7168_Dc256")
 
 
+@dataclass
+class Attention:
+    """Sparse attention over selected rows: B requests, H heads, a latent KV
+    cache of Dk = 576 values per token, idx [B][k] ascending, -1 padded."""
+    q: np.ndarray            # [B][H][576] bf16 bits
+    kv: Optional[np.ndarray]  # [n_tok][576] bf16 bits (None: drawn on the device)
+    idx: np.ndarray          # [B][k] int32
+    kv_off: np.ndarray       # [B+1] int64
+    H: int
+    k: int
+    scale: float
+    seed: int = 0
+    name: str = ""
+
+    @property
+    def B(self):
+        return int(self.kv_off.size - 1)
+
+    @property
+    def n_tok(self):
+        return int(self.kv_off[-1])
+
+
+def _selection(rng, lens, k):
+    idx = np.full((len(lens), k), -1, np.int32)
+    for b, n in enumerate(lens):
+        m = int(min(n, k))
+        if m:
+            idx[b, :m] = np.sort(rng.choice(int(n), m, replace=False))
+    return idx
+
+
+def make_attention(seed, lens, H=64, k=2048, device_kv=False, name="") -> Attention:
+    """q ~ N(0,1) and kv ~ N(0,1) -> bf16; each request selects min(L_b, k)
+    distinct positions uniformly, ascending, -1 padded; scale 1/sqrt(192) (a
+    128 + 64-dim query-key head).  device_kv: the cache is drawn later on the
+    GPU by device_kv_cache(), for caches too large to draw on the host."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, dtype=np.int64)
+    off = _offsets(lens)
+    q = rng.standard_normal((lens.size, H, 576), dtype=np.float32)
+    idx = _selection(rng, lens, k)
+    kv = None if device_kv else encode_bf16(rng.standard_normal((int(off[-1]), 576), dtype=np.float32))
+    return Attention(q=encode_bf16(q), kv=kv, idx=idx, kv_off=off, H=H, k=k, scale=float(1.0 / np.sqrt(192.0)),
+                     seed=seed, name=name)
+
+
+def device_kv_cache(x: Attention):
+    """The cache of a device_kv workload: N(0,1) -> bf16 from a torch generator
+    on the current GPU, seeded by the workload's seed."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(x.seed)
+    return torch.randn((x.n_tok, 576), generator=g, device="cuda").to(torch.bfloat16)
+
+
+def attention_decode() -> Attention:
+    """Sparse attention of one decode step after the indexer: B = 16 requests at
+    L = 131072, 128 heads, k = 2048 selected rows each."""
+    return make_attention(1008, [131072] * 16, H=128, device_kv=True, name="attention_B16_L131072_H128_k2048")
+
+
 def cfg1() -> Decode:
     """Single decode query, L = 4096, integer-valued bf16 q and K, integer w."""
     return make_decode(1001, [4096], k_dt="bf16", dist="int", name="decode_int_L4096")
