@@ -315,7 +315,120 @@ def components(torch, li, inputs, args):
             "tflops": flop / t / 1e12, "mfma_frac_bf16": flop / t / 1e12 / BF16_PEAK_TFLOPS}
         del srcs, dst, lat, ws
     out.update(stack_component(torch, li, args))
+    out.update(attention_component(torch, li, inputs, args))
+    out.update(mli_component(torch, li, args))
     return out
+
+
+def attention_component(torch, li, inputs, args):
+    """The selection's consumer on its own: 16 requests x 128 heads attend k =
+    2048 of 131072 cached rows (576 bf16 values each)."""
+    x = inputs.attention_decode()
+    kv = inputs.device_kv_cache(x)
+    q, idx, off = dev(torch, x.q, "bf16"), dev(torch, x.idx), dev(torch, x.kv_off)
+    o = torch.empty((x.B, x.H, 512), dtype=torch.float32, device="cuda")
+    ws = torch.empty(li.lib().li_sparse_attention_ws(x.B, x.H, x.k), dtype=torch.uint8, device="cuda")
+    fn = lambda: li.li_sparse_attention(q, kv, idx, off, x.scale, out=o, ws=ws)
+    wall, (attn, comb) = timed(torch, li, fn, 2, max(args.comp_iters, 10), 2)
+    nbytes = x.B * x.k * 576 * 2 + q.numel() * 2 + o.numel() * 4 + idx.numel() * 4
+    flop = 2.0 * x.B * x.H * x.k * (576 + 512)
+    t = (attn + comb) * 1e-3
+    res = {x.name: {"attn_ms": attn, "combine_ms": comb, "total_ms": wall, "algorithmic_bytes": nbytes,
+                    "gbs": nbytes / t / 1e9, "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBS,
+                    "tflops": flop / t / 1e12, "mfma_frac_bf16": flop / t / 1e12 / BF16_PEAK_TFLOPS}}
+    del kv, q, idx, off, o, ws
+    return res
+
+
+def mli_component(torch, li, args, n_layers=8, B=16, L=131072, H_idx=64, H_attn=128, k=2048):
+    """Multi-layer Indexer overlap on an n_layers decode stack (each layer with
+    its own fp8 indexer cache and bf16 attention cache).  Serial: every layer
+    scans, then attends its own selection.  MLI (lag 1): layer 0 is serial;
+    layer l attends layer l-1's selection on the main stream while its own
+    indexer runs on a second stream, started once the layer's input exists and
+    joined before the next layer's attention.  Each schedule is captured once
+    into a HIP graph and replayed."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4343)
+    n_tok = B * L
+    off = torch.arange(0, (B + 1) * L, L, dtype=torch.int64, device="cuda")
+    layers = []
+    for _ in range(n_layers):
+        q = torch.randn((B, H_idx, 128), generator=g, device="cuda").to(torch.bfloat16)
+        w = torch.randn((B, H_idx), generator=g, device="cuda") / 8
+        kc = torch.randn((n_tok, 128), generator=g, device="cuda").clamp_(-448, 448).to(torch.float8_e4m3fn)
+        ks = torch.rand((n_tok,), generator=g, device="cuda") * 1.5 + 0.5
+        qa = torch.randn((B, H_attn, 576), generator=g, device="cuda").to(torch.bfloat16)
+        kv = torch.randn((n_tok, 576), generator=g, device="cuda").to(torch.bfloat16)
+        layers.append((q, w, kc, ks, qa, kv))
+    L_ = li.lib()
+    sel = [torch.empty((B, k), dtype=torch.int32, device="cuda") for _ in range(n_layers)]
+    outs = [torch.empty((B, H_attn, 512), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
+    ws_i = torch.empty(L_.li_index_decode_ws(B, n_tok, L, k, 0), dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(L_.li_sparse_attention_ws(B, H_attn, k), dtype=torch.uint8, device="cuda")
+    scale = 1.0 / 192 ** 0.5
+
+    def indexer(l):
+        q, w, kc, ks, _, _ = layers[l]
+        li.li_index_decode(q, w, kc, ks, off, L, k, out_idx=sel[l], ws=ws_i)
+
+    def attention(l, s):
+        qa, kv = layers[l][4], layers[l][5]
+        li.li_sparse_attention(qa, kv, sel[s], off, scale, out=outs[l], ws=ws_a)
+
+    side = torch.cuda.Stream()
+
+    def serial():
+        for l in range(n_layers):
+            indexer(l)
+            attention(l, l)
+
+    def mli():
+        cur = torch.cuda.current_stream()
+        indexer(0)
+        attention(0, 0)
+        for l in range(1, n_layers):
+            side.wait_stream(cur)  # the layer's input exists
+            with torch.cuda.stream(side):
+                indexer(l)
+            attention(l, l - 1)
+            cur.wait_stream(side)  # the next layer attends this selection
+
+    def graph_ms(fn, reps=10):
+        main = torch.cuda.Stream()
+        with torch.cuda.stream(main):
+            fn()  # eager warm-up
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=main):
+            fn()
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            gr.replay()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / reps * 1e3
+        del gr
+        return ms
+
+    _, (i_scan, i_topk) = timed(torch, li, lambda: indexer(1), 2, 10, 2)
+    _, (a_attn, a_comb) = timed(torch, li, lambda: attention(1, 1), 2, 10, 2)
+    t_serial = graph_ms(serial)
+    t_mli = graph_ms(mli)
+    idx_ms = i_scan + i_topk
+    attn_ms = a_attn + a_comb
+    res = {"serial_ms": t_serial, "mli_ms": t_mli, "speedup": t_serial / t_mli,
+           "indexer_ms_per_layer": idx_ms, "attention_ms_per_layer": attn_ms,
+           "hidden_ms": t_serial - t_mli,
+           "hidden_frac_of_overlappable_attention": (t_serial - t_mli) / ((n_layers - 1) * min(idx_ms, attn_ms)),
+           "note": f"{n_layers} layers, B = {B}, L = {L}: per layer an fp8 indexer scan + top-{k} ({H_idx} heads) and "
+                   f"a {H_attn}-head attention over {k} selected rows of a 576-value bf16 cache; graph replays, "
+                   "wall clock; layer 0 stays serial"}
+    del layers, sel, outs, ws_i, ws_a
+    torch.cuda.empty_cache()
+    return {f"mli_{n_layers}L_B{B}_L{L}": res}
 
 
 def stack_component(torch, li, args, n_layers=61, B=16, L=131072, G=4, C=8192):

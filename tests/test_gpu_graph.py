@@ -96,3 +96,42 @@ def test_append_graph():
     ws = torch.empty(li.lib().li_latent_append_ws(x.M, x.d_model, x.Dc), dtype=torch.uint8, device="cuda")
     assert ws.numel() > 0  # the split path (partial sums + reduction) is the one captured
     check_replays(lambda: li.li_latent_append(h, wenc, dst, lat, ws=ws), [lat], "append")
+
+
+def test_two_stream_mli_graph():
+    """Lagged selection (Multi-layer Indexer): layer l attends layer l-1's
+    selection on the capturing stream while its own indexer runs on a second
+    stream; the captured graph's replays match the eager run bit for bit."""
+    from sparse_attention_token_lightning_amd.inputs import make_attention, make_decode
+    n_layers, k = 3, 256
+    dec = [make_decode(910 + l, [3000, 1500], k=k) for l in range(n_layers)]
+    att = [make_attention(920 + l, [3000, 1500], H=64, k=k) for l in range(n_layers)]
+    d_in = [(dev(x.q, "bf16"), dev(x.w), dev(x.kc, "fp8_e4m3"), dev(x.k_scale), dev(x.kv_off)) for x in dec]
+    a_in = [(dev(x.q, "bf16"), dev(x.kv, "bf16")) for x in att]
+    L = 3000
+    sel = [torch.empty((2, k), dtype=torch.int32, device="cuda") for _ in range(n_layers)]
+    outs = [torch.empty((2, 64, 512), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
+    ws_i = torch.empty(li.lib().li_index_decode_ws(2, dec[0].n_tok, L, k, 0), dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(li.lib().li_sparse_attention_ws(2, 64, k), dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+
+    def indexer(l):
+        q, w, kc, ks, off = d_in[l]
+        li.li_index_decode(q, w, kc, ks, off, L, k, out_idx=sel[l], ws=ws_i)
+
+    def attention(l, s):
+        q, kv = a_in[l]
+        li.li_sparse_attention(q, kv, sel[s], d_in[l][4], att[l].scale, out=outs[l], ws=ws_a)
+
+    def run():
+        cur = torch.cuda.current_stream()
+        indexer(0)
+        attention(0, 0)
+        for l in range(1, n_layers):
+            side.wait_stream(cur)
+            with torch.cuda.stream(side):
+                indexer(l)
+            attention(l, l - 1)
+            cur.wait_stream(side)
+
+    check_replays(run, sel + outs, "mli two-stream")
