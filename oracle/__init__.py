@@ -36,9 +36,9 @@ def lib():
         _lib.oracle_index_decode.argtypes = [vp, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32, vp, dp, dp]
         _lib.oracle_index_prefill.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, vp, dp, dp]
         _lib.oracle_latent_absorb.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, i32, dp]
-        _lib.oracle_latent_score_group.argtypes = [vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, vp, dp, dp]
-        _lib.oracle_latent_reconstruct_scores.argtypes = [vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, dp]
-        _lib.oracle_hs_refine.argtypes = [vp, i32, vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, vp, dp, dp]
+        _lib.oracle_latent_score_group.argtypes = [vp, i32, vp, vp, i32, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, i32, vp, dp, dp]
+        _lib.oracle_latent_reconstruct_scores.argtypes = [vp, i32, vp, vp, i32, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, dp]
+        _lib.oracle_hs_refine.argtypes = [vp, i32, vp, i32, vp, vp, i32, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, i32, vp, dp, dp]
         _lib.oracle_latent_append.argtypes = [vp, i32, vp, i32, vp, i32, i32, i32, vp, i64, dp]
         _lib.oracle_sparse_attention.argtypes = [vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, C.c_double, dp, dp]
         _lib.oracle_encode_bf16.restype = C.c_uint16
@@ -125,7 +125,8 @@ def latent_absorb(q, q_dt, w_dec, w_dt, B, G, H, Dh, Dc):
 
 
 def latent_score_group(q, q_dt, w, w_dec, w_dt, latent, c_dt, c_scale, kv_off, G, H, Dh, Dc, k,
-                       want_scores=True):
+                       want_scores=True, c_blocks=1):
+    """c_scale: [n_tok] per-row scales, or [n_tok][c_blocks] (one per Dc/c_blocks values)."""
     q, w_dec, latent = _arr(q, q_dt), _arr(w_dec, w_dt), _arr(latent, c_dt)
     w, c_scale = _f32(w), _f32(c_scale)
     kv_off = np.ascontiguousarray(kv_off, dtype=np.int64)
@@ -135,27 +136,27 @@ def latent_score_group(q, q_dt, w, w_dec, w_dt, latent, c_dt, c_scale, kv_off, G
     sc = np.empty((G, n_tok), dtype=np.float64) if want_scores else None
     ab = np.empty((G, n_tok), dtype=np.float64) if want_scores else None
     rc = lib().oracle_latent_score_group(_p(q), _CODES[q_dt], _p(w), _p(w_dec), _CODES[w_dt], _p(latent),
-                                         _CODES[c_dt], _p(c_scale), _p(kv_off), B, G, H, Dh, Dc, k,
+                                         _CODES[c_dt], _p(c_scale), c_blocks, _p(kv_off), B, G, H, Dh, Dc, k,
                                          _p(idx), _p(sc), _p(ab))
     _check(rc, "oracle_latent_score_group")
     return idx, sc, ab
 
 
-def latent_reconstruct_scores(q, q_dt, w, w_dec, w_dt, latent, c_dt, c_scale, kv_off, G, H, Dh, Dc):
+def latent_reconstruct_scores(q, q_dt, w, w_dec, w_dt, latent, c_dt, c_scale, kv_off, G, H, Dh, Dc, c_blocks=1):
     q, w_dec, latent = _arr(q, q_dt), _arr(w_dec, w_dt), _arr(latent, c_dt)
     w, c_scale = _f32(w), _f32(c_scale)
     kv_off = np.ascontiguousarray(kv_off, dtype=np.int64)
     B = kv_off.size - 1
     sc = np.empty((G, int(kv_off[-1])), dtype=np.float64)
     rc = lib().oracle_latent_reconstruct_scores(_p(q), _CODES[q_dt], _p(w), _p(w_dec), _CODES[w_dt],
-                                                _p(latent), _CODES[c_dt], _p(c_scale), _p(kv_off), B, G, H,
+                                                _p(latent), _CODES[c_dt], _p(c_scale), c_blocks, _p(kv_off), B, G, H,
                                                 Dh, Dc, _p(sc))
     _check(rc, "oracle_latent_reconstruct_scores")
     return sc
 
 
 def hs_refine(cand_idx, q, q_dt, w, w_dec, w_dt, latent, c_dt, c_scale, kv_off, Gf, H, Dh, Dc, k,
-              want_scores=True):
+              want_scores=True, c_blocks=1):
     cand_idx = np.ascontiguousarray(cand_idx, dtype=np.int32)
     q, w_dec, latent = _arr(q, q_dt), _arr(w_dec, w_dt), _arr(latent, c_dt)
     w, c_scale = _f32(w), _f32(c_scale)
@@ -165,7 +166,7 @@ def hs_refine(cand_idx, q, q_dt, w, w_dec, w_dt, latent, c_dt, c_scale, kv_off, 
     sc = np.full((B, Gf, Cn), np.nan) if want_scores else None
     ab = np.full((B, Gf, Cn), np.nan) if want_scores else None
     rc = lib().oracle_hs_refine(_p(cand_idx), Cn, _p(q), _CODES[q_dt], _p(w), _p(w_dec), _CODES[w_dt],
-                                _p(latent), _CODES[c_dt], _p(c_scale), _p(kv_off), B, Gf, H, Dh, Dc, k,
+                                _p(latent), _CODES[c_dt], _p(c_scale), c_blocks, _p(kv_off), B, Gf, H, Dh, Dc, k,
                                 _p(idx), _p(sc), _p(ab))
     _check(rc, "oracle_hs_refine")
     return idx, sc, ab

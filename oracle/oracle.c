@@ -43,6 +43,9 @@
  *     the first layer's hidden state without giving the encoder; read as a
  *     linear down-projection c = W_enc h (W_enc stored [Dc][d_model]), the
  *     sum taken exactly and stored once as bfloat16, nearest, ties to even;
+ *   - latent scales: c_scale holds c_nblk entries per row, entry j scaling
+ *     values j*Dc/c_nblk onward (one per row, or one per 128-value block of an
+ *     fp8 latent);
  *   - sparse-attention consumer: the selected rows of a latent KV cache
  *     shared by all heads (keys = the whole row, values = its first Dv
  *     values), softmax with a caller-given scale, -1 entries skipped.
@@ -305,18 +308,26 @@ int oracle_latent_absorb(const void* q, int q_dt, const void* w_dec, int w_dt, i
   return 0;
 }
 
+/* The scale of value c of latent row `row`: entry c / (Dc / c_nblk) of the
+ * row's c_nblk scale entries (1 when there are none). */
+static double row_scale(const float* c_scale, int c_nblk, int Dc, int64_t row, int c) {
+  return c_scale ? (double)c_scale[row * c_nblk + c / (Dc / c_nblk)] : 1.0;
+}
+
 /* Score the shared latent cache for all G layers of each request, then take
  * each layer's own top-k (layer-specific selection).
- * latent [n_tok][Dc] (c_dt) with c_scale [n_tok] or NULL; w [B][G][H].
+ * latent [n_tok][Dc] (c_dt) with c_scale [n_tok][c_nblk] or NULL: scale entry j of a
+ * row multiplies its values j*Dc/c_nblk .. (j+1)*Dc/c_nblk - 1 (c_nblk = 1: one scale
+ * per row; Dc/128: one per 128-value block); w [B][G][H].
  * out_idx [B][G][k]; out_scores / out_abs [G][n_tok] (may be NULL). */
 int oracle_latent_score_group(const void* q, int q_dt, const float* w, const void* w_dec,
-                              int w_dt, const void* latent, int c_dt, const float* c_scale,
+                              int w_dt, const void* latent, int c_dt, const float* c_scale, int c_nblk,
                               const int64_t* kv_off, int B, int G, int H, int Dh, int Dc, int k,
                               int32_t* out_idx, double* out_scores, double* out_abs) {
   if (!q || !w || !w_dec || !latent || !kv_off || !out_idx || B < 0 || G <= 0 || H <= 0 ||
       Dh <= 0 || Dc <= 0 || k <= 0)
     return -1;
-  if (!dt_ok(c_dt)) return -1;
+  if (!dt_ok(c_dt) || c_nblk < 1 || Dc % c_nblk != 0) return -1;
   double* qt = (double*)malloc((size_t)(B > 0 ? B : 1) * G * H * Dc * sizeof(double));
   if (!qt) return -2;
   int rc = oracle_latent_absorb(q, q_dt, w_dec, w_dt, B, G, H, Dh, Dc, qt);
@@ -337,8 +348,7 @@ int oracle_latent_score_group(const void* q, int q_dt, const float* w, const voi
     } else {
       for (int64_t s = 0; s < L; ++s) {
         int64_t row = off + s;
-        double sig = c_scale ? (double)c_scale[row] : 1.0;
-        for (int c = 0; c < Dc; ++c) cd[c] = sig * dec_at(latent, c_dt, row * Dc + c);
+        for (int c = 0; c < Dc; ++c) cd[c] = row_scale(c_scale, c_nblk, Dc, row, c) * dec_at(latent, c_dt, row * Dc + c);
         double acc = 0.0, mag = 0.0;
         for (int h = 0; h < H; ++h) {
           const double* qh = qt + ((int64_t)bl * H + h) * Dc;
@@ -368,12 +378,12 @@ int oracle_latent_score_group(const void* q, int q_dt, const float* w, const voi
  * Used only to check that absorption changes nothing.  out_scores [G][n_tok]. */
 int oracle_latent_reconstruct_scores(const void* q, int q_dt, const float* w, const void* w_dec,
                                      int w_dt, const void* latent, int c_dt,
-                                     const float* c_scale, const int64_t* kv_off, int B, int G,
+                                     const float* c_scale, int c_nblk, const int64_t* kv_off, int B, int G,
                                      int H, int Dh, int Dc, double* out_scores) {
   if (!q || !w || !w_dec || !latent || !kv_off || !out_scores || B < 0 || G <= 0 || H <= 0 ||
       Dh <= 0 || Dc <= 0)
     return -1;
-  if (!dt_ok(q_dt) || !dt_ok(w_dt) || !dt_ok(c_dt)) return -1;
+  if (!dt_ok(q_dt) || !dt_ok(w_dt) || !dt_ok(c_dt) || c_nblk < 1 || Dc % c_nblk != 0) return -1;
   int64_t n_tok = kv_off[B];
   int rc = 0;
 #pragma omp parallel for schedule(dynamic) reduction(min : rc)
@@ -385,8 +395,7 @@ int oracle_latent_reconstruct_scores(const void* q, int q_dt, const float* w, co
       rc = -2;
     } else {
       for (int64_t row = kv_off[b]; row < kv_off[b + 1]; ++row) {
-        double sig = c_scale ? (double)c_scale[row] : 1.0;
-        for (int c = 0; c < Dc; ++c) cd[c] = sig * dec_at(latent, c_dt, row * Dc + c);
+        for (int c = 0; c < Dc; ++c) cd[c] = row_scale(c_scale, c_nblk, Dc, row, c) * dec_at(latent, c_dt, row * Dc + c);
         double acc = 0.0;
         for (int h = 0; h < H; ++h) {
           for (int j = 0; j < Dh; ++j) {
@@ -421,12 +430,12 @@ int oracle_latent_reconstruct_scores(const void* q, int q_dt, const float* w, co
  * candidate slot (slots past the valid candidates are left untouched). */
 int oracle_hs_refine(const int32_t* cand_idx, int C, const void* q, int q_dt, const float* w,
                      const void* w_dec, int w_dt, const void* latent, int c_dt,
-                     const float* c_scale, const int64_t* kv_off, int B, int Gf, int H, int Dh,
+                     const float* c_scale, int c_nblk, const int64_t* kv_off, int B, int Gf, int H, int Dh,
                      int Dc, int k, int32_t* out_idx, double* out_scores, double* out_abs) {
   if (!cand_idx || !q || !w || !w_dec || !latent || !kv_off || !out_idx || C < 0 || B < 0 ||
       Gf <= 0 || H <= 0 || Dh <= 0 || Dc <= 0 || k <= 0)
     return -1;
-  if (!dt_ok(c_dt)) return -1;
+  if (!dt_ok(c_dt) || c_nblk < 1 || Dc % c_nblk != 0) return -1;
   double* qt = (double*)malloc((size_t)(B > 0 ? B : 1) * Gf * H * Dc * sizeof(double));
   if (!qt) return -2;
   int rc = oracle_latent_absorb(q, q_dt, w_dec, w_dt, B, Gf, H, Dh, Dc, qt);
@@ -447,8 +456,7 @@ int oracle_hs_refine(const int32_t* cand_idx, int C, const void* q, int q_dt, co
     } else {
       for (int64_t j = 0; j < nv; ++j) {
         int64_t row = kv_off[b] + cand[j];
-        double sig = c_scale ? (double)c_scale[row] : 1.0;
-        for (int c = 0; c < Dc; ++c) cd[c] = sig * dec_at(latent, c_dt, row * Dc + c);
+        for (int c = 0; c < Dc; ++c) cd[c] = row_scale(c_scale, c_nblk, Dc, row, c) * dec_at(latent, c_dt, row * Dc + c);
         double acc = 0.0, mag = 0.0;
         for (int h = 0; h < H; ++h) {
           const double* qh = qt + ((int64_t)bf * H + h) * Dc;

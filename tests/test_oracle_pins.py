@@ -490,3 +490,63 @@ def test_attention_ignores_entry_order_and_padding_and_empty_requests():
     b_, _ = oracle.sparse_attention(q, "bf16", kv, "bf16", perm, off, 0.3, 8)
     assert np.allclose(a, b_, rtol=0, atol=1e-13)
     assert np.all(a[1] == 0.0)                          # no selected token
+
+
+# ---- fp8 latent with per-block scales ---------------------------------------------
+
+def _fp8_latent_case(seed, Dc=256):
+    x = inputs.make_latent(seed, [300, 120], G=2, H=16, Dc=Dc, k=40)
+    rng = np.random.default_rng(seed + 1)
+    codes = inputs.encode_fp8(rng.standard_normal((x.n_tok, Dc)) * 3.0)
+    return x, codes
+
+
+def _fp8_values(codes):
+    return torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+
+
+def test_fp8_latent_with_unit_block_scales_equals_the_bf16_latent_of_its_values():
+    # every E4M3 value is exact in bf16, so both latents hold the same numbers
+    x, codes = _fp8_latent_case(41)
+    ones = np.ones((x.n_tok, 2), np.float32)
+    a_idx, a, _ = oracle.latent_score_group(x.q, "bf16", x.w, x.w_dec, "bf16", codes, "fp8_e4m3", ones, x.kv_off,
+                                            x.G, x.H, 128, 256, x.k, c_blocks=2)
+    lat = inputs.encode_bf16(_fp8_values(codes))
+    b_idx, b, _ = oracle.latent_score_group(x.q, "bf16", x.w, x.w_dec, "bf16", lat, "bf16", None, x.kv_off,
+                                            x.G, x.H, 128, 256, x.k)
+    assert np.array_equal(a, b) and np.array_equal(a_idx, b_idx)
+
+
+def test_equal_block_scales_are_a_row_scale_and_a_block_scale_scales_its_block():
+    x, codes = _fp8_latent_case(42)
+    rng = np.random.default_rng(43)
+    sig = rng.uniform(0.5, 2.0, x.n_tok).astype(np.float32)
+    a = oracle.latent_score_group(x.q, "bf16", x.w, x.w_dec, "bf16", codes, "fp8_e4m3",
+                                  np.stack([sig, sig], 1), x.kv_off, x.G, x.H, 128, 256, x.k, c_blocks=2)[1]
+    b = oracle.latent_score_group(x.q, "bf16", x.w, x.w_dec, "bf16", codes, "fp8_e4m3", sig, x.kv_off,
+                                  x.G, x.H, 128, 256, x.k)[1]
+    assert np.allclose(a, b, rtol=1e-13, atol=0)
+    # a scale of 2 on block 1 equals the latent with block 1's values doubled (exact in bf16)
+    two = np.ones((x.n_tok, 2), np.float32); two[:, 1] = 2.0
+    c = oracle.latent_score_group(x.q, "bf16", x.w, x.w_dec, "bf16", codes, "fp8_e4m3", two, x.kv_off,
+                                  x.G, x.H, 128, 256, x.k, c_blocks=2)[1]
+    v = _fp8_values(codes); v[:, 128:] *= 2
+    d = oracle.latent_score_group(x.q, "bf16", x.w, x.w_dec, "bf16", inputs.encode_bf16(v), "bf16", None,
+                                  x.kv_off, x.G, x.H, 128, 256, x.k)[1]
+    assert np.array_equal(c, d)
+
+
+def test_hs_and_reconstruction_take_block_scales_too():
+    x, codes = _fp8_latent_case(44)
+    rng = np.random.default_rng(45)
+    sc = rng.uniform(0.5, 2.0, (x.n_tok, 2)).astype(np.float32)
+    g = oracle.latent_score_group(x.q, "bf16", x.w, x.w_dec, "bf16", codes, "fp8_e4m3", sc, x.kv_off,
+                                  x.G, x.H, 128, 256, x.k, c_blocks=2)
+    r = oracle.latent_reconstruct_scores(x.q, "bf16", x.w, x.w_dec, "bf16", codes, "fp8_e4m3", sc, x.kv_off,
+                                         x.G, x.H, 128, 256, c_blocks=2)
+    assert np.allclose(g[1], r, rtol=0, atol=1e-9 * np.abs(g[2]).max())
+    cand = np.stack([np.arange(x.k, dtype=np.int32), np.arange(x.k, dtype=np.int32)])
+    hi, hs, _ = oracle.hs_refine(cand, x.q, "bf16", x.w, x.w_dec, "bf16", codes, "fp8_e4m3", sc, x.kv_off, x.G,
+                                 x.H, 128, 256, 10, c_blocks=2)
+    for b in range(2):
+        assert np.allclose(hs[b], g[1][:, x.kv_off[b]:x.kv_off[b] + x.k], rtol=1e-13, atol=0)
