@@ -240,7 +240,17 @@ def components(torch, li, inputs, args):
         "absorb_ms": absorb, "scan_ms": scan, "topk_ms": topk, "total_ms": wall,
         "scan_gbs": lat_bytes / (scan * 1e-3) / 1e9, "scan_hbm_frac": lat_bytes / (scan * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "scan_mfma_frac_bf16": 2 * flop / (scan * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
-    del q, w, wd, lat, off, idx, ws, x
+    # the same group over an fp8 latent with one scale per 128 values (264 B per token)
+    inputs.latent_to_fp8(x)
+    lat8, bsc = dev(torch, x.latent, "fp8_e4m3"), dev(torch, x.c_scale)
+    fn = lambda: li.li_latent_score_group(q, w, wd, lat8, bsc, off, 131072, x.k, out_idx=idx, ws=ws)
+    wall, (absorb, scan, topk) = timed(torch, li, fn, 3, args.comp_iters, 2)
+    lat8_bytes = x.n_tok * (x.Dc + 4 * (x.Dc // 128))
+    out["latent_fp8_G4_B16_L131072"] = {
+        "absorb_ms": absorb, "scan_ms": scan, "topk_ms": topk, "total_ms": wall, "bytes_per_token": x.Dc + 4 * (x.Dc // 128),
+        "scan_gbs": lat8_bytes / (scan * 1e-3) / 1e9, "scan_hbm_frac": lat8_bytes / (scan * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "scan_mfma_frac_fp16": flop / (scan * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+    del q, w, wd, lat, lat8, bsc, off, idx, ws, x
     # ---- HS decode: fp8 anchor top-8192 + 3 latent followers, B = 16, L = 131072 --
     h = inputs.cfg5()
     a, f = h.anchor, h.followers

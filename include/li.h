@@ -160,7 +160,10 @@ size_t li_index_prefill_ws(int32_t T, int32_t L, int32_t k, int32_t has_out_scor
  *
  *   q       [B][G][H][Dh] LI_BF16;  w [B][G][H] fp32
  *   w_dec   [G][Dc][H*Dh] LI_BF16
- *   latent  [n_tok][Dc]   LI_BF16;  c_scale [n_tok] fp32 or NULL (= 1)
+ *   latent  [n_tok][Dc]   LI_BF16 with c_scale [n_tok] fp32 or NULL (= 1), or
+ *           LI_FP8_E4M3 with c_scale [n_tok][Dc/128] fp32 (required): one scale
+ *           per 128-value block; each code times its block's scale is rounded
+ *           once to fp16 for the product (fp16 form only)
  *   kv_off  [B+1] int64, device;  max_len >= every L_b
  *   G >= 1;  H 1..64;  Dh must be 128;  Dc 128 or 256;  1 <= k <= LI_MAX_K
  *   out_idx    [B][G][k]  int32 positions, ascending, -1 padded
@@ -186,7 +189,8 @@ size_t li_latent_score_group_ws(int32_t B, int64_t n_tok, int32_t max_len, int32
  * the valid candidates, and keeps its own top-k among them.
  *
  *   q [B][Gf][H][Dh] LI_BF16; w [B][Gf][H] fp32; w_dec [Gf][Dc][H*Dh] LI_BF16
- *   latent [n_tok][Dc] LI_BF16; c_scale [n_tok] or NULL; kv_off [B+1] int64
+ *   latent [n_tok][Dc] LI_BF16 with c_scale [n_tok] or NULL, or LI_FP8_E4M3 with
+ *   block scales [n_tok][Dc/128] (as in li_latent_score_group); kv_off [B+1] int64
  *   1 <= C <= 65536; Gf >= 1; H 1..64; Dh 128; Dc 128 or 256; 1 <= k <= LI_MAX_K
  *   out_idx    [B][Gf][k] int32 TOKEN positions (taken from cand_idx), ascending, -1 padded
  *   out_scores [B][Gf][C] fp32 score of candidate slot j, or NULL (slots past
@@ -254,6 +258,16 @@ li_status li_sparse_attention(const void* q, li_dtype q_dt, const void* kv, li_d
                               const int64_t* kv_off, int32_t B, int64_t n_tok, int32_t H, int32_t Dk, int32_t Dv,
                               int32_t k, float scale, float* out, void* ws, size_t ws_bytes, void* stream);
 size_t li_sparse_attention_ws(int32_t B, int32_t H, int32_t k);
+
+/* ---------------------------------------------------------------------------
+ * Cache layouts in bytes per token (host only).  A key row of D values
+ * (LI_FP8_E4M3: D bytes + one fp32 scale; LI_BF16: 2*D bytes) and a latent row
+ * of Dc values (LI_FP8_E4M3: Dc bytes + one fp32 scale per started 128-value
+ * block; LI_BF16: 2*Dc bytes).  LatentIndex page, Abstract: the shared latent
+ * replaces per-layer indexer key caches.  0 for a dtype without a layout.
+ * ------------------------------------------------------------------------- */
+size_t li_key_row_bytes(int32_t D, li_dtype dt);
+size_t li_latent_row_bytes(int32_t Dc, li_dtype dt);
 
 /* ---------------------------------------------------------------------------
  * li_indexcache_plan — IndexCache layer roles (host only; no device work).

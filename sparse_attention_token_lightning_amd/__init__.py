@@ -26,7 +26,7 @@ LI_MAX_K = 16384
 # Every symbol include/li.h declares.
 SYMBOLS = ("li_index_decode", "li_index_decode_ws", "li_index_prefill", "li_index_prefill_ws",
            "li_latent_score_group", "li_latent_score_group_ws", "li_hs_refine", "li_hs_refine_ws",
-           "li_latent_append", "li_latent_append_ws", "li_sparse_attention", "li_sparse_attention_ws", "li_indexcache_plan", "li_topk", "li_topk_ws", "li_status_str", "li_last_error", "li_trace_events", "li_trace_count")
+           "li_latent_append", "li_latent_append_ws", "li_sparse_attention", "li_sparse_attention_ws", "li_key_row_bytes", "li_latent_row_bytes", "li_indexcache_plan", "li_topk", "li_topk_ws", "li_status_str", "li_last_error", "li_trace_events", "li_trace_count")
 
 _lib = None
 
@@ -60,6 +60,9 @@ def lib():
         L.li_sparse_attention.argtypes = [vp, i32, vp, i32, vp, vp, i32, i64, i32, i32, i32, i32, C.c_float, vp, vp, sz,
                                           vp]
         L.li_sparse_attention_ws.argtypes = [i32, i32, i32]
+        for f in ("li_key_row_bytes", "li_latent_row_bytes"):
+            getattr(L, f).restype = sz
+            getattr(L, f).argtypes = [i32, i32]
         L.li_indexcache_plan.restype = i32
         L.li_indexcache_plan.argtypes = [vp, i32, i32, vp]
         L.li_topk.argtypes = [vp, i64, vp, i32, i32, i32, vp, vp, sz, vp]

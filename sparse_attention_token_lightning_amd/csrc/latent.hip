@@ -42,6 +42,26 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// Eight OCP E4M3 values (bytes 8*half .. +7 of v), each times `scale`, as
+// fp16 (nearest even).  E4M3 -> bf16 is exact, so the only rounding is the
+// final one of code * scale.
+__device__ __forceinline__ i32x4 fp8x8_scaled_to_f16x8(i32x4 v, int half, float scale) {
+  const int w[2] = {half ? v[2] : v[0], half ? v[3] : v[1]};
+  i32x4 r;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const i32x2 b = fp8x4_to_bf16x4(w[k]);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const uint32_t u = (uint32_t)(m ? b.y : b.x);
+      const _Float16 lo = (_Float16)(__builtin_bit_cast(float, u << 16) * scale);
+      const _Float16 hi = (_Float16)(__builtin_bit_cast(float, u & 0xFFFF0000u) * scale);
+      r[2 * k + m] = (int)((uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16));
+    }
+  }
+  return r;
+}
+
 // split = false: qt16[row] = fp16 of the scaled row.  split = true: qt16[row]
 // = hi, qt16[nrows + row] = lo, two bf16 parts with hi + lo = the scaled row
 // to within 2^-17 of its magnitude (hi is the bf16 rounding, lo that of the
@@ -137,7 +157,7 @@ constexpr int kLsMaxRows = kLsMaxTiles * 32;
 // barriers at different times.  Scores collect in LDS and are written in one
 // burst at the end; the level-0 histograms are 16-bit, packed two bins per
 // word (a workgroup covers at most 2048 rows).
-template <int DC, bool GATHER, bool CSCALE>
+template <int DC, bool GATHER, bool CSCALE, bool F8>
 __global__ __launch_bounds__(kLsThreads, 2) void latent_score_kernel(
     const uint16_t* __restrict__ qt16, const float* __restrict__ wsc,
     const uint16_t* __restrict__ latent, const float* __restrict__ c_scale,
@@ -224,17 +244,31 @@ __global__ __launch_bounds__(kLsThreads, 2) void latent_score_kernel(
     if constexpr (GATHER) return off + cb[s];
     else return off + s;
   };
-  auto gload = [&](i32x4 (&dst)[CPT], int tile) {
+  // F8: the thread's 8*CPT values are 8*CPT fp8 bytes (CPT / 2 loads) inside
+  // one 128-value block, whose scale comes with them.
+  auto gload = [&](i32x4 (&dst)[CPT], float& bsc, int tile) {
     const int t = tile < ntiles ? tile : ntiles - 1;
-    const uint16_t* src = latent + row_of(tok0 + (int64_t)t * 32 + pt) * DC + 8 * CPT * p;
+    const int64_t row = row_of(tok0 + (int64_t)t * 32 + pt);
+    if constexpr (F8) {
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(latent) + row * DC + 8 * CPT * p;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) dst[i] = ld16(src + 8 * i);
+      for (int i = 0; i < CPT / 2; ++i) dst[i] = ld16(src + 16 * i);
+      bsc = c_scale[row * (DC / 128) + 8 * CPT * p / 128];
+    } else {
+      const uint16_t* src = latent + row * DC + 8 * CPT * p;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) dst[i] = ld16(src + 8 * i);
+      bsc = 1.0f;
+    }
   };
-  auto lstore = [&](int slot, const i32x4 (&src)[CPT]) {
+  auto lstore = [&](int slot, const i32x4 (&src)[CPT], float bsc) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = CPT * p + i;
-      ktile[slot][((pt >> 4) * KS + (c >> 2)) * 64 + (c & 3) * 16 + (pt & 15)] = bf16x8_to_f16x8(src[i]);
+      i32x4 v;
+      if constexpr (F8) v = fp8x8_scaled_to_f16x8(src[i >> 1], i & 1, bsc);
+      else v = bf16x8_to_f16x8(src[i]);
+      ktile[slot][((pt >> 4) * KS + (c >> 2)) * 64 + (c & 3) * 16 + (pt & 15)] = v;
     }
   };
   // B operand of row block rb, product s: row 16*rb + c16, dims 32*s + 8*g4 .. +7.
@@ -253,12 +287,13 @@ __global__ __launch_bounds__(kLsThreads, 2) void latent_score_kernel(
   // other slot (whose readers finished tile i-1 before the previous barrier)
   // and loads tile i+3 into the register set tile i+1 had.
   i32x4 gk[2][CPT];
+  float gs[2];
   float skr[2];
-  gload(gk[0], 0);
-  gload(gk[1], 1);
+  gload(gk[0], gs[0], 0);
+  gload(gk[1], gs[1], 1);
   skr[0] = row_scale(0);
-  lstore(0, gk[0]);
-  gload(gk[0], 2);
+  lstore(0, gk[0], gs[0]);
+  gload(gk[0], gs[0], 2);
   __syncthreads();
   const int nsteps = (ntiles + 1) / 2 * 2;
   for (int base = 0; base < nsteps; base += 2) {
@@ -299,8 +334,8 @@ __global__ __launch_bounds__(kLsThreads, 2) void latent_score_kernel(
         __builtin_amdgcn_sched_barrier(0);
         bfrag(st, 1, bk);
       }
-      lstore(st ^ 1, gk[st ^ 1]);
-      gload(gk[st ^ 1], it + 3);
+      lstore(st ^ 1, gk[st ^ 1], gs[st ^ 1]);
+      gload(gk[st ^ 1], gs[st ^ 1], it + 3);
       if (work) {
         __builtin_amdgcn_sched_barrier(0);
         issue(4);
@@ -623,17 +658,32 @@ hipError_t launch_ls2(bool split, int Dc, dim3 grid, hipStream_t stream, const u
                          wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
   }
   if (Dc == 256)
-    return launch_kernel(latent_score_kernel<256, GATHER, CSCALE>, grid, dim3(kLsThreads), 0, stream, qt16, wsc,
-                         latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
-  return launch_kernel(latent_score_kernel<128, GATHER, CSCALE>, grid, dim3(kLsThreads), 0, stream, qt16, wsc,
-                       latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
+    return launch_kernel(latent_score_kernel<256, GATHER, CSCALE, false>, grid, dim3(kLsThreads), 0, stream, qt16,
+                         wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
+  return launch_kernel(latent_score_kernel<128, GATHER, CSCALE, false>, grid, dim3(kLsThreads), 0, stream, qt16,
+                       wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
+}
+
+// fp8 latent (c_scale = its block scales, required): the fp16 form only.
+template <bool GATHER>
+hipError_t launch_ls8(int Dc, dim3 grid, hipStream_t stream, const uint16_t* qt16, const float* wsc,
+                      const uint16_t* latent, const float* c_scale, const int64_t* kv_off, const int32_t* cand, int C,
+                      int64_t n_tok, int G, int H, int tpb, int k, float* scores, const SelWs& sel) {
+  if (Dc == 256)
+    return launch_kernel(latent_score_kernel<256, GATHER, false, true>, grid, dim3(kLsThreads), 0, stream, qt16,
+                         wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
+  return launch_kernel(latent_score_kernel<128, GATHER, false, true>, grid, dim3(kLsThreads), 0, stream, qt16,
+                       wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
 }
 
 template <bool GATHER>
-hipError_t launch_ls(bool split, int Dc, dim3 grid, hipStream_t stream, const uint16_t* qt16,
+hipError_t launch_ls(bool split, bool fp8, int Dc, dim3 grid, hipStream_t stream, const uint16_t* qt16,
                      const uint16_t* qlo, const float* wsc, const uint16_t* latent, const float* c_scale,
                      const int64_t* kv_off, const int32_t* cand, int C, int64_t n_tok, int G, int H, int tpb,
                      int k, float* scores, const SelWs& sel) {
+  if (fp8)
+    return launch_ls8<GATHER>(Dc, grid, stream, qt16, wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k,
+                              scores, sel);
   if (c_scale)
     return launch_ls2<GATHER, true>(split, Dc, grid, stream, qt16, qlo, wsc, latent, c_scale, kv_off, cand, C,
                                     n_tok, G, H, tpb, k, scores, sel);
@@ -655,20 +705,21 @@ hipError_t launch_latent_absorb(const uint16_t* q, const float* w, const uint16_
 hipError_t launch_latent_score(const uint16_t* qt16, const float* wsc, const uint16_t* latent,
                                const float* c_scale, const int64_t* kv_off, int32_t B,
                                int64_t n_tok, int32_t max_len, int32_t G, int32_t H, int32_t Dc,
-                               int32_t k, bool split, float* scores, const SelWs& sel, hipStream_t stream) {
+                               int32_t k, bool split, bool fp8, float* scores, const SelWs& sel,
+                               hipStream_t stream) {
   if (B <= 0 || max_len <= 0) return hipSuccess;
   const int64_t chunk = latent_chunk(n_tok);
   const int64_t tpb = chunk / 32;
   dim3 grid((unsigned)((max_len + chunk - 1) / chunk), (unsigned)B,
             (unsigned)((G + kLsWaves - 1) / kLsWaves));
   const uint16_t* qlo = qt16 + (int64_t)B * G * H * Dc;
-  return launch_ls<false>(split, Dc, grid, stream, qt16, qlo, wsc, latent, c_scale, kv_off, nullptr, 0,
+  return launch_ls<false>(split, fp8, Dc, grid, stream, qt16, qlo, wsc, latent, c_scale, kv_off, nullptr, 0,
                           n_tok, G, H, (int)tpb, k, scores, sel);
 }
 
 hipError_t launch_hs_score(const uint16_t* qt16, const float* wsc, const uint16_t* latent,
                            const float* c_scale, const int64_t* kv_off, const int32_t* cand,
-                           int32_t C, int32_t B, int32_t Gf, int32_t H, int32_t Dc, bool split,
+                           int32_t C, int32_t B, int32_t Gf, int32_t H, int32_t Dc, bool split, bool fp8,
                            float* scores, hipStream_t stream) {
   if (B <= 0 || C <= 0) return hipSuccess;
   int64_t tpb = ((int64_t)B * C) / ((int64_t)512 * 32);
@@ -678,7 +729,7 @@ hipError_t launch_hs_score(const uint16_t* qt16, const float* wsc, const uint16_
             (unsigned)((Gf + kLsWaves - 1) / kLsWaves));
   SelWs none = {};
   const uint16_t* qlo = qt16 + (int64_t)B * Gf * H * Dc;
-  return launch_ls<true>(split, Dc, grid, stream, qt16, qlo, wsc, latent, c_scale, kv_off, cand, C, 0, Gf,
+  return launch_ls<true>(split, fp8, Dc, grid, stream, qt16, qlo, wsc, latent, c_scale, kv_off, cand, C, 0, Gf,
                          H, (int)tpb, 0, scores, none);
 }
 

@@ -326,10 +326,14 @@ li_status li_index_prefill(const void* q, li_dtype q_dt, const float* q_scale, c
   return hip_check(li::launch_topk_self(tr, sel, s), "topk launch", s);
 }
 
-static li_status check_latent_common(li_dtype q_dt, li_dtype w_dt, li_dtype c_dt, int32_t H,
-                                     int32_t Dh, int32_t Dc, uint32_t flags) {
-  if (q_dt != LI_BF16 || w_dt != LI_BF16 || c_dt != LI_BF16)
-    return fail(LI_E_DTYPE, "latent q, w_dec and latent must be LI_BF16");
+static li_status check_latent_common(li_dtype q_dt, li_dtype w_dt, li_dtype c_dt, const float* c_scale,
+                                     int32_t H, int32_t Dh, int32_t Dc, uint32_t flags) {
+  if (q_dt != LI_BF16 || w_dt != LI_BF16 || (c_dt != LI_BF16 && c_dt != LI_FP8_E4M3))
+    return fail(LI_E_DTYPE, "q and w_dec must be LI_BF16, the latent LI_BF16 or LI_FP8_E4M3");
+  if (c_dt == LI_FP8_E4M3 && !c_scale)
+    return fail(LI_E_NULL, "an LI_FP8_E4M3 latent needs its block scales (c_scale [n_tok][Dc/128])");
+  if (c_dt == LI_FP8_E4M3 && flags == LI_LATENT_SPLIT_BF16)
+    return fail(LI_E_UNSUPPORTED, "LI_LATENT_SPLIT_BF16 takes a bf16 latent only");
   li_status st;
   if ((st = check_heads(H, Dh, "Dh"))) return st;
   if (Dc != 128 && Dc != 256) return fail(LI_E_UNSUPPORTED, "Dc must be 128 or 256 (got %d)", Dc);
@@ -354,7 +358,7 @@ li_status li_latent_score_group(const void* q, li_dtype q_dt, const float* w, co
   if (!q || !w || !w_dec || !latent || !kv_off || !out_idx)
     return fail(LI_E_NULL, "q, w, w_dec, latent, kv_off and out_idx are required");
   li_status st;
-  if ((st = check_latent_common(q_dt, w_dt, c_dt, H, Dh, Dc, flags))) return st;
+  if ((st = check_latent_common(q_dt, w_dt, c_dt, c_scale, H, Dh, Dc, flags))) return st;
   if (B < 0 || n_tok < 0 || max_len < 0 || G <= 0)
     return fail(LI_E_SHAPE, "need B, n_tok, max_len >= 0 and G >= 1");
   if ((int64_t)G * n_tok >= (int64_t)1 << 40) return fail(LI_E_UNSUPPORTED, "G * n_tok too large");
@@ -368,8 +372,13 @@ li_status li_latent_score_group(const void* q, li_dtype q_dt, const float* w, co
         li::validate_bf16(q, (int64_t)B * G * H * Dh, li::kBadQ, s);
         li::validate_f32(w, (int64_t)B * G * H, li::kBadW, s);
         li::validate_bf16(w_dec, (int64_t)G * Dc * H * Dh, li::kBadWDec, s);
-        li::validate_bf16(latent, n_tok * Dc, li::kBadLatent, s);
-        li::validate_scales(c_scale, n_tok, li::kBadCScale, s);
+        if (c_dt == LI_FP8_E4M3) {
+          li::validate_fp8(latent, n_tok * Dc, li::kBadLatent, s);
+          li::validate_scales(c_scale, n_tok * (Dc / 128), li::kBadCScale, s);
+        } else {
+          li::validate_bf16(latent, n_tok * Dc, li::kBadLatent, s);
+          li::validate_scales(c_scale, n_tok, li::kBadCScale, s);
+        }
       })))
     return st;
   trace_begin();
@@ -384,7 +393,8 @@ li_status li_latent_score_group(const void* q, li_dtype q_dt, const float* w, co
                       "latent_absorb launch", s)))
     return st;
   if ((st = hip_check(li::launch_latent_score(qt16, wsc, (const uint16_t*)latent, c_scale, kv_off, B,
-                                              n_tok, max_len, G, H, Dc, k, split, scores, sel, s),
+                                              n_tok, max_len, G, H, Dc, k, split, c_dt == LI_FP8_E4M3, scores,
+                                              sel, s),
                       "latent_score launch", s)))
     return st;
   li::TopkRows tr = {};
@@ -415,7 +425,7 @@ li_status li_hs_refine(const int32_t* cand_idx, int32_t C, const void* q, li_dty
   if (!cand_idx || !q || !w || !w_dec || !latent || !kv_off || !out_idx)
     return fail(LI_E_NULL, "cand_idx, q, w, w_dec, latent, kv_off and out_idx are required");
   li_status st;
-  if ((st = check_latent_common(q_dt, w_dt, c_dt, H, Dh, Dc, flags))) return st;
+  if ((st = check_latent_common(q_dt, w_dt, c_dt, c_scale, H, Dh, Dc, flags))) return st;
   if (B < 0 || Gf <= 0 || C <= 0) return fail(LI_E_SHAPE, "need B >= 0, Gf >= 1 and C >= 1");
   if (C > 65536) return fail(LI_E_UNSUPPORTED, "C must be <= 65536 (got %d)", C);
   if ((st = check_k(k))) return st;
@@ -443,7 +453,7 @@ li_status li_hs_refine(const int32_t* cand_idx, int32_t C, const void* q, li_dty
                       "latent_absorb launch", s)))
     return st;
   if ((st = hip_check(li::launch_hs_score(qt16, wsc, (const uint16_t*)latent, c_scale, kv_off,
-                                          cand_idx, C, B, Gf, H, Dc, split, scores, s),
+                                          cand_idx, C, B, Gf, H, Dc, split, c_dt == LI_FP8_E4M3, scores, s),
                       "hs_score launch", s)))
     return st;
   li::TopkRows tr = {};
@@ -526,6 +536,20 @@ li_status li_sparse_attention(const void* q, li_dtype q_dt, const void* kv, li_d
   return hip_check(li::launch_sparse_attention((const uint16_t*)q, (const uint16_t*)kv, idx, kv_off, B, H, k, scale,
                                                o_part, ml_part, out, s),
                    "sparse_attention launch", s);
+}
+
+size_t li_key_row_bytes(int32_t D, li_dtype dt) {
+  if (D <= 0) return 0;
+  if (dt == LI_FP8_E4M3) return (size_t)D + 4;
+  if (dt == LI_BF16) return (size_t)D * 2;
+  return 0;
+}
+
+size_t li_latent_row_bytes(int32_t Dc, li_dtype dt) {
+  if (Dc <= 0) return 0;
+  if (dt == LI_FP8_E4M3) return (size_t)Dc + 4 * (size_t)((Dc + 127) / 128);
+  if (dt == LI_BF16) return (size_t)Dc * 2;
+  return 0;
 }
 
 int32_t li_indexcache_plan(const uint8_t* roles, int32_t n_layers, int32_t retain_every, int32_t* src) {

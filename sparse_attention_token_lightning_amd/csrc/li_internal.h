@@ -100,12 +100,13 @@ hipError_t launch_latent_absorb(const uint16_t* q, const float* w, const uint16_
 hipError_t launch_latent_score(const uint16_t* qt16, const float* wsc, const uint16_t* latent,
                                const float* c_scale, const int64_t* kv_off, int32_t B,
                                int64_t n_tok, int32_t max_len, int32_t G, int32_t H, int32_t Dc,
-                               int32_t k, bool split, float* scores, const SelWs& sel, hipStream_t stream);
+                               int32_t k, bool split, bool fp8, float* scores, const SelWs& sel,
+                               hipStream_t stream);
 
 // HS gather scan: scores[(b*Gf + f)*C + j] for the valid candidates j of b.
 hipError_t launch_hs_score(const uint16_t* qt16, const float* wsc, const uint16_t* latent,
                            const float* c_scale, const int64_t* kv_off, const int32_t* cand,
-                           int32_t C, int32_t B, int32_t Gf, int32_t H, int32_t Dc, bool split,
+                           int32_t C, int32_t B, int32_t Gf, int32_t H, int32_t Dc, bool split, bool fp8,
                            float* scores, hipStream_t stream);
 
 // Latent-cache append: latent[dst[m]] = bf16(sum_i h[m][i] * w_enc[c][i]).

@@ -99,8 +99,8 @@ class Latent:
     q: np.ndarray            # [B][G][H][Dh] bf16 bits
     w: np.ndarray            # [B][G][H] float32
     w_dec: np.ndarray        # [G][Dc][H*Dh] bf16 bits
-    latent: np.ndarray       # [n_tok][Dc] bf16 bits
-    c_scale: Optional[np.ndarray]
+    latent: np.ndarray       # [n_tok][Dc] bf16 bits, or fp8 codes (c_dt "fp8_e4m3")
+    c_scale: Optional[np.ndarray]  # [n_tok] row scales, or [n_tok][Dc/128] block scales (fp8)
     kv_off: np.ndarray
     G: int
     H: int
@@ -119,6 +119,33 @@ class Latent:
     @property
     def n_tok(self):
         return int(self.kv_off[-1])
+
+    @property
+    def c_blocks(self):
+        return 1 if self.c_scale is None or self.c_scale.ndim == 1 else int(self.c_scale.shape[1])
+
+
+def quantize_fp8_blocks(values, block=128):
+    """fp8 storage of a latent: per row, one fp32 scale per `block` values (the
+    block's largest magnitude / 448, or 1 for an all-zero block) and the
+    values / scale as OCP E4M3 codes (round to nearest even)."""
+    v = np.ascontiguousarray(values, dtype=np.float32)
+    n, d = v.shape
+    blocks = v.reshape(n, d // block, block)
+    sc = (np.abs(blocks).max(axis=2) / np.float32(FP8_MAX)).astype(np.float32)
+    sc[sc == 0] = 1.0
+    codes = encode_fp8((blocks / sc[:, :, None]).reshape(n, d))
+    return codes, sc
+
+
+def latent_to_fp8(x):
+    """The same workload with its latent stored as fp8 with 128-value block scales
+    (the bf16 values requantised)."""
+    vals = torch.from_numpy(x.latent.view(np.int16)).view(torch.bfloat16).float().numpy()
+    codes, sc = quantize_fp8_blocks(vals)
+    x.latent, x.c_scale, x.c_dt = codes, sc, "fp8_e4m3"
+    x.name = x.name.replace("latent_", "latent_fp8_") if x.name else x.name
+    return x
 
 
 @dataclass

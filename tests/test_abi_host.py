@@ -216,3 +216,20 @@ def test_indexcache_plan():
         li.li_indexcache_plan(8, 0)
     with pytest.raises(li.LiError):
         li.li_indexcache_plan(3, roles=[0, 1, 1])
+
+
+def test_latentindex_storage_closed_form():
+    """LatentIndex page, Abstract: -61.1% logical indexer-cache storage at G = 4
+    on DeepSeek-V3.2.  With 61 indexed layers (Table 5), layer 0 independent,
+    15 groups of 4, native fp8 keys of 64 + 64 dims with one fp32 scale, and a
+    shared fp8 latent of 64 + 128 dims with one fp32 scale per started
+    128-value block, the saving is 1 - (132 + 15 * 200) / (61 * 132)."""
+    L = li.lib()
+    key = L.li_key_row_bytes(128, li.LI_FP8_E4M3)
+    lat = L.li_latent_row_bytes(64 + 128, li.LI_FP8_E4M3)
+    assert (key, lat) == (132, 200)
+    saving = 1 - (key + 15 * lat) / (61 * key)
+    assert round(saving * 100, 1) == 61.1
+    assert L.li_latent_row_bytes(256, li.LI_FP8_E4M3) == 264 and L.li_latent_row_bytes(256, li.LI_BF16) == 512
+    assert L.li_key_row_bytes(128, li.LI_BF16) == 256 and L.li_key_row_bytes(0, li.LI_BF16) == 0
+    assert L.li_latent_row_bytes(128, li.LI_FP32) == 0

@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 def run_latent(x, with_scores=True, flags=li.LI_LATENT_FP16):
     sc = torch.full((x.G, max(x.n_tok, 1)), float("nan"), dtype=torch.float32, device="cuda") if with_scores else None
-    idx = li.li_latent_score_group(dev(x.q, "bf16"), dev(x.w), dev(x.w_dec, "bf16"), dev(x.latent, "bf16"),
+    idx = li.li_latent_score_group(dev(x.q, "bf16"), dev(x.w), dev(x.w_dec, "bf16"), dev(x.latent, x.c_dt),
                                    dev(x.c_scale), dev(x.kv_off), int(np.diff(x.kv_off).max(initial=0)), x.k,
                                    out_scores=sc, flags=flags)
     torch.cuda.synchronize()
@@ -32,7 +32,7 @@ def latent_parity(x, what, flags=li.LI_LATENT_FP16, tol=TOL):
     print(f"[latent parity] {what} B={x.B} G={x.G} Dc={x.Dc} n_tok={x.n_tok} flags={flags}", flush=True)
     gi, gs = run_latent(x, flags=flags)
     ri, rs, ra = oracle.latent_score_group(x.q, x.q_dt, x.w, x.w_dec, x.w_dt, x.latent, x.c_dt, x.c_scale, x.kv_off,
-                                           x.G, x.H, x.Dh, x.Dc, x.k)
+                                           x.G, x.H, x.Dh, x.Dc, x.k, c_blocks=x.c_blocks)
     print(f"[latent parity] {what}: max |err| / A = {rel_err(gs, rs, ra):.3g}", flush=True)
     check_scores(gs, rs, ra, tol=tol, what=what)
     for b in range(x.B):
@@ -93,7 +93,7 @@ def run_anchor(a):
 def run_followers(cand, f, with_scores=True, flags=li.LI_LATENT_FP16):
     B, C = cand.shape
     sc = torch.full((B, f.G, C), float("nan"), dtype=torch.float32, device="cuda") if with_scores else None
-    idx = li.li_hs_refine(cand, dev(f.q, "bf16"), dev(f.w), dev(f.w_dec, "bf16"), dev(f.latent, "bf16"),
+    idx = li.li_hs_refine(cand, dev(f.q, "bf16"), dev(f.w), dev(f.w_dec, "bf16"), dev(f.latent, f.c_dt),
                           dev(f.c_scale), dev(f.kv_off), f.k, out_scores=sc, flags=flags)
     torch.cuda.synchronize()
     return idx.cpu().numpy(), (sc.cpu().numpy() if with_scores else None)
@@ -117,7 +117,7 @@ def hs_parity(h, what, requests=None, flags=li.LI_LATENT_FP16, tol=TOL):
         # (ii) followers fed the GPU's candidates: scores, own-score top-k, sets
         ri, rs, ra = oracle.hs_refine(cand[b:b + 1], f.q[b:b + 1], f.q_dt, f.w[b:b + 1], f.w_dec, f.w_dt,
                                       f.latent[sl], f.c_dt, None if f.c_scale is None else f.c_scale[sl], one,
-                                      f.G, f.H, f.Dh, f.Dc, f.k)
+                                      f.G, f.H, f.Dh, f.Dc, f.k, c_blocks=f.c_blocks)
         nv = int((cand[b] >= 0).sum())
         print(f"[hs parity] {what} b={b}: max |err| / A = {rel_err(gs[b, :, :nv], rs[0, :, :nv], ra[0, :, :nv]):.3g}",
               flush=True)
@@ -185,3 +185,32 @@ def test_latent_group_split_bf16():
 def test_hs_split_bf16():
     hs_parity(inputs.make_hs(411, [9000, 3000, 500, 0], C=4096, Gf=3, k=1024), "split",
               flags=li.LI_LATENT_SPLIT_BF16, tol=SPLIT_TOL)
+
+
+def test_latent_group_fp8_block_scales():
+    # fp8 latent with one scale per 128 values, decoded exactly and scaled into fp16
+    latent_parity(inputs.latent_to_fp8(inputs.make_latent(321, [3000, 0, 77, 1025], G=4, k=512)), "fp8 G4 Dc256")
+    latent_parity(inputs.latent_to_fp8(inputs.make_latent(322, [2000, 500], G=3, Dc=128, k=256)), "fp8 G3 Dc128")
+
+
+def test_hs_fp8_followers():
+    h = inputs.make_hs(323, [9000, 3000, 500], C=2048, Gf=3, k=512)
+    inputs.latent_to_fp8(h.followers)
+    hs_parity(h, "HS fp8 followers")
+
+
+def test_latent_group_fp8_long_rows():
+    # rows longer than one scan segment, so the segmented top-k runs
+    x = inputs.latent_to_fp8(inputs.make_latent(324, [40000, 9000], G=4, k=2048))
+    latent_parity(x, "fp8 G4 L40000")
+
+
+def test_latent_fp8_rejects_missing_scales_and_the_split_form():
+    x = inputs.latent_to_fp8(inputs.make_latent(325, [500], G=2, k=64))
+    args = (dev(x.q, "bf16"), dev(x.w), dev(x.w_dec, "bf16"), dev(x.latent, x.c_dt))
+    with pytest.raises(li.LiError) as e:
+        li.li_latent_score_group(*args, None, dev(x.kv_off), 500, x.k)
+    assert e.value.status == li.LI_E_NULL
+    with pytest.raises(li.LiError) as e:
+        li.li_latent_score_group(*args, dev(x.c_scale), dev(x.kv_off), 500, x.k, flags=li.LI_LATENT_SPLIT_BF16)
+    assert e.value.status == li.LI_E_UNSUPPORTED
