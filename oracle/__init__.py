@@ -39,7 +39,9 @@ def lib():
         _lib.oracle_latent_score_group.argtypes = [vp, i32, vp, vp, i32, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, i32, vp, dp, dp]
         _lib.oracle_latent_reconstruct_scores.argtypes = [vp, i32, vp, vp, i32, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, dp]
         _lib.oracle_hs_refine.argtypes = [vp, i32, vp, i32, vp, vp, i32, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, i32, vp, dp, dp]
-        _lib.oracle_latent_append.argtypes = [vp, i32, vp, i32, vp, i32, i32, i32, vp, i64, dp]
+        _lib.oracle_latent_append.argtypes = [vp, i32, vp, i32, vp, i32, i32, i32, vp, i32, vp, i64, dp]
+        _lib.oracle_encode_e4m3.restype = C.c_uint8
+        _lib.oracle_encode_e4m3.argtypes = [C.c_double]
         _lib.oracle_sparse_attention.argtypes = [vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, C.c_double, dp, dp]
         _lib.oracle_encode_bf16.restype = C.c_uint16
         _lib.oracle_encode_bf16.argtypes = [C.c_double]
@@ -177,22 +179,32 @@ def encode_bf16(v):
     return int(lib().oracle_encode_bf16(float(v)))
 
 
-def latent_append(h, h_dt, w_enc, w_dt, dst_row, latent):
+def encode_e4m3(v):
+    """The OCP E4M3FN code (uint8) nearest to float v, ties to even, saturating at 448."""
+    return int(lib().oracle_encode_e4m3(float(v)))
+
+
+def latent_append(h, h_dt, w_enc, w_dt, dst_row, latent, c_scale=None):
     """Latent-cache append: c[b][d] = sum_i h[b][i] * w_enc[d][i] (fp64), stored
-    as bf16 (nearest, ties to even) at row dst_row[b] of a copy of `latent`
-    ([n_tok][Dc] raw bf16).  Returns (new latent, exact sums [B][Dc])."""
+    at row dst_row[b] of a copy of `latent`: [n_tok][Dc] raw bf16 (uint16), or
+    with c_scale ([n_tok][Dc/128] float32) E4M3 codes (uint8) with per-block
+    scales.  Returns (new latent, exact sums [B][Dc]) or, for fp8,
+    (new latent, new scales, exact sums)."""
     h = _arr(h, h_dt)
     w_enc = _arr(w_enc, w_dt)
     B, d_model = h.shape
     Dc = w_enc.shape[0]
     assert w_enc.shape == (Dc, d_model)
-    out = np.array(_arr(latent, "bf16"), copy=True)
+    fp8 = c_scale is not None
+    out = np.array(latent, dtype=np.uint8 if fp8 else np.uint16, copy=True)
+    sc = np.array(c_scale, dtype=np.float32, copy=True) if fp8 else None
     n_tok = out.shape[0]
     dst = np.ascontiguousarray(dst_row, dtype=np.int64)
     exact = np.zeros((B, Dc), np.float64)
     _check(lib().oracle_latent_append(_p(h), _CODES[h_dt], _p(w_enc), _CODES[w_dt], _p(dst), B, d_model, Dc,
-                                      _p(out), n_tok, _p(exact)), "oracle_latent_append")
-    return out, exact
+                                      _p(out), _CODES["fp8_e4m3" if fp8 else "bf16"], _p(sc), n_tok, _p(exact)),
+           "oracle_latent_append")
+    return (out, sc, exact) if fp8 else (out, exact)
 
 
 def sparse_attention(q, q_dt, kv, kv_dt, idx, kv_off, scale, Dv):

@@ -515,22 +515,71 @@ static uint16_t enc_bf16_rne(double v) {
   return (uint16_t)(sgn | (uint16_t)(biased << 7) | (uint16_t)((int)s - 128));
 }
 
+/* OCP E4M3FN code nearest to a finite value, ties to the even code, values
+ * beyond the largest finite (448 = 1.75 * 2^8) saturated to it.  A normal
+ * value is (8 + m)/8 * 2^e with e in [-6, 8] and m in 0..7 (the code
+ * S.1111.111 is NaN, so m <= 6 at e = 8); below 2^-6 the spacing is 2^-9. */
+static uint8_t enc_e4m3_rne(double v) {
+  uint8_t sgn = signbit(v) ? 0x80u : 0u;
+  double a = fabs(v);
+  if (a >= 464.0) return (uint8_t)(sgn | 0x7Eu); /* 464 is the tie 448|480: even is 448 */
+  if (a < ldexp(1.0, -6)) return (uint8_t)(sgn | (uint8_t)rint(ldexp(a, 9))); /* 8 -> 2^-6, code 0x08 */
+  int e;
+  double m = frexp(a, &e); /* a = m * 2^e, m in [0.5, 1) */
+  double s = rint(ldexp(m, 4)); /* 4 significant bits: [8, 16] */
+  if (s == 16.0) {
+    s = 8.0;
+    e += 1;
+  }
+  int biased = (e - 1) + 7;
+  return (uint8_t)(sgn | (uint8_t)(biased << 3) | (uint8_t)((int)s - 8));
+}
+
+/* Latent-cache append.  c_dt OR_BF16: latent [n_tok][Dc] bf16 codes (uint16).
+ * c_dt OR_FP8_E4M3: latent [n_tok][Dc] E4M3 codes (uint8) and c_scale
+ * [n_tok][Dc/128]: each 128-value block of a row is the exact sum rounded to
+ * fp32, its scale the block's largest magnitude / 448 in fp32 (1 for an
+ * all-zero block) and its codes E4M3 of (value / scale) taken in fp32, nearest
+ * even, saturating: the quantisation steps in the precision of the kernel that
+ * takes them (fp32 sums, divisions and maxima). */
 int oracle_latent_append(const void* h, int h_dt, const void* w_enc, int w_dt, const int64_t* dst_row, int B,
-                         int d_model, int Dc, uint16_t* latent, int64_t n_tok, double* exact) {
+                         int d_model, int Dc, void* latent, int c_dt, float* c_scale, int64_t n_tok, double* exact) {
   if (!dt_ok(h_dt) || !dt_ok(w_dt) || B < 0 || d_model <= 0 || Dc <= 0) return -1;
+  if (c_dt != OR_BF16 && !(c_dt == OR_FP8_E4M3 && Dc % 128 == 0 && c_scale)) return -1;
   for (int b = 0; b < B; ++b)
     if (dst_row[b] < 0 || dst_row[b] >= n_tok) return -1;
+  double* row = (double*)malloc(sizeof(double) * (size_t)Dc);
+  if (!row) return -2;
   for (int b = 0; b < B; ++b) {
     for (int d = 0; d < Dc; ++d) {
       double acc = 0.0;
       for (int i = 0; i < d_model; ++i)
         acc += dec_at(h, h_dt, (int64_t)b * d_model + i) * dec_at(w_enc, w_dt, (int64_t)d * d_model + i);
       if (exact) exact[(int64_t)b * Dc + d] = acc;
-      latent[dst_row[b] * Dc + d] = enc_bf16_rne(acc);
+      row[d] = acc;
+    }
+    if (c_dt == OR_BF16) {
+      for (int d = 0; d < Dc; ++d) ((uint16_t*)latent)[dst_row[b] * Dc + d] = enc_bf16_rne(row[d]);
+      continue;
+    }
+    for (int blk = 0; blk < Dc / 128; ++blk) {
+      float amax = 0.0f;
+      for (int d = 128 * blk; d < 128 * blk + 128; ++d) {
+        const float f = fabsf((float)row[d]);
+        if (f > amax) amax = f;
+      }
+      const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+      c_scale[dst_row[b] * (Dc / 128) + blk] = sc;
+      for (int d = 128 * blk; d < 128 * blk + 128; ++d)
+        ((uint8_t*)latent)[dst_row[b] * Dc + d] = enc_e4m3_rne((double)((float)row[d] / sc));
     }
   }
+  free(row);
   return 0;
 }
+
+/* Exported so that tests can pin the E4M3 encoder on its own. */
+uint8_t oracle_encode_e4m3(double v) { return enc_e4m3_rne(v); }
 
 /* Exported so that tests can pin the bfloat16 encoder on its own. */
 uint16_t oracle_encode_bf16(double v) { return enc_bf16_rne(v); }

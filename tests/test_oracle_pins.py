@@ -550,3 +550,48 @@ def test_hs_and_reconstruction_take_block_scales_too():
                                  x.H, 128, 256, 10, c_blocks=2)
     for b in range(2):
         assert np.allclose(hs[b], g[1][:, x.kv_off[b]:x.kv_off[b] + x.k], rtol=1e-13, atol=0)
+
+
+def test_e4m3_encoder_matches_format_points_and_library_cast():
+    enc = oracle.encode_e4m3
+    assert enc(1.0) == 0x38 and enc(-2.0) == 0xC0 and enc(448.0) == 0x7E
+    assert enc(463.9) == 0x7E and enc(464.0) == 0x7E and enc(500.0) == 0x7E and enc(-1e6) == 0xFE  # saturating
+    assert enc(2.0 ** -9) == 0x01 and enc(0.5 * 2.0 ** -9) == 0x00 and enc(1.5 * 2.0 ** -9) == 0x02
+    assert enc(2.0 ** -6) == 0x08 and enc(0.0) == 0x00 and enc(-0.0) == 0x80
+    assert enc(1.0625) == 0x38 and enc(1.1875) == 0x3A  # ties 1|1.125 -> 1, 1.125|1.25 -> 1.25
+    rng = np.random.default_rng(12)
+    vals = np.concatenate([rng.uniform(-448, 448, 4000), rng.standard_normal(3000) * 10.0 ** rng.integers(-4, 2, 3000),
+                           np.arange(-448, 449, 0.25)]).astype(np.float32)
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([enc(float(v)) for v in vals], dtype=np.uint8)
+    assert np.array_equal(got, ref)
+
+
+def test_latent_append_fp8_identity_encoder_is_the_block_quantisation_of_h():
+    rng = np.random.default_rng(24)
+    B, d = 3, 256
+    hv = (rng.standard_normal((B, d)) * np.exp(rng.uniform(-3, 3, (B, 1)))).astype(np.float32)
+    h = _bf16_codes(hv)
+    eye = _bf16_codes(np.eye(d))
+    dst = np.array([2, 0, 1], np.int64)
+    out, sc, _ = oracle.latent_append(h, "bf16", eye, "bf16", dst, np.zeros((3, d), np.uint8),
+                                      c_scale=np.zeros((3, 2), np.float32))
+    vals = torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).float().numpy()
+    codes, scales = inputs.quantize_fp8_blocks(vals)   # independent: numpy fp32 + torch's E4M3 cast
+    assert np.array_equal(out[dst], codes) and np.array_equal(sc[dst], scales)
+
+
+def test_latent_append_fp8_integer_sums_quantise_in_fp32():
+    rng = np.random.default_rng(25)
+    B, d_model, Dc = 4, 192, 256
+    h = rng.integers(-3, 4, size=(B, d_model))
+    w = rng.integers(-3, 4, size=(Dc, d_model))
+    c = (h @ w.T).astype(np.float32)                   # exact integers
+    out, sc, exact = oracle.latent_append(_bf16_codes(h), "bf16", _bf16_codes(w), "bf16", np.arange(B),
+                                          np.zeros((B, Dc), np.uint8), c_scale=np.zeros((B, 2), np.float32))
+    assert np.array_equal(exact, c.astype(np.float64))
+    amax = np.abs(c.reshape(B, 2, 128)).max(axis=2)
+    want_sc = np.where(amax > 0, amax / np.float32(448), np.float32(1)).astype(np.float32)
+    assert np.array_equal(sc, want_sc)
+    q = (c.reshape(B, 2, 128) / want_sc[:, :, None]).astype(np.float32).reshape(B, Dc)
+    assert np.array_equal(out, torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
