@@ -307,7 +307,7 @@ def components(torch, li, inputs, args):
         srcs = [(dev(torch, x.h, "bf16"), dev(torch, x.w_enc, "bf16")) for _ in range(APPEND_COPIES)]
         dst = dev(torch, x.dst_row)
         lat = torch.zeros((x.n_tok, x.Dc), dtype=torch.bfloat16, device="cuda")
-        ws = torch.empty(L.li_latent_append_ws(x.M, x.d_model, x.Dc), dtype=torch.uint8, device="cuda")
+        ws = torch.empty(L.li_latent_append_ws(x.M, x.d_model, x.Dc, li.LI_BF16), dtype=torch.uint8, device="cuda")
         turn = [0]
 
         def fn():
@@ -319,7 +319,7 @@ def components(torch, li, inputs, args):
         flop = 2.0 * x.M * x.Dc * x.d_model
         t = (gemm + red) * 1e-3
         out[x.name] = {
-            "gemm_ms": gemm, "reduce_ms": red, "total_ms": wall, "splits": L.li_latent_append_ws(x.M, x.d_model, x.Dc)
+            "gemm_ms": gemm, "reduce_ms": red, "total_ms": wall, "splits": L.li_latent_append_ws(x.M, x.d_model, x.Dc, li.LI_BF16)
             // max(1, x.M * x.Dc * 4), "algorithmic_bytes": nbytes,
             "gbs": nbytes / t / 1e9, "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBS,
             "tflops": flop / t / 1e12, "mfma_frac_bf16": flop / t / 1e12 / BF16_PEAK_TFLOPS}

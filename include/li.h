@@ -220,16 +220,22 @@ size_t li_hs_refine_ws(int32_t B, int32_t C, int32_t Gf, int32_t H, int32_t Dc, 
  *   dst_row [M] int64, device; each in [0, n_tok) and all distinct (a repeated
  *           row's contents are unspecified; the range is checked only under
  *           LI_DEBUG_VALIDATE)
- *   latent  [n_tok][Dc]   LI_BF16, written in place; other rows are untouched
+ *   latent  [n_tok][Dc], written in place at the dst rows (other rows untouched):
+ *           c_dt LI_BF16: bf16 (nearest even; c_scale unused, may be NULL);
+ *           c_dt LI_FP8_E4M3: E4M3 codes, with c_scale [n_tok][Dc/128] fp32 written
+ *           too: per 128-value block of a row, scale = the block's largest
+ *           magnitude / 448 (1 for an all-zero block) and codes = E4M3 of
+ *           value / scale, nearest even, saturating; all in fp32.  This is the
+ *           fp8 latent li_latent_score_group and li_hs_refine read.
  *   M >= 0 (M = 0 does nothing; h and dst_row may then be NULL);
  *   d_model a positive multiple of 64;  Dc 128 or 256
- *   ws      li_latent_append_ws(M, d_model, Dc) bytes (fp32 partial sums of
- *           the K split; 0 when one split covers K)
+ *   ws      li_latent_append_ws(M, d_model, Dc, c_dt) bytes (fp32 partial sums
+ *           of the K split; 0 for bf16 output when one split covers K)
  * ------------------------------------------------------------------------- */
 li_status li_latent_append(const void* h, li_dtype h_dt, const void* w_enc, li_dtype w_dt,
                            const int64_t* dst_row, int32_t M, int32_t d_model, int32_t Dc, void* latent,
-                           int64_t n_tok, void* ws, size_t ws_bytes, void* stream);
-size_t li_latent_append_ws(int32_t M, int32_t d_model, int32_t Dc);
+                           li_dtype c_dt, float* c_scale, int64_t n_tok, void* ws, size_t ws_bytes, void* stream);
+size_t li_latent_append_ws(int32_t M, int32_t d_model, int32_t Dc, li_dtype c_dt);
 
 /* ---------------------------------------------------------------------------
  * li_sparse_attention — the consumer of a selection: each request's heads

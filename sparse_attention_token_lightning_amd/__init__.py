@@ -55,8 +55,8 @@ def lib():
         L.li_hs_refine.argtypes = [vp, i32, vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, vp,
                                    vp, u32, vp, sz, vp]
         L.li_hs_refine_ws.argtypes = [i32, i32, i32, i32, i32, i32, i32]
-        L.li_latent_append.argtypes = [vp, i32, vp, i32, vp, i32, i32, i32, vp, i64, vp, sz, vp]
-        L.li_latent_append_ws.argtypes = [i32, i32, i32]
+        L.li_latent_append.argtypes = [vp, i32, vp, i32, vp, i32, i32, i32, vp, i32, vp, i64, vp, sz, vp]
+        L.li_latent_append_ws.argtypes = [i32, i32, i32, i32]
         L.li_sparse_attention.argtypes = [vp, i32, vp, i32, vp, vp, i32, i64, i32, i32, i32, i32, C.c_float, vp, vp, sz,
                                           vp]
         L.li_sparse_attention_ws.argtypes = [i32, i32, i32]
@@ -195,18 +195,20 @@ def li_hs_refine(cand_idx, q, w, w_dec, latent, c_scale, kv_off, k, out_idx=None
     return out_idx
 
 
-def li_latent_append(h, w_enc, dst_row, latent, ws=None, stream=None):
-    """Latent-cache append: latent[dst_row[m]] = bf16(w_enc @ h[m]) in place.
-    h [M,d_model] bf16, w_enc [Dc,d_model] bf16, dst_row [M] int64,
-    latent [n_tok,Dc] bf16.  Returns latent."""
+def li_latent_append(h, w_enc, dst_row, latent, c_scale=None, ws=None, stream=None):
+    """Latent-cache append: latent[dst_row[m]] = quantised(w_enc @ h[m]) in place.
+    h [M,d_model] bf16, w_enc [Dc,d_model] bf16, dst_row [M] int64, latent
+    [n_tok,Dc] bf16, or float8_e4m3fn with c_scale [n_tok,Dc/128] fp32 (block
+    scales, written too).  Returns latent."""
     M, d_model = h.shape
     Dc = w_enc.shape[0]
     n_tok = latent.shape[0]
     L = lib()
-    need = L.li_latent_append_ws(M, d_model, Dc)
+    c_dt = _dt(latent)
+    need = L.li_latent_append_ws(M, d_model, Dc, c_dt)
     wst, wsb = _workspace(need, latent.device, ws)
     _check(L.li_latent_append(_ptr(h), _dt(h), _ptr(w_enc), _dt(w_enc), _ptr(dst_row), M, d_model, Dc, _ptr(latent),
-                              n_tok, _ptr(wst), wsb, _stream(stream)))
+                              c_dt, _ptr(c_scale), n_tok, _ptr(wst), wsb, _stream(stream)))
     return latent
 
 

@@ -37,6 +37,26 @@ __device__ __forceinline__ uint16_t bf16_rne(float v) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// OCP E4M3FN code of a finite fp32 value: nearest, ties to even, saturated at
+// 448 (the codes past it are NaN).  Normal range: the fp32 mantissa rounded to
+// 3 bits (a carry moves into the exponent), exponent rebiased 127 -> 7; below
+// 2^-6 the spacing is 2^-9.
+__device__ __forceinline__ uint32_t e4m3_rne(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const uint32_t sgn = (u >> 24) & 0x80u;
+  const float a = fabsf(x);
+  uint32_t code;
+  if (a >= 464.f) {
+    code = 0x7Eu;  // 464 is the tie between 448 and 480: 448 is the even one
+  } else if (a < 0.015625f) {
+    code = (uint32_t)rintf(a * 512.f);  // 8 gives 0x08, the smallest normal
+  } else {
+    const uint32_t au = u & 0x7FFFFFFFu;
+    code = ((au + 0x7FFFFu + ((au >> 20) & 1u)) >> 20) - (120u << 3);
+  }
+  return sgn | code;
+}
+
 // LDS holds each K step's tiles in MFMA fragment order: slot
 // ((t * 2 + ks) * 64 + lane) is the 16 bytes that `lane` feeds to the MFMA of
 // 16-row tile t and K block ks: row t*16 + (lane & 15), K elements
@@ -194,10 +214,13 @@ __global__ __launch_bounds__(kApThreads, 1) void append_gemm_kernel(
 // ... in increasing order for four consecutive columns of its row, and thread
 // (r, 0, quad) then adds the G group sums in order g = 0 .. G-1.  The order
 // depends only on S and G, never on scheduling.
-template <int DC>
+// F8: the row is stored as E4M3 codes with one fp32 scale per 128 values
+// (the block's largest magnitude / 448, or 1 for an all-zero block); a block
+// is 32 quads held by 32 consecutive lanes.
+template <int DC, bool F8>
 __global__ __launch_bounds__(1024) void append_reduce_kernel(const float* __restrict__ part, int32_t S, int32_t G,
                                                              int32_t M, const int64_t* __restrict__ dst,
-                                                             uint16_t* __restrict__ latent) {
+                                                             uint16_t* __restrict__ latent, float* __restrict__ c_scale) {
   constexpr int QD = DC / 4;
   __shared__ f32x4 red[1024];
   const int tid = threadIdx.x;
@@ -234,10 +257,23 @@ __global__ __launch_bounds__(1024) void append_reduce_kernel(const float* __rest
       for (int e = 0; e < 4; ++e) v[e] += u[e];
     }
   }
-  if (!live) return;
-  const uint32_t lo = (uint32_t)bf16_rne(v[0]) | ((uint32_t)bf16_rne(v[1]) << 16);
-  const uint32_t hi = (uint32_t)bf16_rne(v[2]) | ((uint32_t)bf16_rne(v[3]) << 16);
-  *reinterpret_cast<i32x2*>(latent + dst[row] * DC + 4 * q) = i32x2{(int)lo, (int)hi};
+  if (!live) return;  // uniform over each row's lanes
+  if constexpr (F8) {
+    float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+    const float sc = am > 0.f ? am / 448.f : 1.f;
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) word |= e4m3_rne(v[e] / sc) << (8 * e);
+    const int64_t r = dst[row];
+    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(latent) + r * DC + 4 * q) = word;
+    if ((q & 31) == 0) c_scale[r * (DC / 128) + q / 32] = sc;
+  } else {
+    const uint32_t lo = (uint32_t)bf16_rne(v[0]) | ((uint32_t)bf16_rne(v[1]) << 16);
+    const uint32_t hi = (uint32_t)bf16_rne(v[2]) | ((uint32_t)bf16_rne(v[3]) << 16);
+    *reinterpret_cast<i32x2*>(latent + dst[row] * DC + 4 * q) = i32x2{(int)lo, (int)hi};
+  }
 }
 
 }  // namespace
@@ -254,13 +290,14 @@ int32_t append_splits(int32_t M, int32_t d_model) {
 }
 
 hipError_t launch_latent_append(const uint16_t* h, const uint16_t* w_enc, const int64_t* dst, int32_t M,
-                                int32_t d_model, int32_t Dc, float* part, uint16_t* latent, hipStream_t stream) {
+                                int32_t d_model, int32_t Dc, float* part, uint16_t* latent, bool fp8, float* c_scale,
+                                hipStream_t stream) {
   constexpr int D = kApDepth;
   const int32_t S = append_splits(M, d_model);
   const int32_t nsteps = d_model / kApK;
   const int32_t per = (nsteps + S - 1) / S;
   const dim3 grid((unsigned)((M + kApRows - 1) / kApRows), (unsigned)S);
-  float* p = S > 1 ? part : nullptr;
+  float* p = S > 1 || fp8 ? part : nullptr;  // fp8 output always goes through the split sum
   hipError_t e;
   if (Dc == 256)
     e = launch_kernel(append_gemm_kernel<256, D>, grid, dim3(kApThreads), 0, stream, h, w_enc, dst, M, d_model, per,
@@ -268,7 +305,7 @@ hipError_t launch_latent_append(const uint16_t* h, const uint16_t* w_enc, const 
   else
     e = launch_kernel(append_gemm_kernel<128, D>, grid, dim3(kApThreads), 0, stream, h, w_enc, dst, M, d_model, per,
                       p, latent);
-  if (e != hipSuccess || S == 1) return e;
+  if (e != hipSuccess || !p) return e;
   // G split groups per row, each summing at most eight splits (G <= 16); a
   // workgroup holds 256 threads or one row's Dc/4 * G, whichever is larger.
   int32_t G = 1;
@@ -276,10 +313,17 @@ hipError_t launch_latent_append(const uint16_t* h, const uint16_t* w_enc, const 
   const int32_t per_row = Dc / 4 * G;
   const int32_t rows = per_row >= 256 ? 1 : 256 / per_row;
   const dim3 grid_r((unsigned)((M + rows - 1) / rows)), block_r((unsigned)(rows * per_row));
+  const float* cp = part;
+  if (fp8) {
+    if (Dc == 256)
+      return launch_kernel(append_reduce_kernel<256, true>, grid_r, block_r, 0, stream, cp, S, G, M, dst, latent,
+                           c_scale);
+    return launch_kernel(append_reduce_kernel<128, true>, grid_r, block_r, 0, stream, cp, S, G, M, dst, latent, c_scale);
+  }
   if (Dc == 256)
-    return launch_kernel(append_reduce_kernel<256>, grid_r, block_r, 0, stream, (const float*)part, S, G, M, dst,
-                         latent);
-  return launch_kernel(append_reduce_kernel<128>, grid_r, block_r, 0, stream, (const float*)part, S, G, M, dst, latent);
+    return launch_kernel(append_reduce_kernel<256, false>, grid_r, block_r, 0, stream, cp, S, G, M, dst, latent,
+                         c_scale);
+  return launch_kernel(append_reduce_kernel<128, false>, grid_r, block_r, 0, stream, cp, S, G, M, dst, latent, c_scale);
 }
 
 }  // namespace li

@@ -468,24 +468,26 @@ li_status li_hs_refine(const int32_t* cand_idx, int32_t C, const void* q, li_dty
   return hip_check(li::launch_topk(tr, s), "topk launch", s);
 }
 
-size_t li_latent_append_ws(int32_t M, int32_t d_model, int32_t Dc) {
+size_t li_latent_append_ws(int32_t M, int32_t d_model, int32_t Dc, li_dtype c_dt) {
   if (M <= 0 || d_model < 64 || d_model % 64 != 0 || (Dc != 128 && Dc != 256)) return 0;
   const int32_t S = li::append_splits(M, d_model);
-  return S > 1 ? align_up((size_t)S * M * Dc * 4) : 0;
+  return S > 1 || c_dt == LI_FP8_E4M3 ? align_up((size_t)S * M * Dc * 4) : 0;
 }
 
 li_status li_latent_append(const void* h, li_dtype h_dt, const void* w_enc, li_dtype w_dt,
                            const int64_t* dst_row, int32_t M, int32_t d_model, int32_t Dc, void* latent,
-                           int64_t n_tok, void* ws, size_t ws_bytes, void* stream) {
+                           li_dtype c_dt, float* c_scale, int64_t n_tok, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
   if (!w_enc || !latent) return fail(LI_E_NULL, "w_enc and latent are required");
   if (M > 0 && (!h || !dst_row)) return fail(LI_E_NULL, "h and dst_row are required when M > 0");
   if (h_dt != LI_BF16 || w_dt != LI_BF16) return fail(LI_E_DTYPE, "h and w_enc must be LI_BF16");
+  if (c_dt != LI_BF16 && c_dt != LI_FP8_E4M3) return fail(LI_E_DTYPE, "the latent must be LI_BF16 or LI_FP8_E4M3");
+  if (c_dt == LI_FP8_E4M3 && !c_scale) return fail(LI_E_NULL, "an LI_FP8_E4M3 latent needs c_scale [n_tok][Dc/128]");
   if (M < 0 || d_model <= 0 || n_tok <= 0) return fail(LI_E_SHAPE, "need M >= 0, d_model >= 1 and n_tok >= 1");
   if (d_model % 64 != 0) return fail(LI_E_UNSUPPORTED, "d_model must be a multiple of 64 (got %d)", d_model);
   if (Dc != 128 && Dc != 256) return fail(LI_E_UNSUPPORTED, "Dc must be 128 or 256 (got %d)", Dc);
   li_status st;
-  if ((st = check_ws(ws, ws_bytes, li_latent_append_ws(M, d_model, Dc)))) return st;
+  if ((st = check_ws(ws, ws_bytes, li_latent_append_ws(M, d_model, Dc, c_dt)))) return st;
   if (M == 0) return LI_OK;
   hipStream_t s = (hipStream_t)stream;
   if (validate_on() && (st = run_validation(s, [&] {
@@ -496,7 +498,7 @@ li_status li_latent_append(const void* h, li_dtype h_dt, const void* w_enc, li_d
     return st;
   trace_begin();
   return hip_check(li::launch_latent_append((const uint16_t*)h, (const uint16_t*)w_enc, dst_row, M, d_model, Dc,
-                                            (float*)ws, (uint16_t*)latent, s),
+                                            (float*)ws, (uint16_t*)latent, c_dt == LI_FP8_E4M3, c_scale, s),
                    "latent_append launch", s);
 }
 

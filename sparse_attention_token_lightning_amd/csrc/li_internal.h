@@ -111,7 +111,7 @@ hipError_t launch_hs_score(const uint16_t* qt16, const float* wsc, const uint16_
 
 // Latent-cache append: latent[dst[m]] = bf16(sum_i h[m][i] * w_enc[c][i]).
 // K is split over append_splits(M, d_model) workgroups; with more than one
-// split, `part` ([S][M][Dc] fp32) holds the partial sums.
+// split (and always for fp8 output), `part` ([S][M][Dc] fp32) holds the partial sums.
 int32_t append_splits(int32_t M, int32_t d_model);
 
 // Sparse attention over selected rows (Dk = 576, Dv = 512, H a multiple of
@@ -122,7 +122,8 @@ hipError_t launch_sparse_attention(const uint16_t* q, const uint16_t* kv, const 
                                    int32_t B, int32_t H, int32_t K, float scale, float* o_part, float* ml_part,
                                    float* out, hipStream_t stream);
 hipError_t launch_latent_append(const uint16_t* h, const uint16_t* w_enc, const int64_t* dst, int32_t M,
-                                int32_t d_model, int32_t Dc, float* part, uint16_t* latent, hipStream_t stream);
+                                int32_t d_model, int32_t Dc, float* part, uint16_t* latent, bool fp8, float* c_scale,
+                                hipStream_t stream);
 
 // Opt-in input checks (LI_DEBUG_VALIDATE): validate_begin clears the device
 // record, the validate_* calls enqueue one check each, validate_end waits for

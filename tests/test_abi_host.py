@@ -173,13 +173,15 @@ def test_latent_append_validation_and_workspace():
 
     def ap(**kw):
         a = dict(h=FAKE, h_dt=li.LI_BF16, w=FAKE, w_dt=li.LI_BF16, dst=FAKE, M=4096, d=7168, Dc=256, lat=FAKE,
-                 n_tok=1 << 17, ws=FAKE, wsb=1 << 34)
+                 c_dt=li.LI_BF16, sc=None, n_tok=1 << 17, ws=FAKE, wsb=1 << 34)
         a.update(kw)
         return L.li_latent_append(a["h"], a["h_dt"], a["w"], a["w_dt"], a["dst"], a["M"], a["d"], a["Dc"], a["lat"],
-                                  a["n_tok"], a["ws"], a["wsb"], None)
+                                  a["c_dt"], a["sc"], a["n_tok"], a["ws"], a["wsb"], None)
 
     assert ap(h=None) == li.LI_E_NULL and ap(dst=None) == li.LI_E_NULL and ap(lat=None) == li.LI_E_NULL
     assert ap(h_dt=li.LI_FP8_E4M3) == li.LI_E_DTYPE and ap(w_dt=li.LI_FP32) == li.LI_E_DTYPE
+    assert ap(c_dt=li.LI_FP16) == li.LI_E_DTYPE
+    assert ap(c_dt=li.LI_FP8_E4M3) == li.LI_E_NULL  # fp8 output needs its block scales
     assert ap(M=-1) == li.LI_E_SHAPE and ap(d=0) == li.LI_E_SHAPE and ap(n_tok=0) == li.LI_E_SHAPE
     assert ap(d=7168 + 32) == li.LI_E_UNSUPPORTED
     assert ap(Dc=192) == li.LI_E_UNSUPPORTED
@@ -188,11 +190,12 @@ def test_latent_append_validation_and_workspace():
     assert ap(M=0, h=None, dst=None, ws=None, wsb=0) == li.LI_OK
     assert ap(w=None) == li.LI_E_NULL
     # partial sums of the K split: [S][M][Dc] fp32, S > 1 for a 4096-token chunk
-    need = L.li_latent_append_ws(4096, 7168, 256)
+    need = L.li_latent_append_ws(4096, 7168, 256, li.LI_BF16)
     assert need >= 2 * 4096 * 256 * 4 and need % (4096 * 256 * 4) == 0
-    assert L.li_latent_append_ws(0, 7168, 256) == 0
-    # one K step covers d_model = 64: a single split writes the cache directly
-    assert L.li_latent_append_ws(16, 64, 128) == 0
+    assert L.li_latent_append_ws(0, 7168, 256, li.LI_BF16) == 0
+    # one K step covers d_model = 64: bf16 output is written directly, fp8 output goes through the split sum
+    assert L.li_latent_append_ws(16, 64, 128, li.LI_BF16) == 0
+    assert L.li_latent_append_ws(16, 64, 128, li.LI_FP8_E4M3) >= 16 * 128 * 4
 
 
 def test_indexcache_plan():

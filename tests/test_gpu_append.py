@@ -87,7 +87,7 @@ def test_append_one_split_writes_the_cache_directly():
     # d_model = 64 is one K step, hence one split: no partial sums, no workspace;
     # d_model = 128 splits its two K steps
     for d, seed in ((64, 405), (128, 406)):
-        assert (li.lib().li_latent_append_ws(300, d, 256) == 0) == (d == 64)
+        assert (li.lib().li_latent_append_ws(300, d, 256, li.LI_BF16) == 0) == (d == 64)
         append_parity(inputs.make_append(seed, [2, 9], [131, 126], d_model=d, dist="int"), f"int d{d}",
                       exact_only=True)
         append_parity(inputs.make_append(seed + 10, [2, 9], [131, 126], d_model=d, Dc=128), f"normal d{d} Dc128")
@@ -115,7 +115,7 @@ def test_append_decode_step_full_size():
 
 def test_append_ignores_workspace_contents_and_repeats():
     x = inputs.make_append(410, [40, 7], [300, 90], d_model=3072)
-    need = li.lib().li_latent_append_ws(x.M, x.d_model, x.Dc)
+    need = li.lib().li_latent_append_ws(x.M, x.d_model, x.Dc, li.LI_BF16)
     assert need > 0
     ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda").view(torch.uint8)
     first = run_append(x, ws=ws)
@@ -138,3 +138,83 @@ def test_append_debug_validation_rejects_rows_outside_the_cache(monkeypatch):
     assert e.value.status == li.LI_E_VALUE and "dst_row" in str(e.value)
     torch.cuda.synchronize()
     assert bool((lat == SENTINEL).all())
+
+
+def fp8_append_parity(x, what, exact_only=False):
+    """fp8 output: codes and block scales against the oracle's fp32 quantisation.
+    Integer inputs: identical.  Normal inputs: the kernel's fp32 sum y lies within
+    b of the exact sum e, so its block max within b_max of the exact one, its
+    scale within that / 448 (plus fp32 rounding), and each code between the
+    E4M3 roundings of (e - b) / scale and (e + b) / scale."""
+    print(f"[append parity] {what} fp8 M={x.M} d_model={x.d_model} Dc={x.Dc}", flush=True)
+    nb = x.Dc // 128
+    lat = torch.zeros((x.n_tok, x.Dc), dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+    sc = torch.zeros((x.n_tok, nb), dtype=torch.float32, device="cuda")
+    li.li_latent_append(dev(x.h, "bf16"), dev(x.w_enc, "bf16"), dev(x.dst_row), lat, c_scale=sc)
+    torch.cuda.synchronize()
+    rows = torch.from_numpy(x.dst_row).cuda()
+    got = lat.view(torch.uint8).index_select(0, rows).cpu().numpy()
+    gsc = sc.index_select(0, rows).cpu().numpy()
+    ref, rsc, exact = oracle.latent_append(x.h, "bf16", x.w_enc, "bf16", np.arange(x.M), np.zeros((x.M, x.Dc), np.uint8),
+                                           c_scale=np.zeros((x.M, nb), np.float32))
+    nd = int((got != ref).sum())
+    print(f"[append parity] {what} fp8: {nd} of {got.size} codes and {int((gsc != rsc).sum())} scales differ", flush=True)
+    if exact_only:
+        assert np.array_equal(got, ref) and np.array_equal(gsc, rsc)
+        return
+    hv = np.abs(bf16_values(x.h))
+    wv = np.abs(bf16_values(x.w_enc))
+    b = (x.d_model + 64) * 2.0 ** -24 * (hv @ wv.T)
+    amax = np.abs(exact).reshape(x.M, nb, 128).max(axis=2)
+    bmax = b.reshape(x.M, nb, 128).max(axis=2)
+    assert np.all(np.abs(gsc.astype(np.float64) * 448 - amax) <= bmax + 2.0 ** -22 * amax), f"{what}: scales"
+    s = np.repeat(gsc.astype(np.float64), 128, axis=1)
+    dec = lambda c: torch.from_numpy(np.ascontiguousarray(c)).view(torch.float8_e4m3fn).double().numpy()
+    diff = got != ref
+    if diff.any():
+        e, bb, ss = exact[diff], b[diff], s[diff]
+        lo = dec(np.array([oracle.encode_e4m3(v) for v in (e - bb) / ss], np.uint8))
+        hi = dec(np.array([oracle.encode_e4m3(v) for v in (e + bb) / ss], np.uint8))
+        g = dec(got[diff])
+        assert np.all((lo <= g) & (g <= hi)), f"{what}: a code not explained by fp32 summation"
+    assert nd <= max(4, got.size // 100), f"{what}: too many boundary codes ({nd})"
+    untouched = np.setdiff1d(np.arange(x.n_tok), x.dst_row)
+    if untouched.size:
+        u = torch.from_numpy(untouched[:4096]).cuda()
+        assert int(lat.view(torch.uint8).index_select(0, u).count_nonzero()) == 0
+
+
+def test_append_fp8_integer_exact():
+    fp8_append_parity(inputs.make_append(413, [5, 0, 300], [130, 1, 70], d_model=1024, dist="int"), "int d1024",
+                      exact_only=True)
+    fp8_append_parity(inputs.make_append(414, [9], [40], d_model=64, Dc=128, dist="int"), "int d64 Dc128",
+                      exact_only=True)
+
+
+def test_append_fp8_normal_and_prefill_chunk():
+    fp8_append_parity(inputs.make_append(415, [10, 4000], [150, 77], d_model=2048), "normal d2048")
+    fp8_append_parity(inputs.make_append(416, [64, 3], [129, 255], d_model=1536, Dc=128), "normal Dc128")
+
+
+def test_appended_fp8_latent_feeds_the_scan():
+    # The fp8 rows the append writes are what the latent scan reads.  With
+    # integer-valued inputs the appended codes and scales equal the oracle's,
+    # so the GPU scan of the GPU-appended cache is checked against the oracle's
+    # scan of the oracle-appended cache.
+    x = inputs.make_append(417, [0, 0], [700, 300], d_model=512, dist="int")
+    lat = torch.zeros((x.n_tok, x.Dc), dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+    sc = torch.zeros((x.n_tok, 2), dtype=torch.float32, device="cuda")
+    li.li_latent_append(dev(x.h, "bf16"), dev(x.w_enc, "bf16"), dev(x.dst_row), lat, c_scale=sc)
+    codes, scales, _ = oracle.latent_append(x.h, "bf16", x.w_enc, "bf16", x.dst_row, np.zeros((x.n_tok, x.Dc), np.uint8),
+                                            c_scale=np.zeros((x.n_tok, 2), np.float32))
+    torch.cuda.synchronize()
+    assert np.array_equal(lat.view(torch.uint8).cpu().numpy(), codes) and np.array_equal(sc.cpu().numpy(), scales)
+    y = inputs.make_latent(418, [700, 300], G=2, k=64)
+    ls = torch.empty((2, x.n_tok), dtype=torch.float32, device="cuda")
+    li.li_latent_score_group(dev(y.q, "bf16"), dev(y.w), dev(y.w_dec, "bf16"), lat, sc, dev(y.kv_off), 700, y.k,
+                             out_scores=ls)
+    torch.cuda.synchronize()
+    _, rs, ra = oracle.latent_score_group(y.q, "bf16", y.w, y.w_dec, "bf16", codes, "fp8_e4m3", scales, y.kv_off,
+                                          2, y.H, 128, 256, y.k, c_blocks=2)
+    err = np.abs(ls.cpu().numpy().astype(np.float64) - rs)
+    assert np.all(err <= 2e-3 * ra)

@@ -93,7 +93,7 @@ def test_append_graph():
     assert x.n_tok == x.M
     h, wenc, dst = dev(x.h, "bf16"), dev(x.w_enc, "bf16"), dev(x.dst_row)
     lat = torch.zeros((x.n_tok, x.Dc), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(li.lib().li_latent_append_ws(x.M, x.d_model, x.Dc), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(li.lib().li_latent_append_ws(x.M, x.d_model, x.Dc, li.LI_BF16), dtype=torch.uint8, device="cuda")
     assert ws.numel() > 0  # the split path (partial sums + reduction) is the one captured
     check_replays(lambda: li.li_latent_append(h, wenc, dst, lat, ws=ws), [lat], "append")
 
