@@ -323,6 +323,19 @@ def components(torch, li, inputs, args):
             // max(1, x.M * x.Dc * 4), "algorithmic_bytes": nbytes,
             "gbs": nbytes / t / 1e9, "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBS,
             "tflops": flop / t / 1e12, "mfma_frac_bf16": flop / t / 1e12 / BF16_PEAK_TFLOPS}
+        if x.M > 16:  # the chunk again with fp8 output (codes + one scale per 128 values)
+            lat8 = torch.zeros((x.n_tok, x.Dc), dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+            sc8 = torch.zeros((x.n_tok, x.Dc // 128), dtype=torch.float32, device="cuda")
+            ws8 = torch.empty(L.li_latent_append_ws(x.M, x.d_model, x.Dc, li.LI_FP8_E4M3), dtype=torch.uint8,
+                              device="cuda")
+
+            def fn8():
+                h, wenc = srcs[turn[0] % APPEND_COPIES]
+                turn[0] += 1
+                li.li_latent_append(h, wenc, dst, lat8, c_scale=sc8, ws=ws8)
+            wall8, (gemm8, red8) = timed(torch, li, fn8, 2, max(args.comp_iters, 2 * APPEND_COPIES), 2)
+            out[x.name.replace("append_", "append_fp8_")] = {"gemm_ms": gemm8, "reduce_ms": red8, "total_ms": wall8}
+            del lat8, sc8, ws8
         del srcs, dst, lat, ws
     out.update(stack_component(torch, li, args))
     out.update(attention_component(torch, li, inputs, args))
