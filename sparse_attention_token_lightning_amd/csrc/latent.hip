@@ -34,7 +34,7 @@
 namespace li {
 namespace {
 
-constexpr int kAbsB = 32;  // requests per absorb pass
+constexpr int kAbsB = 16;  // requests per absorb pass
 
 // bf16 of an fp32 value, round to nearest even (finite inputs).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
@@ -66,72 +66,102 @@ __device__ __forceinline__ i32x4 fp8x8_scaled_to_f16x8(i32x4 v, int half, float 
 // = hi, qt16[nrows + row] = lo, two bf16 parts with hi + lo = the scaled row
 // to within 2^-17 of its magnitude (hi is the bf16 rounding, lo that of the
 // exact fp32 residual).
+//
+// One workgroup per (layer l, head h): the [Dc x 128] block of W_l times the
+// [128 x B] queries of that head is a small dense contraction, run on bf16
+// MFMA (v_mfma_f32_16x16x32_bf16, exact bf16 products, fp32 sums) as 16-row
+// tiles of latent dims c against 16 requests, 4 K-steps over the head's 128
+// dims.  Wave w holds decoder rows 16 (w nt + i) .. +15 (nt = Dc / 64 tiles)
+// in registers for all passes over the batch.  Operand lanes: row or request
+// (lane & 15), dims 32 ks + 8 (lane >> 4) .. +7 of K-step ks; the result
+// leaves lane (g, n) rows 4 g .. 4 g + 3 of each tile for request n.
 __global__ __launch_bounds__(256) void latent_absorb_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ w_dec,
     int B, int G, int H, int Dc, bool split, uint16_t* __restrict__ qt16, float* __restrict__ wsc) {
   constexpr int Dh = 128;
-  __shared__ float qs[kAbsB][Dh];
+  constexpr int kMaxTiles = 4;  // 16-row tiles per wave at Dc = 256
   __shared__ float red[kAbsB][4];
   const int l = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
-  const int c = threadIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint16_t* wrow = w_dec + ((int64_t)l * Dc + (c < Dc ? c : 0)) * (int64_t)H * Dh + (int64_t)h * Dh;
+  const int col = lane & 15, g = lane >> 4;
+  const int nt = Dc / 64;
+  // All of the wave's decoder loads are issued together, up front (tiles
+  // past nt repeat the last one and are never used).
+  bf16x8 wa[kMaxTiles][Dh / 32];
+#pragma unroll
+  for (int i = 0; i < kMaxTiles; ++i) {
+    const int c = 16 * (wave * nt + (i < nt ? i : nt - 1)) + col;
+    const uint16_t* wrow = w_dec + ((int64_t)l * Dc + c) * (int64_t)H * Dh + (int64_t)h * Dh + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < Dh / 32; ++ks) wa[i][ks] = __builtin_bit_cast(bf16x8, ld16(wrow + 32 * ks));
+  }
 
   for (int b0 = 0; b0 < B; b0 += kAbsB) {
     const int nb = (B - b0) < kAbsB ? (B - b0) : kAbsB;
-    for (int i = threadIdx.x; i < kAbsB * Dh; i += 256) {
-      const int bi = i / Dh, j = i - (i / Dh) * Dh;
-      float v = 0.0f;
-      if (bi < nb) {
-        const uint16_t raw = q[(((int64_t)(b0 + bi) * G + l) * H + h) * Dh + j];
-        v = __builtin_bit_cast(float, (uint32_t)raw << 16);
+    // Request columns past the batch repeat the last request; their results
+    // are never stored.
+    const int bq = b0 + (col < nb ? col : nb - 1);
+    const uint16_t* qrow = q + (((int64_t)bq * G + l) * H + h) * Dh + 8 * g;
+    bf16x8 qb[Dh / 32];
+#pragma unroll
+    for (int ks = 0; ks < Dh / 32; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, ld16(qrow + 32 * ks));
+    f32x4 acc[kMaxTiles];
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kMaxTiles; ++i) {
+      acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (i < nt) {
+#pragma unroll
+        for (int ks = 0; ks < Dh / 32; ++ks)
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[i][ks], qb[ks], acc[i], 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) am = fmaxf(am, fabsf(acc[i][e]));
       }
-      qs[bi][j] = v;
     }
+    // Largest magnitude of request col's absorbed row over all Dc dims: the
+    // four lanes of the column, then the four waves.
+    am = fmaxf(am, __shfl_xor(am, 16));
+    am = fmaxf(am, __shfl_xor(am, 32));
+    if (g == 0) red[col][wave] = am;
     __syncthreads();
-    float acc[kAbsB];
+    const float mx = fmaxf(fmaxf(red[col][0], red[col][1]), fmaxf(red[col][2], red[col][3]));
+    int E = 0;
+    if (mx > 0.0f) frexpf(mx, &E);
+    const int ex = mx > 0.0f ? 15 - E : 0;  // mx * 2^ex in [2^14, 2^15)
+    if (col < nb) {
+      const int64_t rowi = ((int64_t)(b0 + col) * G + l) * H + h;
 #pragma unroll
-    for (int bi = 0; bi < kAbsB; ++bi) acc[bi] = 0.0f;
-    if (c < Dc) {
-#pragma unroll 1
-      for (int j0 = 0; j0 < Dh; j0 += 8) {
-        const i32x4 v = ld16(wrow + j0);
-        const int parts[4] = {v.x, v.y, v.z, v.w};
+      for (int i = 0; i < kMaxTiles; ++i) {
+        if (i >= nt) continue;
+        const int64_t c0 = 16 * (wave * nt + i) + 4 * g;
+        uint32_t hv[2], lv[2];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int word = parts[e >> 1];
-          const float wv = __builtin_bit_cast(float, (e & 1) ? (word & (int)0xFFFF0000u) : (word << 16));
+        for (int e2 = 0; e2 < 2; ++e2) {
+          uint32_t hp = 0, lp = 0;
 #pragma unroll
-          for (int bi = 0; bi < kAbsB; ++bi) acc[bi] = fmaf(wv, qs[bi][j0 + e], acc[bi]);
+          for (int m = 0; m < 2; ++m) {
+            const float v = ldexpf(acc[i][2 * e2 + m], ex);
+            uint32_t hb, lb = 0;
+            if (split) {
+              const uint16_t hi = f32_to_bf16_rne(v);
+              const float res = v - __builtin_bit_cast(float, (uint32_t)hi << 16);  // exact in fp32
+              hb = hi;
+              lb = f32_to_bf16_rne(res);
+            } else {
+              hb = __builtin_bit_cast(uint16_t, (_Float16)v);
+            }
+            hp |= hb << (16 * m);
+            lp |= lb << (16 * m);
+          }
+          hv[e2] = hp;
+          lv[e2] = lp;
         }
+        *reinterpret_cast<uint2*>(qt16 + rowi * Dc + c0) = make_uint2(hv[0], hv[1]);
+        if (split) *reinterpret_cast<uint2*>(qt16 + ((int64_t)B * G * H + rowi) * Dc + c0) = make_uint2(lv[0], lv[1]);
       }
+      if (wave == 0 && g == 0) wsc[rowi] = ldexpf(w[rowi], -ex);
     }
-#pragma unroll
-    for (int bi = 0; bi < kAbsB; ++bi) {
-      const float m = wave_max(c < Dc ? fabsf(acc[bi]) : 0.0f);
-      if (lane == 0) red[bi][wave] = m;
-    }
-    __syncthreads();
-    for (int bi = 0; bi < nb; ++bi) {
-      const float mx = fmaxf(fmaxf(red[bi][0], red[bi][1]), fmaxf(red[bi][2], red[bi][3]));
-      int E = 0;
-      if (mx > 0.0f) frexpf(mx, &E);
-      const int e = mx > 0.0f ? 15 - E : 0;  // mx * 2^e in [2^14, 2^15)
-      const int64_t rowi = ((int64_t)(b0 + bi) * G + l) * H + h;
-      if (c < Dc) {
-        const float v = ldexpf(acc[bi], e);
-        if (split) {
-          const uint16_t hi = f32_to_bf16_rne(v);
-          const float res = v - __builtin_bit_cast(float, (uint32_t)hi << 16);  // exact in fp32
-          qt16[rowi * Dc + c] = hi;
-          qt16[((int64_t)B * G * H + rowi) * Dc + c] = f32_to_bf16_rne(res);
-        } else {
-          qt16[rowi * Dc + c] = __builtin_bit_cast(uint16_t, (_Float16)v);
-        }
-      }
-      if (c == 0) wsc[rowi] = ldexpf(w[rowi], -e);
-    }
-    __syncthreads();
+    __syncthreads();  // red is reused by the next pass
   }
 }
 
