@@ -231,6 +231,32 @@ def test_prefill_rows_are_decodes_of_the_visible_prefix():
         assert idx[t].max() <= x.qpos0 + t
 
 
+def test_prefill_per_row_query_scales_equal_decodes_with_the_scale_folded_in():
+    """Row t of a prefill uses its own query scale q_scale[t] (one per query
+    token, shared by its heads).  Each scale here has at most 3 significant
+    bits, so sigma_t * q_hat (4 significant bits) is exact in bf16: row t must
+    equal, bit for bit, a decode whose bf16 query is that product.  Reading
+    q_scale[0] for every row, or indexing the scale by key position, fails."""
+    x = inputs.make_prefill(34, T=6, L=150, H=8, D=128, k=100)
+    x.q_scale = np.array([0.75, 4.0, 1.25, 0.0625, 1.75, 24.0], np.float32)
+    idx, sc, ab = oracle.index_prefill(x.q, x.q_dt, x.q_scale, x.w, x.kc, x.k_dt, x.k_scale, x.T, x.L, x.qpos0,
+                                       x.H, x.D, x.k)
+    for t in range(x.T):
+        vis = x.qpos0 + t + 1
+        qf = (oracle.decode_element(x.q[t], "fp8_e4m3") * float(x.q_scale[t])).astype(np.float32)
+        qb = inputs.encode_bf16(qf.reshape(1, 8, 128))
+        assert np.array_equal(oracle.decode_element(qb, "bf16"), qf.reshape(-1).astype(np.float64))
+        d = inputs.Decode(q=qb, w=x.w[t:t + 1], kc=x.kc[:vis], k_scale=x.k_scale[:vis],
+                          kv_off=np.array([0, vis], np.int64), H=8, D=128, k=100)
+        di, ds, da = _run_decode(d)
+        assert np.array_equal(ds, sc[t, :vis]) and np.array_equal(da, ab[t, :vis]), f"row {t}"
+        assert np.array_equal(di[0], idx[t])
+    # the rows differ only through their scales: a shared scale would not reproduce them
+    one = oracle.index_prefill(x.q, x.q_dt, np.full(x.T, x.q_scale[0], np.float32), x.w, x.kc, x.k_dt,
+                               x.k_scale, x.T, x.L, x.qpos0, x.H, x.D, x.k)
+    assert not np.array_equal(one[1][1:], sc[1:])
+
+
 def test_prefill_short_rows_return_everything_visible():
     x = inputs.make_prefill(32, T=5, L=7, H=4, D=128, k=6)
     idx, _, _ = oracle.index_prefill(x.q, x.q_dt, x.q_scale, x.w, x.kc, x.k_dt, x.k_scale, x.T, x.L, x.qpos0,
