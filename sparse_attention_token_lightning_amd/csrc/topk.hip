@@ -588,8 +588,9 @@ __global__ __launch_bounds__(kSegThreads) void topk_segmented_kernel(TopkRows a,
   }
   // Candidates and counts are published with agent-scope atomic stores,
   // which write through the (per-XCD, non-coherent) L2, and read back the same
-  // way by the finishing workgroup; a full __threadfence() would instead write
-  // back every dirty L2 line at each of these workgroups.
+  // way by the finishing workgroup.  One release per workgroup (step 3) orders
+  // them; a __threadfence() in every thread would write back the L2 once per
+  // wave instead.
   uint64_t* dst = reinterpret_cast<uint64_t*>(ws.cand + ((int64_t)r * ws.nseg + s) * kSegLen);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
@@ -604,16 +605,30 @@ __global__ __launch_bounds__(kSegThreads) void topk_segmented_kernel(TopkRows a,
   }
   if (tid == 0)
     __hip_atomic_store(ws.cnt + (int64_t)r * ws.nseg + s, total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();  // segoff is reused below
 
-  // 3. The last segment of the row to finish does the final selection.  The
-  //    workgroup-scope release waits for this workgroup's stores to complete
-  //    before the counter moves.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __syncthreads();
-  if (tid == 0)
-    sh_last = (__hip_atomic_fetch_add(ws.done + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 ==
-               (uint32_t)nseg_row);
+  // 3. The last segment of the row to finish does the final selection.
+  //    Ordering of the hand-off (AMDGPU memory model, agent scope):
+  //    - every wave waits for its own candidate and count stores to complete
+  //      (s_waitcnt 0) before the barrier, so the workgroup's stores are done
+  //      when the counter moves, whatever the barrier's fences imply;
+  //    - the barrier makes them happen-before tid 0's agent-scope release
+  //      fence (L2 write-back), which completes before the counter update;
+  //    - the workgroup that reads the final count does an agent-scope acquire
+  //      (L1/L2 invalidate) before the barrier that lets its other waves read
+  //      the candidates, so it observes every releasing workgroup's stores.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // also: segoff is reused below
+  if (tid == 0) {
+    // Release fence, then an explicit wait: the write-back must be complete
+    // before the counter moves (the compiler's own wait after the write-back
+    // is dropped when no store is pending).
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_s_waitcnt(0);
+    const bool last = __hip_atomic_fetch_add(ws.done + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 ==
+                      (uint32_t)nseg_row;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    sh_last = last;
+  }
   __syncthreads();
   if (!sh_last) return;
   if (tid == 0) __hip_atomic_store(ws.done + r, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
