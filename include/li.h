@@ -2,10 +2,9 @@
  * li.h — C ABI of the MI355X (gfx950) lightning-indexer library.
  *
  * The operation (sources are page titles and sections):
- *   For each query token the lightning indexer scores every visible cached
- *   token, one score per visible position, and keeps the k highest-scoring
- *   positions (k = 2,048 in the pages) as the index tensor that sparse
- *   attention consumes.  ("IndexCache: Cross-Layer Index Reuse for Sparse
+ *   For each query token the lightning indexer gives every cached position the
+ *   query may attend a score, and the k best-scoring positions (k = 2,048 in
+ *   the pages) form the index tensor that sparse attention reads.  ("IndexCache: Cross-Layer Index Reuse for Sparse
  *   Attention", Symbol Map and Deep Dive; "Multi-layer Indexer: Overlapping
  *   Selection and Attention in DeepSeek Sparse Attention", The abstract.)
  *   The score this library computes is
@@ -13,9 +12,9 @@
  *   with per-token scales applied to the dequantised operands, and ties in the
  *   selection go to the lower position.
  *   LatentIndex variant: a group of layers shares one latent cache; each layer's
- *   key decoder is absorbed into its query so the shared cache is scored
- *   directly, with layer-specific selection.  HS variant: follower layers
- *   refine a candidate set proposed by the anchor layer.  ("LatentIndex:
+ *   key decoder is folded into its query, so the shared cache is scored as
+ *   stored and every layer still selects on its own.  HS variant: the anchor
+ *   layer's selection is the pool from which the follower layers pick.  ("LatentIndex:
  *   Cross-Layer Sharing with Layer-Specific Selection for Sparse Attention",
  *   Abstract and Figure 1.)  Shapes: 64 indexer heads x 128 dims per key
  *   (same page, Table 5).
@@ -124,9 +123,16 @@ size_t li_index_decode_ws(int32_t B, int64_t n_tok, int32_t max_len, int32_t k,
  *   q        [T][H][D]  LI_FP8_E4M3 ; q_scale [T] fp32 or NULL (= 1)
  *   w        [T][H]     fp32
  *   k_cache  [L][D]     LI_FP8_E4M3 ; k_scale [L] fp32 or NULL (= 1)
- *   0 <= qpos0, qpos0 + T <= L;  H 1..64;  D must be 128;  1 <= k <= LI_MAX_K
+ *   0 <= qpos0, qpos0 + T <= L;  H 8..64;  D must be 128;  1 <= k <= LI_MAX_K
  *   out_idx    [T][k]   int32 positions, ascending, -1 padded
  *   out_scores [T][L]   fp32 or NULL; masked positions hold -inf
+ *
+ * The products run on fp8 matrix cores, whose accumulation error is relative
+ * to sum_d |q_d k_d| of a head rather than to its dot product; with fewer than
+ * 8 heads one cancelling head can exceed the score tolerance
+ * (|dS| <= 2e-3 * sum_h |w_h x_h|), so H < 8 returns LI_E_UNSUPPORTED.
+ * Measured at H = 8: within 8.3e-5 of that sum on N(0,1) inputs, 4.8e-4 with
+ * query elements spread over 2^-9 .. 2^0; at H = 64 within 1.3e-5.
  * ------------------------------------------------------------------------- */
 li_status li_index_prefill(const void* q, li_dtype q_dt, const float* q_scale, const float* w,
                            const void* k_cache, li_dtype k_dt, const float* k_scale, int32_t T,
@@ -135,12 +141,17 @@ li_status li_index_prefill(const void* q, li_dtype q_dt, const float* q_scale, c
                            void* stream);
 size_t li_index_prefill_ws(int32_t T, int32_t L, int32_t k, int32_t has_out_scores);
 
-/* Selects the MFMA operand form of the absorbed latent queries. */
+/* Selects the MFMA operand form of the absorbed latent queries.  Both forms
+ * need H >= 2 (with one head the absorbed query's rounding can exceed the
+ * score tolerance: LI_E_UNSUPPORTED). */
 #define LI_LATENT_FP16 0u /* fp16 absorbed query (per-row power-of-two range scaling), latent
                              converted bf16 -> fp16 on the fly; requires latent magnitudes
                              within fp16 range (|c| <= 65504).  One product per element;
-                             score error up to about 2e-4 of sum_h |w_h x_h| (measured on
-                             N(0,1) latents). */
+                             score error up to about 2e-4 of sum_h |w_h x_h| at H = 64 and
+                             4e-4 at H = 16 (measured on N(0,1) latents).  With fewer than
+                             16 heads a bf16 latent is scored in the LI_LATENT_SPLIT_BF16
+                             form instead (the fp16 form's error nears the tolerance
+                             there), and an LI_FP8_E4M3 latent is LI_E_UNSUPPORTED. */
 #define LI_LATENT_SPLIT_BF16 1u /* absorbed query as two bf16 parts, hi + lo (lo = the bf16
                                    rounding of the exact residual), against the bf16 latent as
                                    stored (any magnitude bf16 holds).  Two products per element
@@ -165,7 +176,8 @@ size_t li_index_prefill_ws(int32_t T, int32_t L, int32_t k, int32_t has_out_scor
  *           per 128-value block; each code times its block's scale is rounded
  *           once to fp16 for the product (fp16 form only)
  *   kv_off  [B+1] int64, device;  max_len >= every L_b
- *   G >= 1;  H 1..64;  Dh must be 128;  Dc 128 or 256;  1 <= k <= LI_MAX_K
+ *   G >= 1;  H 2..64 (16..64 for LI_FP8_E4M3);  Dh must be 128;  Dc 128 or 256;
+ *   1 <= k <= LI_MAX_K
  *   out_idx    [B][G][k]  int32 positions, ascending, -1 padded
  *   out_scores [G][n_tok] fp32 or NULL
  *   flags      LI_LATENT_FP16 or LI_LATENT_SPLIT_BF16
@@ -191,7 +203,8 @@ size_t li_latent_score_group_ws(int32_t B, int64_t n_tok, int32_t max_len, int32
  *   q [B][Gf][H][Dh] LI_BF16; w [B][Gf][H] fp32; w_dec [Gf][Dc][H*Dh] LI_BF16
  *   latent [n_tok][Dc] LI_BF16 with c_scale [n_tok] or NULL, or LI_FP8_E4M3 with
  *   block scales [n_tok][Dc/128] (as in li_latent_score_group); kv_off [B+1] int64
- *   1 <= C <= 65536; Gf >= 1; H 1..64; Dh 128; Dc 128 or 256; 1 <= k <= LI_MAX_K
+ *   1 <= C <= 65536; Gf >= 1; H 2..64 (16..64 for LI_FP8_E4M3); Dh 128; Dc 128 or 256;
+ *   1 <= k <= LI_MAX_K
  *   out_idx    [B][Gf][k] int32 TOKEN positions (taken from cand_idx), ascending, -1 padded
  *   out_scores [B][Gf][C] fp32 score of candidate slot j, or NULL (slots past
  *              the valid candidates are not written)

@@ -167,6 +167,20 @@ li_status check_heads(int32_t H, int32_t D, const char* dname) {
   return LI_OK;
 }
 
+// Fewest heads each approximate product form is accepted for.  The score bar
+// is |S_gpu - S_exact| <= 2e-3 * sum_h |w_h x_h|; a form whose per-head error
+// is relative to sum_d |q_d k_d| (not to |x_h|) meets it only when no single
+// cancelling head dominates that sum.  Measured worst error / bar on N(0,1)
+// inputs and on queries spread over 2^-9 .. 2^0 inside each head:
+//  - prefill (fp8 MFMA): H = 1 fails (err ~ 1.0 * A), H = 2 fails on spread
+//    queries (9.5e-3 * A); H = 8: 8.3e-5 (random), 4.8e-4 (spread).
+//  - latent, fp16 absorbed query: H = 2 fails (1.7e-2 * A), H = 4 1.9e-3,
+//    H = 8 6.6e-4, H = 16 4.1e-4, H = 64 1.5e-4.
+//  - latent, split bf16 query: H = 1 fails (1.8e-2 * A), H = 2 1.3e-4.
+constexpr int32_t kPrefillMinHeads = 8;
+constexpr int32_t kLatentFp16MinHeads = 16;  // below: the split form runs instead (bf16 latent)
+constexpr int32_t kLatentMinHeads = 2;
+
 li_status check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (ws_bytes < need)
     return fail(LI_E_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", ws_bytes, need);
@@ -289,6 +303,9 @@ li_status li_index_prefill(const void* q, li_dtype q_dt, const float* q_scale, c
                 qpos0);
   li_status st;
   if ((st = check_k(k)) || (st = check_heads(H, D, "D"))) return st;
+  if (H < kPrefillMinHeads)
+    return fail(LI_E_UNSUPPORTED, "prefill needs H >= %d (got %d): the fp8 product's error with fewer heads "
+                "can exceed the score tolerance", kPrefillMinHeads, H);
   if ((st = check_ws(ws, ws_bytes, prefill_ws(T, L, out_scores != nullptr)))) return st;
   if (T == 0) return LI_OK;
   hipStream_t s = (hipStream_t)stream;
@@ -339,7 +356,18 @@ static li_status check_latent_common(li_dtype q_dt, li_dtype w_dt, li_dtype c_dt
   if (Dc != 128 && Dc != 256) return fail(LI_E_UNSUPPORTED, "Dc must be 128 or 256 (got %d)", Dc);
   if (flags != LI_LATENT_FP16 && flags != LI_LATENT_SPLIT_BF16)
     return fail(LI_E_UNSUPPORTED, "unknown flags 0x%x", flags);
+  if (H < kLatentMinHeads)
+    return fail(LI_E_UNSUPPORTED, "the latent forms need H >= %d (got %d): with one head the absorbed "
+                "query's rounding can exceed the score tolerance", kLatentMinHeads, H);
+  if (c_dt == LI_FP8_E4M3 && H < kLatentFp16MinHeads)
+    return fail(LI_E_UNSUPPORTED, "an LI_FP8_E4M3 latent needs H >= %d (got %d)", kLatentFp16MinHeads, H);
   return LI_OK;
+}
+
+// The product form a call runs: the split form when asked for, and for a bf16
+// latent with fewer heads than the fp16 form is accurate for.
+static bool latent_split(uint32_t flags, li_dtype c_dt, int32_t H) {
+  return flags == LI_LATENT_SPLIT_BF16 || (c_dt == LI_BF16 && H < kLatentFp16MinHeads);
 }
 
 size_t li_latent_score_group_ws(int32_t B, int64_t n_tok, int32_t max_len, int32_t G, int32_t H,
@@ -372,19 +400,13 @@ li_status li_latent_score_group(const void* q, li_dtype q_dt, const float* w, co
         li::validate_bf16(q, (int64_t)B * G * H * Dh, li::kBadQ, s);
         li::validate_f32(w, (int64_t)B * G * H, li::kBadW, s);
         li::validate_bf16(w_dec, (int64_t)G * Dc * H * Dh, li::kBadWDec, s);
-        if (c_dt == LI_FP8_E4M3) {
-          li::validate_fp8(latent, n_tok * Dc, li::kBadLatent, s);
-          li::validate_scales(c_scale, n_tok * (Dc / 128), li::kBadCScale, s);
-        } else {
-          li::validate_bf16(latent, n_tok * Dc, li::kBadLatent, s);
-          li::validate_scales(c_scale, n_tok, li::kBadCScale, s);
-        }
+        li::validate_latent(latent, c_dt == LI_FP8_E4M3, n_tok, Dc, c_scale, !latent_split(flags, c_dt, H), s);
       })))
     return st;
   trace_begin();
   Carver cv(ws);
   uint16_t* qt16 = (uint16_t*)cv.take((size_t)B * G * H * Dc * 4);
-  const bool split = flags == LI_LATENT_SPLIT_BF16;
+  const bool split = latent_split(flags, c_dt, H);
   float* wsc = (float*)cv.take((size_t)B * G * H * 4);
   float* scores = out_scores ? out_scores : (float*)cv.take((size_t)G * (size_t)n_tok * 4);
   const li::SelWs sel = carve_sel(cv, (int64_t)B * G, max_len, li::latent_chunk(n_tok), k);
@@ -434,18 +456,24 @@ li_status li_hs_refine(const int32_t* cand_idx, int32_t C, const void* q, li_dty
   hipStream_t s = (hipStream_t)stream;
   // The latent cache's length is not an argument here: its rows are checked
   // through the candidates (each inside its request) and kv_off's order.
-  if (validate_on() && (st = run_validation(s, [&] {
-        li::validate_offsets(kv_off, B, INT64_MAX, INT32_MAX, s);
-        li::validate_cands(cand_idx, B, C, kv_off, s);
-        li::validate_bf16(q, (int64_t)B * Gf * H * Dh, li::kBadQ, s);
-        li::validate_f32(w, (int64_t)B * Gf * H, li::kBadW, s);
-        li::validate_bf16(w_dec, (int64_t)Gf * Dc * H * Dh, li::kBadWDec, s);
-      })))
+  // The latent rows are read through the candidates, so they are checked in a
+  // second pass, once offsets and candidates are known to be in range.
+  if (validate_on() && ((st = run_validation(s, [&] {
+                           li::validate_offsets(kv_off, B, INT64_MAX, INT32_MAX, s);
+                           li::validate_cands(cand_idx, B, C, kv_off, s);
+                           li::validate_bf16(q, (int64_t)B * Gf * H * Dh, li::kBadQ, s);
+                           li::validate_f32(w, (int64_t)B * Gf * H, li::kBadW, s);
+                           li::validate_bf16(w_dec, (int64_t)Gf * Dc * H * Dh, li::kBadWDec, s);
+                         })) ||
+                        (st = run_validation(s, [&] {
+                           li::validate_cand_latent(cand_idx, B, C, kv_off, latent, c_dt == LI_FP8_E4M3, Dc, c_scale,
+                                                    !latent_split(flags, c_dt, H), s);
+                         }))))
     return st;
   trace_begin();
   Carver cv(ws);
   uint16_t* qt16 = (uint16_t*)cv.take((size_t)B * Gf * H * Dc * 4);
-  const bool split = flags == LI_LATENT_SPLIT_BF16;
+  const bool split = latent_split(flags, c_dt, H);
   float* wsc = (float*)cv.take((size_t)B * Gf * H * 4);
   float* scores = out_scores ? out_scores : (float*)cv.take((size_t)B * Gf * (size_t)C * 4);
   if ((st = hip_check(li::launch_latent_absorb((const uint16_t*)q, w, (const uint16_t*)w_dec, B, Gf,

@@ -116,17 +116,22 @@ def test_prefill_validation():
     assert call(D=256) == li.LI_E_UNSUPPORTED
     assert call(wsb=100) == li.LI_E_WORKSPACE
     assert call(T=0, qpos0=0) == li.LI_OK
+    # fewer than 8 heads: the fp8 product's error can exceed the score tolerance
+    for h in (1, 2, 7):
+        assert call(H=h) == li.LI_E_UNSUPPORTED
+    assert b"H >= 8" in L.li_last_error()
+    assert call(H=8, wsb=100) == li.LI_E_WORKSPACE
 
 
 def test_latent_and_hs_validation():
     L = li.lib()
 
     def lat(**kw):
-        a = dict(q_dt=li.LI_BF16, G=4, Dc=256, Dh=128, flags=0, kk=8, wsb=1 << 34, B=2)
+        a = dict(q_dt=li.LI_BF16, c_dt=li.LI_BF16, cs=None, G=4, H=64, Dc=256, Dh=128, flags=0, kk=8, wsb=1 << 34, B=2)
         a.update(kw)
-        return L.li_latent_score_group(FAKE, a["q_dt"], FAKE, FAKE, li.LI_BF16, FAKE, li.LI_BF16, None, FAKE, a["B"],
-                                       1000, 600, a["G"], 64, a["Dh"], a["Dc"], a["kk"], FAKE, None, a["flags"], FAKE,
-                                       a["wsb"], None)
+        return L.li_latent_score_group(FAKE, a["q_dt"], FAKE, FAKE, li.LI_BF16, FAKE, a["c_dt"], a["cs"], FAKE,
+                                       a["B"], 1000, 600, a["G"], a["H"], a["Dh"], a["Dc"], a["kk"], FAKE, None,
+                                       a["flags"], FAKE, a["wsb"], None)
 
     assert lat(q_dt=li.LI_FP8_E4M3) == li.LI_E_DTYPE
     assert lat(G=0) == li.LI_E_SHAPE
@@ -138,16 +143,24 @@ def test_latent_and_hs_validation():
     assert lat(flags=li.LI_LATENT_SPLIT_BF16, wsb=1) == li.LI_E_WORKSPACE
     assert lat(wsb=1) == li.LI_E_WORKSPACE
     assert lat(B=0) == li.LI_OK
+    # one head: rejected in both forms; an fp8 latent needs 16 heads; a bf16
+    # latent with 2..15 heads is accepted (it runs the split form)
+    for fl in (li.LI_LATENT_FP16, li.LI_LATENT_SPLIT_BF16):
+        assert lat(H=1, flags=fl) == li.LI_E_UNSUPPORTED
+        assert lat(H=2, flags=fl, wsb=1) == li.LI_E_WORKSPACE
+    assert lat(H=15, c_dt=li.LI_FP8_E4M3, cs=FAKE) == li.LI_E_UNSUPPORTED
+    assert lat(H=16, c_dt=li.LI_FP8_E4M3, cs=FAKE, wsb=1) == li.LI_E_WORKSPACE
 
     def hs(**kw):
-        a = dict(C=8192, Gf=3, kk=2048, wsb=1 << 34)
+        a = dict(C=8192, Gf=3, H=64, kk=2048, wsb=1 << 34)
         a.update(kw)
         return L.li_hs_refine(FAKE, a["C"], FAKE, li.LI_BF16, FAKE, FAKE, li.LI_BF16, FAKE, li.LI_BF16, None, FAKE,
-                              0, a["Gf"], 64, 128, 256, a["kk"], FAKE, None, 0, FAKE, a["wsb"], None)
+                              0, a["Gf"], a["H"], 128, 256, a["kk"], FAKE, None, 0, FAKE, a["wsb"], None)
 
     assert hs(C=0) == li.LI_E_SHAPE
     assert hs(C=70000) == li.LI_E_UNSUPPORTED
     assert hs(Gf=0) == li.LI_E_SHAPE
+    assert hs(H=1) == li.LI_E_UNSUPPORTED
     assert hs() == li.LI_OK
     assert L.li_hs_refine(None, 8, FAKE, 0, FAKE, FAKE, 0, FAKE, 0, None, FAKE, 1, 1, 64, 128, 256, 4, FAKE, None,
                           0, FAKE, 1 << 30, None) == li.LI_E_NULL

@@ -214,3 +214,40 @@ def test_latent_fp8_rejects_missing_scales_and_the_split_form():
     with pytest.raises(li.LiError) as e:
         li.li_latent_score_group(*args, dev(x.c_scale), dev(x.kv_off), 500, x.k, flags=li.LI_LATENT_SPLIT_BF16)
     assert e.value.status == li.LI_E_UNSUPPORTED
+
+
+# ---- head counts and batch sizes off the tuned shape ---------------------------
+
+def test_latent_few_heads_run_the_split_form():
+    """With 2..15 heads the default form scores a bf16 latent in the split
+    form (the fp16 absorbed query's rounding nears the tolerance there): its
+    scores are bit-identical to an explicit LI_LATENT_SPLIT_BF16 call."""
+    for H, seed in ((2, 331), (4, 332), (8, 333), (15, 334)):
+        x = inputs.make_latent(seed, [1500, 700, 33], G=2, H=H, k=128)
+        latent_parity(x, f"H={H} default")
+        _, s0 = run_latent(x)
+        _, s1 = run_latent(x, flags=li.LI_LATENT_SPLIT_BF16)
+        assert np.array_equal(s0.view(np.uint32), s1.view(np.uint32)), f"H={H}: default form is not the split form"
+
+
+def test_latent_sixteen_heads_fp16_and_fp8():
+    latent_parity(inputs.make_latent(335, [2500, 900], G=3, H=16, k=256), "H=16 fp16")
+    latent_parity(inputs.latent_to_fp8(inputs.make_latent(336, [2500, 900], G=3, H=16, k=256)), "H=16 fp8")
+
+
+def test_latent_batches_past_one_absorption_pass():
+    """B = 17 and 37: the absorption handles 16 requests per pass, so these
+    run a second and a third pass with a partial tail of requests."""
+    for B, seed in ((17, 341), (37, 342)):
+        lens = [40 + 53 * ((7 * i) % B) for i in range(B)]
+        x = inputs.make_latent(seed, lens, G=2, k=96)
+        latent_parity(x, f"B={B} fp16")
+        latent_parity(x, f"B={B} split", flags=li.LI_LATENT_SPLIT_BF16, tol=SPLIT_TOL)
+
+
+def test_hs_batches_past_one_absorption_pass_and_few_heads():
+    lens = [300 + 97 * i for i in range(17)]
+    h = inputs.make_hs(343, lens, C=512, Gf=2, k=128)
+    hs_parity(h, "HS B=17 fp16")
+    hs_parity(h, "HS B=17 split", flags=li.LI_LATENT_SPLIT_BF16, tol=SPLIT_TOL)
+    hs_parity(inputs.make_hs(344, [3000, 1200], C=1024, Gf=2, H=4, k=256), "HS H=4 (split form)")

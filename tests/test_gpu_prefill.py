@@ -53,6 +53,27 @@ def test_prefill_chunk_not_at_the_end_and_few_heads():
     parity_rows(x, gi.cpu().numpy(), gs.cpu().numpy(), range(x.T), "mid-chunk H=24")
 
 
+def test_prefill_eight_heads_random_and_spread_queries():
+    """The fewest heads the fp8 path takes: N(0,1) queries, and queries whose
+    elements spread over 2^-9 .. 2^3 inside each head (the analogue of the
+    decode's spread-query test within E4M3's range), all rows checked."""
+    x = inputs.make_prefill(206, T=40, L=1500, H=8, k=256)
+    gi, gs = run_gpu(x)
+    parity_rows(x, gi.cpu().numpy(), gs.cpu().numpy(), range(x.T), "H=8")
+    x = inputs.make_prefill(207, T=40, L=1500, H=8, k=256)
+    octave = 2.0 ** (3 - (np.arange(128) % 13))
+    x.q = inputs.encode_fp8((np.random.default_rng(2071).standard_normal((x.T, 8, 128)) * octave).astype(np.float32))
+    gi, gs = run_gpu(x)
+    parity_rows(x, gi.cpu().numpy(), gs.cpu().numpy(), range(x.T), "H=8 spread q")
+
+
+def test_prefill_rejects_fewer_than_eight_heads():
+    x = inputs.make_prefill(208, T=4, L=100, H=4, k=16)
+    with pytest.raises(li.LiError) as e:
+        run_gpu(x)
+    assert e.value.status == li.LI_E_UNSUPPORTED
+
+
 def test_prefill_without_score_output_matches():
     x = inputs.make_prefill(204, T=16, L=3000, k=2048)
     i0, _ = run_gpu(x)
