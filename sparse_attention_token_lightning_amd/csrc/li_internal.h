@@ -147,6 +147,8 @@ enum ValidateCheck : uint32_t {
   kBadDstRow,
   kBadHidden,
   kBadWEnc,
+  kBadLatentRange,
+  kBadCScaleRange,
 };
 hipError_t validate_begin(hipStream_t s);
 void validate_offsets(const int64_t* off, int32_t B, int64_t n_tok, int32_t max_len, hipStream_t s);
@@ -155,6 +157,13 @@ void validate_f32(const float* p, int64_t n, uint32_t check, hipStream_t s);
 void validate_bf16(const void* p, int64_t n, uint32_t check, hipStream_t s);
 void validate_fp8(const void* p, int64_t n, uint32_t check, hipStream_t s);
 void validate_cands(const int32_t* cand, int32_t B, int32_t C, const int64_t* off, hipStream_t s);
+// Latent codes and scales (nblk = Dc / 128 block scales per row for fp8, one
+// optional row scale for bf16); with fp16_form also the fp16-range limits.
+void validate_latent(const void* latent, bool fp8, int64_t n_tok, int32_t Dc, const float* c_scale,
+                     bool fp16_form, hipStream_t s);
+// The same over the rows kv_off[b] + cand[b][j] of valid candidates only.
+void validate_cand_latent(const int32_t* cand, int32_t B, int32_t C, const int64_t* off, const void* latent,
+                          bool fp8, int32_t Dc, const float* c_scale, bool fp16_form, hipStream_t s);
 void validate_score_rows(const float* p, int64_t stride, int32_t rows, int32_t n, const int32_t* len,
                          hipStream_t s);
 void validate_row_len(const int32_t* len, int32_t rows, int64_t stride, hipStream_t s);

@@ -105,6 +105,53 @@ __global__ __launch_bounds__(kThreads) void cands_kernel(const int32_t* cand, in
   }
 }
 
+// One latent element (value index i of a cache with Dc values per row): a
+// NaN/Inf code, and for the fp16 product form a bf16 value beyond fp16's
+// range; at the first value of each scale block, that block's scale (finite
+// and positive, and for an fp8 latent in the fp16 form small enough that
+// 448 * scale stays inside fp16's range).
+__device__ void check_latent_elem(const void* latent, bool fp8, int64_t i, int32_t Dc, const float* c_scale,
+                                  int32_t nblk, bool fp16_form) {
+  if (fp8) {
+    if ((reinterpret_cast<const uint8_t*>(latent)[i] & 0x7Fu) == 0x7Fu) report(kBadLatent, i);
+  } else {
+    const uint16_t v = reinterpret_cast<const uint16_t*>(latent)[i];
+    if ((v & 0x7F80u) == 0x7F80u) report(kBadLatent, i);
+    else if (fp16_form && fabsf(__builtin_bit_cast(float, (uint32_t)v << 16)) > 65504.0f)
+      report(kBadLatentRange, i);
+  }
+  const int32_t blk = Dc / nblk;
+  const int64_t row = i / Dc;
+  const int32_t c = (int32_t)(i - row * Dc);
+  if (c_scale && c % blk == 0) {
+    const int64_t si = row * nblk + c / blk;
+    const float sc = c_scale[si];
+    if (!(sc > 0.0f) || !isfinite(sc)) report(kBadCScale, si);
+    else if (fp8 && fp16_form && 448.0f * sc > 65504.0f) report(kBadCScaleRange, si);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void latent_kernel(const void* latent, bool fp8, int64_t n_tok, int32_t Dc,
+                                                          const float* c_scale, int32_t nblk, bool fp16_form) {
+  for (int64_t i = gtid(); i < n_tok * Dc; i += gstride())
+    check_latent_elem(latent, fp8, i, Dc, c_scale, nblk, fp16_form);
+}
+
+// The latent rows an HS call reads: kv_off[b] + cand[b][j] for the entries
+// inside [0, L_b) (entries outside are reported by cands_kernel, and the
+// caller runs this check only once those have passed).
+__global__ __launch_bounds__(kThreads) void cand_latent_kernel(const int32_t* cand, int32_t B, int32_t C,
+                                                               const int64_t* off, const void* latent, bool fp8,
+                                                               int32_t Dc, const float* c_scale, int32_t nblk,
+                                                               bool fp16_form) {
+  for (int64_t i = gtid(); i < (int64_t)B * C * Dc; i += gstride()) {
+    const int64_t bj = i / Dc, b = bj / C;
+    const int32_t v = cand[bj];
+    if (v < 0 || v >= off[b + 1] - off[b]) continue;
+    check_latent_elem(latent, fp8, (off[b] + v) * Dc + (i - bj * Dc), Dc, c_scale, nblk, fp16_form);
+  }
+}
+
 unsigned blocks_for(int64_t n) {
   const int64_t b = (n + kThreads - 1) / kThreads;
   return (unsigned)(b < 1 ? 1 : (b > 2048 ? 2048 : b));
@@ -131,6 +178,19 @@ void validate_bf16(const void* p, int64_t n, uint32_t check, hipStream_t s) {
 }
 void validate_fp8(const void* p, int64_t n, uint32_t check, hipStream_t s) {
   if (p && n > 0) fp8_kernel<<<blocks_for(n), kThreads, 0, s>>>((const uint8_t*)p, n, check);
+}
+void validate_latent(const void* latent, bool fp8, int64_t n_tok, int32_t Dc, const float* c_scale,
+                     bool fp16_form, hipStream_t s) {
+  const int32_t nblk = fp8 ? Dc / 128 : 1;
+  if (latent && n_tok > 0 && Dc > 0)
+    latent_kernel<<<blocks_for(n_tok * Dc), kThreads, 0, s>>>(latent, fp8, n_tok, Dc, c_scale, nblk, fp16_form);
+}
+void validate_cand_latent(const int32_t* cand, int32_t B, int32_t C, const int64_t* off, const void* latent,
+                          bool fp8, int32_t Dc, const float* c_scale, bool fp16_form, hipStream_t s) {
+  const int32_t nblk = fp8 ? Dc / 128 : 1;
+  if (B > 0 && C > 0 && Dc > 0)
+    cand_latent_kernel<<<blocks_for((int64_t)B * C * Dc), kThreads, 0, s>>>(cand, B, C, off, latent, fp8, Dc,
+                                                                            c_scale, nblk, fp16_form);
 }
 void validate_cands(const int32_t* cand, int32_t B, int32_t C, const int64_t* off, hipStream_t s) {
   if (B > 0 && C > 0) cands_kernel<<<blocks_for((int64_t)B * C), kThreads, 0, s>>>(cand, B, C, off);
@@ -180,6 +240,8 @@ const char* validate_name(uint32_t check) {
     case kBadDstRow: return "dst_row entry outside [0, n_tok)";
     case kBadHidden: return "h holds a NaN/Inf code";
     case kBadWEnc: return "w_enc holds a NaN/Inf code";
+    case kBadLatentRange: return "latent value beyond fp16 range (|c| > 65504) for LI_LATENT_FP16";
+    case kBadCScaleRange: return "fp8 latent block scale above 65504 / 448 for LI_LATENT_FP16";
     default: return "unknown check";
   }
 }

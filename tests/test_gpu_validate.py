@@ -113,6 +113,49 @@ def test_latent_and_hs_checks(validating):
     rejected(lambda: hs(bad), "not ascending")
 
 
+def test_hs_latent_rows_and_fp16_range_checks(validating):
+    """The HS call checks the latent rows its candidates name (codes, scales);
+    the fp16 form also checks that the latent fits fp16's range."""
+    x = inputs.make_latent(705, [900, 400], G=2, H=16, k=64)
+    cand = np.full((2, 64), -1, np.int32)
+    cand[0, :50] = np.arange(50) * 3
+    cand[1, :10] = np.arange(10) * 7
+
+    def hs(lat, c_scale=None, c_dt="bf16", flags=li.LI_LATENT_FP16):
+        return li.li_hs_refine(dev(cand), dev(x.q, "bf16"), dev(x.w), dev(x.w_dec, "bf16"), dev(lat, c_dt),
+                               dev(c_scale), dev(x.kv_off), 16, flags=flags)
+    print("[validate] hs latent rows", flush=True)
+    hs(x.latent)
+    lat = x.latent.copy()
+    lat[900 + 63, 100] = 0x7F80  # +Inf in request 1's candidate row 63
+    rejected(lambda: hs(lat), "latent holds")
+    lat = x.latent.copy()
+    lat[900 + 64, 100] = 0x7F80  # a row no candidate names is not read
+    hs(lat)
+    lat = x.latent.copy()
+    lat[3 * 17, 5] = 0x4780  # bf16 65536: past fp16's range
+    rejected(lambda: hs(lat), "fp16 range")
+    hs(lat, flags=li.LI_LATENT_SPLIT_BF16)  # the split form takes any bf16 latent
+    rejected(lambda: li.li_latent_score_group(dev(x.q, "bf16"), dev(x.w), dev(x.w_dec, "bf16"), dev(lat, "bf16"),
+                                              None, dev(x.kv_off), 900, x.k), "fp16 range")
+
+    y = inputs.latent_to_fp8(inputs.make_latent(706, [900, 400], G=2, H=16, k=64))
+    print("[validate] hs fp8 latent rows", flush=True)
+    hs(y.latent, y.c_scale, "fp8_e4m3")
+    sc = y.c_scale.copy()
+    sc[900 + 7 * 9, 1] = 0.0  # request 1's candidate 9, second block
+    rejected(lambda: hs(y.latent, sc, "fp8_e4m3"), "c_scale not finite")
+    sc = y.c_scale.copy()
+    sc[3 * 2, 0] = 200.0  # 448 * 200 is past fp16's range
+    rejected(lambda: hs(y.latent, sc, "fp8_e4m3"), "65504 / 448")
+    rejected(lambda: li.li_latent_score_group(dev(y.q, "bf16"), dev(y.w), dev(y.w_dec, "bf16"),
+                                              dev(y.latent, "fp8_e4m3"), dev(sc), dev(y.kv_off), 900, y.k),
+             "65504 / 448")
+    lat8 = y.latent.copy()
+    lat8[3 * 4, 200] = 0x7F
+    rejected(lambda: hs(lat8, y.c_scale, "fp8_e4m3"), "latent holds")
+
+
 def test_topk_checks(validating):
     s = np.random.default_rng(704).standard_normal((3, 500)).astype(np.float32)
     s[0, 10] = -np.inf
