@@ -14,19 +14,19 @@
  * over every visible cached position s, then the k highest scores, the lower
  * position winning ties.  Sources (page title, section):
  *   - "IndexCache: Cross-Layer Index Reuse for Sparse Attention", Symbol Map:
- *     the indexer produces one score per visible position before top-k, and
- *     the selected set holds k token positions (k = 2,048 per query).
- *   - same page, Deep Dive ("Full and Shared layers ..."): the F layer takes
- *     top-k of its scores to obtain the index tensor.
+ *     a score for each position the query may attend, then a selection of
+ *     k = 2,048 positions per query.
+ *   - same page, Deep Dive: a Full layer turns its scores into the index
+ *     tensor by top-k.
  *   - "Multi-layer Indexer: Overlapping Selection and Attention in DeepSeek
- *     Sparse Attention", The abstract: the lightning indexer scores the whole
- *     cache and keeps the k = 2048 highest-scoring tokens.
+ *     Sparse Attention", The abstract: the selection ranges over the entire
+ *     cache, 2048 tokens per query.
  *   - "LatentIndex: Cross-Layer Sharing with Layer-Specific Selection for
- *     Sparse Attention", Abstract and Figure 1: a layer group shares one latent
- *     cache; each layer's key decoder is absorbed into its query so the shared
- *     cache is scored directly; the hierarchical-selection (HS) variant lets
- *     follower layers refine a candidate set proposed by the anchor layer.
- *   - same page, Table 5: 64 indexer heads, 64 RoPE + 64 NoPE = 128 dims.
+ *     Sparse Attention", Abstract and Figure 1: one latent cache per layer
+ *     group; per-layer key decoders folded into the queries, so nothing is
+ *     decoded per token; in hierarchical selection (HS) the anchor layer's
+ *     selection bounds what the follower layers may pick.
+ *   - same page, Table 5: 64 indexer heads of 128 dims (64 rotary + 64 not).
  *
  * Readings where the pages are silent (each is listed with its reason in the
  * design notes of the repository):
@@ -424,8 +424,8 @@ int oracle_latent_reconstruct_scores(const void* q, int q_dt, const float* w, co
 /* cand_idx [B][C]: the anchor's kept positions, ascending, -1 padded (the
  * output of the anchor's own top-C).  Each follower f < Gf scores the latent
  * rows of those candidates with its absorbed query and keeps its own top-k
- * among them (LatentIndex, Abstract: followers independently refine a shared
- * candidate set proposed by the anchor).  Ties go to the lower position.
+ * among them (LatentIndex, Abstract: the anchor's selection is the pool each
+ * follower picks from, on its own scores).  Ties go to the lower position.
  * out_idx [B][Gf][k] token positions; out_scores / out_abs [B][Gf][C] indexed by
  * candidate slot (slots past the valid candidates are left untouched). */
 int oracle_hs_refine(const int32_t* cand_idx, int C, const void* q, int q_dt, const float* w,

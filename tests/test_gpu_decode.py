@@ -86,9 +86,9 @@ def test_fp8_conversion_covers_every_code():
 
 def test_fp8_decode_query_spanning_many_octaves():
     """fp8 keys against query rows whose elements span 2^0 .. 2^-30 inside each
-    head and whose heads differ by up to 2^40 in size: the fp8 path writes every
-    bf16 query row as two E4M3 rows under a per-head power-of-two scale, and
-    the scores must still meet the tolerance."""
+    head and whose heads differ by up to 2^40 in size.  The scan converts each
+    fp8 key to bf16 exactly and runs the bf16 product chain, so the scores meet
+    the tolerance however the query's magnitudes spread, with one head too."""
     x = inputs.make_decode(111, [3000, 1500, 40], k=256)
     rng = np.random.default_rng(1111)
     octave = 2.0 ** -(np.arange(128) % 31)
