@@ -113,6 +113,30 @@ size_t li_index_decode_ws(int32_t B, int64_t n_tok, int32_t max_len, int32_t k,
                           int32_t has_out_scores);
 
 /* ---------------------------------------------------------------------------
+ * li_index_decode_noalloc — li_index_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments, kernels and results, with the
+ * workspace taken from a static device array of LI_NOALLOC_SCRATCH_BYTES that
+ * the library holds on each GPU it runs on until the process ends.  The call
+ * allocates nothing; the first call on a device looks the array's address up
+ * (hipGetSymbolAddress).
+ *
+ *   A call whose li_index_decode_ws(B, n_tok, max_len, k, out_scores != NULL)
+ *   exceeds LI_NOALLOC_SCRATCH_BYTES returns LI_E_UNSUPPORTED before any
+ *   device work (the B = 32, 131072-token decode without out_scores needs
+ *   about 50 MiB).
+ *   Every call on one GPU shares that GPU's array: calls that can overlap on
+ *   one GPU (different streams, or concurrent host threads) race and must be
+ *   serialised by the caller.  Nothing in the array needs to start at zero:
+ *   the kernels write every scratch value they read in the same call.
+ * ------------------------------------------------------------------------- */
+#define LI_NOALLOC_SCRATCH_BYTES 67108864u /* 64 MiB */
+li_status li_index_decode_noalloc(const void* q, li_dtype q_dt, const float* w, const void* k_cache,
+                                  li_dtype k_dt, const float* k_scale, const int64_t* kv_off, int32_t B,
+                                  int64_t n_tok, int32_t max_len, int32_t H, int32_t D, int32_t k,
+                                  int32_t* out_idx, float* out_scores, void* stream);
+
+/* ---------------------------------------------------------------------------
  * li_index_prefill — the indexer over a prefill chunk of one sequence.
  *
  * T new query tokens at positions qpos0 .. qpos0+T-1 of an L-token cache that

@@ -22,9 +22,10 @@ LI_BF16, LI_FP8_E4M3, LI_FP16, LI_FP32 = range(4)
 LI_LATENT_FP16 = 0
 LI_LATENT_SPLIT_BF16 = 1
 LI_MAX_K = 16384
+LI_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # Every symbol include/li.h declares.
-SYMBOLS = ("li_index_decode", "li_index_decode_ws", "li_index_prefill", "li_index_prefill_ws",
+SYMBOLS = ("li_index_decode", "li_index_decode_ws", "li_index_decode_noalloc", "li_index_prefill", "li_index_prefill_ws",
            "li_latent_score_group", "li_latent_score_group_ws", "li_hs_refine", "li_hs_refine_ws",
            "li_latent_append", "li_latent_append_ws", "li_sparse_attention", "li_sparse_attention_ws", "li_key_row_bytes", "li_latent_row_bytes", "li_indexcache_plan", "li_topk", "li_topk_ws", "li_status_str", "li_last_error", "li_trace_events", "li_trace_count")
 
@@ -47,6 +48,7 @@ def lib():
         vp, i32, i64, sz, u32 = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t, C.c_uint32
         L.li_index_decode.argtypes = [vp, i32, vp, vp, i32, vp, vp, i32, i64, i32, i32, i32, i32, vp, vp, vp, sz, vp]
         L.li_index_decode_ws.argtypes = [i32, i64, i32, i32, i32]
+        L.li_index_decode_noalloc.argtypes = [vp, i32, vp, vp, i32, vp, vp, i32, i64, i32, i32, i32, i32, vp, vp, vp]
         L.li_index_prefill.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp]
         L.li_index_prefill_ws.argtypes = [i32, i32, i32, i32]
         L.li_latent_score_group.argtypes = [vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, i64, i32, i32, i32, i32, i32,
@@ -67,7 +69,8 @@ def lib():
         L.li_indexcache_plan.argtypes = [vp, i32, i32, vp]
         L.li_topk.argtypes = [vp, i64, vp, i32, i32, i32, vp, vp, sz, vp]
         L.li_topk_ws.argtypes = [i32, i32, i32]
-        for f in ("li_index_decode", "li_index_prefill", "li_latent_score_group", "li_hs_refine", "li_latent_append",
+        for f in ("li_index_decode", "li_index_decode_noalloc", "li_index_prefill", "li_latent_score_group", "li_hs_refine",
+                  "li_latent_append",
                   "li_sparse_attention", "li_topk"):
             getattr(L, f).restype = C.c_int32
         for f in ("li_index_decode_ws", "li_index_prefill_ws", "li_latent_score_group_ws", "li_hs_refine_ws",
@@ -138,6 +141,18 @@ def li_index_decode(q, w, k_cache, k_scale, kv_off, max_len, k, out_idx=None, ou
     _check(L.li_index_decode(_ptr(q), _dt(q), _ptr(w), _ptr(k_cache), _dt(k_cache), _ptr(k_scale), _ptr(kv_off), B,
                              n_tok, max_len, H, D, k, _ptr(out_idx), _ptr(out_scores), _ptr(wst), wsb,
                              _stream(stream)))
+    return out_idx
+
+
+def li_index_decode_noalloc(q, w, k_cache, k_scale, kv_off, max_len, k, out_idx, out_scores=None, stream=None):
+    """li_index_decode with the library's static device scratch as workspace
+    (nothing is allocated, here or in the library): the caller passes out_idx
+    [B,k] int32 (and out_scores [n_tok] fp32 or None)."""
+    B, H, D = q.shape
+    n_tok = k_cache.shape[0]
+    _check(lib().li_index_decode_noalloc(_ptr(q), _dt(q), _ptr(w), _ptr(k_cache), _dt(k_cache), _ptr(k_scale),
+                                         _ptr(kv_off), B, n_tok, max_len, H, D, k, _ptr(out_idx), _ptr(out_scores),
+                                         _stream(stream)))
     return out_idx
 
 

@@ -7,6 +7,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/li.h"
@@ -188,6 +189,35 @@ li_status check_ws(void* ws, size_t ws_bytes, size_t need) {
   return LI_OK;
 }
 
+// Device scratch of li_index_decode_noalloc, for callers that cannot
+// allocate: one array per GPU the library runs on, held until the process
+// ends.  Host code reaches it only through the address hipGetSymbolAddress
+// returns for the current device (the array's name is a host-side stand-in).
+constexpr size_t kScratchBytes = LI_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, looked up once per device.
+li_status scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(LI_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(LI_E_UNSUPPORTED, "device %d beyond the scratch table", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail(LI_E_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    if (!p) return fail(LI_E_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LI_OK;
+}
+
 }  // namespace
 
 namespace li {
@@ -234,12 +264,10 @@ size_t li_index_decode_ws(int32_t B, int64_t n_tok, int32_t max_len, int32_t k,
   return decode_ws(B, n_tok, max_len, has_out_scores != 0);
 }
 
-li_status li_index_decode(const void* q, li_dtype q_dt, const float* w, const void* k_cache,
-                          li_dtype k_dt, const float* k_scale, const int64_t* kv_off, int32_t B,
-                          int64_t n_tok, int32_t max_len, int32_t H, int32_t D, int32_t k,
-                          int32_t* out_idx, float* out_scores, void* ws, size_t ws_bytes,
-                          void* stream) {
-  g_err.clear();
+// Host-side argument checks of a decode call (everything but the workspace).
+static li_status check_decode_args(const void* q, li_dtype q_dt, const float* w, const void* k_cache,
+                                   li_dtype k_dt, const int64_t* kv_off, int32_t B, int64_t n_tok, int32_t max_len,
+                                   int32_t H, int32_t D, int32_t k, const int32_t* out_idx) {
   if (!q || !w || !k_cache || !kv_off || !out_idx)
     return fail(LI_E_NULL, "q, w, k_cache, kv_off and out_idx are required");
   if (q_dt != LI_BF16) return fail(LI_E_DTYPE, "decode q must be LI_BF16");
@@ -250,6 +278,17 @@ li_status li_index_decode(const void* q, li_dtype q_dt, const float* w, const vo
   if (n_tok >= (int64_t)1 << 40) return fail(LI_E_UNSUPPORTED, "n_tok too large");
   li_status st;
   if ((st = check_k(k)) || (st = check_heads(H, D, "D"))) return st;
+  return LI_OK;
+}
+
+li_status li_index_decode(const void* q, li_dtype q_dt, const float* w, const void* k_cache,
+                          li_dtype k_dt, const float* k_scale, const int64_t* kv_off, int32_t B,
+                          int64_t n_tok, int32_t max_len, int32_t H, int32_t D, int32_t k,
+                          int32_t* out_idx, float* out_scores, void* ws, size_t ws_bytes,
+                          void* stream) {
+  g_err.clear();
+  li_status st;
+  if ((st = check_decode_args(q, q_dt, w, k_cache, k_dt, kv_off, B, n_tok, max_len, H, D, k, out_idx))) return st;
   if ((st = check_ws(ws, ws_bytes, decode_ws(B, n_tok, max_len, out_scores != nullptr)))) return st;
   if (B == 0) return LI_OK;
   hipStream_t s = (hipStream_t)stream;
@@ -281,6 +320,25 @@ li_status li_index_decode(const void* q, li_dtype q_dt, const float* w, const vo
   tr.k = k;
   tr.out = out_idx;
   return hip_check(li::launch_topk_segmented(tr, sel, s), "topk launch", s);
+}
+
+li_status li_index_decode_noalloc(const void* q, li_dtype q_dt, const float* w, const void* k_cache,
+                                  li_dtype k_dt, const float* k_scale, const int64_t* kv_off, int32_t B,
+                                  int64_t n_tok, int32_t max_len, int32_t H, int32_t D, int32_t k,
+                                  int32_t* out_idx, float* out_scores, void* stream) {
+  g_err.clear();
+  li_status st;
+  if ((st = check_decode_args(q, q_dt, w, k_cache, k_dt, kv_off, B, n_tok, max_len, H, D, k, out_idx))) return st;
+  const size_t need = decode_ws(B, n_tok, max_len, out_scores != nullptr);
+  if (need > kScratchBytes)
+    return fail(LI_E_UNSUPPORTED,
+                "li_index_decode_noalloc: this call needs %zu bytes of scratch; the library's static scratch "
+                "holds %zu (use li_index_decode with a workspace)", need, kScratchBytes);
+  if (B == 0) return LI_OK;
+  void* ws = nullptr;
+  if ((st = scratch_ptr(&ws))) return st;
+  return li_index_decode(q, q_dt, w, k_cache, k_dt, k_scale, kv_off, B, n_tok, max_len, H, D, k, out_idx,
+                         out_scores, ws, kScratchBytes, stream);
 }
 
 size_t li_index_prefill_ws(int32_t T, int32_t L, int32_t k, int32_t has_out_scores) {

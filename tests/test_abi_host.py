@@ -99,6 +99,25 @@ def test_decode_validation():
     assert _decode(B=0) == li.LI_OK  # nothing to do: returns before any launch
 
 
+def test_noalloc_decode_host_checks():
+    """The allocation-free decode rejects a call its static scratch cannot hold,
+    and bad arguments, before any device work."""
+    L = li.lib()
+
+    def call(B=2, n_tok=100, max_len=60, H=64, sc=None, q=FAKE):
+        return L.li_index_decode_noalloc(q, li.LI_BF16, FAKE, FAKE, li.LI_FP8_E4M3, None, FAKE, B, n_tok, max_len,
+                                         H, 128, 16, FAKE, sc, None)
+
+    assert call(n_tok=1 << 25) == li.LI_E_UNSUPPORTED  # 128 MiB of scores alone
+    assert b"scratch" in L.li_last_error()
+    assert L.li_index_decode_ws(2, 1 << 25, 60, 16, 1) < li.LI_NOALLOC_SCRATCH_BYTES
+    assert call(n_tok=1 << 25, B=0) == li.LI_E_UNSUPPORTED  # the size check does not depend on B
+    assert call(q=None) == li.LI_E_NULL
+    assert call(H=65) == li.LI_E_UNSUPPORTED
+    assert call(B=-1) == li.LI_E_SHAPE
+    assert call(B=0) == li.LI_OK
+
+
 def test_prefill_validation():
     L = li.lib()
 
