@@ -590,9 +590,18 @@ def main():
     scan_ms, topk_ms = traced(torch, li, step, 2, args.steps)
     keys = B * Lk
     achieved = keys * FP8_KEY_BYTES / (scan_ms * 1e-3) / 1e9
+    # The read rate this GPU reaches for a plain stream of the same key bytes
+    # with the scan's load pattern (li_read_probe), timed the same way.
+    sink = torch.empty(li.LI_READ_PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        li.li_read_probe(kc, sink)
+    (probe_ms,) = traced(torch, li, lambda: li.li_read_probe(kc, sink), 1, args.steps)
+    probe_bytes = kc.numel() * kc.element_size()
+    probe_gbs = probe_bytes / (probe_ms * 1e-3) / 1e9
+    del sink
     traffic = load_traffic("decode_score", source_hash("decode.hip", "li_device.h"), keys)
     log(f"[bench] step {ms_per_step:.3f} ms, scan {scan_ms * 1e3:.1f} us ({achieved:.0f} GB/s), "
-        f"top-2048 {topk_ms * 1e3:.1f} us")
+        f"top-2048 {topk_ms * 1e3:.1f} us; read probe {probe_ms * 1e3:.1f} us ({probe_gbs:.0f} GB/s)")
 
     result = {
         "metric": METRIC,
@@ -613,6 +622,11 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "decode_score", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": keys * FP8_KEY_BYTES, "avg_launch_ms": scan_ms,
+                     "measured_read_ceiling": {
+                         "gbs": probe_gbs, "bytes": probe_bytes, "avg_launch_ms": probe_ms,
+                         "frac_of_ceiling": achieved / probe_gbs, "ceiling_frac_of_peak": probe_gbs / HBM_PEAK_GBS,
+                         "kernel": "read_probe_kernel (li_read_probe): the key bytes streamed with the scan's "
+                                   "load pattern, back to back, same timing method"},
                      "timing": "HIP start/stop events of the kernel's own launch (hipExtLaunchKernel), on "
                                "the library's stream, averaged over a repetition of the timed steps"},
         "components": {"decode_fp8_B32_L131072": {"scan_ms": scan_ms, "top2048_ms": topk_ms,

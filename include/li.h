@@ -361,6 +361,16 @@ size_t li_topk_ws(int32_t rows, int32_t n, int32_t k);
 void li_trace_events(void** events, int32_t capacity);
 int32_t li_trace_count(void);
 
+/* Read-bandwidth probe (measurement aid, not part of the computation): one
+ * kernel streams `bytes` bytes of `p` with the decode scan's load pattern
+ * (16-byte loads, 1 KB per wave per load, eight loads in flight per lane) and
+ * folds the data into one word per wave of `sink` (LI_READ_PROBE_SINK_WORDS
+ * uint32 words, device), so that its duration (e.g. through li_trace_events)
+ * gives the read rate this GPU reaches for such a stream.  p must be 16-byte
+ * aligned and bytes a multiple of 16 (else LI_E_SHAPE). */
+#define LI_READ_PROBE_SINK_WORDS 8192
+li_status li_read_probe(const void* p, size_t bytes, uint32_t* sink, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* li_status_str(li_status s);
 /* Detail of the last error on this thread (e.g. the HIP error text); "" if none. */

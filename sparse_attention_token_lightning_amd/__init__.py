@@ -23,11 +23,12 @@ LI_LATENT_FP16 = 0
 LI_LATENT_SPLIT_BF16 = 1
 LI_MAX_K = 16384
 LI_NOALLOC_SCRATCH_BYTES = 64 << 20
+LI_READ_PROBE_SINK_WORDS = 8192
 
 # Every symbol include/li.h declares.
 SYMBOLS = ("li_index_decode", "li_index_decode_ws", "li_index_decode_noalloc", "li_index_prefill", "li_index_prefill_ws",
            "li_latent_score_group", "li_latent_score_group_ws", "li_hs_refine", "li_hs_refine_ws",
-           "li_latent_append", "li_latent_append_ws", "li_sparse_attention", "li_sparse_attention_ws", "li_key_row_bytes", "li_latent_row_bytes", "li_indexcache_plan", "li_topk", "li_topk_ws", "li_status_str", "li_last_error", "li_trace_events", "li_trace_count")
+           "li_latent_append", "li_latent_append_ws", "li_sparse_attention", "li_sparse_attention_ws", "li_key_row_bytes", "li_latent_row_bytes", "li_indexcache_plan", "li_topk", "li_topk_ws", "li_status_str", "li_last_error", "li_trace_events", "li_trace_count", "li_read_probe")
 
 _lib = None
 
@@ -84,6 +85,8 @@ def lib():
         L.li_trace_events.restype = None
         L.li_trace_count.argtypes = []
         L.li_trace_count.restype = i32
+        L.li_read_probe.argtypes = [vp, sz, vp, vp]
+        L.li_read_probe.restype = i32
         _lib = L
     return _lib
 
@@ -267,6 +270,12 @@ def li_topk(scores, k, row_len=None, n=None, out_idx=None, ws=None, stream=None)
     _check(L.li_topk(_ptr(scores), stride, _ptr(row_len), rows, n, k, _ptr(out_idx), _ptr(wst), wsb,
                      _stream(stream)))
     return out_idx
+
+
+def li_read_probe(buf, sink, stream=None):
+    """Stream every byte of the CUDA tensor buf once (measurement aid);
+    sink is a [LI_READ_PROBE_SINK_WORDS] int32 CUDA tensor."""
+    _check(lib().li_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
 
 
 def li_trace_events(events, capacity):

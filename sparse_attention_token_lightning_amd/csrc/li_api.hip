@@ -257,6 +257,16 @@ void li_trace_events(void** events, int32_t capacity) {
 
 int32_t li_trace_count(void) { return g_trace_n; }
 
+li_status li_read_probe(const void* p, size_t bytes, uint32_t* sink, void* stream) {
+  g_err.clear();
+  if (!p || !sink) return fail(LI_E_NULL, "p and sink are required");
+  if (bytes % 16 != 0 || ((uintptr_t)p & 15) != 0)
+    return fail(LI_E_SHAPE, "p must be 16-byte aligned and bytes a multiple of 16");
+  trace_begin();
+  return hip_check(li::launch_read_probe(p, (int64_t)bytes, sink, (hipStream_t)stream), "read_probe launch",
+                   (hipStream_t)stream);
+}
+
 
 size_t li_index_decode_ws(int32_t B, int64_t n_tok, int32_t max_len, int32_t k,
                           int32_t has_out_scores) {

@@ -125,6 +125,11 @@ hipError_t launch_latent_append(const uint16_t* h, const uint16_t* w_enc, const 
                                 int32_t d_model, int32_t Dc, float* part, uint16_t* latent, bool fp8, float* c_scale,
                                 hipStream_t stream);
 
+// Read-bandwidth probe (measurement aid): streams bytes / 16 16-byte words of
+// p (16-byte aligned) and writes one fold per wave into sink
+// (LI_READ_PROBE_SINK_WORDS words).
+hipError_t launch_read_probe(const void* p, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
 // Opt-in input checks (LI_DEBUG_VALIDATE): validate_begin clears the device
 // record, the validate_* calls enqueue one check each, validate_end waits for
 // them and returns the first failed check (0 = none) and its element index.

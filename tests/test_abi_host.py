@@ -118,6 +118,14 @@ def test_noalloc_decode_host_checks():
     assert call(B=0) == li.LI_OK
 
 
+def test_read_probe_host_checks():
+    L = li.lib()
+    assert L.li_read_probe(None, 1024, FAKE, None) == li.LI_E_NULL
+    assert L.li_read_probe(FAKE, 1024, None, None) == li.LI_E_NULL
+    assert L.li_read_probe(FAKE, 1000, FAKE, None) == li.LI_E_SHAPE
+    assert L.li_read_probe(FAKE + 8, 1024, FAKE, None) == li.LI_E_SHAPE
+
+
 def test_prefill_validation():
     L = li.lib()
 
