@@ -128,7 +128,8 @@ def latent_absorb(q, q_dt, w_dec, w_dt, B, G, H, Dh, Dc):
 
 def latent_score_group(q, q_dt, w, w_dec, w_dt, latent, c_dt, c_scale, kv_off, G, H, Dh, Dc, k,
                        want_scores=True, c_blocks=1):
-    """c_scale: [n_tok] per-row scales, or [n_tok][c_blocks] (one per Dc/c_blocks values)."""
+    """c_scale: [n_tok] per-row scales, or [n_tok][c_blocks] with c_blocks = ceil(Dc / 128) (one per
+    128-value block, the last one shorter when Dc is not a multiple of 128)."""
     q, w_dec, latent = _arr(q, q_dt), _arr(w_dec, w_dt), _arr(latent, c_dt)
     w, c_scale = _f32(w), _f32(c_scale)
     kv_off = np.ascontiguousarray(kv_off, dtype=np.int64)
@@ -187,7 +188,7 @@ def encode_e4m3(v):
 def latent_append(h, h_dt, w_enc, w_dt, dst_row, latent, c_scale=None):
     """Latent-cache append: c[b][d] = sum_i h[b][i] * w_enc[d][i] (fp64), stored
     at row dst_row[b] of a copy of `latent`: [n_tok][Dc] raw bf16 (uint16), or
-    with c_scale ([n_tok][Dc/128] float32) E4M3 codes (uint8) with per-block
+    with c_scale ([n_tok][ceil(Dc/128)] float32) E4M3 codes (uint8) with per-block
     scales.  Returns (new latent, exact sums [B][Dc]) or, for fp8,
     (new latent, new scales, exact sums)."""
     h = _arr(h, h_dt)

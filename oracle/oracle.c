@@ -43,9 +43,10 @@
  *     the first layer's hidden state without giving the encoder; read as a
  *     linear down-projection c = W_enc h (W_enc stored [Dc][d_model]), the
  *     sum taken exactly and stored once as bfloat16, nearest, ties to even;
- *   - latent scales: c_scale holds c_nblk entries per row, entry j scaling
- *     values j*Dc/c_nblk onward (one per row, or one per 128-value block of an
- *     fp8 latent);
+ *   - latent scales: c_scale holds c_nblk entries per row: one scale for the
+ *     whole row (c_nblk = 1), or one per 128-value block of an fp8 latent
+ *     counted from the row's start, a width that is not a multiple of 128
+ *     ending in a shorter block (Dc = 192: 128 + 64; c_nblk = ceil(Dc / 128));
  *   - sparse-attention consumer: the selected rows of a latent KV cache
  *     shared by all heads (keys = the whole row, values = its first Dv
  *     values), softmax with a caller-given scale, -1 entries skipped.
@@ -308,17 +309,21 @@ int oracle_latent_absorb(const void* q, int q_dt, const void* w_dec, int w_dt, i
   return 0;
 }
 
-/* The scale of value c of latent row `row`: entry c / (Dc / c_nblk) of the
- * row's c_nblk scale entries (1 when there are none). */
-static double row_scale(const float* c_scale, int c_nblk, int Dc, int64_t row, int c) {
-  return c_scale ? (double)c_scale[row * c_nblk + c / (Dc / c_nblk)] : 1.0;
+/* The scale of value c of latent row `row` (1 when there are none): the
+ * row's one scale (c_nblk = 1) or its entry c / 128 (128-value blocks). */
+static double row_scale(const float* c_scale, int c_nblk, int64_t row, int c) {
+  if (!c_scale) return 1.0;
+  return (double)c_scale[row * c_nblk + (c_nblk == 1 ? 0 : c / 128)];
 }
+
+/* c_nblk is 1 or the number of 128-value blocks of a Dc-value row. */
+static int nblk_ok(int c_nblk, int Dc) { return c_nblk == 1 || c_nblk == (Dc + 127) / 128; }
 
 /* Score the shared latent cache for all G layers of each request, then take
  * each layer's own top-k (layer-specific selection).
  * latent [n_tok][Dc] (c_dt) with c_scale [n_tok][c_nblk] or NULL: scale entry j of a
- * row multiplies its values j*Dc/c_nblk .. (j+1)*Dc/c_nblk - 1 (c_nblk = 1: one scale
- * per row; Dc/128: one per 128-value block); w [B][G][H].
+ * row multiplies its values 128 j .. min(128 j + 127, Dc - 1) (c_nblk = 1: one scale
+ * per row; ceil(Dc / 128): one per 128-value block); w [B][G][H].
  * out_idx [B][G][k]; out_scores / out_abs [G][n_tok] (may be NULL). */
 int oracle_latent_score_group(const void* q, int q_dt, const float* w, const void* w_dec,
                               int w_dt, const void* latent, int c_dt, const float* c_scale, int c_nblk,
@@ -327,7 +332,7 @@ int oracle_latent_score_group(const void* q, int q_dt, const float* w, const voi
   if (!q || !w || !w_dec || !latent || !kv_off || !out_idx || B < 0 || G <= 0 || H <= 0 ||
       Dh <= 0 || Dc <= 0 || k <= 0)
     return -1;
-  if (!dt_ok(c_dt) || c_nblk < 1 || Dc % c_nblk != 0) return -1;
+  if (!dt_ok(c_dt) || !nblk_ok(c_nblk, Dc)) return -1;
   double* qt = (double*)malloc((size_t)(B > 0 ? B : 1) * G * H * Dc * sizeof(double));
   if (!qt) return -2;
   int rc = oracle_latent_absorb(q, q_dt, w_dec, w_dt, B, G, H, Dh, Dc, qt);
@@ -348,7 +353,7 @@ int oracle_latent_score_group(const void* q, int q_dt, const float* w, const voi
     } else {
       for (int64_t s = 0; s < L; ++s) {
         int64_t row = off + s;
-        for (int c = 0; c < Dc; ++c) cd[c] = row_scale(c_scale, c_nblk, Dc, row, c) * dec_at(latent, c_dt, row * Dc + c);
+        for (int c = 0; c < Dc; ++c) cd[c] = row_scale(c_scale, c_nblk, row, c) * dec_at(latent, c_dt, row * Dc + c);
         double acc = 0.0, mag = 0.0;
         for (int h = 0; h < H; ++h) {
           const double* qh = qt + ((int64_t)bl * H + h) * Dc;
@@ -383,7 +388,7 @@ int oracle_latent_reconstruct_scores(const void* q, int q_dt, const float* w, co
   if (!q || !w || !w_dec || !latent || !kv_off || !out_scores || B < 0 || G <= 0 || H <= 0 ||
       Dh <= 0 || Dc <= 0)
     return -1;
-  if (!dt_ok(q_dt) || !dt_ok(w_dt) || !dt_ok(c_dt) || c_nblk < 1 || Dc % c_nblk != 0) return -1;
+  if (!dt_ok(q_dt) || !dt_ok(w_dt) || !dt_ok(c_dt) || !nblk_ok(c_nblk, Dc)) return -1;
   int64_t n_tok = kv_off[B];
   int rc = 0;
 #pragma omp parallel for schedule(dynamic) reduction(min : rc)
@@ -395,7 +400,7 @@ int oracle_latent_reconstruct_scores(const void* q, int q_dt, const float* w, co
       rc = -2;
     } else {
       for (int64_t row = kv_off[b]; row < kv_off[b + 1]; ++row) {
-        for (int c = 0; c < Dc; ++c) cd[c] = row_scale(c_scale, c_nblk, Dc, row, c) * dec_at(latent, c_dt, row * Dc + c);
+        for (int c = 0; c < Dc; ++c) cd[c] = row_scale(c_scale, c_nblk, row, c) * dec_at(latent, c_dt, row * Dc + c);
         double acc = 0.0;
         for (int h = 0; h < H; ++h) {
           for (int j = 0; j < Dh; ++j) {
@@ -435,7 +440,7 @@ int oracle_hs_refine(const int32_t* cand_idx, int C, const void* q, int q_dt, co
   if (!cand_idx || !q || !w || !w_dec || !latent || !kv_off || !out_idx || C < 0 || B < 0 ||
       Gf <= 0 || H <= 0 || Dh <= 0 || Dc <= 0 || k <= 0)
     return -1;
-  if (!dt_ok(c_dt) || c_nblk < 1 || Dc % c_nblk != 0) return -1;
+  if (!dt_ok(c_dt) || !nblk_ok(c_nblk, Dc)) return -1;
   double* qt = (double*)malloc((size_t)(B > 0 ? B : 1) * Gf * H * Dc * sizeof(double));
   if (!qt) return -2;
   int rc = oracle_latent_absorb(q, q_dt, w_dec, w_dt, B, Gf, H, Dh, Dc, qt);
@@ -456,7 +461,7 @@ int oracle_hs_refine(const int32_t* cand_idx, int C, const void* q, int q_dt, co
     } else {
       for (int64_t j = 0; j < nv; ++j) {
         int64_t row = kv_off[b] + cand[j];
-        for (int c = 0; c < Dc; ++c) cd[c] = row_scale(c_scale, c_nblk, Dc, row, c) * dec_at(latent, c_dt, row * Dc + c);
+        for (int c = 0; c < Dc; ++c) cd[c] = row_scale(c_scale, c_nblk, row, c) * dec_at(latent, c_dt, row * Dc + c);
         double acc = 0.0, mag = 0.0;
         for (int h = 0; h < H; ++h) {
           const double* qh = qt + ((int64_t)bf * H + h) * Dc;
@@ -537,7 +542,8 @@ static uint8_t enc_e4m3_rne(double v) {
 
 /* Latent-cache append.  c_dt OR_BF16: latent [n_tok][Dc] bf16 codes (uint16).
  * c_dt OR_FP8_E4M3: latent [n_tok][Dc] E4M3 codes (uint8) and c_scale
- * [n_tok][Dc/128]: each 128-value block of a row is the exact sum rounded to
+ * [n_tok][ceil(Dc/128)]: each 128-value block of a row (the last one shorter when Dc
+ * is not a multiple of 128) is the exact sum rounded to
  * fp32, its scale the block's largest magnitude / 448 in fp32 (1 for an
  * all-zero block) and its codes E4M3 of (value / scale) taken in fp32, nearest
  * even, saturating: the quantisation steps in the precision of the kernel that
@@ -545,7 +551,7 @@ static uint8_t enc_e4m3_rne(double v) {
 int oracle_latent_append(const void* h, int h_dt, const void* w_enc, int w_dt, const int64_t* dst_row, int B,
                          int d_model, int Dc, void* latent, int c_dt, float* c_scale, int64_t n_tok, double* exact) {
   if (!dt_ok(h_dt) || !dt_ok(w_dt) || B < 0 || d_model <= 0 || Dc <= 0) return -1;
-  if (c_dt != OR_BF16 && !(c_dt == OR_FP8_E4M3 && Dc % 128 == 0 && c_scale)) return -1;
+  if (c_dt != OR_BF16 && !(c_dt == OR_FP8_E4M3 && c_scale)) return -1;
   for (int b = 0; b < B; ++b)
     if (dst_row[b] < 0 || dst_row[b] >= n_tok) return -1;
   double* row = (double*)malloc(sizeof(double) * (size_t)Dc);
@@ -562,15 +568,17 @@ int oracle_latent_append(const void* h, int h_dt, const void* w_enc, int w_dt, c
       for (int d = 0; d < Dc; ++d) ((uint16_t*)latent)[dst_row[b] * Dc + d] = enc_bf16_rne(row[d]);
       continue;
     }
-    for (int blk = 0; blk < Dc / 128; ++blk) {
+    const int nblk = (Dc + 127) / 128;
+    for (int blk = 0; blk < nblk; ++blk) {
+      const int d1 = 128 * blk + 128 < Dc ? 128 * blk + 128 : Dc;
       float amax = 0.0f;
-      for (int d = 128 * blk; d < 128 * blk + 128; ++d) {
+      for (int d = 128 * blk; d < d1; ++d) {
         const float f = fabsf((float)row[d]);
         if (f > amax) amax = f;
       }
       const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
-      c_scale[dst_row[b] * (Dc / 128) + blk] = sc;
-      for (int d = 128 * blk; d < 128 * blk + 128; ++d)
+      c_scale[dst_row[b] * nblk + blk] = sc;
+      for (int d = 128 * blk; d < d1; ++d)
         ((uint8_t*)latent)[dst_row[b] * Dc + d] = enc_e4m3_rne((double)((float)row[d] / sc));
     }
   }

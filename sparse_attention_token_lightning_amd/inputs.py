@@ -126,16 +126,23 @@ class Latent:
 
 
 def quantize_fp8_blocks(values, block=128):
-    """fp8 storage of a latent: per row, one fp32 scale per `block` values (the
-    block's largest magnitude / 448, or 1 for an all-zero block) and the
-    values / scale as OCP E4M3 codes (round to nearest even)."""
+    """fp8 storage of a latent: per row, one fp32 scale per `block` values
+    counted from the row's start (a width that is not a multiple of `block`
+    ends in a shorter block) -- the block's largest magnitude / 448, or 1 for
+    an all-zero block -- and the values / scale as OCP E4M3 codes (round to
+    nearest even)."""
     v = np.ascontiguousarray(values, dtype=np.float32)
     n, d = v.shape
-    blocks = v.reshape(n, d // block, block)
-    sc = (np.abs(blocks).max(axis=2) / np.float32(FP8_MAX)).astype(np.float32)
-    sc[sc == 0] = 1.0
-    codes = encode_fp8((blocks / sc[:, :, None]).reshape(n, d))
-    return codes, sc
+    nb = (d + block - 1) // block
+    sc = np.empty((n, nb), np.float32)
+    scaled = np.empty_like(v)
+    for j in range(nb):
+        blk = v[:, j * block:(j + 1) * block]
+        s = (np.abs(blk).max(axis=1) / np.float32(FP8_MAX)).astype(np.float32)
+        s[s == 0] = 1.0
+        sc[:, j] = s
+        scaled[:, j * block:(j + 1) * block] = blk / s[:, None]
+    return encode_fp8(scaled), sc
 
 
 def latent_to_fp8(x):

@@ -531,51 +531,68 @@ def _fp8_values(codes):
     return torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
 
 
-def test_fp8_latent_with_unit_block_scales_equals_the_bf16_latent_of_its_values():
+# Dc = 256: two full 128-value blocks; Dc = 192: a 128-value block and a 64-value tail block.
+DC_BLOCKS = [256, 192]
+
+
+@pytest.mark.parametrize("Dc", DC_BLOCKS)
+def test_fp8_latent_with_unit_block_scales_equals_the_bf16_latent_of_its_values(Dc):
     # every E4M3 value is exact in bf16, so both latents hold the same numbers
-    x, codes = _fp8_latent_case(41)
+    x, codes = _fp8_latent_case(41, Dc)
     ones = np.ones((x.n_tok, 2), np.float32)
     a_idx, a, _ = oracle.latent_score_group(x.q, "bf16", x.w, x.w_dec, "bf16", codes, "fp8_e4m3", ones, x.kv_off,
-                                            x.G, x.H, 128, 256, x.k, c_blocks=2)
+                                            x.G, x.H, 128, Dc, x.k, c_blocks=2)
     lat = inputs.encode_bf16(_fp8_values(codes))
     b_idx, b, _ = oracle.latent_score_group(x.q, "bf16", x.w, x.w_dec, "bf16", lat, "bf16", None, x.kv_off,
-                                            x.G, x.H, 128, 256, x.k)
+                                            x.G, x.H, 128, Dc, x.k)
     assert np.array_equal(a, b) and np.array_equal(a_idx, b_idx)
 
 
-def test_equal_block_scales_are_a_row_scale_and_a_block_scale_scales_its_block():
-    x, codes = _fp8_latent_case(42)
+@pytest.mark.parametrize("Dc", DC_BLOCKS)
+def test_equal_block_scales_are_a_row_scale_and_a_block_scale_scales_its_block(Dc):
+    x, codes = _fp8_latent_case(42, Dc)
     rng = np.random.default_rng(43)
     sig = rng.uniform(0.5, 2.0, x.n_tok).astype(np.float32)
     a = oracle.latent_score_group(x.q, "bf16", x.w, x.w_dec, "bf16", codes, "fp8_e4m3",
-                                  np.stack([sig, sig], 1), x.kv_off, x.G, x.H, 128, 256, x.k, c_blocks=2)[1]
+                                  np.stack([sig, sig], 1), x.kv_off, x.G, x.H, 128, Dc, x.k, c_blocks=2)[1]
     b = oracle.latent_score_group(x.q, "bf16", x.w, x.w_dec, "bf16", codes, "fp8_e4m3", sig, x.kv_off,
-                                  x.G, x.H, 128, 256, x.k)[1]
+                                  x.G, x.H, 128, Dc, x.k)[1]
     assert np.allclose(a, b, rtol=1e-13, atol=0)
-    # a scale of 2 on block 1 equals the latent with block 1's values doubled (exact in bf16)
-    two = np.ones((x.n_tok, 2), np.float32); two[:, 1] = 2.0
-    c = oracle.latent_score_group(x.q, "bf16", x.w, x.w_dec, "bf16", codes, "fp8_e4m3", two, x.kv_off,
-                                  x.G, x.H, 128, 256, x.k, c_blocks=2)[1]
-    v = _fp8_values(codes); v[:, 128:] *= 2
-    d = oracle.latent_score_group(x.q, "bf16", x.w, x.w_dec, "bf16", inputs.encode_bf16(v), "bf16", None,
-                                  x.kv_off, x.G, x.H, 128, 256, x.k)[1]
-    assert np.array_equal(c, d)
+    # a scale of 2 on block 1 (values 128 .. Dc-1) equals the latent with those values doubled (exact in bf16),
+    # and a scale of 2 on block 0 doubles values 0 .. 127 only
+    for blk, sl in ((1, slice(128, Dc)), (0, slice(0, 128))):
+        two = np.ones((x.n_tok, 2), np.float32); two[:, blk] = 2.0
+        c = oracle.latent_score_group(x.q, "bf16", x.w, x.w_dec, "bf16", codes, "fp8_e4m3", two, x.kv_off,
+                                      x.G, x.H, 128, Dc, x.k, c_blocks=2)[1]
+        v = _fp8_values(codes); v[:, sl] *= 2
+        d = oracle.latent_score_group(x.q, "bf16", x.w, x.w_dec, "bf16", inputs.encode_bf16(v), "bf16", None,
+                                      x.kv_off, x.G, x.H, 128, Dc, x.k)[1]
+        assert np.array_equal(c, d), f"block {blk}"
 
 
-def test_hs_and_reconstruction_take_block_scales_too():
-    x, codes = _fp8_latent_case(44)
+@pytest.mark.parametrize("Dc", DC_BLOCKS)
+def test_hs_and_reconstruction_take_block_scales_too(Dc):
+    x, codes = _fp8_latent_case(44, Dc)
     rng = np.random.default_rng(45)
     sc = rng.uniform(0.5, 2.0, (x.n_tok, 2)).astype(np.float32)
     g = oracle.latent_score_group(x.q, "bf16", x.w, x.w_dec, "bf16", codes, "fp8_e4m3", sc, x.kv_off,
-                                  x.G, x.H, 128, 256, x.k, c_blocks=2)
+                                  x.G, x.H, 128, Dc, x.k, c_blocks=2)
     r = oracle.latent_reconstruct_scores(x.q, "bf16", x.w, x.w_dec, "bf16", codes, "fp8_e4m3", sc, x.kv_off,
-                                         x.G, x.H, 128, 256, c_blocks=2)
+                                         x.G, x.H, 128, Dc, c_blocks=2)
     assert np.allclose(g[1], r, rtol=0, atol=1e-9 * np.abs(g[2]).max())
     cand = np.stack([np.arange(x.k, dtype=np.int32), np.arange(x.k, dtype=np.int32)])
     hi, hs, _ = oracle.hs_refine(cand, x.q, "bf16", x.w, x.w_dec, "bf16", codes, "fp8_e4m3", sc, x.kv_off, x.G,
-                                 x.H, 128, 256, 10, c_blocks=2)
+                                 x.H, 128, Dc, 10, c_blocks=2)
     for b in range(2):
         assert np.allclose(hs[b], g[1][:, x.kv_off[b]:x.kv_off[b] + x.k], rtol=1e-13, atol=0)
+
+
+def test_block_count_must_match_the_row_width():
+    """One scale per row, or ceil(Dc / 128) block scales; nothing else."""
+    x, codes = _fp8_latent_case(46, 192)
+    with pytest.raises(RuntimeError):
+        oracle.latent_score_group(x.q, "bf16", x.w, x.w_dec, "bf16", codes, "fp8_e4m3",
+                                  np.ones((x.n_tok, 3), np.float32), x.kv_off, x.G, x.H, 128, 192, x.k, c_blocks=3)
 
 
 def test_e4m3_encoder_matches_format_points_and_library_cast():
@@ -593,9 +610,10 @@ def test_e4m3_encoder_matches_format_points_and_library_cast():
     assert np.array_equal(got, ref)
 
 
-def test_latent_append_fp8_identity_encoder_is_the_block_quantisation_of_h():
+@pytest.mark.parametrize("d", DC_BLOCKS)
+def test_latent_append_fp8_identity_encoder_is_the_block_quantisation_of_h(d):
     rng = np.random.default_rng(24)
-    B, d = 3, 256
+    B = 3
     hv = (rng.standard_normal((B, d)) * np.exp(rng.uniform(-3, 3, (B, 1)))).astype(np.float32)
     h = _bf16_codes(hv)
     eye = _bf16_codes(np.eye(d))
