@@ -196,11 +196,12 @@ size_t li_index_prefill_ws(int32_t T, int32_t L, int32_t k, int32_t has_out_scor
  *   q       [B][G][H][Dh] LI_BF16;  w [B][G][H] fp32
  *   w_dec   [G][Dc][H*Dh] LI_BF16
  *   latent  [n_tok][Dc]   LI_BF16 with c_scale [n_tok] fp32 or NULL (= 1), or
- *           LI_FP8_E4M3 with c_scale [n_tok][Dc/128] fp32 (required): one scale
- *           per 128-value block; each code times its block's scale is rounded
+ *           LI_FP8_E4M3 with c_scale [n_tok][ceil(Dc/128)] fp32 (required): one scale
+ *           per 128-value block counted from the row's start (Dc = 192: blocks of
+ *           128 and 64 values); each code times its block's scale is rounded
  *           once to fp16 for the product (fp16 form only)
  *   kv_off  [B+1] int64, device;  max_len >= every L_b
- *   G >= 1;  H 2..64 (16..64 for LI_FP8_E4M3);  Dh must be 128;  Dc 128 or 256;
+ *   G >= 1;  H 2..64 (16..64 for LI_FP8_E4M3);  Dh must be 128;  Dc 128, 192 or 256;
  *   1 <= k <= LI_MAX_K
  *   out_idx    [B][G][k]  int32 positions, ascending, -1 padded
  *   out_scores [G][n_tok] fp32 or NULL
@@ -226,8 +227,8 @@ size_t li_latent_score_group_ws(int32_t B, int64_t n_tok, int32_t max_len, int32
  *
  *   q [B][Gf][H][Dh] LI_BF16; w [B][Gf][H] fp32; w_dec [Gf][Dc][H*Dh] LI_BF16
  *   latent [n_tok][Dc] LI_BF16 with c_scale [n_tok] or NULL, or LI_FP8_E4M3 with
- *   block scales [n_tok][Dc/128] (as in li_latent_score_group); kv_off [B+1] int64
- *   1 <= C <= 65536; Gf >= 1; H 2..64 (16..64 for LI_FP8_E4M3); Dh 128; Dc 128 or 256;
+ *   block scales [n_tok][ceil(Dc/128)] (as in li_latent_score_group); kv_off [B+1] int64
+ *   1 <= C <= 65536; Gf >= 1; H 2..64 (16..64 for LI_FP8_E4M3); Dh 128; Dc 128, 192 or 256;
  *   1 <= k <= LI_MAX_K
  *   out_idx    [B][Gf][k] int32 TOKEN positions (taken from cand_idx), ascending, -1 padded
  *   out_scores [B][Gf][C] fp32 score of candidate slot j, or NULL (slots past
@@ -259,13 +260,14 @@ size_t li_hs_refine_ws(int32_t B, int32_t C, int32_t Gf, int32_t H, int32_t Dc, 
  *           LI_DEBUG_VALIDATE)
  *   latent  [n_tok][Dc], written in place at the dst rows (other rows untouched):
  *           c_dt LI_BF16: bf16 (nearest even; c_scale unused, may be NULL);
- *           c_dt LI_FP8_E4M3: E4M3 codes, with c_scale [n_tok][Dc/128] fp32 written
- *           too: per 128-value block of a row, scale = the block's largest
+ *           c_dt LI_FP8_E4M3: E4M3 codes, with c_scale [n_tok][ceil(Dc/128)] fp32 written
+ *           too: per 128-value block of a row (the last one 64 values at Dc = 192),
+ *           scale = the block's largest
  *           magnitude / 448 (1 for an all-zero block) and codes = E4M3 of
  *           value / scale, nearest even, saturating; all in fp32.  This is the
  *           fp8 latent li_latent_score_group and li_hs_refine read.
  *   M >= 0 (M = 0 does nothing; h and dst_row may then be NULL);
- *   d_model a positive multiple of 64;  Dc 128 or 256
+ *   d_model a positive multiple of 64;  Dc 128, 192 or 256
  *   ws      li_latent_append_ws(M, d_model, Dc, c_dt) bytes (fp32 partial sums
  *           of the K split; 0 for bf16 output when one split covers K)
  * ------------------------------------------------------------------------- */

@@ -9,7 +9,7 @@
 // Multi-head Latent Attention that the page extends.
 //
 // The product is a dense contraction [M][d_model] x [d_model][Dc] with a
-// small Dc (128 or 256) and a long K, so it runs on bf16 MFMA
+// small Dc (128, 192 or 256) and a long K, so it runs on bf16 MFMA
 // (v_mfma_f32_16x16x32_bf16).  A workgroup takes 128 hidden-state rows and
 // every latent column, so h is read from HBM once; K is split over `S`
 // workgroups so that a few thousand rows still fill the chip.  With S > 1
@@ -31,6 +31,9 @@ constexpr int kApSlotsA = kApRows / 16 * 2 * 64;  // 16-byte fragment slots of t
 #define LI_APPEND_DEPTH 2
 #endif
 constexpr int kApDepth = LI_APPEND_DEPTH;  // K steps loaded ahead of their use
+
+// Lanes per row in the split sum: Dc / 4 quads rounded up to a power of two.
+__host__ __device__ constexpr int append_row_lanes(int dc) { return dc / 4 <= 32 ? 32 : (dc / 4 <= 64 ? 64 : 128); }
 
 __device__ __forceinline__ uint16_t bf16_rne(float v) {
   const uint32_t u = __builtin_bit_cast(uint32_t, v);
@@ -73,9 +76,10 @@ __global__ __launch_bounds__(kApThreads, 1) void append_gemm_kernel(
     uint16_t* __restrict__ latent) {
   constexpr int kSlotsB = DC / 16 * 2 * 64;
   constexpr int kPerA = kApSlotsA / 2 / kApThreads;  // 32-byte slot pairs per thread
-  constexpr int kPerB = kSlotsB / 2 / kApThreads;
+  constexpr int kPairsB = kSlotsB / 2;
+  constexpr int kPerB = (kPairsB + kApThreads - 1) / kApThreads;  // the last pass partial at Dc = 192
   constexpr int kWct = DC / 16 / 4;  // 16-column tiles per wave
-  static_assert(2 * kPerA * kApThreads == kApSlotsA && 2 * kPerB * kApThreads == kSlotsB, "tile split");
+  static_assert(2 * kPerA * kApThreads == kApSlotsA && kWct * 64 == DC, "tile split");
   __shared__ i32x4 tile[2][kApSlotsA + kSlotsB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -100,7 +104,8 @@ __global__ __launch_bounds__(kApThreads, 1) void append_gemm_kernel(
   }
 #pragma unroll
   for (int j = 0; j < kPerB; ++j) {
-    const int p = tid + j * kApThreads;
+    // pairs past kPairsB (Dc = 192) load the last pair again and store nothing
+    const int p = min(tid + j * kApThreads, kPairsB - 1);
     const int col = (p >> 6) * 16 + (p & 15);
     boff[j] = (int64_t)col * d_model + 16 * ((p >> 4) & 3);
   }
@@ -128,9 +133,11 @@ __global__ __launch_bounds__(kApThreads, 1) void append_gemm_kernel(
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) tile[buf][slot(j, ks)] = ra[u][j][ks];
 #pragma unroll
-    for (int j = 0; j < kPerB; ++j)
+    for (int j = 0; j < kPerB; ++j) {
+      if (kPerB * kApThreads != kPairsB && tid + j * kApThreads >= kPairsB) continue;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) tile[buf][kApSlotsA + slot(j, ks)] = rb[u][j][ks];
+    }
   };
 
   f32x4 acc[4][kWct];
@@ -215,17 +222,22 @@ __global__ __launch_bounds__(kApThreads, 1) void append_gemm_kernel(
 // (r, 0, quad) then adds the G group sums in order g = 0 .. G-1.  The order
 // depends only on S and G, never on scheduling.
 // F8: the row is stored as E4M3 codes with one fp32 scale per 128 values
-// (the block's largest magnitude / 448, or 1 for an all-zero block); a block
-// is 32 quads held by 32 consecutive lanes.
+// counted from the row's start (the last block shorter when Dc is not a
+// multiple of 128; the block's largest magnitude / 448, or 1 for an all-zero
+// block); a block is up to 32 quads held by 32 consecutive lanes.  A row's
+// quads sit on QP lanes, the next power of two of Dc / 4 (Dc = 192: 48 quads
+// on 64 lanes, the last 16 idle), so each block starts on a 32-lane boundary.
 template <int DC, bool F8>
 __global__ __launch_bounds__(1024) void append_reduce_kernel(const float* __restrict__ part, int32_t S, int32_t G,
                                                              int32_t M, const int64_t* __restrict__ dst,
                                                              uint16_t* __restrict__ latent, float* __restrict__ c_scale) {
   constexpr int QD = DC / 4;
+  constexpr int QP = append_row_lanes(DC);
   __shared__ f32x4 red[1024];
   const int tid = threadIdx.x;
-  const int q = tid % QD, g = (tid / QD) % G;
-  const int64_t row = (int64_t)blockIdx.x * (blockDim.x / (QD * G)) + tid / (QD * G);
+  const int qp = tid % QP, g = (tid / QP) % G;
+  const int q = qp < QD ? qp : QD - 1;  // idle lanes read the last quad and store nothing
+  const int64_t row = (int64_t)blockIdx.x * (blockDim.x / (QP * G)) + tid / (QP * G);
   const bool live = row < M;
   const int64_t plane = (int64_t)M * DC;
   const float* p = part + (live ? row : 0) * DC + 4 * q;
@@ -252,24 +264,27 @@ __global__ __launch_bounds__(1024) void append_reduce_kernel(const float* __rest
     __syncthreads();
     if (g != 0) return;
     for (int j = 1; j < G; ++j) {
-      const f32x4 u = red[tid + j * QD];
+      const f32x4 u = red[tid + j * QP];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] += u[e];
     }
   }
   if (!live) return;  // uniform over each row's lanes
+  const bool own = qp < QD;
   if constexpr (F8) {
-    float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    float am = own ? fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))) : 0.f;
 #pragma unroll
     for (int o = 1; o < 32; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+    if (!own) return;
     const float sc = am > 0.f ? am / 448.f : 1.f;
     uint32_t word = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) word |= e4m3_rne(v[e] / sc) << (8 * e);
     const int64_t r = dst[row];
     *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(latent) + r * DC + 4 * q) = word;
-    if ((q & 31) == 0) c_scale[r * (DC / 128) + q / 32] = sc;
+    if ((q & 31) == 0) c_scale[r * ((DC + 127) / 128) + q / 32] = sc;
   } else {
+    if (!own) return;
     const uint32_t lo = (uint32_t)bf16_rne(v[0]) | ((uint32_t)bf16_rne(v[1]) << 16);
     const uint32_t hi = (uint32_t)bf16_rne(v[2]) | ((uint32_t)bf16_rne(v[3]) << 16);
     *reinterpret_cast<i32x2*>(latent + dst[row] * DC + 4 * q) = i32x2{(int)lo, (int)hi};
@@ -302,6 +317,9 @@ hipError_t launch_latent_append(const uint16_t* h, const uint16_t* w_enc, const 
   if (Dc == 256)
     e = launch_kernel(append_gemm_kernel<256, D>, grid, dim3(kApThreads), 0, stream, h, w_enc, dst, M, d_model, per,
                       p, latent);
+  else if (Dc == 192)
+    e = launch_kernel(append_gemm_kernel<192, D>, grid, dim3(kApThreads), 0, stream, h, w_enc, dst, M, d_model, per,
+                      p, latent);
   else
     e = launch_kernel(append_gemm_kernel<128, D>, grid, dim3(kApThreads), 0, stream, h, w_enc, dst, M, d_model, per,
                       p, latent);
@@ -310,7 +328,7 @@ hipError_t launch_latent_append(const uint16_t* h, const uint16_t* w_enc, const 
   // workgroup holds 256 threads or one row's Dc/4 * G, whichever is larger.
   int32_t G = 1;
   while (G < 16 && G * 8 < S) G *= 2;
-  const int32_t per_row = Dc / 4 * G;
+  const int32_t per_row = append_row_lanes(Dc) * G;
   const int32_t rows = per_row >= 256 ? 1 : 256 / per_row;
   const dim3 grid_r((unsigned)((M + rows - 1) / rows)), block_r((unsigned)(rows * per_row));
   const float* cp = part;
@@ -318,10 +336,16 @@ hipError_t launch_latent_append(const uint16_t* h, const uint16_t* w_enc, const 
     if (Dc == 256)
       return launch_kernel(append_reduce_kernel<256, true>, grid_r, block_r, 0, stream, cp, S, G, M, dst, latent,
                            c_scale);
+    if (Dc == 192)
+      return launch_kernel(append_reduce_kernel<192, true>, grid_r, block_r, 0, stream, cp, S, G, M, dst, latent,
+                           c_scale);
     return launch_kernel(append_reduce_kernel<128, true>, grid_r, block_r, 0, stream, cp, S, G, M, dst, latent, c_scale);
   }
   if (Dc == 256)
     return launch_kernel(append_reduce_kernel<256, false>, grid_r, block_r, 0, stream, cp, S, G, M, dst, latent,
+                         c_scale);
+  if (Dc == 192)
+    return launch_kernel(append_reduce_kernel<192, false>, grid_r, block_r, 0, stream, cp, S, G, M, dst, latent,
                          c_scale);
   return launch_kernel(append_reduce_kernel<128, false>, grid_r, block_r, 0, stream, cp, S, G, M, dst, latent, c_scale);
 }

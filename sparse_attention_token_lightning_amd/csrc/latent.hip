@@ -170,7 +170,7 @@ constexpr int kLsThreads = 64 * kLsWaves;
 constexpr int kLsMaxTiles = 64;  // tiles (32 rows) per workgroup at most
 constexpr int kLsMaxRows = kLsMaxTiles * 32;
 
-// DC: latent width (128 or 256).  GATHER: rows come from the candidate list.
+// DC: latent width (128, 192 or 256).  GATHER: rows come from the candidate list.
 // CSCALE: a per-row latent scale is given.
 //
 // Wave l holds its layer's 64 x DC absorbed query in registers (four 16-head
@@ -196,7 +196,12 @@ __global__ __launch_bounds__(kLsThreads, 2) void latent_score_kernel(
   constexpr int KS = DC / 32;   // products per unit (K = 32 each)
   constexpr int NCR = DC / 8;   // 16-byte chunks per latent row
   constexpr int CPT = NCR / 8;  // chunks per producer thread (8 threads per row)
-  static_assert(CPT >= 1 && 32 * 8 == kLsThreads, "tile producer layout");
+  constexpr int NBLK = (DC + 127) / 128;  // fp8 block scales per row
+  // fp8 rows whose width is not a multiple of 128 (Dc = 192): a thread's 8*CPT
+  // values can straddle a block boundary and need not be 16-byte aligned, so
+  // they come as 8-byte chunks, each with its own block's scale.
+  constexpr bool F8N = F8 && (DC % 128 != 0);
+  static_assert(CPT >= 1 && CPT * 8 == NCR && 32 * 8 == kLsThreads, "tile producer layout");
   // Tile slot in MFMA fragment order: the 16 bytes lane l needs for product s
   // of row block rb sit at (rb * KS + s) * 64 + l, so fragment reads are
   // lane-linear; producer lanes (one row each) also write consecutive slots.
@@ -275,29 +280,47 @@ __global__ __launch_bounds__(kLsThreads, 2) void latent_score_kernel(
     else return off + s;
   };
   // F8: the thread's 8*CPT values are 8*CPT fp8 bytes (CPT / 2 loads) inside
-  // one 128-value block, whose scale comes with them.
-  auto gload = [&](i32x4 (&dst)[CPT], float& bsc, int tile) {
+  // one 128-value block, whose scale comes with them; F8N: CPT 8-byte loads
+  // (chunk i in dst[i].xy) and the scales of the blocks they fall in.
+  auto gload = [&](i32x4 (&dst)[CPT], float (&bsc)[2], int tile) {
     const int t = tile < ntiles ? tile : ntiles - 1;
     const int64_t row = row_of(tok0 + (int64_t)t * 32 + pt);
-    if constexpr (F8) {
+    if constexpr (F8N) {
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(latent) + row * DC + 8 * CPT * p;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const i32x2 v = *reinterpret_cast<const i32x2*>(src + 8 * i);
+        dst[i] = i32x4{v.x, v.y, 0, 0};
+      }
+      const int b0 = 8 * CPT * p / 128, b1 = (8 * CPT * p + 8 * CPT - 1) / 128;
+      bsc[0] = c_scale[row * NBLK + b0];
+      bsc[1] = c_scale[row * NBLK + b1];
+    } else if constexpr (F8) {
       const uint8_t* src = reinterpret_cast<const uint8_t*>(latent) + row * DC + 8 * CPT * p;
 #pragma unroll
       for (int i = 0; i < CPT / 2; ++i) dst[i] = ld16(src + 16 * i);
-      bsc = c_scale[row * (DC / 128) + 8 * CPT * p / 128];
+      bsc[0] = bsc[1] = c_scale[row * NBLK + 8 * CPT * p / 128];
     } else {
       const uint16_t* src = latent + row * DC + 8 * CPT * p;
 #pragma unroll
       for (int i = 0; i < CPT; ++i) dst[i] = ld16(src + 8 * i);
-      bsc = 1.0f;
+      bsc[0] = bsc[1] = 1.0f;
     }
   };
-  auto lstore = [&](int slot, const i32x4 (&src)[CPT], float bsc) {
+  auto lstore = [&](int slot, const i32x4 (&src)[CPT], const float (&bsc)[2]) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = CPT * p + i;
       i32x4 v;
-      if constexpr (F8) v = fp8x8_scaled_to_f16x8(src[i >> 1], i & 1, bsc);
-      else v = bf16x8_to_f16x8(src[i]);
+      if constexpr (F8N) {
+        // chunk c holds values 8c .. 8c+7, all in block 8c / 128
+        const bool second = (8 * c) / 128 != (8 * CPT * p) / 128;
+        v = fp8x8_scaled_to_f16x8(src[i], 0, second ? bsc[1] : bsc[0]);
+      } else if constexpr (F8) {
+        v = fp8x8_scaled_to_f16x8(src[i >> 1], i & 1, bsc[0]);
+      } else {
+        v = bf16x8_to_f16x8(src[i]);
+      }
       ktile[slot][((pt >> 4) * KS + (c >> 2)) * 64 + (c & 3) * 16 + (pt & 15)] = v;
     }
   };
@@ -317,7 +340,7 @@ __global__ __launch_bounds__(kLsThreads, 2) void latent_score_kernel(
   // other slot (whose readers finished tile i-1 before the previous barrier)
   // and loads tile i+3 into the register set tile i+1 had.
   i32x4 gk[2][CPT];
-  float gs[2];
+  float gs[2][2];
   float skr[2];
   gload(gk[0], gs[0], 0);
   gload(gk[1], gs[1], 1);
@@ -449,8 +472,9 @@ __global__ __launch_bounds__(kSpThreads) void latent_split_kernel(
     int G, int H, int tiles_per_block, int k, float* __restrict__ scores, SelWs sel) {
   constexpr int KS = DC / 32;    // products per unit and query part (K = 32 each)
   constexpr int NCR = DC / 8;    // 16-byte chunks per latent row
-  constexpr int CPT = NCR / 16;  // chunks per producer thread (16 threads per row)
-  static_assert(CPT >= 1 && 32 * 16 == kSpThreads, "tile producer layout");
+  constexpr int CPT = (NCR + 15) / 16;  // chunks per producer thread (up to 16 threads per row)
+  constexpr int NPROD = NCR / CPT;      // producer threads per row (12 at Dc = 192, else 16)
+  static_assert(CPT * NPROD == NCR && 32 * 16 == kSpThreads && NPROD % 2 == 0, "tile producer layout");
   // Tile slot in MFMA fragment order: the 16 bytes lane l needs for product s
   // of row block rb sit at (rb * KS + s) * 64 + l.
   __shared__ i32x4 ktile[2][32 * NCR];
@@ -531,13 +555,17 @@ __global__ __launch_bounds__(kSpThreads) void latent_split_kernel(
     if constexpr (GATHER) return off + cb[s];
     else return off + s;
   };
+  // Threads p >= NPROD (a pair of whole waves at Dc = 192) load a valid chunk
+  // too, so the loads stay unconditional, and store nothing.
+  const int pp = p < NPROD ? p : NPROD - 1;
   auto gload = [&](i32x4 (&dst)[CPT], int tile) {
     const int t = tile < ntiles ? tile : ntiles - 1;
-    const uint16_t* src = latent + row_of(tok0 + (int64_t)t * 32 + pt) * DC + 8 * CPT * p;
+    const uint16_t* src = latent + row_of(tok0 + (int64_t)t * 32 + pt) * DC + 8 * CPT * pp;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) dst[i] = ld16(src + 8 * i);
   };
   auto lstore = [&](int slot, const i32x4 (&src)[CPT]) {
+    if (NPROD * 32 < kSpThreads && p >= NPROD) return;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = CPT * p + i;
@@ -684,11 +712,17 @@ hipError_t launch_ls2(bool split, int Dc, dim3 grid, hipStream_t stream, const u
     if (Dc == 256)
       return launch_kernel(latent_split_kernel<256, GATHER, CSCALE>, grid, dim3(kSpThreads), 0, stream, qt16, qlo,
                            wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
+    if (Dc == 192)
+      return launch_kernel(latent_split_kernel<192, GATHER, CSCALE>, grid, dim3(kSpThreads), 0, stream, qt16, qlo,
+                           wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
     return launch_kernel(latent_split_kernel<128, GATHER, CSCALE>, grid, dim3(kSpThreads), 0, stream, qt16, qlo,
                          wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
   }
   if (Dc == 256)
     return launch_kernel(latent_score_kernel<256, GATHER, CSCALE, false>, grid, dim3(kLsThreads), 0, stream, qt16,
+                         wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
+  if (Dc == 192)
+    return launch_kernel(latent_score_kernel<192, GATHER, CSCALE, false>, grid, dim3(kLsThreads), 0, stream, qt16,
                          wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
   return launch_kernel(latent_score_kernel<128, GATHER, CSCALE, false>, grid, dim3(kLsThreads), 0, stream, qt16,
                        wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
@@ -701,6 +735,9 @@ hipError_t launch_ls8(int Dc, dim3 grid, hipStream_t stream, const uint16_t* qt1
                       int64_t n_tok, int G, int H, int tpb, int k, float* scores, const SelWs& sel) {
   if (Dc == 256)
     return launch_kernel(latent_score_kernel<256, GATHER, false, true>, grid, dim3(kLsThreads), 0, stream, qt16,
+                         wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
+  if (Dc == 192)
+    return launch_kernel(latent_score_kernel<192, GATHER, false, true>, grid, dim3(kLsThreads), 0, stream, qt16,
                          wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);
   return launch_kernel(latent_score_kernel<128, GATHER, false, true>, grid, dim3(kLsThreads), 0, stream, qt16,
                        wsc, latent, c_scale, kv_off, cand, C, n_tok, G, H, tpb, k, scores, sel);

@@ -178,6 +178,9 @@ li_status check_heads(int32_t H, int32_t D, const char* dname) {
 //  - latent, fp16 absorbed query: H = 2 fails (1.7e-2 * A), H = 4 1.9e-3,
 //    H = 8 6.6e-4, H = 16 4.1e-4, H = 64 1.5e-4.
 //  - latent, split bf16 query: H = 1 fails (1.8e-2 * A), H = 2 1.3e-4.
+// Latent widths with kernels: 128, 192 (128 + a 64-value block) and 256.
+bool dc_ok(int32_t Dc) { return Dc == 128 || Dc == 192 || Dc == 256; }
+
 constexpr int32_t kPrefillMinHeads = 8;
 constexpr int32_t kLatentFp16MinHeads = 16;  // below: the split form runs instead (bf16 latent)
 constexpr int32_t kLatentMinHeads = 2;
@@ -421,7 +424,7 @@ static li_status check_latent_common(li_dtype q_dt, li_dtype w_dt, li_dtype c_dt
     return fail(LI_E_UNSUPPORTED, "LI_LATENT_SPLIT_BF16 takes a bf16 latent only");
   li_status st;
   if ((st = check_heads(H, Dh, "Dh"))) return st;
-  if (Dc != 128 && Dc != 256) return fail(LI_E_UNSUPPORTED, "Dc must be 128 or 256 (got %d)", Dc);
+  if (!dc_ok(Dc)) return fail(LI_E_UNSUPPORTED, "Dc must be 128, 192 or 256 (got %d)", Dc);
   if (flags != LI_LATENT_FP16 && flags != LI_LATENT_SPLIT_BF16)
     return fail(LI_E_UNSUPPORTED, "unknown flags 0x%x", flags);
   if (H < kLatentMinHeads)
@@ -565,7 +568,7 @@ li_status li_hs_refine(const int32_t* cand_idx, int32_t C, const void* q, li_dty
 }
 
 size_t li_latent_append_ws(int32_t M, int32_t d_model, int32_t Dc, li_dtype c_dt) {
-  if (M <= 0 || d_model < 64 || d_model % 64 != 0 || (Dc != 128 && Dc != 256)) return 0;
+  if (M <= 0 || d_model < 64 || d_model % 64 != 0 || !dc_ok(Dc)) return 0;
   const int32_t S = li::append_splits(M, d_model);
   return S > 1 || c_dt == LI_FP8_E4M3 ? align_up((size_t)S * M * Dc * 4) : 0;
 }
@@ -581,7 +584,7 @@ li_status li_latent_append(const void* h, li_dtype h_dt, const void* w_enc, li_d
   if (c_dt == LI_FP8_E4M3 && !c_scale) return fail(LI_E_NULL, "an LI_FP8_E4M3 latent needs c_scale [n_tok][Dc/128]");
   if (M < 0 || d_model <= 0 || n_tok <= 0) return fail(LI_E_SHAPE, "need M >= 0, d_model >= 1 and n_tok >= 1");
   if (d_model % 64 != 0) return fail(LI_E_UNSUPPORTED, "d_model must be a multiple of 64 (got %d)", d_model);
-  if (Dc != 128 && Dc != 256) return fail(LI_E_UNSUPPORTED, "Dc must be 128 or 256 (got %d)", Dc);
+  if (!dc_ok(Dc)) return fail(LI_E_UNSUPPORTED, "Dc must be 128, 192 or 256 (got %d)", Dc);
   li_status st;
   if ((st = check_ws(ws, ws_bytes, li_latent_append_ws(M, d_model, Dc, c_dt)))) return st;
   if (M == 0) return LI_OK;

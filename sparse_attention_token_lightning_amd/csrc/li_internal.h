@@ -162,7 +162,7 @@ void validate_f32(const float* p, int64_t n, uint32_t check, hipStream_t s);
 void validate_bf16(const void* p, int64_t n, uint32_t check, hipStream_t s);
 void validate_fp8(const void* p, int64_t n, uint32_t check, hipStream_t s);
 void validate_cands(const int32_t* cand, int32_t B, int32_t C, const int64_t* off, hipStream_t s);
-// Latent codes and scales (nblk = Dc / 128 block scales per row for fp8, one
+// Latent codes and scales (ceil(Dc / 128) block scales per row for fp8, one
 // optional row scale for bf16); with fp16_form also the fp16-range limits.
 void validate_latent(const void* latent, bool fp8, int64_t n_tok, int32_t Dc, const float* c_scale,
                      bool fp16_form, hipStream_t s);

@@ -120,7 +120,7 @@ __device__ void check_latent_elem(const void* latent, bool fp8, int64_t i, int32
     else if (fp16_form && fabsf(__builtin_bit_cast(float, (uint32_t)v << 16)) > 65504.0f)
       report(kBadLatentRange, i);
   }
-  const int32_t blk = Dc / nblk;
+  const int32_t blk = nblk == 1 ? Dc : 128;
   const int64_t row = i / Dc;
   const int32_t c = (int32_t)(i - row * Dc);
   if (c_scale && c % blk == 0) {
@@ -181,13 +181,13 @@ void validate_fp8(const void* p, int64_t n, uint32_t check, hipStream_t s) {
 }
 void validate_latent(const void* latent, bool fp8, int64_t n_tok, int32_t Dc, const float* c_scale,
                      bool fp16_form, hipStream_t s) {
-  const int32_t nblk = fp8 ? Dc / 128 : 1;
+  const int32_t nblk = fp8 ? (Dc + 127) / 128 : 1;
   if (latent && n_tok > 0 && Dc > 0)
     latent_kernel<<<blocks_for(n_tok * Dc), kThreads, 0, s>>>(latent, fp8, n_tok, Dc, c_scale, nblk, fp16_form);
 }
 void validate_cand_latent(const int32_t* cand, int32_t B, int32_t C, const int64_t* off, const void* latent,
                           bool fp8, int32_t Dc, const float* c_scale, bool fp16_form, hipStream_t s) {
-  const int32_t nblk = fp8 ? Dc / 128 : 1;
+  const int32_t nblk = fp8 ? (Dc + 127) / 128 : 1;
   if (B > 0 && C > 0 && Dc > 0)
     cand_latent_kernel<<<blocks_for((int64_t)B * C * Dc), kThreads, 0, s>>>(cand, B, C, off, latent, fp8, Dc,
                                                                             c_scale, nblk, fp16_form);

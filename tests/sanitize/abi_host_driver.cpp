@@ -73,7 +73,7 @@ int main() {
   EXPECT(li_index_prefill(F, LI_FP8_E4M3, nullptr, Ff, F, LI_FP8_E4M3, nullptr, 0, 100, 0, 64, 128, 5, Fi,
                           nullptr, F, big, nullptr), LI_OK);
   // latent and HS
-  EXPECT(li_latent_score_group(F, LI_BF16, Ff, F, LI_BF16, F, LI_BF16, nullptr, Fo, 2, 1000, 600, 4, 64, 128, 192,
+  EXPECT(li_latent_score_group(F, LI_BF16, Ff, F, LI_BF16, F, LI_BF16, nullptr, Fo, 2, 1000, 600, 4, 64, 128, 160,
                                8, Fi, nullptr, 0, F, big, nullptr), LI_E_UNSUPPORTED);
   EXPECT(li_latent_score_group(F, LI_BF16, Ff, F, LI_BF16, F, LI_FP8_E4M3, nullptr, Fo, 2, 1000, 600, 4, 64, 128,
                                256, 8, Fi, nullptr, 0, F, big, nullptr), LI_E_NULL);

@@ -162,7 +162,8 @@ def test_latent_and_hs_validation():
 
     assert lat(q_dt=li.LI_FP8_E4M3) == li.LI_E_DTYPE
     assert lat(G=0) == li.LI_E_SHAPE
-    assert lat(Dc=192) == li.LI_E_UNSUPPORTED
+    assert lat(Dc=160) == li.LI_E_UNSUPPORTED
+    assert lat(Dc=192, wsb=1) == li.LI_E_WORKSPACE  # 128 + a 64-value block: accepted
     assert lat(Dh=64) == li.LI_E_UNSUPPORTED
     assert lat(flags=7) == li.LI_E_UNSUPPORTED
     assert lat(flags=2) == li.LI_E_UNSUPPORTED
@@ -224,7 +225,8 @@ def test_latent_append_validation_and_workspace():
     assert ap(c_dt=li.LI_FP8_E4M3) == li.LI_E_NULL  # fp8 output needs its block scales
     assert ap(M=-1) == li.LI_E_SHAPE and ap(d=0) == li.LI_E_SHAPE and ap(n_tok=0) == li.LI_E_SHAPE
     assert ap(d=7168 + 32) == li.LI_E_UNSUPPORTED
-    assert ap(Dc=192) == li.LI_E_UNSUPPORTED
+    assert ap(Dc=160) == li.LI_E_UNSUPPORTED
+    assert ap(Dc=192, wsb=1) == li.LI_E_WORKSPACE  # accepted: stops at the workspace check, before any launch
     assert ap(wsb=1) == li.LI_E_WORKSPACE
     assert ap(M=0, ws=None, wsb=0) == li.LI_OK
     assert ap(M=0, h=None, dst=None, ws=None, wsb=0) == li.LI_OK
@@ -273,6 +275,10 @@ def test_latentindex_storage_closed_form():
     assert (key, lat) == (132, 200)
     saving = 1 - (key + 15 * lat) / (61 * key)
     assert round(saving * 100, 1) == 61.1
+    # and it is a layout the library takes: an fp8 latent of 192 values per row
+    # passes the host checks of the group scan (this call stops at the workspace check)
+    assert L.li_latent_score_group(FAKE, li.LI_BF16, FAKE, FAKE, li.LI_BF16, FAKE, li.LI_FP8_E4M3, FAKE, FAKE, 2, 1000,
+                                   600, 4, 64, 128, 64 + 128, 8, FAKE, None, 0, FAKE, 1, None) == li.LI_E_WORKSPACE
     assert L.li_latent_row_bytes(256, li.LI_FP8_E4M3) == 264 and L.li_latent_row_bytes(256, li.LI_BF16) == 512
     assert L.li_key_row_bytes(128, li.LI_BF16) == 256 and L.li_key_row_bytes(0, li.LI_BF16) == 0
     assert L.li_latent_row_bytes(128, li.LI_FP32) == 0

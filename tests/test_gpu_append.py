@@ -147,7 +147,8 @@ def fp8_append_parity(x, what, exact_only=False):
     scale within that / 448 (plus fp32 rounding), and each code between the
     E4M3 roundings of (e - b) / scale and (e + b) / scale."""
     print(f"[append parity] {what} fp8 M={x.M} d_model={x.d_model} Dc={x.Dc}", flush=True)
-    nb = x.Dc // 128
+    nb = (x.Dc + 127) // 128  # 128-value blocks from the row's start (Dc = 192: 128 + 64)
+    blk = np.arange(x.Dc) // 128
     lat = torch.zeros((x.n_tok, x.Dc), dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
     sc = torch.zeros((x.n_tok, nb), dtype=torch.float32, device="cuda")
     li.li_latent_append(dev(x.h, "bf16"), dev(x.w_enc, "bf16"), dev(x.dst_row), lat, c_scale=sc)
@@ -165,10 +166,10 @@ def fp8_append_parity(x, what, exact_only=False):
     hv = np.abs(bf16_values(x.h))
     wv = np.abs(bf16_values(x.w_enc))
     b = (x.d_model + 64) * 2.0 ** -24 * (hv @ wv.T)
-    amax = np.abs(exact).reshape(x.M, nb, 128).max(axis=2)
-    bmax = b.reshape(x.M, nb, 128).max(axis=2)
+    amax = np.stack([np.abs(exact[:, blk == j]).max(axis=1) for j in range(nb)], 1)
+    bmax = np.stack([b[:, blk == j].max(axis=1) for j in range(nb)], 1)
     assert np.all(np.abs(gsc.astype(np.float64) * 448 - amax) <= bmax + 2.0 ** -22 * amax), f"{what}: scales"
-    s = np.repeat(gsc.astype(np.float64), 128, axis=1)
+    s = gsc.astype(np.float64)[:, blk]
     dec = lambda c: torch.from_numpy(np.ascontiguousarray(c)).view(torch.float8_e4m3fn).double().numpy()
     diff = got != ref
     if diff.any():
@@ -218,3 +219,17 @@ def test_appended_fp8_latent_feeds_the_scan():
                                           2, y.H, 128, 256, y.k, c_blocks=2)
     err = np.abs(ls.cpu().numpy().astype(np.float64) - rs)
     assert np.all(err <= 2e-3 * ra)
+
+
+def test_append_dc192_bf16_and_fp8():
+    """Dc = 192 (the shared latent of 64 rotary + 128 other dims): the
+    contraction's column tiles do not split evenly over its threads, and the
+    fp8 output has a 128-value block and a 64-value tail block."""
+    x = inputs.make_append(419, [5, 0, 300], [130, 1, 70], d_model=1024, Dc=192, dist="int")
+    append_parity(x, "int d1024 Dc192", exact_only=True)
+    fp8_append_parity(x, "int d1024 Dc192", exact_only=True)
+    x = inputs.make_append(420, [10, 4000], [150, 77], d_model=2048, Dc=192)
+    append_parity(x, "normal d2048 Dc192")
+    fp8_append_parity(x, "normal d2048 Dc192")
+    x = inputs.make_append(421, [3], [40], d_model=64, Dc=192)
+    append_parity(x, "normal d64 Dc192 (one split, direct write)")

@@ -251,3 +251,18 @@ def test_hs_batches_past_one_absorption_pass_and_few_heads():
     hs_parity(h, "HS B=17 fp16")
     hs_parity(h, "HS B=17 split", flags=li.LI_LATENT_SPLIT_BF16, tol=SPLIT_TOL)
     hs_parity(inputs.make_hs(344, [3000, 1200], C=1024, Gf=2, H=4, k=256), "HS H=4 (split form)")
+
+
+def test_latent_and_hs_dc192():
+    """Dc = 192 (64 rotary + 128 other dims, the shared latent of the page's
+    DeepSeek-V3.2 configuration): fp16, split and fp8 (a 128-value block and a
+    64-value tail block) forms, rows longer than a scan segment, and HS."""
+    x = inputs.make_latent(351, [3000, 0, 77, 1025], G=4, Dc=192, k=512)
+    latent_parity(x, "Dc192 fp16")
+    latent_parity(x, "Dc192 split", flags=li.LI_LATENT_SPLIT_BF16, tol=SPLIT_TOL)
+    latent_parity(inputs.latent_to_fp8(inputs.make_latent(352, [40000, 9000], G=3, Dc=192, k=2048)), "Dc192 fp8 L40000")
+    h = inputs.make_hs(353, [9000, 3000, 500], C=2048, Gf=3, Dc=192, k=512)
+    hs_parity(h, "HS Dc192")
+    hs_parity(h, "HS Dc192 split", flags=li.LI_LATENT_SPLIT_BF16, tol=SPLIT_TOL)
+    inputs.latent_to_fp8(h.followers)
+    hs_parity(h, "HS Dc192 fp8")
