@@ -198,8 +198,9 @@ size_t li_index_prefill_ws(int32_t T, int32_t L, int32_t k, int32_t has_out_scor
  *   latent  [n_tok][Dc]   LI_BF16 with c_scale [n_tok] fp32 or NULL (= 1), or
  *           LI_FP8_E4M3 with c_scale [n_tok][ceil(Dc/128)] fp32 (required): one scale
  *           per 128-value block counted from the row's start (Dc = 192: blocks of
- *           128 and 64 values); each code times its block's scale is rounded
- *           once to fp16 for the product (fp16 form only)
+ *           128 and 64 values); for the fp16 product each code is taken times
+ *           the scale's power of two (exact) and times its mantissa factor
+ *           (rounded to fp16), rounding once to fp16 (fp16 form only)
  *   kv_off  [B+1] int64, device;  max_len >= every L_b
  *   G >= 1;  H 2..64 (16..64 for LI_FP8_E4M3);  Dh must be 128;  Dc 128, 192 or 256;
  *   1 <= k <= LI_MAX_K

@@ -42,22 +42,33 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-// Eight OCP E4M3 values (bytes 8*half .. +7 of v), each times `scale`, as
-// fp16 (nearest even).  E4M3 -> bf16 is exact, so the only rounding is the
-// final one of code * scale.
-__device__ __forceinline__ i32x4 fp8x8_scaled_to_f16x8(i32x4 v, int half, float scale) {
+// A positive fp32 block scale split as 2^e * m with m in [1, 2): gfx950's
+// scaled fp8 conversion applies only a scale's power of two, so the codes are
+// converted exactly times 2^e and the mantissa factor m (rounded to fp16) is
+// applied with one packed fp16 multiply.
+struct F8Scale {
+  float pow2;  // 2^e
+  f16x2 m2;    // m, twice
+};
+__device__ __forceinline__ F8Scale f8_scale(float scale) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, scale);
+  const _Float16 m = (_Float16)__builtin_bit_cast(float, (u & 0x007FFFFFu) | 0x3F800000u);
+  return F8Scale{__builtin_bit_cast(float, u & 0x7F800000u), f16x2{m, m}};
+}
+
+// Eight OCP E4M3 values (bytes 8*half .. +7 of v), each times the block
+// scale, as fp16: code * 2^e is exact in fp16 (inside its range), then the
+// product with m rounds once (nearest even).  One conversion and one packed
+// multiply per two values.
+__device__ __forceinline__ i32x4 fp8x8_scaled_to_f16x8(i32x4 v, int half, F8Scale sc) {
   const int w[2] = {half ? v[2] : v[0], half ? v[3] : v[1]};
   i32x4 r;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    const i32x2 b = fp8x4_to_bf16x4(w[k]);
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const uint32_t u = (uint32_t)(m ? b.y : b.x);
-      const _Float16 lo = (_Float16)(__builtin_bit_cast(float, u << 16) * scale);
-      const _Float16 hi = (_Float16)(__builtin_bit_cast(float, u & 0xFFFF0000u) * scale);
-      r[2 * k + m] = (int)((uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16));
-    }
+    const f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[k], sc.pow2, false) * sc.m2;  // bytes 0, 1
+    const f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[k], sc.pow2, true) * sc.m2;   // bytes 2, 3
+    r[2 * k] = __builtin_bit_cast(int, lo);
+    r[2 * k + 1] = __builtin_bit_cast(int, hi);
   }
   return r;
 }
@@ -308,6 +319,9 @@ __global__ __launch_bounds__(kLsThreads, 2) void latent_score_kernel(
     }
   };
   auto lstore = [&](int slot, const i32x4 (&src)[CPT], const float (&bsc)[2]) {
+    F8Scale f0 = {}, f1 = {};
+    if constexpr (F8) f0 = f8_scale(bsc[0]);
+    if constexpr (F8N) f1 = f8_scale(bsc[1]);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = CPT * p + i;
@@ -315,9 +329,9 @@ __global__ __launch_bounds__(kLsThreads, 2) void latent_score_kernel(
       if constexpr (F8N) {
         // chunk c holds values 8c .. 8c+7, all in block 8c / 128
         const bool second = (8 * c) / 128 != (8 * CPT * p) / 128;
-        v = fp8x8_scaled_to_f16x8(src[i], 0, second ? bsc[1] : bsc[0]);
+        v = fp8x8_scaled_to_f16x8(src[i], 0, second ? f1 : f0);
       } else if constexpr (F8) {
-        v = fp8x8_scaled_to_f16x8(src[i >> 1], i & 1, bsc[0]);
+        v = fp8x8_scaled_to_f16x8(src[i >> 1], i & 1, f0);
       } else {
         v = bf16x8_to_f16x8(src[i]);
       }
