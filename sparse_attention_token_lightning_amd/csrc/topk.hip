@@ -270,6 +270,10 @@ __device__ void select_regs(const Row& row, const uint2 (&v)[R], int64_t count, 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   constexpr int kW = NT / 64;
   static_assert(R * kW <= NT, "one (round, wave) count per thread");
+  // Rounds past the last candidate hold nothing: skipped with a wave-uniform
+  // branch (the finishing workgroup's time is VALU issue on 2 waves per SIMD,
+  // and a 131072-score row at k = 2048 fills about 6 of 16 rounds).
+  const int nr = (int)((count + NT - 1) / NT);
 #pragma unroll 1
   for (int level = 1; level < 3; ++level) {
     const int shift = level == 1 ? 10 : 0;
@@ -278,8 +282,10 @@ __device__ void select_regs(const Row& row, const uint2 (&v)[R], int64_t count, 
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      if (j * NT + tid < (int)count && (v[j].x & pmask) == prefix)
-        atomicAdd(&hist[(v[j].x >> shift) & (uint32_t)(nb - 1)], 1u);
+      if (j < nr) {
+        if (j * NT + tid < (int)count && (v[j].x & pmask) == prefix)
+          atomicAdd(&hist[(v[j].x >> shift) & (uint32_t)(nb - 1)], 1u);
+      }
     }
     __syncthreads();
     hist_digit<NT>(hist, nb, remaining, wsum, out);
@@ -297,8 +303,12 @@ __device__ void select_regs(const Row& row, const uint2 (&v)[R], int64_t count, 
   auto eq = [&](int j) { return __ballot(j * NT + tid < cnt32 && (v[j].x & pmask) == prefix); };
 #pragma unroll
   for (int j = 0; j < R; ++j) {
-    const uint64_t bg = gt(j), be = eq(j);
-    if (lane == 0) rcnt[j * kW + wave] = ((uint32_t)__popcll(bg) << 16) | (uint32_t)__popcll(be);
+    uint32_t c = 0;
+    if (j < nr) {
+      const uint64_t bg = gt(j), be = eq(j);
+      c = ((uint32_t)__popcll(bg) << 16) | (uint32_t)__popcll(be);
+    }
+    if (lane == 0) rcnt[j * kW + wave] = c;
   }
   __syncthreads();
   {
@@ -313,14 +323,16 @@ __device__ void select_regs(const Row& row, const uint2 (&v)[R], int64_t count, 
   int32_t slot[R], src[R];
 #pragma unroll
   for (int j = 0; j < R; ++j) {
-    const uint64_t bg = gt(j), be = eq(j);
-    const uint32_t base = rcnt[j * kW + wave];
-    const uint32_t gb = (base >> 16) + (uint32_t)__popcll(bg & below);
-    const uint32_t eb = (base & 0xFFFFu) + (uint32_t)__popcll(be & below);
     slot[j] = -1;
-    if ((bg >> lane) & 1ull) slot[j] = (int32_t)(gb + (eb < m ? eb : m));
-    else if (((be >> lane) & 1ull) && eb < m) slot[j] = (int32_t)(gb + eb);
     src[j] = (int32_t)v[j].y;
+    if (j < nr) {
+      const uint64_t bg = gt(j), be = eq(j);
+      const uint32_t base = rcnt[j * kW + wave];
+      const uint32_t gb = (base >> 16) + (uint32_t)__popcll(bg & below);
+      const uint32_t eb = (base & 0xFFFFu) + (uint32_t)__popcll(be & below);
+      if ((bg >> lane) & 1ull) slot[j] = (int32_t)(gb + (eb < m ? eb : m));
+      else if (((be >> lane) & 1ull) && eb < m) slot[j] = (int32_t)(gb + eb);
+    }
   }
   emit_slots<R>(row, slot, src, kk);
 }
