@@ -366,6 +366,45 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkRows a, SelWs
   auto gkey = [&](int64_t i) { return score_key(row.p[i]); };
   auto gpos = [&](int64_t i) { return i; };
 
+  // Rows of at most kRegCand * kRowThreads (8192) scores, e.g. the HS
+  // followers' candidate rows: every key is loaded once into registers
+  // (thread t holds positions t + 512 j, position order), the level-0
+  // histogram comes from the registers, and the register selection runs on
+  // the whole row (keys below the threshold bin are never kept), instead of
+  // a second pass over the row into LDS.
+  if (n <= (int64_t)kRegCand * kRowThreads) {
+    uint2 v[kRegCand];
+#pragma unroll
+    for (int j = 0; j < kRegCand; ++j) {
+      const int64_t i = (int64_t)j * kRowThreads + tid;
+      v[j] = make_uint2(key_clamped(row.p, i, n), (uint32_t)i);
+    }
+    uint32_t bs, ab;
+    const bool own = how == kSelFull || ws.thr[(int64_t)r * 4 + 3] == 0u;
+    if (own) {
+      for (int i = tid; i < kSelBins; i += kRowThreads) hist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kRegCand; ++j)
+        if ((int64_t)j * kRowThreads + tid < n) atomicAdd(&hist[v[j].x >> kSelShift], 1u);
+      __syncthreads();
+      constexpr int PER = kSelBins / kRowThreads;
+      uint32_t h[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) h[i] = hist[kSelBins - 1 - (tid * PER + i)];
+      find_digit<kRowThreads, PER>(h, kSelBins - 1, (uint32_t)kk, wsum, shb);
+      bs = shb[0];
+      ab = shb[1];
+      __syncthreads();  // hist and shb are reused by the selection
+    } else {
+      bs = ws.thr[(int64_t)r * 4];
+      ab = ws.thr[(int64_t)r * 4 + 1];
+    }
+    select_regs<kRowThreads, kRegCand>(row, v, n, bs << kSelShift, 0xFFE00000u, (uint32_t)kk - ab, kk, hist, wsum,
+                                       rcnt, shb);
+    return;
+  }
+
   uint32_t bstar, above, eq;
   // kSelSelf rows whose scan histogram overflowed (thr[3] == 0) build it here.
   const bool build = how == kSelFull || ws.thr[(int64_t)r * 4 + 3] == 0u;
