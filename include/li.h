@@ -147,9 +147,16 @@ li_status li_index_decode_noalloc(const void* q, li_dtype q_dt, const float* w, 
  *   q        [T][H][D]  LI_FP8_E4M3 ; q_scale [T] fp32 or NULL (= 1)
  *   w        [T][H]     fp32
  *   k_cache  [L][D]     LI_FP8_E4M3 ; k_scale [L] fp32 or NULL (= 1)
- *   0 <= qpos0, qpos0 + T <= L;  H 8..64;  D must be 128;  1 <= k <= LI_MAX_K
+ *   0 <= qpos0, qpos0 + T <= L <= 2^26;  H 8..64;  D must be 128;  1 <= k <= LI_MAX_K
  *   out_idx    [T][k]   int32 positions, ascending, -1 padded
  *   out_scores [T][L]   fp32 or NULL; masked positions hold -inf
+ *
+ * The scan keeps, for each row, only the keys that can still be among its
+ * top k: those whose level-0 bin is at or above a floor, the bin of the k-th
+ * largest key seen so far, which rises as the row's keys go by.  The selection
+ * reads these (key, position) lists instead of all T x L scores.  The
+ * workspace (li_index_prefill_ws) sizes them for the worst case, 8 bytes per
+ * (t, s) pair: about T * L * 8 bytes.
  *
  * The products run on fp8 matrix cores, whose accumulation error is relative
  * to sum_d |q_d k_d| of a head rather than to its dot product; with fewer than

@@ -129,10 +129,13 @@ size_t decode_ws(int32_t B, int64_t n_tok, int32_t max_len, bool scores_given) {
   return s;
 }
 
+// The prefill's candidate lists are sized for the worst case (every visible
+// key of a row), so they cannot overflow; rows use a fraction of them.
 size_t prefill_ws(int32_t T, int32_t L, bool scores_given) {
+  (void)scores_given;
   size_t s = 0;
-  if (!scores_given) s += align_up((size_t)T * (size_t)L * 4);
   const size_t rows = T > 0 ? (size_t)T : 0;
+  s += align_up(rows * (size_t)(L > 0 ? L : 0) * 8) + align_up(rows * 4);
   s += align_up(rows * li::kLinRows * 128) + align_up(rows * li::kLinRows * 4);
   s += sel_ws(T > 0 ? T : 0, 0, 0);
   return s;
@@ -373,6 +376,8 @@ li_status li_index_prefill(const void* q, li_dtype q_dt, const float* q_scale, c
     return fail(LI_E_SHAPE, "need T >= 0, qpos0 >= 0 and qpos0 + T <= L (T=%d L=%d qpos0=%d)", T, L,
                 qpos0);
   li_status st;
+  if (L > li::kPrefillMaxL)
+    return fail(LI_E_SHAPE, "prefill needs L <= %d (got %d)", li::kPrefillMaxL, L);
   if ((st = check_k(k)) || (st = check_heads(H, D, "D"))) return st;
   if (H < kPrefillMinHeads)
     return fail(LI_E_UNSUPPORTED, "prefill needs H >= %d (got %d): the fp8 product's error with fewer heads "
@@ -390,7 +395,8 @@ li_status li_index_prefill(const void* q, li_dtype q_dt, const float* q_scale, c
     return st;
   trace_begin();
   Carver cv(ws);
-  float* scores = out_scores ? out_scores : (float*)cv.take((size_t)T * (size_t)L * 4);
+  uint2* clist = (uint2*)cv.take((size_t)T * (size_t)L * 8);
+  uint32_t* ccnt = (uint32_t*)cv.take((size_t)T * 4);
   uint8_t* uq = (uint8_t*)cv.take((size_t)T * li::kLinRows * 128);
   float* usc = (float*)cv.take((size_t)T * li::kLinRows * 4);
   const li::SelWs sel = carve_sel(cv, T, 0, 0, k);
@@ -399,11 +405,10 @@ li_status li_index_prefill(const void* q, li_dtype q_dt, const float* q_scale, c
     return st;
   if ((st = hip_check(li::launch_prefill_score((const uint8_t*)q, q_scale, w, uq, usc,
                                                (const uint8_t*)k_cache, k_scale, T, L, qpos0, H, k,
-                                               out_scores != nullptr, scores, sel, s),
+                                               out_scores, sel, clist, ccnt, s),
                       "prefill_score launch", s)))
     return st;
   li::TopkRows tr = {};
-  tr.scores = scores;
   tr.mode = li::kRowsCausal;
   tr.rows = T;
   tr.row_stride = L;
@@ -411,7 +416,7 @@ li_status li_index_prefill(const void* q, li_dtype q_dt, const float* q_scale, c
   tr.qpos0 = qpos0;
   tr.k = k;
   tr.out = out_idx;
-  return hip_check(li::launch_topk_self(tr, sel, s), "topk launch", s);
+  return hip_check(li::launch_topk_list(tr, sel, clist, ccnt, s), "topk launch", s);
 }
 
 static li_status check_latent_common(li_dtype q_dt, li_dtype w_dt, li_dtype c_dt, const float* c_scale,

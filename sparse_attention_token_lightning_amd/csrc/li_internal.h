@@ -63,6 +63,10 @@ int32_t seg_cap_for(int32_t k);
 int64_t seg_len_for(int64_t rows, int64_t max_len);
 // Top-k from scan-built thresholds, one workgroup per row collecting its own candidates.
 hipError_t launch_topk_self(const TopkRows& a, const SelWs& ws, hipStream_t stream);
+// Top-k of causal rows (a.n = L, a.qpos0, a.row_stride = L) given as the
+// prefill scan's candidate lists (list [rows][L] pairs, lcnt [rows]).
+hipError_t launch_topk_list(const TopkRows& a, const SelWs& ws, const uint2* list, const uint32_t* lcnt,
+                            hipStream_t stream);
 // Positions of one row covered by one scan workgroup (decode / latent).
 int64_t decode_chunk(int64_t n_tok);
 int64_t latent_chunk(int64_t n_tok);
@@ -74,18 +78,22 @@ hipError_t launch_decode_score(const uint16_t* q, const float* w, const void* kc
                                int64_t n_tok, int32_t max_len, int32_t H, int32_t k,
                                float* scores, const SelWs& sel, hipStream_t stream);
 
-// Prefill scan: scores[t][s] for s <= qpos0 + t; with fill_masked also -inf
-// for the masked rest of every row.  Rows with more than k visible keys get
-// their threshold bin in sel.thr.
 // Prefill: u = sum_h w_h q_hat_h per token as kLinRows fp8 rows + scales
-// (uq [T][4][128] bytes, usc [T][4]), then the causal scan.
+// (uq [T][4][128] bytes, usc [T][4]), then the causal scan, which appends
+// each row's candidates (keys that can still be among its top k) to a list
+// and leaves the threshold bin of rows with more than k visible keys in
+// sel.thr.  kPrefillMaxL bounds the cache length so that the candidate rows
+// of one wave fit one buffer resource.
 constexpr int kLinRows = 4;
+constexpr int32_t kPrefillMaxL = 1 << 26;
 hipError_t launch_prefill_linear(const uint8_t* q, const float* w, int32_t T, int32_t H, uint8_t* uq,
                                  float* usc, hipStream_t stream);
+// scores: the dense [T][L] output (out_scores) or null; clist [T][L] (key,
+// position) pairs and ccnt [T] receive each row's candidate list.
 hipError_t launch_prefill_score(const uint8_t* q, const float* q_scale, const float* w,
                                 const uint8_t* uq, const float* usc, const uint8_t* kc,
                                 const float* k_scale, int32_t T, int32_t L, int32_t qpos0, int32_t H,
-                                int32_t k, bool fill_masked, float* scores, const SelWs& sel,
+                                int32_t k, float* scores, const SelWs& sel, uint2* clist, uint32_t* ccnt,
                                 hipStream_t stream);
 
 // Latent absorption: qt16[b][l][h][Dc] (range-scaled by 2^e per row) and

@@ -33,6 +33,15 @@
 //
 // A wave owns whole rows, so it also builds each row's level-0 selection
 // histogram in LDS and finds the row's threshold bin for the top-k itself.
+//
+// Candidates instead of a dense score matrix: a row's final top-k threshold is
+// at least the k-th largest key seen so far, so a key whose level-0 bin is
+// below the bin of that running k-th largest can never be selected.  Each row
+// keeps such a floor (recomputed from its LDS histogram whenever k more keys
+// have passed it) and appends the (key, position) pairs at or above it, in
+// position order, to its own candidate list; on N(0,1)-like rows of 65536 keys
+// at k = 2048 that is about a sixth of the row.  The dense scores are written
+// only when the caller asks for them.
 #include "li_device.h"
 #include "li_internal.h"
 #include "li_select.h"
@@ -43,6 +52,12 @@ namespace {
 constexpr int kPfWaves = 4;
 constexpr int kPfTokPerWave = 2;
 constexpr int kPfTokPerBlock = kPfWaves * kPfTokPerWave;
+// Buffer resource word 3 for gfx9 parts (32-bit data format, raw
+// addressing), and an offset past the end of any resource: a store there is
+// dropped by the range check.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr uint32_t kBufferDrop = 0x80000000u;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 __device__ __forceinline__ i32x8 ld32(const uint8_t* p) {
   const i32x4 x = ld16(p), y = ld16(p + 16);
@@ -55,32 +70,67 @@ __device__ __forceinline__ i32x8 ld32(const uint8_t* p) {
 // 65535 carries into its neighbour or wraps, so the bins then no longer sum to
 // the row's visible count; that is detected here and the row is marked for
 // the top-k kernel to rebuild its histogram itself (thr[3] = 0).
-__device__ __forceinline__ uint32_t hist16(const uint32_t* h, int b) { return (h[b >> 1] >> (16 * (b & 1))) & 0xFFFFu; }
 
-// The wave's lanes each own 32 consecutive bins of a row's histogram (from the
-// top); the lane whose bins cross the kk-th largest key writes the threshold.
-__device__ void wave_find_bin(const uint32_t* hist, uint32_t kk, uint32_t n, uint32_t* thr) {
-  const int lane = threadIdx.x & 63;
-  constexpr int PER = kSelBins / 64;
-  uint32_t sum = 0;
-  for (int i = 0; i < PER; ++i) sum += hist16(hist, kSelBins - 1 - (lane * PER + i));
-  const uint32_t incl = wave_incl_scan(sum);
-  const uint32_t total = __shfl(incl, 63, 64);
-  if (total != n) {  // a bin overflowed
-    if (lane == 0) thr[3] = 0u;
-    return;
-  }
-  uint32_t run = incl - sum;
-  for (int i = 0; i < PER; ++i) {
-    const uint32_t h = hist16(hist, kSelBins - 1 - (lane * PER + i));
-    if (run < kk && run + h >= kk) {
-      thr[0] = (uint32_t)(kSelBins - 1 - (lane * PER + i));
-      thr[1] = run;
-      thr[2] = h;
-      thr[3] = 1u;
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
+
+// Where the kk-th largest key of a row falls in its histogram: the bin, the
+// keys in bins above it and in it.  found is false when the row holds fewer
+// than kk keys; ok is false when the bins do not sum to the row's count.
+struct Cross {
+  uint32_t bin, above, eq;
+  bool found, ok;
+};
+
+// Both rows of a wave at once: lane half g takes the histogram of row slot g
+// (packed words hist[g * kSelBins / 2 ...]) holding `counted` keys.  Lane c of
+// the half sums bins [64c, 64c + 64) with eight 16-byte reads; a suffix sum
+// over the half finds the lane whose bins hold the crossing, then each lane
+// reads one word (two bins) of that lane's range and a second suffix sum finds
+// the bin.  Every lane of the half returns its row's result.
+__device__ Cross pair_cross(const uint32_t* hist, uint32_t kk, uint32_t counted) {
+  const int lane = threadIdx.x & 63, c = lane & 31, g = lane >> 5;
+  const uint32_t* h = hist + (kSelBins / 2) * g;
+  const i32x4* p = reinterpret_cast<const i32x4*>(h + 32 * c);
+  i32x4 v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = p[j];
+  const u16x2 ones = {1, 1};
+  auto add2 = [&](int w, uint32_t acc) { return __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, w), ones, acc, false); };
+  uint32_t s = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s = add2(v[j].x, add2(v[j].y, add2(v[j].z, add2(v[j].w, s))));
+  // keys in the bins of lanes >= c of the half
+  auto suffix = [&](uint32_t x) {
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) {
+      const uint32_t o = (uint32_t)__shfl_down((int)x, d, 32);
+      x += c + d < 32 ? o : 0u;
     }
-    run += h;
-  }
+    return x;
+  };
+  const uint32_t suf = suffix(s);
+  Cross r;
+  r.ok = (uint32_t)__shfl((int)suf, 0, 32) == counted;
+  const uint64_t m1 = __builtin_amdgcn_ballot_w64(suf - s < kk && suf >= kk);
+  const uint32_t h1 = (uint32_t)(m1 >> (32 * g));
+  r.found = h1 != 0u;
+  const int c1 = r.found ? __builtin_ctz(h1) : 0;
+  const uint32_t above1 = (uint32_t)__shfl((int)(suf - s), c1, 32);
+  const uint32_t w = h[32 * c1 + c];
+  const uint32_t lo = w & 0xFFFFu, hi = w >> 16, cnt = lo + hi;
+  const uint32_t suf2 = suffix(cnt) + above1;
+  const uint64_t m2 = __builtin_amdgcn_ballot_w64(suf2 - cnt < kk && suf2 >= kk);
+  const uint32_t h2 = (uint32_t)(m2 >> (32 * g));
+  const int c2 = h2 ? __builtin_ctz(h2) : 0;
+  // in lane c2: the upper bin of its word first
+  const uint32_t ab = suf2 - cnt;
+  const bool upper = ab + hi >= kk;
+  const uint32_t bin = (uint32_t)(64 * c1 + 2 * c) + (upper ? 1u : 0u);
+  r.bin = (uint32_t)__shfl((int)bin, c2, 32);
+  r.above = (uint32_t)__shfl((int)(upper ? ab : ab + hi), c2, 32);
+  r.eq = (uint32_t)__shfl((int)(upper ? hi : lo), c2, 32);
+  r.found = r.found && h2 != 0u;
+  return r;
 }
 
 constexpr int kLinTerms = kLinRows;  // fp8 rows per token for u
@@ -90,6 +140,7 @@ constexpr int kPfWrite = 2;  // ... and written to LDS this many tiles before
 constexpr int kPfRegs = kPfLead - kPfWrite + 1;  // register slots for loads in flight
 static_assert(kPfRegs == 4 && kPfRing == 4, "the main loop is unrolled by 4");
 constexpr int kTileBytes = 32 * 128;
+constexpr int kFloorGrowShift = 1;
 
 // u[t][d] = sum_h w[t][h] * q_hat[t][h][d] in fp32, then split into
 // kLinTerms fp8 rows: row i holds round(r_i * 2^-e_i) with 2^e_i chosen so the
@@ -145,14 +196,16 @@ __global__ __launch_bounds__(256) void prefill_linear_kernel(const uint8_t* __re
   }
 }
 
-template <bool KSCALE>
+// DENSE: also write every score (out_scores given).  clist [T][L] (key,
+// position) pairs and ccnt [T] receive each row's candidate list.
+template <bool KSCALE, bool DENSE>
 __global__ __launch_bounds__(256) void prefill_score_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ uq, const float* __restrict__ usc, const uint8_t* __restrict__ kc,
     const float* __restrict__ k_scale, int T, int L, int qpos0, int H, int k, int fill_masked,
-    float* __restrict__ scores, uint32_t* __restrict__ thr) {
+    float* __restrict__ scores, uint32_t* __restrict__ thr, uint2* __restrict__ clist, uint32_t* __restrict__ ccnt) {
   static_assert(kPfTokPerWave == 2 && kPfWaves == 4, "lane half g finishes token slot g; 4 loader waves");
-  __shared__ uint32_t phist[kPfWaves][kPfTokPerWave][kSelBins / 2];
+  __shared__ __attribute__((aligned(16))) uint32_t phist[kPfWaves][kPfTokPerWave][kSelBins / 2];
   // Key tiles shared by the workgroup's waves (which walk the same keys): 32
   // keys x 128 bytes per slot, 16-byte chunk c of key r stored at chunk
   // c ^ (r & 7) so that the MFMA operand reads are free of bank conflicts.
@@ -215,6 +268,9 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
   // This half's token (the one lane l finishes: slot l >> 5) and its scale.
   const int tg = trow[g];
   const float sq = (q_scale ? q_scale[tg] : 1.0f) * 0.5f;
+  // The last key position this lane's row counts (-1 for a slot past the end
+  // of the chunk): visible keys inside the cache.
+  const int last_counted = g < nt ? min(qpos0 + tg, L - 1) : -1;
 
   // Tiles this wave needs, and tiles the workgroup walks (every wave takes
   // part in every tile's barrier; the extra tiles are fully masked for it).
@@ -256,6 +312,17 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
     else return 1.0f;
   };
 
+  // Candidate list state: per row slot, the number of pairs appended (nc0,
+  // nc1, wave-uniform); the floor bin of the lane's own row.
+  uint32_t floor_bin = 0u, nc0 = 0u, nc1 = 0u;
+  // The wave's candidate rows as one buffer resource (L <= kPrefillMaxL keeps
+  // it under 1 GiB).  A lane with nothing to append stores at an offset past
+  // its end, which the hardware drops: the store is straight-line code in
+  // every tile, so the waits for the key loads in flight stay exact.
+  const uint32_t row_bytes = (uint32_t)L * 8u;
+  const __amdgpu_buffer_rsrc_t lrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      clist + (int64_t)(nt > 0 ? t_base : 0) * L, (short)0, (int)(row_bytes * (uint32_t)nt), kBufferWord3);
+  const uint32_t row_off = (uint32_t)g * row_bytes;
   auto compute = [&](const i32x8 (&kb)[2], float sk, int it, bool live) {
     const int s = it * 32 + col;
     const int srow = key_row(it);
@@ -306,12 +373,39 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
     const float val = vis ? pa * sq * sk : -INFINITY;
     // Straight-line store (a lane past the end rewrites row L-1 with its own
     // value) so the loads of the next tiles stay in flight.
-    scores[(int64_t)tg * L + srow] = val;
+    if constexpr (DENSE) scores[(int64_t)tg * L + srow] = val;
     // Unconditional LDS update (adds 0 where the score is not counted), so
     // the tile stays one basic block.
-    const uint32_t b = score_key(val) >> kSelShift;
-    const uint32_t inc = (live && g < nt && it < n_tiles && s < L && vis) ? 1u : 0u;
-    atomicAdd(&phist[wave][g][b >> 1], inc << (16 * (b & 1)));
+    const uint32_t key = score_key(val), b = key >> kSelShift;
+    const bool counted = (live & (it < n_tiles)) & (s <= last_counted);
+    atomicAdd(&phist[wave][g][b >> 1], (counted ? 1u : 0u) << (16 * (b & 1)));
+    // Append the keys at or above the floor, ranked within the half by the
+    // ballot (ascending key position = lane order).  The upper half's rank
+    // counts the lower half's kept lanes too; its base takes them off.
+    const bool keep = counted && b >= floor_bin;
+    const uint64_t km = __builtin_amdgcn_ballot_w64(keep);
+    const uint32_t klo = (uint32_t)km, khi = (uint32_t)(km >> 32);
+    const uint32_t clo = (uint32_t)__builtin_popcount(klo), chi = (uint32_t)__builtin_popcount(khi);
+    const uint32_t rank = __builtin_amdgcn_mbcnt_hi(khi, __builtin_amdgcn_mbcnt_lo(klo, 0u));
+    const uint32_t off = keep ? row_off + 8u * (rank + (g ? nc1 - clo : nc0)) : kBufferDrop;
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{key, (uint32_t)srow}, lrsrc, off, 0, 0);
+    nc0 += clo;
+    nc1 += chi;
+  };
+  // Rows' floors move up on a schedule shared by the workgroup's waves (they
+  // meet at a barrier every tile, so a refresh in one wave would stall the
+  // others; refreshing together overlaps them): first once k keys have been
+  // seen, then each time the keys seen grow by a factor 1 + 2^-kFloorGrowShift.
+  // After step i, the keys counted for a row are its visible keys among the
+  // first min(i, n_wg - 1) + 1 tiles.
+  int next_refresh = k;
+  auto refresh_floor = [&](int i) {
+    const int seen = ((i < n_wg ? i : n_wg - 1) + 1) * 32;
+    if (seen < next_refresh) return;  // uniform over the workgroup
+    next_refresh = seen + max(seen >> kFloorGrowShift, 128);
+    const int v = qpos0 + tg + 1;
+    const Cross cr = pair_cross(&phist[wave][0][0], (uint32_t)k, g < nt ? (uint32_t)min(seen, min(L, v)) : 0u);
+    floor_bin = cr.ok && cr.found ? cr.bin : 0u;
   };
 
   // Software pipeline over the workgroup's tiles (step i computes tile i):
@@ -347,14 +441,32 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
       compute(kbuf[st & 1], skr[st], it, i < n_wg);
       skr[st] = load_scale(clamp_tile(i + kPfRegs));
     }
+    // Once per unrolled iteration, so that its four steps stay one block of
+    // straight-line code for the scheduler.
+    refresh_floor(base + kPfRegs - 1);
   }
+  // Each row's list length (lane 0 of its half).
+  if (col == 0 && g < nt) ccnt[tg] = g ? nc1 : nc0;
   __syncthreads();
-  for (int tk = 0; tk < nt; ++tk) {
-    const int t = t_base + tk;
-    const int vis = qpos0 + t + 1;
-    if (vis > k) wave_find_bin(phist[wave][tk], (uint32_t)k, (uint32_t)(vis < L ? vis : L), thr + (int64_t)t * 4);
+  {
+    // Each row's threshold bin (rows with more than k visible keys), or the
+    // overflow mark.
+    const int vis = qpos0 + tg + 1;
+    const uint32_t n = (uint32_t)(vis < L ? vis : L);
+    const Cross cr = pair_cross(&phist[wave][0][0], (uint32_t)k, g < nt ? n : 0u);
+    if (col == 0 && g < nt && vis > k) {
+      uint32_t* t = thr + (int64_t)tg * 4;
+      if (cr.ok && cr.found) {
+        t[0] = cr.bin;
+        t[1] = cr.above;
+        t[2] = cr.eq;
+        t[3] = 1u;
+      } else {
+        t[3] = 0u;
+      }
+    }
   }
-  if (fill_masked) {
+  if (DENSE && fill_masked) {
     for (int tk = 0; tk < nt; ++tk) {
       const int t = t_base + tk;
       for (int s = n_wg * 32 + lane; s < L; s += 64) scores[(int64_t)t * L + s] = -INFINITY;
@@ -374,16 +486,24 @@ hipError_t launch_prefill_linear(const uint8_t* q, const float* w, int32_t T, in
 hipError_t launch_prefill_score(const uint8_t* q, const float* q_scale, const float* w,
                                 const uint8_t* uq, const float* usc, const uint8_t* kc,
                                 const float* k_scale, int32_t T, int32_t L, int32_t qpos0, int32_t H,
-                                int32_t k, bool fill_masked, float* scores, const SelWs& sel,
+                                int32_t k, float* scores, const SelWs& sel, uint2* clist, uint32_t* ccnt,
                                 hipStream_t stream) {
   if (T <= 0 || L <= 0) return hipSuccess;
   dim3 grid((unsigned)((T + kPfTokPerBlock - 1) / kPfTokPerBlock));
-  const int fill = fill_masked ? 1 : 0;
-  if (k_scale)
-    return launch_kernel(prefill_score_kernel<true>, grid, dim3(64 * kPfWaves), 0, stream, q, q_scale, w, uq, usc,
-                         kc, k_scale, T, L, qpos0, H, k, fill, scores, sel.thr);
-  return launch_kernel(prefill_score_kernel<false>, grid, dim3(64 * kPfWaves), 0, stream, q, q_scale, w, uq, usc,
-                       kc, k_scale, T, L, qpos0, H, k, fill, scores, sel.thr);
+  const int fill = scores ? 1 : 0;
+  const dim3 block(64 * kPfWaves);
+  if (k_scale) {
+    if (scores)
+      return launch_kernel(prefill_score_kernel<true, true>, grid, block, 0, stream, q, q_scale, w, uq, usc, kc,
+                           k_scale, T, L, qpos0, H, k, fill, scores, sel.thr, clist, ccnt);
+    return launch_kernel(prefill_score_kernel<true, false>, grid, block, 0, stream, q, q_scale, w, uq, usc, kc,
+                         k_scale, T, L, qpos0, H, k, fill, scores, sel.thr, clist, ccnt);
+  }
+  if (scores)
+    return launch_kernel(prefill_score_kernel<false, true>, grid, block, 0, stream, q, q_scale, w, uq, usc, kc,
+                         k_scale, T, L, qpos0, H, k, fill, scores, sel.thr, clist, ccnt);
+  return launch_kernel(prefill_score_kernel<false, false>, grid, block, 0, stream, q, q_scale, w, uq, usc, kc,
+                       k_scale, T, L, qpos0, H, k, fill, scores, sel.thr, clist, ccnt);
 }
 
 }  // namespace li

@@ -497,6 +497,118 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkRows a, SelWs
                            1, kk, hist, wsum, shb);
 }
 
+// Causal rows given as candidate lists (the prefill scan's output): row r's
+// visible positions are 0 .. min(L, qpos0 + r) and its list, list + r * L,
+// holds lcnt[r] (key, position) pairs in position order: every visible key
+// at or above a floor that never exceeds the row's final threshold bin, so
+// the list contains the row's top-k and, for every bin at or above b*, all
+// of that bin's keys.  b* comes from the scan (thr) or, when the scan's
+// 16-bit histogram overflowed, from a histogram of the list.  One workgroup
+// per row; dynamic LDS holds `cap` candidate pairs.
+__global__ __launch_bounds__(kRowThreads) void topk_list_kernel(TopkRows a, SelWs ws, const uint2* list_base,
+                                                                const uint32_t* lcnt, int cap) {
+  extern __shared__ uint2 cand[];
+  __shared__ uint32_t hist[kSelBins];
+  constexpr int kRounds = 16;  // collection rounds per chunk
+  constexpr int kW = kRowThreads / 64;
+  __shared__ uint32_t rcnt[kRounds * kW];
+  __shared__ uint32_t wsum[kW];
+  __shared__ uint32_t shb[4];
+  const int tid = threadIdx.x;
+  const int r = blockIdx.x;
+  Row row;
+  row.p = nullptr;
+  row.map = nullptr;
+  row.out = a.out + (int64_t)r * a.k;
+  const int64_t vis0 = (int64_t)a.qpos0 + r + 1;
+  row.n = vis0 < a.n ? vis0 : a.n;
+  const int64_t n = row.n;
+  const int k = a.k;
+  if (n <= k) {
+    keep_all<kRowThreads>(row, n, k);
+    return;
+  }
+  const int64_t kk = k;
+  const uint2* list = list_base + (int64_t)r * a.row_stride;
+  const int64_t nl = lcnt[r];
+  auto lkey = [&](int64_t i) { return list[i].x; };
+  auto lpos = [&](int64_t i) { return (int64_t)list[i].y; };
+
+  uint32_t bstar, above, eq;
+  if (ws.thr[(int64_t)r * 4 + 3] == 0u) {
+    for (int i = tid; i < kSelBins; i += kRowThreads) hist[i] = 0;
+    __syncthreads();
+    for (int64_t i = tid; i < nl; i += kRowThreads) atomicAdd(&hist[list[i].x >> kSelShift], 1u);
+    __syncthreads();
+    constexpr int PER = kSelBins / kRowThreads;
+    uint32_t h[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) h[i] = hist[kSelBins - 1 - (tid * PER + i)];
+    find_digit<kRowThreads, PER>(h, kSelBins - 1, (uint32_t)kk, wsum, shb);
+    bstar = shb[0];
+    above = shb[1];
+    eq = shb[2];
+  } else {
+    const uint32_t* t = ws.thr + (int64_t)r * 4;
+    bstar = t[0];
+    above = t[1];
+    eq = t[2];
+  }
+  const int64_t nc = (int64_t)above + eq;
+  if (nc > cap || above >= (uint32_t)kk) {
+    select_keys<kRowThreads>(row, lkey, lpos, nl, 0u, 0u, (uint32_t)kk, 0, kk, hist, wsum, shb);
+    return;
+  }
+  // Ordered collection of the list entries whose level-0 bin is >= b*, as in
+  // topk_row_kernel: chunks of kRounds * kRowThreads entries, a ballot per
+  // round and one scan over the (round, wave) counts.
+  const int lane = tid & 63, wave = tid >> 6;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint32_t run = 0;
+  uint2 e[kRounds], ne[kRounds];
+  auto load_chunk = [&](uint2 (&dst)[kRounds], int64_t base) {
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      const int64_t i = base + (int64_t)j * kRowThreads + tid;
+      dst[j] = list[i < nl ? i : nl - 1];  // clamped, branch-free (nl >= k >= 1 here)
+    }
+  };
+  load_chunk(ne, 0);
+#pragma unroll 1
+  for (int64_t base = 0; base < nl; base += (int64_t)kRounds * kRowThreads) {
+    uint64_t ball[kRounds];
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) e[j] = ne[j];
+    load_chunk(ne, base + (int64_t)kRounds * kRowThreads);
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      const int64_t i = base + (int64_t)j * kRowThreads + tid;
+      ball[j] = __ballot(i < nl && (e[j].x >> kSelShift) >= bstar);
+      if (lane == 0) rcnt[j * kW + wave] = (uint32_t)__popcll(ball[j]);
+    }
+    __syncthreads();
+    uint32_t total;
+    const uint32_t cv = tid < kRounds * kW ? rcnt[tid] : 0u;
+    const uint32_t ex = block_excl_scan<kRowThreads>(cv, wsum, total);
+    if (tid < kRounds * kW) rcnt[tid] = ex;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      if ((ball[j] >> lane) & 1ull) {
+        const uint32_t pos = run + rcnt[j * kW + wave] + (uint32_t)__popcll(ball[j] & below);
+        if (pos < (uint32_t)cap) cand[pos] = e[j];
+      }
+    }
+    run += total;
+    __syncthreads();  // rcnt is reused
+  }
+  __syncthreads();
+  auto ckey = [&](int64_t i) { return cand[i].x; };
+  auto cpos = [&](int64_t i) { return (int64_t)cand[i].y; };
+  select_keys<kRowThreads>(row, ckey, cpos, nc, bstar << kSelShift, 0xFFE00000u, (uint32_t)kk - above, 1, kk, hist,
+                           wsum, shb);
+}
+
 // One workgroup per (segment, row); see the file comment.  Dynamic LDS holds
 // the last workgroup's candidates (ws.cap pairs).
 // SEGPER: positions per thread in a segment (segment = SEGPER * kSegThreads).
@@ -843,6 +955,16 @@ static hipError_t launch_row(const TopkRows& a, const SelWs& ws, int how, hipStr
 
 hipError_t launch_topk_self(const TopkRows& a, const SelWs& ws, hipStream_t stream) {
   return launch_row(a, ws, kSelSelf, stream);
+}
+
+hipError_t launch_topk_list(const TopkRows& a, const SelWs& ws, const uint2* list, const uint32_t* lcnt,
+                            hipStream_t stream) {
+  if (a.rows <= 0) return hipSuccess;
+  static bool lds_set = false;
+  if (hipError_t e = allow_lds(topk_list_kernel, lds_set)) return e;
+  const int cap = seg_cap_for(a.k);
+  return launch_kernel(topk_list_kernel, dim3((unsigned)a.rows), dim3(kRowThreads), (uint32_t)(cap * sizeof(uint2)),
+                       stream, a, ws, list, lcnt, cap);
 }
 
 hipError_t launch_topk(const TopkRows& a, hipStream_t stream) {

@@ -64,7 +64,8 @@ def test_workspace_queries():
     with_s = L.li_index_decode_ws(32, n, 32768, 2048, 1)
     without = L.li_index_decode_ws(32, n, 32768, 2048, 0)
     assert without - with_s >= n * 4 and with_s >= 32 * 2048 * 4
-    assert L.li_index_prefill_ws(4096, 65536, 2048, 0) >= 4096 * 65536 * 4
+    # per-row candidate lists at their worst case: a (key, position) pair per visible key
+    assert L.li_index_prefill_ws(4096, 65536, 2048, 0) >= 4096 * 65536 * 8
     # absorbed fp16 queries + scaled weights + scores
     assert L.li_latent_score_group_ws(16, 1 << 21, 131072, 4, 64, 256, 2048, 0) >= 16 * 4 * 64 * 256 * 2 + 4 * (1 << 21) * 4
     assert L.li_hs_refine_ws(16, 8192, 3, 64, 256, 2048, 0) >= 16 * 3 * 8192 * 4
@@ -148,6 +149,10 @@ def test_prefill_validation():
         assert call(H=h) == li.LI_E_UNSUPPORTED
     assert b"H >= 8" in L.li_last_error()
     assert call(H=8, wsb=100) == li.LI_E_WORKSPACE
+    # the cache length is bounded (a wave's candidate rows fit one buffer resource)
+    assert call(T=0, Lc=(1 << 26) + 1, qpos0=0) == li.LI_E_SHAPE
+    assert b"L <= 67108864" in L.li_last_error()
+    assert call(T=0, Lc=1 << 26, qpos0=0) == li.LI_OK
 
 
 def test_latent_and_hs_validation():

@@ -129,3 +129,36 @@ def test_prefill_all_equal_scores_overflow_a_histogram_bin():
         ri, _, _ = oracle.index_prefill(x.q[t:t + 1], x.q_dt, x.q_scale[t:t + 1], x.w[t:t + 1], x.kc, x.k_dt,
                                         x.k_scale, 1, x.L, x.qpos0 + t, x.H, x.D, x.k, want_scores=False)
         assert np.array_equal(gi[t], ri[0]) and np.array_equal(ri[0], np.arange(x.k, dtype=np.int32))
+    # the same rows without a score output (the selection reads only the lists)
+    gi2, _ = run_gpu(x, with_scores=False)
+    assert np.array_equal(gi2.cpu().numpy(), gi)
+
+
+def test_cfg3_every_row_selects_the_top_k_of_its_own_scores():
+    """All 4096 rows of the T = 4096, L = 65536 chunk: the selection (read from
+    the scan's candidate lists, whose floors rise several times per row) is
+    exactly the top k of the scores the scan wrote, with ties going to the
+    lowest positions; without a score output the indices are the same."""
+    x = inputs.cfg3()
+    print(f"[prefill parity] cfg3 every row T={x.T} L={x.L}", flush=True)
+    gi, gs = run_gpu(x)
+    assert x.qpos0 + 1 > x.k  # every row has more than k visible keys
+    gil = gi.long()
+    assert bool((gi >= 0).all()) and bool((gil.diff(dim=1) > 0).all())
+    kth = gs.gather(1, gil).min(dim=1).values
+    rest = gs.clone()
+    rest.scatter_(1, gil, float("-inf"))
+    top_rest = rest.max(dim=1).values
+    assert bool((kth >= top_rest).all()), "a key above a selected one was left out"
+    tied = torch.nonzero(kth == top_rest).flatten().tolist()
+    for t in tied:
+        g = gs[t].cpu().numpy()
+        sel = gi[t].cpu().numpy()
+        v = kth[t].item()
+        in_sel = sel[g[sel] == v]
+        out = np.setdiff1d(np.nonzero(g == v)[0], sel)
+        assert out.min() > in_sel.max(), f"row {t}: a tie went to a higher position"
+    print(f"[prefill parity] cfg3 every row: {len(tied)} rows with ties at the threshold", flush=True)
+    del rest, gs
+    gi2, _ = run_gpu(x, with_scores=False)
+    assert torch.equal(gi, gi2)
