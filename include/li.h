@@ -103,6 +103,17 @@ typedef int32_t li_dtype;
  *   H        1..64 heads; D must be 128; 1 <= k <= LI_MAX_K
  *   out_idx  [B][k]      int32 positions in [0, L_b), ascending, -1 padded
  *   out_scores [n_tok]   fp32 score of every cache row, or NULL
+ *
+ * Selection (both ways give the same indices): when max_len <= 2^17 and a
+ * request spans at most 32 scan workgroups of at least 2k positions each (a
+ * workgroup covers 512 .. 8192 positions, more as n_tok grows: k = 2048 takes
+ * this way from about 2M cached tokens on), every scan workgroup leaves its keys at or
+ * above its own k-th largest level-0 bin as (key, position) lists ordered by
+ * bin, and one workgroup per request reads only the part at or above the
+ * request's threshold bin; the workspace then holds those lists (8 bytes per
+ * key) and no score buffer.  Otherwise many workgroups per request collect
+ * candidates from a score buffer in the workspace (4 bytes per key, unless
+ * out_scores is given) and the last one to finish selects.
  * ------------------------------------------------------------------------- */
 li_status li_index_decode(const void* q, li_dtype q_dt, const float* w, const void* k_cache,
                           li_dtype k_dt, const float* k_scale, const int64_t* kv_off, int32_t B,
@@ -123,8 +134,7 @@ size_t li_index_decode_ws(int32_t B, int64_t n_tok, int32_t max_len, int32_t k,
  *
  *   A call whose li_index_decode_ws(B, n_tok, max_len, k, out_scores != NULL)
  *   exceeds LI_NOALLOC_SCRATCH_BYTES returns LI_E_UNSUPPORTED before any
- *   device work (the B = 32, 131072-token decode without out_scores needs
- *   about 50 MiB).
+ *   device work (the B = 32, 131072-token decode needs about 34 MiB).
  *   Every call on one GPU shares that GPU's array: calls that can overlap on
  *   one GPU (different streams, or concurrent host threads) race and must be
  *   serialised by the caller.  Nothing in the array needs to start at zero:

@@ -55,11 +55,13 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
   constexpr int NV = FP8 ? 4 : 8;             // 16-byte vectors per lane per tile
   constexpr int kRowBytes = FP8 ? 128 : 256;  // one key row
   constexpr int kStages = FP8 ? kStagesFp8 : kStagesBf16;
-  __shared__ uint32_t lhist[kSelBins];
+  __shared__ uint32_t lhist[kSelBins + 64];  // + spare words for the bucket epilogue
   // The workgroup's scores, written to HBM in one burst at the end: small
   // writes interleaved with the key stream cost far more read bandwidth than
   // their own size.
   __shared__ __attribute__((aligned(16))) float ssc[kDecMaxChunk];
+  __shared__ uint32_t wsum[kDecWaves];
+  __shared__ uint32_t sh_floor[2];
 
   const int b = blockIdx.y;
   const int64_t off = kv_off[b];
@@ -72,8 +74,8 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
   if (wg0 >= L) return;  // whole workgroup: no key of this request here
   const bool select = L > k;
   for (int i = tid; i < kSelBins; i += 256) lhist[i] = 0;
-  // The top-k kernel that follows counts finished segments per request.
-  if (select && blockIdx.x == 0 && tid == 0) sel.done[b] = 0u;
+  // The segmented top-k kernel that follows counts finished segments per request.
+  if (select && !sel.bucket && blockIdx.x == 0 && tid == 0) sel.done[b] = 0u;
 
   // Query heads as MFMA A operand: row = head (hb*32 + col), dims 64g + 8j .. +7.
   bf16x8 qa[2][8];
@@ -169,23 +171,31 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
   }
   __syncthreads();
   // Scores of positions wg0 .. min(wg0 + chunk, L) - 1, 16 bytes per store
-  // where the request's offset keeps them aligned.
+  // where the request's offset keeps them aligned (bucket mode: only when the
+  // caller asked for them).
   const int64_t n = (L - wg0) < chunk ? (L - wg0) : chunk;
-  float* dst = scores + off + wg0;
-  if (((off + wg0) & 3) == 0) {
-    const int64_t n4 = n >> 2;
-    for (int64_t i = tid; i < n4; i += 256)
-      *reinterpret_cast<f32x4*>(dst + 4 * i) = *reinterpret_cast<const f32x4*>(&ssc[4 * i]);
-    for (int64_t i = 4 * n4 + tid; i < n; i += 256) dst[i] = ssc[i];
-  } else {
-    for (int64_t i = tid; i < n; i += 256) dst[i] = ssc[i];
+  if (scores) {
+    float* dst = scores + off + wg0;
+    if (((off + wg0) & 3) == 0) {
+      const int64_t n4 = n >> 2;
+      for (int64_t i = tid; i < n4; i += 256)
+        *reinterpret_cast<f32x4*>(dst + 4 * i) = *reinterpret_cast<const f32x4*>(&ssc[4 * i]);
+      for (int64_t i = 4 * n4 + tid; i < n; i += 256) dst[i] = ssc[i];
+    } else {
+      for (int64_t i = tid; i < n; i += 256) dst[i] = ssc[i];
+    }
   }
   if (!select) return;
 
   // This workgroup's share of the request's level-0 histogram, as 16-bit
-  // partials (a workgroup covers at most 8192 positions).
+  // partials (a workgroup covers at most 8192 positions); in bucket mode as
+  // prefix counts, with its candidate list.
   const int64_t pi = (int64_t)b * sel.nwg + blockIdx.x;
-  store_partial<256>(lhist, sel.part + pi * kSelBins, sel.cpart + pi * kSelCoarse);
+  if (sel.bucket)
+    bucket_epilogue<256, kDecMaxChunk>(lhist, ssc, (int)n, k, (uint32_t)wg0, sel.part + pi * kSelBins,
+                                       sel.blist + pi * sel.chunk, wsum, sh_floor);
+  else
+    store_partial<256>(lhist, sel.part + pi * kSelBins, sel.cpart + pi * kSelCoarse);
 }
 
 }  // namespace

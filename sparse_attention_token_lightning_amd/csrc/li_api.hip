@@ -87,45 +87,63 @@ int64_t nseg_for(int64_t rows, int64_t max_len) {
 }
 
 // Selection state for `rows` rows: per-row thresholds; with `chunk` > 0 also
-// the scan workgroups' partial histograms (ceil(max_len / chunk) per row), the
-// summed histograms and the collect segments' candidates.
-size_t sel_ws(int64_t rows, int64_t max_len, int64_t chunk) {
+// the scan workgroups' partial histograms (ceil(max_len / chunk) per row) and
+// either the bucket lists (bucket mode) or the summed histograms and the
+// collect segments' candidates.
+size_t sel_ws(int64_t rows, int64_t max_len, int64_t chunk, bool bucket) {
   size_t s = align_up((size_t)rows * 16);  // thr
   if (chunk > 0) {
-    const int64_t nwg = (max_len + chunk - 1) / chunk, nseg = nseg_for(rows, max_len);
-    const int64_t seg = li::seg_len_for(rows, max_len);
-    s += align_up((size_t)rows * nwg * kHistBins * 2) + align_up((size_t)rows * nwg * li::kSelCoarse * 2) +
-         align_up((size_t)rows * 4);
-    s += align_up((size_t)rows * nseg * 4) + align_up((size_t)rows * nseg * seg * 8);
+    const int64_t nwg = (max_len + chunk - 1) / chunk;
+    s += align_up((size_t)rows * nwg * kHistBins * 2);
+    if (bucket) {
+      s += align_up((size_t)rows * nwg * chunk * 8);
+    } else {
+      const int64_t nseg = nseg_for(rows, max_len), seg = li::seg_len_for(rows, max_len);
+      s += align_up((size_t)rows * nwg * li::kSelCoarse * 2) + align_up((size_t)rows * 4);
+      s += align_up((size_t)rows * nseg * 4) + align_up((size_t)rows * nseg * seg * 8);
+    }
   }
   return s;
 }
 
-li::SelWs carve_sel(Carver& cv, int64_t rows, int64_t max_len, int64_t chunk, int32_t k) {
+li::SelWs carve_sel(Carver& cv, int64_t rows, int64_t max_len, int64_t chunk, int32_t k, bool bucket) {
   li::SelWs w = {};
   w.thr = (uint32_t*)cv.take((size_t)rows * 16);
   if (chunk > 0) {
-    const int64_t nwg = (max_len + chunk - 1) / chunk, nseg = nseg_for(rows, max_len);
-    const int64_t seg = li::seg_len_for(rows, max_len);
+    const int64_t nwg = (max_len + chunk - 1) / chunk;
     w.part = (uint16_t*)cv.take((size_t)rows * nwg * kHistBins * 2);
-    w.cpart = (uint16_t*)cv.take((size_t)rows * nwg * li::kSelCoarse * 2);
-    w.done = (uint32_t*)cv.take((size_t)rows * 4);
-    w.cnt = (uint32_t*)cv.take((size_t)rows * nseg * 4);
-    w.cand = (uint2*)cv.take((size_t)rows * nseg * seg * 8);
     w.nwg = (int32_t)nwg;
     w.chunk = (int32_t)chunk;
-    w.nseg = (int32_t)nseg;
-    w.seg = (int32_t)seg;
-    w.cap = li::seg_cap_for(k);
+    if (bucket) {
+      w.blist = (uint2*)cv.take((size_t)rows * nwg * chunk * 8);
+      w.bucket = 1;
+    } else {
+      const int64_t nseg = nseg_for(rows, max_len), seg = li::seg_len_for(rows, max_len);
+      w.cpart = (uint16_t*)cv.take((size_t)rows * nwg * li::kSelCoarse * 2);
+      w.done = (uint32_t*)cv.take((size_t)rows * 4);
+      w.cnt = (uint32_t*)cv.take((size_t)rows * nseg * 4);
+      w.cand = (uint2*)cv.take((size_t)rows * nseg * seg * 8);
+      w.nseg = (int32_t)nseg;
+      w.seg = (int32_t)seg;
+      w.cap = li::seg_cap_for(k);
+    }
   }
   return w;
 }
 
-size_t decode_ws(int32_t B, int64_t n_tok, int32_t max_len, bool scores_given) {
+// Decode selects in bucket mode when its rows fit it (see li::bucket_ok);
+// then the scan writes no dense scores unless the caller wants them.
+bool decode_bucket(int64_t n_tok, int32_t max_len, int32_t k) {
+  const int64_t chunk = li::decode_chunk(n_tok);
+  return max_len > 0 && li::bucket_ok((max_len + chunk - 1) / chunk, chunk, k, max_len);
+}
+
+size_t decode_ws(int32_t B, int64_t n_tok, int32_t max_len, int32_t k, bool scores_given) {
+  const bool bucket = decode_bucket(n_tok, max_len, k);
   size_t s = 0;
-  if (!scores_given) s += align_up((size_t)n_tok * 4);
+  if (!scores_given && !bucket) s += align_up((size_t)n_tok * 4);
   const int64_t rows = B > 0 ? B : 0;
-  s += sel_ws(rows, max_len > 0 ? max_len : 0, li::decode_chunk(n_tok));
+  s += sel_ws(rows, max_len > 0 ? max_len : 0, li::decode_chunk(n_tok), bucket);
   return s;
 }
 
@@ -137,7 +155,7 @@ size_t prefill_ws(int32_t T, int32_t L, bool scores_given) {
   const size_t rows = T > 0 ? (size_t)T : 0;
   s += align_up(rows * (size_t)(L > 0 ? L : 0) * 8) + align_up(rows * 4);
   s += align_up(rows * li::kLinRows * 128) + align_up(rows * li::kLinRows * 4);
-  s += sel_ws(T > 0 ? T : 0, 0, 0);
+  s += sel_ws(T > 0 ? T : 0, 0, 0, false);
   return s;
 }
 
@@ -147,7 +165,7 @@ size_t latent_ws(int32_t B, int64_t n_tok, int32_t max_len, int32_t G, int32_t H
   // absorbed queries: room for the two bf16 parts of LI_LATENT_SPLIT_BF16
   size_t s = align_up(rows * H * Dc * 4) + align_up(rows * H * 4);
   if (!scores_given) s += align_up((size_t)G * (size_t)n_tok * 4);
-  s += sel_ws((int64_t)rows, max_len > 0 ? max_len : 0, li::latent_chunk(n_tok));
+  s += sel_ws((int64_t)rows, max_len > 0 ? max_len : 0, li::latent_chunk(n_tok), false);
   return s;
 }
 
@@ -277,7 +295,7 @@ li_status li_read_probe(const void* p, size_t bytes, uint32_t* sink, void* strea
 size_t li_index_decode_ws(int32_t B, int64_t n_tok, int32_t max_len, int32_t k,
                           int32_t has_out_scores) {
   (void)k;
-  return decode_ws(B, n_tok, max_len, has_out_scores != 0);
+  return decode_ws(B, n_tok, max_len, k, has_out_scores != 0);
 }
 
 // Host-side argument checks of a decode call (everything but the workspace).
@@ -305,7 +323,7 @@ li_status li_index_decode(const void* q, li_dtype q_dt, const float* w, const vo
   g_err.clear();
   li_status st;
   if ((st = check_decode_args(q, q_dt, w, k_cache, k_dt, kv_off, B, n_tok, max_len, H, D, k, out_idx))) return st;
-  if ((st = check_ws(ws, ws_bytes, decode_ws(B, n_tok, max_len, out_scores != nullptr)))) return st;
+  if ((st = check_ws(ws, ws_bytes, decode_ws(B, n_tok, max_len, k, out_scores != nullptr)))) return st;
   if (B == 0) return LI_OK;
   hipStream_t s = (hipStream_t)stream;
   if (validate_on() && (st = run_validation(s, [&] {
@@ -319,8 +337,9 @@ li_status li_index_decode(const void* q, li_dtype q_dt, const float* w, const vo
     return st;
   trace_begin();
   Carver cv(ws);
-  float* scores = out_scores ? out_scores : (float*)cv.take((size_t)n_tok * 4);
-  const li::SelWs sel = carve_sel(cv, B, max_len, li::decode_chunk(n_tok), k);
+  const bool bucket = decode_bucket(n_tok, max_len, k);
+  float* scores = out_scores ? out_scores : (bucket ? nullptr : (float*)cv.take((size_t)n_tok * 4));
+  const li::SelWs sel = carve_sel(cv, B, max_len, li::decode_chunk(n_tok), k, bucket);
   if ((st = hip_check(li::launch_decode_score((const uint16_t*)q, w, k_cache, k_dt == LI_FP8_E4M3,
                                               k_scale, kv_off, B, n_tok, max_len, H, k, scores, sel,
                                               s),
@@ -335,6 +354,7 @@ li_status li_index_decode(const void* q, li_dtype q_dt, const float* w, const vo
   tr.G = 1;
   tr.k = k;
   tr.out = out_idx;
+  if (bucket) return hip_check(li::launch_topk_bucket(tr, sel, max_len, s), "topk launch", s);
   return hip_check(li::launch_topk_segmented(tr, sel, s), "topk launch", s);
 }
 
@@ -345,7 +365,7 @@ li_status li_index_decode_noalloc(const void* q, li_dtype q_dt, const float* w, 
   g_err.clear();
   li_status st;
   if ((st = check_decode_args(q, q_dt, w, k_cache, k_dt, kv_off, B, n_tok, max_len, H, D, k, out_idx))) return st;
-  const size_t need = decode_ws(B, n_tok, max_len, out_scores != nullptr);
+  const size_t need = decode_ws(B, n_tok, max_len, k, out_scores != nullptr);
   if (need > kScratchBytes)
     return fail(LI_E_UNSUPPORTED,
                 "li_index_decode_noalloc: this call needs %zu bytes of scratch; the library's static scratch "
@@ -399,7 +419,7 @@ li_status li_index_prefill(const void* q, li_dtype q_dt, const float* q_scale, c
   uint32_t* ccnt = (uint32_t*)cv.take((size_t)T * 4);
   uint8_t* uq = (uint8_t*)cv.take((size_t)T * li::kLinRows * 128);
   float* usc = (float*)cv.take((size_t)T * li::kLinRows * 4);
-  const li::SelWs sel = carve_sel(cv, T, 0, 0, k);
+  const li::SelWs sel = carve_sel(cv, T, 0, 0, k, false);
   if ((st = hip_check(li::launch_prefill_linear((const uint8_t*)q, w, T, H, uq, usc, s),
                       "prefill_linear launch", s)))
     return st;
@@ -485,7 +505,7 @@ li_status li_latent_score_group(const void* q, li_dtype q_dt, const float* w, co
   const bool split = latent_split(flags, c_dt, H);
   float* wsc = (float*)cv.take((size_t)B * G * H * 4);
   float* scores = out_scores ? out_scores : (float*)cv.take((size_t)G * (size_t)n_tok * 4);
-  const li::SelWs sel = carve_sel(cv, (int64_t)B * G, max_len, li::latent_chunk(n_tok), k);
+  const li::SelWs sel = carve_sel(cv, (int64_t)B * G, max_len, li::latent_chunk(n_tok), k, false);
   if ((st = hip_check(li::launch_latent_absorb((const uint16_t*)q, w, (const uint16_t*)w_dec, B, G,
                                                H, Dh, Dc, split, qt16, wsc, s),
                       "latent_absorb launch", s)))

@@ -61,6 +61,17 @@ int32_t seg_cap_for(int32_t k);
 // Scores per collect segment of the segmented top-k for `rows` rows of up to
 // max_len scores (larger segments when the grid would not fit the GPU at once).
 int64_t seg_len_for(int64_t rows, int64_t max_len);
+// Bucket mode (SelWs::bucket, decode): one workgroup per row reads the scan's
+// prefix partials and bin-ordered candidate lists.  Used when a row spans at
+// most kBucketMaxNwg scan workgroups of at least 2k positions, max_len <=
+// kBucketMaxLen (the LDS position bitmaps) and the LDS candidate capacity
+// left is useful.
+constexpr int kBucketMaxNwg = 32;
+constexpr int64_t kBucketMaxLen = 1 << 17;  // also keeps the packed word prefixes exact
+constexpr int64_t kBucketLds = 147456;  // dynamic LDS of the bucket top-k kernel
+int32_t bucket_cap_for(int32_t k, int64_t max_len);
+bool bucket_ok(int64_t nwg, int64_t chunk, int32_t k, int64_t max_len);
+hipError_t launch_topk_bucket(const TopkRows& a, const SelWs& ws, int64_t max_len, hipStream_t stream);
 // Top-k from scan-built thresholds, one workgroup per row collecting its own candidates.
 hipError_t launch_topk_self(const TopkRows& a, const SelWs& ws, hipStream_t stream);
 // Top-k of causal rows (a.n = L, a.qpos0, a.row_stride = L) given as the

@@ -27,6 +27,12 @@ struct SelWs {
   int32_t seg;      // scores per collect segment (kSeg or 2 * kSeg)
   uint32_t* done;   // [rows] finished-segment counters (zeroed by the scan kernel)
   int32_t cap;      // LDS candidates of the final selection in the segmented top-k
+  // Bucket mode (bucket = 1): part holds each scan workgroup's descending
+  // prefix counts (part[b] = its keys in bins >= b) and blist [rows][nwg][chunk]
+  // its keys at or above its own k-th largest bin as (key, position) pairs in
+  // descending bin order, so the keys in bins >= b are the first part[b].
+  uint2* blist;
+  int32_t bucket;
 };
 
 // Writes a workgroup's LDS histogram (one 32-bit counter per bin, counts <
@@ -78,6 +84,104 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
   __syncthreads();
   total = tot;
   return before + inc - v;
+}
+
+// Buffer resource word 3 for gfx9 parts (32-bit data format, raw addressing)
+// and an offset past the end of any resource: a buffer store there is dropped
+// by the range check, so a masked store needs no branch.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr uint32_t kBufferDrop = 0x80000000u;
+
+// End of a scan workgroup in bucket mode.  lhist holds the level-0 counts of
+// the workgroup's n scores (ssc[0 .. n-1], positions pos0 + i) followed by 64
+// spare words; NT threads, PER = 8 bins each.  Stores the descending prefix
+// counts to pdst (16-bit: n <= CH <= 65535), then writes every key whose bin
+// is at or above the bin of the workgroup's own min(k, n)-th largest key to
+// ldst, bin by bin from the top (a key of a lower bin cannot be among the
+// row's k largest: the k-th largest of a part of the row is at most the k-th
+// largest of the row).  The order inside a bin is that of the LDS cursor
+// atomics; the selection does not depend on it.  lhist and ssc are
+// overwritten (cursors; the list is staged over the scores when it fits);
+// sh holds two words of scratch.
+template <int NT, int CH>
+__device__ __forceinline__ void bucket_epilogue(uint32_t* lhist, float* ssc, int n, int k, uint32_t pos0,
+                                                uint16_t* pdst, uint2* ldst, uint32_t* wsum, uint32_t* sh) {
+  constexpr int PER = kSelBins / NT;
+  static_assert(PER == 8 && CH % NT == 0 && CH < 65536, "eight bins (one 16-byte partial store) per thread");
+  const int t = threadIdx.x;
+  uint32_t h[PER];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    h[i] = lhist[kSelBins - 1 - (t * PER + i)];
+    sum += h[i];
+  }
+  uint32_t total;
+  uint32_t run = block_excl_scan<NT>(sum, wsum, total);  // keys in the bins above this thread's
+  const uint32_t kk = (uint32_t)(k < n ? k : n);
+  uint32_t pv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int bin = kSelBins - 1 - (t * PER + i);
+    const uint32_t above = run;
+    run += h[i];
+    pv[i] = run;
+    lhist[bin] = above;  // first slot of the bin's keys
+    if (above < kk && run >= kk) {
+      sh[0] = (uint32_t)bin;  // the floor bin
+      sh[1] = run;            // keys written
+    }
+  }
+  // bins 2040 - 8t .. 2047 - 8t in ascending order
+  const i32x4 pk = {(int)(pv[7] | (pv[6] << 16)), (int)(pv[5] | (pv[4] << 16)), (int)(pv[3] | (pv[2] << 16)),
+                    (int)(pv[1] | (pv[0] << 16))};
+  *reinterpret_cast<i32x4*>(pdst + (kSelBins - PER) - PER * t) = pk;
+  __syncthreads();
+  const uint32_t f = sh[0], nkeep = sh[1];
+  constexpr int R = CH / NT;
+  uint32_t key[R], slot[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int i = t + NT * j;
+    key[j] = score_key(ssc[i < n ? i : n - 1]);
+  }
+  // Branch-free: a lane with nothing to write adds 0 to its own spare word.
+  const int lane = t & 63;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const uint32_t b = key[j] >> kSelShift;
+    const bool keep = t + NT * j < n && b >= f;
+    const uint32_t s = atomicAdd(&lhist[keep ? (int)b : kSelBins + lane], keep ? 1u : 0u);
+    slot[j] = keep ? s : 0xFFFFFFFFu;
+  }
+  typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+  constexpr int kStage = CH / 2;  // pairs that fit where the scores were
+  if (nkeep <= (uint32_t)kStage) {
+    // Staged in LDS over the scores (all read above), then written out with
+    // 16-byte stores.
+    __syncthreads();
+    u32x2* stage = reinterpret_cast<u32x2*>(ssc);
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      if (slot[j] != 0xFFFFFFFFu) stage[slot[j]] = u32x2{key[j], pos0 + (uint32_t)(t + NT * j)};
+    __syncthreads();
+    const i32x4* src = reinterpret_cast<const i32x4*>(ssc);
+    i32x4* dst = reinterpret_cast<i32x4*>(ldst);
+    for (uint32_t i = (uint32_t)t; 2 * i < nkeep; i += NT) {
+      if (2 * i + 1 < nkeep) {
+        dst[i] = src[i];
+      } else {
+        const i32x4 v = src[i];
+        ldst[2 * i] = make_uint2((uint32_t)v.x, (uint32_t)v.y);
+      }
+    }
+  } else {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(ldst, (short)0, 8 * n, kBufferWord3);
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{key[j], pos0 + (uint32_t)(t + NT * j)}, rs,
+                                            slot[j] != 0xFFFFFFFFu ? 8u * slot[j] : kBufferDrop, 0, 0);
+  }
 }
 
 // Given a level-0 histogram (read through `get(bin)`), find the bin that

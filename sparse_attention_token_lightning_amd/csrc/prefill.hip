@@ -52,11 +52,6 @@ namespace {
 constexpr int kPfWaves = 4;
 constexpr int kPfTokPerWave = 2;
 constexpr int kPfTokPerBlock = kPfWaves * kPfTokPerWave;
-// Buffer resource word 3 for gfx9 parts (32-bit data format, raw
-// addressing), and an offset past the end of any resource: a store there is
-// dropped by the range check.
-constexpr int kBufferWord3 = 0x00020000;
-constexpr uint32_t kBufferDrop = 0x80000000u;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 __device__ __forceinline__ i32x8 ld32(const uint8_t* p) {

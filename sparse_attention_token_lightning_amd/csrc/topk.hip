@@ -893,6 +893,216 @@ __global__ __launch_bounds__(kSegThreads) void topk_segmented_kernel(TopkRows a,
   }
 }
 
+// Bucket mode (decode): one workgroup per row, reading what the scan left
+// (SelWs::bucket).  Summing the scan workgroups' descending prefix counts
+// gives Q[b], the row's keys in bins >= b, so the threshold bin b* (Q[b*] >= k
+// > Q[b*+1]) needs no scan, and the first part_w[b*] entries of every list are
+// exactly the row's keys in bins >= b*.  Those lists' first entries are
+// loaded together with the partials (one round trip; the rest, if a list
+// holds more, afterwards), two more radix levels inside b* give the k-th key
+// T and the number m of keys equal to T that fit, and the kept positions are
+// marked in two LDS bitmaps (> T, == T); with per-word prefix counts of
+// those, every kept candidate finds its place in position order,
+//   slot = #greater-before + min(#equal-before, m),
+// in an LDS copy of the output row, written out with coalesced stores.
+// Dynamic LDS: `cap` candidate pairs (reused for the output row), then the
+// two bitmaps and the word prefixes (nwords each).  Candidate sets beyond cap
+// are read from global memory instead.
+constexpr int kBucketThreads = 512;
+
+template <int NT, typename KeyAt, typename PosAt>
+__device__ void bucket_finish(const Row& row, KeyAt key_at, PosAt pos_at, int64_t N, uint32_t bstar, uint32_t above,
+                              uint32_t eq, int64_t kk, int64_t n, uint32_t* gbits, uint32_t* ebits, uint32_t* wpre,
+                              uint32_t* stage, uint32_t* hist, uint32_t* wsum, uint32_t* shb) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = bstar << kSelShift, pmask = 0xFFE00000u, rem = (uint32_t)kk - above, cnt = eq;
+#pragma unroll 1
+  for (int level = 1; level < 3 && cnt != rem; ++level) {
+    const int shift = level == 1 ? 10 : 0;
+    const int nb = level == 1 ? kSelBins : kSelBins / 2;
+    radix_level<NT>(key_at, N, prefix, pmask, shift, nb, rem, hist, wsum, shb);
+    prefix |= shb[0] << shift;
+    pmask |= (uint32_t)(nb - 1) << shift;
+    rem -= shb[1];
+    cnt = shb[2];
+    __syncthreads();
+  }
+  // Keys above the resolved prefix are kept; of those equal to it, the first
+  // rem by position.
+#pragma unroll 1
+  for (int64_t e = tid; e < N; e += NT) {
+    const uint32_t key = key_at(e) & pmask;
+    const uint32_t p = (uint32_t)pos_at(e);
+    if (key > prefix) atomicOr(&gbits[p >> 5], 1u << (p & 31));
+    else if (key == prefix) atomicOr(&ebits[p >> 5], 1u << (p & 31));
+  }
+  __syncthreads();
+  // Per bitmap word, the marked positions before it: #greater << 18 | #equal
+  // (#greater < k <= 2^14, #equal <= n <= 2^17), one block scan over each
+  // thread's W consecutive words.
+  const int nwr = (int)((n + 31) / 32);
+  const int W = (nwr + NT - 1) / NT;
+  const int w0 = tid * W;
+  uint32_t c = 0;
+  for (int i = 0; i < W; ++i) {
+    if (w0 + i < nwr)
+      c += ((uint32_t)__builtin_popcount(gbits[w0 + i]) << 18) + (uint32_t)__builtin_popcount(ebits[w0 + i]);
+  }
+  uint32_t total;
+  uint32_t run = block_excl_scan<NT>(c, wsum, total);
+  for (int i = 0; i < W; ++i) {
+    if (w0 + i < nwr) {
+      wpre[w0 + i] = run;
+      run += ((uint32_t)__builtin_popcount(gbits[w0 + i]) << 18) + (uint32_t)__builtin_popcount(ebits[w0 + i]);
+    }
+  }
+  __syncthreads();
+  // Each kept candidate's slot: #greater-before + min(#equal-before, m), or
+  // for an equal key #greater-before + #equal-before when that is below m.
+  const uint32_t m = rem;
+#pragma unroll 1
+  for (int64_t e = tid; e < N; e += NT) {
+    const uint32_t key = key_at(e) & pmask;
+    const uint32_t p = (uint32_t)pos_at(e);
+    const uint32_t w = p >> 5, below = (1u << (p & 31)) - 1u;
+    const uint32_t pre = wpre[w];
+    const uint32_t gb = (pre >> 18) + (uint32_t)__builtin_popcount(gbits[w] & below);
+    const uint32_t eb = (pre & 0x3FFFFu) + (uint32_t)__builtin_popcount(ebits[w] & below);
+    uint32_t slot = 0xFFFFFFFFu;
+    if (key > prefix) slot = gb + (eb < m ? eb : m);
+    else if (key == prefix && eb < m) slot = gb + eb;
+    if (slot < (uint32_t)kk) stage[slot] = p;
+  }
+  __syncthreads();
+  for (int i = tid; i < kk; i += NT) row.out[i] = (int32_t)stage[i];
+}
+
+template <int NWMAX>
+__global__ __launch_bounds__(kBucketThreads) void topk_bucket_kernel(TopkRows a, SelWs ws, int cap, int nwords) {
+  constexpr int NT = kBucketThreads;
+  static_assert(4 * NT == kSelBins, "four level-0 bins per thread");
+  constexpr int TPC = NT / NWMAX;  // threads per list in the up-front loads
+  constexpr int RS = 8;            // up-front entries per thread
+  constexpr int SPW = TPC * RS;    // entries per list loaded up front (<= 512 <= any chunk)
+  extern __shared__ uint2 bdyn[];
+  uint2* cand = bdyn;
+  uint32_t* gbits = reinterpret_cast<uint32_t*>(bdyn + cap);
+  uint32_t* ebits = gbits + nwords;
+  uint32_t* wpre = ebits + nwords;
+  __shared__ uint32_t hist[kSelBins];
+  __shared__ uint32_t qfirst[NT];
+  __shared__ uint32_t ccnt[NWMAX];
+  __shared__ uint32_t cstart[NWMAX + 1];
+  __shared__ uint32_t wsum[NT / 64];
+  __shared__ uint32_t shb[4];
+  __shared__ int32_t sh[4];
+  const int tid = threadIdx.x;
+  const int r = blockIdx.x;
+  const Row row = get_row(a, r, sh);
+  const int64_t n = row.n;
+  const int k = a.k;
+  if (n <= k) {
+    keep_all<NT>(row, n, k);
+    return;
+  }
+  const int nw = (int)((n + ws.chunk - 1) / ws.chunk);  // <= ws.nwg <= NWMAX (host-checked)
+  const int64_t prow = (int64_t)r * ws.nwg;
+  // 1. One round of loads: the 8 bytes of bins 4t .. 4t+3 of every partial,
+  //    and entries sl + TPC*j of list sw (slots the scan may not have written
+  //    this call are loaded too and ignored).  Indices are clamped, not
+  //    branched on.
+  const int sw = tid / TPC, sl = tid % TPC;
+  const int swc = sw < nw ? sw : nw - 1;
+  const uint2* slist = ws.blist + (prow + swc) * ws.chunk;
+  uint2 sv[RS];
+#pragma unroll
+  for (int j = 0; j < RS; ++j) sv[j] = slist[sl + TPC * j];
+  uint2 pw[NWMAX];
+#pragma unroll
+  for (int w = 0; w < NWMAX; ++w) {
+    const int wc = w < nw ? w : nw - 1;
+    pw[w] = *reinterpret_cast<const uint2*>(ws.part + (prow + wc) * kSelBins + 4 * tid);
+  }
+  const int nwr = (int)((n + 31) / 32);
+  for (int i = tid; i < nwr; i += NT) {
+    gbits[i] = 0u;
+    ebits[i] = 0u;
+  }
+  uint32_t q[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int w = 0; w < NWMAX; ++w) {
+    if (w < nw) {
+      q[0] += pw[w].x & 0xFFFFu;
+      q[1] += pw[w].x >> 16;
+      q[2] += pw[w].y & 0xFFFFu;
+      q[3] += pw[w].y >> 16;
+    }
+  }
+  qfirst[tid] = q[0];
+  __syncthreads();
+  {
+    // Q is non-increasing with Q[0] = n > k and Q[2048] = 0: one bin crosses.
+    const uint32_t qn = tid + 1 < NT ? qfirst[tid + 1] : 0u;
+    const uint32_t kk = (uint32_t)k;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t qa = q[i], qb = i < 3 ? q[i + 1] : qn;
+      if (qa >= kk && qb < kk) {
+        shb[0] = (uint32_t)(4 * tid + i);
+        shb[1] = qb;
+        shb[2] = qa - qb;
+#pragma unroll
+        for (int w = 0; w < NWMAX; ++w) {
+          const uint32_t word = (i < 2) ? pw[w].x : pw[w].y;
+          if (w < nw) ccnt[w] = (i & 1) ? (word >> 16) : (word & 0xFFFFu);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const uint32_t c = tid < nw ? ccnt[tid] : 0u;
+    const uint32_t inc = wave_incl_scan(c);
+    if (tid < nw) cstart[tid + 1] = inc;
+    if (tid == 0) cstart[0] = 0u;
+  }
+  __syncthreads();
+  const uint32_t bstar = shb[0], above = shb[1], eq = shb[2];
+  const int64_t N = (int64_t)above + eq;  // = cstart[nw]
+  __syncthreads();  // shb is reused by the radix levels
+
+  uint32_t* stage = reinterpret_cast<uint32_t*>(cand);  // the output row, once the candidates are done
+  if (N <= cap) {
+    // 2. The row's candidates into LDS: list w's first ccnt[w] entries.
+    if (sw < nw) {
+      const uint32_t cw = ccnt[sw], base = cstart[sw];
+#pragma unroll
+      for (int j = 0; j < RS; ++j) {
+        const uint32_t e = (uint32_t)(sl + TPC * j);
+        if (e < cw) cand[base + e] = sv[j];
+      }
+      for (uint32_t e = (uint32_t)(SPW + sl); e < cw; e += TPC) cand[base + e] = slist[e];
+    }
+    __syncthreads();
+    auto lkey = [&](int64_t e) { return cand[e].x; };
+    auto lpos = [&](int64_t e) { return (int64_t)cand[e].y; };
+    bucket_finish<NT>(row, lkey, lpos, N, bstar, above, eq, k, n, gbits, ebits, wpre, stage, hist, wsum, shb);
+  } else {
+    // Entry e of the row's candidates: the last list whose start is <= e.
+    auto gcand = [&](int64_t e) {
+      int lo = 0, hi = nw - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cstart[mid] <= (uint32_t)e) lo = mid; else hi = mid - 1;
+      }
+      return ws.blist[(prow + lo) * ws.chunk + ((uint32_t)e - cstart[lo])];
+    };
+    auto gkey = [&](int64_t e) { return gcand(e).x; };
+    auto gpos = [&](int64_t e) { return (int64_t)gcand(e).y; };
+    bucket_finish<NT>(row, gkey, gpos, N, bstar, above, eq, k, n, gbits, ebits, wpre, stage, hist, wsum, shb);
+  }
+}
+
 }  // namespace
 
 int64_t seg_len_for(int64_t rows, int64_t max_len) {
@@ -965,6 +1175,50 @@ hipError_t launch_topk_list(const TopkRows& a, const SelWs& ws, const uint2* lis
   const int cap = seg_cap_for(a.k);
   return launch_kernel(topk_list_kernel, dim3((unsigned)a.rows), dim3(kRowThreads), (uint32_t)(cap * sizeof(uint2)),
                        stream, a, ws, list, lcnt, cap);
+}
+
+int32_t bucket_cap_for(int32_t k, int64_t max_len) {
+  const int64_t bitmaps = 3 * ((max_len + 31) / 32) * 4;  // two bitmaps and the word prefixes
+  const int64_t room = (kBucketLds - bitmaps) / 8;
+  const int64_t want = 2 * (int64_t)k > (int64_t)k + 4096 ? 2 * (int64_t)k : (int64_t)k + 4096;
+  const int64_t cap = want < room ? want : room;
+  return (int32_t)(cap > 0 ? cap : 0);
+}
+
+bool bucket_ok(int64_t nwg, int64_t chunk, int32_t k, int64_t max_len) {
+  // The scan's own floor has to leave out at least half of each workgroup's
+  // keys for the lists to pay; the LDS candidate buffer also holds the output
+  // row (4 bytes per slot).
+  const int32_t cap = bucket_cap_for(k, max_len);
+  return nwg >= 1 && nwg <= kBucketMaxNwg && max_len <= kBucketMaxLen && 2 * (int64_t)k <= chunk &&
+         cap >= 1024 && 2 * (int64_t)cap >= k;
+}
+
+hipError_t launch_topk_bucket(const TopkRows& a, const SelWs& ws, int64_t max_len, hipStream_t stream) {
+  if (a.rows <= 0) return hipSuccess;
+  const int cap = bucket_cap_for(a.k, max_len);
+  const int nwords = (int)((max_len + 31) / 32);
+  const uint32_t lds = (uint32_t)cap * 8u + 3u * (uint32_t)nwords * 4u;
+  if (ws.nwg <= 16) {
+    static bool lds_set = false;
+    if (!lds_set) {
+      if (hipError_t e = hipFuncSetAttribute((const void*)topk_bucket_kernel<16>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBucketLds))
+        return e;
+      lds_set = true;
+    }
+    return launch_kernel(topk_bucket_kernel<16>, dim3((unsigned)a.rows), dim3(kBucketThreads), lds, stream, a, ws,
+                         cap, nwords);
+  }
+  static bool lds_set32 = false;
+  if (!lds_set32) {
+    if (hipError_t e = hipFuncSetAttribute((const void*)topk_bucket_kernel<kBucketMaxNwg>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBucketLds))
+      return e;
+    lds_set32 = true;
+  }
+  return launch_kernel(topk_bucket_kernel<kBucketMaxNwg>, dim3((unsigned)a.rows), dim3(kBucketThreads), lds, stream,
+                       a, ws, cap, nwords);
 }
 
 hipError_t launch_topk(const TopkRows& a, hipStream_t stream) {

@@ -61,8 +61,10 @@ int main() {
                          nullptr), LI_E_WORKSPACE);
   EXPECT(li_index_decode(F, LI_BF16, Ff, F, LI_FP8_E4M3, nullptr, Fo, 0, 100, 60, 64, 128, 16, Fi, nullptr, F, big,
                          nullptr), LI_OK);
-  EXPECT(li_index_decode_noalloc(F, LI_BF16, Ff, F, LI_FP8_E4M3, nullptr, Fo, 2, (int64_t)1 << 25, 60, 64, 128, 16,
-                                 Fi, nullptr, nullptr), LI_E_UNSUPPORTED);
+  EXPECT(li_index_decode_noalloc(F, LI_BF16, Ff, F, LI_FP8_E4M3, nullptr, Fo, 2, (int64_t)1 << 25, 1 << 22, 64, 128,
+                                 16, Fi, nullptr, nullptr), LI_E_UNSUPPORTED);
+  EXPECT(li_index_decode_noalloc(F, LI_BF16, Ff, F, LI_FP8_E4M3, nullptr, Fo, 64, (int64_t)64 << 17, 1 << 17, 64,
+                                 128, 16, Fi, nullptr, nullptr), LI_E_UNSUPPORTED);
   EXPECT(li_index_decode_noalloc(F, LI_BF16, Ff, F, LI_FP8_E4M3, nullptr, Fo, 0, 100, 60, 64, 128, 16, Fi, nullptr,
                                  nullptr), LI_OK);
   // prefill

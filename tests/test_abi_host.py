@@ -60,10 +60,21 @@ def test_status_strings():
 
 def test_workspace_queries():
     L = li.lib()
-    n = 655360
-    with_s = L.li_index_decode_ws(32, n, 32768, 2048, 1)
-    without = L.li_index_decode_ws(32, n, 32768, 2048, 0)
-    assert without - with_s >= n * 4 and with_s >= 32 * 2048 * 4
+    # rows spanning many scan workgroups (here 256 of 512 keys): the segmented
+    # selection, which reads a dense score matrix from the workspace when the
+    # caller passes none
+    n = 2 * 131072
+    with_s = L.li_index_decode_ws(2, n, 131072, 2048, 1)
+    without = L.li_index_decode_ws(2, n, 131072, 2048, 0)
+    assert without - with_s >= n * 4 and with_s >= 2 * 131072 * 8
+    # rows of at most 32 scan workgroups of at least 2k keys (here 16 of 8192):
+    # bucket lists (a pair per key) and no dense scores either way
+    n = 32 * 131072
+    with_s = L.li_index_decode_ws(32, n, 131072, 2048, 1)
+    without = L.li_index_decode_ws(32, n, 131072, 2048, 0)
+    assert without == with_s and with_s >= 32 * 131072 * 8
+    # the same rows with k = 8192 (more than half of a workgroup's keys): segmented
+    assert L.li_index_decode_ws(32, n, 131072, 8192, 0) - L.li_index_decode_ws(32, n, 131072, 8192, 1) >= n * 4
     # per-row candidate lists at their worst case: a (key, position) pair per visible key
     assert L.li_index_prefill_ws(4096, 65536, 2048, 0) >= 4096 * 65536 * 8
     # absorbed fp16 queries + scaled weights + scores
@@ -109,10 +120,14 @@ def test_noalloc_decode_host_checks():
         return L.li_index_decode_noalloc(q, li.LI_BF16, FAKE, FAKE, li.LI_FP8_E4M3, None, FAKE, B, n_tok, max_len,
                                          H, 128, 16, FAKE, sc, None)
 
-    assert call(n_tok=1 << 25) == li.LI_E_UNSUPPORTED  # 128 MiB of scores alone
+    # segmented selection (rows of 4M keys): 128 MiB of dense scores alone
+    assert L.li_index_decode_ws(2, 1 << 25, 1 << 22, 16, 0) > li.LI_NOALLOC_SCRATCH_BYTES
+    assert call(n_tok=1 << 25, max_len=1 << 22) == li.LI_E_UNSUPPORTED
     assert b"scratch" in L.li_last_error()
-    assert L.li_index_decode_ws(2, 1 << 25, 60, 16, 1) < li.LI_NOALLOC_SCRATCH_BYTES
-    assert call(n_tok=1 << 25, B=0) == li.LI_E_UNSUPPORTED  # the size check does not depend on B
+    assert call(n_tok=1 << 25, max_len=1 << 22, B=0) == li.LI_E_UNSUPPORTED  # the check does not depend on B
+    # bucket lists: a (key, position) pair per key of 64 rows of 128K
+    assert L.li_index_decode_ws(64, 64 << 17, 1 << 17, 16, 0) > li.LI_NOALLOC_SCRATCH_BYTES
+    assert call(B=64, n_tok=64 << 17, max_len=1 << 17) == li.LI_E_UNSUPPORTED
     assert call(q=None) == li.LI_E_NULL
     assert call(H=65) == li.LI_E_UNSUPPORTED
     assert call(B=-1) == li.LI_E_SHAPE

@@ -162,3 +162,52 @@ def test_decode_many_short_requests():
     keep all their keys, the rest select from a few hundred."""
     lens = np.random.default_rng(112).integers(0, 401, size=300)
     parity(inputs.make_decode(112, lens.tolist(), k=64), what="B=300 short")
+
+
+def test_decode_bucket_selection_ties_and_capacity():
+    """Rows of at most 32 scan workgroups of at least 2k keys select from the
+    scan's bin-ordered candidate lists (one workgroup per row); here k = 256
+    and 512 keys per scan workgroup.  With w = 0 every key ties at +0: the
+    3000-key row fits the selection's LDS candidate buffer (4352 pairs), the
+    5000- and 16384-key rows exceed it and are read from global memory; the
+    lowest positions win either way."""
+    lens = [5000, 3000, 16384, 257, 256, 0, 9000]
+    x = inputs.make_decode(113, lens, k=256)
+    parity(x, what="bucket random")
+    x.w = np.zeros_like(x.w)
+    parity(x, exact=True, what="bucket all-equal")
+    gi, _ = run_gpu(x, with_scores=False)
+    for b, n in enumerate(lens):
+        want = np.concatenate([np.arange(min(n, 256)), -np.ones(256 - min(n, 256))]).astype(np.int32)
+        assert np.array_equal(gi[b], want), f"bucket all-equal b={b}"
+
+
+def test_decode_128k_every_row_selects_the_top_k_of_its_own_scores():
+    """B = 32 requests of 131072 fp8 keys, k = 2048 (bucket selection, 16 scan
+    workgroups per row): every row's indices are the top k of the scores the
+    scan wrote, ties to the lowest positions, and the same without a score
+    output.  With w = 0 (all scores +0) the candidate sets are whole rows,
+    read from global memory, and the selection is positions 0 .. k-1."""
+    x = inputs.decode_sweep(131072)
+    print(f"[decode parity] sweep every row B={x.B}", flush=True)
+    q, w, kc, ks, off = dev(x.q, "bf16"), dev(x.w), dev(x.kc, x.k_dt), dev(x.k_scale), dev(x.kv_off)
+    sc = torch.empty(x.n_tok, dtype=torch.float32, device="cuda")
+    gi = li.li_index_decode(q, w, kc, ks, off, 131072, x.k, out_scores=sc)
+    torch.cuda.synchronize()
+    gs = sc.view(x.B, 131072)
+    gil = gi.long()
+    assert bool((gi >= 0).all()) and bool((gil.diff(dim=1) > 0).all())
+    kth = gs.gather(1, gil).min(dim=1).values
+    rest = gs.clone()
+    rest.scatter_(1, gil, float("-inf"))
+    top_rest = rest.max(dim=1).values
+    assert bool((kth >= top_rest).all()), "a key above a selected one was left out"
+    for b in torch.nonzero(kth == top_rest).flatten().tolist():
+        g, sel = gs[b].cpu().numpy(), gi[b].cpu().numpy()
+        v = kth[b].item()
+        out = np.setdiff1d(np.nonzero(g == v)[0], sel)
+        assert out.min() > sel[g[sel] == v].max(), f"row {b}: a tie went to a higher position"
+    gi2 = li.li_index_decode(q, w, kc, ks, off, 131072, x.k)
+    assert torch.equal(gi, gi2)
+    gi3 = li.li_index_decode(q, torch.zeros_like(w), kc, ks, off, 131072, x.k)
+    assert torch.equal(gi3.cpu(), torch.arange(x.k, dtype=torch.int32).expand(x.B, x.k))

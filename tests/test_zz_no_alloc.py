@@ -53,11 +53,12 @@ def test_noalloc_rejects_a_call_beyond_the_scratch():
     x = inputs.make_decode(1203, [64], k=16)
     q, w, kc, ks, off = dev(x.q, "bf16"), dev(x.w), dev(x.kc, x.k_dt), dev(x.k_scale), dev(x.kv_off)
     out = torch.empty((1, 16), dtype=torch.int32, device="cuda")
-    # n_tok as the caller states it sizes the score scratch: 2^25 rows need 128 MiB
+    # n_tok and max_len as the caller states them size the scratch: rows of up
+    # to 4M keys select through a dense score buffer, 128 MiB for 2^25 keys
     with pytest.raises(li.LiError) as e:
         li.lib()
         st = li.lib().li_index_decode_noalloc(li._ptr(q), li.LI_BF16, li._ptr(w), li._ptr(kc), li.LI_FP8_E4M3,
-                                              li._ptr(ks), li._ptr(off), 1, 1 << 25, 64, 64, 128, 16, li._ptr(out),
-                                              None, None)
+                                              li._ptr(ks), li._ptr(off), 1, 1 << 25, 1 << 22, 64, 128, 16,
+                                              li._ptr(out), None, None)
         li._check(st)
     assert e.value.status == li.LI_E_UNSUPPORTED and "scratch" in str(e.value)
