@@ -125,15 +125,20 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 // folds the two results of that builtin into one register.)
 __device__ __forceinline__ float sum_halves(float v) { return v + __shfl_xor(v, 32, 64); }
 
-// Inclusive scan of a uint32 over the 64 lanes of a wavefront.
+// Inclusive scan of a uint32 over the 64 lanes of a wavefront (every lane
+// active), with DPP moves instead of LDS-crossbar shuffles: within each row
+// of 16 lanes by row_shr 1, 2, 4 and 8 (a lane whose source lies outside its
+// row adds the 0 it keeps), then lane 15 of rows 0 and 2 into rows 1 and 3
+// (row_bcast:15) and lane 31 into rows 2 and 3 (row_bcast:31).
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    uint32_t o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
-  }
-  return v;
+  int x = (int)v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
+  return (uint32_t)x;
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -938,24 +938,28 @@ __device__ void bucket_finish(const Row& row, KeyAt key_at, PosAt pos_at, int64_
   }
   __syncthreads();
   // Per bitmap word, the marked positions before it: #greater << 18 | #equal
-  // (#greater < k <= 2^14, #equal <= n <= 2^17), one block scan over each
-  // thread's W consecutive words.
+  // (#greater < k <= 2^14, #equal <= n <= 2^17).  Wave v takes words
+  // [v*WPW, (v+1)*WPW) in rounds of 64 consecutive words (one per lane, no
+  // bank conflicts), scans each round within the wave and keeps a running
+  // total; the waves' totals then give each wave its offset.
+  constexpr int NWV = NT / 64;
   const int nwr = (int)((n + 31) / 32);
-  const int W = (nwr + NT - 1) / NT;
-  const int w0 = tid * W;
-  uint32_t c = 0;
-  for (int i = 0; i < W; ++i) {
-    if (w0 + i < nwr)
-      c += ((uint32_t)__builtin_popcount(gbits[w0 + i]) << 18) + (uint32_t)__builtin_popcount(ebits[w0 + i]);
+  const int WPW = ((nwr + NWV - 1) / NWV + 63) / 64 * 64;
+  const int wv = tid >> 6, ln = tid & 63;
+  uint32_t run = 0;
+  for (int w = wv * WPW + ln; w < (wv + 1) * WPW; w += 64) {
+    const uint32_t c = w < nwr ? ((uint32_t)__builtin_popcount(gbits[w]) << 18) +
+                                     (uint32_t)__builtin_popcount(ebits[w])
+                               : 0u;
+    const uint32_t inc = wave_incl_scan(c);
+    if (w < nwr) wpre[w] = run + inc - c;
+    run += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
   }
-  uint32_t total;
-  uint32_t run = block_excl_scan<NT>(c, wsum, total);
-  for (int i = 0; i < W; ++i) {
-    if (w0 + i < nwr) {
-      wpre[w0 + i] = run;
-      run += ((uint32_t)__builtin_popcount(gbits[w0 + i]) << 18) + (uint32_t)__builtin_popcount(ebits[w0 + i]);
-    }
-  }
+  if (ln == 0) wsum[wv] = run;
+  __syncthreads();
+  uint32_t woff = 0;
+  for (int v = 0; v < NWV; ++v) woff += v < wv ? wsum[v] : 0u;
+  for (int w = wv * WPW + ln; w < (wv + 1) * WPW && w < nwr; w += 64) wpre[w] += woff;
   __syncthreads();
   // Each kept candidate's slot: #greater-before + min(#equal-before, m), or
   // for an equal key #greater-before + #equal-before when that is below m.
@@ -998,6 +1002,23 @@ __global__ __launch_bounds__(kBucketThreads) void topk_bucket_kernel(TopkRows a,
   __shared__ int32_t sh[4];
   const int tid = threadIdx.x;
   const int r = blockIdx.x;
+  const int64_t prow = (int64_t)r * ws.nwg;
+  // 1. One round of loads, issued before the row's length is known (so they
+  //    do not wait for kv_off): the 8 bytes of bins 4t .. 4t+3 of every
+  //    partial, and entries sl + TPC*j of list sw.  Indices are clamped to the
+  //    workspace, not branched on; partials and list slots that the scan did
+  //    not write this call (past the row's end) are loaded and ignored.
+  const int sw = tid / TPC, sl = tid % TPC;
+  const uint2* slist = ws.blist + (prow + (sw < ws.nwg ? sw : ws.nwg - 1)) * ws.chunk;
+  uint2 sv[RS];
+#pragma unroll
+  for (int j = 0; j < RS; ++j) sv[j] = slist[sl + TPC * j];
+  uint2 pw[NWMAX];
+#pragma unroll
+  for (int w = 0; w < NWMAX; ++w) {
+    const int wc = w < ws.nwg ? w : ws.nwg - 1;
+    pw[w] = *reinterpret_cast<const uint2*>(ws.part + (prow + wc) * kSelBins + 4 * tid);
+  }
   const Row row = get_row(a, r, sh);
   const int64_t n = row.n;
   const int k = a.k;
@@ -1006,23 +1027,6 @@ __global__ __launch_bounds__(kBucketThreads) void topk_bucket_kernel(TopkRows a,
     return;
   }
   const int nw = (int)((n + ws.chunk - 1) / ws.chunk);  // <= ws.nwg <= NWMAX (host-checked)
-  const int64_t prow = (int64_t)r * ws.nwg;
-  // 1. One round of loads: the 8 bytes of bins 4t .. 4t+3 of every partial,
-  //    and entries sl + TPC*j of list sw (slots the scan may not have written
-  //    this call are loaded too and ignored).  Indices are clamped, not
-  //    branched on.
-  const int sw = tid / TPC, sl = tid % TPC;
-  const int swc = sw < nw ? sw : nw - 1;
-  const uint2* slist = ws.blist + (prow + swc) * ws.chunk;
-  uint2 sv[RS];
-#pragma unroll
-  for (int j = 0; j < RS; ++j) sv[j] = slist[sl + TPC * j];
-  uint2 pw[NWMAX];
-#pragma unroll
-  for (int w = 0; w < NWMAX; ++w) {
-    const int wc = w < nw ? w : nw - 1;
-    pw[w] = *reinterpret_cast<const uint2*>(ws.part + (prow + wc) * kSelBins + 4 * tid);
-  }
   const int nwr = (int)((n + 31) / 32);
   for (int i = tid; i < nwr; i += NT) {
     gbits[i] = 0u;
