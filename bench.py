@@ -599,7 +599,7 @@ def main():
     probe_bytes = kc.numel() * kc.element_size()
     probe_gbs = probe_bytes / (probe_ms * 1e-3) / 1e9
     del sink
-    traffic = load_traffic("decode_score", source_hash("decode.hip", "li_device.h"), keys)
+    traffic = load_traffic("decode_score", source_hash("decode.hip", "li_device.h", "li_select.h"), keys)
     log(f"[bench] step {ms_per_step:.3f} ms, scan {scan_ms * 1e3:.1f} us ({achieved:.0f} GB/s), "
         f"top-2048 {topk_ms * 1e3:.1f} us; read probe {probe_ms * 1e3:.1f} us ({probe_gbs:.0f} GB/s)")
 
