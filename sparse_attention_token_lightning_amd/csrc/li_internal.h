@@ -63,12 +63,14 @@ int32_t seg_cap_for(int32_t k);
 int64_t seg_len_for(int64_t rows, int64_t max_len);
 // Bucket mode (SelWs::bucket, decode): one workgroup per row reads the scan's
 // prefix partials and bin-ordered candidate lists.  Used when a row spans at
-// most kBucketMaxNwg scan workgroups of at least 2k positions, max_len <=
-// kBucketMaxLen (the LDS position bitmaps) and the LDS candidate capacity
-// left is useful.
+// most kBucketMaxNwg scan workgroups, each of at least 2k positions or at most
+// 4096 (every key then fits the scan's LDS staging), max_len <= kBucketMaxLen
+// (the LDS position bitmaps) and the LDS left for the threshold bin's keys is
+// useful.
 constexpr int kBucketMaxNwg = 32;
 constexpr int64_t kBucketMaxLen = 1 << 17;  // also keeps the packed word prefixes exact
 constexpr int64_t kBucketLds = 147456;  // dynamic LDS of the bucket top-k kernel
+constexpr int32_t kBucketStageK = 4096;  // output rows up to this k are staged in LDS
 int32_t bucket_cap_for(int32_t k, int64_t max_len);
 bool bucket_ok(int64_t nwg, int64_t chunk, int32_t k, int64_t max_len);
 hipError_t launch_topk_bucket(const TopkRows& a, const SelWs& ws, int64_t max_len, hipStream_t stream);

@@ -896,41 +896,43 @@ __global__ __launch_bounds__(kSegThreads) void topk_segmented_kernel(TopkRows a,
 // Bucket mode (decode): one workgroup per row, reading what the scan left
 // (SelWs::bucket).  Summing the scan workgroups' descending prefix counts
 // gives Q[b], the row's keys in bins >= b, so the threshold bin b* (Q[b*] >= k
-// > Q[b*+1]) needs no scan, and the first part_w[b*] entries of every list are
-// exactly the row's keys in bins >= b*.  Those lists' first entries are
-// loaded together with the partials (one round trip; the rest, if a list
-// holds more, afterwards), two more radix levels inside b* give the k-th key
-// T and the number m of keys equal to T that fit, and the kept positions are
-// marked in two LDS bitmaps (> T, == T); with per-word prefix counts of
-// those, every kept candidate finds its place in position order,
+// > Q[b*+1]) needs no scan; list w holds its keys in bins > b* first
+// (part_w[b*+1] of them), then those in b* (up to part_w[b*]).  The lists'
+// first entries are loaded together with the partials (one round trip; the
+// rest, where a list holds more, afterwards).  Keys above b* are all kept:
+// their positions are marked in a bitmap and kept as 4-byte positions.  Only
+// the keys in b* go through two more radix levels, which give the k-th key T
+// and the number m of keys equal to T that fit; those are marked in the
+// bitmaps (> T, == T) too.  With per-word prefix counts of the bitmaps every
+// kept position finds its place in position order,
 //   slot = #greater-before + min(#equal-before, m),
-// in an LDS copy of the output row, written out with coalesced stores.
-// Dynamic LDS: `cap` candidate pairs (reused for the output row), then the
-// two bitmaps and the word prefixes (nwords each).  Candidate sets beyond cap
-// are read from global memory instead.
+// in an LDS copy of the output row (k <= kBucketStageK; beyond, straight to
+// the output).  Dynamic LDS: ecap (key, position) pairs of bin b*, k
+// positions above it, the two bitmaps and the word prefixes (nwords each),
+// then the staged row.  A bin b* beyond ecap is read from global memory.
 constexpr int kBucketThreads = 512;
 
 template <int NT, typename KeyAt, typename PosAt>
-__device__ void bucket_finish(const Row& row, KeyAt key_at, PosAt pos_at, int64_t N, uint32_t bstar, uint32_t above,
-                              uint32_t eq, int64_t kk, int64_t n, uint32_t* gbits, uint32_t* ebits, uint32_t* wpre,
-                              uint32_t* stage, uint32_t* hist, uint32_t* wsum, uint32_t* shb) {
+__device__ void bucket_finish(const Row& row, KeyAt key_at, PosAt pos_at, uint32_t neq, const uint32_t* gpos,
+                              uint32_t ngt, uint32_t bstar, int64_t kk, int64_t n, uint32_t* gbits, uint32_t* ebits,
+                              uint32_t* wpre, uint32_t* stage, uint32_t* hist, uint32_t* wsum, uint32_t* shb) {
   const int tid = threadIdx.x;
-  uint32_t prefix = bstar << kSelShift, pmask = 0xFFE00000u, rem = (uint32_t)kk - above, cnt = eq;
+  uint32_t prefix = bstar << kSelShift, pmask = 0xFFE00000u, rem = (uint32_t)kk - ngt, cnt = neq;
 #pragma unroll 1
   for (int level = 1; level < 3 && cnt != rem; ++level) {
     const int shift = level == 1 ? 10 : 0;
     const int nb = level == 1 ? kSelBins : kSelBins / 2;
-    radix_level<NT>(key_at, N, prefix, pmask, shift, nb, rem, hist, wsum, shb);
+    radix_level<NT>(key_at, (int64_t)neq, prefix, pmask, shift, nb, rem, hist, wsum, shb);
     prefix |= shb[0] << shift;
     pmask |= (uint32_t)(nb - 1) << shift;
     rem -= shb[1];
     cnt = shb[2];
     __syncthreads();
   }
-  // Keys above the resolved prefix are kept; of those equal to it, the first
-  // rem by position.
+  // Keys of b* above the resolved prefix are kept; of those equal to it, the
+  // first rem by position.
 #pragma unroll 1
-  for (int64_t e = tid; e < N; e += NT) {
+  for (uint32_t e = tid; e < neq; e += NT) {
     const uint32_t key = key_at(e) & pmask;
     const uint32_t p = (uint32_t)pos_at(e);
     if (key > prefix) atomicOr(&gbits[p >> 5], 1u << (p & 31));
@@ -961,42 +963,53 @@ __device__ void bucket_finish(const Row& row, KeyAt key_at, PosAt pos_at, int64_
   for (int v = 0; v < NWV; ++v) woff += v < wv ? wsum[v] : 0u;
   for (int w = wv * WPW + ln; w < (wv + 1) * WPW && w < nwr; w += 64) wpre[w] += woff;
   __syncthreads();
-  // Each kept candidate's slot: #greater-before + min(#equal-before, m), or
-  // for an equal key #greater-before + #equal-before when that is below m.
+  // Every kept position's slot: #greater-before + min(#equal-before, m), or for
+  // an equal key #greater-before + #equal-before when that is below m.
   const uint32_t m = rem;
-#pragma unroll 1
-  for (int64_t e = tid; e < N; e += NT) {
-    const uint32_t key = key_at(e) & pmask;
-    const uint32_t p = (uint32_t)pos_at(e);
+  auto place = [&](uint32_t p, bool greater) {
     const uint32_t w = p >> 5, below = (1u << (p & 31)) - 1u;
     const uint32_t pre = wpre[w];
     const uint32_t gb = (pre >> 18) + (uint32_t)__builtin_popcount(gbits[w] & below);
     const uint32_t eb = (pre & 0x3FFFFu) + (uint32_t)__builtin_popcount(ebits[w] & below);
-    uint32_t slot = 0xFFFFFFFFu;
-    if (key > prefix) slot = gb + (eb < m ? eb : m);
-    else if (key == prefix && eb < m) slot = gb + eb;
-    if (slot < (uint32_t)kk) stage[slot] = p;
+    const uint32_t slot = greater ? gb + (eb < m ? eb : m) : (eb < m ? gb + eb : 0xFFFFFFFFu);
+    if (slot < (uint32_t)kk) {
+      if (stage) stage[slot] = p;
+      else row.out[slot] = (int32_t)p;
+    }
+  };
+#pragma unroll 1
+  for (uint32_t e = tid; e < ngt; e += NT) place(gpos[e], true);
+#pragma unroll 1
+  for (uint32_t e = tid; e < neq; e += NT) {
+    const uint32_t key = key_at(e) & pmask;
+    if (key >= prefix) place((uint32_t)pos_at(e), key > prefix);
   }
-  __syncthreads();
-  for (int i = tid; i < kk; i += NT) row.out[i] = (int32_t)stage[i];
+  if (stage) {
+    __syncthreads();
+    for (int i = tid; i < kk; i += NT) row.out[i] = (int32_t)stage[i];
+  }
 }
 
 template <int NWMAX>
-__global__ __launch_bounds__(kBucketThreads) void topk_bucket_kernel(TopkRows a, SelWs ws, int cap, int nwords) {
+__global__ __launch_bounds__(kBucketThreads) void topk_bucket_kernel(TopkRows a, SelWs ws, int ecap, int nwords,
+                                                                     int staged) {
   constexpr int NT = kBucketThreads;
   static_assert(4 * NT == kSelBins, "four level-0 bins per thread");
-  constexpr int TPC = NT / NWMAX;  // threads per list in the up-front loads
-  constexpr int RS = 8;            // up-front entries per thread
-  constexpr int SPW = TPC * RS;    // entries per list loaded up front (<= 512 <= any chunk)
+  constexpr int TPC = NT / NWMAX;              // threads per list in the up-front loads
+  constexpr int RS = NWMAX <= 16 ? 8 : 24;     // up-front entries per thread
+  constexpr int SPW = TPC * RS;                // entries per list loaded up front (256 or 384)
   extern __shared__ uint2 bdyn[];
-  uint2* cand = bdyn;
-  uint32_t* gbits = reinterpret_cast<uint32_t*>(bdyn + cap);
+  const int k = a.k;
+  uint2* eqc = bdyn;
+  uint32_t* gpos = reinterpret_cast<uint32_t*>(bdyn + ecap);
+  uint32_t* gbits = gpos + k;
   uint32_t* ebits = gbits + nwords;
   uint32_t* wpre = ebits + nwords;
+  uint32_t* stage = staged ? wpre + nwords : nullptr;
   __shared__ uint32_t hist[kSelBins];
-  __shared__ uint32_t qfirst[NT];
-  __shared__ uint32_t ccnt[NWMAX];
-  __shared__ uint32_t cstart[NWMAX + 1];
+  __shared__ uint32_t qfirst[NT], qlast[NT];
+  __shared__ uint32_t cge[NWMAX], cgt[NWMAX];  // per list: keys in bins >= b*, in bins > b*
+  __shared__ uint32_t gstart[NWMAX + 1], estart[NWMAX + 1];
   __shared__ uint32_t wsum[NT / 64];
   __shared__ uint32_t shb[4];
   __shared__ int32_t sh[4];
@@ -1021,7 +1034,6 @@ __global__ __launch_bounds__(kBucketThreads) void topk_bucket_kernel(TopkRows a,
   }
   const Row row = get_row(a, r, sh);
   const int64_t n = row.n;
-  const int k = a.k;
   if (n <= k) {
     keep_all<NT>(row, n, k);
     return;
@@ -1033,21 +1045,26 @@ __global__ __launch_bounds__(kBucketThreads) void topk_bucket_kernel(TopkRows a,
     ebits[i] = 0u;
   }
   uint32_t q[4] = {0u, 0u, 0u, 0u};
+  auto half = [&](const uint2& v, int i) {
+    const uint32_t word = i < 2 ? v.x : v.y;
+    return (i & 1) ? (word >> 16) : (word & 0xFFFFu);
+  };
 #pragma unroll
   for (int w = 0; w < NWMAX; ++w) {
     if (w < nw) {
-      q[0] += pw[w].x & 0xFFFFu;
-      q[1] += pw[w].x >> 16;
-      q[2] += pw[w].y & 0xFFFFu;
-      q[3] += pw[w].y >> 16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] += half(pw[w], i);
     }
   }
   qfirst[tid] = q[0];
+  qlast[tid] = q[3];
   __syncthreads();
   {
     // Q is non-increasing with Q[0] = n > k and Q[2048] = 0: one bin crosses.
-    const uint32_t qn = tid + 1 < NT ? qfirst[tid + 1] : 0u;
+    // Its thread records part_w[b*] and, but for the last bin of its four,
+    // part_w[b*+1]; in that case the next thread records the latter.
     const uint32_t kk = (uint32_t)k;
+    const uint32_t qn = tid + 1 < NT ? qfirst[tid + 1] : 0u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t qa = q[i], qb = i < 3 ? q[i + 1] : qn;
@@ -1057,53 +1074,86 @@ __global__ __launch_bounds__(kBucketThreads) void topk_bucket_kernel(TopkRows a,
         shb[2] = qa - qb;
 #pragma unroll
         for (int w = 0; w < NWMAX; ++w) {
-          const uint32_t word = (i < 2) ? pw[w].x : pw[w].y;
-          if (w < nw) ccnt[w] = (i & 1) ? (word >> 16) : (word & 0xFFFFu);
+          if (w < nw) {
+            cge[w] = half(pw[w], i);
+            if (i < 3) cgt[w] = half(pw[w], i + 1);
+            else if (tid == NT - 1) cgt[w] = 0u;
+          }
         }
       }
+    }
+    if (tid > 0 && q[0] < kk && qlast[tid - 1] >= kk) {
+#pragma unroll
+      for (int w = 0; w < NWMAX; ++w)
+        if (w < nw) cgt[w] = half(pw[w], 0);
     }
   }
   __syncthreads();
   if (tid < 64) {
-    const uint32_t c = tid < nw ? ccnt[tid] : 0u;
-    const uint32_t inc = wave_incl_scan(c);
-    if (tid < nw) cstart[tid + 1] = inc;
-    if (tid == 0) cstart[0] = 0u;
+    const uint32_t g = tid < nw ? cgt[tid] : 0u, e = tid < nw ? cge[tid] - cgt[tid] : 0u;
+    const uint32_t gi = wave_incl_scan(g), ei = wave_incl_scan(e);
+    if (tid < nw) {
+      gstart[tid + 1] = gi;
+      estart[tid + 1] = ei;
+    }
+    if (tid == 0) {
+      gstart[0] = 0u;
+      estart[0] = 0u;
+    }
   }
   __syncthreads();
-  const uint32_t bstar = shb[0], above = shb[1], eq = shb[2];
-  const int64_t N = (int64_t)above + eq;  // = cstart[nw]
+  const uint32_t bstar = shb[0], ngt = shb[1], neq = shb[2];
   __syncthreads();  // shb is reused by the radix levels
+  const bool eq_lds = neq <= (uint32_t)ecap;
 
-  uint32_t* stage = reinterpret_cast<uint32_t*>(cand);  // the output row, once the candidates are done
-  if (N <= cap) {
-    // 2. The row's candidates into LDS: list w's first ccnt[w] entries.
-    if (sw < nw) {
-      const uint32_t cw = ccnt[sw], base = cstart[sw];
-#pragma unroll
-      for (int j = 0; j < RS; ++j) {
-        const uint32_t e = (uint32_t)(sl + TPC * j);
-        if (e < cw) cand[base + e] = sv[j];
+  // 2. Entry e of list w: below cgt[w] a key above b* (its position is kept
+  //    and marked), below cge[w] a key of b* (into LDS when they fit).
+  if (sw < nw) {
+    const uint32_t cw = cge[sw], gw = cgt[sw], gb = gstart[sw], eb = estart[sw];
+    auto put = [&](uint32_t e, const uint2& v) {
+      if (e < gw) {
+        gpos[gb + e] = v.y;
+        atomicOr(&gbits[v.y >> 5], 1u << (v.y & 31));
+      } else if (e < cw && eq_lds) {
+        eqc[eb + (e - gw)] = v;
       }
-      for (uint32_t e = (uint32_t)(SPW + sl); e < cw; e += TPC) cand[base + e] = slist[e];
+    };
+#pragma unroll
+    for (int j = 0; j < RS; ++j) put((uint32_t)(sl + TPC * j), sv[j]);
+    // the rest of a long list, eight loads per thread at a time
+#pragma unroll 1
+    for (uint32_t e0 = (uint32_t)(SPW + sl); e0 < cw; e0 += 8 * TPC) {
+      uint2 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t e = e0 + TPC * j;
+        v[j] = slist[e < cw ? e : cw - 1];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t e = e0 + TPC * j;
+        if (e < cw) put(e, v[j]);
+      }
     }
-    __syncthreads();
-    auto lkey = [&](int64_t e) { return cand[e].x; };
-    auto lpos = [&](int64_t e) { return (int64_t)cand[e].y; };
-    bucket_finish<NT>(row, lkey, lpos, N, bstar, above, eq, k, n, gbits, ebits, wpre, stage, hist, wsum, shb);
+  }
+  __syncthreads();
+  if (eq_lds) {
+    auto lkey = [&](int64_t e) { return eqc[e].x; };
+    auto lpos = [&](int64_t e) { return (int64_t)eqc[e].y; };
+    bucket_finish<NT>(row, lkey, lpos, neq, gpos, ngt, bstar, k, n, gbits, ebits, wpre, stage, hist, wsum, shb);
   } else {
-    // Entry e of the row's candidates: the last list whose start is <= e.
+    // Entry e of bin b*: list w with estart[w] <= e < estart[w+1], at cgt[w] + (e - estart[w]).
     auto gcand = [&](int64_t e) {
       int lo = 0, hi = nw - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (cstart[mid] <= (uint32_t)e) lo = mid; else hi = mid - 1;
+        if (estart[mid] <= (uint32_t)e) lo = mid; else hi = mid - 1;
       }
-      return ws.blist[(prow + lo) * ws.chunk + ((uint32_t)e - cstart[lo])];
+      return ws.blist[(prow + lo) * ws.chunk + cgt[lo] + ((uint32_t)e - estart[lo])];
     };
     auto gkey = [&](int64_t e) { return gcand(e).x; };
-    auto gpos = [&](int64_t e) { return (int64_t)gcand(e).y; };
-    bucket_finish<NT>(row, gkey, gpos, N, bstar, above, eq, k, n, gbits, ebits, wpre, stage, hist, wsum, shb);
+    auto gpos_at = [&](int64_t e) { return (int64_t)gcand(e).y; };
+    bucket_finish<NT>(row, gkey, gpos_at, neq, gpos, ngt, bstar, k, n, gbits, ebits, wpre, stage, hist, wsum, shb);
   }
 }
 
@@ -1181,28 +1231,32 @@ hipError_t launch_topk_list(const TopkRows& a, const SelWs& ws, const uint2* lis
                        stream, a, ws, list, lcnt, cap);
 }
 
+// LDS of the bucket top-k besides the (key, position) pairs of bin b*: k
+// positions above b*, two bitmaps and the word prefixes, and the staged
+// output row when k <= kBucketStageK.
+static int64_t bucket_fixed_lds(int32_t k, int64_t max_len) {
+  return 4 * (int64_t)k + 3 * ((max_len + 31) / 32) * 4 + (k <= kBucketStageK ? 4 * (int64_t)k : 0);
+}
+
 int32_t bucket_cap_for(int32_t k, int64_t max_len) {
-  const int64_t bitmaps = 3 * ((max_len + 31) / 32) * 4;  // two bitmaps and the word prefixes
-  const int64_t room = (kBucketLds - bitmaps) / 8;
-  const int64_t want = 2 * (int64_t)k > (int64_t)k + 4096 ? 2 * (int64_t)k : (int64_t)k + 4096;
-  const int64_t cap = want < room ? want : room;
-  return (int32_t)(cap > 0 ? cap : 0);
+  const int64_t room = (kBucketLds - bucket_fixed_lds(k, max_len)) / 8;
+  return (int32_t)(room > 0 ? room : 0);
 }
 
 bool bucket_ok(int64_t nwg, int64_t chunk, int32_t k, int64_t max_len) {
-  // The scan's own floor has to leave out at least half of each workgroup's
-  // keys for the lists to pay; the LDS candidate buffer also holds the output
-  // row (4 bytes per slot).
-  const int32_t cap = bucket_cap_for(k, max_len);
-  return nwg >= 1 && nwg <= kBucketMaxNwg && max_len <= kBucketMaxLen && 2 * (int64_t)k <= chunk &&
-         cap >= 1024 && 2 * (int64_t)cap >= k;
+  // The scan's lists must fit its LDS staging (every key when the workgroup
+  // holds at most 4096, else the floor must leave out at least half), and the
+  // selection needs useful room for the keys of the threshold bin.
+  return nwg >= 1 && nwg <= kBucketMaxNwg && max_len <= kBucketMaxLen &&
+         (2 * (int64_t)k <= chunk || chunk <= 4096) && bucket_cap_for(k, max_len) >= 1024;
 }
 
 hipError_t launch_topk_bucket(const TopkRows& a, const SelWs& ws, int64_t max_len, hipStream_t stream) {
   if (a.rows <= 0) return hipSuccess;
-  const int cap = bucket_cap_for(a.k, max_len);
+  const int ecap = bucket_cap_for(a.k, max_len);
   const int nwords = (int)((max_len + 31) / 32);
-  const uint32_t lds = (uint32_t)cap * 8u + 3u * (uint32_t)nwords * 4u;
+  const int staged = a.k <= kBucketStageK ? 1 : 0;
+  const uint32_t lds = (uint32_t)ecap * 8u + (uint32_t)bucket_fixed_lds(a.k, max_len);
   if (ws.nwg <= 16) {
     static bool lds_set = false;
     if (!lds_set) {
@@ -1212,7 +1266,7 @@ hipError_t launch_topk_bucket(const TopkRows& a, const SelWs& ws, int64_t max_le
       lds_set = true;
     }
     return launch_kernel(topk_bucket_kernel<16>, dim3((unsigned)a.rows), dim3(kBucketThreads), lds, stream, a, ws,
-                         cap, nwords);
+                         ecap, nwords, staged);
   }
   static bool lds_set32 = false;
   if (!lds_set32) {
@@ -1222,7 +1276,7 @@ hipError_t launch_topk_bucket(const TopkRows& a, const SelWs& ws, int64_t max_le
     lds_set32 = true;
   }
   return launch_kernel(topk_bucket_kernel<kBucketMaxNwg>, dim3((unsigned)a.rows), dim3(kBucketThreads), lds, stream,
-                       a, ws, cap, nwords);
+                       a, ws, ecap, nwords, staged);
 }
 
 hipError_t launch_topk(const TopkRows& a, hipStream_t stream) {

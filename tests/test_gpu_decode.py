@@ -167,10 +167,9 @@ def test_decode_many_short_requests():
 def test_decode_bucket_selection_ties_and_capacity():
     """Rows of at most 32 scan workgroups of at least 2k keys select from the
     scan's bin-ordered candidate lists (one workgroup per row); here k = 256
-    and 512 keys per scan workgroup.  With w = 0 every key ties at +0: the
-    3000-key row fits the selection's LDS candidate buffer (4352 pairs), the
-    5000- and 16384-key rows exceed it and are read from global memory; the
-    lowest positions win either way."""
+    and 512 keys per scan workgroup.  With w = 0 every key ties at +0, so the
+    whole row is the threshold bin and goes through both radix levels; the
+    lowest positions win."""
     lens = [5000, 3000, 16384, 257, 256, 0, 9000]
     x = inputs.make_decode(113, lens, k=256)
     parity(x, what="bucket random")
@@ -211,3 +210,38 @@ def test_decode_128k_every_row_selects_the_top_k_of_its_own_scores():
     assert torch.equal(gi, gi2)
     gi3 = li.li_index_decode(q, torch.zeros_like(w), kc, ks, off, 131072, x.k)
     assert torch.equal(gi3.cpu(), torch.arange(x.k, dtype=torch.int32).expand(x.B, x.k))
+
+
+def check_rows_are_top_k_of_own_scores(gi, gs):
+    gil = gi.long()
+    assert bool((gi >= 0).all()) and bool((gil.diff(dim=1) > 0).all())
+    kth = gs.gather(1, gil).min(dim=1).values
+    rest = gs.clone()
+    rest.scatter_(1, gil, float("-inf"))
+    top_rest = rest.max(dim=1).values
+    assert bool((kth >= top_rest).all()), "a key above a selected one was left out"
+    for b in torch.nonzero(kth == top_rest).flatten().tolist():
+        g, sel = gs[b].cpu().numpy(), gi[b].cpu().numpy()
+        out = np.setdiff1d(np.nonzero(g == kth[b].item())[0], sel)
+        assert out.min() > sel[g[sel] == kth[b].item()].max(), f"row {b}: a tie went to a higher position"
+
+
+def test_decode_anchor_shape_k8192_every_row():
+    """The HS anchor's shape: B = 16 requests of 131072 fp8 keys with k = 8192
+    (4096 keys per scan workgroup, so the scan lists every key and the
+    selection resolves the threshold bin from them).  Every row is the top k of
+    its own scores; all tied, positions 0 .. k-1."""
+    x = inputs.decode_sweep(131072)
+    nb, L = 16, 131072
+    q, w = dev(x.q[:nb], "bf16"), dev(x.w[:nb])
+    kc, ks = dev(x.kc[:nb * L], x.k_dt), dev(x.k_scale[:nb * L])
+    off = dev(x.kv_off[:nb + 1])
+    k = 8192
+    print(f"[decode parity] anchor shape B={nb} L={L} k={k}", flush=True)
+    sc = torch.empty(nb * L, dtype=torch.float32, device="cuda")
+    gi = li.li_index_decode(q, w, kc, ks, off, L, k, out_scores=sc)
+    torch.cuda.synchronize()
+    check_rows_are_top_k_of_own_scores(gi, sc.view(nb, L))
+    assert torch.equal(gi, li.li_index_decode(q, w, kc, ks, off, L, k))
+    gi0 = li.li_index_decode(q, torch.zeros_like(w), kc, ks, off, L, k)
+    assert torch.equal(gi0.cpu(), torch.arange(k, dtype=torch.int32).expand(nb, k))
