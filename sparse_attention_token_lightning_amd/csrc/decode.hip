@@ -160,14 +160,7 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
     for (int st = 0; st < kStages - 1; ++st) load_tile(buf[st], scb[st], st < nt ? st : nt - 1);
     const int nit = (nt + kStages - 1) / kStages * kStages;
     for (int base = 0; base < nit; base += kStages) {
-      // Waves further from their end get a higher issue priority (quarters
-      // of the tiles: 3 .. 0), so the two workgroups of a CU, of which the
-      // older would otherwise win every tie, stream at similar rates.
-      const int qtr = (4 * base) / nit;
-      if (qtr == 0) __builtin_amdgcn_s_setprio(3);
-      else if (qtr == 1) __builtin_amdgcn_s_setprio(2);
-      else if (qtr == 2) __builtin_amdgcn_s_setprio(1);
-      else __builtin_amdgcn_s_setprio(0);
+      set_progress_priority(base, nit);
 #pragma unroll
       for (int st = 0; st < kStages; ++st) {
         const int it = base + st;

@@ -293,9 +293,17 @@ __global__ __launch_bounds__(kLsThreads, 2) void latent_score_kernel(
   // F8: the thread's 8*CPT values are 8*CPT fp8 bytes (CPT / 2 loads) inside
   // one 128-value block, whose scale comes with them; F8N: CPT 8-byte loads
   // (chunk i in dst[i].xy) and the scales of the blocks they fall in.
-  auto gload = [&](i32x4 (&dst)[CPT], float (&bsc)[2], int tile) {
-    const int t = tile < ntiles ? tile : ntiles - 1;
-    const int64_t row = row_of(tok0 + (int64_t)t * 32 + pt);
+  // The gather's candidate index of the producer's row in a tile, loaded one
+  // step ahead of that tile's latent row so the two loads do not chain.
+  auto cidx_of = [&](int tile) -> int64_t {
+    if constexpr (GATHER) {
+      int64_t s = tok0 + (int64_t)(tile < ntiles ? tile : ntiles - 1) * 32 + pt;
+      return cb[s < n ? s : n - 1];
+    } else {
+      return 0;
+    }
+  };
+  auto gload_row = [&](i32x4 (&dst)[CPT], float (&bsc)[2], int64_t row) {
     if constexpr (F8N) {
       const uint8_t* src = reinterpret_cast<const uint8_t*>(latent) + row * DC + 8 * CPT * p;
 #pragma unroll
@@ -317,6 +325,10 @@ __global__ __launch_bounds__(kLsThreads, 2) void latent_score_kernel(
       for (int i = 0; i < CPT; ++i) dst[i] = ld16(src + 8 * i);
       bsc[0] = bsc[1] = 1.0f;
     }
+  };
+  auto gload = [&](i32x4 (&dst)[CPT], float (&bsc)[2], int tile) {
+    const int t = tile < ntiles ? tile : ntiles - 1;
+    gload_row(dst, bsc, row_of(tok0 + (int64_t)t * 32 + pt));
   };
   auto lstore = [&](int slot, const i32x4 (&src)[CPT], const float (&bsc)[2]) {
     F8Scale f0 = {}, f1 = {};
@@ -361,9 +373,11 @@ __global__ __launch_bounds__(kLsThreads, 2) void latent_score_kernel(
   skr[0] = row_scale(0);
   lstore(0, gk[0], gs[0]);
   gload(gk[0], gs[0], 2);
+  int64_t cnext = cidx_of(3);  // gather: the index of the producer's row of tile 3
   __syncthreads();
   const int nsteps = (ntiles + 1) / 2 * 2;
   for (int base = 0; base < nsteps; base += 2) {
+    set_progress_priority(base, nsteps);
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int it = base + st;
@@ -402,7 +416,12 @@ __global__ __launch_bounds__(kLsThreads, 2) void latent_score_kernel(
         bfrag(st, 1, bk);
       }
       lstore(st ^ 1, gk[st ^ 1], gs[st ^ 1]);
-      gload(gk[st ^ 1], gs[st ^ 1], it + 3);
+      if constexpr (GATHER) {
+        gload_row(gk[st ^ 1], gs[st ^ 1], off + cnext);
+        cnext = cidx_of(it + 4);
+      } else {
+        gload(gk[st ^ 1], gs[st ^ 1], it + 3);
+      }
       if (work) {
         __builtin_amdgcn_sched_barrier(0);
         issue(4);
@@ -436,6 +455,7 @@ __global__ __launch_bounds__(kLsThreads, 2) void latent_score_kernel(
     }
   }
 
+  __builtin_amdgcn_s_setprio(0);
   // Scores of this workgroup's rows, one burst per layer (16-byte stores
   // where the destination is aligned).
   const int nrow = (int)((n - tok0) < (int64_t)ntiles * 32 ? (n - tok0) : (int64_t)ntiles * 32);
@@ -610,6 +630,7 @@ __global__ __launch_bounds__(kSpThreads) void latent_split_kernel(
   __syncthreads();
   const int nsteps = (ntiles + 1) / 2 * 2;
   for (int base = 0; base < nsteps; base += 2) {
+    set_progress_priority(base, nsteps);
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int it = base + st;
@@ -662,6 +683,7 @@ __global__ __launch_bounds__(kSpThreads) void latent_split_kernel(
     }
   }
 
+  __builtin_amdgcn_s_setprio(0);
   // Scores of this workgroup's rows, one pass per layer (16-byte stores where
   // the destination is aligned), and their histogram counts.
   const int nrow = (int)((n - tok0) < (int64_t)ntiles * 32 ? (n - tok0) : (int64_t)ntiles * 32);

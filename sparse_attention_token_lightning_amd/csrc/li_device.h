@@ -141,6 +141,18 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return (uint32_t)x;
 }
 
+// Issue priority by progress: 3 in the first quarter of a wave's steps down
+// to 0 in the last.  Two workgroups share each CU in the streaming scans, and
+// the older one's waves would otherwise win every issue tie and finish well
+// before the other's.
+__device__ __forceinline__ void set_progress_priority(int step, int nsteps) {
+  const int qtr = (4 * step) / (nsteps > 0 ? nsteps : 1);
+  if (qtr == 0) __builtin_amdgcn_s_setprio(3);
+  else if (qtr == 1) __builtin_amdgcn_s_setprio(2);
+  else if (qtr == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
