@@ -55,11 +55,11 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
   constexpr int NV = FP8 ? 4 : 8;             // 16-byte vectors per lane per tile
   constexpr int kRowBytes = FP8 ? 128 : 256;  // one key row
   constexpr int kStages = FP8 ? kStagesFp8 : kStagesBf16;
-  __shared__ uint32_t lhist[kSelBins + 64];  // + spare words for the bucket epilogue
-  // The workgroup's scores, written to HBM in one burst at the end: small
-  // writes interleaved with the key stream cost far more read bandwidth than
-  // their own size.
-  __shared__ __attribute__((aligned(16))) float ssc[kDecMaxChunk];
+  __shared__ __attribute__((aligned(16))) uint32_t lhist[kSelBins + 128];  // + spare words for the bucket epilogue
+  // The workgroup's scores as order-preserving keys (score_key), written to
+  // HBM in one burst at the end: small writes interleaved with the key stream
+  // cost far more read bandwidth than their own size.
+  __shared__ __attribute__((aligned(16))) uint32_t ssc[kDecMaxChunk];
   __shared__ uint32_t wsum[kDecWaves];
   __shared__ uint32_t sh_floor[2];
 
@@ -145,9 +145,9 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
     // loads' wait counting stays exact).  Positions past L are dropped at the
     // final write; a repeated padding tile rewrites identical values.
     const int64_t s = tok(it);
-    const float val = part * sc;
-    if (g == 0) ssc[s - wg0] = val;
-    if (select && live && g == 0 && s < L) atomicAdd(&lhist[score_key(val) >> kSelShift], 1u);
+    const uint32_t key = score_key(part * sc);
+    if (g == 0) ssc[s - wg0] = key;
+    if (select && live && g == 0 && s < L) atomicAdd(&lhist[key >> kSelShift], 1u);
   };
 
   if (nt > 0) {
@@ -180,11 +180,14 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
     float* dst = scores + off + wg0;
     if (((off + wg0) & 3) == 0) {
       const int64_t n4 = n >> 2;
-      for (int64_t i = tid; i < n4; i += 256)
-        *reinterpret_cast<f32x4*>(dst + 4 * i) = *reinterpret_cast<const f32x4*>(&ssc[4 * i]);
-      for (int64_t i = 4 * n4 + tid; i < n; i += 256) dst[i] = ssc[i];
+      for (int64_t i = tid; i < n4; i += 256) {
+        const i32x4 kv = *reinterpret_cast<const i32x4*>(&ssc[4 * i]);
+        *reinterpret_cast<f32x4*>(dst + 4 * i) =
+            f32x4{key_score(kv.x), key_score(kv.y), key_score(kv.z), key_score(kv.w)};
+      }
+      for (int64_t i = 4 * n4 + tid; i < n; i += 256) dst[i] = key_score(ssc[i]);
     } else {
-      for (int64_t i = tid; i < n; i += 256) dst[i] = ssc[i];
+      for (int64_t i = tid; i < n; i += 256) dst[i] = key_score(ssc[i]);
     }
   }
   if (!select) return;

@@ -120,6 +120,11 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The score of a key (the inverse of score_key; -0 comes back as +0).
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __builtin_bit_cast(float, (k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
 // Sum of v over lanes l and l^32, in every lane.  (A cross-lane shuffle;
 // gfx950's v_permlane32_swap would avoid the LDS crossbar, but this compiler
 // folds the two results of that builtin into one register.)

@@ -93,21 +93,21 @@ constexpr int kBufferWord3 = 0x00020000;
 constexpr uint32_t kBufferDrop = 0x80000000u;
 
 // End of a scan workgroup in bucket mode.  lhist holds the level-0 counts of
-// the workgroup's n scores (ssc[0 .. n-1], positions pos0 + i) followed by 64
-// spare words; NT threads, PER = 8 bins each.  Stores the descending prefix
-// counts to pdst (16-bit: n <= CH <= 65535), then writes every key whose bin
-// is at or above the bin of the workgroup's own min(k, n)-th largest key to
-// ldst, bin by bin from the top (a key of a lower bin cannot be among the
-// row's k largest: the k-th largest of a part of the row is at most the k-th
-// largest of the row).  The order inside a bin is that of the LDS cursor
-// atomics; the selection does not depend on it.  lhist and ssc are
-// overwritten (cursors; the list is staged over the scores when it fits);
-// sh holds two words of scratch.
+// the workgroup's n keys (sk[0 .. n-1], score_key of the scores, positions
+// pos0 + i) followed by 128 spare words; NT threads, PER = 8 bins each.
+// Stores the descending prefix counts to pdst (16-bit: n <= CH <= 65535), then
+// writes every key whose bin is at or above the bin of the workgroup's own
+// min(k, n)-th largest key to ldst, bin by bin from the top (a key of a lower
+// bin cannot be among the row's k largest: the k-th largest of a part of the
+// row is at most the k-th largest of the row).  The order inside a bin is that
+// of the LDS cursor atomics; the selection does not depend on it.  lhist and
+// sk are overwritten (cursors; the list is staged over the keys when it
+// fits); sh holds two words of scratch.
 template <int NT, int CH>
-__device__ __forceinline__ void bucket_epilogue(uint32_t* lhist, float* ssc, int n, int k, uint32_t pos0,
+__device__ __forceinline__ void bucket_epilogue(uint32_t* lhist, uint32_t* sk, int n, int k, uint32_t pos0,
                                                 uint16_t* pdst, uint2* ldst, uint32_t* wsum, uint32_t* sh) {
   constexpr int PER = kSelBins / NT;
-  static_assert(PER == 8 && CH % NT == 0 && CH < 65536, "eight bins (one 16-byte partial store) per thread");
+  static_assert(PER == 8 && CH % (4 * NT) == 0 && CH < 65536, "eight bins (one 16-byte partial store) per thread");
   const int t = threadIdx.x;
   uint32_t h[PER];
   uint32_t sum = 0;
@@ -138,34 +138,42 @@ __device__ __forceinline__ void bucket_epilogue(uint32_t* lhist, float* ssc, int
   *reinterpret_cast<i32x4*>(pdst + (kSelBins - PER) - PER * t) = pk;
   __syncthreads();
   const uint32_t f = sh[0], nkeep = sh[1];
-  constexpr int R = CH / NT;
-  uint32_t key[R], slot[R];
+  // Thread t takes keys 4t .. 4t+3 of each 4*NT (16-byte LDS reads).
+  constexpr int R4 = CH / (4 * NT);
+  uint32_t key[4 * R4], slot[4 * R4];
 #pragma unroll
-  for (int j = 0; j < R; ++j) {
-    const int i = t + NT * j;
-    key[j] = score_key(ssc[i < n ? i : n - 1]);
+  for (int j = 0; j < R4; ++j) {
+    const i32x4 v = *reinterpret_cast<const i32x4*>(&sk[4 * (t + NT * j)]);
+    key[4 * j] = (uint32_t)v.x;
+    key[4 * j + 1] = (uint32_t)v.y;
+    key[4 * j + 2] = (uint32_t)v.z;
+    key[4 * j + 3] = (uint32_t)v.w;
   }
-  // Branch-free: a lane with nothing to write adds 0 to its own spare word.
+  auto idx = [&](int e) { return 4 * (t + NT * (e >> 2)) + (e & 3); };
+  auto keep = [&](int e) { return idx(e) < n && (key[e] >> kSelShift) >= f; };
+  // Every cursor update is issued before any result is used; a lane with
+  // nothing to place adds 0 to a spare word of its own (no branch).
   const int lane = t & 63;
 #pragma unroll
-  for (int j = 0; j < R; ++j) {
-    const uint32_t b = key[j] >> kSelShift;
-    const bool keep = t + NT * j < n && b >= f;
-    const uint32_t s = atomicAdd(&lhist[keep ? (int)b : kSelBins + lane], keep ? 1u : 0u);
-    slot[j] = keep ? s : 0xFFFFFFFFu;
+  for (int e = 0; e < 4 * R4; ++e) {
+    const bool kp = keep(e);
+    slot[e] = atomicAdd(&lhist[kp ? (int)(key[e] >> kSelShift) : kSelBins + lane], kp ? 1u : 0u);
   }
   typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
-  constexpr int kStage = CH / 2;  // pairs that fit where the scores were
+  constexpr int kStage = CH / 2;  // pairs that fit where the keys were
   if (nkeep <= (uint32_t)kStage) {
-    // Staged in LDS over the scores (all read above), then written out with
-    // 16-byte stores.
+    // Staged in LDS over the keys (all read above), then written out with
+    // 16-byte stores.  A lane with nothing to stage writes a spare pair.
     __syncthreads();
-    u32x2* stage = reinterpret_cast<u32x2*>(ssc);
+    u32x2* stage = reinterpret_cast<u32x2*>(sk);
+    u32x2* spare = reinterpret_cast<u32x2*>(lhist + kSelBins) + lane;
 #pragma unroll
-    for (int j = 0; j < R; ++j)
-      if (slot[j] != 0xFFFFFFFFu) stage[slot[j]] = u32x2{key[j], pos0 + (uint32_t)(t + NT * j)};
+    for (int e = 0; e < 4 * R4; ++e) {
+      const bool kp = keep(e);
+      *(kp ? stage + slot[e] : spare) = u32x2{key[e], pos0 + (uint32_t)idx(e)};
+    }
     __syncthreads();
-    const i32x4* src = reinterpret_cast<const i32x4*>(ssc);
+    const i32x4* src = reinterpret_cast<const i32x4*>(sk);
     i32x4* dst = reinterpret_cast<i32x4*>(ldst);
     for (uint32_t i = (uint32_t)t; 2 * i < nkeep; i += NT) {
       if (2 * i + 1 < nkeep) {
@@ -178,9 +186,9 @@ __device__ __forceinline__ void bucket_epilogue(uint32_t* lhist, float* ssc, int
   } else {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(ldst, (short)0, 8 * n, kBufferWord3);
 #pragma unroll
-    for (int j = 0; j < R; ++j)
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2{key[j], pos0 + (uint32_t)(t + NT * j)}, rs,
-                                            slot[j] != 0xFFFFFFFFu ? 8u * slot[j] : kBufferDrop, 0, 0);
+    for (int e = 0; e < 4 * R4; ++e)
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{key[e], pos0 + (uint32_t)idx(e)}, rs,
+                                            keep(e) ? 8u * slot[e] : kBufferDrop, 0, 0);
   }
 }
 
