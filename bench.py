@@ -197,6 +197,27 @@ def host_cpu():
     return None
 
 
+MFMA_PROBE_FLOP = {0: 16384.0, 1: 32768.0, 2: 65536.0}  # per product: f16 16x16x32, bf16 32x32x16, fp8 16x16x128
+
+
+def mfma_ceiling(torch, li, form, iters, reps=3):
+    """The matrix-core rate and shader clock of li_mfma_probe's product form
+    on constant (1.0) and on random operands, timed like the scans."""
+    sink = torch.empty(li.LI_MFMA_PROBE_SINK_WORDS, dtype=torch.float32, device="cuda")
+    clk = torch.empty(li.LI_MFMA_PROBE_CLOCK_WORDS, dtype=torch.int32, device="cuda")
+    flop = li.LI_MFMA_PROBE_WAVES * iters * li.LI_MFMA_PROBE_PRODUCTS_PER_ITER * MFMA_PROBE_FLOP[form]
+    res = {}
+    for name, rnd in (("constant", False), ("random", True)):
+        for _ in range(2):
+            li.li_mfma_probe(form, rnd, iters, sink, clk)
+        (ms,) = traced(torch, li, lambda: li.li_mfma_probe(form, rnd, iters, sink, clk), 1, reps)
+        c = clk.cpu().numpy().view("uint32").astype("float64").reshape(-1, 2)
+        res[name] = {"tflops": flop / (ms * 1e-3) / 1e12, "avg_launch_ms": ms,
+                     "shader_clock_mhz": float(c[:, 0].sum() / max(c[:, 1].sum(), 1.0) * 100.0)}
+    del sink, clk
+    return res
+
+
 def components(torch, li, inputs, args):
     import numpy as np
     out = {}
@@ -216,6 +237,12 @@ def components(torch, li, inputs, args):
         "tflops": flop / (scan * 1e-3) / 1e12, "mfma_frac_fp8": flop / (scan * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
         "mfma_frac_fp8_incl_prep": flop / ((scan + prep) * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
         "topk_us_per_row": topk * 1e3 / x.T}
+    # the fp8 product's rate on this GPU (li_mfma_probe), constant and random operands
+    ceil = mfma_ceiling(torch, li, li.LI_MFMA_PROBE_FP8, 400)
+    ceil["kernel"] = "mfma_probe_kernel<fp8> (li_mfma_probe): v_mfma_f32_16x16x128_f8f6f4 chains, 8 waves per SIMD"
+    out["prefill_fp8_T4096_L65536"]["measured_mfma_ceiling"] = ceil
+    out["prefill_fp8_T4096_L65536"]["mfma_frac_of_measured_random"] = \
+        flop / (scan * 1e-3) / 1e12 / ceil["random"]["tflops"]
     del q, qs, w, kc, ks, idx, ws, x
     # ---- LatentIndex group: G = 4, B = 16, L = 131072, Dc = 256 (bf16) ----------
     x = inputs.cfg4()
@@ -232,6 +259,12 @@ def components(torch, li, inputs, args):
         "absorb_ms": absorb, "scan_ms": scan, "topk_ms": topk, "total_ms": wall,
         "scan_gbs": lat_bytes / (scan * 1e-3) / 1e9, "scan_hbm_frac": lat_bytes / (scan * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "scan_mfma_frac_fp16": flop / (scan * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+    # the fp16 product's rate on this GPU (li_mfma_probe), constant and random operands
+    ceil = mfma_ceiling(torch, li, li.LI_MFMA_PROBE_F16, 800)
+    ceil["kernel"] = "mfma_probe_kernel<f16> (li_mfma_probe): v_mfma_f32_16x16x32_f16 chains, 6 waves per SIMD"
+    out["latent_G4_B16_L131072"]["measured_mfma_ceiling"] = ceil
+    out["latent_G4_B16_L131072"]["scan_mfma_frac_of_measured_random"] = \
+        flop / (scan * 1e-3) / 1e12 / ceil["random"]["tflops"]
     # the same step with LI_LATENT_SPLIT_BF16 (two bf16 products per element)
     fn = lambda: li.li_latent_score_group(q, w, wd, lat, None, off, 131072, x.k, out_idx=idx, ws=ws,
                                           flags=li.LI_LATENT_SPLIT_BF16)

@@ -391,6 +391,37 @@ int32_t li_trace_count(void);
 #define LI_READ_PROBE_SINK_WORDS 8192
 li_status li_read_probe(const void* p, size_t bytes, uint32_t* sink, void* stream);
 
+/* Matrix-core rate probe (measurement aid, not part of the computation): one
+ * kernel of LI_MFMA_PROBE_WAVES waves (2048 workgroups of four, eight waves per
+ * SIMD) in which every wave runs `iters` iterations of
+ * LI_MFMA_PROBE_PRODUCTS_PER_ITER matrix products of one form, in two
+ * independent accumulator chains over eight A and eight B operand registers:
+ *   LI_MFMA_PROBE_F16   v_mfma_f32_16x16x32_f16       (16384 FLOP per product)
+ *   LI_MFMA_PROBE_BF16  v_mfma_f32_32x32x16_bf16      (32768 FLOP)
+ *   LI_MFMA_PROBE_FP8   v_mfma_f32_16x16x128_f8f6f4, E4M3 (65536 FLOP)
+ * random_operands = 0 fills every operand element with 1.0, so that each
+ * chain's accumulator grows by K (32, 16, 128) per product and sink word w
+ * (one float per wave, LI_MFMA_PROBE_SINK_WORDS, device) is
+ * 2 * 8 * K * iters exactly while that stays below 2^24; otherwise the
+ * operands are pseudo-random values of the form (random signs and mantissas,
+ * 16 octaves of exponents for fp16 / bf16, any finite E4M3 code).  clk
+ * (LI_MFMA_PROBE_CLOCK_WORDS uint32 words, device) receives, per workgroup,
+ * the shader clock cycles it ran (word 2i) and the 100 MHz real-time ticks it
+ * ran (word 2i + 1), from which the shader clock follows.  The kernel's
+ * duration (e.g. through li_trace_events) gives the product rate; the two
+ * operand kinds bracket it, since the GPU lowers its clock under the power
+ * drawn by products on varying data.  iters in [1, 2^20] and a known form,
+ * else LI_E_SHAPE; null sink or clk: LI_E_NULL. */
+#define LI_MFMA_PROBE_F16 0
+#define LI_MFMA_PROBE_BF16 1
+#define LI_MFMA_PROBE_FP8 2
+#define LI_MFMA_PROBE_WAVES 8192
+#define LI_MFMA_PROBE_PRODUCTS_PER_ITER 16
+#define LI_MFMA_PROBE_SINK_WORDS 8192
+#define LI_MFMA_PROBE_CLOCK_WORDS 4096
+li_status li_mfma_probe(int32_t form, int32_t random_operands, int32_t iters, float* sink, uint32_t* clk,
+                        void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* li_status_str(li_status s);
 /* Detail of the last error on this thread (e.g. the HIP error text); "" if none. */

@@ -24,11 +24,16 @@ LI_LATENT_SPLIT_BF16 = 1
 LI_MAX_K = 16384
 LI_NOALLOC_SCRATCH_BYTES = 64 << 20
 LI_READ_PROBE_SINK_WORDS = 8192
+LI_MFMA_PROBE_F16, LI_MFMA_PROBE_BF16, LI_MFMA_PROBE_FP8 = 0, 1, 2
+LI_MFMA_PROBE_WAVES = 8192
+LI_MFMA_PROBE_PRODUCTS_PER_ITER = 16
+LI_MFMA_PROBE_SINK_WORDS = 8192
+LI_MFMA_PROBE_CLOCK_WORDS = 4096
 
 # Every symbol include/li.h declares.
 SYMBOLS = ("li_index_decode", "li_index_decode_ws", "li_index_decode_noalloc", "li_index_prefill", "li_index_prefill_ws",
            "li_latent_score_group", "li_latent_score_group_ws", "li_hs_refine", "li_hs_refine_ws",
-           "li_latent_append", "li_latent_append_ws", "li_sparse_attention", "li_sparse_attention_ws", "li_key_row_bytes", "li_latent_row_bytes", "li_indexcache_plan", "li_topk", "li_topk_ws", "li_status_str", "li_last_error", "li_trace_events", "li_trace_count", "li_read_probe")
+           "li_latent_append", "li_latent_append_ws", "li_sparse_attention", "li_sparse_attention_ws", "li_key_row_bytes", "li_latent_row_bytes", "li_indexcache_plan", "li_topk", "li_topk_ws", "li_status_str", "li_last_error", "li_trace_events", "li_trace_count", "li_read_probe", "li_mfma_probe")
 
 _lib = None
 
@@ -87,6 +92,8 @@ def lib():
         L.li_trace_count.restype = i32
         L.li_read_probe.argtypes = [vp, sz, vp, vp]
         L.li_read_probe.restype = i32
+        L.li_mfma_probe.argtypes = [i32, i32, i32, vp, vp, vp]
+        L.li_mfma_probe.restype = i32
         _lib = L
     return _lib
 
@@ -276,6 +283,15 @@ def li_read_probe(buf, sink, stream=None):
     """Stream every byte of the CUDA tensor buf once (measurement aid);
     sink is a [LI_READ_PROBE_SINK_WORDS] int32 CUDA tensor."""
     _check(lib().li_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
+
+
+def li_mfma_probe(form, random_operands, iters, sink, clk, stream=None):
+    """Run the matrix-core rate probe (measurement aid): form LI_MFMA_PROBE_*,
+    constant (False) or random (True) operands; sink is a
+    [LI_MFMA_PROBE_SINK_WORDS] float32 and clk a [LI_MFMA_PROBE_CLOCK_WORDS]
+    int32 CUDA tensor."""
+    _check(lib().li_mfma_probe(int(form), 1 if random_operands else 0, int(iters), _ptr(sink), _ptr(clk),
+                               _stream(stream)))
 
 
 def li_trace_events(events, capacity):

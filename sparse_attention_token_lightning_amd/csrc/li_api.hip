@@ -291,6 +291,18 @@ li_status li_read_probe(const void* p, size_t bytes, uint32_t* sink, void* strea
                    (hipStream_t)stream);
 }
 
+li_status li_mfma_probe(int32_t form, int32_t random_operands, int32_t iters, float* sink, uint32_t* clk,
+                        void* stream) {
+  g_err.clear();
+  if (!sink || !clk) return fail(LI_E_NULL, "sink and clk are required");
+  if (form != LI_MFMA_PROBE_F16 && form != LI_MFMA_PROBE_BF16 && form != LI_MFMA_PROBE_FP8)
+    return fail(LI_E_SHAPE, "form must be LI_MFMA_PROBE_F16, LI_MFMA_PROBE_BF16 or LI_MFMA_PROBE_FP8");
+  if (iters < 1 || iters > (1 << 20)) return fail(LI_E_SHAPE, "iters must be in [1, 2^20]");
+  trace_begin();
+  return hip_check(li::launch_mfma_probe(form, random_operands != 0, iters, sink, clk, (hipStream_t)stream),
+                   "mfma_probe launch", (hipStream_t)stream);
+}
+
 
 size_t li_index_decode_ws(int32_t B, int64_t n_tok, int32_t max_len, int32_t k,
                           int32_t has_out_scores) {

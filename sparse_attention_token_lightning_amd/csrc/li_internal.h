@@ -150,6 +150,12 @@ hipError_t launch_latent_append(const uint16_t* h, const uint16_t* w_enc, const 
 // p (16-byte aligned) and writes one fold per wave into sink
 // (LI_READ_PROBE_SINK_WORDS words).
 hipError_t launch_read_probe(const void* p, int64_t bytes, uint32_t* sink, hipStream_t stream);
+// Matrix-core rate probe (measurement aid): form LI_MFMA_PROBE_*, operands
+// constant or random, iters iterations of LI_MFMA_PROBE_PRODUCTS_PER_ITER
+// products per wave; sink LI_MFMA_PROBE_SINK_WORDS floats, clk
+// LI_MFMA_PROBE_CLOCK_WORDS words.
+hipError_t launch_mfma_probe(int form, bool random_operands, int iters, float* sink, uint32_t* clk,
+                             hipStream_t stream);
 
 // Opt-in input checks (LI_DEBUG_VALIDATE): validate_begin clears the device
 // record, the validate_* calls enqueue one check each, validate_end waits for

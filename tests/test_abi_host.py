@@ -142,6 +142,16 @@ def test_read_probe_host_checks():
     assert L.li_read_probe(FAKE + 8, 1024, FAKE, None) == li.LI_E_SHAPE
 
 
+def test_mfma_probe_host_checks():
+    L = li.lib()
+    assert L.li_mfma_probe(li.LI_MFMA_PROBE_F16, 0, 16, None, FAKE, None) == li.LI_E_NULL
+    assert L.li_mfma_probe(li.LI_MFMA_PROBE_F16, 0, 16, FAKE, None, None) == li.LI_E_NULL
+    assert L.li_mfma_probe(3, 0, 16, FAKE, FAKE, None) == li.LI_E_SHAPE
+    assert L.li_mfma_probe(-1, 1, 16, FAKE, FAKE, None) == li.LI_E_SHAPE
+    assert L.li_mfma_probe(li.LI_MFMA_PROBE_FP8, 1, 0, FAKE, FAKE, None) == li.LI_E_SHAPE
+    assert L.li_mfma_probe(li.LI_MFMA_PROBE_BF16, 0, (1 << 20) + 1, FAKE, FAKE, None) == li.LI_E_SHAPE
+
+
 def test_prefill_validation():
     L = li.lib()
 
