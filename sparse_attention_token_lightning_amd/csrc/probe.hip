@@ -73,16 +73,16 @@ __device__ __forceinline__ uint32_t probe_hash(uint32_t x) {
 // One operand word (two 16-bit values or four fp8 bytes) of form F: 1.0 in
 // every element, or random signs and mantissas with exponents spanning 16
 // octaves around 1 (fp16 / bf16) or any finite E4M3 code.
-template <int F>
-__device__ __forceinline__ int probe_word(bool rnd, uint32_t seed) {
+template <int F, bool RND>
+__device__ __forceinline__ int probe_word(uint32_t seed) {
   if (F == LI_MFMA_PROBE_FP8) {
-    if (!rnd) return 0x38383838;
+    if (!RND) return 0x38383838;
     uint32_t w = probe_hash(seed);
     // bytes whose low seven bits are all ones (NaN) become 0x77 / 0xF7
     const uint32_t nan = ((w & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
     return (int)(w ^ (nan >> 4));
   }
-  if (!rnd) return F == LI_MFMA_PROBE_F16 ? 0x3C003C00 : 0x3F803F80;
+  if (!RND) return F == LI_MFMA_PROBE_F16 ? 0x3C003C00 : 0x3F803F80;
   uint32_t h[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -95,8 +95,9 @@ __device__ __forceinline__ int probe_word(bool rnd, uint32_t seed) {
   return (int)(h[0] | (h[1] << 16));
 }
 
-template <int F>
-__global__ __launch_bounds__(kProbeThreads) void mfma_probe_kernel(int rnd, int iters, float* __restrict__ sink,
+// F: product form; RND: random (true) or constant operands.
+template <int F, bool RND>
+__global__ __launch_bounds__(kProbeThreads) void mfma_probe_kernel(int iters, float* __restrict__ sink,
                                                                    uint32_t* __restrict__ clk) {
   const uint64_t c0 = __builtin_amdgcn_s_memtime();
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
@@ -107,8 +108,8 @@ __global__ __launch_bounds__(kProbeThreads) void mfma_probe_kernel(int rnd, int 
   for (int r = 0; r < 8; ++r)
 #pragma unroll
     for (int j = 0; j < W; ++j) {
-      a[r][j] = probe_word<F>(rnd != 0, seed + r * W + j);
-      b[r][j] = probe_word<F>(rnd != 0, seed + 128u + r * W + j);
+      a[r][j] = probe_word<F, RND>(seed + r * W + j);
+      b[r][j] = probe_word<F, RND>(seed + 128u + r * W + j);
     }
   float out;
   if constexpr (F == LI_MFMA_PROBE_BF16) {
@@ -163,17 +164,26 @@ __global__ __launch_bounds__(kProbeThreads) void mfma_probe_kernel(int rnd, int 
 
 }  // namespace
 
+namespace {
+
+template <int F>
+hipError_t launch_mfma_probe_form(bool random_operands, int iters, float* sink, uint32_t* clk, hipStream_t stream) {
+  if (random_operands)
+    return launch_kernel(mfma_probe_kernel<F, true>, dim3(kMfmaBlocks), dim3(kProbeThreads), 0u, stream, iters, sink,
+                         clk);
+  return launch_kernel(mfma_probe_kernel<F, false>, dim3(kMfmaBlocks), dim3(kProbeThreads), 0u, stream, iters, sink,
+                       clk);
+}
+
+}  // namespace
+
 hipError_t launch_mfma_probe(int form, bool random_operands, int iters, float* sink, uint32_t* clk,
                              hipStream_t stream) {
-  const int rnd = random_operands ? 1 : 0;
   if (form == LI_MFMA_PROBE_F16)
-    return launch_kernel(mfma_probe_kernel<LI_MFMA_PROBE_F16>, dim3(kMfmaBlocks), dim3(kProbeThreads), 0u, stream,
-                         rnd, iters, sink, clk);
+    return launch_mfma_probe_form<LI_MFMA_PROBE_F16>(random_operands, iters, sink, clk, stream);
   if (form == LI_MFMA_PROBE_BF16)
-    return launch_kernel(mfma_probe_kernel<LI_MFMA_PROBE_BF16>, dim3(kMfmaBlocks), dim3(kProbeThreads), 0u, stream,
-                         rnd, iters, sink, clk);
-  return launch_kernel(mfma_probe_kernel<LI_MFMA_PROBE_FP8>, dim3(kMfmaBlocks), dim3(kProbeThreads), 0u, stream,
-                       rnd, iters, sink, clk);
+    return launch_mfma_probe_form<LI_MFMA_PROBE_BF16>(random_operands, iters, sink, clk, stream);
+  return launch_mfma_probe_form<LI_MFMA_PROBE_FP8>(random_operands, iters, sink, clk, stream);
 }
 
 hipError_t launch_read_probe(const void* p, int64_t bytes, uint32_t* sink, hipStream_t stream) {
