@@ -383,10 +383,11 @@ int32_t li_trace_count(void);
 
 /* Read-bandwidth probe (measurement aid, not part of the computation): one
  * kernel streams `bytes` bytes of `p` with the decode scan's load pattern
- * (16-byte loads, 1 KB per wave per load, eight loads in flight per lane) and
- * folds the data into one word per wave of `sink` (LI_READ_PROBE_SINK_WORDS
- * uint32 words, device), so that its duration (e.g. through li_trace_events)
- * gives the read rate this GPU reaches for such a stream.  p must be 16-byte
+ * (16-byte non-temporal loads, 1 KB per wave per load, eight loads in flight
+ * per lane) and folds the data into one word per wave of `sink`
+ * (LI_READ_PROBE_SINK_WORDS uint32 words, device), so that its duration
+ * (e.g. through li_trace_events) gives the read rate this GPU reaches for such
+ * a stream.  p must be 16-byte
  * aligned and bytes a multiple of 16 (else LI_E_SHAPE). */
 #define LI_READ_PROBE_SINK_WORDS 8192
 li_status li_read_probe(const void* p, size_t bytes, uint32_t* sink, void* stream);

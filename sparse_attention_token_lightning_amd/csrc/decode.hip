@@ -13,8 +13,12 @@
 // Mapping: the 64 query heads are the MFMA's M (two 32-row blocks held in
 // registers for the whole kernel), 32 consecutive keys are its N, and the 128
 // dims are its K.  Lane l works on key (l & 31) and dims 64*(l >> 5) .. +63 of
-// it, so each lane streams one contiguous 64-byte (fp8) or 128-byte (bf16)
-// half row with 16-byte loads and converts fp8 -> bf16 exactly in registers.
+// it and converts fp8 -> bf16 exactly in registers.  bf16 keys: each lane
+// streams its 128-byte half row with 16-byte loads.  fp8 keys: every 16-byte
+// load instruction of a wave covers 8 whole key rows (1 KB contiguous), read
+// with the non-temporal hint (a stream of whole lines runs about 14% faster
+// with it; a line split over several instructions runs far slower), and the
+// wave turns the 4 KB tile into the per-key layout through its own LDS slice.
 // The contraction index is summed, so A and B use the same dims-to-lane
 // assignment and any such assignment is valid.  The MFMA result leaves each
 // lane 16 heads of its key per block: ReLU, the head weight and the sum over
@@ -62,6 +66,9 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
   __shared__ __attribute__((aligned(16))) uint32_t ssc[kDecMaxChunk];
   __shared__ uint32_t wsum[kDecWaves];
   __shared__ uint32_t sh_floor[2];
+  // fp8: each wave's key tile (32 rows x 128 B) on its way from the
+  // row-contiguous load layout to the MFMA operand layout.
+  __shared__ __attribute__((aligned(16))) uint8_t ktl[FP8 ? kDecWaves : 1][FP8 ? kTile * 128 : 16];
 
   const int b = blockIdx.y;
   const int64_t off = kv_off[b];
@@ -108,25 +115,61 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
     const int64_t t = (L - w0 + (int64_t)kDecWaves * kTile - 1) / ((int64_t)kDecWaves * kTile);
     nt = (int)(t < tiles_per_wave ? t : tiles_per_wave);
   }
-  const uint8_t* kbase = kc + off * kRowBytes + (FP8 ? 64 : 128) * g;
+  const uint8_t* kbase = kc + off * kRowBytes + (FP8 ? 0 : 128 * g);
   auto tok = [&](int it) { return w0 + (int64_t)it * kDecWaves * kTile + col; };
+  // fp8: load v of lane l is 16 bytes (chunk l & 7) of the tile's row
+  // 8v + (l >> 3), so every load instruction reads 8 whole rows (1 KB), which
+  // lets it stream with the non-temporal hint; bf16: lane (col, g) reads its
+  // own half row.  Rows past L repeat row L-1 (their scores are dropped).
   auto load_tile = [&](i32x4 (&raw)[NV], float& sc, int it) {
-    int64_t s = tok(it);
-    s = s < L ? s : L - 1;
-    const uint8_t* p = kbase + s * kRowBytes;
+    const int64_t t0 = w0 + (int64_t)it * kDecWaves * kTile;
+    if constexpr (FP8) {
 #pragma unroll
-    for (int v = 0; v < NV; ++v) raw[v] = ld16(p + 16 * v);
+      for (int v = 0; v < NV; ++v) {
+        int64_t r = t0 + 8 * v + (lane >> 3);
+        r = r < L ? r : L - 1;
+        raw[v] = ld16_stream(kbase + r * kRowBytes + 16 * (lane & 7));
+      }
+    } else {
+      int64_t r = t0 + col;
+      r = r < L ? r : L - 1;
+      const uint8_t* p = kbase + r * kRowBytes;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) raw[v] = ld16(p + 16 * v);
+    }
+    int64_t s = t0 + col;
+    s = s < L ? s : L - 1;
     sc = k_scale ? k_scale[off + s] : 1.0f;
+  };
+  // The fp8 tile through this wave's LDS slice: 16-byte chunk c of row r
+  // sits at chunk c ^ swz(r) of the row, so that both the row-wise writes
+  // (8 lanes per row) and the key-wise reads (one row per lane) spread over
+  // all banks, for 32 and for 64 banks of 4 bytes.  The wave's LDS
+  // operations run in order, so the next tile's writes cannot overtake these
+  // reads and no barrier is needed.
+  auto swz = [](int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); };
+  auto transpose = [&](const i32x4 (&raw)[NV], i32x4 (&kr)[NV]) {
+    uint8_t* tl = ktl[FP8 ? wave : 0];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int r = 8 * v + (lane >> 3);
+      *reinterpret_cast<i32x4*>(tl + r * 128 + (((lane & 7) ^ swz(r)) << 4)) = raw[v];
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      kr[j] = *reinterpret_cast<const i32x4*>(tl + col * 128 + ((((g << 2) + j) ^ swz(col)) << 4));
   };
   // `it` is already clamped to a valid tile; `live` is false for the repeated
   // last tile that pads the pipeline, whose (identical) scores are not counted.
   auto compute = [&](const i32x4 (&raw)[NV], float sc, int it, bool live) {
+    i32x4 kr[FP8 ? NV : 1];
+    if constexpr (FP8) transpose(raw, kr);
     f32x16 a0 = {}, a1 = {};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       bf16x8 kb;
       if constexpr (FP8) {
-        const i32x4 v = raw[j >> 1];
+        const i32x4 v = kr[j >> 1];
         kb = (j & 1) ? fp8x8_to_bf16x8(v.z, v.w) : fp8x8_to_bf16x8(v.x, v.y);
       } else {
         kb = __builtin_bit_cast(bf16x8, raw[j]);

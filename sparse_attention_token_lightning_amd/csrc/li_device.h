@@ -29,6 +29,18 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 // 16-byte global load / store through a plain vector type.
 __device__ __forceinline__ i32x4 ld16(const void* p) { return *reinterpret_cast<const i32x4*>(p); }
 
+// Loads of data a call streams once (key cache, latent cache and their
+// scales): non-temporal, so the lines are not kept for reuse in the caches.
+// A plain 553 MB read stream with the decode scan's pattern runs at about
+// 6.1 TB/s with ordinary loads and 7.0 TB/s with these.
+__device__ __forceinline__ i32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p));
+}
+__device__ __forceinline__ i32x2 ld8_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const i32x2*>(p));
+}
+__device__ __forceinline__ float ldf_stream(const float* p) { return __builtin_nontemporal_load(p); }
+
 // Four OCP E4M3FN bytes (one dword, byte 0 first) -> four bf16, exact: every
 // E4M3FN value, subnormals included, is a bf16 normal number.  Uses gfx950's
 // packed fp8 -> bf16 conversion with a unit scale.

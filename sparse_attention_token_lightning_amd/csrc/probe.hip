@@ -2,9 +2,9 @@
 //
 // Read-bandwidth probe:
 // Streams a buffer once with the access pattern of the decode scan's key
-// loads (16-byte loads, each wave covering 1 KB contiguous per load, eight
-// loads in flight per lane, a grid of 2048 four-wave workgroups striding over
-// the buffer) and does nothing with the data but fold it into one word per
+// loads (16-byte non-temporal loads, each wave covering 1 KB contiguous per
+// load, eight loads in flight per lane, a grid of 2048 four-wave workgroups
+// striding over the buffer) and does nothing with the data but fold it into one word per
 // wave, so the loads cannot be dropped.  Its duration gives the read rate
 // this GPU reaches for such a stream, the practical ceiling that the
 // HBM-bound kernels are compared against next to the published peak.
@@ -40,14 +40,14 @@ __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const i32x4* 
   for (; i + (kProbeUnroll - 1) * kProbeThreads < n16; i += stride) {
     i32x4 v[kProbeUnroll];
 #pragma unroll
-    for (int u = 0; u < kProbeUnroll; ++u) v[u] = p[i + u * kProbeThreads];
+    for (int u = 0; u < kProbeUnroll; ++u) v[u] = ld16_stream(p + i + u * kProbeThreads);
 #pragma unroll
     for (int u = 0; u < kProbeUnroll; ++u) acc ^= (uint32_t)(v[u].x ^ v[u].y ^ v[u].z ^ v[u].w);
   }
   for (int u = 0; u < kProbeUnroll; ++u) {
     const int64_t j = i + u * kProbeThreads;
     if (j < n16) {
-      const i32x4 v = p[j];
+      const i32x4 v = ld16_stream(p + j);
       acc ^= (uint32_t)(v.x ^ v.y ^ v.z ^ v.w);
     }
   }
