@@ -944,24 +944,38 @@ __device__ void bucket_finish(const Row& row, KeyAt key_at, PosAt pos_at, uint32
   // [v*WPW, (v+1)*WPW) in rounds of 64 consecutive words (one per lane, no
   // bank conflicts), scans each round within the wave and keeps a running
   // total; the waves' totals then give each wave its offset.
+  // All of a wave's bitmap reads are issued before its first scan, and the
+  // wave's offset is added in registers, so each word's prefix is written once.
   constexpr int NWV = NT / 64;
+  constexpr int WR = (kBucketMaxLen / 32 + NT - 1) / NT;  // rounds of 64 words per wave at most
   const int nwr = (int)((n + 31) / 32);
-  const int WPW = ((nwr + NWV - 1) / NWV + 63) / 64 * 64;
+  const int WPW = ((nwr + NWV - 1) / NWV + 63) / 64 * 64;  // <= 64 * WR
   const int wv = tid >> 6, ln = tid & 63;
+  uint32_t cw[WR], iw[WR];
+#pragma unroll
+  for (int i = 0; i < WR; ++i) {
+    const int w = wv * WPW + 64 * i + ln;
+    const bool in = 64 * i < WPW && w < nwr;
+    const int wc = in ? w : 0;
+    const uint32_t gb = gbits[wc], eb = ebits[wc];
+    cw[i] = in ? ((uint32_t)__builtin_popcount(gb) << 18) + (uint32_t)__builtin_popcount(eb) : 0u;
+  }
   uint32_t run = 0;
-  for (int w = wv * WPW + ln; w < (wv + 1) * WPW; w += 64) {
-    const uint32_t c = w < nwr ? ((uint32_t)__builtin_popcount(gbits[w]) << 18) +
-                                     (uint32_t)__builtin_popcount(ebits[w])
-                               : 0u;
-    const uint32_t inc = wave_incl_scan(c);
-    if (w < nwr) wpre[w] = run + inc - c;
+#pragma unroll
+  for (int i = 0; i < WR; ++i) {
+    const uint32_t inc = wave_incl_scan(cw[i]);
+    iw[i] = run + inc - cw[i];
     run += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
   }
   if (ln == 0) wsum[wv] = run;
   __syncthreads();
   uint32_t woff = 0;
   for (int v = 0; v < NWV; ++v) woff += v < wv ? wsum[v] : 0u;
-  for (int w = wv * WPW + ln; w < (wv + 1) * WPW && w < nwr; w += 64) wpre[w] += woff;
+#pragma unroll
+  for (int i = 0; i < WR; ++i) {
+    const int w = wv * WPW + 64 * i + ln;
+    if (64 * i < WPW && w < nwr) wpre[w] = woff + iw[i];
+  }
   __syncthreads();
   // Every kept position's slot: #greater-before + min(#equal-before, m), or for
   // an equal key #greater-before + #equal-before when that is below m.
