@@ -497,6 +497,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkRows a, SelWs
                            1, kk, hist, wsum, shb);
 }
 
+constexpr int kListCap = 5632;  // list top-k candidate pairs in LDS at most
+
 // Causal rows given as candidate lists (the prefill scan's output): row r's
 // visible positions are 0 .. min(L, qpos0 + r) and its list, list + r * L,
 // holds lcnt[r] (key, position) pairs in position order: every visible key
@@ -509,7 +511,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_list_kernel(TopkRows a, SelW
                                                                 const uint32_t* lcnt, int cap) {
   extern __shared__ uint2 cand[];
   __shared__ uint32_t hist[kSelBins];
-  constexpr int kRounds = 16;  // collection rounds per chunk
+  constexpr int kRounds = 8;  // collection rounds per chunk (16 entries in registers per thread)
   constexpr int kW = kRowThreads / 64;
   __shared__ uint32_t rcnt[kRounds * kW];
   __shared__ uint32_t wsum[kW];
@@ -1240,7 +1242,9 @@ hipError_t launch_topk_list(const TopkRows& a, const SelWs& ws, const uint2* lis
   if (a.rows <= 0) return hipSuccess;
   static bool lds_set = false;
   if (hipError_t e = allow_lds(topk_list_kernel, lds_set)) return e;
-  const int cap = seg_cap_for(a.k);
+  // Three workgroups per CU (68 VGPRs, 8.3 KB of static LDS): the candidate
+  // room is capped at 5632 pairs (44 KB); rows with more take the global path.
+  const int cap = seg_cap_for(a.k) < kListCap ? seg_cap_for(a.k) : kListCap;
   return launch_kernel(topk_list_kernel, dim3((unsigned)a.rows), dim3(kRowThreads), (uint32_t)(cap * sizeof(uint2)),
                        stream, a, ws, list, lcnt, cap);
 }
