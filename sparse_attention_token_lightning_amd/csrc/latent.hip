@@ -232,17 +232,22 @@ __global__ __launch_bounds__(kLsThreads, 2) void latent_score_kernel(
   int64_t n;
   const int32_t* cb = nullptr;
   if constexpr (GATHER) {
+    // Valid candidates come first, then -1 padding.  This workgroup only
+    // reads its own range tok0 .. tok0 + 32 * tiles_per_block - 1, so the
+    // valid ones there, counted from one round of loads, give n for it
+    // (tok0 + that count; every use of n below is inside the range).
     cb = cand + (int64_t)b * C;
-    if (tid == 0) {
-      int lo = 0, hi = C;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (cb[mid] < 0) hi = mid; else lo = mid + 1;
-      }
-      sh_n = lo;
-    }
+    const int64_t t0 = (int64_t)blockIdx.x * tiles_per_block * 32;
+    if (tid == 0) sh_n = 0;
     __syncthreads();
-    n = sh_n;
+    uint32_t cv = 0;
+    for (int i = tid; i < tiles_per_block * 32; i += kLsThreads)
+      cv += (t0 + i < C && cb[t0 + i] >= 0) ? 1u : 0u;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) cv += (uint32_t)__shfl_xor((int)cv, o);
+    if ((tid & 63) == 0) atomicAdd(&sh_n, (int32_t)cv);
+    __syncthreads();
+    n = t0 + sh_n;
   } else {
     n = kv_off[b + 1] - off;
   }
@@ -528,17 +533,22 @@ __global__ __launch_bounds__(kSpThreads) void latent_split_kernel(
   int64_t n;
   const int32_t* cb = nullptr;
   if constexpr (GATHER) {
+    // Valid candidates come first, then -1 padding.  This workgroup only
+    // reads its own range tok0 .. tok0 + 32 * tiles_per_block - 1, so the
+    // valid ones there, counted from one round of loads, give n for it
+    // (tok0 + that count; every use of n below is inside the range).
     cb = cand + (int64_t)b * C;
-    if (tid == 0) {
-      int lo = 0, hi = C;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (cb[mid] < 0) hi = mid; else lo = mid + 1;
-      }
-      sh_n = lo;
-    }
+    const int64_t t0 = (int64_t)blockIdx.x * tiles_per_block * 32;
+    if (tid == 0) sh_n = 0;
     __syncthreads();
-    n = sh_n;
+    uint32_t cv = 0;
+    for (int i = tid; i < tiles_per_block * 32; i += kSpThreads)
+      cv += (t0 + i < C && cb[t0 + i] >= 0) ? 1u : 0u;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) cv += (uint32_t)__shfl_xor((int)cv, o);
+    if ((tid & 63) == 0) atomicAdd(&sh_n, (int32_t)cv);
+    __syncthreads();
+    n = t0 + sh_n;
   } else {
     n = kv_off[b + 1] - off;
   }

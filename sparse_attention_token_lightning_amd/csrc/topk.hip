@@ -342,7 +342,10 @@ enum SelHow : int32_t { kSelSelf = 1, kSelFull = 2 };
 // One workgroup per row.  kSelSelf: the row's level-0 threshold is in ws.thr
 // (prefill scan), unless the scan flagged it invalid (thr[3] == 0).
 // kSelFull: the workgroup builds the histogram itself.
-// Dynamic LDS holds `cap` candidate pairs.
+// Dynamic LDS holds `cap` candidate pairs.  CANDS: candidate rows (the HS
+// followers), whose short rows take the early loads below (a separate
+// instantiation, so that the other rows keep the smaller register budget).
+template <bool CANDS>
 __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkRows a, SelWs ws, int how, int cap) {
   extern __shared__ uint2 cand[];
   __shared__ uint32_t hist[kSelBins];
@@ -354,7 +357,42 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkRows a, SelWs
   __shared__ uint32_t shb[4];
   const int tid = threadIdx.x;
   const int r = blockIdx.x;
-  const Row row = get_row(a, r, sh);
+  // Candidate rows of at most kRegCand * kRowThreads scores (the HS
+  // followers): the scores and the row's candidate positions are loaded
+  // before its valid length is known (clamped to its C entries, which the
+  // buffers hold), so the loads overlap the length search.
+  const bool early = CANDS && a.C <= kRegCand * kRowThreads;
+  uint2 v[kRegCand];
+  int32_t mp[kRegCand];
+  if (early) {
+    const float* sp = a.scores + (int64_t)r * a.C;
+    const int32_t* cp = a.cand + (int64_t)(r / a.G) * a.C;
+#pragma unroll
+    for (int j = 0; j < kRegCand; ++j) {
+      const int i = j * kRowThreads + tid;
+      const int ic = i < a.C ? i : a.C - 1;
+      v[j] = make_uint2(score_key(sp[ic]), (uint32_t)i);
+      mp[j] = cp[ic];
+    }
+  }
+  Row row;
+  if (early) {
+    // Valid candidates come first, then -1 padding: the row's length is the
+    // number of non-negative entries, counted from the loaded positions.
+    if (tid == 0) sh[0] = 0;
+    __syncthreads();
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < kRegCand; ++j) c += (uint32_t)__popcll(__ballot(j * kRowThreads + tid < a.C && mp[j] >= 0));
+    if ((tid & 63) == 0) atomicAdd(&sh[0], (int32_t)c);
+    __syncthreads();
+    row.p = a.scores + (int64_t)r * a.C;
+    row.n = sh[0];
+    row.map = a.cand + (int64_t)(r / a.G) * a.C;
+    row.out = a.out + (int64_t)r * a.k;
+  } else {
+    row = get_row(a, r, sh);
+  }
   const int64_t n = row.n;
   const int k = a.k;
   const int64_t kk = n < k ? n : (int64_t)k;
@@ -373,11 +411,23 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkRows a, SelWs
   // the whole row (keys below the threshold bin are never kept), instead of
   // a second pass over the row into LDS.
   if (n <= (int64_t)kRegCand * kRowThreads) {
-    uint2 v[kRegCand];
+    if (early) {
+      // The candidate positions move to the (here unused) dynamic LDS when it
+      // holds them (cap pairs >= kRegCand * kRowThreads words), where the final
+      // position lookups read them; the barriers of the selection order these
+      // writes before those reads.
+      if (2 * cap >= kRegCand * kRowThreads) {
+        int32_t* lmap = reinterpret_cast<int32_t*>(cand);
 #pragma unroll
-    for (int j = 0; j < kRegCand; ++j) {
-      const int64_t i = (int64_t)j * kRowThreads + tid;
-      v[j] = make_uint2(key_clamped(row.p, i, n), (uint32_t)i);
+        for (int j = 0; j < kRegCand; ++j) lmap[j * kRowThreads + tid] = mp[j];
+        row.map = lmap;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kRegCand; ++j) {
+        const int64_t i = (int64_t)j * kRowThreads + tid;
+        v[j] = make_uint2(key_clamped(row.p, i, n), (uint32_t)i);
+      }
     }
     uint32_t bs, ab;
     const bool own = how == kSelFull || ws.thr[(int64_t)r * 4 + 3] == 0u;
@@ -1226,11 +1276,17 @@ hipError_t launch_topk_segmented(const TopkRows& a, const SelWs& ws, hipStream_t
 
 static hipError_t launch_row(const TopkRows& a, const SelWs& ws, int how, hipStream_t stream) {
   if (a.rows <= 0) return hipSuccess;
-  static bool lds_set = false;
-  if (hipError_t e = allow_lds(topk_row_kernel, lds_set)) return e;
   const int cap = seg_cap_for(a.k);
-  return launch_kernel(topk_row_kernel, dim3((unsigned)a.rows), dim3(kRowThreads), (uint32_t)(cap * sizeof(uint2)),
-                       stream, a, ws, how, cap);
+  if (a.mode == kRowsCands) {
+    static bool lds_set = false;
+    if (hipError_t e = allow_lds(topk_row_kernel<true>, lds_set)) return e;
+    return launch_kernel(topk_row_kernel<true>, dim3((unsigned)a.rows), dim3(kRowThreads),
+                         (uint32_t)(cap * sizeof(uint2)), stream, a, ws, how, cap);
+  }
+  static bool lds_set = false;
+  if (hipError_t e = allow_lds(topk_row_kernel<false>, lds_set)) return e;
+  return launch_kernel(topk_row_kernel<false>, dim3((unsigned)a.rows), dim3(kRowThreads),
+                       (uint32_t)(cap * sizeof(uint2)), stream, a, ws, how, cap);
 }
 
 hipError_t launch_topk_self(const TopkRows& a, const SelWs& ws, hipStream_t stream) {
