@@ -97,6 +97,9 @@ int main() {
   EXPECT(li_topk(Ff, 5, nullptr, 1, 10, 1, Fi, F, big, nullptr), LI_E_SHAPE);
   EXPECT(li_topk(Ff, 10, nullptr, 0, 10, 3, Fi, F, big, nullptr), LI_OK);
   EXPECT(li_read_probe(F, 1000, static_cast<uint32_t*>(F), nullptr), LI_E_SHAPE);
+  EXPECT(li_mfma_probe(LI_MFMA_PROBE_F16, 0, 16, nullptr, static_cast<uint32_t*>(F), nullptr), LI_E_NULL);
+  EXPECT(li_mfma_probe(3, 1, 16, static_cast<float*>(F), static_cast<uint32_t*>(F), nullptr), LI_E_SHAPE);
+  EXPECT(li_mfma_probe(LI_MFMA_PROBE_FP8, 1, 0, static_cast<float*>(F), static_cast<uint32_t*>(F), nullptr), LI_E_SHAPE);
 
   // IndexCache planner (host only)
   int32_t src[61];
