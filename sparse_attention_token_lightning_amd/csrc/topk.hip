@@ -359,8 +359,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkRows a, SelWs
   const int r = blockIdx.x;
   // Candidate rows of at most kRegCand * kRowThreads scores (the HS
   // followers): the scores and the row's candidate positions are loaded
-  // before its valid length is known (clamped to its C entries, which the
-  // buffers hold), so the loads overlap the length search.
+  // first (clamped to its C entries, which the buffers hold), and the row's
+  // valid length is counted from those positions instead of searched for.
   const bool early = CANDS && a.C <= kRegCand * kRowThreads;
   uint2 v[kRegCand];
   int32_t mp[kRegCand];
