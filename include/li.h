@@ -99,7 +99,8 @@ typedef int32_t li_dtype;
  *   k_cache  [n_tok][D]  LI_BF16 or LI_FP8_E4M3 (one key per token, shared by all heads)
  *   k_scale  [n_tok]     fp32 per-token dequantisation scale, or NULL (= 1)
  *   kv_off   [B+1]       int64, device
- *   n_tok    rows in k_cache (>= kv_off[B]); max_len >= every L_b (grid sizing)
+ *   n_tok    rows in k_cache (>= kv_off[B]); max_len >= every L_b (grid sizing);
+ *            with LI_FP8_E4M3 keys max_len <= 33550336 (else LI_E_UNSUPPORTED)
  *   H        1..64 heads; D must be 128; 1 <= k <= LI_MAX_K
  *   out_idx  [B][k]      int32 positions in [0, L_b), ascending, -1 padded
  *   out_scores [n_tok]   fp32 score of every cache row, or NULL

@@ -116,30 +116,40 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
     nt = (int)(t < tiles_per_wave ? t : tiles_per_wave);
   }
   const uint8_t* kbase = kc + off * kRowBytes + (FP8 ? 0 : 128 * g);
-  auto tok = [&](int it) { return w0 + (int64_t)it * kDecWaves * kTile + col; };
+  // Positions relative to the request fit in 32 bits (max_len is an int32).
+  const int w0i = (int)w0, wg0i = (int)wg0;
+  const int Li = L < 0x7fffffff ? (int)L : 0x7fffffff;
+  auto tok = [&](int it) { return w0i + it * kDecWaves * kTile + col; };
   // fp8: load v of lane l is 16 bytes (chunk l & 7) of the tile's row
   // 8v + (l >> 3), so every load instruction reads 8 whole rows (1 KB), which
   // lets it stream with the non-temporal hint; bf16: lane (col, g) reads its
-  // own half row.  Rows past L repeat row L-1 (their scores are dropped).
+  // own half row.  Rows past L repeat row L-1 (bf16) or read as zeros (fp8);
+  // their scores are dropped.
   auto load_tile = [&](i32x4 (&raw)[NV], float& sc, int it) {
-    const int64_t t0 = w0 + (int64_t)it * kDecWaves * kTile;
     if constexpr (FP8) {
+      // The tile's keys as a buffer resource (wave-uniform, built on the
+      // scalar unit) that ends at the request's end: rows past it read as
+      // zeros without touching memory (their scores are dropped).  Row
+      // 8v + (lane >> 3) of the tile, chunk lane & 7, is byte 1024 v + 16 lane,
+      // so the lane offsets are constants.  (The scale stays a clamped global
+      // load: as a buffer load this compiler drains every load in flight at
+      // the top of the unrolled loop.)
+      const int t0 = w0i + it * kDecWaves * kTile;
+      const int left = Li - t0;  // > 0: the tile index is clamped to the wave's last tile
+      const __amdgpu_buffer_rsrc_t krs = buf_rsrc(kbase + (int64_t)t0 * kRowBytes, (uint32_t)left * kRowBytes);
 #pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        int64_t r = t0 + 8 * v + (lane >> 3);
-        r = r < L ? r : L - 1;
-        raw[v] = ld16_stream(kbase + r * kRowBytes + 16 * (lane & 7));
-      }
+      for (int v = 0; v < NV; ++v) raw[v] = buf_ld16_stream(krs, 16 * lane + 1024 * v);
+      const int ss = t0 + col < Li ? t0 + col : Li - 1;
+      sc = k_scale ? k_scale[off + ss] : 1.0f;
     } else {
+      const int64_t t0 = w0 + (int64_t)it * kDecWaves * kTile;
       int64_t r = t0 + col;
       r = r < L ? r : L - 1;
       const uint8_t* p = kbase + r * kRowBytes;
 #pragma unroll
       for (int v = 0; v < NV; ++v) raw[v] = ld16(p + 16 * v);
+      sc = k_scale ? k_scale[off + r] : 1.0f;
     }
-    int64_t s = t0 + col;
-    s = s < L ? s : L - 1;
-    sc = k_scale ? k_scale[off + s] : 1.0f;
   };
   // The fp8 tile through this wave's LDS slice: 16-byte chunk c of row r
   // sits at chunk c ^ swz(r) of the row, so that both the row-wise writes
@@ -187,10 +197,10 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
     // LDS only from here on (no global-memory op under a branch, so the
     // loads' wait counting stays exact).  Positions past L are dropped at the
     // final write; a repeated padding tile rewrites identical values.
-    const int64_t s = tok(it);
+    const int s = tok(it);
     const uint32_t key = score_key(part * sc);
-    if (g == 0) ssc[s - wg0] = key;
-    if (select && live && g == 0 && s < L) atomicAdd(&lhist[key >> kSelShift], 1u);
+    if (g == 0) ssc[s - wg0i] = key;
+    if (select && live && g == 0 && s < Li) atomicAdd(&lhist[key >> kSelShift], 1u);
   };
 
   if (nt > 0) {

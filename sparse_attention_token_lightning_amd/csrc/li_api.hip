@@ -322,6 +322,9 @@ static li_status check_decode_args(const void* q, li_dtype q_dt, const float* w,
   if (B < 0 || n_tok < 0 || max_len < 0)
     return fail(LI_E_SHAPE, "B, n_tok and max_len must be >= 0");
   if (n_tok >= (int64_t)1 << 40) return fail(LI_E_UNSUPPORTED, "n_tok too large");
+  // fp8 keys are read through 32-bit buffer offsets within a request
+  if (k_dt == LI_FP8_E4M3 && max_len > li::kDecodeFp8MaxLen)
+    return fail(LI_E_UNSUPPORTED, "fp8 decode: max_len above 33550336");
   li_status st;
   if ((st = check_k(k)) || (st = check_heads(H, D, "D"))) return st;
   return LI_OK;

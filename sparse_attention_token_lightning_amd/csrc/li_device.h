@@ -41,6 +41,21 @@ __device__ __forceinline__ i32x2 ld8_stream(const void* p) {
 }
 __device__ __forceinline__ float ldf_stream(const float* p) { return __builtin_nontemporal_load(p); }
 
+// Raw buffer resource over `bytes` bytes from p (stride 0, 32-bit data
+// format word of the gfx9 family).  A buffer load whose per-lane offset
+// (register offset + instruction offset) is at or past `bytes` returns zeros
+// and touches no memory, so loads near the end of a range need no clamp, and
+// their offsets are 32-bit with the constant part in the instruction.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+// 16-byte buffer load with the non-temporal hint (cache-policy bit NT); a
+// constant added to voff lands in the instruction's offset field.
+__device__ __forceinline__ i32x4 buf_ld16_stream(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 2);
+}
+
+
 // Four OCP E4M3FN bytes (one dword, byte 0 first) -> four bf16, exact: every
 // E4M3FN value, subnormals included, is a bf16 normal number.  Uses gfx950's
 // packed fp8 -> bf16 conversion with a unit scale.

@@ -82,6 +82,9 @@ hipError_t launch_topk_list(const TopkRows& a, const SelWs& ws, const uint2* lis
                             hipStream_t stream);
 // Positions of one row covered by one scan workgroup (decode / latent).
 int64_t decode_chunk(int64_t n_tok);
+// Longest fp8 request of the decode scan: its keys are addressed with 32-bit
+// byte offsets (position * 128 plus at most 4095 within a tile).
+constexpr int32_t kDecodeFp8MaxLen = (1 << 25) - 4096;
 int64_t latent_chunk(int64_t n_tok);
 
 // Decode scan: scores[kv_off[b] + s] for every request b and s < L_b; rows

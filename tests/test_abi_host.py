@@ -109,6 +109,12 @@ def test_decode_validation():
     assert _decode(ws=None) == li.LI_E_NULL
     assert b"workspace" in li.lib().li_last_error()
     assert _decode(B=0) == li.LI_OK  # nothing to do: returns before any launch
+    # fp8 keys are addressed with 32-bit byte offsets inside a request
+    big = (1 << 25) - 4096
+    assert _decode(max_len=big + 1, n_tok=1 << 26) == li.LI_E_UNSUPPORTED
+    assert b"max_len" in li.lib().li_last_error()
+    assert _decode(max_len=big + 1, n_tok=1 << 26, k_dt=li.LI_BF16, B=0) == li.LI_OK
+    assert _decode(max_len=big, n_tok=1 << 26, B=0) == li.LI_OK
 
 
 def test_noalloc_decode_host_checks():
