@@ -568,6 +568,66 @@ def stack_component(torch, li, args, n_layers=61, B=16, L=131072, G=4, C=8192):
     return {f"stack{n_layers}_B{B}_L{L}": res}
 
 
+def ab_compare(torch, li, inputs, args):
+    """Two builds of the library on one workload, alternating in one process
+    (same inputs, same GPU state drift for both): per round and build, a few
+    warm-up calls and then traced calls; prints the median per-kernel
+    microseconds of each build and whether their indices agree."""
+    import statistics
+    builds = {}
+    for name, path in (("package", li.LIB_PATH), ("other", os.path.abspath(args.ab_lib))):
+        li._lib = None
+        li.LIB_PATH = path
+        builds[name] = li.lib()
+    if args.ab_workload == "decode":
+        x = inputs.decode_sweep(131072)
+        q, w, kc, ks, off = dev(torch, x.q, "bf16"), dev(torch, x.w), dev(torch, x.kc, "fp8_e4m3"), \
+            dev(torch, x.k_scale), dev(torch, x.kv_off)
+        kernels, iters = ("scan", "top-k"), 20
+        def setup(L):
+            ws = torch.empty(L.li_index_decode_ws(x.B, x.n_tok, 131072, x.k, 0), dtype=torch.uint8, device="cuda")
+            idx = torch.empty((x.B, x.k), dtype=torch.int32, device="cuda")
+            return idx, lambda: li.li_index_decode(q, w, kc, ks, off, 131072, x.k, out_idx=idx, ws=ws)
+    elif args.ab_workload == "prefill":
+        x = inputs.cfg3()
+        q, qs, w, kc, ks = dev(torch, x.q, "fp8_e4m3"), dev(torch, x.q_scale), dev(torch, x.w), \
+            dev(torch, x.kc, "fp8_e4m3"), dev(torch, x.k_scale)
+        kernels, iters = ("prep", "scan", "top-k"), 5
+        def setup(L):
+            ws = torch.empty(L.li_index_prefill_ws(x.T, x.L, x.k, 0), dtype=torch.uint8, device="cuda")
+            idx = torch.empty((x.T, x.k), dtype=torch.int32, device="cuda")
+            return idx, lambda: li.li_index_prefill(q, qs, w, kc, ks, x.qpos0, x.k, out_idx=idx, ws=ws)
+    else:
+        x = inputs.cfg4()
+        q, w, wd, lat, off = dev(torch, x.q, "bf16"), dev(torch, x.w), dev(torch, x.w_dec, "bf16"), \
+            dev(torch, x.latent, "bf16"), dev(torch, x.kv_off)
+        B = len(x.kv_off) - 1
+        kernels, iters = ("absorb", "scan", "top-k"), 10
+        def setup(L):
+            ws = torch.empty(L.li_latent_score_group_ws(B, x.n_tok, 131072, x.G, x.H, x.Dc, x.k, 0),
+                             dtype=torch.uint8, device="cuda")
+            idx = torch.empty((B, x.G, x.k), dtype=torch.int32, device="cuda")
+            return idx, lambda: li.li_latent_score_group(q, w, wd, lat, None, off, 131072, x.k, out_idx=idx, ws=ws)
+    times, outs = {n: [] for n in builds}, {}
+    for rnd in range(args.ab_rounds):
+        for name, L in builds.items():
+            li._lib = L
+            idx, fn = setup(L)
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            t = traced(torch, li, fn, len(kernels), iters)
+            times[name].append([v * 1e3 for v in t])
+            outs[name] = idx.clone()
+            log(f"[ab] round {rnd} {name}: " + ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in zip(kernels, t)))
+            del idx, fn
+    res = {"workload": args.ab_workload, "other": args.ab_lib, "rounds": args.ab_rounds, "traced_calls": iters,
+           "median_us": {n: {k: statistics.median(r[j] for r in v) for j, k in enumerate(kernels)}
+                         for n, v in times.items()},
+           "indices_identical": bool(torch.equal(outs["package"], outs["other"]))}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -579,6 +639,11 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=32, help="requests in the oracle's timed sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counter scaling)")
+    ap.add_argument("--ab-lib", default=None,
+                    help="A/B mode: path of another build of libli.so; alternate it with the package's build on "
+                         "--ab-workload in one process and print the per-kernel medians (no bench line)")
+    ap.add_argument("--ab-workload", default="decode", choices=["decode", "prefill", "latent"])
+    ap.add_argument("--ab-rounds", type=int, default=4)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -591,6 +656,9 @@ def main():
     from sparse_attention_token_lightning_amd import inputs
 
     torch.cuda.set_device(0)
+    if args.ab_lib:
+        ab_compare(torch, li, inputs, args)
+        return
     log("[bench] generating decode B=32 L=131072 fp8 inputs")
     x = inputs.decode_sweep(131072)
     B, Lk = x.B, 131072
