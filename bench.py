@@ -579,8 +579,8 @@ def ab_compare(torch, li, inputs, args):
         li._lib = None
         li.LIB_PATH = path
         builds[name] = li.lib()
-    if args.ab_workload == "decode":
-        x = inputs.decode_sweep(131072)
+    if args.ab_workload in ("decode", "decode16"):
+        x = inputs.decode_sweep(131072, B=32 if args.ab_workload == "decode" else 16)
         q, w, kc, ks, off = dev(torch, x.q, "bf16"), dev(torch, x.w), dev(torch, x.kc, "fp8_e4m3"), \
             dev(torch, x.k_scale), dev(torch, x.kv_off)
         kernels, iters = ("scan", "top-k"), 20
@@ -588,6 +588,22 @@ def ab_compare(torch, li, inputs, args):
             ws = torch.empty(L.li_index_decode_ws(x.B, x.n_tok, 131072, x.k, 0), dtype=torch.uint8, device="cuda")
             idx = torch.empty((x.B, x.k), dtype=torch.int32, device="cuda")
             return idx, lambda: li.li_index_decode(q, w, kc, ks, off, 131072, x.k, out_idx=idx, ws=ws)
+    elif args.ab_workload == "ragged":
+        # as the ragged component: calls rotate over copies of the cache so the keys come from HBM
+        x = inputs.cfg2()
+        q, w, off = dev(torch, x.q, "bf16"), dev(torch, x.w), dev(torch, x.kv_off)
+        copies = [(dev(torch, x.kc, "fp8_e4m3"), dev(torch, x.k_scale)) for _ in range(RAGGED_COPIES)]
+        ml = int(x.lens.max())
+        kernels, iters = ("scan", "top-k"), 4 * RAGGED_COPIES
+        def setup(L):
+            ws = torch.empty(L.li_index_decode_ws(x.B, x.n_tok, ml, x.k, 0), dtype=torch.uint8, device="cuda")
+            idx = torch.empty((x.B, x.k), dtype=torch.int32, device="cuda")
+            turn = [0]
+            def fn():
+                kc, ks = copies[turn[0] % RAGGED_COPIES]
+                turn[0] += 1
+                li.li_index_decode(q, w, kc, ks, off, ml, x.k, out_idx=idx, ws=ws)
+            return idx, fn
     elif args.ab_workload == "prefill":
         x = inputs.cfg3()
         q, qs, w, kc, ks = dev(torch, x.q, "fp8_e4m3"), dev(torch, x.q_scale), dev(torch, x.w), \
@@ -642,7 +658,7 @@ def main():
     ap.add_argument("--ab-lib", default=None,
                     help="A/B mode: path of another build of libli.so; alternate it with the package's build on "
                          "--ab-workload in one process and print the per-kernel medians (no bench line)")
-    ap.add_argument("--ab-workload", default="decode", choices=["decode", "prefill", "latent"])
+    ap.add_argument("--ab-workload", default="decode", choices=["decode", "decode16", "ragged", "prefill", "latent"])
     ap.add_argument("--ab-rounds", type=int, default=4)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))

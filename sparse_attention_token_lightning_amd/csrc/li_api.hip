@@ -133,17 +133,17 @@ li::SelWs carve_sel(Carver& cv, int64_t rows, int64_t max_len, int64_t chunk, in
 
 // Decode selects in bucket mode when its rows fit it (see li::bucket_ok);
 // then the scan writes no dense scores unless the caller wants them.
-bool decode_bucket(int64_t n_tok, int32_t max_len, int32_t k) {
-  const int64_t chunk = li::decode_chunk(n_tok);
+bool decode_bucket(int64_t n_tok, int32_t B, int32_t max_len, int32_t k) {
+  const int64_t chunk = li::decode_chunk(n_tok, B);
   return max_len > 0 && li::bucket_ok((max_len + chunk - 1) / chunk, chunk, k, max_len);
 }
 
 size_t decode_ws(int32_t B, int64_t n_tok, int32_t max_len, int32_t k, bool scores_given) {
-  const bool bucket = decode_bucket(n_tok, max_len, k);
+  const bool bucket = decode_bucket(n_tok, B, max_len, k);
   size_t s = 0;
   if (!scores_given && !bucket) s += align_up((size_t)n_tok * 4);
   const int64_t rows = B > 0 ? B : 0;
-  s += sel_ws(rows, max_len > 0 ? max_len : 0, li::decode_chunk(n_tok), bucket);
+  s += sel_ws(rows, max_len > 0 ? max_len : 0, li::decode_chunk(n_tok, B), bucket);
   return s;
 }
 
@@ -352,9 +352,9 @@ li_status li_index_decode(const void* q, li_dtype q_dt, const float* w, const vo
     return st;
   trace_begin();
   Carver cv(ws);
-  const bool bucket = decode_bucket(n_tok, max_len, k);
+  const bool bucket = decode_bucket(n_tok, B, max_len, k);
   float* scores = out_scores ? out_scores : (bucket ? nullptr : (float*)cv.take((size_t)n_tok * 4));
-  const li::SelWs sel = carve_sel(cv, B, max_len, li::decode_chunk(n_tok), k, bucket);
+  const li::SelWs sel = carve_sel(cv, B, max_len, li::decode_chunk(n_tok, B), k, bucket);
   if ((st = hip_check(li::launch_decode_score((const uint16_t*)q, w, k_cache, k_dt == LI_FP8_E4M3,
                                               k_scale, kv_off, B, n_tok, max_len, H, k, scores, sel,
                                               s),

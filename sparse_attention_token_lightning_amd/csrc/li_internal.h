@@ -81,7 +81,7 @@ hipError_t launch_topk_self(const TopkRows& a, const SelWs& ws, hipStream_t stre
 hipError_t launch_topk_list(const TopkRows& a, const SelWs& ws, const uint2* list, const uint32_t* lcnt,
                             hipStream_t stream);
 // Positions of one row covered by one scan workgroup (decode / latent).
-int64_t decode_chunk(int64_t n_tok);
+int64_t decode_chunk(int64_t n_tok, int32_t B);
 // Longest fp8 request of the decode scan: its keys are addressed with 32-bit
 // byte offsets (position * 128 plus at most 4095 within a tile).
 constexpr int32_t kDecodeFp8MaxLen = (1 << 25) - 4096;
