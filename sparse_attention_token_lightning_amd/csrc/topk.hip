@@ -1056,14 +1056,15 @@ __device__ void bucket_finish(const Row& row, KeyAt key_at, PosAt pos_at, uint32
   }
 }
 
-template <int NWMAX>
+// NWMAX: scan workgroups per request at most; RS: list entries per thread in
+// the up-front loads.
+template <int NWMAX, int RS>
 __global__ __launch_bounds__(kBucketThreads) void topk_bucket_kernel(TopkRows a, SelWs ws, int ecap, int nwords,
                                                                      int staged) {
   constexpr int NT = kBucketThreads;
   static_assert(4 * NT == kSelBins, "four level-0 bins per thread");
   constexpr int TPC = NT / NWMAX;              // threads per list in the up-front loads
-  constexpr int RS = NWMAX <= 16 ? 8 : 24;     // up-front entries per thread
-  constexpr int SPW = TPC * RS;                // entries per list loaded up front (256 or 384)
+  constexpr int SPW = TPC * RS;                // entries per list loaded up front (128 .. 384)
   extern __shared__ uint2 bdyn[];
   const int k = a.k;
   uint2* eqc = bdyn;
@@ -1331,26 +1332,24 @@ hipError_t launch_topk_bucket(const TopkRows& a, const SelWs& ws, int64_t max_le
   const int nwords = (int)((max_len + 31) / 32);
   const int staged = a.k <= kBucketStageK ? 1 : 0;
   const uint32_t lds = (uint32_t)ecap * 8u + (uint32_t)bucket_fixed_lds(a.k, max_len);
-  if (ws.nwg <= 16) {
-    static bool lds_set = false;
+  // Up-front list loads: a request's lists hold k keys above b* and the keys
+  // of b* itself (about 3K in all at k = 2048 over 128K positions), so 16
+  // lists take 256 entries each and 32 lists 128 each at k <= 2048; a larger k
+  // loads 384 per list.  The rest of a longer list follows in a second round.
+  auto go = [&](auto kernel, bool& lds_set) -> hipError_t {
     if (!lds_set) {
-      if (hipError_t e = hipFuncSetAttribute((const void*)topk_bucket_kernel<16>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBucketLds))
+      if (hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)kBucketLds))
         return e;
       lds_set = true;
     }
-    return launch_kernel(topk_bucket_kernel<16>, dim3((unsigned)a.rows), dim3(kBucketThreads), lds, stream, a, ws,
-                         ecap, nwords, staged);
-  }
-  static bool lds_set32 = false;
-  if (!lds_set32) {
-    if (hipError_t e = hipFuncSetAttribute((const void*)topk_bucket_kernel<kBucketMaxNwg>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBucketLds))
-      return e;
-    lds_set32 = true;
-  }
-  return launch_kernel(topk_bucket_kernel<kBucketMaxNwg>, dim3((unsigned)a.rows), dim3(kBucketThreads), lds, stream,
-                       a, ws, ecap, nwords, staged);
+    return launch_kernel(kernel, dim3((unsigned)a.rows), dim3(kBucketThreads), lds, stream, a, ws, ecap, nwords,
+                         staged);
+  };
+  static bool set16 = false, set32s = false, set32 = false;
+  if (ws.nwg <= 16) return go(topk_bucket_kernel<16, 8>, set16);
+  if (a.k <= 2048) return go(topk_bucket_kernel<kBucketMaxNwg, 8>, set32s);
+  return go(topk_bucket_kernel<kBucketMaxNwg, 24>, set32);
 }
 
 hipError_t launch_topk(const TopkRows& a, hipStream_t stream) {
