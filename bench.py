@@ -228,9 +228,8 @@ def components(torch, li, inputs, args):
     idx = torch.empty((x.T, x.k), dtype=torch.int32, device="cuda")
     ws = torch.empty(li.lib().li_index_prefill_ws(x.T, x.L, x.k, 0), dtype=torch.uint8, device="cuda")
     fn = lambda: li.li_index_prefill(q, qs, w, kc, ks, x.qpos0, x.k, out_idx=idx, ws=ws)
-    # u-row preparation, scan (+ thresholds), select; the first calls in a
-    # process run slower while the 2 GB candidate-list workspace is first
-    # touched, so three warm-up calls
+    # u-row preparation, scan (+ thresholds), select; the first prefill calls
+    # in a process run slower than the settled ones, so three warm-up calls
     wall, (prep, scan, topk) = timed(torch, li, fn, 3, args.comp_iters, 3)
     pairs = sum(x.qpos0 + t + 1 for t in range(x.T))
     flop = 2.0 * x.H * x.D * pairs
