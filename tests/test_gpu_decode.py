@@ -245,3 +245,32 @@ def test_decode_anchor_shape_k8192_every_row():
     assert torch.equal(gi, li.li_index_decode(q, w, kc, ks, off, L, k))
     gi0 = li.li_index_decode(q, torch.zeros_like(w), kc, ks, off, L, k)
     assert torch.equal(gi0.cpu(), torch.arange(k, dtype=torch.int32).expand(nb, k))
+
+
+def test_decode_b16_32_lists_every_row():
+    """B = 16 requests of 131072 fp8 keys: 32 scan workgroups per request, so
+    the selection reads 32 lists, 128 entries of each up front at k <= 2048
+    (the rest of a longer list in a second round).  k = 2048 and k = 1500:
+    every row is the top k of its own scores, the same without a score
+    output, and one request matches the oracle's set; all tied, 0 .. k-1."""
+    x = inputs.decode_sweep(131072)
+    nb, L = 16, 131072
+    q, w = dev(x.q[:nb], "bf16"), dev(x.w[:nb])
+    kc, ks = dev(x.kc[:nb * L], x.k_dt), dev(x.k_scale[:nb * L])
+    off = dev(x.kv_off[:nb + 1])
+    for k in (2048, 1500):
+        print(f"[decode parity] B={nb} L={L} k={k} (32 lists)", flush=True)
+        sc = torch.empty(nb * L, dtype=torch.float32, device="cuda")
+        gi = li.li_index_decode(q, w, kc, ks, off, L, k, out_scores=sc)
+        torch.cuda.synchronize()
+        check_rows_are_top_k_of_own_scores(gi, sc.view(nb, L))
+        assert torch.equal(gi, li.li_index_decode(q, w, kc, ks, off, L, k))
+        b = 5
+        sl = slice(b * L, (b + 1) * L)
+        ri, rs, ra = oracle.index_decode(x.q[b:b + 1], x.q_dt, x.w[b:b + 1], x.kc[sl], x.k_dt, x.k_scale[sl],
+                                         np.array([0, L], np.int64), 64, 128, k)
+        gs = sc.cpu().numpy()[sl]
+        check_scores(gs, rs, ra, what=f"B=16 k={k} b={b}")
+        check_sets(gi[b].cpu().numpy(), ri[0], rs, ra, L, what=f"B=16 k={k} b={b}")
+    gi0 = li.li_index_decode(q, torch.zeros_like(w), kc, ks, off, L, 2048)
+    assert torch.equal(gi0.cpu(), torch.arange(2048, dtype=torch.int32).expand(nb, 2048))
