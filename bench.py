@@ -646,6 +646,46 @@ def ab_compare(torch, li, inputs, args):
     print(json.dumps(res), flush=True)
 
 
+def phase_stamps(torch, li, inputs, args, calls=20):
+    """The bucket top-k's phases at the headline shape, from the stamps build:
+    after each call, thread 0 of every row's workgroup has recorded the
+    100 MHz real-time counter after each phase's barrier.  Prints, per phase,
+    the median over rows and calls of the time from the row's start, and the
+    median over calls of the slowest row."""
+    import statistics
+    li._lib = None
+    li.LIB_PATH = os.path.abspath(args.stamps_lib)
+    L = li.lib()
+    L.li_read_stamps.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+    L.li_read_stamps.restype = ctypes.c_int32
+    x = inputs.decode_sweep(131072)
+    q, w, kc, ks, off = dev(torch, x.q, "bf16"), dev(torch, x.w), dev(torch, x.kc, "fp8_e4m3"), \
+        dev(torch, x.k_scale), dev(torch, x.kv_off)
+    ws = torch.empty(L.li_index_decode_ws(x.B, x.n_tok, 131072, x.k, 0), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((x.B, x.k), dtype=torch.int32, device="cuda")
+    phases = {1: "partials and list prefixes loaded, Q summed", 2: "b* and the list starts",
+              3: "candidates in LDS", 5: "radix levels", 6: "bitmaps marked", 7: "word prefixes",
+              8: "slots placed", 9: "output row written"}
+    buf = (ctypes.c_ulonglong * (64 * 10))()
+    per, slow = {p: [] for p in phases}, {p: [] for p in phases}
+    for c in range(calls + 3):
+        li.li_index_decode(q, w, kc, ks, off, 131072, x.k, out_idx=idx, ws=ws)
+        torch.cuda.synchronize()
+        if c < 3:
+            continue
+        if L.li_read_stamps(ctypes.addressof(buf), 64 * 10) != 0:
+            raise RuntimeError("li_read_stamps failed")
+        t0 = min(buf[r * 10] for r in range(x.B))
+        for p in phases:
+            v = [(buf[r * 10 + p] - buf[r * 10]) / 100.0 for r in range(x.B)]
+            per[p] += v
+            slow[p].append(max((buf[r * 10 + p] - t0) / 100.0 for r in range(x.B)))
+    res = {"workload": "decode fp8 B=32 L=131072 top-2048", "calls": calls, "unit": "us",
+           "phases": {phases[p]: {"median_row": statistics.median(per[p]), "slowest_row": statistics.median(slow[p])}
+                      for p in phases}}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -662,6 +702,9 @@ def main():
                          "--ab-workload in one process and print the per-kernel medians (no bench line)")
     ap.add_argument("--ab-workload", default="decode", choices=["decode", "decode16", "ragged", "prefill", "latent"])
     ap.add_argument("--ab-rounds", type=int, default=4)
+    ap.add_argument("--stamps-lib", default=None,
+                    help="phase mode: path of the stamps build (build.py --stamps); run the headline decode and "
+                         "print the bucket top-k's per-phase times (no bench line)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -676,6 +719,9 @@ def main():
     torch.cuda.set_device(0)
     if args.ab_lib:
         ab_compare(torch, li, inputs, args)
+        return
+    if args.stamps_lib:
+        phase_stamps(torch, li, inputs, args)
         return
     log("[bench] generating decode B=32 L=131072 fp8 inputs")
     x = inputs.decode_sweep(131072)

@@ -19,20 +19,26 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, extra=None) -> str:
+def build(verbose: bool = False, extra=None, out=None) -> str:
+    lib = out or LIB
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            # MFMA accumulators in ordinary VGPRs: the epilogues read them with
            # VALU ops, which would otherwise need a copy out of AGPRs each time.
            "-mllvm", "-amdgpu-mfma-vgpr-form",
            "-Wno-unused-command-line-argument", "-I", os.path.join(HERE, "..", "include"),
-           "-o", LIB + ".tmp"] + sources() + list(extra or [])
+           "-o", lib + ".tmp"] + sources() + list(extra or [])
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--stamps" in sys.argv:
+        # measurement build: the bucket top-k records per-phase time stamps
+        # (bench.py --stamps-lib); not the library the package loads
+        print(build(verbose="-v" in sys.argv, extra=["-DLI_STAMPS"], out=os.path.join(HERE, "libli_stamps.so")))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -30,6 +30,24 @@
 #include "li_select.h"
 
 namespace li {
+
+// Phase stamps of the bucket top-k, a measurement aid compiled in only with
+// -DLI_STAMPS (build.py --stamps, a separate library): thread 0 of the row's
+// workgroup records the 100 MHz real-time counter after each phase's
+// barrier.  The product build has none of this code.
+#ifdef LI_STAMPS
+constexpr int kStampRows = 64, kStampPhases = 10;
+__device__ unsigned long long li_stamp_buf[kStampRows * kStampPhases];
+#define LI_STAMP(i)                                                                              \
+  do {                                                                                           \
+    if (threadIdx.x == 0 && blockIdx.x < kStampRows)                                             \
+      li_stamp_buf[blockIdx.x * kStampPhases + (i)] = __builtin_amdgcn_s_memrealtime();          \
+  } while (0)
+#else
+#define LI_STAMP(i) \
+  do {              \
+  } while (0)
+#endif
 namespace {
 
 constexpr int kRowThreads = 512;   // per-row kernel
@@ -981,6 +999,7 @@ __device__ void bucket_finish(const Row& row, KeyAt key_at, PosAt pos_at, uint32
     cnt = shb[2];
     __syncthreads();
   }
+  LI_STAMP(5);
   // Keys of b* above the resolved prefix are kept; of those equal to it, the
   // first rem by position.
 #pragma unroll 1
@@ -991,6 +1010,7 @@ __device__ void bucket_finish(const Row& row, KeyAt key_at, PosAt pos_at, uint32
     else if (key == prefix) atomicOr(&ebits[p >> 5], 1u << (p & 31));
   }
   __syncthreads();
+  LI_STAMP(6);
   // Per bitmap word, the marked positions before it: #greater << 18 | #equal
   // (#greater < k <= 2^14, #equal <= n <= 2^17).  Wave v takes words
   // [v*WPW, (v+1)*WPW) in rounds of 64 consecutive words (one per lane, no
@@ -1029,6 +1049,7 @@ __device__ void bucket_finish(const Row& row, KeyAt key_at, PosAt pos_at, uint32
     if (64 * i < WPW && w < nwr) wpre[w] = woff + iw[i];
   }
   __syncthreads();
+  LI_STAMP(7);
   // Every kept position's slot: #greater-before + min(#equal-before, m), or for
   // an equal key #greater-before + #equal-before when that is below m.
   const uint32_t m = rem;
@@ -1052,8 +1073,10 @@ __device__ void bucket_finish(const Row& row, KeyAt key_at, PosAt pos_at, uint32
   }
   if (stage) {
     __syncthreads();
+    LI_STAMP(8);
     for (int i = tid; i < kk; i += NT) row.out[i] = (int32_t)stage[i];
   }
+  LI_STAMP(9);
 }
 
 // NWMAX: scan workgroups per request at most; RS: list entries per thread in
@@ -1083,6 +1106,7 @@ __global__ __launch_bounds__(kBucketThreads) void topk_bucket_kernel(TopkRows a,
   const int tid = threadIdx.x;
   const int r = blockIdx.x;
   const int64_t prow = (int64_t)r * ws.nwg;
+  LI_STAMP(0);
   // 1. One round of loads, issued before the row's length is known (so they
   //    do not wait for kv_off): the 8 bytes of bins 4t .. 4t+3 of every
   //    partial, and entries sl + TPC*j of list sw.  Indices are clamped to the
@@ -1126,6 +1150,7 @@ __global__ __launch_bounds__(kBucketThreads) void topk_bucket_kernel(TopkRows a,
   qfirst[tid] = q[0];
   qlast[tid] = q[3];
   __syncthreads();
+  LI_STAMP(1);
   {
     // Q is non-increasing with Q[0] = n > k and Q[2048] = 0: one bin crosses.
     // Its thread records part_w[b*] and, but for the last bin of its four,
@@ -1169,6 +1194,7 @@ __global__ __launch_bounds__(kBucketThreads) void topk_bucket_kernel(TopkRows a,
     }
   }
   __syncthreads();
+  LI_STAMP(2);
   const uint32_t bstar = shb[0], ngt = shb[1], neq = shb[2];
   __syncthreads();  // shb is reused by the radix levels
   const bool eq_lds = neq <= (uint32_t)ecap;
@@ -1204,6 +1230,7 @@ __global__ __launch_bounds__(kBucketThreads) void topk_bucket_kernel(TopkRows a,
     }
   }
   __syncthreads();
+  LI_STAMP(3);
   if (eq_lds) {
     auto lkey = [&](int64_t e) { return eqc[e].x; };
     auto lpos = [&](int64_t e) { return (int64_t)eqc[e].y; };
@@ -1356,5 +1383,14 @@ hipError_t launch_topk(const TopkRows& a, hipStream_t stream) {
   SelWs none = {};
   return launch_row(a, none, kSelFull, stream);
 }
+
+#ifdef LI_STAMPS
+// Copies the stamps of the last bucket top-k call (rows < 64, 10 phases each,
+// 100 MHz ticks) to host memory; 0 on success.
+extern "C" int li_read_stamps(unsigned long long* host, int n) {
+  if (!host || n < 0 || n > kStampRows * kStampPhases) return -1;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(li_stamp_buf), (size_t)n * 8) == hipSuccess ? 0 : -1;
+}
+#endif
 
 }  // namespace li
