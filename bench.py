@@ -335,6 +335,30 @@ def components(torch, li, inputs, args):
         "note": f"calls rotate over {RAGGED_COPIES} copies of the 86.5 MB cache so the keys come from HBM, "
                 "not the 256 MB MALL"}
     del q, w, off, copies, idx, ws, x
+    # ---- decode at shorter contexts: B = 32 x L for L = 8K, 32K (the 128K point
+    # is the headline); each cache fits the 256 MB MALL, so the calls rotate over
+    # copies holding more than 512 MB together
+    sweep = {}
+    for Ls in (8192, 32768):
+        x = inputs.decode_sweep(Ls)
+        q, w, off = dev(torch, x.q, "bf16"), dev(torch, x.w), dev(torch, x.kv_off)
+        ncp = -(-(512 << 20) // (x.n_tok * FP8_KEY_BYTES))
+        copies = [(dev(torch, x.kc, "fp8_e4m3"), dev(torch, x.k_scale)) for _ in range(ncp)]
+        idx = torch.empty((x.B, x.k), dtype=torch.int32, device="cuda")
+        ws = torch.empty(L.li_index_decode_ws(x.B, x.n_tok, Ls, x.k, 0), dtype=torch.uint8, device="cuda")
+        turn = [0]
+
+        def fn():
+            kc, ks = copies[turn[0] % ncp]
+            turn[0] += 1
+            li.li_index_decode(q, w, kc, ks, off, Ls, x.k, out_idx=idx, ws=ws)
+        wall, (scan, topk) = timed(torch, li, fn, 2, max(args.comp_iters, 2 * ncp), 2)
+        sweep[f"L{Ls}"] = {"scan_ms": scan, "topk_ms": topk, "total_ms": wall, "copies": ncp,
+                           "keys_per_s": x.n_tok / (wall * 1e-3),
+                           "scan_gbs": x.n_tok * FP8_KEY_BYTES / (scan * 1e-3) / 1e9,
+                           "scan_hbm_frac": x.n_tok * FP8_KEY_BYTES / (scan * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del q, w, off, copies, idx, ws, x
+    out["decode_fp8_B32_sweep"] = sweep
     # ---- latent-cache append: prefill chunk (T = 4096) and decode step (B = 16) ---
     # h and W_enc rotate over copies (the chunk's 59 MB would otherwise be served
     # from the 256 MB MALL), as a model step streams other weights in between.
