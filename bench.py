@@ -614,19 +614,20 @@ def ab_compare(torch, li, inputs, args):
             ws = torch.empty(L.li_index_decode_ws(x.B, x.n_tok, 131072, x.k, 0), dtype=torch.uint8, device="cuda")
             idx = torch.empty((x.B, x.k), dtype=torch.int32, device="cuda")
             return idx, lambda: li.li_index_decode(q, w, kc, ks, off, 131072, x.k, out_idx=idx, ws=ws)
-    elif args.ab_workload == "ragged":
-        # as the ragged component: calls rotate over copies of the cache so the keys come from HBM
-        x = inputs.cfg2()
+    elif args.ab_workload in ("ragged", "decode8k"):
+        # as the ragged and sweep components: calls rotate over copies of the cache so the keys come from HBM
+        x = inputs.cfg2() if args.ab_workload == "ragged" else inputs.decode_sweep(8192)
         q, w, off = dev(torch, x.q, "bf16"), dev(torch, x.w), dev(torch, x.kv_off)
-        copies = [(dev(torch, x.kc, "fp8_e4m3"), dev(torch, x.k_scale)) for _ in range(RAGGED_COPIES)]
+        ncp = max(RAGGED_COPIES, -(-(512 << 20) // (x.n_tok * FP8_KEY_BYTES)))
+        copies = [(dev(torch, x.kc, "fp8_e4m3"), dev(torch, x.k_scale)) for _ in range(ncp)]
         ml = int(x.lens.max())
-        kernels, iters = ("scan", "top-k"), 4 * RAGGED_COPIES
+        kernels, iters = ("scan", "top-k"), 2 * ncp
         def setup(L):
             ws = torch.empty(L.li_index_decode_ws(x.B, x.n_tok, ml, x.k, 0), dtype=torch.uint8, device="cuda")
             idx = torch.empty((x.B, x.k), dtype=torch.int32, device="cuda")
             turn = [0]
             def fn():
-                kc, ks = copies[turn[0] % RAGGED_COPIES]
+                kc, ks = copies[turn[0] % ncp]
                 turn[0] += 1
                 li.li_index_decode(q, w, kc, ks, off, ml, x.k, out_idx=idx, ws=ws)
             return idx, fn
@@ -724,7 +725,8 @@ def main():
     ap.add_argument("--ab-lib", default=None,
                     help="A/B mode: path of another build of libli.so; alternate it with the package's build on "
                          "--ab-workload in one process and print the per-kernel medians (no bench line)")
-    ap.add_argument("--ab-workload", default="decode", choices=["decode", "decode16", "ragged", "prefill", "latent"])
+    ap.add_argument("--ab-workload", default="decode",
+                    choices=["decode", "decode16", "decode8k", "ragged", "prefill", "latent"])
     ap.add_argument("--ab-rounds", type=int, default=4)
     ap.add_argument("--stamps-lib", default=None,
                     help="phase mode: path of the stamps build (build.py --stamps); run the headline decode and "
