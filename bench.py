@@ -683,18 +683,19 @@ def phase_stamps(torch, li, inputs, args, calls=20):
     L = li.lib()
     L.li_read_stamps.argtypes = [ctypes.c_void_p, ctypes.c_int32]
     L.li_read_stamps.restype = ctypes.c_int32
-    x = inputs.decode_sweep(131072)
+    x = inputs.decode_sweep(131072, B=32 if args.stamps_workload == "decode" else 16)
+    k = 2048 if args.stamps_workload == "decode" else 8192
     q, w, kc, ks, off = dev(torch, x.q, "bf16"), dev(torch, x.w), dev(torch, x.kc, "fp8_e4m3"), \
         dev(torch, x.k_scale), dev(torch, x.kv_off)
-    ws = torch.empty(L.li_index_decode_ws(x.B, x.n_tok, 131072, x.k, 0), dtype=torch.uint8, device="cuda")
-    idx = torch.empty((x.B, x.k), dtype=torch.int32, device="cuda")
+    ws = torch.empty(L.li_index_decode_ws(x.B, x.n_tok, 131072, k, 0), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((x.B, k), dtype=torch.int32, device="cuda")
     phases = {1: "partials and list prefixes loaded, Q summed", 2: "b* and the list starts",
               3: "candidates in LDS", 5: "radix levels", 6: "bitmaps marked", 7: "word prefixes",
               8: "slots placed", 9: "output row written"}
     buf = (ctypes.c_ulonglong * (64 * 10))()
     per, slow = {p: [] for p in phases}, {p: [] for p in phases}
     for c in range(calls + 3):
-        li.li_index_decode(q, w, kc, ks, off, 131072, x.k, out_idx=idx, ws=ws)
+        li.li_index_decode(q, w, kc, ks, off, 131072, k, out_idx=idx, ws=ws)
         torch.cuda.synchronize()
         if c < 3:
             continue
@@ -705,7 +706,7 @@ def phase_stamps(torch, li, inputs, args, calls=20):
             v = [(buf[r * 10 + p] - buf[r * 10]) / 100.0 for r in range(x.B)]
             per[p] += v
             slow[p].append(max((buf[r * 10 + p] - t0) / 100.0 for r in range(x.B)))
-    res = {"workload": "decode fp8 B=32 L=131072 top-2048", "calls": calls, "unit": "us",
+    res = {"workload": f"decode fp8 B={x.B} L=131072 top-{k}", "calls": calls, "unit": "us",
            "phases": {phases[p]: {"median_row": statistics.median(per[p]), "slowest_row": statistics.median(slow[p])}
                       for p in phases}}
     print(json.dumps(res), flush=True)
@@ -728,6 +729,8 @@ def main():
     ap.add_argument("--ab-workload", default="decode",
                     choices=["decode", "decode16", "decode8k", "ragged", "prefill", "latent"])
     ap.add_argument("--ab-rounds", type=int, default=4)
+    ap.add_argument("--stamps-workload", default="decode", choices=["decode", "anchor"],
+                    help="decode: B = 32 x 131072, k = 2048; anchor: the HS anchor, B = 16 x 131072, k = 8192")
     ap.add_argument("--stamps-lib", default=None,
                     help="phase mode: path of the stamps build (build.py --stamps); run the headline decode and "
                          "print the bucket top-k's per-phase times (no bench line)")

@@ -1075,6 +1075,8 @@ __device__ void bucket_finish(const Row& row, KeyAt key_at, PosAt pos_at, uint32
     __syncthreads();
     LI_STAMP(8);
     for (int i = tid; i < kk; i += NT) row.out[i] = (int32_t)stage[i];
+  } else {
+    LI_STAMP(8);  // (slots written straight to the output: thread 0's own progress)
   }
   LI_STAMP(9);
 }
