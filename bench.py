@@ -605,15 +605,17 @@ def ab_compare(torch, li, inputs, args):
         li._lib = None
         li.LIB_PATH = path
         builds[name] = li.lib()
-    if args.ab_workload in ("decode", "decode16"):
+    if args.ab_workload in ("decode", "decode16", "anchor"):
+        # the headline; B = 16 at k = 2048; the HS anchor (B = 16, k = 8192)
         x = inputs.decode_sweep(131072, B=32 if args.ab_workload == "decode" else 16)
+        kk = 8192 if args.ab_workload == "anchor" else x.k
         q, w, kc, ks, off = dev(torch, x.q, "bf16"), dev(torch, x.w), dev(torch, x.kc, "fp8_e4m3"), \
             dev(torch, x.k_scale), dev(torch, x.kv_off)
         kernels, iters = ("scan", "top-k"), 20
         def setup(L):
-            ws = torch.empty(L.li_index_decode_ws(x.B, x.n_tok, 131072, x.k, 0), dtype=torch.uint8, device="cuda")
-            idx = torch.empty((x.B, x.k), dtype=torch.int32, device="cuda")
-            return idx, lambda: li.li_index_decode(q, w, kc, ks, off, 131072, x.k, out_idx=idx, ws=ws)
+            ws = torch.empty(L.li_index_decode_ws(x.B, x.n_tok, 131072, kk, 0), dtype=torch.uint8, device="cuda")
+            idx = torch.empty((x.B, kk), dtype=torch.int32, device="cuda")
+            return idx, lambda: li.li_index_decode(q, w, kc, ks, off, 131072, kk, out_idx=idx, ws=ws)
     elif args.ab_workload in ("ragged", "decode8k"):
         # as the ragged and sweep components: calls rotate over copies of the cache so the keys come from HBM
         x = inputs.cfg2() if args.ab_workload == "ragged" else inputs.decode_sweep(8192)
@@ -727,7 +729,7 @@ def main():
                     help="A/B mode: path of another build of libli.so; alternate it with the package's build on "
                          "--ab-workload in one process and print the per-kernel medians (no bench line)")
     ap.add_argument("--ab-workload", default="decode",
-                    choices=["decode", "decode16", "decode8k", "ragged", "prefill", "latent"])
+                    choices=["decode", "decode16", "anchor", "decode8k", "ragged", "prefill", "latent"])
     ap.add_argument("--ab-rounds", type=int, default=4)
     ap.add_argument("--stamps-workload", default="decode", choices=["decode", "anchor"],
                     help="decode: B = 32 x 131072, k = 2048; anchor: the HS anchor, B = 16 x 131072, k = 8192")
