@@ -1116,9 +1116,11 @@ __global__ __launch_bounds__(kBucketThreads) void topk_bucket_kernel(TopkRows a,
   //    not write this call (past the row's end) are loaded and ignored.
   const int sw = tid / TPC, sl = tid % TPC;
   const uint2* slist = ws.blist + (prow + (sw < ws.nwg ? sw : ws.nwg - 1)) * ws.chunk;
-  uint2 sv[RS];
+  // Two entries per 16-byte load: entries 2 (sl + TPC j) and 2 (sl + TPC j) + 1.
+  static_assert(RS % 2 == 0, "entry pairs");
+  i32x4 sv[RS / 2];
 #pragma unroll
-  for (int j = 0; j < RS; ++j) sv[j] = slist[sl + TPC * j];
+  for (int j = 0; j < RS / 2; ++j) sv[j] = ld16(slist + 2 * (sl + TPC * j));
   uint2 pw[NWMAX];
 #pragma unroll
   for (int w = 0; w < NWMAX; ++w) {
@@ -1214,7 +1216,10 @@ __global__ __launch_bounds__(kBucketThreads) void topk_bucket_kernel(TopkRows a,
       }
     };
 #pragma unroll
-    for (int j = 0; j < RS; ++j) put((uint32_t)(sl + TPC * j), sv[j]);
+    for (int j = 0; j < RS / 2; ++j) {
+      put((uint32_t)(2 * (sl + TPC * j)), make_uint2((uint32_t)sv[j].x, (uint32_t)sv[j].y));
+      put((uint32_t)(2 * (sl + TPC * j) + 1), make_uint2((uint32_t)sv[j].z, (uint32_t)sv[j].w));
+    }
     // the rest of a long list, eight loads per thread at a time
 #pragma unroll 1
     for (uint32_t e0 = (uint32_t)(SPW + sl); e0 < cw; e0 += 8 * TPC) {
